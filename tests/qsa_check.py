@@ -1,0 +1,79 @@
+"""Acceptance rules used by the parity tests.
+
+Selection: the top-k boundary is discontinuous, so a selection is compared
+with the oracle's scores, not only with the oracle's own choice. For a row
+with ``m`` scored slots let ``s_m`` be the m-th best oracle score and
+``s_m1`` the best dropped one. If their relative gap
+``(s_m - s_m1) / max(|s_m|, |s_m1|)`` exceeds ``REL_GAP`` the kept set must
+equal the oracle's exactly; otherwise every kept candidate must score at
+least ``s_m - tol`` and every dropped one at most ``s_m1 + tol`` with
+``tol = REL_GAP * max(|s_m|, |s_m1|)``.
+
+Overlap between two selections is reported as the Jaccard index
+``|A ∩ B| / |A ∪ B|`` ("Qwen4 in llama.cpp: Dissecting PR #27742", section
+"QSA Is an Address-Selection Problem, Not a New Attention Equation").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_GAP = 1e-3
+BF16_ABS_TOL = 2e-2
+F32_REL_TOL = 1e-5
+
+
+class SelectionMismatch(AssertionError):
+    pass
+
+
+def jaccard(a, b) -> float:
+    a = {int(x) for x in a if x >= 0}
+    b = {int(x) for x in b if x >= 0}
+    if not a and not b:
+        return 1.0
+    return len(a & b) / len(a | b)
+
+
+def check_selection(sel_row, scores, own_block: int, top_k: int, rel_gap: float = REL_GAP) -> str:
+    """Validate one row's selection against the oracle's float64 candidate scores.
+
+    Returns ``"clear"`` (exact match required and found) or ``"ambiguous"``
+    (boundary within the gap, selection valid); raises
+    :class:`SelectionMismatch` otherwise.
+    """
+    sel = [int(x) for x in sel_row]
+    kept = [x for x in sel if x >= 0]
+    pad = sel[len(kept):]
+    if any(x >= 0 for x in pad) or len(sel) != top_k:
+        raise SelectionMismatch(f"padding not at the tail: {sel}")
+    if kept != sorted(set(kept)):
+        raise SelectionMismatch(f"ids not strictly ascending: {sel}")
+    if own_block not in kept or kept[-1] != own_block:
+        raise SelectionMismatch(f"own block {own_block} missing or not last: {sel}")
+    scored = kept[:-1]
+    slots = min(top_k - 1, own_block)
+    if len(scored) != slots:
+        raise SelectionMismatch(f"expected {slots} scored blocks, got {len(scored)}: {sel}")
+    if any(c < 0 or c >= own_block for c in scored):
+        raise SelectionMismatch(f"scored id out of range: {sel}")
+    if slots == own_block or slots == 0:
+        return "clear"  # every candidate (or none) is kept: one valid answer
+    scores = np.asarray(scores, dtype=np.float64)
+    order = sorted(range(own_block), key=lambda c: (-scores[c], c))
+    expect = sorted(order[:slots])
+    s_m, s_m1 = scores[order[slots - 1]], scores[order[slots]]
+    denom = max(abs(s_m), abs(s_m1))
+    gap = (s_m - s_m1) / denom if denom > 0 else 0.0
+    if gap > rel_gap:
+        if scored != expect:
+            raise SelectionMismatch(
+                f"clear row (gap {gap:.3e}) differs: got {scored}, expected {expect}")
+        return "clear"
+    tol = rel_gap * denom
+    chosen = set(scored)
+    for c in range(own_block):
+        if c in chosen and scores[c] < s_m - tol:
+            raise SelectionMismatch(f"kept block {c} scores {scores[c]} below cutoff {s_m}")
+        if c not in chosen and scores[c] > s_m1 + tol:
+            raise SelectionMismatch(f"dropped block {c} scores {scores[c]} above cutoff {s_m1}")
+    return "ambiguous"
