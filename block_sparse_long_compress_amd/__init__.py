@@ -1,0 +1,76 @@
+"""Qwen Sparse Attention (QSA) for AMD MI355X (gfx950).
+
+Keys are mean-pooled into one compressed key per block, every (token, KV
+head) scores the compressed blocks and keeps its top-k (own block included),
+and exact softmax attention runs over the kept blocks only. All steps run in
+the hand-written HIP kernels of ``lib/libqsa.so`` behind the C ABI of
+``include/qsa.h``; this package is the Python binding (argument marshalling)
+plus two convenience pipelines that chain the ABI calls.
+"""
+from __future__ import annotations
+
+import torch
+
+from .binding import (  # noqa: F401
+    EXPORTED,
+    LIB,
+    LIB_PATH,
+    QSA_BF16,
+    QSA_F32,
+    QSA_OP_COMPRESS,
+    QSA_OP_DECODE,
+    QSA_OP_PREFILL,
+    QSA_OP_SELECT,
+    QsaError,
+    QsaShape,
+    abi_version,
+    make_shape,
+    qsa_compress_keys,
+    qsa_score_select,
+    qsa_sparse_attn_decode,
+    qsa_sparse_attn_prefill,
+    qsa_workspace_bytes,
+    status_str,
+)
+
+
+def shape_for(q: torch.Tensor, k: torch.Tensor, block_size: int, top_k: int, scale: float = 0.0) -> QsaShape:
+    """ABI shape from Q ``[b][q_len][Hq][d]`` (or ``[b][Hq][d]``) and K ``[b][Hkv][cap][d]``."""
+    return make_shape(k.shape[0], q.shape[-2], k.shape[1], k.shape[3], block_size, top_k, q.dtype, scale)
+
+
+def prefill(q, k, v, block_size, top_k, q_pos0=0, scale=0.0, k_comp=None, with_scores=False):
+    """Compress, select and attend for ``q_len`` query rows at positions ``q_pos0 ..``.
+
+    Returns ``(out, sel, k_comp[, sel_scores])``; ``k_comp`` is computed for
+    every complete block below ``q_pos0 + q_len`` unless given.
+    """
+    b, q_len, hq, d = q.shape
+    hkv, cap = k.shape[1], k.shape[2]
+    kv_len = q_pos0 + q_len
+    shape = shape_for(q, k, block_size, top_k, scale)
+    if k_comp is None:
+        k_comp = torch.empty(b, hkv, cap // block_size, d, dtype=torch.float32, device=q.device)
+        qsa_compress_keys(shape, k, kv_len, k_comp)
+    sel = torch.empty(b, q_len, hkv, top_k, dtype=torch.int32, device=q.device)
+    scores = torch.empty(b, q_len, hkv, top_k, dtype=torch.float32, device=q.device) if with_scores else None
+    qsa_score_select(shape, q, q_pos0, k_comp, kv_len, cap, sel, scores)
+    out = torch.empty_like(q)
+    qsa_sparse_attn_prefill(shape, q, k, v, q_pos0, sel, out)
+    return (out, sel, k_comp, scores) if with_scores else (out, sel, k_comp)
+
+
+def decode(q, k, v, kv_len, block_size, top_k, k_comp, scale=0.0, with_scores=False):
+    """One decode step for ``q`` ``[b][Hq][d]`` at position ``kv_len - 1`` given compressed keys.
+
+    Returns ``(out, sel[, sel_scores])`` with ``sel`` ``[b][Hkv][k]``.
+    """
+    b, hq, d = q.shape
+    hkv, cap = k.shape[1], k.shape[2]
+    shape = shape_for(q, k, block_size, top_k, scale)
+    sel = torch.empty(b, hkv, top_k, dtype=torch.int32, device=q.device)
+    scores = torch.empty(b, hkv, top_k, dtype=torch.float32, device=q.device) if with_scores else None
+    qsa_score_select(shape, q.view(b, 1, hq, d), kv_len - 1, k_comp, kv_len, cap, sel, scores)
+    out = torch.empty_like(q)
+    qsa_sparse_attn_decode(shape, q, k, v, kv_len, sel, out)
+    return (out, sel, scores) if with_scores else (out, sel)

@@ -1,0 +1,157 @@
+"""ctypes binding of the QSA C ABI (``include/qsa.h``).
+
+Argument marshalling only: torch tensors supply device pointers, sizes come
+from their shapes, and work is enqueued on torch's current stream of the
+tensors' device. Every step of the computation runs in the HIP kernels of
+``lib/libqsa.so``; there is no fallback. The library must have been built
+(``python -m block_sparse_long_compress_amd.build``); importing this module
+without it raises immediately.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("QSA_LIB", os.path.join(HERE, "lib", "libqsa.so"))
+
+QSA_F32, QSA_BF16 = 0, 1
+QSA_OP_COMPRESS, QSA_OP_SELECT, QSA_OP_DECODE, QSA_OP_PREFILL = 0, 1, 2, 3
+STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_ERR_WORKSPACE", 4: "QSA_ERR_HIP"}
+EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
+            "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill")
+
+
+class QsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class QsaShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"QSA HIP library not built: {LIB_PATH} is missing "
+                          "(run python -m block_sparse_long_compress_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    SH = ctypes.POINTER(QsaShape)
+    lib.qsa_abi_version.restype = ctypes.c_int
+    lib.qsa_abi_version.argtypes = []
+    lib.qsa_status_str.restype = ctypes.c_char_p
+    lib.qsa_status_str.argtypes = [ctypes.c_int]
+    lib.qsa_workspace_bytes.restype = SZ
+    lib.qsa_workspace_bytes.argtypes = [SH, ctypes.c_int, I64, I64]
+    lib.qsa_compress_keys.restype = ctypes.c_int
+    lib.qsa_compress_keys.argtypes = [SH, P, I64, I64, I64, P, P]
+    lib.qsa_score_select.restype = ctypes.c_int
+    lib.qsa_score_select.argtypes = [SH, P, I64, I64, P, I64, I64, P, P, P, SZ, P]
+    lib.qsa_sparse_attn_decode.restype = ctypes.c_int
+    lib.qsa_sparse_attn_decode.argtypes = [SH, P, P, P, I64, I64, P, P, P, SZ, P]
+    lib.qsa_sparse_attn_prefill.restype = ctypes.c_int
+    lib.qsa_sparse_attn_prefill.argtypes = [SH, P, P, P, I64, I64, I64, P, P, P, SZ, P]
+    return lib
+
+
+LIB = _load()
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, top_k, dtype, scale=0.0) -> QsaShape:
+    """Build the ABI shape struct; ``dtype`` is a torch dtype or QSA_F32/QSA_BF16."""
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: QSA_F32, torch.bfloat16: QSA_BF16}[dtype]
+    return QsaShape(batch, n_q_heads, n_kv_heads, head_dim, block_size, top_k, dtype, float(scale))
+
+
+def abi_version() -> int:
+    return LIB.qsa_abi_version()
+
+
+def status_str(status: int) -> str:
+    return LIB.qsa_status_str(status).decode()
+
+
+def qsa_workspace_bytes(shape: QsaShape, op: int, q_len: int, kv_len: int) -> int:
+    n = LIB.qsa_workspace_bytes(ctypes.byref(shape), op, q_len, kv_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise QsaError(1, "qsa_workspace_bytes")
+    return n
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _workspace(shape, op, q_len, kv_len, ws, device):
+    need = qsa_workspace_bytes(shape, op, q_len, kv_len)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, (ws.numel() * ws.element_size() if ws is not None else 0)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QsaError(status, where)
+
+
+def qsa_compress_keys(shape: QsaShape, k, kv_len: int, k_comp, block_begin: int = 0, stream=None):
+    """Mean-pool complete key blocks ``block_begin .. kv_len//Bs - 1`` into ``k_comp`` (float32)."""
+    _check(LIB.qsa_compress_keys(ctypes.byref(shape), _ptr(k), kv_len, k.shape[2], block_begin, _ptr(k_comp),
+                                 _stream(k, stream)), "qsa_compress_keys")
+    return k_comp
+
+
+def qsa_score_select(shape: QsaShape, q, q_pos0: int, k_comp, kv_len: int, kv_cap: int, sel, sel_scores=None,
+                     ws=None, stream=None):
+    """Score compressed blocks and write the kept block ids of every (token, KV head) into ``sel``."""
+    q_len = q.shape[1]
+    ws, nbytes = _workspace(shape, QSA_OP_SELECT, q_len, kv_len, ws, q.device)
+    _check(LIB.qsa_score_select(ctypes.byref(shape), _ptr(q), q_len, q_pos0, _ptr(k_comp), kv_len, kv_cap, _ptr(sel),
+                                _ptr(sel_scores), _ptr(ws), nbytes, _stream(q, stream)), "qsa_score_select")
+    return sel
+
+
+def qsa_sparse_attn_decode(shape: QsaShape, q, k, v, kv_len: int, sel, out, ws=None, stream=None):
+    """Attention of one token per sequence (``q`` ``[b][Hq][d]``) over its selected blocks."""
+    ws, nbytes = _workspace(shape, QSA_OP_DECODE, 1, kv_len, ws, q.device)
+    _check(LIB.qsa_sparse_attn_decode(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), kv_len, k.shape[2], _ptr(sel),
+                                      _ptr(out), _ptr(ws), nbytes, _stream(q, stream)), "qsa_sparse_attn_decode")
+    return out
+
+
+def qsa_sparse_attn_prefill(shape: QsaShape, q, k, v, q_pos0: int, sel, out, ws=None, stream=None):
+    """Causal attention of ``q_len`` tokens (``q`` ``[b][q_len][Hq][d]``) over their selected blocks."""
+    q_len = q.shape[1]
+    ws, nbytes = _workspace(shape, QSA_OP_PREFILL, q_len, q_pos0 + q_len, ws, q.device)
+    _check(LIB.qsa_sparse_attn_prefill(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), q_len, q_pos0, k.shape[2],
+                                       _ptr(sel), _ptr(out), _ptr(ws), nbytes, _stream(q, stream)),
+           "qsa_sparse_attn_prefill")
+    return out

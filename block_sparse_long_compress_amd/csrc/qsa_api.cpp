@@ -1,0 +1,182 @@
+// C ABI of the QSA library: argument validation, workspace sizing and
+// dispatch to the kernels. Every check runs on the host before any HIP call;
+// on failure nothing is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/qsa.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+int prefill_smem_bytes(const Dims& s, int64_t q_len, int64_t q_pos0);
+}
+
+namespace {
+
+using qsa::Dims;
+
+constexpr int kMaxLds = 160 * 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+// Shape checks shared by every entry point.
+qsa_status check_shape(const qsa_shape* sh, Dims* out) {
+  if (!sh) return QSA_ERR_INVALID;
+  if (sh->batch <= 0 || sh->n_q_heads <= 0 || sh->n_kv_heads <= 0 || sh->head_dim <= 0 || sh->block_size <= 0 ||
+      sh->top_k <= 0)
+    return QSA_ERR_INVALID;
+  if (sh->n_q_heads % sh->n_kv_heads != 0) return QSA_ERR_INVALID;
+  if (sh->dtype != QSA_F32 && sh->dtype != QSA_BF16) return QSA_ERR_INVALID;
+  if (!std::isfinite(sh->scale) || sh->scale < 0.f) return QSA_ERR_INVALID;
+  const int G = sh->n_q_heads / sh->n_kv_heads;
+  if (sh->head_dim != 64 && sh->head_dim != 128) return QSA_ERR_UNSUPPORTED;
+  if (!pow2_in(sh->block_size, 32, 128)) return QSA_ERR_UNSUPPORTED;
+  if (sh->top_k > 64) return QSA_ERR_UNSUPPORTED;
+  if (!pow2_in(G, 1, 16)) return QSA_ERR_UNSUPPORTED;
+  if (sh->batch > 65535 || sh->n_kv_heads > 65535) return QSA_ERR_UNSUPPORTED;
+  out->batch = sh->batch;
+  out->hq = sh->n_q_heads;
+  out->hkv = sh->n_kv_heads;
+  out->group = G;
+  out->d = sh->head_dim;
+  out->bs = sh->block_size;
+  out->top_k = sh->top_k;
+  out->dtype = sh->dtype;
+  out->scale = sh->scale == 0.f ? (float)(1.0 / std::sqrt((double)sh->head_dim)) : sh->scale;
+  return QSA_OK;
+}
+
+// Positions are bounded so that block ids fit in int32 and grids stay small.
+constexpr int64_t kMaxPositions = int64_t(1) << 31;
+
+qsa_status check_prefill_limits(const Dims& s, int64_t q_len, int64_t q_pos0) {
+  if (q_len > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (s.dtype == QSA_BF16 && qsa::prefill_smem_bytes(s, q_len, q_pos0) > kMaxLds) return QSA_ERR_UNSUPPORTED;
+  return QSA_OK;
+}
+
+qsa_status hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char* qsa_status_str(qsa_status status) {
+  switch (status) {
+    case QSA_OK:
+      return "QSA_OK";
+    case QSA_ERR_INVALID:
+      return "QSA_ERR_INVALID: invalid argument";
+    case QSA_ERR_UNSUPPORTED:
+      return "QSA_ERR_UNSUPPORTED: valid but unsupported shape";
+    case QSA_ERR_WORKSPACE:
+      return "QSA_ERR_WORKSPACE: workspace missing or too small";
+    case QSA_ERR_HIP:
+      return "QSA_ERR_HIP: kernel launch failed";
+  }
+  return "QSA_ERR_UNKNOWN";
+}
+
+size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_t kv_len) {
+  Dims s;
+  if (check_shape(shape, &s) != QSA_OK) return (size_t)-1;
+  switch (op) {
+    case QSA_OP_COMPRESS:
+      return 0;
+    case QSA_OP_SELECT:
+      if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
+      return qsa::plan_select(s, q_len, kv_len - q_len).ws_bytes;
+    case QSA_OP_DECODE:
+      if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
+      return s.dtype == QSA_BF16 ? qsa::plan_decode(s, kv_len).ws_bytes : 0;
+    case QSA_OP_PREFILL:
+      if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
+      return qsa::plan_prefill(s, q_len, kv_len - q_len).ws_bytes;
+  }
+  return (size_t)-1;
+}
+
+qsa_status qsa_compress_keys(const qsa_shape* shape, const void* k, int64_t kv_len, int64_t kv_cap,
+                             int64_t block_begin, float* k_comp, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (kv_len < 0 || kv_cap <= 0 || kv_len > kv_cap || block_begin < 0) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  const int64_t blk_end = kv_len / s.bs;
+  if (block_begin >= blk_end) return QSA_OK;  // no complete block in range: nothing is read or written
+  if (!k || !k_comp || !aligned16(k) || !aligned16(k_comp)) return QSA_ERR_INVALID;
+  return hip_status(qsa::launch_compress(s, k, kv_cap, block_begin, blk_end, k_comp,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+qsa_status qsa_score_select(const qsa_shape* shape, const void* q, int64_t q_len, int64_t q_pos0,
+                            const float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                            void* ws, size_t ws_bytes, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !sel || !aligned16(q) || !aligned16(sel)) return QSA_ERR_INVALID;
+  if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
+  if (q_len <= 0 || q_pos0 < 0 || kv_len != q_pos0 + q_len || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
+  // k_comp is read only for candidate blocks, which exist once a row sits past the first block
+  if ((kv_len - 1) / s.bs > 0 && (!k_comp || !aligned16(k_comp))) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  const qsa::SelectPlan plan = qsa::plan_select(s, q_len, q_pos0);
+  const int64_t grid = plan.tiled ? (q_len + 15) / 16 : (int64_t)s.batch * q_len * s.hkv * plan.n_chunks;
+  if (grid > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  return hip_status(qsa::launch_select(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+qsa_status qsa_sparse_attn_decode(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                  int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !k || !v || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) || !aligned16(out)) return QSA_ERR_INVALID;
+  if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (s.dtype == QSA_F32)
+    return hip_status(qsa::launch_attn_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), 1, kv_len - 1, kv_cap, sel,
+                                           static_cast<float*>(out), hs));
+  const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len);
+  if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  return hip_status(qsa::launch_decode(s, plan, q, k, v, kv_len, kv_cap, sel, out, ws, hs));
+}
+
+qsa_status qsa_sparse_attn_prefill(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                   int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !k || !v || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) || !aligned16(out)) return QSA_ERR_INVALID;
+  if (q_len <= 0 || q_pos0 < 0 || kv_cap <= 0 || q_pos0 + q_len > kv_cap) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  st = check_prefill_limits(s, q_len, q_pos0);
+  if (st != QSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (s.dtype == QSA_F32)
+    return hip_status(qsa::launch_attn_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), q_len, q_pos0, kv_cap, sel,
+                                           static_cast<float*>(out), hs));
+  const qsa::PrefillPlan plan = qsa::plan_prefill(s, q_len, q_pos0);
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  return hip_status(qsa::launch_prefill(s, plan, q, k, v, q_len, q_pos0, kv_cap, sel, out, ws, hs));
+}
+
+}  // extern "C"

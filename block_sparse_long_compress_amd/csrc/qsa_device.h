@@ -1,0 +1,141 @@
+// Device helpers shared by the QSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round-to-nearest-even float -> bf16 (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element loads of the two supported storage types, widened to float.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+};
+
+// ---------------------------------------------------------------- shuffles
+
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
+  return (uint32_t)__shfl_xor((int)v, mask, kWave);
+}
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = shfl_xor_u32((uint32_t)v, mask);
+  uint32_t hi = shfl_xor_u32((uint32_t)(v >> 32), mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, kWave);
+  uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  for (int m = 32; m > 0; m >>= 1) v = fmaxf(v, shfl_xor_f32(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  for (int m = 32; m > 0; m >>= 1) v += shfl_xor_f32(v, m);
+  return v;
+}
+
+// ---------------------------------------------------------------- selection keys
+//
+// A candidate block is ranked by (score descending, block id ascending).
+// Both go into one 64-bit key so that a larger key is a better candidate:
+// high word = order-preserving image of the float score (-0 folded onto +0),
+// low word = ~id. Key 0 is below every real key and marks "no candidate".
+
+__device__ __forceinline__ uint32_t score_order_bits(float s) {
+  uint32_t u = (s == 0.0f) ? 0u : __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t make_key(float score, int id) {
+  return ((uint64_t)score_order_bits(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+__device__ __forceinline__ float key_score(uint64_t key) {
+  uint32_t o = (uint32_t)(key >> 32);
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+
+// Bitonic sort of one key per lane across the wave, descending (lane 0 = largest).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint64_t y = shfl_xor_u64(x, j);
+      bool lower = (lane & j) == 0;
+      bool desc = (lane & k) == 0;
+      bool take_max = (lower == desc);
+      x = take_max ? (x > y ? x : y) : (x < y ? x : y);
+    }
+  }
+  return x;
+}
+
+// Top-64 of two descending lists held one key per lane; result descending.
+__device__ __forceinline__ uint64_t wave_merge_desc(uint64_t cur, uint64_t fresh_desc) {
+  const int lane = lane_id();
+  uint64_t rev = shfl_u64(fresh_desc, kWave - 1 - lane);
+  uint64_t x = cur > rev ? cur : rev;  // bitonic sequence holding the top 64
+#pragma unroll
+  for (int j = kWave / 2; j > 0; j >>= 1) {
+    uint64_t y = shfl_xor_u64(x, j);
+    bool lower = (lane & j) == 0;
+    x = lower ? (x > y ? x : y) : (x < y ? x : y);
+  }
+  return x;
+}
+
+// Fold one lane-per-candidate batch into a running descending top list
+// (`cur`, lane j = j-th best). Only the first `m` entries of `cur` matter;
+// the batch is skipped when no key beats the current m-th best.
+__device__ __forceinline__ uint64_t topk_fold(uint64_t cur, uint64_t fresh, int m) {
+  uint64_t thr = shfl_u64(cur, m - 1);
+  if (__ballot(fresh > thr) == 0) return cur;
+  return wave_merge_desc(cur, wave_sort_desc(fresh));
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace qsa

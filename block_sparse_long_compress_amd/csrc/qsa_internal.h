@@ -1,0 +1,58 @@
+// Host-side launch entry points shared between the C ABI layer and the
+// kernel translation units. Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct Dims {
+  int batch, hq, hkv, group, d, bs, top_k, dtype;
+  float scale;  // resolved (never 0)
+};
+
+// Block compression, blocks [blk_begin, blk_end) of every (b, g).
+hipError_t launch_compress(const Dims& s, const void* k, int64_t kv_cap, int64_t blk_begin, int64_t blk_end,
+                           float* k_comp, hipStream_t st);
+
+// Selection ------------------------------------------------------------------
+struct SelectPlan {
+  bool tiled;          // prefill-style tile path (rows share candidates)
+  int chunk;           // split path: candidates per chunk (multiple of 64)
+  int64_t n_chunks;    // split path: chunks per row
+  size_t ws_bytes;
+};
+SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0);
+hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,
+                         const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
+                         hipStream_t st);
+
+// Decode attention --------------------------------------------------------------
+struct DecodePlan {
+  int blocks_per_wg;
+  int n_split;
+  size_t ws_bytes;
+};
+DecodePlan plan_decode(const Dims& s, int64_t kv_len);
+hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
+                         int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* ws, hipStream_t st);
+
+// Prefill attention -------------------------------------------------------------
+struct PrefillPlan {
+  int rows_per_wg;
+  size_t ws_bytes;
+};
+PrefillPlan plan_prefill(const Dims& s, int64_t q_len, int64_t q_pos0);
+hipError_t launch_prefill(const Dims& s, const PrefillPlan& plan, const void* q, const void* k, const void* v,
+                          int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* ws,
+                          hipStream_t st);
+
+// Generic float32 attention (one wave per query row); used for dtype QSA_F32.
+hipError_t launch_attn_f32(const Dims& s, const float* q, const float* k, const float* v, int64_t q_len,
+                           int64_t q_pos0, int64_t kv_cap, const int32_t* sel, float* out, hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace qsa

@@ -1,0 +1,338 @@
+// Indexer scoring and top-k block selection ("Qwen4 in llama.cpp: Dissecting
+// PR #27742", section "QSA Is an Address-Selection Problem, Not a New
+// Attention Equation": compressed blocks are scored, the top-k kept and
+// turned into cache addresses).
+//
+// Score of candidate c for (token, KV head g): scale * <qbar, kc[c]> with
+// qbar the float32 sum of the group's G query heads (equal to the sum of the
+// per-head scores). Selection keeps the query's own block plus the
+// min(k-1, i) best candidates, ranked by the 64-bit key of qsa_device.h
+// (score descending, id ascending), and writes ids ascending.
+//
+// Two paths:
+//  * tile path (many query rows, prefill): a workgroup takes 16 consecutive
+//    rows of one (b, g), which share the candidate prefix. Candidate chunks
+//    of 64 compressed keys are staged in LDS and scored with fp32 MFMA
+//    (16x16x4, full fp32 products); each wave then folds four rows' scores
+//    into running top lists with wave-wide bitonic merges.
+//  * split path (few rows, decode): the candidates of a row are cut into
+//    chunks spread over the whole GPU. Each wave streams 64 compressed keys
+//    per step with fully coalesced 16-byte loads (1 KiB per instruction),
+//    finishes the dot products with a transpose-reduce butterfly, and keeps a
+//    running top list; the chunk's list goes to the workspace and a merge
+//    kernel reduces the lists of a row, skipping every key below the best
+//    chunk-local cutoff (a valid lower bound of the row's cutoff).
+#include "qsa_device.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+// Write one row's selection from a descending top list held one key per
+// lane (lanes < slots valid): ids ascending, own block last, -1 padding.
+__device__ void finalize_row(uint64_t cur, int slots, int own, int top_k, int32_t* sel_row, float* score_row) {
+  const int lane = lane_id();
+  int id = lane < slots ? key_id(cur) : own;
+  float sc = lane < slots ? key_score(cur) : __builtin_inff();
+  // Sort lanes 0..slots by ascending id: descending on the complemented id.
+  uint64_t k2 = lane <= slots ? (((uint64_t)(0xFFFFFFFFu - (uint32_t)id) << 32) | __float_as_uint(sc)) : 0ull;
+  k2 = wave_sort_desc(k2);
+  const bool real = lane <= slots;
+  const int out_id = real ? (int)(0xFFFFFFFFu - (uint32_t)(k2 >> 32)) : -1;
+  const float out_sc = real ? __uint_as_float((uint32_t)k2) : -__builtin_inff();
+  if (lane < top_k) {
+    sel_row[lane] = out_id;
+    if (score_row) score_row[lane] = out_sc;
+  }
+}
+
+// ------------------------------------------------------------------ tile path
+
+constexpr int kTileRows = 16;
+constexpr int kTileCands = 64;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ q, const float* __restrict__ k_comp,
+                                                          int32_t* __restrict__ sel, float* __restrict__ sel_scores,
+                                                          int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
+                                                          int hkv, int G, int bs, int top_k, float scale) {
+  constexpr int QP = D + 4;  // padded row strides (floats): conflict-free 16-byte reads
+  __shared__ float qbar[kTileRows][QP];
+  __shared__ float kc[kTileCands][QP];
+  __shared__ float sc[kTileRows][kTileCands + 4];
+
+  const int64_t t0 = (int64_t)blockIdx.x * kTileRows;
+  const int g = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int64_t rows = q_len - t0 < kTileRows ? q_len - t0 : kTileRows;
+
+  for (int idx = tid; idx < kTileRows * D; idx += 256) {
+    const int r = idx / D, e = idx % D;
+    float v = 0.f;
+    if (r < rows) {
+      const T* src = q + ((b * q_len + t0 + r) * hq + (int64_t)g * G) * D + e;
+      for (int j = 0; j < G; ++j) v += Elem<T>::load(src, (int64_t)j * D);
+    }
+    qbar[r][e] = v;
+  }
+
+  const int64_t own_last = (q_pos0 + t0 + rows - 1) / bs;  // candidates of every row are < own_last
+  const float* kc_src = k_comp + ((b * hkv + g) * nb_cap) * D;
+  uint64_t cur[4] = {0ull, 0ull, 0ull, 0ull};
+
+  for (int64_t c0 = 0; c0 < own_last; c0 += kTileCands) {
+    __syncthreads();  // previous chunk fully consumed
+    for (int idx = tid; idx < kTileCands * D / 4; idx += 256) {
+      const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
+      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+      if (c0 + r < own_last) v = *reinterpret_cast<const f32x4_t*>(kc_src + (c0 + r) * D + e4);
+      *reinterpret_cast<f32x4_t*>(&kc[r][e4]) = v;
+    }
+    __syncthreads();
+    {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      const int m = lane % 16, kg = lane / 16;
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&qbar[m][16 * u + 4 * kg]);
+        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&kc[16 * w + m][16 * u + 4 * kg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], bv[e], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * kg + i][16 * w + m] = acc[i] * scale;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 4 * w + rr;
+      if (r >= rows) continue;
+      const int64_t own = (q_pos0 + t0 + r) / bs;
+      const int slots = own < top_k - 1 ? (int)own : top_k - 1;
+      if (slots == 0) continue;
+      const int64_t cand = c0 + lane;
+      const uint64_t key = cand < own ? make_key(sc[r][lane], (int)cand) : 0ull;
+      cur[rr] = topk_fold(cur[rr], key, slots);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = 4 * w + rr;
+    if (r >= rows) continue;
+    const int64_t t = t0 + r;
+    const int own = (int)((q_pos0 + t) / bs);
+    const int slots = own < top_k - 1 ? own : top_k - 1;
+    const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
+    finalize_row(cur[rr], slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+  }
+}
+
+// ------------------------------------------------------------------ split path
+
+// Dot products of 64 consecutive compressed keys with qbar. Lane l reads the
+// 16-byte column slice (l % LPR) of rows (l / LPR) + RPL*j; after the
+// butterfly lane l holds the full dot product of row RPL*(l % LPR) + l / LPR.
+template <int D>
+__device__ __forceinline__ float dot64_rows(const float* __restrict__ rows_base, int64_t n_valid, const f32x4_t& qv) {
+  constexpr int LPR = D / 4;
+  constexpr int RPL = kWave / LPR;
+  constexpr int N = LPR;  // loads per lane = values per lane before the butterfly
+  const int lane = lane_id();
+  float vals[N];
+  f32x4_t raw[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int row = RPL * j + lane / LPR;
+    raw[j] = row < n_valid ? *reinterpret_cast<const f32x4_t*>(rows_base + (int64_t)row * D + 4 * (lane % LPR))
+                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) vals[j] = raw[j][0] * qv[0] + raw[j][1] * qv[1] + raw[j][2] * qv[2] + raw[j][3] * qv[3];
+#pragma unroll
+  for (int half = N / 2; half >= 1; half /= 2) {
+    const bool upper = (lane & half) != 0;
+#pragma unroll
+    for (int v = 0; v < half; ++v) {
+      const float send = upper ? vals[v] : vals[v + half];
+      const float keep = upper ? vals[v + half] : vals[v];
+      vals[v] = keep + shfl_xor_f32(send, half);
+    }
+  }
+  return vals[0];
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__ q, const float* __restrict__ k_comp,
+                                                           int32_t* __restrict__ sel, float* __restrict__ sel_scores,
+                                                           uint64_t* __restrict__ ws, int64_t q_len, int64_t q_pos0,
+                                                           int64_t nb_cap, int hq, int hkv, int G, int bs, int top_k,
+                                                           float scale, int chunk, int64_t n_chunks) {
+  constexpr int LPR = D / 4;
+  constexpr int RPL = kWave / LPR;
+  __shared__ float qbar[D];
+  __shared__ uint64_t lists[4][kWave];
+
+  const int64_t row = blockIdx.x / n_chunks;
+  const int64_t ch = blockIdx.x % n_chunks;
+  const int64_t b = row / (q_len * hkv);
+  const int64_t t = (row / hkv) % q_len;
+  const int g = (int)(row % hkv);
+  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  const int own = (int)((q_pos0 + t) / bs);
+  const int slots = own < top_k - 1 ? own : top_k - 1;
+
+  if (slots == 0) {  // nothing to score: the own block alone
+    if (ch == 0 && w == 0) {
+      const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
+      finalize_row(0ull, 0, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+    }
+    return;
+  }
+  for (int e = tid; e < D; e += 256) {
+    const T* src = q + ((b * q_len + t) * hq + (int64_t)g * G) * D + e;
+    float v = 0.f;
+    for (int j = 0; j < G; ++j) v += Elem<T>::load(src, (int64_t)j * D);
+    qbar[e] = v;
+  }
+  __syncthreads();
+  const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(&qbar[4 * (lane % LPR)]);
+
+  const int64_t c_begin = ch * chunk;
+  const int64_t c_end = c_begin + chunk < own ? c_begin + chunk : own;
+  const float* kc_src = k_comp + ((b * hkv + g) * nb_cap) * D;
+  uint64_t cur = 0ull;
+  for (int64_t base = c_begin + (int64_t)kWave * w; base < c_end; base += 4 * kWave) {
+    const float s = dot64_rows<D>(kc_src + base * D, c_end - base, qv);
+    const int64_t cand = base + RPL * (lane % LPR) + lane / LPR;
+    const uint64_t key = cand < c_end ? make_key(s * scale, (int)cand) : 0ull;
+    cur = topk_fold(cur, key, slots);
+  }
+  lists[w][lane] = cur;
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int o = 1; o < 4; ++o) {
+    const uint64_t other = lists[o][lane];
+    const uint64_t thr = shfl_u64(cur, slots - 1);
+    if (__ballot(other > thr) != 0) cur = wave_merge_desc(cur, other);
+  }
+  if (n_chunks == 1) {
+    const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
+    finalize_row(cur, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+  } else if (lane < slots) {
+    ws[(row * n_chunks + ch) * (top_k - 1) + lane] = cur;
+  }
+}
+
+// One workgroup per row: reduce the row's chunk lists to the final top list.
+__global__ __launch_bounds__(256) void select_merge_kernel(int32_t* __restrict__ sel, float* __restrict__ sel_scores,
+                                                           const uint64_t* __restrict__ ws, int64_t q_len,
+                                                           int64_t q_pos0, int hkv, int bs, int top_k,
+                                                           int64_t n_chunks) {
+  __shared__ uint64_t lists[4][kWave];
+  __shared__ uint64_t red[4];
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / (q_len * hkv);
+  const int64_t t = (row / hkv) % q_len;
+  const int g = (int)(row % hkv);
+  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  const int own = (int)((q_pos0 + t) / bs);
+  const int slots = own < top_k - 1 ? own : top_k - 1;
+  if (slots == 0) return;  // written by the split kernel
+  const int sm = top_k - 1;
+  const uint64_t* lst = ws + row * n_chunks * sm;
+
+  // Lower bound of the row cutoff: the best chunk-local slots-th key.
+  uint64_t bound = 0ull;
+  for (int64_t c = tid; c < n_chunks; c += 256) {
+    const uint64_t x = lst[c * sm + slots - 1];
+    bound = x > bound ? x : bound;
+  }
+  for (int m = 32; m > 0; m >>= 1) {
+    const uint64_t y = shfl_xor_u64(bound, m);
+    bound = y > bound ? y : bound;
+  }
+  if (lane == 0) red[w] = bound;
+  __syncthreads();
+  bound = red[0];
+  for (int o = 1; o < 4; ++o) bound = red[o] > bound ? red[o] : bound;
+
+  uint64_t cur = 0ull;
+  const int64_t n_keys = n_chunks * sm;
+  for (int64_t base = (int64_t)kWave * w; base < n_keys; base += 4 * kWave) {
+    const int64_t idx = base + lane;
+    uint64_t key = 0ull;
+    if (idx < n_keys && (int)(idx % sm) < slots) key = lst[idx];
+    key = key >= bound ? key : 0ull;
+    cur = topk_fold(cur, key, slots);
+  }
+  lists[w][lane] = cur;
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int o = 1; o < 4; ++o) {
+    const uint64_t other = lists[o][lane];
+    const uint64_t thr = shfl_u64(cur, slots - 1);
+    if (__ballot(other > thr) != 0) cur = wave_merge_desc(cur, other);
+  }
+  const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
+  finalize_row(cur, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, int64_t q_len, int64_t q_pos0,
+                        const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
+                        hipStream_t st) {
+  const T* q = static_cast<const T*>(qv);
+  const int64_t nb_cap = kv_cap / s.bs;
+  if (plan.tiled) {
+    dim3 grid((unsigned)((q_len + kTileRows - 1) / kTileRows), (unsigned)s.hkv, (unsigned)s.batch);
+    hipLaunchKernelGGL((select_tile_kernel<T, D>), grid, dim3(256), 0, st, q, k_comp, sel, sel_scores, q_len, q_pos0,
+                       nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, s.scale);
+    return hipGetLastError();
+  }
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  uint64_t* wsk = static_cast<uint64_t*>(ws);
+  hipLaunchKernelGGL((select_split_kernel<T, D>), dim3((unsigned)(rows * plan.n_chunks)), dim3(256), 0, st, q,
+                     k_comp, sel, sel_scores, wsk, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
+                     s.scale, plan.chunk, plan.n_chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.n_chunks == 1) return e;
+  hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256), 0, st, sel, sel_scores, wsk, q_len, q_pos0,
+                     s.hkv, s.bs, s.top_k, plan.n_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
+  SelectPlan p{};
+  const int64_t kv_len = q_pos0 + q_len;
+  const int64_t max_cand = (kv_len - 1) / s.bs;  // candidates of the last row
+  p.tiled = q_len >= kTileRows;
+  p.chunk = 256;
+  p.n_chunks = 1;
+  p.ws_bytes = 0;
+  if (p.tiled) return p;
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  // Aim for >= 1024 workgroups over the GPU while keeping >= 64 keys per wave step.
+  int chunk = 1024;
+  while (chunk > 64 && rows * ((max_cand + chunk - 1) / chunk) < 1024) chunk /= 2;
+  p.chunk = chunk;
+  p.n_chunks = max_cand > 0 ? (max_cand + chunk - 1) / chunk : 1;
+  if (p.n_chunks > 1) p.ws_bytes = (size_t)rows * p.n_chunks * (s.top_k - 1) * sizeof(uint64_t);
+  return p;
+}
+
+hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,
+                         const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
+                         hipStream_t st) {
+  if (s.dtype == 1)
+    return s.d == 64 ? launch_typed<uint16_t, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st)
+                     : launch_typed<uint16_t, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st);
+  return s.d == 64 ? launch_typed<float, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st)
+                   : launch_typed<float, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st);
+}
+
+}  // namespace qsa

@@ -1,0 +1,162 @@
+/*
+ * qsa.h - C ABI of the MI355X (gfx950) Qwen Sparse Attention (QSA) library.
+ *
+ * QSA compresses the key cache into small blocks, scores those compressed
+ * blocks against each query, keeps the best contiguous token blocks and runs
+ * exact softmax attention over only those blocks
+ * ("Qwen4 architecture: QSA, GatedResidual, PLE", codebridge-ai.com,
+ * section 1 "QSA: not looking at every token equally").
+ * The split into a selector that returns cache addresses and an attention
+ * step that reads only those addresses follows
+ * "Qwen4 in llama.cpp: Dissecting PR #27742" (ramgpt.org), section
+ * "QSA Is an Address-Selection Problem, Not a New Attention Equation".
+ *
+ * Notation: b = batch, Hq / Hkv = query / KV heads, G = Hq / Hkv, d = head
+ * dim, Bs = block size, k = top_k, N = kv_len. Query head h reads KV head
+ * h / G. A query at absolute position p has own block i = p / Bs; its
+ * candidates are the complete blocks 0 .. i-1.
+ *
+ * Semantics (the library's reading of the pages where they are silent):
+ *   compressed key   kc[b][g][c] = mean of K[b][g][c*Bs .. c*Bs+Bs-1]
+ *   score            s(c) = scale * sum_{j<G} <q_{g*G+j}, kc[c]>
+ *   selection        own block i always kept and counted in k; the other
+ *                    min(k-1, i) slots take the best scores, equal scores
+ *                    going to the smaller block id; written ascending and
+ *                    padded with -1
+ *   attention        softmax(scale * <q_h, K_t>) weighted sum of V_t over
+ *                    the positions of the kept complete blocks plus
+ *                    i*Bs .. p of the own block
+ *   scale            1/sqrt(d) when qsa_shape.scale == 0
+ *
+ * Layouts (all contiguous, row-major, 16-byte aligned base pointers):
+ *   Q, out    [b][q_len][Hq][d]            dtype of qsa_shape
+ *   K, V      [b][Hkv][kv_cap][d]          dtype of qsa_shape
+ *   k_comp    [b][Hkv][kv_cap / Bs][d]     float32
+ *   sel       [b][q_len][Hkv][k]           int32
+ *   sel_scores[b][q_len][Hkv][k]           float32 (optional)
+ *
+ * Ownership: the caller allocates and frees every buffer (device memory for
+ * all tensors and the workspace; `shape` is host memory read during the
+ * call). The library never allocates, frees, synchronises, or keeps a
+ * pointer after returning. All work is enqueued on `stream` (a hipStream_t;
+ * NULL = the null stream), in order; results are ready when the stream
+ * reaches that point.
+ *
+ * Errors: every argument is validated on the host before any HIP call.
+ *   QSA_ERR_INVALID      null required pointer, non-positive size, Hq not a
+ *                        multiple of Hkv, kv_len > kv_cap, inconsistent
+ *                        positions, misaligned pointer, unknown op/dtype
+ *   QSA_ERR_UNSUPPORTED  valid but not implemented: d not in {64,128},
+ *                        Bs not in {32,64,128}, k outside [1,64],
+ *                        G not in {1,2,4,8,16}, too many blocks
+ *   QSA_ERR_WORKSPACE    ws_bytes below qsa_workspace_bytes(...) or ws NULL
+ *                        while bytes are needed
+ *   QSA_ERR_HIP          a kernel launch was rejected by the runtime
+ * On error nothing is enqueued (QSA_ERR_HIP: launches before the failing
+ * one may have been enqueued). Faults during execution surface at the
+ * caller's next synchronisation. Kernels trust that sel holds valid ids for
+ * the given positions and that inputs are finite.
+ *
+ * Determinism: identical inputs and shapes give bitwise identical outputs
+ * (no floating-point atomics, fixed reduction orders).
+ * Thread safety: calls may come from several host threads; calls that
+ * share output or workspace buffers must be ordered by the caller.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+enum { QSA_F32 = 0, QSA_BF16 = 1 };
+
+enum { QSA_OP_COMPRESS = 0, QSA_OP_SELECT = 1, QSA_OP_DECODE = 2, QSA_OP_PREFILL = 3 };
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_INVALID = 1,
+  QSA_ERR_UNSUPPORTED = 2,
+  QSA_ERR_WORKSPACE = 3,
+  QSA_ERR_HIP = 4
+} qsa_status;
+
+typedef struct {
+  int32_t batch;       /* sequences in the call */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;    /* d */
+  int32_t block_size;  /* Bs: tokens per compressed block */
+  int32_t top_k;       /* k: kept blocks per (token, KV head), own block included */
+  int32_t dtype;       /* QSA_F32 or QSA_BF16: type of Q, K, V and out */
+  float scale;         /* softmax/score scale; 0 selects 1/sqrt(head_dim) */
+} qsa_shape;
+
+/* Version of this ABI (QSA_ABI_VERSION). */
+int qsa_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* qsa_status_str(qsa_status status);
+
+/* Bytes of device workspace the given op needs for these sizes (0 if none;
+ * (size_t)-1 if the arguments are invalid). op is one of QSA_OP_*.
+ * QSA_OP_SELECT and QSA_OP_PREFILL take q_len and kv_len = q_pos0 + q_len;
+ * QSA_OP_DECODE takes kv_len (q_len ignored). The workspace holds only
+ * scratch data of one call; its contents need no initialisation. */
+size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_t kv_len);
+
+/* Block compression ("Qwen4 architecture: QSA, GatedResidual, PLE", section 1:
+ * keys are compressed into small blocks; the mean is this library's reading).
+ * Writes k_comp rows for the complete blocks block_begin .. kv_len/Bs - 1 of
+ * every (b, KV head); other rows are left untouched. block_begin = 0
+ * compresses everything; a decode loop passes the first block not yet
+ * compressed. k: device [b][Hkv][kv_cap][d]; k_comp: device float32
+ * [b][Hkv][kv_cap/Bs][d]. Needs no workspace. When the range holds no
+ * complete block the call does nothing and k, k_comp may be NULL. */
+qsa_status qsa_compress_keys(const qsa_shape* shape, const void* k, int64_t kv_len, int64_t kv_cap,
+                             int64_t block_begin, float* k_comp, void* stream);
+
+/* Indexer scoring and top-k block selection ("Qwen4 in llama.cpp: Dissecting
+ * PR #27742", section "QSA Is an Address-Selection Problem...": compressed
+ * blocks are scored, the top-k kept and turned into cache addresses).
+ * Query row t of q ([b][q_len][Hq][d]) sits at absolute position q_pos0 + t;
+ * requires kv_len == q_pos0 + q_len (decode: q_len = 1, q_pos0 = kv_len-1).
+ * k_comp must hold the complete blocks below each row's own block; it may
+ * be NULL when no row has a candidate (kv_len <= Bs).
+ * Writes sel [b][q_len][Hkv][k] (block ids ascending, own block last,
+ * padded with -1) and, if sel_scores is not NULL, the float32 score of each
+ * kept block at the same index (+inf for the own block, -inf for padding).
+ * ws: device scratch of qsa_workspace_bytes(shape, QSA_OP_SELECT, q_len, kv_len). */
+qsa_status qsa_score_select(const qsa_shape* shape, const void* q, int64_t q_len, int64_t q_pos0,
+                            const float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel,
+                            float* sel_scores, void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse attention for one new token per sequence at position kv_len-1
+ * ("Qwen4 in llama.cpp: Dissecting PR #27742", section "QSA Is an
+ * Address-Selection Problem...": ordinary attention restricted to the
+ * selected cells). q: [b][Hq][d]; k, v: [b][Hkv][kv_cap][d];
+ * sel: [b][Hkv][k] from qsa_score_select; out: [b][Hq][d].
+ * ws: device scratch of qsa_workspace_bytes(shape, QSA_OP_DECODE, 1, kv_len). */
+qsa_status qsa_sparse_attn_decode(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                  int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Causal sparse attention for q_len query rows at positions q_pos0 .. q_pos0+q_len-1
+ * (same passage as decode, every row with its own selection; causal inside
+ * the own block). q, out: [b][q_len][Hq][d]; k, v: [b][Hkv][kv_cap][d]
+ * holding at least q_pos0 + q_len positions; sel: [b][q_len][Hkv][k].
+ * ws: device scratch of qsa_workspace_bytes(shape, QSA_OP_PREFILL, q_len, q_pos0 + q_len). */
+qsa_status qsa_sparse_attn_prefill(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                   int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel,
+                                   void* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,139 @@
+"""C ABI contract checks that need no GPU.
+
+The library loads, exports every function ``include/qsa.h`` declares, and
+rejects invalid arguments on the host with the documented status code
+before making any HIP call. Every call here is invalid on purpose, so no
+kernel is ever launched (the pointers are never dereferenced).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+@pytest.fixture(scope="module")
+def qsa():
+    import block_sparse_long_compress_amd as m
+
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_steps():
+    names = declared_functions()
+    for n in ("qsa_compress_keys", "qsa_score_select", "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(qsa):
+    lib = ctypes.CDLL(qsa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(qsa.EXPORTED) == declared_functions()
+
+
+def test_version_and_status_strings(qsa):
+    assert qsa.abi_version() == 1
+    for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
+                       (4, "QSA_ERR_HIP")]:
+        assert qsa.status_str(code).startswith(name)
+    assert qsa.status_str(99) == "QSA_ERR_UNKNOWN"
+
+
+def good_shape(qsa, **kw):
+    args = dict(batch=1, n_q_heads=16, n_kv_heads=2, head_dim=128, block_size=64, top_k=16, dtype=qsa.QSA_BF16)
+    args.update(kw)
+    return qsa.QsaShape(args["batch"], args["n_q_heads"], args["n_kv_heads"], args["head_dim"], args["block_size"],
+                        args["top_k"], args["dtype"], args.get("scale", 0.0))
+
+
+def test_workspace_sizes(qsa):
+    sh = good_shape(qsa)
+    assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_COMPRESS, 1, 100) == 0
+    # prefill: a V^T staging copy of the cache up to kv_len rounded to blocks
+    assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_PREFILL, 8192, 8192) == 2 * 8192 * 128 * 2
+    assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_PREFILL, 100, 100) == 2 * 128 * 128 * 2
+    # decode: one partial softmax state per (row, slice) when a row is split
+    dec = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE, 1, 32768)
+    assert dec % (2 * (2 * 8 + 8 * 128) * 4) == 0
+    # select: chunk lists of the split path (decode) or nothing (tile path)
+    assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 8192, 8192) == 0
+    assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 1, 1 << 20) % (2 * 15 * 8) == 0
+    f32 = good_shape(qsa, dtype=qsa.QSA_F32, head_dim=64, n_q_heads=2, n_kv_heads=1, block_size=32, top_k=4)
+    assert qsa.qsa_workspace_bytes(f32, qsa.QSA_OP_PREFILL, 512, 512) == 0
+    assert qsa.qsa_workspace_bytes(f32, qsa.QSA_OP_DECODE, 1, 512) == 0
+    with pytest.raises(qsa.QsaError):
+        qsa.qsa_workspace_bytes(sh, 7, 1, 1)
+    with pytest.raises(qsa.QsaError):
+        qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 10, 5)
+
+
+BAD_SHAPES = [
+    (dict(batch=0), 1), (dict(n_q_heads=15), 1), (dict(n_kv_heads=0), 1), (dict(top_k=0), 1), (dict(dtype=5), 1),
+    (dict(scale=float("nan")), 1), (dict(scale=-1.0), 1), (dict(head_dim=96), 2), (dict(block_size=48), 2),
+    (dict(block_size=16), 2), (dict(block_size=256), 2), (dict(top_k=65), 2), (dict(n_q_heads=24, n_kv_heads=2), 2),
+    (dict(n_q_heads=64, n_kv_heads=2), 2),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_SHAPES)
+def test_shape_validation(qsa, kw, code):
+    sh = good_shape(qsa, **kw)
+    P = ctypes.c_void_p(4096)
+    lib = qsa.LIB
+    assert lib.qsa_compress_keys(ctypes.byref(sh), P, 64, 64, 0, P, None) == code
+    assert lib.qsa_score_select(ctypes.byref(sh), P, 1, 63, P, 64, 64, P, None, P, 1 << 20, None) == code
+    assert lib.qsa_sparse_attn_decode(ctypes.byref(sh), P, P, P, 64, 64, P, P, P, 1 << 20, None) == code
+    assert lib.qsa_sparse_attn_prefill(ctypes.byref(sh), P, P, P, 64, 0, 64, P, P, P, 1 << 20, None) == code
+
+
+def test_argument_validation(qsa):
+    lib = qsa.LIB
+    sh = ctypes.byref(good_shape(qsa))
+    P, N, MIS = ctypes.c_void_p(4096), None, ctypes.c_void_p(4100)
+    big = 1 << 30
+    INV, WS = 1, 3
+    # compress
+    assert lib.qsa_compress_keys(None, P, 64, 64, 0, P, N) == INV
+    assert lib.qsa_compress_keys(sh, N, 64, 64, 0, P, N) == INV
+    assert lib.qsa_compress_keys(sh, P, 64, 64, 0, N, N) == INV
+    assert lib.qsa_compress_keys(sh, MIS, 64, 64, 0, P, N) == INV
+    assert lib.qsa_compress_keys(sh, P, 65, 64, 0, P, N) == INV  # kv_len > kv_cap
+    assert lib.qsa_compress_keys(sh, P, -1, 64, 0, P, N) == INV
+    assert lib.qsa_compress_keys(sh, P, 64, 64, -1, P, N) == INV
+    assert lib.qsa_compress_keys(sh, P, 63, 64, 0, P, N) == 0  # no complete block: nothing to do, no launch
+    assert lib.qsa_compress_keys(sh, P, 128, 128, 2, P, N) == 0  # range already compressed
+    # select
+    assert lib.qsa_score_select(sh, P, 1, 63, P, 65, 128, P, N, P, big, N) == INV  # kv_len != q_pos0 + q_len
+    assert lib.qsa_score_select(sh, P, 0, 64, P, 64, 128, P, N, P, big, N) == INV
+    assert lib.qsa_score_select(sh, P, 1, 64, P, 65, 64, P, N, P, big, N) == INV  # beyond capacity
+    assert lib.qsa_score_select(sh, P, 1, -1, P, 0, 64, P, N, P, big, N) == INV
+    assert lib.qsa_score_select(sh, N, 1, 63, P, 64, 64, P, N, P, big, N) == INV
+    assert lib.qsa_score_select(sh, P, 1, 63, P, 64, 64, MIS, N, P, big, N) == INV
+    assert lib.qsa_score_select(sh, P, 1, 63, P, 64, 64, P, MIS, P, big, N) == INV
+    assert lib.qsa_score_select(sh, P, 1, (1 << 20) - 1, P, 1 << 20, 1 << 20, P, N, N, 0, N) == WS
+    assert lib.qsa_score_select(sh, P, 1, (1 << 20) - 1, P, 1 << 20, 1 << 20, P, N, P, 8, N) == WS
+    # decode
+    assert lib.qsa_sparse_attn_decode(sh, P, P, P, 0, 64, P, P, P, big, N) == INV
+    assert lib.qsa_sparse_attn_decode(sh, P, P, P, 65, 64, P, P, P, big, N) == INV
+    assert lib.qsa_sparse_attn_decode(sh, P, N, P, 64, 64, P, P, P, big, N) == INV
+    assert lib.qsa_sparse_attn_decode(sh, P, P, P, 64, 64, P, MIS, P, big, N) == INV
+    assert lib.qsa_sparse_attn_decode(sh, P, P, P, 32768, 32768, P, P, N, 0, N) == WS
+    # prefill
+    assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 0, 0, 64, P, P, P, big, N) == INV
+    assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 64, 1, 64, P, P, P, big, N) == INV  # beyond capacity
+    assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 64, -1, 64, P, P, P, big, N) == INV
+    assert lib.qsa_sparse_attn_prefill(sh, P, P, N, 64, 0, 64, P, P, P, big, N) == INV
+    assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 64, 0, 64, P, P, N, 0, N) == WS
+    assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 64, 0, 64, P, P, P, 16, N) == WS

@@ -1,0 +1,159 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Selections must satisfy the acceptance rule of ``qsa_check`` (bit-exact on
+clear rows), compressed keys must stay within the float32 summation bound,
+outputs within 2e-2 absolute (bf16) or 1e-5 relative per row (fp32) of the
+oracle's attention over the GPU's own (validated) selection.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_compress_amd as qsa
+import qsa_synth as S
+from gpu_common import Case, check_compress, check_rows, from_device, log
+
+pytestmark = pytest.mark.gpu
+
+
+def W(**kw) -> S.Workload:
+    base = dict(name="case", cfg_id=90, mode="prefill", batch=1, kv_len=512, n_q_heads=16, n_kv_heads=2,
+                head_dim=128, block_size=64, top_k=4, dtype="bf16", sigma=0.5)
+    base.update(kw)
+    return S.Workload(**base)
+
+
+def run_prefill(case: Case, q_pos0: int = 0, q_rows=None):
+    """Full prefill path on rows [q_pos0, kv_len); returns host (sel, out, scores, k_comp)."""
+    w = case.w
+    q = case.q if q_rows is None else case.q[:, q_rows].contiguous()
+    out, sel, k_comp, scores = qsa.prefill(q, case.k, case.v, w.block_size, w.top_k, q_pos0=q_pos0, with_scores=True)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), from_device(out), scores.cpu().numpy(), k_comp
+
+
+def all_rows(w: S.Workload, q_len: int):
+    return [(b, t, g) for b in range(w.batch) for t in range(q_len) for g in range(w.n_kv_heads)]
+
+
+PREFILL_CASES = [
+    # tiny fp32 prefill (the 512-token workload), sparse and dense top-k
+    S.WORKLOADS["prefill_512_f32"],
+    S.WORKLOADS["prefill_512_f32"].replace(top_k=16),
+    # bf16, several query tiles, ragged last block and last tile, batch 2
+    W(batch=2, kv_len=1000, top_k=4),
+    W(kv_len=777, top_k=8, head_dim=64, block_size=32),
+    W(kv_len=600, top_k=3, block_size=128),
+    W(kv_len=700, top_k=1),                                   # own block only
+    W(kv_len=700, top_k=64, block_size=32),                    # k beyond the candidates: dense
+    W(kv_len=530, n_q_heads=4, n_kv_heads=4, top_k=5),         # G = 1
+    W(kv_len=530, n_q_heads=8, n_kv_heads=4, top_k=5),         # G = 2
+    W(kv_len=530, n_q_heads=8, n_kv_heads=2, top_k=5),         # G = 4
+    W(kv_len=530, n_q_heads=16, n_kv_heads=1, top_k=5),        # G = 16
+    W(kv_len=300, dtype="f32", sigma=1.0, top_k=3, head_dim=128),
+    W(kv_len=15, top_k=2),                                     # shorter than one block
+]
+
+
+@pytest.mark.parametrize("w", PREFILL_CASES, ids=lambda w: f"{w.dtype}-b{w.batch}-n{w.kv_len}-h{w.n_q_heads}x{w.n_kv_heads}"
+                         f"-d{w.head_dim}-bs{w.block_size}-k{w.top_k}")
+def test_prefill_parity(w):
+    log(f"prefill parity {w}")
+    case = Case(w, seed=1, kv_cap=w.kv_len + 40)
+    sel, out, scores, k_comp = run_prefill(case)
+    check_compress(case, k_comp)
+    st = check_rows(case, sel, out, all_rows(w, w.kv_len), 0, scores_gpu=scores)
+    log(f"  {st}")
+
+
+def test_chunked_prefill_parity():
+    """Query rows [q_pos0, kv_len) over a cache that already holds the earlier keys."""
+    w = W(batch=2, kv_len=900, top_k=6)
+    case = Case(w, seed=2)
+    q_pos0 = 333
+    sel, out, scores, _ = run_prefill(case, q_pos0=q_pos0, q_rows=slice(q_pos0, w.kv_len))
+    # oracle rows are indexed by absolute position: shift the query view
+    case.Q = case.Q[:, q_pos0:]
+    st = check_rows(case, sel, out, all_rows(w, w.kv_len - q_pos0), q_pos0, scores_gpu=scores)
+    log(f"chunked prefill {st}")
+
+
+DECODE_CASES = [
+    W(mode="decode", batch=3, kv_len=1000, top_k=8),
+    W(mode="decode", batch=2, kv_len=64 * 16, top_k=16),        # exactly dense
+    W(mode="decode", batch=2, kv_len=50, top_k=4),              # only the own block
+    W(mode="decode", batch=2, kv_len=5000, top_k=1),
+    W(mode="decode", batch=1, kv_len=9000, top_k=64, block_size=32),
+    W(mode="decode", batch=5, kv_len=4099, top_k=12, head_dim=64, block_size=128),
+    W(mode="decode", batch=2, kv_len=3000, n_q_heads=16, n_kv_heads=1, top_k=7),
+    W(mode="decode", batch=2, kv_len=3000, n_q_heads=2, n_kv_heads=2, top_k=7),
+    W(mode="decode", batch=2, kv_len=2222, dtype="f32", sigma=1.0, top_k=5),
+]
+
+
+def run_decode(case: Case):
+    w = case.w
+    b, hq, d = w.batch, w.n_q_heads, w.head_dim
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    k_comp = torch.full((b, w.n_kv_heads, case.kv_cap // w.block_size, d), float("nan"), device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    q = case.q.view(b, hq, d)
+    out, sel, scores = qsa.decode(q, case.k, case.v, w.kv_len, w.block_size, w.top_k, k_comp, with_scores=True)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy()[:, None], from_device(out)[:, None], scores.cpu().numpy()[:, None], k_comp
+
+
+@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: f"{w.dtype}-b{w.batch}-n{w.kv_len}-h{w.n_q_heads}x{w.n_kv_heads}"
+                         f"-d{w.head_dim}-bs{w.block_size}-k{w.top_k}")
+def test_decode_parity(w):
+    log(f"decode parity {w}")
+    case = Case(w, seed=3, kv_cap=w.kv_len + 100)
+    sel, out, scores, k_comp = run_decode(case)
+    check_compress(case, k_comp)
+    rows = [(b, 0, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    st = check_rows(case, sel, out, rows, w.kv_len - 1, scores_gpu=scores)
+    log(f"  {st}")
+
+
+def test_decode_matches_last_prefill_row():
+    w = W(batch=2, kv_len=1500, top_k=6)
+    case = Case(w, seed=4)
+    sel_p, out_p, _, k_comp = run_prefill(case)
+    q = case.q[:, -1].contiguous()
+    out_d, sel_d = qsa.decode(q, case.k, case.v, w.kv_len, w.block_size, w.top_k, k_comp)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel_d.cpu().numpy(), sel_p[:, -1])
+    np.testing.assert_allclose(from_device(out_d), out_p[:, -1], rtol=0, atol=2e-2)
+
+
+def test_bitwise_determinism():
+    w = W(batch=2, kv_len=2100, top_k=6)
+    case = Case(w, seed=5)
+    a = run_prefill(case)
+    b = run_prefill(case)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(a[2], b[2])
+    d = W(mode="decode", batch=4, kv_len=70000, top_k=16)
+    dc = Case(d, seed=6)
+    x, y = run_decode(dc), run_decode(dc)
+    np.testing.assert_array_equal(x[0], y[0])
+    np.testing.assert_array_equal(x[1], y[1])
+
+
+def test_incremental_compress_matches_full():
+    """Compressing block by block (a decode loop) gives the same compressed keys as one call."""
+    w = W(batch=2, kv_len=1100)
+    case = Case(w, seed=7)
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    nb = w.kv_len // w.block_size
+    full = torch.zeros(2, 2, nb, 128, device="cuda")
+    inc = torch.zeros(2, 2, nb, 128, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, full)
+    for n in range(1, w.kv_len + 1):
+        if n % w.block_size == 0:
+            qsa.qsa_compress_keys(shape, case.k, n, inc, block_begin=n // w.block_size - 1)
+    torch.cuda.synchronize()
+    assert torch.equal(full, inc)

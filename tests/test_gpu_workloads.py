@@ -1,0 +1,93 @@
+"""GPU parity at the full sizes of the four bf16 workloads, in the launch
+configuration the benchmark times (plans depend only on the shapes).
+
+Selections are checked row by row wherever the oracle can afford it (every
+row of the 32K, 8K and 1M workloads; sampled rows of the 64 x 128K batch,
+plus the planted-block property on all of its rows). Outputs are compared on
+every row of the decode workloads and on sampled rows of the prefill.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_compress_amd as qsa
+import qsa_synth as S
+from gpu_common import Case, check_compress, check_rows, from_device, log
+
+pytestmark = pytest.mark.gpu
+
+
+def decode_full(case: Case):
+    w = case.w
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    k_comp = torch.empty(w.batch, w.n_kv_heads, case.kv_cap // w.block_size, w.head_dim, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    q = case.q.view(w.batch, w.n_q_heads, w.head_dim)
+    out, sel, scores = qsa.decode(q, case.k, case.v, w.kv_len, w.block_size, w.top_k, k_comp, with_scores=True)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy()[:, None], from_device(out)[:, None], scores.cpu().numpy()[:, None], k_comp
+
+
+@pytest.mark.parametrize("name", ["decode_32k", "decode_1m"])
+def test_decode_workload(name):
+    w = S.WORKLOADS[name]
+    log(f"workload {name}: generating")
+    case = Case(w, seed=0)
+    log(f"workload {name}: running")
+    sel, out, scores, k_comp = decode_full(case)
+    check_compress(case, k_comp)
+    rows = [(b, 0, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    st = check_rows(case, sel, out, rows, w.kv_len - 1, scores_gpu=scores)
+    log(f"  {name}: {st}")
+
+
+def test_prefill_8k_workload():
+    w = S.WORKLOADS["prefill_8k"]
+    log("workload prefill_8k: generating")
+    case = Case(w, seed=0)
+    out, sel, k_comp, scores = qsa.prefill(case.q, case.k, case.v, w.block_size, w.top_k, with_scores=True)
+    torch.cuda.synchronize()
+    sel, out, scores = sel.cpu().numpy(), from_device(out), scores.cpu().numpy()
+    check_compress(case, k_comp)
+    rows = [(0, t, g) for t in range(w.kv_len) for g in range(w.n_kv_heads)]
+    st = check_rows(case, sel, out, rows, 0, check_output=False)
+    log(f"  selections: {st}")
+    rng = np.random.default_rng(0)
+    sample = sorted(set(rng.integers(0, w.kv_len, 200).tolist()) | {0, 1, 63, 64, 1023, 1024, w.kv_len - 1})
+    st = check_rows(case, sel, out, [(0, t, g) for t in sample for g in range(2)], 0, scores_gpu=scores)
+    log(f"  sampled outputs: {st}")
+
+
+def test_batched_decode_planted_workload():
+    w = S.WORKLOADS["decode_b64_128k"]
+    log("workload decode_b64_128k: generating 2 x 4 GiB")
+    case = Case(w, seed=0)
+    # the oracle compresses only the sampled rows' keys
+    log("workload decode_b64_128k: running")
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    k_comp = torch.empty(w.batch, 2, w.kv_len // w.block_size, w.head_dim, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    q = case.q.view(w.batch, w.n_q_heads, w.head_dim)
+    out, sel, scores = qsa.decode(q, case.k, case.v, w.kv_len, w.block_size, w.top_k, k_comp, with_scores=True)
+    torch.cuda.synchronize()
+    sel_h = sel.cpu().numpy()
+    for b in range(w.batch):
+        for g in range(2):
+            planted = set(S.planted_blocks(w, 0, b, g).tolist())
+            assert planted <= set(sel_h[b, g].tolist()), (b, g)
+    sample = [(0, 0), (1, 1), (17, 0), (31, 1), (40, 0), (63, 1)]
+    sub_b = sorted({b for b, _ in sample})
+    # restrict the oracle's inputs to the sampled sequences
+    case.K, case.V, case.Q = case.K[sub_b], case.V[sub_b], case.Q[sub_b]
+    idx = {b: i for i, b in enumerate(sub_b)}
+    sub = Case.__new__(Case)
+    sub.__dict__.update(case.__dict__)
+    sub.w = w.replace(batch=len(sub_b))
+    sub._kc = None
+    sel_s = sel_h[sub_b][:, None]
+    out_s = from_device(out)[sub_b][:, None]
+    sc_s = scores.cpu().numpy()[sub_b][:, None]
+    st = check_rows(sub, sel_s, out_s, [(idx[b], 0, g) for b, g in sample], w.kv_len - 1, scores_gpu=sc_s)
+    log(f"  sampled rows: {st}")
