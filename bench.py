@@ -1,0 +1,337 @@
+"""QSA benchmark on one MI355X.
+
+``python bench.py [--workload NAME] [--steps K] [--warmup W] [--gpus 1]``
+
+A step is one pass of the whole QSA hot path over one batch of synthetic
+input, with every input already resident in HBM:
+
+* decode workloads: compress the key block completed by the new token (when
+  its position closes a block), score + select, sparse decode attention;
+  throughput is tokens (= sequences) per second;
+* prefill workloads: compress every block, score + select for every token,
+  sparse prefill attention; throughput is prompt tokens per second.
+
+The whole step is captured once in a HIP graph and the timed region replays
+it `steps` times (wall clock, synchronised on both sides). A second timed
+region replays each ABI call's own graph with HIP events recorded between the
+calls on the launch stream, giving per-call durations. The roofline entry is
+the call with the largest average duration, against the bound of its kernels
+(HBM bytes or bf16 MFMA flops, algorithmic counts only).
+
+The CPU baseline is the fp64 oracle, unmodified, timed on a bounded sample of
+the same workload on the host (single thread), scaled to the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA decode tokens/s + achieved HBM GB/s (% peak); prefill MFMA TFLOP/s (% peak)"
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2516.6         # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk
+DEFAULT_WORKLOAD = "decode_32k"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch the calls eagerly instead of replaying graphs")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------- algorithmic work
+
+def visible_keys(p: int, bs: int, k: int) -> int:
+    """Keys a query at position p attends to under the selection rule."""
+    return min(p + 1, (k - 1) * bs + (p % bs) + 1)
+
+
+def work_model(w, n_new_blocks: int):
+    """Algorithmic bytes / flops per ABI call of one step (nothing QSA skips is counted)."""
+    b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    el = 2 if w.dtype == "bf16" else 4
+    m = {}
+    if w.mode == "decode":
+        p = w.kv_len - 1
+        cand = p // bs
+        rows = b * hkv
+        m["compress"] = {"bytes": rows * n_new_blocks * (bs * d * el + d * 4), "flops": 0}
+        m["select"] = {"bytes": rows * cand * d * 4 + b * hq * d * el + rows * k * 4,
+                       "flops": 2 * d * rows * cand}
+        vis = visible_keys(p, bs, k)
+        m["attend"] = {"bytes": rows * vis * d * el * 2 + 2 * b * hq * d * el + rows * k * 4,
+                       "flops": 4 * d * hq * b * vis}
+    else:
+        T = w.kv_len
+        nb = T // bs
+        rows = b * hkv
+        m["compress"] = {"bytes": rows * nb * (bs * d * el + d * 4), "flops": 0}
+        cand_sum = sum(t // bs for t in range(T))
+        m["select"] = {"bytes": rows * nb * d * 4 + b * T * hq * d * el + b * T * hkv * k * 4,
+                       "flops": 2 * d * rows * cand_sum}
+        vis_sum = sum(visible_keys(t, bs, k) for t in range(T))
+        m["attend"] = {"bytes": 2 * b * T * hq * d * el + rows * T * d * el * 2 + b * T * hkv * k * 4,
+                       "flops": 4 * d * hq * b * vis_sum}
+    return m
+
+
+# ------------------------------------------------------------- GPU step
+
+class Step:
+    """The ABI calls of one step on resident device buffers."""
+
+    def __init__(self, w, seed):
+        import torch
+        import qsa_synth as S
+        import block_sparse_long_compress_amd as qsa
+
+        self.w, self.qsa, self.torch = w, qsa, torch
+        Qs, Ks, Vs = S.gen_all(w, seed)
+
+        def dev(x):
+            t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" else torch.from_numpy(x)
+            return t.cuda()
+
+        self.q, self.k, self.v = dev(Qs), dev(Ks), dev(Vs)
+        del Qs, Ks, Vs
+        b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+        cap = w.kv_len
+        self.shape = qsa.make_shape(b, hq, hkv, d, bs, k, self.q.dtype)
+        self.k_comp = torch.empty(b, hkv, cap // bs, d, dtype=torch.float32, device="cuda")
+        q_len, q_pos0 = w.q_len, w.q_pos0
+        self.sel = torch.empty(b, q_len, hkv, k, dtype=torch.int32, device="cuda")
+        self.out = torch.empty_like(self.q)
+        self.ws_sel = self._ws(qsa.QSA_OP_SELECT, q_len, w.kv_len)
+        if w.mode == "decode":
+            self.q_dec = self.q.view(b, hq, d)
+            self.out_dec = self.out.view(b, hq, d)
+            self.ws_att = self._ws(qsa.QSA_OP_DECODE, 1, w.kv_len)
+            # everything before the new token is already compressed
+            qsa.qsa_compress_keys(self.shape, self.k, w.kv_len - 1, self.k_comp)
+            self.blk_begin = (w.kv_len - 1) // bs
+            self.n_new_blocks = w.kv_len // bs - self.blk_begin
+        else:
+            self.ws_att = self._ws(qsa.QSA_OP_PREFILL, q_len, w.kv_len)
+            self.blk_begin = 0
+            self.n_new_blocks = w.kv_len // bs
+        torch.cuda.synchronize()
+        self.calls = [("select", self.select), ("attend", self.attend)]
+        if self.n_new_blocks > 0:
+            self.calls.insert(0, ("compress", self.compress))
+
+    def _ws(self, op, q_len, kv_len):
+        n = self.qsa.qsa_workspace_bytes(self.shape, op, q_len, kv_len)
+        return self.torch.empty(max(n, 16), dtype=self.torch.uint8, device="cuda")
+
+    def compress(self):
+        self.qsa.qsa_compress_keys(self.shape, self.k, self.w.kv_len, self.k_comp, block_begin=self.blk_begin)
+
+    def select(self):
+        w = self.w
+        self.qsa.qsa_score_select(self.shape, self.q, w.q_pos0, self.k_comp, w.kv_len, w.kv_len, self.sel,
+                                  ws=self.ws_sel)
+
+    def attend(self):
+        w = self.w
+        if w.mode == "decode":
+            self.qsa.qsa_sparse_attn_decode(self.shape, self.q_dec, self.k, self.v, w.kv_len, self.sel,
+                                            self.out_dec, ws=self.ws_att)
+        else:
+            self.qsa.qsa_sparse_attn_prefill(self.shape, self.q, self.k, self.v, 0, self.sel, self.out,
+                                             ws=self.ws_att)
+
+
+def run_gpu(w, steps, warmup, seed, use_graph):
+    """Timed region: `steps` replays of one graph holding a whole step (wall clock,
+    synchronised on both sides). Per-call durations: a second timed region in
+    which each call's own graph is replayed with HIP events between calls,
+    queued behind a short GPU sleep so that host submission never starves the
+    GPU between two calls."""
+    import torch
+
+    st = Step(w, seed)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _, fn in st.calls:
+            fn()  # eager warm-up before capture
+        torch.cuda.synchronize()
+        call_graphs = []
+        step_graph = None
+        if use_graph:
+            for name, fn in st.calls:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    fn()
+                call_graphs.append((name, g.replay))
+            step_graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(step_graph, stream=stream):
+                for _, fn in st.calls:
+                    fn()
+            run_step = step_graph.replay
+        else:
+            call_graphs = list(st.calls)
+
+            def run_step():
+                for _, fn in st.calls:
+                    fn()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            run_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run_step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+        # per-call durations (HIP events on the launch stream)
+        n_calls = len(call_graphs)
+        reps = max(10, min(steps, 200))
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2e7))  # ~10 ms of GPU time: lets the host queue every launch below
+        for r in range(reps):
+            ev = events[r]
+            ev[0].record(stream)
+            for i, (_, fn) in enumerate(call_graphs):
+                fn()
+                ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+    per_call = {}
+    for i, (name, _) in enumerate(call_graphs):
+        per_call[name] = 1e-3 * float(np.mean([events[r][i].elapsed_time(events[r][i + 1]) for r in range(reps)]))
+    return st, wall, per_call
+
+
+# ------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, seed, budget_s):
+    """fp64 oracle on a bounded sample of the same workload, single thread."""
+    from threadpoolctl import threadpool_limits
+
+    import qsa_synth as S
+    from oracle import qsa_oracle as O
+
+    with threadpool_limits(limits=1):
+        G, bs, k = w.group, w.block_size, w.top_k
+        scale = O.default_scale(w.head_dim)
+        if w.mode == "decode":
+            # one sequence: its keys compressed once beforehand (as on the GPU), then repeated steps
+            q = S.gen_q(w, seed, 0)
+            K = np.stack([S.gen_kv(w, seed, S.TENSOR_K, 0, g, q) for g in range(w.n_kv_heads)])
+            V = np.stack([S.gen_kv(w, seed, S.TENSOR_V, 0, g) for g in range(w.n_kv_heads)])
+            kc = O.compress_keys(K[:, : w.kv_len - 1], bs)
+            p = w.kv_len - 1
+            n_steps, t0 = 0, time.perf_counter()
+            while True:
+                blk = O.compress_keys(K[:, (p // bs) * bs:(p // bs + 1) * bs], bs) if (p + 1) % bs == 0 else None
+                for g in range(w.n_kv_heads):
+                    qg = q[0, g * G:(g + 1) * G].astype(np.float64)
+                    sc = O.block_scores(qg, kc[g], p // bs, scale)
+                    sel = O.select_blocks(sc, p // bs, k)
+                    O.attend_given_selection(qg, K[g], V[g], sel, p, bs, scale)
+                del blk
+                n_steps += 1
+                el = time.perf_counter() - t0
+                if el >= budget_s or n_steps >= 100000:
+                    break
+            return {"value": n_steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{n_steps} decode steps of one sequence (both KV heads: compress of the completed "
+                              f"block, scores over {p // bs} candidates, top-{k} selection, attention) in {el:.1f} s"}
+        # prefill: compress everything, then a uniform sample of query rows, scaled to the full prompt
+        Qs, Ks, Vs = S.gen_all(w, seed)
+        Q, K, V = (S.as_f32(x, w.dtype) for x in (Qs, Ks, Vs))
+        t0 = time.perf_counter()
+        kc = O.compress_keys(K, bs)
+        t_comp = time.perf_counter() - t0
+        rng = np.random.default_rng(seed)
+        order = rng.permutation(w.kv_len)
+        done, t1 = 0, time.perf_counter()
+        for t in order:
+            for g in range(w.n_kv_heads):
+                qg = Q[0, t, g * G:(g + 1) * G].astype(np.float64)
+                sc = O.block_scores(qg, kc[0, g], t // bs, scale)
+                sel = O.select_blocks(sc, t // bs, k)
+                O.attend_given_selection(qg, K[0, g], V[0, g], sel, t, bs, scale)
+            done += 1
+            if time.perf_counter() - t1 >= budget_s:
+                break
+        t_rows = time.perf_counter() - t1
+        est = t_comp + t_rows * w.kv_len / done
+        return {"value": w.batch * w.kv_len / est, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"compress of all {w.kv_len // bs} blocks ({t_comp:.2f} s) + {done} uniformly sampled "
+                          f"query tokens of {w.kv_len} ({t_rows:.1f} s), scaled to the whole prompt"}
+
+
+# ------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import qsa_synth as S
+
+    w = S.WORKLOADS[args.workload]
+    st, wall, per_call = run_gpu(w, args.steps, args.warmup, args.seed, not args.no_graph)
+    model = work_model(w, st.n_new_blocks)
+    ms_per_step = 1e3 * wall / args.steps
+    tokens = w.batch if w.mode == "decode" else w.batch * w.kv_len
+    value = tokens * args.steps / wall
+
+    dominant = max(per_call, key=lambda n: per_call[n])
+    dur = per_call[dominant]
+    if w.mode == "prefill" and dominant == "attend":
+        achieved, peak, unit, bound = model[dominant]["flops"] / dur / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = model[dominant]["bytes"] / dur / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    calls = {}
+    for n, t in per_call.items():
+        entry = {"us": round(t * 1e6, 3), "bytes": model[n]["bytes"], "GB/s": round(model[n]["bytes"] / t / 1e9, 1)}
+        if model[n]["flops"]:
+            entry["TFLOP/s"] = round(model[n]["flops"] / t / 1e12, 2)
+        calls[n] = entry
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "mode": w.mode, "batch": w.batch, "kv_len": w.kv_len,
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "top_k": w.top_k, "seed": args.seed,
+                   "graphs": not args.no_graph},
+        "roofline": {"bound": bound, "kernel": f"{dominant} call", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": None},
+        "calls": calls,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
+        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 3)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -212,28 +212,29 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
   }
 }
 
+// Merge the slices' partial softmax states of one (row, query head), one
+// output dim per thread, slices in order.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                             int hq, int hkv, int G, int n_split) {
-  const int64_t row = blockIdx.x;
+__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                           int hq, int hkv, int G, int n_split) {
+  const int64_t row = blockIdx.x / G;
+  const int h = blockIdx.x % G;
+  const int e = threadIdx.x;
   const int64_t b = row / hkv;
   const int g = (int)(row % hkv);
   const int64_t stride = 2 * G + G * D;
   const float* pr = part + row * n_split * stride;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, e = idx % D;
-    float M = -__builtin_inff();
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pr[s * stride + h]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float ms = pr[s * stride + h];
-      if (ms == -__builtin_inff()) continue;
-      const float f = __builtin_amdgcn_exp2f(ms - M);
-      L += f * pr[s * stride + G + h];
-      O += f * pr[s * stride + 2 * G + h * D + e];
-    }
-    out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
+  float M = -__builtin_inff();
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pr[s * stride + h]);
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const float ms = pr[s * stride + h];
+    if (ms == -__builtin_inff()) continue;
+    const float f = __builtin_amdgcn_exp2f(ms - M);
+    L += f * pr[s * stride + G + h];
+    O += f * pr[s * stride + 2 * G + h * D + e];
   }
+  out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
 }
 
 template <int D>
@@ -248,7 +249,7 @@ hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const 
                      plan.n_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_split == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)rows), dim3(256), 0, st,
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(rows * s.group)), dim3(D), 0, st,
                      static_cast<const float*>(ws), static_cast<uint16_t*>(out), s.hq, s.hkv, s.group, plan.n_split);
   return hipGetLastError();
 }

@@ -13,6 +13,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+// Keeps a value in a VGPR at this point: stops the optimiser from fusing
+// lane-dependent selects across steps of a butterfly into index chains.
+__device__ __forceinline__ void reg_fence(float& v) { asm volatile("" : "+v"(v)); }
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
@@ -88,6 +92,39 @@ __device__ __forceinline__ float key_score(uint64_t key) {
   return __uint_as_float(u);
 }
 
+// Lane exchange with lane ^ j for a compile-time j (after unrolling).
+// xor 1, 2: DPP quad permutes; xor 4: two DPP row rotations (row_ror:N
+// moves lane i to lane i+N within its row of 16); xor 8: DPP row_ror:8;
+// xor 16: ds_swizzle in bit-mask mode; xor 32: ds_bpermute.
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int j) {
+  const int x = (int)v;
+  switch (j) {
+    case 1:
+      return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+    case 2:
+      return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const int up = __builtin_amdgcn_mov_dpp(x, 0x12C, 0xF, 0xF, false);    // lane i <- i+4
+      const int down = __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false);  // lane i <- i-4
+      return (uint32_t)((lane_id() & 4) ? down : up);
+    }
+    case 8:
+      return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);
+    case 16:
+      return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);
+    default:
+      return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ j) << 2, x);
+  }
+}
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v, int j) {
+  const uint32_t lo = xor_lane_u32((uint32_t)v, j);
+  const uint32_t hi = xor_lane_u32((uint32_t)(v >> 32), j);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float xor_lane_f32(float v, int j) {
+  return __uint_as_float(xor_lane_u32(__float_as_uint(v), j));
+}
+
 // Bitonic sort of one key per lane across the wave, descending (lane 0 = largest).
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
   const int lane = lane_id();
@@ -95,7 +132,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
   for (int k = 2; k <= kWave; k <<= 1) {
 #pragma unroll
     for (int j = k >> 1; j > 0; j >>= 1) {
-      uint64_t y = shfl_xor_u64(x, j);
+      uint64_t y = xor_lane_u64(x, j);
       bool lower = (lane & j) == 0;
       bool desc = (lane & k) == 0;
       bool take_max = (lower == desc);
@@ -112,20 +149,34 @@ __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t cur, uint64_t fresh
   uint64_t x = cur > rev ? cur : rev;  // bitonic sequence holding the top 64
 #pragma unroll
   for (int j = kWave / 2; j > 0; j >>= 1) {
-    uint64_t y = shfl_xor_u64(x, j);
+    uint64_t y = xor_lane_u64(x, j);
     bool lower = (lane & j) == 0;
     x = lower ? (x > y ? x : y) : (x < y ? x : y);
   }
   return x;
 }
 
+// Value of `v` in lane `src` (wave-uniform src), via the scalar unit.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Fold one lane-per-candidate batch into a running descending top list
 // (`cur`, lane j = j-th best). Only the first `m` entries of `cur` matter;
 // the batch is skipped when no key beats the current m-th best.
 __device__ __forceinline__ uint64_t topk_fold(uint64_t cur, uint64_t fresh, int m) {
-  uint64_t thr = shfl_u64(cur, m - 1);
+  const uint64_t thr = readlane_u64(cur, m - 1);
   if (__ballot(fresh > thr) == 0) return cur;
   return wave_merge_desc(cur, wave_sort_desc(fresh));
+}
+
+// Same for a batch that is already a descending list.
+__device__ __forceinline__ uint64_t topk_fold_sorted(uint64_t cur, uint64_t fresh_desc, int m) {
+  const uint64_t thr = readlane_u64(cur, m - 1);
+  if (readlane_u64(fresh_desc, 0) <= thr) return cur;
+  return wave_merge_desc(cur, fresh_desc);
 }
 
 // ---------------------------------------------------------------- MFMA

@@ -46,6 +46,21 @@ __device__ void finalize_row(uint64_t cur, int slots, int own, int top_k, int32_
   }
 }
 
+// Merge the descending lists of the 4 waves of a workgroup (lists[w][lane]
+// holds wave w's list); wave 0 returns the merged list, other waves return 0.
+__device__ uint64_t merge_wave_lists(uint64_t (*lists)[kWave], uint64_t cur, int m) {
+  const int lane = lane_id(), w = wave_id();
+  lists[w][lane] = cur;
+  __syncthreads();
+  if (w == 0 || w == 2) {
+    cur = topk_fold_sorted(cur, lists[w + 1][lane], m);
+    lists[w][lane] = cur;
+  }
+  __syncthreads();
+  if (w == 0) cur = topk_fold_sorted(cur, lists[2][lane], m);
+  return cur;
+}
+
 // ------------------------------------------------------------------ tile path
 
 constexpr int kTileRows = 16;
@@ -130,36 +145,63 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
 
 // ------------------------------------------------------------------ split path
 
-// Dot products of 64 consecutive compressed keys with qbar. Lane l reads the
-// 16-byte column slice (l % LPR) of rows (l / LPR) + RPL*j; after the
-// butterfly lane l holds the full dot product of row RPL*(l % LPR) + l / LPR.
+// Dot products of 64 consecutive compressed keys with qbar, one per lane.
+// Lane l reads the 16-byte column slice (l % LPR) of its rows, so every load
+// instruction covers 1 KiB of consecutive keys. A pass issues 16 loads; a
+// transpose-reduce butterfly over lane bits 3..0 leaves each lane one row of
+// the pass summed over 16 lanes, and plain xor-reductions over the remaining
+// lane bits of the row finish the sum. Row held by lane l: see dot64_row().
 template <int D>
-__device__ __forceinline__ float dot64_rows(const float* __restrict__ rows_base, int64_t n_valid, const f32x4_t& qv) {
+__device__ __forceinline__ int dot64_row(int lane) {
   constexpr int LPR = D / 4;
   constexpr int RPL = kWave / LPR;
-  constexpr int N = LPR;  // loads per lane = values per lane before the butterfly
+  constexpr int ROWS_PASS = 16 * RPL;
+  const int pass = (kWave / ROWS_PASS == 2) ? ((lane >> 4) & 1) : 0;
+  return pass * ROWS_PASS + RPL * (lane % 16) + lane / LPR;
+}
+
+template <int D>
+__device__ __forceinline__ float dot64_rows(const float* __restrict__ rows_base, int64_t n_valid, const f32x4_t& qv) {
+  constexpr int LPR = D / 4;               // lanes covering one key row
+  constexpr int RPL = kWave / LPR;         // rows per load instruction
+  constexpr int ROWS_PASS = 16 * RPL;      // rows per pass of 16 loads
+  constexpr int PASSES = kWave / ROWS_PASS;
   const int lane = lane_id();
-  float vals[N];
-  f32x4_t raw[N];
+  float res[PASSES];
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
-    const int row = RPL * j + lane / LPR;
-    raw[j] = row < n_valid ? *reinterpret_cast<const f32x4_t*>(rows_base + (int64_t)row * D + 4 * (lane % LPR))
-                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int pass = 0; pass < PASSES; ++pass) {
+    f32x4_t raw[16];
 #pragma unroll
-  for (int j = 0; j < N; ++j) vals[j] = raw[j][0] * qv[0] + raw[j][1] * qv[1] + raw[j][2] * qv[2] + raw[j][3] * qv[3];
-#pragma unroll
-  for (int half = N / 2; half >= 1; half /= 2) {
-    const bool upper = (lane & half) != 0;
-#pragma unroll
-    for (int v = 0; v < half; ++v) {
-      const float send = upper ? vals[v] : vals[v + half];
-      const float keep = upper ? vals[v + half] : vals[v];
-      vals[v] = keep + shfl_xor_f32(send, half);
+    for (int j = 0; j < 16; ++j) {
+      const int row = pass * ROWS_PASS + RPL * j + lane / LPR;
+      raw[j] = row < n_valid ? *reinterpret_cast<const f32x4_t*>(rows_base + (int64_t)row * D + 4 * (lane % LPR))
+                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    float vals[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      vals[j] = raw[j][0] * qv[0] + raw[j][1] * qv[1] + raw[j][2] * qv[2] + raw[j][3] * qv[3];
+    }
+#pragma unroll
+    for (int half = 8; half >= 1; half /= 2) {
+      const bool upper = (lane & half) != 0;
+#pragma unroll
+      for (int v = 0; v < half; ++v) {
+        float lo = vals[v], hi = vals[v + half];
+        reg_fence(lo);  // opaque operands: keeps the selects from becoming indexed array reads
+        reg_fence(hi);
+        const float send = upper ? lo : hi;
+        const float keep = upper ? hi : lo;
+        vals[v] = keep + xor_lane_f32(send, half);
+      }
+    }
+#pragma unroll
+    for (int m = 16; m < LPR; m <<= 1) vals[0] += xor_lane_f32(vals[0], m);
+    res[pass] = vals[0];
+    reg_fence(res[pass]);
   }
-  return vals[0];
+  if constexpr (PASSES == 2) return ((lane >> 4) & 1) ? res[1] : res[0];
+  return res[0];
 }
 
 template <typename T, int D>
@@ -169,7 +211,6 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
                                                            int64_t nb_cap, int hq, int hkv, int G, int bs, int top_k,
                                                            float scale, int chunk, int64_t n_chunks) {
   constexpr int LPR = D / 4;
-  constexpr int RPL = kWave / LPR;
   __shared__ float qbar[D];
   __shared__ uint64_t lists[4][kWave];
 
@@ -204,19 +245,12 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   uint64_t cur = 0ull;
   for (int64_t base = c_begin + (int64_t)kWave * w; base < c_end; base += 4 * kWave) {
     const float s = dot64_rows<D>(kc_src + base * D, c_end - base, qv);
-    const int64_t cand = base + RPL * (lane % LPR) + lane / LPR;
+    const int64_t cand = base + dot64_row<D>(lane);
     const uint64_t key = cand < c_end ? make_key(s * scale, (int)cand) : 0ull;
     cur = topk_fold(cur, key, slots);
   }
-  lists[w][lane] = cur;
-  __syncthreads();
+  cur = merge_wave_lists(lists, cur, slots);
   if (w != 0) return;
-#pragma unroll
-  for (int o = 1; o < 4; ++o) {
-    const uint64_t other = lists[o][lane];
-    const uint64_t thr = shfl_u64(cur, slots - 1);
-    if (__ballot(other > thr) != 0) cur = wave_merge_desc(cur, other);
-  }
   if (n_chunks == 1) {
     const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
     finalize_row(cur, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
@@ -225,13 +259,21 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   }
 }
 
-// One workgroup per row: reduce the row's chunk lists to the final top list.
+// One workgroup per row: reduce the row's chunk lists (each descending) to
+// the final top list. The slots-th largest of the chunk maxima is a key that
+// at least `slots` real keys reach, so every key below it can be dropped:
+// only a short prefix of each list survives (on noise-like scores a few keys
+// beyond `slots` in total). Survivors are folded in groups of 64.
+constexpr int kMergeCap = 2048;  // survivors kept in LDS; more go straight from memory
+
 __global__ __launch_bounds__(256) void select_merge_kernel(int32_t* __restrict__ sel, float* __restrict__ sel_scores,
                                                            const uint64_t* __restrict__ ws, int64_t q_len,
                                                            int64_t q_pos0, int hkv, int bs, int top_k,
                                                            int64_t n_chunks) {
   __shared__ uint64_t lists[4][kWave];
-  __shared__ uint64_t red[4];
+  __shared__ uint64_t surv[kMergeCap];
+  __shared__ uint64_t bound_s;
+  __shared__ int n_surv;
   const int64_t row = blockIdx.x;
   const int64_t b = row / (q_len * hkv);
   const int64_t t = (row / hkv) % q_len;
@@ -243,39 +285,48 @@ __global__ __launch_bounds__(256) void select_merge_kernel(int32_t* __restrict__
   const int sm = top_k - 1;
   const uint64_t* lst = ws + row * n_chunks * sm;
 
-  // Lower bound of the row cutoff: the best chunk-local slots-th key.
-  uint64_t bound = 0ull;
+  // bound = slots-th largest chunk maximum (0 when there are fewer chunks)
+  if (w == 0) {
+    uint64_t cur = 0ull;
+    for (int64_t base = 0; base < n_chunks; base += kWave) {
+      const uint64_t x = base + lane < n_chunks ? lst[(base + lane) * sm] : 0ull;
+      cur = topk_fold(cur, x, slots);
+    }
+    if (lane == 0) {
+      bound_s = n_chunks >= slots ? readlane_u64(cur, slots - 1) : 0ull;
+      n_surv = 0;
+    }
+  }
+  __syncthreads();
+  const uint64_t bound = bound_s;
+  // survivors: the prefix of each list at or above the bound
   for (int64_t c = tid; c < n_chunks; c += 256) {
-    const uint64_t x = lst[c * sm + slots - 1];
-    bound = x > bound ? x : bound;
+    for (int j = 0; j < slots; ++j) {
+      const uint64_t x = lst[c * sm + j];
+      if (x < bound) break;
+      const int at = atomicAdd(&n_surv, 1);
+      if (at < kMergeCap) surv[at] = x;
+    }
   }
-  for (int m = 32; m > 0; m >>= 1) {
-    const uint64_t y = shfl_xor_u64(bound, m);
-    bound = y > bound ? y : bound;
-  }
-  if (lane == 0) red[w] = bound;
   __syncthreads();
-  bound = red[0];
-  for (int o = 1; o < 4; ++o) bound = red[o] > bound ? red[o] : bound;
-
+  const int total = n_surv;
   uint64_t cur = 0ull;
-  const int64_t n_keys = n_chunks * sm;
-  for (int64_t base = (int64_t)kWave * w; base < n_keys; base += 4 * kWave) {
-    const int64_t idx = base + lane;
-    uint64_t key = 0ull;
-    if (idx < n_keys && (int)(idx % sm) < slots) key = lst[idx];
-    key = key >= bound ? key : 0ull;
-    cur = topk_fold(cur, key, slots);
+  if (total <= kMergeCap) {
+    for (int base = kWave * w; base < total; base += 4 * kWave) {
+      const uint64_t x = base + lane < total ? surv[base + lane] : 0ull;
+      cur = topk_fold(cur, x, slots);
+    }
+  } else {  // adversarial inputs: fold every key at or above the bound from memory
+    const int64_t n_keys = n_chunks * sm;
+    for (int64_t base = (int64_t)kWave * w; base < n_keys; base += 4 * kWave) {
+      const int64_t idx = base + lane;
+      uint64_t key = 0ull;
+      if (idx < n_keys && (int)(idx % sm) < slots) key = lst[idx];
+      cur = topk_fold(cur, key >= bound ? key : 0ull, slots);
+    }
   }
-  lists[w][lane] = cur;
-  __syncthreads();
+  cur = merge_wave_lists(lists, cur, slots);
   if (w != 0) return;
-#pragma unroll
-  for (int o = 1; o < 4; ++o) {
-    const uint64_t other = lists[o][lane];
-    const uint64_t thr = shfl_u64(cur, slots - 1);
-    if (__ballot(other > thr) != 0) cur = wave_merge_desc(cur, other);
-  }
   const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
   finalize_row(cur, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
 }
@@ -314,13 +365,19 @@ SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
   p.chunk = 256;
   p.n_chunks = 1;
   p.ws_bytes = 0;
-  if (p.tiled) return p;
+  if (p.tiled || max_cand <= 0) return p;
   const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
-  // Aim for >= 1024 workgroups over the GPU while keeping >= 64 keys per wave step.
-  int chunk = 1024;
-  while (chunk > 64 && rows * ((max_cand + chunk - 1) / chunk) < 1024) chunk /= 2;
-  p.chunk = chunk;
-  p.n_chunks = max_cand > 0 ? (max_cand + chunk - 1) / chunk : 1;
+  if (rows * max_cand <= 8192 && max_cand <= 2048) {
+    // small problem: one workgroup per row, no merge launch
+    p.chunk = (int)((max_cand + 255) / 256 * 256);
+  } else {
+    // 4 waves x 64 keys x u per workgroup; the largest u that still spreads
+    // the scan over >= 512 workgroups (two per CU)
+    int u = 8;
+    while (u > 1 && rows * ((max_cand + 256 * u - 1) / (256 * u)) < 512) u /= 2;
+    p.chunk = 256 * u;
+  }
+  p.n_chunks = (max_cand + p.chunk - 1) / p.chunk;
   if (p.n_chunks > 1) p.ws_bytes = (size_t)rows * p.n_chunks * (s.top_k - 1) * sizeof(uint64_t);
   return p;
 }
