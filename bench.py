@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the calls eagerly instead of replaying graphs")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (reference for memory counters)")
     return ap.parse_args()
 
 
@@ -327,6 +329,16 @@ def main():
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": None},
         "calls": calls,
     }
+    if args.copy_calibration_mib > 0:
+        import torch
+
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.seed, args.cpu_seconds)
         line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 3)
