@@ -158,6 +158,15 @@ class Step:
                                              ws=self.ws_att)
 
 
+def capture_step(torch, st, stream):
+    """Enqueue one step: the ABI calls in order on the launch stream. (A decode
+    step's compression could run beside select + attend, since the block it
+    closes is the token's own block and never one of its candidates; a
+    forked graph branch costs more than the few microseconds it would hide.)"""
+    for _, fn in st.calls:
+        fn()
+
+
 def run_gpu(w, steps, warmup, seed, use_graph):
     """Timed region: `steps` replays of one graph holding a whole step (wall clock,
     synchronised on both sides). Per-call durations: a second timed region in
@@ -182,15 +191,13 @@ def run_gpu(w, steps, warmup, seed, use_graph):
                 call_graphs.append((name, g.replay))
             step_graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(step_graph, stream=stream):
-                for _, fn in st.calls:
-                    fn()
+                capture_step(torch, st, stream)
             run_step = step_graph.replay
         else:
             call_graphs = list(st.calls)
 
             def run_step():
-                for _, fn in st.calls:
-                    fn()
+                capture_step(torch, st, stream)
         torch.cuda.synchronize()
         for _ in range(warmup):
             run_step()

@@ -130,8 +130,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
         x[st][i] = ok ? sacc[st][i] * scale_log2 : -__builtin_inff();
         mloc = fmaxf(mloc, x[st][i]);
       }
-    mloc = fmaxf(mloc, shfl_xor_f32(mloc, 16));
-    mloc = fmaxf(mloc, shfl_xor_f32(mloc, 32));
+    mloc = max_col4(mloc);
     const float m_new = fmaxf(m_run, mloc);  // finite: key0 <= p is visible
     if (__ballot(m_new > m_run) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -171,8 +170,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  l_run += shfl_xor_f32(l_run, 16);
-  l_run += shfl_xor_f32(l_run, 32);
+  l_run = sum_col4(l_run);
   __syncthreads();  // staging area becomes the combine area
   float* cm = reinterpret_cast<float*>(smem);  // [4][16] running maxima
   float* cl = cm + 4 * 16;                     // [4][16] sums
@@ -224,15 +222,34 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   const int g = (int)(row % hkv);
   const int64_t stride = 2 * G + G * D;
   const float* pr = part + row * n_split * stride;
-  float M = -__builtin_inff();
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pr[s * stride + h]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float ms = pr[s * stride + h];
-    if (ms == -__builtin_inff()) continue;
-    const float f = __builtin_amdgcn_exp2f(ms - M);
-    L += f * pr[s * stride + G + h];
-    O += f * pr[s * stride + 2 * G + h * D + e];
+  // Slices in batches of 8 whose loads all go out at once (one memory round
+  // trip per batch), folded in slice order into a running state.
+  constexpr int kBatch = 8;
+  float M = -__builtin_inff(), L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+    float ms[kBatch], ls[kBatch], os[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const bool ok = s0 + j < n_split;
+      const float* ps = pr + (int64_t)(s0 + j) * stride;
+      ms[j] = ok ? ps[h] : -__builtin_inff();
+      ls[j] = ok ? ps[G + h] : 0.f;
+      os[j] = ok ? ps[2 * G + h * D + e] : 0.f;
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, ms[j]);
+    if (mb == -__builtin_inff()) continue;  // no visible key so far
+    const float a = __builtin_amdgcn_exp2f(M - mb);  // 0 while M = -inf
+    L *= a;
+    O *= a;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float f = __builtin_amdgcn_exp2f(ms[j] - mb);  // 0 for empty slices
+      L += f * ls[j];
+      O += f * os[j];
+    }
+    M = mb;
   }
   out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
 }

@@ -289,20 +289,37 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   }
   wait_vmcnt<0>();  // Q is in registers before the DMA queue starts counting
 
-  for (int ui = 0; ui < stages - 1 && ui < n_union; ++ui) issue(ui, ui);
   const int wave_shift = w * NCG * tpc;
   const unsigned long long cg_mask = (1ull << tpc) - 1ull;
 
-  for (int ui = 0; ui < n_union; ++ui) {
-    const int slot = ui % stages;
-    int ahead = n_union - 1 - ui;
-    ahead = ahead < stages - 2 ? ahead : stages - 2;
-    if (ahead >= 2) wait_vmcnt<2 * ST::kPerWave>();
-    else if (ahead == 1) wait_vmcnt<ST::kPerWave>();
-    else wait_vmcnt<0>();
-    stage_barrier();  // every wave is past block ui-1: its stage may be refilled
-    if (ui + stages - 1 < n_union) issue(ui + stages - 1, (ui + stages - 1) % stages);
+  // Consume the union in groups of `per_it` blocks per barrier (2 when four
+  // stages fit: the next group's copies run during the current group's math),
+  // which also averages the per-wave work of the group before the barrier.
+  const int per_it = stages >= 4 ? 2 : 1;
+  const int ring = per_it == 2 ? 4 : stages;
+  if (per_it == 2) {
+    for (int ui = 0; ui < 2 && ui < n_union; ++ui) issue(ui, ui);
+  } else {
+    for (int ui = 0; ui < stages - 1 && ui < n_union; ++ui) issue(ui, ui);
+  }
 
+  for (int u0 = 0; u0 < n_union; u0 += per_it) {
+    if (per_it == 2) {
+      wait_vmcnt<0>();
+      stage_barrier();  // every wave is past the previous group: its stages may be refilled
+      for (int a = 2; a < 4; ++a)
+        if (u0 + a < n_union) issue(u0 + a, (u0 + a) % ring);
+    } else {
+      int ahead = n_union - 1 - u0;
+      ahead = ahead < stages - 2 ? ahead : stages - 2;
+      if (ahead >= 2) wait_vmcnt<2 * ST::kPerWave>();
+      else if (ahead == 1) wait_vmcnt<ST::kPerWave>();
+      else wait_vmcnt<0>();
+      stage_barrier();
+      if (u0 + stages - 1 < n_union) issue(u0 + stages - 1, (u0 + stages - 1) % stages);
+    }
+    for (int ui = u0; ui < u0 + per_it && ui < n_union; ++ui) {
+    const int slot = ui % ring;
     const int64_t c = ulist[ui];
     const unsigned long long tm = tokmask[ui] >> wave_shift;
     unsigned need = 0u;
@@ -315,11 +332,12 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
     }
     if (need == 0u) continue;
     const bool diag = (c + 1) * BS > pos_first;  // own block of some token of the tile: causal mask
+    const int key_base = (int)(c * BS);          // positions fit in int32 (checked on the host)
     const unsigned char* kb = smem + slot * ST::kBytes;
     const unsigned char* vb = kb + ST::kKFrags * 1024;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      const int64_t key0 = c * BS + ch * CH;
+      const int key0 = key_base + ch * CH;
       u32x4_t kf[SUB][KS];
 #pragma unroll
       for (int su = 0; su < SUB; ++su)
@@ -344,15 +362,15 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
           for (int su = 0; su < SUB; ++su)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int64_t pos = key0 + 16 * su + 4 * lg + i;
+              const int pos = key0 + 16 * su + 4 * lg + i;
               x[su * 4 + i] = pos <= pos_q[n] ? x[su * 4 + i] : -__builtin_inff();
             }
         }
         float mx = x[0];
 #pragma unroll
-        for (int i = 1; i < SUB * 4; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, xor_lane_f32(mx, 16));
-        mx = fmaxf(mx, xor_lane_f32(mx, 32));
+        for (int i = 1; i + 1 < SUB * 4; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(x[i], x[i + 1]));
+        if constexpr ((SUB * 4) % 2 == 0) mx = __builtin_fmaxf(mx, x[SUB * 4 - 1]);
+        mx = max_col4(mx);
         // The exponent offset m_run is raised only when a score exceeds it by
         // more than 2^8: p stays <= 256 (exact in fp32, representable in
         // bf16) and the accumulators are rescaled rarely.
@@ -394,13 +412,12 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
           }
         }
     }
+    }
   }
 
 #pragma unroll
   for (int n = 0; n < NCG; ++n) {
-    float l = l_run[n];
-    l += xor_lane_f32(l, 16);
-    l += xor_lane_f32(l, 32);
+    const float l = sum_col4(l_run[n]);
     if (!row_ok[n]) continue;
     const float inv = 1.0f / l;
     const int r = (w * NCG + n) * tpc + tau;
@@ -479,8 +496,9 @@ hipError_t launch_bs(const Dims& s, int64_t q_len, int64_t q_pos0, int64_t kv_ca
       return launch_kernel<D, BS, 4, 2>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
     case 4:
       return launch_kernel<D, BS, 8, 2>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
-    default:
-      return launch_kernel<D, BS, 8, 4>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
+    default:  // 8 CGs (d = 64 only)
+      if constexpr (D == 64) return launch_kernel<D, BS, 8, 4>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
+      else return launch_kernel<D, BS, 8, 2>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
   }
 }
 

@@ -92,10 +92,36 @@ __device__ __forceinline__ float key_score(uint64_t key) {
   return __uint_as_float(u);
 }
 
+// v_permlane16_swap / v_permlane32_swap with both operands = v: element 0
+// holds v of the lower half of each 32-lane (resp. 64-lane) group in both
+// halves, element 1 the upper half. So lane l sees v[l & ~16] and v[l | 16]
+// (resp. v[l & ~32] and v[l | 32]) in one VALU instruction.
+__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (lane_id() & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (lane_id() & 32) ? r[0] : r[1];
+}
+// max / sum over the four lanes {l, l^16, l^32, l^48} (one MFMA output column).
+__device__ __forceinline__ float max_col4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_col4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Lane exchange with lane ^ j for a compile-time j (after unrolling).
 // xor 1, 2: DPP quad permutes; xor 4: two DPP row rotations (row_ror:N
 // moves lane i to lane i+N within its row of 16); xor 8: DPP row_ror:8;
-// xor 16: ds_swizzle in bit-mask mode; xor 32: ds_bpermute.
+// xor 16, 32: permlane swaps.
 __device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int j) {
   const int x = (int)v;
   switch (j) {
@@ -111,7 +137,9 @@ __device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int j) {
     case 8:
       return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);
     case 16:
-      return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);
+      return xor16_u32(v);
+    case 32:
+      return xor32_u32(v);
     default:
       return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ j) << 2, x);
   }

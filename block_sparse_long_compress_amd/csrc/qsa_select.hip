@@ -211,7 +211,6 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
                                                            int64_t nb_cap, int hq, int hkv, int G, int bs, int top_k,
                                                            float scale, int chunk, int64_t n_chunks) {
   constexpr int LPR = D / 4;
-  __shared__ float qbar[D];
   __shared__ uint64_t lists[4][kWave];
 
   const int64_t row = blockIdx.x / n_chunks;
@@ -230,14 +229,15 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
     }
     return;
   }
-  for (int e = tid; e < D; e += 256) {
-    const T* src = q + ((b * q_len + t) * hq + (int64_t)g * G) * D + e;
-    float v = 0.f;
-    for (int j = 0; j < G; ++j) v += Elem<T>::load(src, (int64_t)j * D);
-    qbar[e] = v;
+  // Each lane sums its own 4 dims of the group's queries: no barrier, so the
+  // first compressed-key loads go out together with the query loads.
+  f32x4_t qv = {0.f, 0.f, 0.f, 0.f};
+  {
+    const T* src = q + ((b * q_len + t) * hq + (int64_t)g * G) * D + 4 * (lane % LPR);
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] += Elem<T>::load(src, (int64_t)j * D + i);
   }
-  __syncthreads();
-  const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(&qbar[4 * (lane % LPR)]);
 
   const int64_t c_begin = ch * chunk;
   const int64_t c_end = c_begin + chunk < own ? c_begin + chunk : own;

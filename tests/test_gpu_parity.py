@@ -157,3 +157,41 @@ def test_incremental_compress_matches_full():
             qsa.qsa_compress_keys(shape, case.k, n, inc, block_begin=n // w.block_size - 1)
     torch.cuda.synchronize()
     assert torch.equal(full, inc)
+
+
+def test_workspace_reuse_across_decode_steps():
+    """One select and one decode workspace, filled with garbage once, serve a
+    run of decode steps (split selection and split attention): every step
+    equals a call with fresh workspaces."""
+    w = W(mode="decode", batch=4, kv_len=40033, block_size=32, top_k=16)
+    case = Case(w, seed=8)
+    b, hq, d = w.batch, w.n_q_heads, w.head_dim
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    k_comp = torch.zeros(b, w.n_kv_heads, w.kv_len // w.block_size, d, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    q_sel = case.q.view(b, 1, hq, d)
+    q_dec = case.q.view(b, hq, d)
+    steps = [40000, 40031, 40032, 40033, 39000]
+    n_sel = max(qsa.qsa_workspace_bytes(shape, qsa.QSA_OP_SELECT, 1, n) for n in steps)
+    n_dec = max(qsa.qsa_workspace_bytes(shape, qsa.QSA_OP_DECODE, 1, n) for n in steps)
+    assert n_sel > 0 and n_dec > 0, "both calls must take their split paths"
+    ws_sel = torch.full((n_sel,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws_dec = torch.full((n_dec,), 0x5A, dtype=torch.uint8, device="cuda")
+    for n in steps:
+        log(f"workspace reuse step kv_len={n}")
+        outs = []
+        for wss, wsd in ((ws_sel, ws_dec), (None, None)):
+            sel = torch.empty(b, 1, w.n_kv_heads, w.top_k, dtype=torch.int32, device="cuda")
+            out = torch.empty(b, hq, d, dtype=case.q.dtype, device="cuda")
+            qsa.qsa_score_select(shape, q_sel, n - 1, k_comp, n, w.kv_len, sel, ws=wss)
+            qsa.qsa_sparse_attn_decode(shape, q_dec, case.k, case.v, n, sel.view(b, w.n_kv_heads, w.top_k), out,
+                                       ws=wsd)
+            outs.append((sel, out))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0], outs[1][0])
+        assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    # the last step against the oracle (rows at position n - 1 read only
+    # blocks and keys below n)
+    rows = [(bb, 0, g) for bb in range(b) for g in range(w.n_kv_heads)]
+    st = check_rows(case, outs[0][0].cpu().numpy(), from_device(outs[0][1])[:, None], rows, steps[-1] - 1)
+    log(f"  {st}")
