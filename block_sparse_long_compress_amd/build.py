@@ -38,7 +38,7 @@ def hipcc() -> str:
 
 def compile_flags() -> list[str]:
     return [
-        "-x", "hip", "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
+        "-x", "hip", "-std=c++20", "-O3", "-fPIC", f"--offload-arch={ARCH}",
         # packed fp32 VALU ops stay off: plain scalar/float2 code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function", "-Wno-unused-variable",

@@ -79,38 +79,52 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   unsigned char* vs = smem + w * kUnit * RS;
 
-  for (int idx = w; idx < n_units; idx += 4) {
-    const int c = sel_row[e0 + idx / upb];
-    if (c < 0) continue;
-    const int64_t key0 = (int64_t)c * bs + (int64_t)(idx % upb) * kUnit;
-    if (key0 > p) continue;
-    const uint16_t* kb = k + (kv_off + key0) * D;
-    const uint16_t* vb = v + (kv_off + key0) * D;
+  // The slice's block ids, one per lane (bpw <= 64), loaded with Q.
+  const int sel_mine = lane < e1 - e0 ? sel_row[e0 + lane] : -1;
 
+  // A wave's units are idx = w, w + 4, ...
+  constexpr int VCH = kUnit * D / 8 / kWave;  // 16-byte V chunks per lane
+  struct Unit {
     u32x4_t kf[2][KS];
+    u32x4_t vr[VCH];
+    int64_t key0;
+    bool ok;
+  };
+  auto fetch = [&](int idx, Unit& u) {
+    u.ok = false;
+    if (idx >= n_units) return;
+    const int c = __builtin_amdgcn_readlane(sel_mine, idx / upb);
+    if (c < 0) return;
+    u.key0 = (int64_t)c * bs + (int64_t)(idx % upb) * kUnit;
+    if (u.key0 > p) return;
+    u.ok = true;
+    const uint16_t* kb = k + (kv_off + u.key0) * D;
+    const uint16_t* vb = v + (kv_off + u.key0) * D;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int kr = 16 * st + col;
-      const bool ok = key0 + kr <= p;
+      const bool ok = u.key0 + kr <= p;
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        kf[st][s] = ok ? *reinterpret_cast<const u32x4_t*>(kb + (int64_t)kr * D + 32 * s + 8 * lg)
-                       : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    constexpr int VCH = kUnit * D / 8 / kWave;  // 16-byte V chunks per lane
-    u32x4_t vr[VCH];
-#pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int ci = lane + kWave * j;
-      const int r = ci / (D / 8), c8 = ci % (D / 8);
-      vr[j] = key0 + r <= p ? *reinterpret_cast<const u32x4_t*>(vb + (int64_t)r * D + 8 * c8)
-                            : u32x4_t{0u, 0u, 0u, 0u};
+        u.kf[st][s] = ok ? *reinterpret_cast<const u32x4_t*>(kb + (int64_t)kr * D + 32 * s + 8 * lg)
+                         : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < VCH; ++j) {
       const int ci = lane + kWave * j;
       const int r = ci / (D / 8), c8 = ci % (D / 8);
-      *reinterpret_cast<u32x4_t*>(vs + r * RS + 16 * c8) = vr[j];
+      u.vr[j] = u.key0 + r <= p ? *reinterpret_cast<const u32x4_t*>(vb + (int64_t)r * D + 8 * c8)
+                                : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto consume = [&](const Unit& u) {
+    if (!u.ok) return;
+    const int64_t key0 = u.key0;
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      const int ci = lane + kWave * j;
+      const int r = ci / (D / 8), c8 = ci % (D / 8);
+      *reinterpret_cast<u32x4_t*>(vs + r * RS + 16 * c8) = u.vr[j];
     }
 
     f32x4_t sacc[2];
@@ -118,7 +132,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
     for (int st = 0; st < 2; ++st) {
       sacc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sacc[st] = mfma_bf16(kf[st][s], qf[s], sacc[st]);
+      for (int s = 0; s < KS; ++s) sacc[st] = mfma_bf16(u.kf[st][s], qf[s], sacc[st]);
     }
     float x[2][4];
     float mloc = -__builtin_inff();
@@ -168,6 +182,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // One unit in flight per wave: a second register set would halve the
+  // waves per SIMD, and more waves hide latency at least as well.
+  for (int idx = w; idx < n_units; idx += 4) {
+    Unit u;
+    fetch(idx, u);
+    consume(u);
   }
 
   l_run = sum_col4(l_run);

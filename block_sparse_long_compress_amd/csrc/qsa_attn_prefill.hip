@@ -27,8 +27,8 @@
 // membership is one LDS compare per block.
 //
 // V^T fragments come from vt_pack_kernel, which writes V in exactly the lane
-// order the PV product consumes. K fragments are read straight from the
-// cache in operand order by the DMA lane addresses.
+// order the PV product consumes. K rows are copied as whole lines into a
+// swizzled row-major layout (k_swz()).
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -53,15 +53,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier that does not drain the DMA queue (the release fence of
-// __syncthreads would wait for every outstanding global load); the asm
-// statements keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // vt[(bg * n_units + u) * (D/16) + dt][lane][j] = V[32u + kkey(lane/16, j)][16 dt + lane % 16]
@@ -112,29 +103,109 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict
   }
 }
 
-template <int D, int BS, int W>
+// K rows of a stage sit in LDS row-major, as 256-byte lines of sixteen
+// 16-byte chunks, chunk q of line L stored in slot q ^ (L % (D/8)). A copy
+// instruction then moves four whole lines (full cache lines from global
+// memory; a 16-rows-by-64-bytes operand pattern copies about 3x slower), and
+// the 16 lanes that read one MFMA operand column (16 consecutive keys, same
+// dims) hit 16 different slots: no LDS bank conflicts.
+template <int D>
+__device__ __forceinline__ int k_swz(int line, int q) {
+  return line * 256 + 16 * (q ^ (line % (D / 8)));
+}
+// LDS byte offset of the 16 bytes that lane (lg, col) holds for K operand
+// (su, s): key 16 su + col of the stage, dims 32 s + 8 lg .. + 7.
+template <int D>
+__device__ __forceinline__ int k_operand_offset(int su, int s, int lg, int col) {
+  const int off = (16 * su + col) * (2 * D) + 64 * s + 16 * lg;
+  return k_swz<D>(off >> 8, (off >> 4) & 15);
+}
+
+// Keys per LDS stage, which is also the softmax step: 64 when registers
+// allow, else 32 (the K operands of a step stay in VGPRs).
+template <int D, int BS, int W, int NCG>
+constexpr int stage_keys() {
+  return (W == 16) ? 32 : (W == 8) ? ((BS == 64 && D * NCG <= 128) ? 64 : 32) : ((D * NCG >= 256 || BS < 64) ? 32 : 64);
+}
+
+// One ring stage: the K and V^T operand fragments of SK consecutive keys.
+template <int D, int SK, int W>
 struct Stage {
-  static constexpr int kKFrags = (BS / 16) * (D / 32);  // 1 KiB each: 16 keys x 32 dims
-  static constexpr int kVFrags = (BS / 32) * (D / 16);  // 1 KiB each: 16 dims x 32 keys
+  static constexpr int kKFrags = (SK / 16) * (D / 32);  // 1 KiB each: 16 keys x 32 dims
+  static constexpr int kVFrags = (SK / 32) * (D / 16);  // 1 KiB each: 16 dims x 32 keys
   static constexpr int kFrags = kKFrags + kVFrags;
-  static constexpr int kPerWave = kFrags / W;           // DMA instructions per wave per block
   static constexpr int kBytes = kFrags * 1024;
-  static constexpr int kMaxStages = (4 * kBytes <= 128 * 1024) ? 4 : ((3 * kBytes <= 128 * 1024) ? 3 : 2);
-  static_assert(kFrags % W == 0, "fragments per block");
+  // Items a producer keeps in flight after each wait: the wait leaves kLag
+  // items outstanding, and issuing the next item must keep the count within
+  // what vmcnt tracks (63), else the issue itself stalls.
+  static constexpr int kLag = (63 - kFrags) / kFrags < 1 ? 1 : ((63 - kFrags) / kFrags < 3 ? (63 - kFrags) / kFrags : 3);
+  // up to 8 stages in 128 KiB (16 KiB stages), 4 for 32 KiB stages
+  static constexpr int kMaxStages = (128 * 1024 / kBytes) < 8 ? (128 * 1024 / kBytes) : 8;
+  static_assert(kLag >= 1, "copies per stage");
 };
 
+// s_waitcnt vmcnt(n) for a runtime n <= 63 (larger n waits for everything).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le_impl(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) wait_vmcnt<N>();
+    else wait_vmcnt_le_impl<N - 1>(n);
+  }
+}
+__device__ __forceinline__ void wait_vmcnt_le(int n) { wait_vmcnt_le_impl<63>(n > 63 ? 0 : n); }
+
+// LDS counters of the ring (one pair per stage), accessed with explicit
+// ds instructions: the compiler makes every atomic or volatile LDS access
+// wait for all direct-to-LDS copies in flight (vmcnt(0)), which would
+// serialise the ring. Each asm block waits for its own LDS operation, and
+// the hardware runs one wave's LDS operations in order, after the explicit
+// vmcnt waits that publish a wave's copies.
+__device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(uintptr_t)p; }
+// Word 3 of a raw buffer descriptor (byte offsets, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ lds_void_t* lds_ptr(void* p) { return (lds_void_t*)(uintptr_t)lds_addr(p); }
+// 16 bytes per lane from buffer `rs` at byte offset voff into LDS at dst + 16 * lane.
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, unsigned voff, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst), 16, voff, 0, 0, 0);
+}
+// Every wait of the ring ends (the wave furthest behind never waits on
+// another wave); the spin is still bounded (about 2^20 polls), so that a
+// broken invariant shows up as wrong output instead of a hung GPU.
+__device__ __forceinline__ void lds_wait_ge(const unsigned* c, unsigned target) {
+  for (int spin = 0; spin < (1 << 20); ++spin) {
+    unsigned v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(c)) : "memory");
+    if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+// Adds 1 (one lane of the wave).
+__device__ __forceinline__ void lds_signal(unsigned* c) {
+  if (lane_id() == 0) asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_addr(c)), "v"(1u) : "memory");
+}
+// Stores v (one lane of the wave); nothing waits on a store.
+__device__ __forceinline__ void lds_store(unsigned* c, unsigned v) {
+  if (lane_id() == 0) asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(c)), "v"(v) : "memory");
+}
 // LDS layout after the ring of `stages` x Stage::kBytes:
-//   mask[n_words] (u32)  wprefix[n_words] (u32)  tokmask[u_cap] (u64)  ulist[u_cap] (i32)
+//   ready[stages] done[stages] (u32)  mask[n_words] (u32)  wprefix[n_words] (u32)
+//   tokmask[u_cap] (u64)  ulist[u_cap] (i32)  needers[u_cap] (i32)
 struct PrefillLds {
-  int mask, wprefix, tokmask, ulist, total;
+  int ready, done, mask, wprefix, tokmask, ulist, needers, total;
 };
 __host__ __device__ inline PrefillLds prefill_lds(int stage_bytes, int stages, int n_words, int u_cap) {
   PrefillLds L;
-  L.mask = stage_bytes * stages;
+  L.ready = stage_bytes * stages;
+  L.done = L.ready + stages * 4;
+  L.mask = L.done + stages * 4;
   L.wprefix = L.mask + n_words * 4;
   L.tokmask = (L.wprefix + n_words * 4 + 7) / 8 * 8;
   L.ulist = L.tokmask + u_cap * 8;
-  L.total = L.ulist + u_cap * 4;
+  L.needers = L.ulist + u_cap * 4;
+  L.total = L.needers + u_cap * 4;
   return L;
 }
 
@@ -144,36 +215,45 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
     const int32_t* __restrict__ sel, uint16_t* __restrict__ out, int64_t q_len, int64_t q_pos0, int64_t kv_cap,
     int64_t n_units, int hq, int hkv, int G, int top_k, float scale_log2, int n_tiles, int xcd_groups, int stages,
     int n_words_max, int u_cap) {
-  using ST = Stage<D, BS, W>;
+  constexpr int SK = stage_keys<D, BS, W, NCG>();
+  using ST = Stage<D, SK, W>;
   constexpr int NT = W * 64;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int UPB = BS / kUnit;
-  // keys per softmax step: 64 when registers allow, else 32 (the K operands of a step stay in VGPRs)
-  constexpr int CH = (W == 8) ? ((BS == 64 && D * NCG <= 256) ? 64 : 32) : ((D * NCG >= 512 || BS < 64) ? 32 : 64);
-  constexpr int NCH = BS / CH;
-  constexpr int SUB = CH / 16;           // 16-key S^T tiles per step
-  constexpr int UPC = CH / kUnit;        // 32-key PV steps per softmax step
+  constexpr int IPB = BS / SK;           // ring items (stages' worth of keys) per block
+  constexpr int SUB = SK / 16;           // 16-key S^T tiles per item
+  constexpr int UPC = SK / kUnit;        // 32-key PV steps per item
   extern __shared__ __align__(16) unsigned char smem[];
 
   // Work item: (sequence, KV head, tile). Workgroups go to the 8 XCDs
-  // round-robin; when the (sequence, KV head) pairs split evenly over the
-  // XCDs, each XCD serves one pair so that its L2 keeps that pair's K and V.
+  // round-robin (XCD = workgroup id mod 8), each XCD with its own L2. With
+  // xcd_groups = n pairs (n divides 8), each group of 8/n XCDs serves one
+  // (sequence, KV head) pair, so an XCD's L2 holds one pair's K and V^T;
+  // with xcd_groups = -m (m pairs per XCD) each XCD walks its own m pairs.
+  // Slots past the last tile exit at once.
   int bg, tile;
   if (xcd_groups > 0) {
     const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
     const int per = 8 / xcd_groups;  // XCDs per pair
     bg = xcd / per;
     tile = slot * per + xcd % per;
+  } else if (xcd_groups < 0) {
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    bg = xcd + 8 * (slot / n_tiles);
+    tile = slot % n_tiles;
   } else {
     bg = blockIdx.x / n_tiles;
     tile = blockIdx.x % n_tiles;
   }
+  if (tile >= n_tiles) return;
   tile = n_tiles - 1 - tile;  // latest tokens (most blocks) first
   const int64_t b = bg / hkv;
   const int g = bg % hkv;
   const int tpc = 16 / G;
-  const int qt = W * NCG * tpc;
+  constexpr int NP = 1;  // producer waves (they only copy)
+  constexpr int WC = W - NP;           // consumer waves
+  const int qt = WC * NCG * tpc;
   const int64_t t0 = (int64_t)tile * qt;
   const int tid = threadIdx.x, lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -184,13 +264,17 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   const int64_t own_last = (pos_first + rows - 1) / BS;
   const int n_words = (int)(own_last / 32) + 1;
   const PrefillLds L = prefill_lds(ST::kBytes, stages, n_words_max, u_cap);
+  unsigned* ready = reinterpret_cast<unsigned*>(smem + L.ready);
+  unsigned* done = reinterpret_cast<unsigned*>(smem + L.done);
   uint32_t* mask = reinterpret_cast<uint32_t*>(smem + L.mask);
   uint32_t* wprefix = reinterpret_cast<uint32_t*>(smem + L.wprefix);
   unsigned long long* tokmask = reinterpret_cast<unsigned long long*>(smem + L.tokmask);
   int32_t* ulist = reinterpret_cast<int32_t*>(smem + L.ulist);
+  int32_t* needers = reinterpret_cast<int32_t*>(smem + L.needers);
 
   // ---- union of the tile's selections, ascending, with the token set of each block
   for (int i = tid; i < n_words; i += NT) mask[i] = 0u;
+  for (int i = tid; i < stages; i += NT) ready[i] = done[i] = 0u;
   for (int i = tid; i < u_cap; i += NT) tokmask[i] = 0ull;
   __syncthreads();
   const int32_t* sel_tile = sel + ((b * q_len + t0) * hkv + g) * top_k;
@@ -226,45 +310,95 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
     }
   }
   __syncthreads();
+  // consumer waves whose tokens selected each union block
+  const int wtok = NCG * tpc;  // tokens per consumer wave
+  const unsigned long long wmask = wtok >= 64 ? ~0ull : (1ull << wtok) - 1ull;
+  for (int i = tid; i < n_union; i += NT) {
+    const unsigned long long tm = tokmask[i];
+    int n = 0;
+    for (int cw = 0; cw < WC; ++cw) n += ((tm >> (cw * wtok)) & wmask) != 0ull ? 1 : 0;
+    needers[i] = n;
+  }
+  __syncthreads();
 
-  // ---- per-wave DMA plan: fragment f = w + W*j of each block
   const uint16_t* kg = k + ((b * hkv + g) * kv_cap) * D;
   const uint16_t* vtg = vt + ((b * hkv + g) * n_units) * DT * kWave * 8;
-  int src_off[ST::kPerWave];  // elements from the block's base (K rows or V^T units)
+  const int n_items = n_union * IPB;
+  const int ring = stages;
+
+  // Producer / consumer ring, no workgroup barrier. Wave 0 copies each item
+  // (SK keys of one union block: K lines and V^T fragments) into stage
+  // it % ring with direct-to-LDS loads, keeps kLag items in flight, and
+  // publishes ready[stage] = generation + 1 once an item has landed. Each
+  // consumer wave walks every item: it waits for ready, computes if one of
+  // its tokens selected the block, and adds 1 to done[stage]. An item goes
+  // into a stage only after every consumer is done with the stage's
+  // previous item, so consumers drift up to `ring` items apart and a wave
+  // that needs a block holds up none of the waves that do not.
+  if (w < NP) {
+    // producer w takes items it = w, w + NP, ...; `lag` of its items in flight
+    int lag = (ring - 1) / NP;
+    lag = lag < ST::kLag ? lag : ST::kLag;
+    // K: lines 4f .. 4f+3 of the item's rows, this lane fills slot col of
+    // line 4f + lg (k_swz()); V^T: fragments are contiguous.
+    unsigned k_voff[ST::kKFrags], v_voff[ST::kVFrags];
 #pragma unroll
-  for (int j = 0; j < ST::kPerWave; ++j) {
-    const int f = w + W * j;
-    if (f < ST::kKFrags) {
-      const int su = f / KS, s = f % KS;
-      src_off[j] = (16 * su + col) * D + 32 * s + 8 * lg;
-    } else {
-      src_off[j] = ((f - ST::kKFrags) * kWave + lane) * 8;
+    for (int f = 0; f < ST::kKFrags; ++f) {
+      const int line = 4 * f + lg;
+      k_voff[f] = (unsigned)(line * 256 + 16 * (col ^ (line % (D / 8))));
     }
-  }
-  auto issue = [&](int ui, int slot) {
-    const int64_t c = ulist[ui];
-    unsigned char* dst = smem + slot * ST::kBytes;
-    const uint16_t* kbase = kg + c * BS * D;
-    const uint16_t* vbase = vtg + c * (UPB * DT * kWave * 8);
-    const bool tail = (c + 1) * BS > kv_total;  // block runs past the prefix: clamp K rows
 #pragma unroll
-    for (int j = 0; j < ST::kPerWave; ++j) {
-      const int f = w + W * j;
-      const uint16_t* src;
-      if (f < ST::kKFrags) {
-        src = kbase + src_off[j];
-        if (tail) {
-          const int su = f / KS, s = f % KS;
-          int64_t key = c * BS + 16 * su + col;
-          key = key < kv_total ? key : kv_total - 1;  // any finite row: masked out below
-          src = kg + key * D + 32 * s + 8 * lg;
-        }
-      } else {
-        src = vbase + src_off[j];
+    for (int f = 0; f < ST::kVFrags; ++f) v_voff[f] = (unsigned)((f * kWave + lane) * 16);
+    int ul = -1, ul_base = -1;  // 64 union block ids, one per lane
+    int mine = 0;
+    for (int it = w; it < n_items; it += NP) {
+      const int slot = it % ring;
+      if (it >= ring) {
+        // every consumer that needs the stage's previous item is done with it
+        lds_wait_ge(&done[slot], (unsigned)needers[(it - ring) / IPB]);
+        lds_store(&done[slot], 0u);
       }
-      __builtin_amdgcn_global_load_lds(src, dst + f * 1024, 16, 0, 0);
+      const int ui = it / IPB;
+      if ((ui >> 6) != ul_base) {
+        ul_base = ui >> 6;
+        ul = (ul_base << 6) + lane < n_union ? ulist[(ul_base << 6) + lane] : 0;
+      }
+      const int64_t c = __builtin_amdgcn_readlane(ul, ui & 63);
+      const int part = it % IPB;
+      const int64_t key_first = c * BS + (int64_t)part * SK;
+      unsigned char* dst = smem + slot * ST::kBytes;
+      // Buffer descriptors of the item's K rows and V^T fragments: the base
+      // and range live in scalar registers, each lane's offset is fixed, so
+      // issuing a copy needs no vector ALU work (the consumers keep the
+      // vector ALUs busy). Rows past the prefix fall outside the K range and
+      // read as zero (masked out below).
+      const int64_t k_left = key_first < kv_total ? (kv_total - key_first) * (D * 2) : 0;
+      const int k_bytes = k_left < ST::kKFrags * 1024 ? (int)k_left : ST::kKFrags * 1024;
+      const __amdgpu_buffer_rsrc_t krs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kg + key_first * D), (short)0, k_bytes, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vtg + (c * UPB + part * UPC) * (DT * kWave * 8)), (short)0, ST::kVFrags * 1024, kBufferFlags);
+#pragma unroll
+      for (int f = 0; f < ST::kKFrags; ++f) copy_to_lds(krs, k_voff[f], dst + f * 1024);
+#pragma unroll
+      for (int f = 0; f < ST::kVFrags; ++f) copy_to_lds(vrs, v_voff[f], dst + (ST::kKFrags + f) * 1024);
+      if (++mine > lag) {
+        // this producer's item lag steps back has landed
+        if (lag == ST::kLag) wait_vmcnt<ST::kLag * ST::kFrags>();
+        else wait_vmcnt_le(lag * ST::kFrags);
+        const int done_it = it - lag * NP;
+        lds_store(&ready[done_it % ring], (unsigned)(done_it / ring + 1));
+      }
     }
-  };
+    wait_vmcnt<0>();
+    const int n_mine = mine;
+    for (int j = n_mine - lag > 0 ? n_mine - lag : 0; j < n_mine; ++j) {
+      const int it = w + j * NP;
+      lds_store(&ready[it % ring], (unsigned)(it / ring + 1));
+    }
+    return;
+  }
+  const int cw = w - NP;
 
   // ---- per CG: this lane's column token, its position, softmax state, Q operands
   u32x4_t qf[NCG][KS];
@@ -275,7 +409,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   const int tau = col / G;
 #pragma unroll
   for (int n = 0; n < NCG; ++n) {
-    const int r = (w * NCG + n) * tpc + tau;
+    const int r = (cw * NCG + n) * tpc + tau;
     row_ok[n] = r < rows;
     pos_q[n] = (int)(pos_first + r);
     m_run[n] = -__builtin_inff();
@@ -287,39 +421,18 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[n][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  wait_vmcnt<0>();  // Q is in registers before the DMA queue starts counting
 
-  const int wave_shift = w * NCG * tpc;
+  const int wave_shift = cw * NCG * tpc;
   const unsigned long long cg_mask = (1ull << tpc) - 1ull;
 
-  // Consume the union in groups of `per_it` blocks per barrier (2 when four
-  // stages fit: the next group's copies run during the current group's math),
-  // which also averages the per-wave work of the group before the barrier.
-  const int per_it = stages >= 4 ? 2 : 1;
-  const int ring = per_it == 2 ? 4 : stages;
-  if (per_it == 2) {
-    for (int ui = 0; ui < 2 && ui < n_union; ++ui) issue(ui, ui);
-  } else {
-    for (int ui = 0; ui < stages - 1 && ui < n_union; ++ui) issue(ui, ui);
-  }
-
-  for (int u0 = 0; u0 < n_union; u0 += per_it) {
-    if (per_it == 2) {
-      wait_vmcnt<0>();
-      stage_barrier();  // every wave is past the previous group: its stages may be refilled
-      for (int a = 2; a < 4; ++a)
-        if (u0 + a < n_union) issue(u0 + a, (u0 + a) % ring);
-    } else {
-      int ahead = n_union - 1 - u0;
-      ahead = ahead < stages - 2 ? ahead : stages - 2;
-      if (ahead >= 2) wait_vmcnt<2 * ST::kPerWave>();
-      else if (ahead == 1) wait_vmcnt<ST::kPerWave>();
-      else wait_vmcnt<0>();
-      stage_barrier();
-      if (u0 + stages - 1 < n_union) issue(u0 + stages - 1, (u0 + stages - 1) % stages);
-    }
-    for (int ui = u0; ui < u0 + per_it && ui < n_union; ++ui) {
-    const int slot = ui % ring;
+  // Only the blocks this wave's tokens selected: a ballot over 64 union
+  // entries at a time, then their items in order.
+  for (int base = 0; base < n_union; base += kWave) {
+    const bool mine = base + lane < n_union && ((tokmask[base + lane] >> wave_shift) & wmask) != 0ull;
+    unsigned long long todo = __ballot(mine);
+    while (todo != 0ull) {
+    const int ui = base + __builtin_ctzll(todo);
+    todo &= todo - 1ull;
     const int64_t c = ulist[ui];
     const unsigned long long tm = tokmask[ui] >> wave_shift;
     unsigned need = 0u;
@@ -330,87 +443,116 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
       need |= bits != 0ull ? (1u << n) : 0u;
       mem[n] = row_ok[n] && ((bits >> tau) & 1ull);
     }
-    if (need == 0u) continue;
-    const bool diag = (c + 1) * BS > pos_first;  // own block of some token of the tile: causal mask
-    const int key_base = (int)(c * BS);          // positions fit in int32 (checked on the host)
+#pragma unroll 1
+    for (int part = 0; part < IPB; ++part) {
+    const int it = ui * IPB + part;
+    const int slot = it % ring;
+    lds_wait_ge(&ready[slot], (unsigned)(it / ring + 1));
+    {
+    const int key0 = (int)(c * BS) + part * SK;  // positions fit in int32 (checked on the host)
+    const bool diag = key0 + SK > pos_first;           // holds the own block of some token: causal mask
     const unsigned char* kb = smem + slot * ST::kBytes;
     const unsigned char* vb = kb + ST::kKFrags * 1024;
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const int key0 = key_base + ch * CH;
+
+    // The work of one item for the CGs in the compile-time set MASK: all S
+    // products first, then the softmax updates, then the PV products, with
+    // no branch between the MFMAs of one phase so that LDS reads are batched
+    // ahead of their MFMAs.
+    auto run = [&]<unsigned MASK>() {
       u32x4_t kf[SUB][KS];
 #pragma unroll
       for (int su = 0; su < SUB; ++su)
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          kf[su][s] = *reinterpret_cast<const u32x4_t*>(kb + (((ch * SUB + su) * KS + s) * kWave + lane) * 16);
+          kf[su][s] = *reinterpret_cast<const u32x4_t*>(kb + k_operand_offset<D>(su, s, lg, col));
+      f32x4_t acc[NCG][SUB];
+#pragma unroll
+      for (int n = 0; n < NCG; ++n) {
+        if (((MASK >> n) & 1u) != 0u) {
+#pragma unroll
+          for (int su = 0; su < SUB; ++su) {
+            acc[n][su] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) acc[n][su] = mfma_bf16(kf[su][s], qf[n][s], acc[n][su]);
+          }
+        }
+      }
       u32x4_t pf[NCG][UPC];
 #pragma unroll
       for (int n = 0; n < NCG; ++n) {
-        if (!((need >> n) & 1u)) continue;
-        float x[SUB * 4];
-#pragma unroll
-        for (int su = 0; su < SUB; ++su) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) acc = mfma_bf16(kf[su][s], qf[n][s], acc);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[su * 4 + i] = acc[i];
-        }
-        if (diag) {
+        if (((MASK >> n) & 1u) != 0u) {
+          float x[SUB * 4];
 #pragma unroll
           for (int su = 0; su < SUB; ++su)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int pos = key0 + 16 * su + 4 * lg + i;
-              x[su * 4 + i] = pos <= pos_q[n] ? x[su * 4 + i] : -__builtin_inff();
-            }
-        }
-        float mx = x[0];
+            for (int i = 0; i < 4; ++i) x[su * 4 + i] = acc[n][su][i];
+          if (diag) {
 #pragma unroll
-        for (int i = 1; i + 1 < SUB * 4; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(x[i], x[i + 1]));
-        if constexpr ((SUB * 4) % 2 == 0) mx = __builtin_fmaxf(mx, x[SUB * 4 - 1]);
-        mx = max_col4(mx);
-        // The exponent offset m_run is raised only when a score exceeds it by
-        // more than 2^8: p stays <= 256 (exact in fp32, representable in
-        // bf16) and the accumulators are rescaled rarely.
-        const float m_old = m_run[n];
-        const float cand = mx * scale_log2;
-        const bool grow = mem[n] && cand > m_old + kRescaleSlack;
-        const float m_new = grow ? cand : m_old;
-        if (__ballot(grow && m_old != -__builtin_inff()) != 0) {
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m_old - m_new) : 1.0f;
-          l_run[n] *= alpha;
+            for (int su = 0; su < SUB; ++su)
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[n][dt] *= alpha;
-        }
-        m_run[n] = m_new;
-        const float negm = (mem[n] && m_new != -__builtin_inff()) ? -m_new : -__builtin_inff();
-        float pv[SUB * 4];
+              for (int i = 0; i < 4; ++i) {
+                const int pos = key0 + 16 * su + 4 * lg + i;
+                x[su * 4 + i] = pos <= pos_q[n] ? x[su * 4 + i] : -__builtin_inff();
+              }
+          }
+          float mx = x[0];
 #pragma unroll
-        for (int i = 0; i < SUB * 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scale_log2, negm));
-          l_run[n] += pv[i];
-        }
-        // P^T operand of 32-key step u: tiles 2u, 2u+1 (see kkey())
+          for (int i = 1; i + 1 < SUB * 4; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(x[i], x[i + 1]));
+          if constexpr ((SUB * 4) % 2 == 0) mx = __builtin_fmaxf(mx, x[SUB * 4 - 1]);
+          mx = max_col4(mx);
+          // The exponent offset m_run is raised only when a score exceeds it
+          // by more than 2^8: p stays <= 256 (exact in fp32, representable in
+          // bf16) and the accumulators are rescaled rarely.
+          const float m_old = m_run[n];
+          const float cand = mx * scale_log2;
+          const bool grow = mem[n] && cand > m_old + kRescaleSlack;
+          const float m_new = grow ? cand : m_old;
+          if (__ballot(grow && m_old != -__builtin_inff()) != 0) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_old - m_new) : 1.0f;
+            l_run[n] *= alpha;
 #pragma unroll
-        for (int u = 0; u < UPC; ++u) {
-          const float* a = pv + 8 * u;
-          pf[n][u] = u32x4_t{cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3]), cvt_pk_bf16(a[4], a[5]),
-                             cvt_pk_bf16(a[6], a[7])};
+            for (int dt = 0; dt < DT; ++dt) o[n][dt] *= alpha;
+          }
+          m_run[n] = m_new;
+          const float negm = (mem[n] && m_new != -__builtin_inff()) ? -m_new : -__builtin_inff();
+          float pv[SUB * 4];
+#pragma unroll
+          for (int i = 0; i < SUB * 4; ++i) {
+            pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scale_log2, negm));
+            l_run[n] += pv[i];
+          }
+          // P^T operand of 32-key step u: tiles 2u, 2u+1 (see kkey())
+#pragma unroll
+          for (int u = 0; u < UPC; ++u) {
+            const float* pa = pv + 8 * u;
+            pf[n][u] = u32x4_t{cvt_pk_bf16(pa[0], pa[1]), cvt_pk_bf16(pa[2], pa[3]), cvt_pk_bf16(pa[4], pa[5]),
+                               cvt_pk_bf16(pa[6], pa[7])};
+          }
         }
       }
 #pragma unroll
       for (int u = 0; u < UPC; ++u)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vb + (((ch * UPC + u) * DT + dt) * kWave + lane) * 16);
+          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vb + ((u * DT + dt) * kWave + lane) * 16);
 #pragma unroll
-          for (int n = 0; n < NCG; ++n) {
-            if (!((need >> n) & 1u)) continue;
-            o[n][dt] = mfma_bf16(vf, pf[n][u], o[n][dt]);
-          }
+          for (int n = 0; n < NCG; ++n)
+            if (((MASK >> n) & 1u) != 0u) o[n][dt] = mfma_bf16(vf, pf[n][u], o[n][dt]);
         }
+    };
+    if constexpr (NCG == 2) {
+      if (need == 3u) run.template operator()<3u>();
+      else if (need == 1u) run.template operator()<1u>();
+      else run.template operator()<2u>();
+    } else {
+      // one CG at a time (every subset would multiply the code)
+      if (need & 1u) run.template operator()<1u>();
+      if constexpr (NCG > 1) if (need & 2u) run.template operator()<2u>();
+      if constexpr (NCG > 2) if (need & 4u) run.template operator()<4u>();
+      if constexpr (NCG > 3) if (need & 8u) run.template operator()<8u>();
+    }
+    }
+    lds_signal(&done[slot]);
     }
     }
   }
@@ -420,7 +562,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
     const float l = sum_col4(l_run[n]);
     if (!row_ok[n]) continue;
     const float inv = 1.0f / l;
-    const int r = (w * NCG + n) * tpc + tau;
+    const int r = (cw * NCG + n) * tpc + tau;
     uint16_t* dst = out + ((b * q_len + t0 + r) * hq + (int64_t)g * G + col % G) * D + 4 * lg;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -431,26 +573,35 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   }
 }
 
-// CGs per wave: tiles of at most 64 tokens, and for d = 128 at most 4 CGs
-// (4 x 32 accumulator AGPRs plus the Q and K operands fill the register file).
+// CGs per workgroup tile: tiles of at most 64 tokens, and for d = 128 at
+// most 16 CGs.
 inline int ncg_for(int G, int D) {
   const int cap = D == 128 ? 4 : 8;
   return G >= cap ? cap : G;
 }
-// Waves per workgroup: 8 (two per SIMD, 2 CGs each) where the CG count allows.
-inline int waves_for(int G, int D) { return ncg_for(G, D) >= 4 ? 8 : 4; }
-inline int ncg_per_wave(int G, int D) { return waves_for(G, D) == 8 ? ncg_for(G, D) / 2 : ncg_for(G, D); }
+// Waves per workgroup and CGs per wave. d = 128 with G >= 4: 16 waves of one
+// CG each (four per SIMD: one wave's MFMA work overlaps another's softmax,
+// and a block needed by few tokens stalls few waves). Otherwise 8 waves of
+// 2 or 4 CGs, or 4 waves.
+inline int waves_for(int G, int D) {
+  if (D == 128 && ncg_for(G, D) >= 4) return 16;
+  return ncg_for(G, D) >= 4 ? 8 : 4;
+}
+inline int ncg_per_wave(int G, int D) {
+  const int w = waves_for(G, D);
+  return w == 16 ? 1 : (w == 8 ? ncg_for(G, D) / 2 : ncg_for(G, D));
+}
 
 struct PrefillGeom {
   int qt, n_tiles, n_words, u_cap, stages, lds;
 };
 
-template <int D, int BS>
+template <int D, int BS, int W, int NCG>
 PrefillGeom prefill_geom(const Dims& s, int64_t q_len, int64_t q_pos0) {
-  using ST = Stage<D, BS, 4>;  // stage bytes do not depend on the wave count
+  using ST = Stage<D, stage_keys<D, BS, W, NCG>(), W>;
   PrefillGeom gm;
   const int64_t kv_total = q_pos0 + q_len;
-  gm.qt = waves_for(s.group, D) * ncg_per_wave(s.group, D) * (16 / s.group);
+  gm.qt = (W - 1) * NCG * (16 / s.group);  // the producer wave only copies
   gm.n_tiles = (int)((q_len + gm.qt - 1) / gm.qt);
   gm.n_words = (int)(((kv_total - 1) / BS) / 32) + 1;
   const int64_t n_blocks = (kv_total + BS - 1) / BS;
@@ -476,29 +627,52 @@ hipError_t launch_kernel(const Dims& s, const PrefillGeom& gm, int64_t q_len, in
   const int n_bg = s.batch * s.hkv;
   // one (sequence, KV head) pair per group of XCDs when pairs and tiles split evenly over the 8 XCDs
   int xcd_groups = 0;
-  if (n_bg <= 8 && 8 % n_bg == 0 && gm.n_tiles % (8 / n_bg) == 0) xcd_groups = n_bg;
+  unsigned n_wg = (unsigned)(gm.n_tiles * n_bg);
+  if (n_bg <= 8 && 8 % n_bg == 0) {
+    xcd_groups = n_bg;
+    const int per = 8 / n_bg;
+    n_wg = 8u * (unsigned)((gm.n_tiles + per - 1) / per);
+  } else if (n_bg % 8 == 0) {
+    xcd_groups = -(n_bg / 8);
+  }
   const float scale_log2 = s.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((prefill_attn_kernel<D, BS, W, NCG>), dim3((unsigned)(gm.n_tiles * n_bg)), dim3(W * 64), gm.lds, st,
+  hipLaunchKernelGGL((prefill_attn_kernel<D, BS, W, NCG>), dim3(n_wg), dim3(W * 64), gm.lds, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, sel,
                      static_cast<uint16_t*>(out), q_len, q_pos0, kv_cap, n_units, s.hq, s.hkv, s.group, s.top_k,
                      scale_log2, gm.n_tiles, xcd_groups, gm.stages, gm.n_words, gm.u_cap);
   return hipGetLastError();
 }
 
+// Kernel variant (waves, CGs per wave) used at group size G: 1 -> <4,1>,
+// 2 -> <4,2>, and for larger groups <16,1> at d = 128, <8,2> (G = 4) or
+// <8,4> (G >= 8) at d = 64.
 template <int D, int BS>
 hipError_t launch_bs(const Dims& s, int64_t q_len, int64_t q_pos0, int64_t kv_cap, int64_t n_units, const void* q,
                      const void* k, const uint16_t* vt, const int32_t* sel, void* out, hipStream_t st) {
-  const PrefillGeom gm = prefill_geom<D, BS>(s, q_len, q_pos0);
-  switch (ncg_for(s.group, D)) {
-    case 1:
-      return launch_kernel<D, BS, 4, 1>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
-    case 2:
-      return launch_kernel<D, BS, 4, 2>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
-    case 4:
-      return launch_kernel<D, BS, 8, 2>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
-    default:  // 8 CGs (d = 64 only)
-      if constexpr (D == 64) return launch_kernel<D, BS, 8, 4>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
-      else return launch_kernel<D, BS, 8, 2>(s, gm, q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st);
+#define QSA_LAUNCH(W, NCG) \
+  launch_kernel<D, BS, W, NCG>(s, prefill_geom<D, BS, W, NCG>(s, q_len, q_pos0), q_len, q_pos0, kv_cap, n_units, q, k, vt, sel, out, st)
+  const int ncg = ncg_for(s.group, D);
+  if (ncg == 1) return QSA_LAUNCH(4, 1);
+  if (ncg == 2) return QSA_LAUNCH(4, 2);
+  if constexpr (D == 64) {
+    if (ncg == 4) return QSA_LAUNCH(8, 2);
+    return QSA_LAUNCH(8, 4);
+  } else {
+    return QSA_LAUNCH(16, 1);
+  }
+#undef QSA_LAUNCH
+}
+
+template <int D, int BS>
+int smem_bytes(const Dims& s, int64_t q_len, int64_t q_pos0) {
+  const int ncg = ncg_for(s.group, D);
+  if (ncg == 1) return prefill_geom<D, BS, 4, 1>(s, q_len, q_pos0).lds;
+  if (ncg == 2) return prefill_geom<D, BS, 4, 2>(s, q_len, q_pos0).lds;
+  if constexpr (D == 64) {
+    if (ncg == 4) return prefill_geom<D, BS, 8, 2>(s, q_len, q_pos0).lds;
+    return prefill_geom<D, BS, 8, 4>(s, q_len, q_pos0).lds;
+  } else {
+    return prefill_geom<D, BS, 16, 1>(s, q_len, q_pos0).lds;
   }
 }
 
@@ -531,7 +705,8 @@ hipError_t launch_d(const Dims& s, const PrefillPlan& plan, const void* q, const
 
 PrefillPlan plan_prefill(const Dims& s, int64_t q_len, int64_t q_pos0) {
   PrefillPlan p{};
-  p.rows_per_wg = waves_for(s.group, s.d) * ncg_per_wave(s.group, s.d) * (16 / s.group);
+  const int w = waves_for(s.group, s.d);
+  p.rows_per_wg = (w - 1) * ncg_per_wave(s.group, s.d) * (16 / s.group);
   if (s.dtype != 1) {
     p.ws_bytes = 0;
     return p;
@@ -545,11 +720,11 @@ PrefillPlan plan_prefill(const Dims& s, int64_t q_len, int64_t q_pos0) {
 // LDS footprint of the prefill kernel for these sizes.
 int prefill_smem_bytes(const Dims& s, int64_t q_len, int64_t q_pos0) {
   if (s.d == 64) {
-    return s.bs == 32 ? prefill_geom<64, 32>(s, q_len, q_pos0).lds
-                      : (s.bs == 64 ? prefill_geom<64, 64>(s, q_len, q_pos0).lds : prefill_geom<64, 128>(s, q_len, q_pos0).lds);
+    return s.bs == 32 ? smem_bytes<64, 32>(s, q_len, q_pos0)
+                      : (s.bs == 64 ? smem_bytes<64, 64>(s, q_len, q_pos0) : smem_bytes<64, 128>(s, q_len, q_pos0));
   }
-  return s.bs == 32 ? prefill_geom<128, 32>(s, q_len, q_pos0).lds
-                    : (s.bs == 64 ? prefill_geom<128, 64>(s, q_len, q_pos0).lds : prefill_geom<128, 128>(s, q_len, q_pos0).lds);
+  return s.bs == 32 ? smem_bytes<128, 32>(s, q_len, q_pos0)
+                    : (s.bs == 64 ? smem_bytes<128, 64>(s, q_len, q_pos0) : smem_bytes<128, 128>(s, q_len, q_pos0));
 }
 
 hipError_t launch_prefill(const Dims& s, const PrefillPlan& plan, const void* q, const void* k, const void* v,

@@ -45,6 +45,29 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 };
 
+// Four consecutive elements widened to float (one 8- or 16-byte load).
+__device__ __forceinline__ f32x4_t load4_f32(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+__device__ __forceinline__ f32x4_t load4_f32(const uint16_t* p) {
+  const u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
+  return f32x4_t{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+}
+
+// Sum over the G (<= 16) query heads of a group of four consecutive dims:
+// p points at head 0, heads are `stride` elements apart. All loads are
+// issued before the first add; the sum runs in head order from 0.
+template <typename T>
+__device__ __forceinline__ f32x4_t group_sum4(const T* p, int G, int64_t stride) {
+  f32x4_t v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < G) v[j] = load4_f32(p + j * stride);
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < G) s += v[j];
+  return s;
+}
+
 // ---------------------------------------------------------------- shuffles
 
 __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
@@ -168,6 +191,128 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
     }
   }
   return x;
+}
+
+// Same network restricted to the first N lanes' groups (N = 16, 32 or 64):
+// every group of N lanes is sorted descending on its own.
+template <int N>
+__device__ __forceinline__ uint64_t wave_sort_desc_n(uint64_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      uint64_t y = xor_lane_u64(x, j);
+      bool lower = (lane & j) == 0;
+      bool desc = (lane & k) == 0;
+      bool take_max = (lower == desc);
+      x = take_max ? (x > y ? x : y) : (x < y ? x : y);
+    }
+  }
+  return x;
+}
+
+// ------------------------------------------------------------ threshold select
+//
+// Exact selection of the m largest of the keys held P per lane (key 0 =
+// empty slot, never selected) without sorting: the m-th largest key is found
+// bit by bit from the most significant end, counting keys at or above each
+// trial value with ballots. Keys are distinct (the low word is the
+// complemented block id), so exactly min(m, #keys) keys are >= the result.
+
+__device__ __forceinline__ int lanes_set(bool pred) { return __builtin_popcountll(__ballot(pred)); }
+
+// Smallest key value T with exactly min(m, #nonzero keys) keys >= T
+// (1 when there are fewer than m keys).
+template <int P>
+__device__ __forceinline__ uint64_t kth_largest_key(const uint64_t (&x)[P], int m) {
+  uint32_t h[P], l[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    h[p] = (uint32_t)(x[p] >> 32);
+    l[p] = (uint32_t)x[p];
+  }
+  // Largest th with #(high word >= th) >= m. Real keys have a nonzero high
+  // word (the order image of a finite float), so th = 0 means < m keys.
+  uint32_t th = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = th | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) n += lanes_set(h[p] >= c);
+    th = n >= m ? c : th;
+  }
+  if (th == 0) return 1ull;
+  int n_gt = 0, n_ge = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    n_gt += lanes_set(h[p] > th);
+    n_ge += lanes_set(h[p] >= th);
+  }
+  if (n_ge == m) return (uint64_t)th << 32;
+  // High words tie at th: keep the (m - n_gt) largest low words among them.
+  const int need = m - n_gt;
+  uint32_t tl = 0;
+#pragma unroll 4
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = tl | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) n += lanes_set(h[p] == th && l[p] >= c);
+    tl = n >= need ? c : tl;
+  }
+  return ((uint64_t)th << 32) | tl;
+}
+
+// Keys >= t (t >= 1) packed into lanes 0 .. count-1 in no particular order;
+// `scratch` is 64 keys of LDS owned by the calling wave.
+template <int P>
+__device__ __forceinline__ uint64_t gather_keys_ge(const uint64_t (&x)[P], uint64_t t, uint64_t* scratch, int& count) {
+  int base = 0;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const bool s = x[p] >= t;
+    const uint64_t msk = __ballot(s);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0));
+    if (s) scratch[base + below] = x[p];
+    base += __builtin_popcountll(msk);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t r = lane_id() < base ? scratch[lane_id()] : 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  count = base;
+  return r;
+}
+
+// Running top-m set of one row kept by one wave: `keys` in lanes < count,
+// unordered; `thr` = the last selection threshold (every kept key is >= it).
+struct TopSet {
+  uint64_t keys;
+  int count;
+  uint64_t thr;
+};
+
+// Absorb P fresh keys per lane into the set (skipped when the set is full
+// and no fresh key beats its threshold).
+template <int P>
+__device__ __forceinline__ void topset_absorb(TopSet& s, const uint64_t (&fresh)[P], int m, uint64_t* scratch) {
+  if (s.count == m) {
+    bool any = false;
+#pragma unroll
+    for (int p = 0; p < P; ++p) any |= fresh[p] > s.thr;
+    if (__ballot(any) == 0) return;
+  }
+  uint64_t x[P + 1];
+#pragma unroll
+  for (int p = 0; p < P; ++p) x[p] = fresh[p];
+  x[P] = s.keys;
+  s.thr = kth_largest_key<P + 1>(x, m);
+  s.keys = gather_keys_ge<P + 1>(x, s.thr, scratch, s.count);
 }
 
 // Top-64 of two descending lists held one key per lane; result descending.

@@ -13,30 +13,36 @@
 //  * tile path (many query rows, prefill): a workgroup takes 16 consecutive
 //    rows of one (b, g), which share the candidate prefix. Candidate chunks
 //    of 64 compressed keys are staged in LDS and scored with fp32 MFMA
-//    (16x16x4, full fp32 products); each wave then folds four rows' scores
-//    into running top lists with wave-wide bitonic merges.
+//    (16x16x4, full fp32 products); every 128 candidates each wave updates
+//    four rows' running top sets by threshold selection (the m-th largest
+//    key found bit by bit with ballot counts, no sorting), and the final set
+//    is sorted by id once.
 //  * split path (few rows, decode): the candidates of a row are cut into
 //    chunks spread over the whole GPU. Each wave streams 64 compressed keys
 //    per step with fully coalesced 16-byte loads (1 KiB per instruction),
 //    finishes the dot products with a transpose-reduce butterfly, and keeps a
 //    running top list; the chunk's list goes to the workspace and a merge
 //    kernel reduces the lists of a row, skipping every key below the best
-//    chunk-local cutoff (a valid lower bound of the row's cutoff).
+//    chunk-local cutoff (a valid lower bound of the row's cutoff); when all
+//    the lists of a row hold at most 256 keys, one wave takes them at once.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
-// Write one row's selection from a descending top list held one key per
-// lane (lanes < slots valid): ids ascending, own block last, -1 padding.
+// Write one row's selection from the kept keys held one per lane (lanes <
+// slots valid, any order): ids ascending, own block last, -1 padding.
 __device__ void finalize_row(uint64_t cur, int slots, int own, int top_k, int32_t* sel_row, float* score_row) {
   const int lane = lane_id();
   int id = lane < slots ? key_id(cur) : own;
   float sc = lane < slots ? key_score(cur) : __builtin_inff();
-  // Sort lanes 0..slots by ascending id: descending on the complemented id.
+  // Sort lanes 0..slots by ascending id: descending on the complemented id,
+  // with the smallest network that holds slots + 1 entries.
   uint64_t k2 = lane <= slots ? (((uint64_t)(0xFFFFFFFFu - (uint32_t)id) << 32) | __float_as_uint(sc)) : 0ull;
-  k2 = wave_sort_desc(k2);
+  if (slots < 16) k2 = wave_sort_desc_n<16>(k2);
+  else if (slots < 32) k2 = wave_sort_desc_n<32>(k2);
+  else k2 = wave_sort_desc_n<64>(k2);
   const bool real = lane <= slots;
   const int out_id = real ? (int)(0xFFFFFFFFu - (uint32_t)(k2 >> 32)) : -1;
   const float out_sc = real ? __uint_as_float((uint32_t)k2) : -__builtin_inff();
@@ -64,7 +70,8 @@ __device__ uint64_t merge_wave_lists(uint64_t (*lists)[kWave], uint64_t cur, int
 // ------------------------------------------------------------------ tile path
 
 constexpr int kTileRows = 16;
-constexpr int kTileCands = 64;
+constexpr int kTileCands = 64;   // candidates staged and scored per pass
+constexpr int kTilePasses = 2;   // passes per selection step (128 candidates, 2 per lane)
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ q, const float* __restrict__ k_comp,
@@ -72,9 +79,11 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
                                                           int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
                                                           int hkv, int G, int bs, int top_k, float scale) {
   constexpr int QP = D + 4;  // padded row strides (floats): conflict-free 16-byte reads
+  constexpr int SPAN = kTileCands * kTilePasses;
   __shared__ float qbar[kTileRows][QP];
   __shared__ float kc[kTileCands][QP];
-  __shared__ float sc[kTileRows][kTileCands + 4];
+  __shared__ float sc[kTileRows][SPAN + 4];
+  __shared__ uint64_t scratch[4][kWave];
 
   const int64_t t0 = (int64_t)blockIdx.x * kTileRows;
   const int g = blockIdx.y;
@@ -82,30 +91,32 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int64_t rows = q_len - t0 < kTileRows ? q_len - t0 : kTileRows;
 
-  for (int idx = tid; idx < kTileRows * D; idx += 256) {
-    const int r = idx / D, e = idx % D;
-    float v = 0.f;
-    if (r < rows) {
-      const T* src = q + ((b * q_len + t0 + r) * hq + (int64_t)g * G) * D + e;
-      for (int j = 0; j < G; ++j) v += Elem<T>::load(src, (int64_t)j * D);
-    }
-    qbar[r][e] = v;
+  for (int idx = tid; idx < kTileRows * D / 4; idx += 256) {
+    const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (r < rows) v = group_sum4(q + ((b * q_len + t0 + r) * hq + (int64_t)g * G) * D + e4, G, D);
+    *reinterpret_cast<f32x4_t*>(&qbar[r][e4]) = v;
   }
 
   const int64_t own_last = (q_pos0 + t0 + rows - 1) / bs;  // candidates of every row are < own_last
   const float* kc_src = k_comp + ((b * hkv + g) * nb_cap) * D;
-  uint64_t cur[4] = {0ull, 0ull, 0ull, 0ull};
+  TopSet set[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) set[rr] = TopSet{0ull, 0, 0ull};
 
-  for (int64_t c0 = 0; c0 < own_last; c0 += kTileCands) {
-    __syncthreads();  // previous chunk fully consumed
-    for (int idx = tid; idx < kTileCands * D / 4; idx += 256) {
-      const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
-      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-      if (c0 + r < own_last) v = *reinterpret_cast<const f32x4_t*>(kc_src + (c0 + r) * D + e4);
-      *reinterpret_cast<f32x4_t*>(&kc[r][e4]) = v;
-    }
-    __syncthreads();
-    {
+  for (int64_t c0 = 0; c0 < own_last; c0 += SPAN) {
+    // score SPAN candidates for all 16 rows, one staged pass of 64 at a time
+#pragma unroll
+    for (int pass = 0; pass < kTilePasses; ++pass) {
+      const int64_t p0 = c0 + pass * kTileCands;
+      __syncthreads();  // kc (and sc) of the previous pass fully consumed
+      for (int idx = tid; idx < kTileCands * D / 4; idx += 256) {
+        const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
+        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+        if (p0 + r < own_last) v = *reinterpret_cast<const f32x4_t*>(kc_src + (p0 + r) * D + e4);
+        *reinterpret_cast<f32x4_t*>(&kc[r][e4]) = v;
+      }
+      __syncthreads();
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       const int m = lane % 16, kg = lane / 16;
 #pragma unroll
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
         for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], bv[e], acc);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[4 * kg + i][16 * w + m] = acc[i] * scale;
+      for (int i = 0; i < 4; ++i) sc[4 * kg + i][pass * kTileCands + 16 * w + m] = acc[i] * scale;
     }
     __syncthreads();
 #pragma unroll
@@ -126,9 +137,13 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
       const int64_t own = (q_pos0 + t0 + r) / bs;
       const int slots = own < top_k - 1 ? (int)own : top_k - 1;
       if (slots == 0) continue;
-      const int64_t cand = c0 + lane;
-      const uint64_t key = cand < own ? make_key(sc[r][lane], (int)cand) : 0ull;
-      cur[rr] = topk_fold(cur[rr], key, slots);
+      uint64_t fresh[kTilePasses];
+#pragma unroll
+      for (int pass = 0; pass < kTilePasses; ++pass) {
+        const int64_t cand = c0 + pass * kTileCands + lane;
+        fresh[pass] = cand < own ? make_key(sc[r][pass * kTileCands + lane], (int)cand) : 0ull;
+      }
+      topset_absorb<kTilePasses>(set[rr], fresh, slots, scratch[w]);
     }
   }
 #pragma unroll
@@ -139,7 +154,7 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
     const int own = (int)((q_pos0 + t) / bs);
     const int slots = own < top_k - 1 ? own : top_k - 1;
     const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-    finalize_row(cur[rr], slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+    finalize_row(set[rr].keys, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
   }
 }
 
@@ -231,13 +246,7 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   }
   // Each lane sums its own 4 dims of the group's queries: no barrier, so the
   // first compressed-key loads go out together with the query loads.
-  f32x4_t qv = {0.f, 0.f, 0.f, 0.f};
-  {
-    const T* src = q + ((b * q_len + t) * hq + (int64_t)g * G) * D + 4 * (lane % LPR);
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qv[i] += Elem<T>::load(src, (int64_t)j * D + i);
-  }
+  const f32x4_t qv = group_sum4(q + ((b * q_len + t) * hq + (int64_t)g * G) * D + 4 * (lane % LPR), G, D);
 
   const int64_t c_begin = ch * chunk;
   const int64_t c_end = c_begin + chunk < own ? c_begin + chunk : own;
@@ -331,6 +340,39 @@ __global__ __launch_bounds__(256) void select_merge_kernel(int32_t* __restrict__
   finalize_row(cur, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
 }
 
+// Merge for rows whose chunk lists hold at most 256 keys in total: one wave
+// loads every key at once (4 per lane) and takes the top set directly.
+constexpr int kSmallMergeKeys = 4 * kWave;
+
+__global__ __launch_bounds__(64) void select_merge_small_kernel(int32_t* __restrict__ sel,
+                                                                float* __restrict__ sel_scores,
+                                                                const uint64_t* __restrict__ ws, int64_t q_len,
+                                                                int64_t q_pos0, int hkv, int bs, int top_k,
+                                                                int64_t n_chunks) {
+  __shared__ uint64_t scratch[kWave];
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / (q_len * hkv);
+  const int64_t t = (row / hkv) % q_len;
+  const int g = (int)(row % hkv);
+  const int lane = lane_id();
+  const int own = (int)((q_pos0 + t) / bs);
+  const int slots = own < top_k - 1 ? own : top_k - 1;
+  if (slots == 0) return;  // written by the split kernel
+  const int sm = top_k - 1;
+  const uint64_t* lst = ws + row * n_chunks * sm;
+  const int n_keys = (int)n_chunks * slots;  // the first `slots` entries of each list
+  uint64_t x[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = lane + kWave * p;
+    x[p] = i < n_keys ? lst[(int64_t)(i / slots) * sm + i % slots] : 0ull;
+  }
+  TopSet set{0ull, 0, 0ull};
+  topset_absorb<4>(set, x, slots, scratch);
+  const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
+  finalize_row(set.keys, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, int64_t q_len, int64_t q_pos0,
                         const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
@@ -350,8 +392,12 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
                      s.scale, plan.chunk, plan.n_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_chunks == 1) return e;
-  hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256), 0, st, sel, sel_scores, wsk, q_len, q_pos0,
-                     s.hkv, s.bs, s.top_k, plan.n_chunks);
+  if (plan.n_chunks * (s.top_k - 1) <= kSmallMergeKeys)
+    hipLaunchKernelGGL(select_merge_small_kernel, dim3((unsigned)rows), dim3(64), 0, st, sel, sel_scores, wsk, q_len,
+                       q_pos0, s.hkv, s.bs, s.top_k, plan.n_chunks);
+  else
+    hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256), 0, st, sel, sel_scores, wsk, q_len,
+                       q_pos0, s.hkv, s.bs, s.top_k, plan.n_chunks);
   return hipGetLastError();
 }
 
