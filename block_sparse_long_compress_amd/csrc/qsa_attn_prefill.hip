@@ -135,13 +135,11 @@ struct Stage {
   static constexpr int kVFrags = (SK / 32) * (D / 16);  // 1 KiB each: 16 dims x 32 keys
   static constexpr int kFrags = kKFrags + kVFrags;
   static constexpr int kBytes = kFrags * 1024;
-  // Items a producer keeps in flight after each wait: the wait leaves kLag
-  // items outstanding, and issuing the next item must keep the count within
-  // what vmcnt tracks (63), else the issue itself stalls.
-  static constexpr int kLag = (63 - kFrags) / kFrags < 1 ? 1 : ((63 - kFrags) / kFrags < 3 ? (63 - kFrags) / kFrags : 3);
-  // up to 8 stages in 128 KiB (16 KiB stages), 4 for 32 KiB stages
+  // up to 8 stages in 128 KiB (16 KiB stages), 4 for 32 KiB stages; the
+  // host drops stages while the block lists do not fit beside them (a 9th
+  // 16 KiB stage measured no faster)
   static constexpr int kMaxStages = (128 * 1024 / kBytes) < 8 ? (128 * 1024 / kBytes) : 8;
-  static_assert(kLag >= 1, "copies per stage");
+  static_assert(kKFrags == kVFrags, "K and V^T copies per stage");
 };
 
 // s_waitcnt vmcnt(n) for a runtime n <= 63 (larger n waits for everything).
@@ -192,11 +190,11 @@ __device__ __forceinline__ void lds_store(unsigned* c, unsigned v) {
 }
 // LDS layout after the ring of `stages` x Stage::kBytes:
 //   ready[stages] done[stages] (u32)  mask[n_words] (u32)  wprefix[n_words] (u32)
-//   tokmask[u_cap] (u64)  ulist[u_cap] (i32)  needers[u_cap] (i32)
+//   tokmask[u_cap] (u64)  ulist[u_cap] (i32)  needers[u_cap] (i32)  cum_done[u_cap * ipb] (i32)
 struct PrefillLds {
-  int ready, done, mask, wprefix, tokmask, ulist, needers, total;
+  int ready, done, mask, wprefix, tokmask, ulist, needers, cum_done, total;
 };
-__host__ __device__ inline PrefillLds prefill_lds(int stage_bytes, int stages, int n_words, int u_cap) {
+__host__ __device__ inline PrefillLds prefill_lds(int stage_bytes, int stages, int n_words, int u_cap, int ipb) {
   PrefillLds L;
   L.ready = stage_bytes * stages;
   L.done = L.ready + stages * 4;
@@ -205,7 +203,8 @@ __host__ __device__ inline PrefillLds prefill_lds(int stage_bytes, int stages, i
   L.tokmask = (L.wprefix + n_words * 4 + 7) / 8 * 8;
   L.ulist = L.tokmask + u_cap * 8;
   L.needers = L.ulist + u_cap * 4;
-  L.total = L.needers + u_cap * 4;
+  L.cum_done = L.needers + u_cap * 4;
+  L.total = L.cum_done + u_cap * ipb * 4;
   return L;
 }
 
@@ -251,7 +250,14 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   const int64_t b = bg / hkv;
   const int g = bg % hkv;
   const int tpc = 16 / G;
-  constexpr int NP = 1;  // producer waves (they only copy)
+  // One producer wave (a second one, splitting K and V^T, measured slower:
+  // it takes a consumer's place and the two shares of an item must both land).
+  constexpr int NP = 1;
+  constexpr int FPP = (Stage<D, stage_keys<D, BS, W, NCG>(), W>::kFrags) / NP;  // copies per producer per item
+  // Items a producer keeps in flight after each wait: issuing the next item
+  // must keep its outstanding copies within what vmcnt tracks (63), else the
+  // issue itself stalls.
+  constexpr int kLagP = (63 - FPP) / FPP < 1 ? 1 : ((63 - FPP) / FPP < 6 ? (63 - FPP) / FPP : 6);
   constexpr int WC = W - NP;           // consumer waves
   const int qt = WC * NCG * tpc;
   const int64_t t0 = (int64_t)tile * qt;
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   const int64_t pos_first = q_pos0 + t0;
   const int64_t own_last = (pos_first + rows - 1) / BS;
   const int n_words = (int)(own_last / 32) + 1;
-  const PrefillLds L = prefill_lds(ST::kBytes, stages, n_words_max, u_cap);
+  const PrefillLds L = prefill_lds(ST::kBytes, stages, n_words_max, u_cap, IPB);
   unsigned* ready = reinterpret_cast<unsigned*>(smem + L.ready);
   unsigned* done = reinterpret_cast<unsigned*>(smem + L.done);
   uint32_t* mask = reinterpret_cast<uint32_t*>(smem + L.mask);
@@ -271,6 +277,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   unsigned long long* tokmask = reinterpret_cast<unsigned long long*>(smem + L.tokmask);
   int32_t* ulist = reinterpret_cast<int32_t*>(smem + L.ulist);
   int32_t* needers = reinterpret_cast<int32_t*>(smem + L.needers);
+  int32_t* cum_done = reinterpret_cast<int32_t*>(smem + L.cum_done);
 
   // ---- union of the tile's selections, ascending, with the token set of each block
   for (int i = tid; i < n_words; i += NT) mask[i] = 0u;
@@ -320,25 +327,38 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
     needers[i] = n;
   }
   __syncthreads();
+  // cum_done[it]: done signals that stage it % ring has received once
+  // every needer of item it (and of the stage's earlier items) is done
+  const int n_items = n_union * IPB;
+  const int ring = stages;
+  for (int s0 = tid; s0 < ring; s0 += NT) {
+    int acc = 0;
+    for (int it = s0; it < n_items; it += ring) {
+      acc += needers[it / IPB];
+      cum_done[it] = acc;
+    }
+  }
+  __syncthreads();
 
   const uint16_t* kg = k + ((b * hkv + g) * kv_cap) * D;
   const uint16_t* vtg = vt + ((b * hkv + g) * n_units) * DT * kWave * 8;
-  const int n_items = n_union * IPB;
-  const int ring = stages;
 
-  // Producer / consumer ring, no workgroup barrier. Wave 0 copies each item
-  // (SK keys of one union block: K lines and V^T fragments) into stage
-  // it % ring with direct-to-LDS loads, keeps kLag items in flight, and
-  // publishes ready[stage] = generation + 1 once an item has landed. Each
-  // consumer wave walks every item: it waits for ready, computes if one of
-  // its tokens selected the block, and adds 1 to done[stage]. An item goes
-  // into a stage only after every consumer is done with the stage's
-  // previous item, so consumers drift up to `ring` items apart and a wave
-  // that needs a block holds up none of the waves that do not.
+  // Producer / consumer ring, no workgroup barrier. The producer waves copy
+  // each item (SK keys of one union block: K lines and V^T fragments) into
+  // stage it % ring with direct-to-LDS loads (with two producers, one copies
+  // K and one V^T), keep up to kLagP items in flight, and add 1 to
+  // ready[stage] once their share of an item has landed. A consumer wave
+  // visits only the items its tokens selected: it waits until ready shows
+  // all NP shares of that item, computes, and adds 1 to done[stage]. An item
+  // goes into a stage only after every consumer that needs one of the
+  // stage's earlier items is done with it (cum_done), so consumers drift up
+  // to `ring` items apart and a wave that needs a block holds up none of the
+  // waves that do not.
   if (w < NP) {
-    // producer w takes items it = w, w + NP, ...; `lag` of its items in flight
-    int lag = (ring - 1) / NP;
-    lag = lag < ST::kLag ? lag : ST::kLag;
+    // every producer walks all items; `lag` of its items stay in flight
+    const int lag = kLagP < ring - 1 ? kLagP : ring - 1;
+    const bool do_k = NP == 1 || w == 0;
+    const bool do_v = NP == 1 || w == 1;
     // K: lines 4f .. 4f+3 of the item's rows, this lane fills slot col of
     // line 4f + lg (k_swz()); V^T: fragments are contiguous.
     unsigned k_voff[ST::kKFrags], v_voff[ST::kVFrags];
@@ -350,14 +370,10 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
 #pragma unroll
     for (int f = 0; f < ST::kVFrags; ++f) v_voff[f] = (unsigned)((f * kWave + lane) * 16);
     int ul = -1, ul_base = -1;  // 64 union block ids, one per lane
-    int mine = 0;
-    for (int it = w; it < n_items; it += NP) {
+    for (int it = 0; it < n_items; ++it) {
       const int slot = it % ring;
-      if (it >= ring) {
-        // every consumer that needs the stage's previous item is done with it
-        lds_wait_ge(&done[slot], (unsigned)needers[(it - ring) / IPB]);
-        lds_store(&done[slot], 0u);
-      }
+      // every consumer that needs one of the stage's earlier items is done with it
+      if (it >= ring) lds_wait_ge(&done[slot], (unsigned)cum_done[it - ring]);
       const int ui = it / IPB;
       if ((ui >> 6) != ul_base) {
         ul_base = ui >> 6;
@@ -372,30 +388,29 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
       // issuing a copy needs no vector ALU work (the consumers keep the
       // vector ALUs busy). Rows past the prefix fall outside the K range and
       // read as zero (masked out below).
-      const int64_t k_left = key_first < kv_total ? (kv_total - key_first) * (D * 2) : 0;
-      const int k_bytes = k_left < ST::kKFrags * 1024 ? (int)k_left : ST::kKFrags * 1024;
-      const __amdgpu_buffer_rsrc_t krs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(kg + key_first * D), (short)0, k_bytes, kBufferFlags);
-      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vtg + (c * UPB + part * UPC) * (DT * kWave * 8)), (short)0, ST::kVFrags * 1024, kBufferFlags);
+      if (do_k) {
+        const int64_t k_left = key_first < kv_total ? (kv_total - key_first) * (D * 2) : 0;
+        const int k_bytes = k_left < ST::kKFrags * 1024 ? (int)k_left : ST::kKFrags * 1024;
+        const __amdgpu_buffer_rsrc_t krs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kg + key_first * D), (short)0, k_bytes, kBufferFlags);
 #pragma unroll
-      for (int f = 0; f < ST::kKFrags; ++f) copy_to_lds(krs, k_voff[f], dst + f * 1024);
+        for (int f = 0; f < ST::kKFrags; ++f) copy_to_lds(krs, k_voff[f], dst + f * 1024);
+      }
+      if (do_v) {
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vtg + (c * UPB + part * UPC) * (DT * kWave * 8)), (short)0, ST::kVFrags * 1024, kBufferFlags);
 #pragma unroll
-      for (int f = 0; f < ST::kVFrags; ++f) copy_to_lds(vrs, v_voff[f], dst + (ST::kKFrags + f) * 1024);
-      if (++mine > lag) {
-        // this producer's item lag steps back has landed
-        if (lag == ST::kLag) wait_vmcnt<ST::kLag * ST::kFrags>();
-        else wait_vmcnt_le(lag * ST::kFrags);
-        const int done_it = it - lag * NP;
-        lds_store(&ready[done_it % ring], (unsigned)(done_it / ring + 1));
+        for (int f = 0; f < ST::kVFrags; ++f) copy_to_lds(vrs, v_voff[f], dst + (ST::kKFrags + f) * 1024);
+      }
+      if (it >= lag) {
+        // this producer's share of item it - lag has landed
+        if (lag == kLagP) wait_vmcnt<kLagP * FPP>();
+        else wait_vmcnt_le(lag * FPP);
+        lds_signal(&ready[(it - lag) % ring]);
       }
     }
     wait_vmcnt<0>();
-    const int n_mine = mine;
-    for (int j = n_mine - lag > 0 ? n_mine - lag : 0; j < n_mine; ++j) {
-      const int it = w + j * NP;
-      lds_store(&ready[it % ring], (unsigned)(it / ring + 1));
-    }
+    for (int it = n_items - lag > 0 ? n_items - lag : 0; it < n_items; ++it) lds_signal(&ready[it % ring]);
     return;
   }
   const int cw = w - NP;
@@ -447,7 +462,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
     for (int part = 0; part < IPB; ++part) {
     const int it = ui * IPB + part;
     const int slot = it % ring;
-    lds_wait_ge(&ready[slot], (unsigned)(it / ring + 1));
+    lds_wait_ge(&ready[slot], (unsigned)(NP * (it / ring + 1)));
     {
     const int key0 = (int)(c * BS) + part * SK;  // positions fit in int32 (checked on the host)
     const bool diag = key0 + SK > pos_first;           // holds the own block of some token: causal mask
@@ -608,10 +623,10 @@ PrefillGeom prefill_geom(const Dims& s, int64_t q_len, int64_t q_pos0) {
   const int64_t cap = (int64_t)gm.qt * s.top_k;
   gm.u_cap = (int)(cap < n_blocks ? cap : n_blocks);
   gm.stages = ST::kMaxStages;
-  gm.lds = prefill_lds(ST::kBytes, gm.stages, gm.n_words, gm.u_cap).total;
+  gm.lds = prefill_lds(ST::kBytes, gm.stages, gm.n_words, gm.u_cap, BS / stage_keys<D, BS, W, NCG>()).total;
   while (gm.stages > 2 && gm.lds > 160 * 1024) {
     --gm.stages;
-    gm.lds = prefill_lds(ST::kBytes, gm.stages, gm.n_words, gm.u_cap).total;
+    gm.lds = prefill_lds(ST::kBytes, gm.stages, gm.n_words, gm.u_cap, BS / stage_keys<D, BS, W, NCG>()).total;
   }
   return gm;
 }
