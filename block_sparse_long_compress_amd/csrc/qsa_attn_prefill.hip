@@ -14,17 +14,18 @@
 // O^T += V^T P^T, with P^T taken from the S^T accumulators without any lane
 // exchange (see kkey()).
 //
-// A workgroup of 4 waves owns NCG CGs per wave (a 64-token tile for G = 8)
-// of one (sequence, KV head) and walks the union of their selections in
-// ascending block order. Each block's K and V^T operand fragments are copied
-// into a ring of NS LDS stages by direct global->LDS loads
-// (global_load_lds_dwordx4: no VGPR staging), NS-1 blocks ahead of the one
-// being computed; a stage is released with a plain s_barrier after an
-// explicit vmcnt wait, so the copies of later stages stay in flight. Every
-// fragment is one 16-byte LDS read per lane, shared by all CGs of the wave
-// that selected the block. Accumulators (NCG x d/16 x 4 floats per lane) sit
-// in AGPRs. Each token keeps a cursor into its ascending selection list, so
-// membership is one LDS compare per block.
+// A workgroup owns one tile of consecutive tokens of one (sequence, KV
+// head): W - 1 consumer waves with NCG CGs each (at d = 128 and G = 8: 15
+// waves of one CG, a 30-token tile) and one producer wave. The tile's
+// selections are merged into the ascending union of their blocks, each with
+// the set of tile tokens that selected it. The producer copies the union,
+// SK keys at a time (an "item": K rows and V^T operand fragments, 16 KiB at
+// d = 128), into a ring of LDS stages with direct-to-LDS buffer loads; LDS
+// counters (ready / done per stage) replace workgroup barriers, so each
+// consumer visits only the blocks its own tokens selected, at its own pace.
+// A consumer computes S^T for its CG from the staged K, runs the online
+// softmax (exp2 domain, lazy rescale), and accumulates O^T from the staged
+// V^T; accumulators stay in registers for the whole tile.
 //
 // V^T fragments come from vt_pack_kernel, which writes V in exactly the lane
 // order the PV product consumes. K rows are copied as whole lines into a
