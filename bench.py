@@ -169,10 +169,13 @@ def capture_step(torch, st, stream):
 
 def run_gpu(w, steps, warmup, seed, use_graph):
     """Timed region: `steps` replays of one graph holding a whole step (wall clock,
-    synchronised on both sides). Per-call durations: a second timed region in
-    which each call's own graph is replayed with HIP events between calls,
-    queued behind a short GPU sleep so that host submission never starves the
-    GPU between two calls."""
+    synchronised on both sides).
+
+    Per-call durations: the calls are launched eagerly, HIP events recorded
+    between them on the launch stream, all queued behind a GPU sleep so that
+    the events bracket GPU work only (no host submission gaps, no graph launch
+    cost). Cold steps: the step graph replayed after a 1 GiB device read that
+    evicts L2 and the 256 MiB MALL, timed by events around the replay."""
     import torch
 
     st = Step(w, seed)
@@ -181,21 +184,12 @@ def run_gpu(w, steps, warmup, seed, use_graph):
         for _, fn in st.calls:
             fn()  # eager warm-up before capture
         torch.cuda.synchronize()
-        call_graphs = []
-        step_graph = None
         if use_graph:
-            for name, fn in st.calls:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    fn()
-                call_graphs.append((name, g.replay))
             step_graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(step_graph, stream=stream):
                 capture_step(torch, st, stream)
             run_step = step_graph.replay
         else:
-            call_graphs = list(st.calls)
-
             def run_step():
                 capture_step(torch, st, stream)
         torch.cuda.synchronize()
@@ -208,23 +202,49 @@ def run_gpu(w, steps, warmup, seed, use_graph):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
-        # per-call durations (HIP events on the launch stream)
-        n_calls = len(call_graphs)
-        reps = max(10, min(steps, 200))
+        # per-call durations (HIP events on the launch stream, eager launches)
+        n_calls = len(st.calls)
+        reps = max(10, min(steps, 50))
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)] for _ in range(reps)]
+        for _, fn in st.calls:
+            fn()
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(2e7))  # ~10 ms of GPU time: lets the host queue every launch below
+        s0 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        torch.cuda._sleep(int(1e8))  # GPU busy while the host queues every launch below
+        h0 = time.perf_counter()
         for r in range(reps):
             ev = events[r]
             ev[0].record(stream)
-            for i, (_, fn) in enumerate(call_graphs):
+            for i, (_, fn) in enumerate(st.calls):
                 fn()
                 ev[i + 1].record(stream)
+        enqueue_s = time.perf_counter() - h0
         torch.cuda.synchronize()
+        # the host must finish queueing before the sleep ends, or gaps enter the events
+        sleep_s = 1e-3 * s0.elapsed_time(events[0][0])
+
+        # cold steps: evict L2 and MALL before each replay by reading 1 GiB
+        # (a read leaves clean lines: nothing is written back during the step)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        cold_reps = 10
+        cold = []
+        for _ in range(cold_reps):
+            flush.amax()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run_step()
+            b.record(stream)
+            cold.append((a, b))
+        torch.cuda.synchronize()
+        del flush
     per_call = {}
-    for i, (name, _) in enumerate(call_graphs):
+    for i, (name, _) in enumerate(st.calls):
         per_call[name] = 1e-3 * float(np.mean([events[r][i].elapsed_time(events[r][i + 1]) for r in range(reps)]))
-    return st, wall, per_call
+    cold_s = 1e-3 * float(np.mean([a.elapsed_time(b) for a, b in cold]))
+    return st, wall, per_call, cold_s, {"host_enqueue_ms": round(1e3 * enqueue_s, 2),
+                                        "gpu_sleep_ms": round(1e3 * sleep_s, 2), "reps": reps}
 
 
 # ------------------------------------------------------------- CPU baseline
@@ -297,7 +317,7 @@ def main():
     import qsa_synth as S
 
     w = S.WORKLOADS[args.workload]
-    st, wall, per_call = run_gpu(w, args.steps, args.warmup, args.seed, not args.no_graph)
+    st, wall, per_call, cold_s, call_timing = run_gpu(w, args.steps, args.warmup, args.seed, not args.no_graph)
     model = work_model(w, st.n_new_blocks)
     ms_per_step = 1e3 * wall / args.steps
     tokens = w.batch if w.mode == "decode" else w.batch * w.kv_len
@@ -335,6 +355,9 @@ def main():
         "roofline": {"bound": bound, "kernel": f"{dominant} call", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": None},
         "calls": calls,
+        "call_timing": call_timing,
+        "cold": {"ms_per_step": round(1e3 * cold_s, 5), "value": round(tokens / cold_s, 2),
+                 "note": "step replayed after reading 1 GiB, which evicts L2 and MALL"},
     }
     if args.copy_calibration_mib > 0:
         import torch
