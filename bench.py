@@ -307,6 +307,37 @@ def cpu_baseline(w, seed, budget_s):
                           f"query tokens of {w.kv_len} ({t_rows:.1f} s), scaled to the whole prompt"}
 
 
+# ------------------------------------------------------------- measured traffic
+
+def source_sha256():
+    """SHA-256 over the kernel sources (name, then bytes, in name order)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "block_sparse_long_compress_amd", "csrc")
+    for n in sorted(os.listdir(d)):
+        if n.endswith((".hip", ".h", ".cpp")):
+            h.update(n.encode())
+            with open(os.path.join(d, n), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, call):
+    """HBM bytes (read + written) per launch of `call` from the committed memory-counter
+    table, or None when it is missing or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    try:
+        text = open(path).read()
+        table = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if table.get("source_sha256") != source_sha256():
+        return None
+    entry = table.get("workloads", {}).get(workload, {}).get(call)
+    return None if entry is None else entry["read_bytes"] + entry["write_bytes"]
+
+
 # ------------------------------------------------------------- main
 
 def main():
@@ -353,7 +384,8 @@ def main():
                    "block_size": w.block_size, "top_k": w.top_k, "seed": args.seed,
                    "graphs": not args.no_graph},
         "roofline": {"bound": bound, "kernel": f"{dominant} call", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": None},
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(w.name, dominant)},
         "calls": calls,
         "call_timing": call_timing,
         "cold": {"ms_per_step": round(1e3 * cold_s, 5), "value": round(tokens / cold_s, 2),
