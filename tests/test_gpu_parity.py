@@ -52,6 +52,11 @@ PREFILL_CASES = [
     W(kv_len=530, n_q_heads=8, n_kv_heads=4, top_k=5),         # G = 2
     W(kv_len=530, n_q_heads=8, n_kv_heads=2, top_k=5),         # G = 4
     W(kv_len=530, n_q_heads=16, n_kv_heads=1, top_k=5),        # G = 16
+    # d = 64 with every kernel variant (G decides waves and CGs per wave)
+    W(kv_len=900, head_dim=64, n_q_heads=8, n_kv_heads=2, top_k=6),                   # G = 4
+    W(kv_len=650, head_dim=64, n_q_heads=4, n_kv_heads=2, top_k=5, block_size=128),   # G = 2
+    W(kv_len=530, head_dim=64, n_q_heads=2, n_kv_heads=2, top_k=4),                   # G = 1
+    W(kv_len=530, head_dim=64, n_q_heads=16, n_kv_heads=1, top_k=4, block_size=64),   # G = 16
     W(kv_len=300, dtype="f32", sigma=1.0, top_k=3, head_dim=128),
     W(kv_len=15, top_k=2),                                     # shorter than one block
 ]
