@@ -34,6 +34,12 @@ Readings taken where the pages are silent (each restated where it is used):
 * ``top_k`` counts the query's own block, which is always kept; the other
   ``min(top_k - 1, i)`` slots go to the best-scoring candidates, equal
   scores going to the smaller block index;
+* optional ``keep_tail`` frame, the one behind the released configuration of
+  [port] (visible width at most ``budget + ratio - 1`` with a budget of
+  whole blocks): every complete block among the ``p + 1`` cached positions
+  is a candidate, the own block included once it is complete, and only the
+  positions not yet in a complete block are always visible; their block
+  takes one of the ``top_k`` slots when it is not empty (so ``top_k >= 2``);
 * the selection is reported as ascending block ids padded with -1;
 * attention is exact softmax attention with the same scale over the keys of
   the selected complete blocks plus positions ``i*Bs .. p`` of the own block.
@@ -85,25 +91,51 @@ def block_scores(q_group: np.ndarray, k_comp: np.ndarray, n_candidates: int, sca
     return scale * total
 
 
-def select_blocks(scores: np.ndarray, own_block: int, top_k: int) -> list[int]:
+def selection_frame(p: int, block_size: int, keep_tail: bool = False) -> tuple[int, int | None]:
+    """``(n_candidates, forced)`` for a query at absolute position ``p``.
+
+    Default: the candidates are the complete blocks ``0 .. i-1`` before the
+    own block ``i = p // Bs`` and block ``i`` is always kept.
+    ``keep_tail`` ([port], released budget and the bound
+    ``min(n_kv, budget + ratio - 1)``): the candidates are all
+    ``(p + 1) // Bs`` complete blocks; the block holding the positions past
+    the last complete block is always kept when there are such positions,
+    else nothing is forced.
+    """
+    if not keep_tail:
+        own = p // block_size
+        return own, own
+    n_complete = (p + 1) // block_size
+    return n_complete, (n_complete if (p + 1) % block_size else None)
+
+
+def select_in_frame(scores: np.ndarray, n_candidates: int, forced: int | None, top_k: int) -> list[int]:
     """Kept block ids for one token and KV head ([port] top-k selection -> cache-cell IDs).
 
-    ``scores[c]`` for candidates ``c < own_block``. The own block always
-    counts as one of the ``top_k`` slots; the remaining slots take the
-    best-scoring candidates (ties to the smaller id). Returns ``top_k`` ids,
-    ascending, padded with -1.
+    ``scores[c]`` for candidates ``c < n_candidates``. One of the ``top_k``
+    slots is reserved for the forced block; ``min(top_k - 1, n_candidates)``
+    slots take the best-scoring candidates (ties to the smaller id). Returns
+    ``top_k`` ids, ascending, padded with -1.
     """
-    slots = min(top_k - 1, own_block)
-    ranked = sorted(range(own_block), key=lambda c: (-float(scores[c]), c))
-    kept = sorted(ranked[:slots] + [own_block])
+    if forced is None and top_k < 2:
+        raise ValueError("a frame without a forced block needs top_k >= 2 (else nothing is visible)")
+    slots = min(top_k - 1, n_candidates)
+    ranked = sorted(range(n_candidates), key=lambda c: (-float(scores[c]), c))
+    kept = sorted(ranked[:slots] + ([] if forced is None else [forced]))
     return kept + [-1] * (top_k - len(kept))
+
+
+def select_blocks(scores: np.ndarray, own_block: int, top_k: int) -> list[int]:
+    """Default frame: candidates ``c < own_block``, the own block always kept and counted in ``top_k``."""
+    return select_in_frame(scores, own_block, own_block, top_k)
 
 
 def visible_positions(selection, p: int, block_size: int) -> np.ndarray:
     """Absolute key positions one query at position ``p`` attends to.
 
     Complete selected blocks contribute all their positions; the own block
-    contributes ``i*Bs .. p`` (causal inside the block).
+    contributes ``i*Bs .. p`` (causal inside the block), which is the whole
+    block once ``p`` is its last position.
     """
     own = p // block_size
     positions: list[int] = []
@@ -138,13 +170,14 @@ def attend_given_selection(q_group, K, V, selection, p, block_size, scale):
     return np.stack([attend(q_group[j], K, V, pos, scale) for j in range(q_group.shape[0])])
 
 
-def qsa_rows(Q, K, V, block_size, top_k, scale=None, q_pos0=0, rows=None, k_comp=None):
+def qsa_rows(Q, K, V, block_size, top_k, scale=None, q_pos0=0, rows=None, k_comp=None, keep_tail=False):
     """QSA for every (sequence, query row, KV head) requested.
 
     ``Q``: ``[b][q_len][Hq][d]``; ``K``, ``V``: ``[b][Hkv][N][d]``; query row
     ``t`` sits at absolute position ``q_pos0 + t``. ``rows`` is an iterable
     of ``(b, t, g)`` (default: all). ``k_comp`` may pass precomputed
-    compressed keys ``[b][Hkv][N//Bs][d]``.
+    compressed keys ``[b][Hkv][N//Bs][d]``. ``keep_tail`` picks the frame of
+    :func:`selection_frame`.
 
     Returns a dict ``(b, t, g) -> (selection, scores, out[G][d])`` where
     ``scores`` are the float64 candidate scores of that row.
@@ -161,21 +194,21 @@ def qsa_rows(Q, K, V, block_size, top_k, scale=None, q_pos0=0, rows=None, k_comp
     result = {}
     for b, t, g in rows:
         p = q_pos0 + t
-        own = p // block_size
+        n_cand, forced = selection_frame(p, block_size, keep_tail)
         q_group = Q[b, t, g * G:(g + 1) * G, :].astype(np.float64)
-        scores = block_scores(q_group, k_comp[b, g], own, scale)
-        sel = select_blocks(scores, own, top_k)
+        scores = block_scores(q_group, k_comp[b, g], n_cand, scale)
+        sel = select_in_frame(scores, n_cand, forced, top_k)
         out = attend_given_selection(q_group, K[b, g], V[b, g], sel, p, block_size, scale)
         result[(b, t, g)] = (sel, scores, out)
     return result
 
 
-def qsa_prefill(Q, K, V, block_size, top_k, scale=None, q_pos0=0):
+def qsa_prefill(Q, K, V, block_size, top_k, scale=None, q_pos0=0, keep_tail=False):
     """Causal QSA prefill: returns (out float64 ``[b][q_len][Hq][d]``, sel int32 ``[b][q_len][Hkv][k]``)."""
     b_n, q_len, n_q, d = Q.shape
     n_kv = K.shape[1]
     G = n_q // n_kv
-    res = qsa_rows(Q, K, V, block_size, top_k, scale, q_pos0)
+    res = qsa_rows(Q, K, V, block_size, top_k, scale, q_pos0, keep_tail=keep_tail)
     out = np.zeros((b_n, q_len, n_q, d), dtype=np.float64)
     sel = np.zeros((b_n, q_len, n_kv, top_k), dtype=np.int32)
     for (b, t, g), (s, _, o) in res.items():
@@ -184,10 +217,11 @@ def qsa_prefill(Q, K, V, block_size, top_k, scale=None, q_pos0=0):
     return out, sel
 
 
-def qsa_decode(q, K, V, kv_len, block_size, top_k, scale=None):
+def qsa_decode(q, K, V, kv_len, block_size, top_k, scale=None, keep_tail=False):
     """One decode step: ``q`` ``[b][Hq][d]`` at position ``kv_len-1`` over the first ``kv_len`` cached keys.
 
     Returns (out float64 ``[b][Hq][d]``, sel int32 ``[b][Hkv][k]``).
     """
-    out, sel = qsa_prefill(q[:, None], K[:, :, :kv_len], V[:, :, :kv_len], block_size, top_k, scale, q_pos0=kv_len - 1)
+    out, sel = qsa_prefill(q[:, None], K[:, :, :kv_len], V[:, :, :kv_len], block_size, top_k, scale,
+                           q_pos0=kv_len - 1, keep_tail=keep_tail)
     return out[:, 0], sel[:, 0]

@@ -49,6 +49,7 @@ class Workload:
     dtype: str  # "f32" or "bf16"
     sigma: float
     planted: int = 0
+    keep_tail: bool = False  # selection frame of the released budget (see the oracle)
 
     @property
     def q_len(self) -> int:
@@ -67,13 +68,18 @@ class Workload:
 
 
 # The five workloads: tiny fp32 prefill, bf16 decode at 32K, bf16 prefill at
-# 8K, batched bf16 decode at 128K with planted blocks, bf16 decode at 1M.
+# 8K, batched bf16 decode at 128K with planted blocks, bf16 decode at 1M; then
+# bf16 decode in the released budget regime at 256K.
 WORKLOADS = {
     "prefill_512_f32": Workload("prefill_512_f32", 1, "prefill", 1, 512, 2, 1, 64, 32, 4, "f32", 1.0),
     "decode_32k": Workload("decode_32k", 2, "decode", 1, 32768, 16, 2, 128, 64, 16, "bf16", 0.5),
     "prefill_8k": Workload("prefill_8k", 3, "prefill", 1, 8192, 16, 2, 128, 64, 16, "bf16", 0.5),
     "decode_b64_128k": Workload("decode_b64_128k", 4, "decode", 64, 131072, 16, 2, 128, 64, 16, "bf16", 0.5, planted=8),
     "decode_1m": Workload("decode_1m", 5, "decode", 1, 1048576, 16, 2, 128, 64, 32, "bf16", 0.5),
+    # the released budget regime: ratio 4, 2048-token budget (512 blocks + the
+    # partial-tail slot), 262144-token context = 65536 compressed blocks
+    "decode_256k_r4": Workload("decode_256k_r4", 6, "decode", 1, 262144, 16, 2, 128, 4, 513, "bf16", 0.5,
+                               keep_tail=True),
 }
 
 

@@ -35,8 +35,15 @@ def jaccard(a, b) -> float:
 
 
 def check_selection(sel_row, scores, own_block: int, top_k: int, rel_gap: float = REL_GAP) -> str:
+    """Validate one row's selection (default frame: own block forced, candidates below it)."""
+    return check_selection_frame(sel_row, scores, own_block, own_block, top_k, rel_gap)
+
+
+def check_selection_frame(sel_row, scores, n_cand: int, forced, top_k: int, rel_gap: float = REL_GAP) -> str:
     """Validate one row's selection against the oracle's float64 candidate scores.
 
+    ``n_cand`` candidates ``0 .. n_cand-1`` compete for ``min(top_k-1, n_cand)``
+    slots; ``forced`` (a block id, or None) must be kept, as the last entry.
     Returns ``"clear"`` (exact match required and found) or ``"ambiguous"``
     (boundary within the gap, selection valid); raises
     :class:`SelectionMismatch` otherwise.
@@ -48,18 +55,21 @@ def check_selection(sel_row, scores, own_block: int, top_k: int, rel_gap: float 
         raise SelectionMismatch(f"padding not at the tail: {sel}")
     if kept != sorted(set(kept)):
         raise SelectionMismatch(f"ids not strictly ascending: {sel}")
-    if own_block not in kept or kept[-1] != own_block:
-        raise SelectionMismatch(f"own block {own_block} missing or not last: {sel}")
-    scored = kept[:-1]
-    slots = min(top_k - 1, own_block)
+    if forced is not None:
+        if forced not in kept or kept[-1] != forced:
+            raise SelectionMismatch(f"forced block {forced} missing or not last: {sel}")
+        scored = kept[:-1]
+    else:
+        scored = kept
+    slots = min(top_k - 1, n_cand)
     if len(scored) != slots:
         raise SelectionMismatch(f"expected {slots} scored blocks, got {len(scored)}: {sel}")
-    if any(c < 0 or c >= own_block for c in scored):
+    if any(c < 0 or c >= n_cand for c in scored):
         raise SelectionMismatch(f"scored id out of range: {sel}")
-    if slots == own_block or slots == 0:
+    if slots == n_cand or slots == 0:
         return "clear"  # every candidate (or none) is kept: one valid answer
     scores = np.asarray(scores, dtype=np.float64)
-    order = sorted(range(own_block), key=lambda c: (-scores[c], c))
+    order = sorted(range(n_cand), key=lambda c: (-scores[c], c))
     expect = sorted(order[:slots])
     s_m, s_m1 = scores[order[slots - 1]], scores[order[slots]]
     denom = max(abs(s_m), abs(s_m1))
@@ -71,7 +81,7 @@ def check_selection(sel_row, scores, own_block: int, top_k: int, rel_gap: float 
         return "clear"
     tol = rel_gap * denom
     chosen = set(scored)
-    for c in range(own_block):
+    for c in range(n_cand):
         if c in chosen and scores[c] < s_m - tol:
             raise SelectionMismatch(f"kept block {c} scores {scores[c]} below cutoff {s_m}")
         if c not in chosen and scores[c] > s_m1 + tol:

@@ -126,6 +126,100 @@ def test_brute_force_tiny(N, Bs, k):
                         np.testing.assert_allclose(out[bb, t, g * G + j], ref, rtol=1e-12, atol=1e-13)
 
 
+# ------------------------------------------- the keep_tail frame, by brute force
+
+def brute_select_tail(scores, p, Bs, top_k):
+    """Released-budget frame from first principles: blocks whose last position is at most p compete."""
+    complete = [c for c in range(p // Bs + 1) if (c + 1) * Bs - 1 <= p]
+    slots = min(top_k - 1, len(complete))
+
+    def beats(x, y):
+        return scores[x] > scores[y] or (scores[x] == scores[y] and x < y)
+
+    valid = [sub for sub in itertools.combinations(complete, slots)
+             if all(beats(x, y) for x in sub for y in complete if y not in sub)]
+    assert len(valid) == 1
+    kept = list(valid[0])
+    if (p + 1) % Bs:  # positions past the last complete block: their block is always kept
+        kept.append(p // Bs)
+    kept = sorted(kept)
+    return kept + [-1] * (top_k - len(kept))
+
+
+def brute_attend_tail(q, K, V, sel, p, Bs, scale):
+    """Logits of every position <= p that lies in a selected block or past the last complete block."""
+    last_complete_end = (p + 1) // Bs * Bs
+    logits = np.full(K.shape[0], -np.inf)
+    for t in range(p + 1):
+        if t // Bs in sel or t >= last_complete_end:
+            logits[t] = scale * sum(float(q[e]) * float(K[t, e]) for e in range(K.shape[1]))
+    w = np.exp(logits - logits.max())
+    return (w[:, None] * V.astype(np.float64)).sum(0) / w.sum()
+
+
+def test_keep_tail_needs_two_slots():
+    """With top_k = 1 the keep_tail frame would leave a complete-block row with nothing to attend."""
+    with pytest.raises(ValueError):
+        O.select_in_frame(np.zeros(4), 4, None, 1)
+
+
+@pytest.mark.parametrize("N,Bs,k", [(N, Bs, k) for N in (9, 24) for Bs in (1, 2, 4) for k in (2, 3, 5)])
+def test_brute_force_tiny_keep_tail(N, Bs, k):
+    """The keep_tail frame equals a brute force written from its definition, ties included."""
+    b, hq, hkv, d = 1, 4, 2, 4
+    G = hq // hkv
+    for seed in range(8):
+        rng = np.random.default_rng([seed, N, Bs, k, 7])
+        Q, K, V = _tiny_inputs(rng, b, N, hq, hkv, d, integer=(seed % 2 == 0))
+        scale = O.default_scale(d)
+        kc = O.compress_keys(K, Bs)
+        out, sel = O.qsa_prefill(Q, K, V, Bs, k, keep_tail=True)
+        for t in range(N):
+            n_complete = (t + 1) // Bs
+            for g in range(hkv):
+                qg = Q[0, t, g * G:(g + 1) * G]
+                sc = brute_scores(qg, kc[0, g], n_complete, scale)
+                if math.comb(n_complete, min(k - 1, n_complete)) <= 5000:
+                    assert list(sel[0, t, g]) == brute_select_tail(sc, t, Bs, k)
+                for j in range(G):
+                    ref = brute_attend_tail(qg[j], K[0, g], V[0, g], list(sel[0, t, g]), t, Bs, scale)
+                    np.testing.assert_allclose(out[0, t, g * G + j], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_keep_tail_matches_default_while_own_block_fills():
+    """The two frames differ only for rows whose own block is complete ((p + 1) % Bs == 0)."""
+    rng = np.random.default_rng(11)
+    N, Bs, k = 120, 4, 6
+    Q = rng.standard_normal((1, N, 4, 8))
+    K = rng.standard_normal((1, 2, N, 8))
+    V = rng.standard_normal((1, 2, N, 8))
+    out_d, sel_d = O.qsa_prefill(Q, K, V, Bs, k)
+    out_t, sel_t = O.qsa_prefill(Q, K, V, Bs, k, keep_tail=True)
+    filling = np.array([(t + 1) % Bs != 0 for t in range(N)])
+    np.testing.assert_array_equal(sel_d[0, filling], sel_t[0, filling])
+    np.testing.assert_array_equal(out_d[0, filling], out_t[0, filling])
+    assert (sel_d[0, ~filling] != sel_t[0, ~filling]).any()
+
+
+def test_keep_tail_drops_a_complete_own_block():
+    """A complete own block that scores lowest is not visible, not even to its last query (SDPA mask)."""
+    d, Bs = 4, 2
+    Q = np.zeros((1, 4, 1, d))
+    Q[0, :, 0, 0] = 1.0
+    K = np.zeros((1, 1, 4, d))
+    K[0, 0, :2, 0] = 2.0    # block 0 points along the query
+    K[0, 0, 2:, 0] = -2.0   # block 1 points away from it
+    K[0, 0, :, 1] = [0.3, -0.1, 0.7, 0.2]
+    V = np.arange(16, dtype=np.float64).reshape(1, 1, 4, d)
+    out, sel = O.qsa_prefill(Q, K, V, Bs, 2, keep_tail=True)
+    assert list(sel[0, 3, 0]) == [0, -1]
+    mask = np.array([[True, True, False, False]])
+    ref = _sdpa(Q[:, 3:4], K, V, O.default_scale(d), mask=mask)
+    np.testing.assert_allclose(out[0, 3], ref[0, 0], rtol=0, atol=1e-12)
+    _, sel_default = O.qsa_prefill(Q, K, V, Bs, 2)
+    assert list(sel_default[0, 3, 0]) == [0, 1]  # the default frame keeps it
+
+
 def test_tie_break_smaller_index():
     scores = np.array([1.0, 3.0, 3.0, 2.0, 3.0])
     assert O.select_blocks(scores, 5, 3) == [1, 2, 5]
@@ -167,6 +261,18 @@ def test_dense_equivalence_below_budget(N, Bs, k, G):
     for t in range(N):
         own = t // Bs
         assert list(sel[0, t, 0][: own + 1]) == list(range(own + 1))
+
+
+@pytest.mark.parametrize("N,Bs,k", [(64, 4, 17), (99, 8, 13), (50, 1, 51)])
+def test_dense_equivalence_keep_tail(N, Bs, k):
+    """keep_tail: with top_k - 1 slots for every complete block, sparse equals dense causal attention."""
+    assert k - 1 >= N // Bs
+    rng = np.random.default_rng(N * k)
+    Q = rng.standard_normal((1, N, 4, 16))
+    K = rng.standard_normal((1, 2, N, 16))
+    V = rng.standard_normal((1, 2, N, 16))
+    out, _ = O.qsa_prefill(Q, K, V, Bs, k, keep_tail=True)
+    np.testing.assert_allclose(out, _sdpa(Q, K, V, O.default_scale(16), causal=True), rtol=0, atol=1e-12)
 
 
 def test_dense_rows_of_sparse_config():
@@ -248,6 +354,30 @@ def test_pages_released_regime():
     assert max(w for p, w in widths.items() if p % Bs <= Bs - 2) == bound
     assert len(O.block_scores(np.zeros((1, 1)), np.zeros((gold["compressed_blocks"], 1)),
                               (n_ctx - 1) // Bs, 1.0)) == gold["compressed_blocks"] - 1
+
+
+def test_pages_released_regime_keep_tail():
+    """keep_tail reproduces the printed bound exactly: width <= min(n_kv, 2051) at every position,
+    dense up to 2051 cached positions, 2051 reached, and all 65536 blocks compete at 262144."""
+    with open(os.path.join(GOLDEN, "pages_regime.json")) as f:
+        gold = json.load(f)
+    Bs = gold["compression_ratio"]
+    k = gold["indexer_budget_tokens"] // Bs + 1  # budget blocks + the slot of the partial tail
+    bound = gold["visible_width_bound"]
+    n_ctx = gold["context_tokens"]
+    rng = np.random.default_rng(1)
+    widest = 0
+    for p in list(range(0, 2100)) + list(range(4090, 4110)) + list(range(n_ctx - 8, n_ctx)):
+        n_kv = p + 1
+        n_cand, forced = O.selection_frame(p, Bs, keep_tail=True)
+        sel = O.select_in_frame(rng.standard_normal(n_cand), n_cand, forced, k)
+        width = len(O.visible_positions(sel, p, Bs))
+        assert width <= min(n_kv, bound)
+        if n_kv <= bound:
+            assert width == n_kv  # below the budget nothing can be discarded
+        widest = max(widest, width)
+    assert widest == bound
+    assert O.selection_frame(n_ctx - 1, Bs, keep_tail=True) == (gold["compressed_blocks"], None)
 
 
 # ------------------------------------------------------------ invariances
