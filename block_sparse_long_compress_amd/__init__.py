@@ -1,7 +1,7 @@
 """Qwen Sparse Attention (QSA) for AMD MI355X (gfx950).
 
 Keys are mean-pooled into one compressed key per block, every (token, KV
-head) scores the compressed blocks and keeps its top-k (own block included),
+head) scores the compressed blocks and keeps its top-k (the always-kept block included),
 and exact softmax attention runs over the kept blocks only. All steps run in
 the hand-written HIP kernels of ``lib/libqsa.so`` behind the C ABI of
 ``include/qsa.h``; this package is the Python binding (argument marshalling)
@@ -34,12 +34,13 @@ from .binding import (  # noqa: F401
 )
 
 
-def shape_for(q: torch.Tensor, k: torch.Tensor, block_size: int, top_k: int, scale: float = 0.0) -> QsaShape:
+def shape_for(q: torch.Tensor, k: torch.Tensor, block_size: int, top_k: int, scale: float = 0.0,
+              keep_tail: bool = False) -> QsaShape:
     """ABI shape from Q ``[b][q_len][Hq][d]`` (or ``[b][Hq][d]``) and K ``[b][Hkv][cap][d]``."""
-    return make_shape(k.shape[0], q.shape[-2], k.shape[1], k.shape[3], block_size, top_k, q.dtype, scale)
+    return make_shape(k.shape[0], q.shape[-2], k.shape[1], k.shape[3], block_size, top_k, q.dtype, scale, keep_tail)
 
 
-def prefill(q, k, v, block_size, top_k, q_pos0=0, scale=0.0, k_comp=None, with_scores=False):
+def prefill(q, k, v, block_size, top_k, q_pos0=0, scale=0.0, k_comp=None, with_scores=False, keep_tail=False):
     """Compress, select and attend for ``q_len`` query rows at positions ``q_pos0 ..``.
 
     Returns ``(out, sel, k_comp[, sel_scores])``; ``k_comp`` is computed for
@@ -48,7 +49,7 @@ def prefill(q, k, v, block_size, top_k, q_pos0=0, scale=0.0, k_comp=None, with_s
     b, q_len, hq, d = q.shape
     hkv, cap = k.shape[1], k.shape[2]
     kv_len = q_pos0 + q_len
-    shape = shape_for(q, k, block_size, top_k, scale)
+    shape = shape_for(q, k, block_size, top_k, scale, keep_tail)
     if k_comp is None:
         k_comp = torch.empty(b, hkv, cap // block_size, d, dtype=torch.float32, device=q.device)
         qsa_compress_keys(shape, k, kv_len, k_comp)
@@ -60,14 +61,14 @@ def prefill(q, k, v, block_size, top_k, q_pos0=0, scale=0.0, k_comp=None, with_s
     return (out, sel, k_comp, scores) if with_scores else (out, sel, k_comp)
 
 
-def decode(q, k, v, kv_len, block_size, top_k, k_comp, scale=0.0, with_scores=False):
+def decode(q, k, v, kv_len, block_size, top_k, k_comp, scale=0.0, with_scores=False, keep_tail=False):
     """One decode step for ``q`` ``[b][Hq][d]`` at position ``kv_len - 1`` given compressed keys.
 
     Returns ``(out, sel[, sel_scores])`` with ``sel`` ``[b][Hkv][k]``.
     """
     b, hq, d = q.shape
     hkv, cap = k.shape[1], k.shape[2]
-    shape = shape_for(q, k, block_size, top_k, scale)
+    shape = shape_for(q, k, block_size, top_k, scale, keep_tail)
     sel = torch.empty(b, hkv, top_k, dtype=torch.int32, device=q.device)
     scores = torch.empty(b, hkv, top_k, dtype=torch.float32, device=q.device) if with_scores else None
     qsa_score_select(shape, q.view(b, 1, hq, d), kv_len - 1, k_comp, kv_len, cap, sel, scores)

@@ -40,6 +40,7 @@ class QsaShape(ctypes.Structure):
         ("top_k", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("keep_tail", ctypes.c_int32),
     ]
 
 
@@ -70,11 +71,12 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 
-def make_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, top_k, dtype, scale=0.0) -> QsaShape:
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, top_k, dtype, scale=0.0,
+               keep_tail=False) -> QsaShape:
     """Build the ABI shape struct; ``dtype`` is a torch dtype or QSA_F32/QSA_BF16."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: QSA_F32, torch.bfloat16: QSA_BF16}[dtype]
-    return QsaShape(batch, n_q_heads, n_kv_heads, head_dim, block_size, top_k, dtype, float(scale))
+    return QsaShape(batch, n_q_heads, n_kv_heads, head_dim, block_size, top_k, dtype, float(scale), int(keep_tail))
 
 
 def abi_version() -> int:

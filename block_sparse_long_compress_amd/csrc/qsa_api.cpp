@@ -32,10 +32,12 @@ qsa_status check_shape(const qsa_shape* sh, Dims* out) {
   if (sh->n_q_heads % sh->n_kv_heads != 0) return QSA_ERR_INVALID;
   if (sh->dtype != QSA_F32 && sh->dtype != QSA_BF16) return QSA_ERR_INVALID;
   if (!std::isfinite(sh->scale) || sh->scale < 0.f) return QSA_ERR_INVALID;
+  if (sh->keep_tail != 0 && sh->keep_tail != 1) return QSA_ERR_INVALID;
+  if (sh->keep_tail && sh->top_k < 2) return QSA_ERR_INVALID;  // a complete-block row would see nothing
   const int G = sh->n_q_heads / sh->n_kv_heads;
   if (sh->head_dim != 64 && sh->head_dim != 128) return QSA_ERR_UNSUPPORTED;
-  if (!pow2_in(sh->block_size, 32, 128)) return QSA_ERR_UNSUPPORTED;
-  if (sh->top_k > 64) return QSA_ERR_UNSUPPORTED;
+  if (!pow2_in(sh->block_size, 4, 128)) return QSA_ERR_UNSUPPORTED;
+  if (sh->top_k > qsa::kMaxTopKLarge) return QSA_ERR_UNSUPPORTED;
   if (!pow2_in(G, 1, 16)) return QSA_ERR_UNSUPPORTED;
   if (sh->batch > 65535 || sh->n_kv_heads > 65535) return QSA_ERR_UNSUPPORTED;
   out->batch = sh->batch;
@@ -47,6 +49,7 @@ qsa_status check_shape(const qsa_shape* sh, Dims* out) {
   out->top_k = sh->top_k;
   out->dtype = sh->dtype;
   out->scale = sh->scale == 0.f ? (float)(1.0 / std::sqrt((double)sh->head_dim)) : sh->scale;
+  out->keep_tail = sh->keep_tail;
   return QSA_OK;
 }
 
@@ -55,6 +58,9 @@ constexpr int64_t kMaxPositions = int64_t(1) << 31;
 
 qsa_status check_prefill_limits(const Dims& s, int64_t q_len, int64_t q_pos0) {
   if (q_len > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  // the bf16 MFMA kernel stages whole 32-key units of one block and holds a
+  // row's selection in one 64-bit token mask
+  if (s.dtype == QSA_BF16 && (s.bs < 32 || s.top_k > 64)) return QSA_ERR_UNSUPPORTED;
   if (s.dtype == QSA_BF16 && qsa::prefill_smem_bytes(s, q_len, q_pos0) > kMaxLds) return QSA_ERR_UNSUPPORTED;
   return QSA_OK;
 }
@@ -126,8 +132,9 @@ qsa_status qsa_score_select(const qsa_shape* shape, const void* q, int64_t q_len
   if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
   if (q_len <= 0 || q_pos0 < 0 || kv_len != q_pos0 + q_len || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
   // k_comp is read only for candidate blocks, which exist once a row sits past the first block
-  if ((kv_len - 1) / s.bs > 0 && (!k_comp || !aligned16(k_comp))) return QSA_ERR_INVALID;
+  if (qsa::max_candidates(s, kv_len) > 0 && (!k_comp || !aligned16(k_comp))) return QSA_ERR_INVALID;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
   const qsa::SelectPlan plan = qsa::plan_select(s, q_len, q_pos0);
   const int64_t grid = plan.tiled ? (q_len + 15) / 16 : (int64_t)s.batch * q_len * s.hkv * plan.n_chunks;
   if (grid > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;

@@ -4,7 +4,11 @@
 // attention restricted to the cells the selector returned).
 //
 // bf16 inputs, bf16 MFMA (v_mfma_f32_16x16x32_bf16), float32 softmax and
-// accumulation. Work unit = 32 consecutive keys of one selected block.
+// accumulation. Work unit = 32 keys: 32 consecutive keys of one selected
+// block, or for blocks shorter than 32 keys (Bs = 4, 8, 16) the keys of
+// 32/Bs consecutive entries of the selection list, each row addressed on
+// its own (the position of every key row is computed once per unit and
+// shared across lanes with ds_bpermute).
 // Per unit a wave computes S^T = K Q^T with the keys as the 16-row M operand
 // and the G query heads of the KV head as the N columns (G <= 16; columns
 // >= G are zero queries and are ignored), keeps an online softmax per column
@@ -40,7 +44,7 @@ struct DecodeSmem {
   static constexpr int kBytes = kStage > kComb ? kStage : kComb;
 };
 
-template <int D>
+template <int D, bool GATHER>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, const int32_t* __restrict__ sel,
                                                           uint16_t* __restrict__ out, float* __restrict__ part,
@@ -59,10 +63,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
   const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
   const int lg = lane / 16, col = lane % 16;
   const int64_t p = kv_len - 1;
-  const int upb = bs / kUnit;
+  const int upb = GATHER ? 1 : bs / kUnit;   // units per block
+  const int bpu = GATHER ? kUnit / bs : 1;   // blocks per unit
   const int e0 = split * bpw;
   const int e1 = e0 + bpw < top_k ? e0 + bpw : top_k;
-  const int n_units = (e1 - e0) * upb;
+  const int n_e = e1 - e0;
+  const int n_units = GATHER ? (n_e + bpu - 1) / bpu : n_e * upb;
   const int32_t* sel_row = sel + row * top_k;
   const int64_t kv_off = ((int64_t)b * hkv + g) * kv_cap;
 
@@ -87,39 +93,70 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
   struct Unit {
     u32x4_t kf[2][KS];
     u32x4_t vr[VCH];
-    int64_t key0;
+    int64_t key0;  // contiguous units: position of key row 0
+    int mpos[2];   // gathered units: position of key row 16*st + 4*lg (-1: not visible)
     bool ok;
   };
   auto fetch = [&](int idx, Unit& u) {
     u.ok = false;
     if (idx >= n_units) return;
-    const int c = __builtin_amdgcn_readlane(sel_mine, idx / upb);
-    if (c < 0) return;
-    u.key0 = (int64_t)c * bs + (int64_t)(idx % upb) * kUnit;
-    if (u.key0 > p) return;
-    u.ok = true;
-    const uint16_t* kb = k + (kv_off + u.key0) * D;
-    const uint16_t* vb = v + (kv_off + u.key0) * D;
+    if constexpr (GATHER) {
+      // Row r of the unit is key r % Bs of slice entry idx*bpu + r/Bs; lanes
+      // r and r + 32 compute it, every other lane fetches it with bpermute.
+      // idx*bpu + r/Bs < 64: the slice holds at most 64 entries and bpu
+      // divides 64.
+      const int r = lane & (kUnit - 1);
+      const int slot = idx * bpu + r / bs;
+      const int c = __builtin_amdgcn_ds_bpermute(slot << 2, sel_mine);
+      const int64_t pos = (int64_t)c * bs + (r % bs);
+      const int rowpos = (slot < n_e && c >= 0 && pos <= p) ? (int)pos : -1;
+      if (__ballot(rowpos >= 0) == 0) return;
+      u.ok = true;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int kr = 16 * st + col;
-      const bool ok = u.key0 + kr <= p;
+      for (int st = 0; st < 2; ++st) {
+        const int kp = __builtin_amdgcn_ds_bpermute((16 * st + col) << 2, rowpos);
+        u.mpos[st] = __builtin_amdgcn_ds_bpermute((16 * st + 4 * lg) << 2, rowpos);
+        const uint16_t* kb = k + (kv_off + (kp >= 0 ? kp : 0)) * D;
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        u.kf[st][s] = ok ? *reinterpret_cast<const u32x4_t*>(kb + (int64_t)kr * D + 32 * s + 8 * lg)
-                         : u32x4_t{0u, 0u, 0u, 0u};
-    }
+        for (int s = 0; s < KS; ++s)
+          u.kf[st][s] = kp >= 0 ? *reinterpret_cast<const u32x4_t*>(kb + 32 * s + 8 * lg) : u32x4_t{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int ci = lane + kWave * j;
-      const int r = ci / (D / 8), c8 = ci % (D / 8);
-      u.vr[j] = u.key0 + r <= p ? *reinterpret_cast<const u32x4_t*>(vb + (int64_t)r * D + 8 * c8)
-                                : u32x4_t{0u, 0u, 0u, 0u};
+      for (int j = 0; j < VCH; ++j) {
+        const int ci = lane + kWave * j;
+        const int rr = ci / (D / 8), c8 = ci % (D / 8);
+        const int vp = __builtin_amdgcn_ds_bpermute(rr << 2, rowpos);
+        u.vr[j] = vp >= 0 ? *reinterpret_cast<const u32x4_t*>(v + (kv_off + (vp >= 0 ? vp : 0)) * D + 8 * c8)
+                          : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    } else {
+      const int c = __builtin_amdgcn_readlane(sel_mine, idx / upb);
+      if (c < 0) return;
+      u.key0 = (int64_t)c * bs + (int64_t)(idx % upb) * kUnit;
+      if (u.key0 > p) return;
+      u.ok = true;
+      const uint16_t* kb = k + (kv_off + u.key0) * D;
+      const uint16_t* vb = v + (kv_off + u.key0) * D;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int kr = 16 * st + col;
+        const bool ok = u.key0 + kr <= p;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          u.kf[st][s] = ok ? *reinterpret_cast<const u32x4_t*>(kb + (int64_t)kr * D + 32 * s + 8 * lg)
+                           : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int ci = lane + kWave * j;
+        const int r = ci / (D / 8), c8 = ci % (D / 8);
+        u.vr[j] = u.key0 + r <= p ? *reinterpret_cast<const u32x4_t*>(vb + (int64_t)r * D + 8 * c8)
+                                  : u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
   };
   auto consume = [&](const Unit& u) {
     if (!u.ok) return;
-    const int64_t key0 = u.key0;
 #pragma unroll
     for (int j = 0; j < VCH; ++j) {
       const int ci = lane + kWave * j;
@@ -140,12 +177,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = key0 + 16 * st + 4 * lg + i <= p;
+        // rows 16*st + 4*lg + i (i < 4) lie in one block of >= 4 keys
+        const bool ok = GATHER ? (u.mpos[st] >= 0 && u.mpos[st] + i <= p) : (u.key0 + 16 * st + 4 * lg + i <= p);
         x[st][i] = ok ? sacc[st][i] * scale_log2 : -__builtin_inff();
         mloc = fmaxf(mloc, x[st][i]);
       }
     mloc = max_col4(mloc);
-    const float m_new = fmaxf(m_run, mloc);  // finite: key0 <= p is visible
+    const float m_new = fmaxf(m_run, mloc);  // finite: the unit has a visible key
     if (__ballot(m_new > m_run) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -281,11 +319,11 @@ hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const 
                     int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* ws, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const float scale_log2 = s.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((decode_attn_kernel<D>), dim3((unsigned)(rows * plan.n_split)), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), static_cast<float*>(ws),
-                     kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, scale_log2, plan.blocks_per_wg,
-                     plan.n_split);
+  auto kern = s.bs < kUnit ? decode_attn_kernel<D, true> : decode_attn_kernel<D, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rows * plan.n_split)), dim3(256), 0, st, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sel,
+                     static_cast<uint16_t*>(out), static_cast<float*>(ws), kv_len, kv_cap, s.hq, s.hkv, s.group,
+                     s.bs, s.top_k, scale_log2, plan.blocks_per_wg, plan.n_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_split == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(rows * s.group)), dim3(D), 0, st,
@@ -300,10 +338,11 @@ DecodePlan plan_decode(const Dims& s, int64_t kv_len) {
   DecodePlan p{};
   const int64_t rows = (int64_t)s.batch * s.hkv;
   // Smallest slices that still give every wave a unit, grown while the grid
-  // stays above ~512 workgroups (fewer partial states to merge).
+  // stays above ~512 workgroups (fewer partial states to merge). A slice
+  // holds at most 64 entries (one per lane).
   int bpw = (4 * kUnit + s.bs - 1) / s.bs;  // blocks giving one unit per wave
   if (bpw < 1) bpw = 1;
-  while (bpw < s.top_k && rows * ((s.top_k + 2 * bpw - 1) / (2 * bpw)) >= 512) bpw *= 2;
+  while (2 * bpw <= kWave && bpw < s.top_k && rows * ((s.top_k + 2 * bpw - 1) / (2 * bpw)) >= 512) bpw *= 2;
   if (bpw > s.top_k) bpw = s.top_k;
   p.blocks_per_wg = bpw;
   p.n_split = (s.top_k + bpw - 1) / bpw;

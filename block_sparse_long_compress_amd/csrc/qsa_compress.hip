@@ -22,8 +22,10 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ k, 
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
   constexpr int LPR = D / VEC;         // lanes covering one key row
   constexpr int RPL = kWave / LPR;     // rows per wave-wide load
-  constexpr int NLOAD = BS / RPL;      // loads per lane
-  static_assert(RPL >= 1 && NLOAD >= 1, "shape");
+  // loads per lane; a block shorter than one wave-wide load leaves the lanes
+  // of its missing rows idle (they add zeros)
+  constexpr int NLOAD = BS >= RPL ? BS / RPL : 1;
+  static_assert(RPL >= 1, "shape");
 
   const int64_t item = (int64_t)blockIdx.x * 4 + wave_id();
   if (item >= n_items) return;
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ k, 
   const int row0 = lane / LPR;
   const int col = (lane % LPR) * VEC;
 
-  const T* src = k + (bg * kv_cap + c * BS + row0) * D + col;
+  const T* src = k + (bg * kv_cap + c * BS + (row0 < BS ? row0 : 0)) * D + col;
   constexpr int BATCH = NLOAD < 16 ? NLOAD : 16;  // loads kept in flight together
   float acc[VEC];
 #pragma unroll
@@ -43,7 +45,8 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ k, 
     u32x4_t raw[BATCH];
 #pragma unroll
     for (int j = 0; j < BATCH; ++j)
-      raw[j] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)(j0 + j) * RPL * D);
+      raw[j] = row0 < BS ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)(j0 + j) * RPL * D)
+                         : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       if constexpr (sizeof(T) == 2) {
@@ -80,6 +83,18 @@ hipError_t launch_d(int bs, const void* k, float* k_comp, int64_t kv_cap, int64_
   const int64_t grid = (n_items + 3) / 4;
   const T* kp = static_cast<const T*>(k);
   switch (bs) {
+    case 4:
+      hipLaunchKernelGGL((compress_kernel<T, D, 4>), dim3(grid), dim3(256), 0, st, kp, k_comp, kv_cap, nb_cap,
+                         blk_begin, n_blk, n_items);
+      break;
+    case 8:
+      hipLaunchKernelGGL((compress_kernel<T, D, 8>), dim3(grid), dim3(256), 0, st, kp, k_comp, kv_cap, nb_cap,
+                         blk_begin, n_blk, n_items);
+      break;
+    case 16:
+      hipLaunchKernelGGL((compress_kernel<T, D, 16>), dim3(grid), dim3(256), 0, st, kp, k_comp, kv_cap, nb_cap,
+                         blk_begin, n_blk, n_items);
+      break;
     case 32:
       hipLaunchKernelGGL((compress_kernel<T, D, 32>), dim3(grid), dim3(256), 0, st, kp, k_comp, kv_cap, nb_cap,
                          blk_begin, n_blk, n_items);

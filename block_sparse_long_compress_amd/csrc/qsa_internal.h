@@ -10,7 +10,8 @@ namespace qsa {
 
 struct Dims {
   int batch, hq, hkv, group, d, bs, top_k, dtype;
-  float scale;  // resolved (never 0)
+  float scale;     // resolved (never 0)
+  int keep_tail;   // selection frame: 0 = own block kept, 1 = only the partial tail kept
 };
 
 // Block compression, blocks [blk_begin, blk_end) of every (b, g).
@@ -20,10 +21,17 @@ hipError_t launch_compress(const Dims& s, const void* k, int64_t kv_cap, int64_t
 // Selection ------------------------------------------------------------------
 struct SelectPlan {
   bool tiled;          // prefill-style tile path (rows share candidates)
+  bool large;          // top_k > 64: score pass + per-row radix select
   int chunk;           // split path: candidates per chunk (multiple of 64)
-  int64_t n_chunks;    // split path: chunks per row
+  int64_t n_chunks;    // split / large path: chunks per row (the longest row's)
   size_t ws_bytes;
 };
+// Largest top_k of the large-k selection path (its candidate pool fits LDS).
+constexpr int kMaxTopKLarge = 513;
+// Largest candidate count per row of the large-k selection path.
+constexpr int64_t kMaxCandLarge = 65536;
+// Candidate blocks of the row at position kv_len - 1 (the most of any row).
+int64_t max_candidates(const Dims& s, int64_t kv_len);
 SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0);
 hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,
                          const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,

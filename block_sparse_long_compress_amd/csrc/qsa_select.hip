@@ -5,11 +5,16 @@
 //
 // Score of candidate c for (token, KV head g): scale * <qbar, kc[c]> with
 // qbar the float32 sum of the group's G query heads (equal to the sum of the
-// per-head scores). Selection keeps the query's own block plus the
-// min(k-1, i) best candidates, ranked by the 64-bit key of qsa_device.h
-// (score descending, id ascending), and writes ids ascending.
+// per-head scores). A row's frame gives its candidates and its forced block:
+// by default the complete blocks before the own block i = p / Bs, with block
+// i forced; in the keep-tail frame (the released budget of the same page,
+// visible width bounded by budget + ratio - 1) all (p+1)/Bs complete blocks,
+// with the block of the positions past them forced when there are such
+// positions. Selection keeps the forced block plus the min(k-1, n_cand) best
+// candidates, ranked by the 64-bit key of qsa_device.h (score descending, id
+// ascending), and writes ids ascending.
 //
-// Two paths:
+// Three paths:
 //  * tile path (many query rows, prefill): a workgroup takes 16 consecutive
 //    rows of one (b, g), which share the candidate prefix. Candidate chunks
 //    of 64 compressed keys are staged in LDS and scored with fp32 MFMA
@@ -25,25 +30,51 @@
 //    kernel reduces the lists of a row, skipping every key below the best
 //    chunk-local cutoff (a valid lower bound of the row's cutoff); when all
 //    the lists of a row hold at most 256 keys, one wave takes them at once.
+//  * large path (k > 64, the released budget of 512 blocks): a score pass
+//    writes every candidate's score and, per chunk of 256 candidates, the
+//    chunk's 16 best keys in order; one workgroup per row then finds the
+//    cutoff by radix selection over the union of those lists, re-expands the
+//    few chunks whose 16th key still reaches the cutoff (only they can hide
+//    more kept keys), and emits the kept ids in ascending order straight from
+//    an LDS bitmap of the candidates.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
+// Candidates 0 .. n_cand-1 and the always-kept block (-1: none) of a row
+// whose query sits at absolute position p.
+struct Frame {
+  int n_cand;
+  int forced;
+};
+__device__ __forceinline__ Frame row_frame(int64_t p, int bs, int keep_tail) {
+  if (!keep_tail) {
+    const int own = (int)(p / bs);
+    return Frame{own, own};
+  }
+  const int n = (int)((p + 1) / bs);
+  return Frame{n, ((p + 1) % bs) ? n : -1};
+}
+__device__ __forceinline__ int frame_slots(const Frame& f, int top_k) {
+  return f.n_cand < top_k - 1 ? f.n_cand : top_k - 1;
+}
+
 // Write one row's selection from the kept keys held one per lane (lanes <
-// slots valid, any order): ids ascending, own block last, -1 padding.
-__device__ void finalize_row(uint64_t cur, int slots, int own, int top_k, int32_t* sel_row, float* score_row) {
+// slots valid, any order): ids ascending, forced block last, -1 padding.
+__device__ void finalize_row(uint64_t cur, int slots, int forced, int top_k, int32_t* sel_row, float* score_row) {
   const int lane = lane_id();
-  int id = lane < slots ? key_id(cur) : own;
+  const int n_real = slots + (forced >= 0 ? 1 : 0);
+  int id = lane < slots ? key_id(cur) : forced;
   float sc = lane < slots ? key_score(cur) : __builtin_inff();
-  // Sort lanes 0..slots by ascending id: descending on the complemented id,
-  // with the smallest network that holds slots + 1 entries.
-  uint64_t k2 = lane <= slots ? (((uint64_t)(0xFFFFFFFFu - (uint32_t)id) << 32) | __float_as_uint(sc)) : 0ull;
-  if (slots < 16) k2 = wave_sort_desc_n<16>(k2);
-  else if (slots < 32) k2 = wave_sort_desc_n<32>(k2);
+  // Sort the n_real entries by ascending id: descending on the complemented
+  // id, with the smallest network that holds them.
+  uint64_t k2 = lane < n_real ? (((uint64_t)(0xFFFFFFFFu - (uint32_t)id) << 32) | __float_as_uint(sc)) : 0ull;
+  if (n_real <= 16) k2 = wave_sort_desc_n<16>(k2);
+  else if (n_real <= 32) k2 = wave_sort_desc_n<32>(k2);
   else k2 = wave_sort_desc_n<64>(k2);
-  const bool real = lane <= slots;
+  const bool real = lane < n_real;
   const int out_id = real ? (int)(0xFFFFFFFFu - (uint32_t)(k2 >> 32)) : -1;
   const float out_sc = real ? __uint_as_float((uint32_t)k2) : -__builtin_inff();
   if (lane < top_k) {
@@ -77,7 +108,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ q, const float* __restrict__ k_comp,
                                                           int32_t* __restrict__ sel, float* __restrict__ sel_scores,
                                                           int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
-                                                          int hkv, int G, int bs, int top_k, float scale) {
+                                                          int hkv, int G, int bs, int top_k, float scale,
+                                                          int keep_tail) {
   constexpr int QP = D + 4;  // padded row strides (floats): conflict-free 16-byte reads
   constexpr int SPAN = kTileCands * kTilePasses;
   __shared__ float qbar[kTileRows][QP];
@@ -98,13 +130,14 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
     *reinterpret_cast<f32x4_t*>(&qbar[r][e4]) = v;
   }
 
-  const int64_t own_last = (q_pos0 + t0 + rows - 1) / bs;  // candidates of every row are < own_last
+  // candidates of every row are below the last row's candidate count
+  const int64_t cand_end = row_frame(q_pos0 + t0 + rows - 1, bs, keep_tail).n_cand;
   const float* kc_src = k_comp + ((b * hkv + g) * nb_cap) * D;
   TopSet set[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) set[rr] = TopSet{0ull, 0, 0ull};
 
-  for (int64_t c0 = 0; c0 < own_last; c0 += SPAN) {
+  for (int64_t c0 = 0; c0 < cand_end; c0 += SPAN) {
     // score SPAN candidates for all 16 rows, one staged pass of 64 at a time
 #pragma unroll
     for (int pass = 0; pass < kTilePasses; ++pass) {
@@ -113,7 +146,7 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
       for (int idx = tid; idx < kTileCands * D / 4; idx += 256) {
         const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
         f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-        if (p0 + r < own_last) v = *reinterpret_cast<const f32x4_t*>(kc_src + (p0 + r) * D + e4);
+        if (p0 + r < cand_end) v = *reinterpret_cast<const f32x4_t*>(kc_src + (p0 + r) * D + e4);
         *reinterpret_cast<f32x4_t*>(&kc[r][e4]) = v;
       }
       __syncthreads();
@@ -134,14 +167,14 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
     for (int rr = 0; rr < 4; ++rr) {
       const int r = 4 * w + rr;
       if (r >= rows) continue;
-      const int64_t own = (q_pos0 + t0 + r) / bs;
-      const int slots = own < top_k - 1 ? (int)own : top_k - 1;
+      const Frame fr = row_frame(q_pos0 + t0 + r, bs, keep_tail);
+      const int slots = frame_slots(fr, top_k);
       if (slots == 0) continue;
       uint64_t fresh[kTilePasses];
 #pragma unroll
       for (int pass = 0; pass < kTilePasses; ++pass) {
         const int64_t cand = c0 + pass * kTileCands + lane;
-        fresh[pass] = cand < own ? make_key(sc[r][pass * kTileCands + lane], (int)cand) : 0ull;
+        fresh[pass] = cand < fr.n_cand ? make_key(sc[r][pass * kTileCands + lane], (int)cand) : 0ull;
       }
       topset_absorb<kTilePasses>(set[rr], fresh, slots, scratch[w]);
     }
@@ -151,10 +184,10 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
     const int r = 4 * w + rr;
     if (r >= rows) continue;
     const int64_t t = t0 + r;
-    const int own = (int)((q_pos0 + t) / bs);
-    const int slots = own < top_k - 1 ? own : top_k - 1;
+    const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
     const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-    finalize_row(set[rr].keys, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+    finalize_row(set[rr].keys, frame_slots(fr, top_k), fr.forced, top_k, sel + off,
+                 sel_scores ? sel_scores + off : nullptr);
   }
 }
 
@@ -224,7 +257,7 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
                                                            int32_t* __restrict__ sel, float* __restrict__ sel_scores,
                                                            uint64_t* __restrict__ ws, int64_t q_len, int64_t q_pos0,
                                                            int64_t nb_cap, int hq, int hkv, int G, int bs, int top_k,
-                                                           float scale, int chunk, int64_t n_chunks) {
+                                                           float scale, int keep_tail, int chunk, int64_t n_chunks) {
   constexpr int LPR = D / 4;
   __shared__ uint64_t lists[4][kWave];
 
@@ -233,14 +266,14 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   const int64_t b = row / (q_len * hkv);
   const int64_t t = (row / hkv) % q_len;
   const int g = (int)(row % hkv);
-  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
-  const int own = (int)((q_pos0 + t) / bs);
-  const int slots = own < top_k - 1 ? own : top_k - 1;
+  const int lane = lane_id(), w = wave_id();
+  const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
+  const int slots = frame_slots(fr, top_k);
 
-  if (slots == 0) {  // nothing to score: the own block alone
+  if (slots == 0) {  // nothing to score: the forced block alone
     if (ch == 0 && w == 0) {
       const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-      finalize_row(0ull, 0, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+      finalize_row(0ull, 0, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
     }
     return;
   }
@@ -249,7 +282,7 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   const f32x4_t qv = group_sum4(q + ((b * q_len + t) * hq + (int64_t)g * G) * D + 4 * (lane % LPR), G, D);
 
   const int64_t c_begin = ch * chunk;
-  const int64_t c_end = c_begin + chunk < own ? c_begin + chunk : own;
+  const int64_t c_end = c_begin + chunk < fr.n_cand ? c_begin + chunk : fr.n_cand;
   const float* kc_src = k_comp + ((b * hkv + g) * nb_cap) * D;
   uint64_t cur = 0ull;
   for (int64_t base = c_begin + (int64_t)kWave * w; base < c_end; base += 4 * kWave) {
@@ -262,7 +295,7 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   if (w != 0) return;
   if (n_chunks == 1) {
     const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-    finalize_row(cur, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+    finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
   } else if (lane < slots) {
     ws[(row * n_chunks + ch) * (top_k - 1) + lane] = cur;
   }
@@ -277,7 +310,7 @@ constexpr int kMergeCap = 2048;  // survivors kept in LDS; more go straight from
 
 __global__ __launch_bounds__(256) void select_merge_kernel(int32_t* __restrict__ sel, float* __restrict__ sel_scores,
                                                            const uint64_t* __restrict__ ws, int64_t q_len,
-                                                           int64_t q_pos0, int hkv, int bs, int top_k,
+                                                           int64_t q_pos0, int hkv, int bs, int top_k, int keep_tail,
                                                            int64_t n_chunks) {
   __shared__ uint64_t lists[4][kWave];
   __shared__ uint64_t surv[kMergeCap];
@@ -288,8 +321,8 @@ __global__ __launch_bounds__(256) void select_merge_kernel(int32_t* __restrict__
   const int64_t t = (row / hkv) % q_len;
   const int g = (int)(row % hkv);
   const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
-  const int own = (int)((q_pos0 + t) / bs);
-  const int slots = own < top_k - 1 ? own : top_k - 1;
+  const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
+  const int slots = frame_slots(fr, top_k);
   if (slots == 0) return;  // written by the split kernel
   const int sm = top_k - 1;
   const uint64_t* lst = ws + row * n_chunks * sm;
@@ -337,7 +370,7 @@ __global__ __launch_bounds__(256) void select_merge_kernel(int32_t* __restrict__
   cur = merge_wave_lists(lists, cur, slots);
   if (w != 0) return;
   const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-  finalize_row(cur, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+  finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
 }
 
 // Merge for rows whose chunk lists hold at most 256 keys in total: one wave
@@ -348,15 +381,15 @@ __global__ __launch_bounds__(64) void select_merge_small_kernel(int32_t* __restr
                                                                 float* __restrict__ sel_scores,
                                                                 const uint64_t* __restrict__ ws, int64_t q_len,
                                                                 int64_t q_pos0, int hkv, int bs, int top_k,
-                                                                int64_t n_chunks) {
+                                                                int keep_tail, int64_t n_chunks) {
   __shared__ uint64_t scratch[kWave];
   const int64_t row = blockIdx.x;
   const int64_t b = row / (q_len * hkv);
   const int64_t t = (row / hkv) % q_len;
   const int g = (int)(row % hkv);
   const int lane = lane_id();
-  const int own = (int)((q_pos0 + t) / bs);
-  const int slots = own < top_k - 1 ? own : top_k - 1;
+  const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
+  const int slots = frame_slots(fr, top_k);
   if (slots == 0) return;  // written by the split kernel
   const int sm = top_k - 1;
   const uint64_t* lst = ws + row * n_chunks * sm;
@@ -370,7 +403,305 @@ __global__ __launch_bounds__(64) void select_merge_small_kernel(int32_t* __restr
   TopSet set{0ull, 0, 0ull};
   topset_absorb<4>(set, x, slots, scratch);
   const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-  finalize_row(set.keys, slots, own, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+  finalize_row(set.keys, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+}
+
+// ------------------------------------------------------------------ large path
+
+constexpr int kLargeChunk = 256;   // candidates per score workgroup (4 waves x 64)
+constexpr int kLargeList = 16;     // best keys kept per chunk
+constexpr int kPickThreads = 1024;
+constexpr int kPoolPerThread = 12;  // candidate keys each pick thread holds
+constexpr int kPoolCap = kPickThreads * kPoolPerThread;
+constexpr int kBitmapWords = (int)(kMaxCandLarge / 32);
+// A re-expanded chunk has all 16 list keys at or above the pool cutoff, so at
+// most (top_k - 1) / 16 chunks expand: the second pool stays within capacity.
+static_assert(kLargeList * (kMaxCandLarge / kLargeChunk) +
+                  (kLargeChunk - kLargeList) * ((kMaxTopKLarge - 1) / kLargeList) <= kPoolCap,
+              "pool capacity");
+
+__device__ __forceinline__ float order_to_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Score pass: one workgroup per (row, chunk of 256 candidates). Writes the
+// order image of every candidate's score (ws_scores, row stride n_chunks*256)
+// and, for rows with more candidates than the pick kernel holds at once, the
+// chunk's 16 best keys in descending order (ws_lists, 0 = empty).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_large_score_kernel(
+    const T* __restrict__ q, const float* __restrict__ k_comp, uint32_t* __restrict__ ws_scores,
+    uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs,
+    float scale, int keep_tail, int64_t n_chunks) {
+  constexpr int LPR = D / 4;
+  __shared__ uint64_t tops[4][kLargeList];
+  const int64_t row = blockIdx.x / n_chunks;
+  const int64_t ch = blockIdx.x % n_chunks;
+  const int64_t b = row / (q_len * hkv);
+  const int64_t t = (row / hkv) % q_len;
+  const int g = (int)(row % hkv);
+  const int lane = lane_id(), w = wave_id();
+  const int n_cand = row_frame(q_pos0 + t, bs, keep_tail).n_cand;
+  const int64_t c_begin = ch * kLargeChunk;
+  if (c_begin >= n_cand) return;  // uniform over the workgroup
+
+  const f32x4_t qv = group_sum4(q + ((b * q_len + t) * hq + (int64_t)g * G) * D + 4 * (lane % LPR), G, D);
+  const int64_t base = c_begin + (int64_t)kWave * w;
+  uint64_t key = 0ull;
+  if (base < n_cand) {
+    const float sc = dot64_rows<D>(k_comp + ((b * hkv + g) * nb_cap + base) * D, n_cand - base, qv);
+    const int64_t cand = base + dot64_row<D>(lane);
+    if (cand < n_cand) {
+      key = make_key(sc * scale, (int)cand);
+      ws_scores[row * n_chunks * kLargeChunk + cand] = (uint32_t)(key >> 32);
+    }
+  }
+  if (n_cand <= kPoolCap) return;  // the pick kernel takes every score directly
+  key = wave_sort_desc(key);
+  if (lane < kLargeList) tops[w][lane] = key;
+  __syncthreads();
+  if (w == 0) {
+    uint64_t x = tops[lane / kLargeList][lane % kLargeList];
+    x = wave_sort_desc(x);
+    if (lane < kLargeList) ws_lists[(row * n_chunks + ch) * kLargeList + lane] = x;
+  }
+}
+
+struct PickSmem {
+  uint32_t bitmap[kBitmapWords];    // kept candidates
+  uint32_t word_pre[kBitmapWords];  // kept candidates in the words before
+  uint32_t hist[2][256];            // radix histograms (alternating)
+  uint64_t red_max[kPickThreads / kWave], red_min[kPickThreads / kWave];
+  int red_cnt[kPickThreads / kWave];
+  uint32_t wave_tot[kPickThreads / kWave];
+  uint32_t digit[3];                // chosen digit, keys above its bin, keys in its bin
+  uint32_t sat_mask[8];             // re-expanded chunks
+  int sat_list[kMaxCandLarge / kLargeChunk];
+  int n_sat;
+};
+
+__device__ __forceinline__ uint64_t high_bits(uint64_t x, int n_low) { return n_low >= 64 ? 0ull : x >> n_low; }
+
+// Smallest key value T such that exactly min(m, #keys) of the nonzero keys
+// held by the workgroup (KP per thread, distinct) are >= T; 1 when there are
+// none. Most-significant-digit radix descent with 8-bit digits, starting at
+// the highest bit in which the largest and smallest key differ, and stopping
+// as soon as the remaining keys of the chosen bin are all needed.
+template <int KP>
+__device__ uint64_t block_kth_largest(const uint64_t (&x)[KP], int m, PickSmem& sm) {
+  constexpr int NW = kPickThreads / kWave;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  __syncthreads();  // shared state of an earlier call fully consumed
+  uint64_t mx = 0ull, mn = ~0ull;
+  int cnt = 0;
+#pragma unroll
+  for (int p = 0; p < KP; ++p) {
+    if (x[p] != 0ull) {
+      mx = x[p] > mx ? x[p] : mx;
+      mn = x[p] < mn ? x[p] : mn;
+      ++cnt;
+    }
+  }
+#pragma unroll
+  for (int j = 1; j < kWave; j <<= 1) {
+    const uint64_t a = shfl_xor_u64(mx, j), c = shfl_xor_u64(mn, j);
+    mx = a > mx ? a : mx;
+    mn = c < mn ? c : mn;
+    cnt += __shfl_xor(cnt, j, kWave);
+  }
+  if (lane == 0) {
+    sm.red_max[w] = mx;
+    sm.red_min[w] = mn;
+    sm.red_cnt[w] = cnt;
+  }
+  if (tid < 256) sm.hist[0][tid] = 0u;
+  __syncthreads();
+  mx = 0ull;
+  mn = ~0ull;
+  cnt = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    mx = sm.red_max[i] > mx ? sm.red_max[i] : mx;
+    mn = sm.red_min[i] < mn ? sm.red_min[i] : mn;
+    cnt += sm.red_cnt[i];
+  }
+  if (cnt == 0) return 1ull;
+  if (cnt <= m) return mn;
+
+  int cur = 64 - __builtin_clzll(mx ^ mn);  // low bits still open (mx != mn: >= 2 distinct keys)
+  uint64_t prefix = high_bits(mx, cur);
+  int need = m;
+  int buf = 0;
+  while (true) {
+    const int wd = cur < 8 ? cur : 8;
+    const int shift = cur - wd;
+    const uint32_t dmask = (1u << wd) - 1u;
+#pragma unroll
+    for (int p = 0; p < KP; ++p)
+      if (x[p] != 0ull && high_bits(x[p], cur) == prefix)
+        atomicAdd(&sm.hist[buf][(uint32_t)(x[p] >> shift) & dmask], 1u);
+    __syncthreads();
+    if (w == 0) {
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = sm.hist[buf][4 * lane + i];
+      const uint32_t own = h[0] + h[1] + h[2] + h[3];
+      uint32_t incl = own;  // inclusive suffix sum over lanes (higher lanes hold higher digits)
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_down((int)incl, off, kWave);
+        if (lane + off < kWave) incl += v;
+      }
+      uint32_t above = incl - own;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (above < (uint32_t)need && (uint32_t)need <= above + h[i]) {
+          sm.digit[0] = 4 * lane + i;
+          sm.digit[1] = above;
+          sm.digit[2] = h[i];
+        }
+        above += h[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.hist[buf ^ 1][4 * lane + i] = 0u;
+    }
+    __syncthreads();
+    const uint32_t d = sm.digit[0];
+    need -= (int)sm.digit[1];
+    const int in_bin = (int)sm.digit[2];
+    prefix = (prefix << wd) | d;
+    cur = shift;
+    if (need == in_bin || cur == 0) return prefix << cur;
+    buf ^= 1;
+  }
+}
+
+// One workgroup per row: cutoff, then the kept ids in ascending order.
+__global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
+    int32_t* __restrict__ sel, float* __restrict__ sel_scores, const uint32_t* __restrict__ ws_scores,
+    const uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int hkv, int bs, int top_k, int keep_tail,
+    int64_t n_chunks) {
+  __shared__ PickSmem sm;
+  const int64_t row = blockIdx.x;
+  const int64_t b = row / (q_len * hkv);
+  const int64_t t = (row / hkv) % q_len;
+  const int g = (int)(row % hkv);
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
+  const int slots = frame_slots(fr, top_k);
+  const int n_cand = fr.n_cand;
+  const uint32_t* sc_row = ws_scores + row * n_chunks * kLargeChunk;
+  const uint64_t* ls_row = ws_lists + row * n_chunks * kLargeList;
+  const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
+  int32_t* sel_row = sel + off;
+  float* score_row = sel_scores ? sel_scores + off : nullptr;
+
+  // forced block right after the kept ids, then padding
+  for (int i = slots + tid; i < top_k; i += kPickThreads) {
+    const bool f = i == slots && fr.forced >= 0;
+    sel_row[i] = f ? fr.forced : -1;
+    if (score_row) score_row[i] = f ? __builtin_inff() : -__builtin_inff();
+  }
+  if (slots == 0) return;
+  if (slots == n_cand) {  // every candidate kept
+    for (int c = tid; c < n_cand; c += kPickThreads) {
+      sel_row[c] = c;
+      if (score_row) score_row[c] = order_to_float(sc_row[c]);
+    }
+    return;
+  }
+  const int n_words = (n_cand + 31) / 32;
+  for (int i = tid; i < n_words; i += kPickThreads) sm.bitmap[i] = 0u;
+  auto key_of = [&](int c) -> uint64_t {
+    return ((uint64_t)sc_row[c] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
+  };
+
+  uint64_t x[kPoolPerThread];
+  uint64_t cut;
+  if (n_cand <= kPoolCap) {
+#pragma unroll
+    for (int p = 0; p < kPoolPerThread; ++p) {
+      const int c = tid + kPickThreads * p;
+      x[p] = c < n_cand ? key_of(c) : 0ull;
+    }
+    cut = block_kth_largest(x, slots, sm);
+  } else {
+    // first pool: the chunk lists (every chunk's 16 best)
+    const int nch = (n_cand + kLargeChunk - 1) / kLargeChunk;
+    const int n_list = nch * kLargeList;
+#pragma unroll
+    for (int p = 0; p < kPoolPerThread; ++p) {
+      const int i = tid + kPickThreads * p;
+      x[p] = i < n_list ? ls_row[i] : 0ull;
+    }
+    if (tid < 8) sm.sat_mask[tid] = 0u;
+    if (tid == 0) sm.n_sat = 0;
+    cut = block_kth_largest(x, slots, sm);
+    // A chunk whose 16th key reaches the cutoff may hold more kept keys than
+    // its list shows; every other chunk's unlisted keys lie below the cutoff.
+    if (tid < nch) {
+      const uint64_t last = ls_row[tid * kLargeList + kLargeList - 1];
+      if (last != 0ull && last >= cut) {
+        sm.sat_list[atomicAdd(&sm.n_sat, 1)] = tid;
+        atomicOr(&sm.sat_mask[tid >> 5], 1u << (tid & 31));
+      }
+    }
+    __syncthreads();
+    const int n_sat = sm.n_sat;
+    if (n_sat > 0) {
+      // second pool: lists of the other chunks plus every key of the expanded ones
+#pragma unroll
+      for (int p = 0; p < kPoolPerThread; ++p) {
+        const int i = tid + kPickThreads * p;
+        uint64_t v = 0ull;
+        if (i < n_list) {
+          const int c = i / kLargeList;
+          if (!((sm.sat_mask[c >> 5] >> (c & 31)) & 1u)) v = ls_row[i];
+        } else if (i < n_list + n_sat * kLargeChunk) {
+          const int j = i - n_list;
+          const int c = sm.sat_list[j / kLargeChunk] * kLargeChunk + j % kLargeChunk;
+          if (c < n_cand) v = key_of(c);
+        }
+        x[p] = v;
+      }
+      cut = block_kth_largest(x, slots, sm);
+    }
+  }
+
+  // kept = keys >= cut (exactly `slots` of them); positions from the bitmap
+#pragma unroll
+  for (int p = 0; p < kPoolPerThread; ++p)
+    if (x[p] != 0ull && x[p] >= cut) {
+      const int id = key_id(x[p]);
+      atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31));
+    }
+  __syncthreads();
+  const uint32_t w0 = 2 * tid < n_words ? sm.bitmap[2 * tid] : 0u;
+  const uint32_t w1 = 2 * tid + 1 < n_words ? sm.bitmap[2 * tid + 1] : 0u;
+  const uint32_t own = __builtin_popcount(w0) + __builtin_popcount(w1);
+  uint32_t incl = own;  // inclusive prefix over the wave
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t v = (uint32_t)__shfl_up((int)incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  if (lane == kWave - 1) sm.wave_tot[w] = incl;
+  __syncthreads();
+  uint32_t before = incl - own;
+  for (int i = 0; i < w; ++i) before += sm.wave_tot[i];
+  if (2 * tid < n_words) sm.word_pre[2 * tid] = before;
+  if (2 * tid + 1 < n_words) sm.word_pre[2 * tid + 1] = before + __builtin_popcount(w0);
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kPoolPerThread; ++p)
+    if (x[p] != 0ull && x[p] >= cut) {
+      const int id = key_id(x[p]);
+      const int pos = (int)(sm.word_pre[id >> 5] + __builtin_popcount(sm.bitmap[id >> 5] & ((1u << (id & 31)) - 1u)));
+      if (pos < slots) {  // always true for distinct keys
+        sel_row[pos] = id;
+        if (score_row) score_row[pos] = key_score(x[p]);
+      }
+    }
 }
 
 template <typename T, int D>
@@ -379,40 +710,64 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
                         hipStream_t st) {
   const T* q = static_cast<const T*>(qv);
   const int64_t nb_cap = kv_cap / s.bs;
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  if (plan.large) {
+    uint32_t* wss = static_cast<uint32_t*>(ws);
+    uint64_t* wsl = reinterpret_cast<uint64_t*>(wss + rows * plan.n_chunks * kLargeChunk);
+    if (plan.n_chunks > 0) {
+      hipLaunchKernelGGL((select_large_score_kernel<T, D>), dim3((unsigned)(rows * plan.n_chunks)), dim3(256), 0, st,
+                         q, k_comp, wss, wsl, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.scale,
+                         s.keep_tail, plan.n_chunks);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(select_large_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, st, sel, sel_scores,
+                       wss, wsl, q_len, q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, plan.n_chunks);
+    return hipGetLastError();
+  }
   if (plan.tiled) {
     dim3 grid((unsigned)((q_len + kTileRows - 1) / kTileRows), (unsigned)s.hkv, (unsigned)s.batch);
     hipLaunchKernelGGL((select_tile_kernel<T, D>), grid, dim3(256), 0, st, q, k_comp, sel, sel_scores, q_len, q_pos0,
-                       nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, s.scale);
+                       nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, s.scale, s.keep_tail);
     return hipGetLastError();
   }
-  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
   uint64_t* wsk = static_cast<uint64_t*>(ws);
   hipLaunchKernelGGL((select_split_kernel<T, D>), dim3((unsigned)(rows * plan.n_chunks)), dim3(256), 0, st, q,
                      k_comp, sel, sel_scores, wsk, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
-                     s.scale, plan.chunk, plan.n_chunks);
+                     s.scale, s.keep_tail, plan.chunk, plan.n_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_chunks == 1) return e;
   if (plan.n_chunks * (s.top_k - 1) <= kSmallMergeKeys)
     hipLaunchKernelGGL(select_merge_small_kernel, dim3((unsigned)rows), dim3(64), 0, st, sel, sel_scores, wsk, q_len,
-                       q_pos0, s.hkv, s.bs, s.top_k, plan.n_chunks);
+                       q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, plan.n_chunks);
   else
     hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256), 0, st, sel, sel_scores, wsk, q_len,
-                       q_pos0, s.hkv, s.bs, s.top_k, plan.n_chunks);
+                       q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, plan.n_chunks);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int64_t max_candidates(const Dims& s, int64_t kv_len) {
+  return s.keep_tail ? kv_len / s.bs : (kv_len - 1) / s.bs;
+}
+
 SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
   SelectPlan p{};
   const int64_t kv_len = q_pos0 + q_len;
-  const int64_t max_cand = (kv_len - 1) / s.bs;  // candidates of the last row
-  p.tiled = q_len >= kTileRows;
+  const int64_t max_cand = max_candidates(s, kv_len);  // candidates of the last row
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
   p.chunk = 256;
   p.n_chunks = 1;
   p.ws_bytes = 0;
+  if (s.top_k > 64) {
+    p.large = true;
+    p.n_chunks = (max_cand + kLargeChunk - 1) / kLargeChunk;
+    p.ws_bytes = (size_t)rows * p.n_chunks * (kLargeChunk * sizeof(uint32_t) + kLargeList * sizeof(uint64_t));
+    return p;
+  }
+  p.tiled = q_len >= kTileRows;
   if (p.tiled || max_cand <= 0) return p;
-  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
   if (rows * max_cand <= 8192 && max_cand <= 2048) {
     // small problem: one workgroup per row, no merge launch
     p.chunk = (int)((max_cand + 255) / 256 * 256);

@@ -13,19 +13,26 @@
  *
  * Notation: b = batch, Hq / Hkv = query / KV heads, G = Hq / Hkv, d = head
  * dim, Bs = block size, k = top_k, N = kv_len. Query head h reads KV head
- * h / G. A query at absolute position p has own block i = p / Bs; its
- * candidates are the complete blocks 0 .. i-1.
+ * h / G. A query at absolute position p has own block i = p / Bs.
  *
  * Semantics (the library's reading of the pages where they are silent):
  *   compressed key   kc[b][g][c] = mean of K[b][g][c*Bs .. c*Bs+Bs-1]
  *   score            s(c) = scale * sum_{j<G} <q_{g*G+j}, kc[c]>
- *   selection        own block i always kept and counted in k; the other
- *                    min(k-1, i) slots take the best scores, equal scores
- *                    going to the smaller block id; written ascending and
- *                    padded with -1
+ *   frame            which blocks compete and which one is always kept:
+ *                    keep_tail = 0: candidates 0 .. i-1, block i always kept
+ *                    keep_tail = 1 (the released budget of "Qwen4 in
+ *                    llama.cpp: Dissecting PR #27742", section "QSA Is an
+ *                    Address-Selection Problem...", whose visible width is
+ *                    at most budget + ratio - 1): candidates are all
+ *                    n = (p+1)/Bs complete blocks, the own block included
+ *                    once complete; block n (the positions past the last
+ *                    complete block) is always kept when (p+1) % Bs != 0
+ *   selection        the kept block (if any) counts in k; the other
+ *                    min(k-1, #candidates) slots take the best scores, equal
+ *                    scores going to the smaller block id; written ascending
+ *                    and padded with -1
  *   attention        softmax(scale * <q_h, K_t>) weighted sum of V_t over
- *                    the positions of the kept complete blocks plus
- *                    i*Bs .. p of the own block
+ *                    the positions of the kept blocks that are <= p
  *   scale            1/sqrt(d) when qsa_shape.scale == 0
  *
  * Layouts (all contiguous, row-major, 16-byte aligned base pointers):
@@ -45,10 +52,13 @@
  * Errors: every argument is validated on the host before any HIP call.
  *   QSA_ERR_INVALID      null required pointer, non-positive size, Hq not a
  *                        multiple of Hkv, kv_len > kv_cap, inconsistent
- *                        positions, misaligned pointer, unknown op/dtype
+ *                        positions, misaligned pointer, unknown op/dtype,
+ *                        keep_tail not 0/1, keep_tail with k < 2
  *   QSA_ERR_UNSUPPORTED  valid but not implemented: d not in {64,128},
- *                        Bs not in {32,64,128}, k outside [1,64],
- *                        G not in {1,2,4,8,16}, too many blocks
+ *                        Bs not a power of two in [4,128], k > 513,
+ *                        G not in {1,2,4,8,16}; selection with k > 64 and
+ *                        more than 65536 candidates per row; bf16 prefill
+ *                        attention with Bs < 32 or k > 64; too many blocks
  *   QSA_ERR_WORKSPACE    ws_bytes below qsa_workspace_bytes(...) or ws NULL
  *                        while bytes are needed
  *   QSA_ERR_HIP          a kernel launch was rejected by the runtime
@@ -72,7 +82,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -92,9 +102,10 @@ typedef struct {
   int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0 */
   int32_t head_dim;    /* d */
   int32_t block_size;  /* Bs: tokens per compressed block */
-  int32_t top_k;       /* k: kept blocks per (token, KV head), own block included */
+  int32_t top_k;       /* k: kept blocks per (token, KV head), always-kept block included */
   int32_t dtype;       /* QSA_F32 or QSA_BF16: type of Q, K, V and out */
   float scale;         /* softmax/score scale; 0 selects 1/sqrt(head_dim) */
+  int32_t keep_tail;   /* selection frame: 0 = own block always kept, 1 = only the partial tail */
 } qsa_shape;
 
 /* Version of this ABI (QSA_ABI_VERSION). */
@@ -126,11 +137,15 @@ qsa_status qsa_compress_keys(const qsa_shape* shape, const void* k, int64_t kv_l
  * blocks are scored, the top-k kept and turned into cache addresses).
  * Query row t of q ([b][q_len][Hq][d]) sits at absolute position q_pos0 + t;
  * requires kv_len == q_pos0 + q_len (decode: q_len = 1, q_pos0 = kv_len-1).
- * k_comp must hold the complete blocks below each row's own block; it may
- * be NULL when no row has a candidate (kv_len <= Bs).
- * Writes sel [b][q_len][Hkv][k] (block ids ascending, own block last,
- * padded with -1) and, if sel_scores is not NULL, the float32 score of each
- * kept block at the same index (+inf for the own block, -inf for padding).
+ * k_comp must hold every candidate block of the rows' frames (the complete
+ * blocks before the own block, or with keep_tail all complete blocks among
+ * the first kv_len positions); it may be NULL when no row has a candidate.
+ * Writes sel [b][q_len][Hkv][k] (block ids ascending, the always-kept block
+ * last, padded with -1) and, if sel_scores is not NULL, the float32 score
+ * of each kept block at the same index (+inf for the always-kept block, -inf
+ * for padding). k <= 64 keeps the running top set in registers; k > 64 (up
+ * to the released budget of 512 blocks plus the tail slot) writes every
+ * candidate score to the workspace and radix-selects the cutoff per row.
  * ws: device scratch of qsa_workspace_bytes(shape, QSA_OP_SELECT, q_len, kv_len). */
 qsa_status qsa_score_select(const qsa_shape* shape, const void* q, int64_t q_len, int64_t q_pos0,
                             const float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel,
@@ -140,7 +155,8 @@ qsa_status qsa_score_select(const qsa_shape* shape, const void* q, int64_t q_len
  * ("Qwen4 in llama.cpp: Dissecting PR #27742", section "QSA Is an
  * Address-Selection Problem...": ordinary attention restricted to the
  * selected cells). q: [b][Hq][d]; k, v: [b][Hkv][kv_cap][d];
- * sel: [b][Hkv][k] from qsa_score_select; out: [b][Hq][d].
+ * sel: [b][Hkv][k] from qsa_score_select; out: [b][Hq][d]. Blocks shorter
+ * than 32 keys are gathered several to one 32-key MFMA step.
  * ws: device scratch of qsa_workspace_bytes(shape, QSA_OP_DECODE, 1, kv_len). */
 qsa_status qsa_sparse_attn_decode(const qsa_shape* shape, const void* q, const void* k, const void* v,
                                   int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out,

@@ -8,7 +8,7 @@ import torch
 
 import qsa_synth as S
 from oracle import qsa_oracle as O
-from qsa_check import BF16_ABS_TOL, F32_REL_TOL, check_selection, jaccard
+from qsa_check import BF16_ABS_TOL, F32_REL_TOL, check_selection_frame, jaccard
 
 
 def log(msg: str) -> None:
@@ -84,20 +84,23 @@ def check_rows(case: Case, sel: np.ndarray, out: np.ndarray, rows, q_pos0: int, 
     max_err = 0.0
     for b, t, g in rows:
         p = q_pos0 + t
-        own = p // Bs
+        n_cand, forced = O.selection_frame(p, Bs, w.keep_tail)
         qg = case.Q[b, t, g * G:(g + 1) * G].astype(np.float64)
-        sc = O.block_scores(qg, kc[b, g], own, case.scale)
+        sc = O.block_scores(qg, kc[b, g], n_cand, case.scale)
         row_sel = [int(x) for x in sel[b, t, g]]
-        stats[check_selection(row_sel, sc, own, k)] += 1
-        stats["jaccard"].append(jaccard(row_sel, O.select_blocks(sc, own, k)))
+        stats[check_selection_frame(row_sel, sc, n_cand, forced, k)] += 1
+        stats["jaccard"].append(jaccard(row_sel, O.select_in_frame(sc, n_cand, forced, k)))
         if scores_gpu is not None:
-            kept = [c for c in row_sel if 0 <= c < own]
+            kept = [c for c in row_sel if 0 <= c < n_cand]
             got = scores_gpu[b, t, g, : len(kept)]
             ref = sc[kept]
             mag = case.scale * (np.abs(qg).sum(0)[None, :] * np.abs(kc[b, g, kept])).sum(1)
             assert (np.abs(got - ref) <= (w.head_dim + G + Bs + 8) * 2.0 ** -24 * mag + 1e-30).all()
-            assert scores_gpu[b, t, g, len(kept)] == np.inf
-            assert (scores_gpu[b, t, g, len(kept) + 1:] == -np.inf).all()
+            rest = scores_gpu[b, t, g, len(kept):]
+            if forced is not None:
+                assert rest[0] == np.inf
+                rest = rest[1:]
+            assert (rest == -np.inf).all()
         if check_output:
             ref = O.attend_given_selection(qg, case.K[b, g], case.V[b, g], row_sel, p, Bs, case.scale)
             got = out[b, t, g * G:(g + 1) * G].astype(np.float64)

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 1
+    assert qsa.abi_version() == 2
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -55,7 +55,7 @@ def good_shape(qsa, **kw):
     args = dict(batch=1, n_q_heads=16, n_kv_heads=2, head_dim=128, block_size=64, top_k=16, dtype=qsa.QSA_BF16)
     args.update(kw)
     return qsa.QsaShape(args["batch"], args["n_q_heads"], args["n_kv_heads"], args["head_dim"], args["block_size"],
-                        args["top_k"], args["dtype"], args.get("scale", 0.0))
+                        args["top_k"], args["dtype"], args.get("scale", 0.0), args.get("keep_tail", 0))
 
 
 def test_workspace_sizes(qsa):
@@ -82,8 +82,8 @@ def test_workspace_sizes(qsa):
 BAD_SHAPES = [
     (dict(batch=0), 1), (dict(n_q_heads=15), 1), (dict(n_kv_heads=0), 1), (dict(top_k=0), 1), (dict(dtype=5), 1),
     (dict(scale=float("nan")), 1), (dict(scale=-1.0), 1), (dict(head_dim=96), 2), (dict(block_size=48), 2),
-    (dict(block_size=16), 2), (dict(block_size=256), 2), (dict(top_k=65), 2), (dict(n_q_heads=24, n_kv_heads=2), 2),
-    (dict(n_q_heads=64, n_kv_heads=2), 2),
+    (dict(block_size=2), 2), (dict(block_size=256), 2), (dict(top_k=514), 2), (dict(n_q_heads=24, n_kv_heads=2), 2),
+    (dict(n_q_heads=64, n_kv_heads=2), 2), (dict(keep_tail=2), 1), (dict(keep_tail=1, top_k=1), 1),
 ]
 
 
@@ -96,6 +96,22 @@ def test_shape_validation(qsa, kw, code):
     assert lib.qsa_score_select(ctypes.byref(sh), P, 1, 63, P, 64, 64, P, None, P, 1 << 20, None) == code
     assert lib.qsa_sparse_attn_decode(ctypes.byref(sh), P, P, P, 64, 64, P, P, P, 1 << 20, None) == code
     assert lib.qsa_sparse_attn_prefill(ctypes.byref(sh), P, P, P, 64, 0, 64, P, P, P, 1 << 20, None) == code
+
+
+def test_op_specific_limits(qsa):
+    """Shapes every op accepts except the one whose kernels lack the path (checked before any launch)."""
+    lib = qsa.LIB
+    P = ctypes.c_void_p(4096)
+    for kw in (dict(block_size=16), dict(top_k=65), dict(block_size=4, top_k=513, keep_tail=1)):
+        sh = ctypes.byref(good_shape(qsa, **kw))
+        assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 64, 0, 64, P, P, P, 1 << 30, None) == 2
+    # k > 64 selection holds at most 65536 candidates per row
+    sh = good_shape(qsa, block_size=4, top_k=513, keep_tail=1)
+    n = 4 * 65536
+    assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 1, n) == 2 * 256 * (256 * 4 + 16 * 8)
+    # a too-small workspace is reported only for a supported shape (no launch either way)
+    assert lib.qsa_score_select(ctypes.byref(sh), P, 1, n - 1, P, n, n, P, None, P, 8, None) == 3
+    assert lib.qsa_score_select(ctypes.byref(sh), P, 1, n + 3, P, n + 4, n + 4, P, None, P, 8, None) == 2
 
 
 def test_argument_validation(qsa):

@@ -29,7 +29,8 @@ def run_prefill(case: Case, q_pos0: int = 0, q_rows=None):
     """Full prefill path on rows [q_pos0, kv_len); returns host (sel, out, scores, k_comp)."""
     w = case.w
     q = case.q if q_rows is None else case.q[:, q_rows].contiguous()
-    out, sel, k_comp, scores = qsa.prefill(q, case.k, case.v, w.block_size, w.top_k, q_pos0=q_pos0, with_scores=True)
+    out, sel, k_comp, scores = qsa.prefill(q, case.k, case.v, w.block_size, w.top_k, q_pos0=q_pos0, with_scores=True,
+                                           keep_tail=w.keep_tail)
     torch.cuda.synchronize()
     return sel.cpu().numpy(), from_device(out), scores.cpu().numpy(), k_comp
 
@@ -59,11 +60,22 @@ PREFILL_CASES = [
     W(kv_len=530, head_dim=64, n_q_heads=16, n_kv_heads=1, top_k=4, block_size=64),   # G = 16
     W(kv_len=300, dtype="f32", sigma=1.0, top_k=3, head_dim=128),
     W(kv_len=15, top_k=2),                                     # shorter than one block
+    # keep_tail frame: a complete own block competes (tile select, MFMA attention)
+    W(kv_len=777, top_k=6, keep_tail=True),
+    W(batch=2, kv_len=640, top_k=3, head_dim=64, block_size=32, keep_tail=True),
+    # blocks shorter than 32 keys and k > 64 (float32 attention, large-k selection)
+    W(kv_len=300, dtype="f32", sigma=1.0, head_dim=64, n_q_heads=4, n_kv_heads=2, block_size=8, top_k=5),
+    W(kv_len=700, dtype="f32", sigma=1.0, head_dim=64, n_q_heads=2, n_kv_heads=1, block_size=4, top_k=100,
+      keep_tail=True),
 ]
 
 
-@pytest.mark.parametrize("w", PREFILL_CASES, ids=lambda w: f"{w.dtype}-b{w.batch}-n{w.kv_len}-h{w.n_q_heads}x{w.n_kv_heads}"
-                         f"-d{w.head_dim}-bs{w.block_size}-k{w.top_k}")
+def case_id(w: S.Workload) -> str:
+    return (f"{w.dtype}-b{w.batch}-n{w.kv_len}-h{w.n_q_heads}x{w.n_kv_heads}-d{w.head_dim}-bs{w.block_size}"
+            f"-k{w.top_k}" + ("-tail" if w.keep_tail else ""))
+
+
+@pytest.mark.parametrize("w", PREFILL_CASES, ids=case_id)
 def test_prefill_parity(w):
     log(f"prefill parity {w}")
     case = Case(w, seed=1, kv_cap=w.kv_len + 40)
@@ -95,23 +107,39 @@ DECODE_CASES = [
     W(mode="decode", batch=2, kv_len=3000, n_q_heads=16, n_kv_heads=1, top_k=7),
     W(mode="decode", batch=2, kv_len=3000, n_q_heads=2, n_kv_heads=2, top_k=7),
     W(mode="decode", batch=2, kv_len=2222, dtype="f32", sigma=1.0, top_k=5),
+    # keep_tail: own block complete (it competes) and still filling
+    W(mode="decode", batch=2, kv_len=64 * 40, top_k=8, keep_tail=True),
+    W(mode="decode", batch=2, kv_len=64 * 40 + 17, top_k=8, keep_tail=True),
+    # blocks of 4, 8, 16 keys: several blocks per 32-key MFMA step
+    W(mode="decode", batch=2, kv_len=3001, top_k=9, block_size=4),
+    W(mode="decode", batch=2, kv_len=2050, top_k=17, block_size=8, head_dim=64),
+    W(mode="decode", batch=1, kv_len=5003, top_k=12, block_size=16, keep_tail=True),
+    # k > 64: every score to the workspace, radix-selected cutoff
+    W(mode="decode", batch=2, kv_len=4 * 4096 + 3, top_k=129, block_size=4),             # pool of all scores
+    W(mode="decode", batch=1, kv_len=60001, top_k=513, block_size=4, keep_tail=True),     # pool of chunk lists
+    W(mode="decode", batch=1, kv_len=4 * 30000, top_k=513, block_size=4, keep_tail=True, n_kv_heads=1,
+      n_q_heads=8),
+    W(mode="decode", batch=1, kv_len=2051, top_k=513, block_size=4, keep_tail=True),      # dense: 2051 positions
+    W(mode="decode", batch=1, kv_len=2052, top_k=513, block_size=4, keep_tail=True),      # first discard
+    W(mode="decode", batch=1, kv_len=64 * 3000 + 10, top_k=200, block_size=64),
+    W(mode="decode", batch=1, kv_len=9000, top_k=100, block_size=8, dtype="f32", sigma=1.0, keep_tail=True),
 ]
 
 
 def run_decode(case: Case):
     w = case.w
     b, hq, d = w.batch, w.n_q_heads, w.head_dim
-    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k, keep_tail=w.keep_tail)
     k_comp = torch.full((b, w.n_kv_heads, case.kv_cap // w.block_size, d), float("nan"), device="cuda")
     qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
     q = case.q.view(b, hq, d)
-    out, sel, scores = qsa.decode(q, case.k, case.v, w.kv_len, w.block_size, w.top_k, k_comp, with_scores=True)
+    out, sel, scores = qsa.decode(q, case.k, case.v, w.kv_len, w.block_size, w.top_k, k_comp, with_scores=True,
+                                  keep_tail=w.keep_tail)
     torch.cuda.synchronize()
     return sel.cpu().numpy()[:, None], from_device(out)[:, None], scores.cpu().numpy()[:, None], k_comp
 
 
-@pytest.mark.parametrize("w", DECODE_CASES, ids=lambda w: f"{w.dtype}-b{w.batch}-n{w.kv_len}-h{w.n_q_heads}x{w.n_kv_heads}"
-                         f"-d{w.head_dim}-bs{w.block_size}-k{w.top_k}")
+@pytest.mark.parametrize("w", DECODE_CASES, ids=case_id)
 def test_decode_parity(w):
     log(f"decode parity {w}")
     case = Case(w, seed=3, kv_cap=w.kv_len + 100)
@@ -148,14 +176,15 @@ def test_bitwise_determinism():
     np.testing.assert_array_equal(x[1], y[1])
 
 
-def test_incremental_compress_matches_full():
+@pytest.mark.parametrize("bs,d", [(64, 128), (4, 128), (4, 64), (8, 64), (16, 128)])
+def test_incremental_compress_matches_full(bs, d):
     """Compressing block by block (a decode loop) gives the same compressed keys as one call."""
-    w = W(batch=2, kv_len=1100)
+    w = W(batch=2, kv_len=1100, block_size=bs, head_dim=d)
     case = Case(w, seed=7)
     shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
     nb = w.kv_len // w.block_size
-    full = torch.zeros(2, 2, nb, 128, device="cuda")
-    inc = torch.zeros(2, 2, nb, 128, device="cuda")
+    full = torch.zeros(2, 2, nb, d, device="cuda")
+    inc = torch.zeros(2, 2, nb, d, device="cuda")
     qsa.qsa_compress_keys(shape, case.k, w.kv_len, full)
     for n in range(1, w.kv_len + 1):
         if n % w.block_size == 0:
@@ -164,19 +193,25 @@ def test_incremental_compress_matches_full():
     assert torch.equal(full, inc)
 
 
-def test_workspace_reuse_across_decode_steps():
+REUSE_CASES = [
+    (W(mode="decode", batch=4, kv_len=40033, block_size=32, top_k=16), [40000, 40031, 40032, 40033, 39000]),
+    (W(mode="decode", batch=1, kv_len=4 * 20000 + 3, block_size=4, top_k=513, keep_tail=True),
+     [80003, 80000, 79999, 60001, 40000, 50000]),
+]
+
+
+@pytest.mark.parametrize("w,steps", REUSE_CASES, ids=lambda x: case_id(x) if isinstance(x, S.Workload) else "")
+def test_workspace_reuse_across_decode_steps(w, steps):
     """One select and one decode workspace, filled with garbage once, serve a
     run of decode steps (split selection and split attention): every step
     equals a call with fresh workspaces."""
-    w = W(mode="decode", batch=4, kv_len=40033, block_size=32, top_k=16)
     case = Case(w, seed=8)
     b, hq, d = w.batch, w.n_q_heads, w.head_dim
-    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k, keep_tail=w.keep_tail)
     k_comp = torch.zeros(b, w.n_kv_heads, w.kv_len // w.block_size, d, device="cuda")
     qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
     q_sel = case.q.view(b, 1, hq, d)
     q_dec = case.q.view(b, hq, d)
-    steps = [40000, 40031, 40032, 40033, 39000]
     n_sel = max(qsa.qsa_workspace_bytes(shape, qsa.QSA_OP_SELECT, 1, n) for n in steps)
     n_dec = max(qsa.qsa_workspace_bytes(shape, qsa.QSA_OP_DECODE, 1, n) for n in steps)
     assert n_sel > 0 and n_dec > 0, "both calls must take their split paths"
@@ -200,3 +235,53 @@ def test_workspace_reuse_across_decode_steps():
     rows = [(bb, 0, g) for bb in range(b) for g in range(w.n_kv_heads)]
     st = check_rows(case, outs[0][0].cpu().numpy(), from_device(outs[0][1])[:, None], rows, steps[-1] - 1)
     log(f"  {st}")
+
+
+def _restore_keys(case: Case, K32: np.ndarray) -> None:
+    """Replace the case's keys by ``K32`` rounded to its storage type (host view and device copy)."""
+    w = case.w
+    if w.dtype == "bf16":
+        bits = S.f32_to_bf16_bits(K32.astype(np.float32))
+        case.K = S.bf16_bits_to_f32(bits)
+        case.k = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        case.K = K32.astype(np.float32)
+        case.k = torch.from_numpy(case.K).cuda()
+    case._kc = None
+
+
+def test_large_k_equal_scores_keep_smallest_ids():
+    """Zero queries give every candidate the same score: the smallest ids win. The list pool's cutoff
+    is reached by the lists of the first 32 chunks, so all 32 are re-expanded from the stored scores
+    (the most the pool allows at k = 513)."""
+    w = W(mode="decode", batch=1, kv_len=4 * 20000, top_k=513, block_size=4)
+    case = Case(w, seed=6)
+    case.Q = np.zeros_like(case.Q)
+    case.q = torch.zeros_like(case.q)
+    sel, out, scores, _ = run_decode(case)
+    own = (w.kv_len - 1) // 4
+    for g in range(w.n_kv_heads):
+        assert sel[0, 0, g].tolist() == list(range(512)) + [own]
+    st = check_rows(case, sel, out, [(0, 0, g) for g in range(2)], w.kv_len - 1, scores_gpu=scores)
+    log(f"equal scores: {st}")
+
+
+def test_large_k_clustered_winners():
+    """Keys of 600 consecutive blocks shifted toward the query (about four noise deviations of the
+    score): most kept blocks sit in three chunks of 256 candidates, whose lists saturate and are
+    re-expanded."""
+    w = W(mode="decode", batch=1, kv_len=4 * 40000 + 2, top_k=513, block_size=4, keep_tail=True)
+    case = Case(w, seed=7)
+    K32 = case.K.astype(np.float64)
+    G = w.group
+    for g in range(w.n_kv_heads):
+        u = case.Q[0, -1, g * G:(g + 1) * G].astype(np.float64).sum(0)
+        u /= np.linalg.norm(u)
+        K32[0, g, 4 * 10000:4 * 10600] += 2.0 * w.sigma * u
+    _restore_keys(case, K32)
+    sel, out, scores, _ = run_decode(case)
+    for g in range(w.n_kv_heads):
+        inside = sum(1 for c in sel[0, 0, g] if 10000 <= c < 10600)
+        assert inside > 300, inside
+    st = check_rows(case, sel, out, [(0, 0, g) for g in range(2)], w.kv_len - 1, scores_gpu=scores)
+    log(f"clustered winners: {st}")
