@@ -58,9 +58,18 @@ def parse():
 
 # ------------------------------------------------------------- algorithmic work
 
-def visible_keys(p: int, bs: int, k: int) -> int:
+def frame(p: int, bs: int, keep_tail: bool):
+    """(candidate blocks, always-kept block or None) of a query at position p."""
+    if not keep_tail:
+        return p // bs, p // bs
+    n = (p + 1) // bs
+    return n, (n if (p + 1) % bs else None)
+
+
+def visible_keys(p: int, bs: int, k: int, keep_tail: bool = False) -> int:
     """Keys a query at position p attends to under the selection rule."""
-    return min(p + 1, (k - 1) * bs + (p % bs) + 1)
+    n_cand, forced = frame(p, bs, keep_tail)
+    return min(k - 1, n_cand) * bs + (0 if forced is None else p - forced * bs + 1)
 
 
 def work_model(w, n_new_blocks: int):
@@ -70,12 +79,12 @@ def work_model(w, n_new_blocks: int):
     m = {}
     if w.mode == "decode":
         p = w.kv_len - 1
-        cand = p // bs
+        cand = frame(p, bs, w.keep_tail)[0]
         rows = b * hkv
         m["compress"] = {"bytes": rows * n_new_blocks * (bs * d * el + d * 4), "flops": 0}
         m["select"] = {"bytes": rows * cand * d * 4 + b * hq * d * el + rows * k * 4,
                        "flops": 2 * d * rows * cand}
-        vis = visible_keys(p, bs, k)
+        vis = visible_keys(p, bs, k, w.keep_tail)
         m["attend"] = {"bytes": rows * vis * d * el * 2 + 2 * b * hq * d * el + rows * k * 4,
                        "flops": 4 * d * hq * b * vis}
     else:
@@ -83,10 +92,10 @@ def work_model(w, n_new_blocks: int):
         nb = T // bs
         rows = b * hkv
         m["compress"] = {"bytes": rows * nb * (bs * d * el + d * 4), "flops": 0}
-        cand_sum = sum(t // bs for t in range(T))
+        cand_sum = sum(frame(t, bs, w.keep_tail)[0] for t in range(T))
         m["select"] = {"bytes": rows * nb * d * 4 + b * T * hq * d * el + b * T * hkv * k * 4,
                        "flops": 2 * d * rows * cand_sum}
-        vis_sum = sum(visible_keys(t, bs, k) for t in range(T))
+        vis_sum = sum(visible_keys(t, bs, k, w.keep_tail) for t in range(T))
         m["attend"] = {"bytes": 2 * b * T * hq * d * el + rows * T * d * el * 2 + b * T * hkv * k * 4,
                        "flops": 4 * d * hq * b * vis_sum}
     return m
@@ -113,7 +122,7 @@ class Step:
         del Qs, Ks, Vs
         b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
         cap = w.kv_len
-        self.shape = qsa.make_shape(b, hq, hkv, d, bs, k, self.q.dtype)
+        self.shape = qsa.make_shape(b, hq, hkv, d, bs, k, self.q.dtype, keep_tail=w.keep_tail)
         self.k_comp = torch.empty(b, hkv, cap // bs, d, dtype=torch.float32, device="cuda")
         q_len, q_pos0 = w.q_len, w.q_pos0
         self.sel = torch.empty(b, q_len, hkv, k, dtype=torch.int32, device="cuda")
@@ -264,24 +273,27 @@ def cpu_baseline(w, seed, budget_s):
             q = S.gen_q(w, seed, 0)
             K = np.stack([S.gen_kv(w, seed, S.TENSOR_K, 0, g, q) for g in range(w.n_kv_heads)])
             V = np.stack([S.gen_kv(w, seed, S.TENSOR_V, 0, g) for g in range(w.n_kv_heads)])
-            kc = O.compress_keys(K[:, : w.kv_len - 1], bs)
             p = w.kv_len - 1
+            n_prev = p // bs  # blocks complete before the new token
+            kc = np.zeros((w.n_kv_heads, w.kv_len // bs, w.head_dim))
+            kc[:, :n_prev] = O.compress_keys(K[:, : n_prev * bs], bs)
+            n_cand, forced = O.selection_frame(p, bs, w.keep_tail)
             n_steps, t0 = 0, time.perf_counter()
             while True:
-                blk = O.compress_keys(K[:, (p // bs) * bs:(p // bs + 1) * bs], bs) if (p + 1) % bs == 0 else None
+                if (p + 1) % bs == 0:  # the new token completes its block
+                    kc[:, n_prev:n_prev + 1] = O.compress_keys(K[:, n_prev * bs:(n_prev + 1) * bs], bs)
                 for g in range(w.n_kv_heads):
                     qg = q[0, g * G:(g + 1) * G].astype(np.float64)
-                    sc = O.block_scores(qg, kc[g], p // bs, scale)
-                    sel = O.select_blocks(sc, p // bs, k)
+                    sc = O.block_scores(qg, kc[g], n_cand, scale)
+                    sel = O.select_in_frame(sc, n_cand, forced, k)
                     O.attend_given_selection(qg, K[g], V[g], sel, p, bs, scale)
-                del blk
                 n_steps += 1
                 el = time.perf_counter() - t0
                 if el >= budget_s or n_steps >= 100000:
                     break
             return {"value": n_steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                     "sample": f"{n_steps} decode steps of one sequence (both KV heads: compress of the completed "
-                              f"block, scores over {p // bs} candidates, top-{k} selection, attention) in {el:.1f} s"}
+                              f"block, scores over {n_cand} candidates, top-{k} selection, attention) in {el:.1f} s"}
         # prefill: compress everything, then a uniform sample of query rows, scaled to the full prompt
         Qs, Ks, Vs = S.gen_all(w, seed)
         Q, K, V = (S.as_f32(x, w.dtype) for x in (Qs, Ks, Vs))
@@ -292,10 +304,11 @@ def cpu_baseline(w, seed, budget_s):
         order = rng.permutation(w.kv_len)
         done, t1 = 0, time.perf_counter()
         for t in order:
+            n_cand, forced = O.selection_frame(int(t), bs, w.keep_tail)
             for g in range(w.n_kv_heads):
                 qg = Q[0, t, g * G:(g + 1) * G].astype(np.float64)
-                sc = O.block_scores(qg, kc[0, g], t // bs, scale)
-                sel = O.select_blocks(sc, t // bs, k)
+                sc = O.block_scores(qg, kc[0, g], n_cand, scale)
+                sel = O.select_in_frame(sc, n_cand, forced, k)
                 O.attend_given_selection(qg, K[0, g], V[0, g], sel, t, bs, scale)
             done += 1
             if time.perf_counter() - t1 >= budget_s:
@@ -381,7 +394,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "mode": w.mode, "batch": w.batch, "kv_len": w.kv_len,
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
-                   "block_size": w.block_size, "top_k": w.top_k, "seed": args.seed,
+                   "block_size": w.block_size, "top_k": w.top_k, "keep_tail": w.keep_tail, "seed": args.seed,
                    "graphs": not args.no_graph},
         "roofline": {"bound": bound, "kernel": f"{dominant} call", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),

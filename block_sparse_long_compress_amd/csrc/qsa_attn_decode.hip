@@ -282,9 +282,9 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   const int g = (int)(row % hkv);
   const int64_t stride = 2 * G + G * D;
   const float* pr = part + row * n_split * stride;
-  // Slices in batches of 8 whose loads all go out at once (one memory round
+  // Slices in batches of 32 whose loads all go out at once (one memory round
   // trip per batch), folded in slice order into a running state.
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 32;
   float M = -__builtin_inff(), L = 0.f, O = 0.f;
   for (int s0 = 0; s0 < n_split; s0 += kBatch) {
     float ms[kBatch], ls[kBatch], os[kBatch];

@@ -176,6 +176,38 @@ __device__ __forceinline__ float xor_lane_f32(float v, int j) {
   return __uint_as_float(xor_lane_u32(__float_as_uint(v), j));
 }
 
+// Lane sums with xor butterflies (DPP and permlane steps, no LDS round trips):
+// total over the wave, inclusive prefix (lanes <= l) and inclusive suffix
+// (lanes >= l). At step j every lane holds the total of its aligned group of
+// j lanes; the partner group is the other half of the group of 2j.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int j = 1; j < kWave; j <<= 1) v += xor_lane_u32(v, j);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_prefix_sum_u32(uint32_t v) {
+  const int lane = lane_id();
+  uint32_t total = v;
+#pragma unroll
+  for (int j = 1; j < kWave; j <<= 1) {
+    const uint32_t t = xor_lane_u32(total, j);
+    if (lane & j) v += t;
+    total += t;
+  }
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_suffix_sum_u32(uint32_t v) {
+  const int lane = lane_id();
+  uint32_t total = v;
+#pragma unroll
+  for (int j = 1; j < kWave; j <<= 1) {
+    const uint32_t t = xor_lane_u32(total, j);
+    if (!(lane & j)) v += t;
+    total += t;
+  }
+  return v;
+}
+
 // Bitonic sort of one key per lane across the wave, descending (lane 0 = largest).
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
   const int lane = lane_id();

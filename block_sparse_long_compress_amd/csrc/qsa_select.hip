@@ -410,9 +410,11 @@ __global__ __launch_bounds__(64) void select_merge_small_kernel(int32_t* __restr
 
 constexpr int kLargeChunk = 256;   // candidates per score workgroup (4 waves x 64)
 constexpr int kLargeList = 16;     // best keys kept per chunk
-constexpr int kPickThreads = 1024;
-constexpr int kPoolPerThread = 12;  // candidate keys each pick thread holds
+constexpr int kPickThreads = 512;
+constexpr int kListPerThread = 8;   // keys per pick thread in the pool of chunk lists
+constexpr int kPoolPerThread = 24;  // keys per pick thread in a pool of whole chunks
 constexpr int kPoolCap = kPickThreads * kPoolPerThread;
+static_assert(kPickThreads * kListPerThread == kLargeList * (kMaxCandLarge / kLargeChunk), "list pool");
 constexpr int kBitmapWords = (int)(kMaxCandLarge / 32);
 // A re-expanded chunk has all 16 list keys at or above the pool cutoff, so at
 // most (top_k - 1) / 16 chunks expand: the second pool stays within capacity.
@@ -470,11 +472,13 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
 struct PickSmem {
   uint32_t bitmap[kBitmapWords];    // kept candidates
   uint32_t word_pre[kBitmapWords];  // kept candidates in the words before
+  static_assert(kBitmapWords % kPickThreads == 0, "bitmap words per thread");
   uint32_t hist[2][256];            // radix histograms (alternating)
   uint64_t red_max[kPickThreads / kWave], red_min[kPickThreads / kWave];
   int red_cnt[kPickThreads / kWave];
   uint32_t wave_tot[kPickThreads / kWave];
   uint32_t digit[3];                // chosen digit, keys above its bin, keys in its bin
+  uint64_t last[kMaxCandLarge / kLargeChunk];  // 16th list key of every chunk
   uint32_t sat_mask[8];             // re-expanded chunks
   int sat_list[kMaxCandLarge / kLargeChunk];
   int n_sat;
@@ -504,11 +508,11 @@ __device__ uint64_t block_kth_largest(const uint64_t (&x)[KP], int m, PickSmem& 
   }
 #pragma unroll
   for (int j = 1; j < kWave; j <<= 1) {
-    const uint64_t a = shfl_xor_u64(mx, j), c = shfl_xor_u64(mn, j);
+    const uint64_t a = xor_lane_u64(mx, j), c = xor_lane_u64(mn, j);
     mx = a > mx ? a : mx;
     mn = c < mn ? c : mn;
-    cnt += __shfl_xor(cnt, j, kWave);
   }
+  cnt = (int)wave_sum_u32((uint32_t)cnt);
   if (lane == 0) {
     sm.red_max[w] = mx;
     sm.red_min[w] = mn;
@@ -546,13 +550,8 @@ __device__ uint64_t block_kth_largest(const uint64_t (&x)[KP], int m, PickSmem& 
 #pragma unroll
       for (int i = 0; i < 4; ++i) h[i] = sm.hist[buf][4 * lane + i];
       const uint32_t own = h[0] + h[1] + h[2] + h[3];
-      uint32_t incl = own;  // inclusive suffix sum over lanes (higher lanes hold higher digits)
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t v = (uint32_t)__shfl_down((int)incl, off, kWave);
-        if (lane + off < kWave) incl += v;
-      }
-      uint32_t above = incl - own;
+      // keys in the bins of higher lanes (higher digits)
+      uint32_t above = wave_suffix_sum_u32(own) - own;
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         if (above < (uint32_t)need && (uint32_t)need <= above + h[i]) {
@@ -616,7 +615,7 @@ __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
     return ((uint64_t)sc_row[c] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
   };
 
-  uint64_t x[kPoolPerThread];
+  uint64_t x[kPoolPerThread];  // the pool the cutoff is taken over (0 = empty)
   uint64_t cut;
   if (n_cand <= kPoolCap) {
 #pragma unroll
@@ -624,26 +623,30 @@ __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
       const int c = tid + kPickThreads * p;
       x[p] = c < n_cand ? key_of(c) : 0ull;
     }
-    cut = block_kth_largest(x, slots, sm);
+    cut = block_kth_largest<kPoolPerThread>(x, slots, sm);
   } else {
     // first pool: the chunk lists (every chunk's 16 best)
     const int nch = (n_cand + kLargeChunk - 1) / kLargeChunk;
     const int n_list = nch * kLargeList;
+    uint64_t y[kListPerThread];
 #pragma unroll
-    for (int p = 0; p < kPoolPerThread; ++p) {
+    for (int p = 0; p < kListPerThread; ++p) {
       const int i = tid + kPickThreads * p;
-      x[p] = i < n_list ? ls_row[i] : 0ull;
+      y[p] = i < n_list ? ls_row[i] : 0ull;
+      if (i < n_list && i % kLargeList == kLargeList - 1) sm.last[i / kLargeList] = y[p];
     }
+#pragma unroll
+    for (int p = 0; p < kPoolPerThread; ++p) x[p] = p < kListPerThread ? y[p] : 0ull;
     if (tid < 8) sm.sat_mask[tid] = 0u;
     if (tid == 0) sm.n_sat = 0;
-    cut = block_kth_largest(x, slots, sm);
+    cut = block_kth_largest<kListPerThread>(y, slots, sm);
     // A chunk whose 16th key reaches the cutoff may hold more kept keys than
     // its list shows; every other chunk's unlisted keys lie below the cutoff.
-    if (tid < nch) {
-      const uint64_t last = ls_row[tid * kLargeList + kLargeList - 1];
+    for (int c = tid; c < nch; c += kPickThreads) {
+      const uint64_t last = sm.last[c];
       if (last != 0ull && last >= cut) {
-        sm.sat_list[atomicAdd(&sm.n_sat, 1)] = tid;
-        atomicOr(&sm.sat_mask[tid >> 5], 1u << (tid & 31));
+        sm.sat_list[atomicAdd(&sm.n_sat, 1)] = c;
+        atomicOr(&sm.sat_mask[c >> 5], 1u << (c & 31));
       }
     }
     __syncthreads();
@@ -664,7 +667,7 @@ __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
         }
         x[p] = v;
       }
-      cut = block_kth_largest(x, slots, sm);
+      cut = block_kth_largest<kPoolPerThread>(x, slots, sm);
     }
   }
 
@@ -676,21 +679,28 @@ __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
       atomicOr(&sm.bitmap[id >> 5], 1u << (id & 31));
     }
   __syncthreads();
-  const uint32_t w0 = 2 * tid < n_words ? sm.bitmap[2 * tid] : 0u;
-  const uint32_t w1 = 2 * tid + 1 < n_words ? sm.bitmap[2 * tid + 1] : 0u;
-  const uint32_t own = __builtin_popcount(w0) + __builtin_popcount(w1);
-  uint32_t incl = own;  // inclusive prefix over the wave
+  // exclusive prefix of the kept counts over the bitmap words; thread t owns
+  // words WPT*t .. WPT*t + WPT-1
+  constexpr int WPT = kBitmapWords / kPickThreads;
+  uint32_t cnt[WPT];
+  uint32_t own = 0u;
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t v = (uint32_t)__shfl_up((int)incl, o, kWave);
-    if (lane >= o) incl += v;
+  for (int i = 0; i < WPT; ++i) {
+    const int wi = WPT * tid + i;
+    cnt[i] = wi < n_words ? (uint32_t)__builtin_popcount(sm.bitmap[wi]) : 0u;
+    own += cnt[i];
   }
+  const uint32_t incl = wave_prefix_sum_u32(own);
   if (lane == kWave - 1) sm.wave_tot[w] = incl;
   __syncthreads();
   uint32_t before = incl - own;
   for (int i = 0; i < w; ++i) before += sm.wave_tot[i];
-  if (2 * tid < n_words) sm.word_pre[2 * tid] = before;
-  if (2 * tid + 1 < n_words) sm.word_pre[2 * tid + 1] = before + __builtin_popcount(w0);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int wi = WPT * tid + i;
+    if (wi < n_words) sm.word_pre[wi] = before;
+    before += cnt[i];
+  }
   __syncthreads();
 #pragma unroll
   for (int p = 0; p < kPoolPerThread; ++p)

@@ -1,8 +1,8 @@
-"""GPU parity at the full sizes of the four bf16 workloads, in the launch
+"""GPU parity at the full sizes of the bf16 workloads, in the launch
 configuration the benchmark times (plans depend only on the shapes).
 
 Selections are checked row by row wherever the oracle can afford it (every
-row of the 32K, 8K and 1M workloads; sampled rows of the 64 x 128K batch,
+row of the 32K, 8K, 1M and 256K ratio-4 workloads; sampled rows of the 64 x 128K batch,
 plus the planted-block property on all of its rows). Outputs are compared on
 every row of the decode workloads and on sampled rows of the prefill.
 """
@@ -21,16 +21,17 @@ pytestmark = pytest.mark.gpu
 
 def decode_full(case: Case):
     w = case.w
-    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k, keep_tail=w.keep_tail)
     k_comp = torch.empty(w.batch, w.n_kv_heads, case.kv_cap // w.block_size, w.head_dim, device="cuda")
     qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
     q = case.q.view(w.batch, w.n_q_heads, w.head_dim)
-    out, sel, scores = qsa.decode(q, case.k, case.v, w.kv_len, w.block_size, w.top_k, k_comp, with_scores=True)
+    out, sel, scores = qsa.decode(q, case.k, case.v, w.kv_len, w.block_size, w.top_k, k_comp, with_scores=True,
+                                  keep_tail=w.keep_tail)
     torch.cuda.synchronize()
     return sel.cpu().numpy()[:, None], from_device(out)[:, None], scores.cpu().numpy()[:, None], k_comp
 
 
-@pytest.mark.parametrize("name", ["decode_32k", "decode_1m"])
+@pytest.mark.parametrize("name", ["decode_32k", "decode_1m", "decode_256k_r4"])
 def test_decode_workload(name):
     w = S.WORKLOADS[name]
     log(f"workload {name}: generating")
