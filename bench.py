@@ -146,8 +146,8 @@ class Step:
             self.calls.insert(0, ("compress", self.compress))
 
     def _ws(self, op, q_len, kv_len):
-        n = self.qsa.qsa_workspace_bytes(self.shape, op, q_len, kv_len)
-        return self.torch.empty(max(n, 16), dtype=self.torch.uint8, device="cuda")
+        ws = self.qsa.workspace(self.shape, op, q_len, kv_len, "cuda")
+        return ws if ws is not None else self.torch.empty(16, dtype=self.torch.uint8, device="cuda")
 
     def compress(self):
         self.qsa.qsa_compress_keys(self.shape, self.k, self.w.kv_len, self.k_comp, block_begin=self.blk_begin)

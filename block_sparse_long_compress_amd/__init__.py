@@ -31,6 +31,7 @@ from .binding import (  # noqa: F401
     qsa_sparse_attn_prefill,
     qsa_workspace_bytes,
     status_str,
+    workspace,
 )
 
 

@@ -112,10 +112,19 @@ def _stream(t, stream):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _workspace(shape, op, q_len, kv_len, ws, device):
+def workspace(shape: QsaShape, op: int, q_len: int, kv_len: int, device) -> torch.Tensor | None:
+    """A workspace for these sizes, ready for its first call (decode workspaces start zero-filled)."""
     need = qsa_workspace_bytes(shape, op, q_len, kv_len)
-    if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if need == 0:
+        return None
+    if op == QSA_OP_DECODE:
+        return torch.zeros(need, dtype=torch.uint8, device=device)
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def _workspace(shape, op, q_len, kv_len, ws, device):
+    if ws is None:
+        ws = workspace(shape, op, q_len, kv_len, device)
     return ws, (ws.numel() * ws.element_size() if ws is not None else 0)
 
 

@@ -20,8 +20,11 @@
 // Grid: one workgroup (4 waves) per (sequence, KV head, slice of the
 // selection list). Waves take units round-robin; the workgroup merges its
 // waves' partial softmax states in LDS and writes the output directly when a
-// row has one slice, else a partial state that decode_combine_kernel merges
-// in slice order. No atomics: results are bitwise reproducible.
+// row has one slice. Otherwise it writes its partial state to the workspace
+// at the device-coherent level and takes a ticket from the row's arrival
+// counter; the last workgroup of the row merges all slices in slice order
+// and resets the counter to zero. The merge order is fixed, so results are
+// bitwise reproducible whichever workgroup arrives last.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 
@@ -44,17 +47,92 @@ struct DecodeSmem {
   static constexpr int kBytes = kStage > kComb ? kStage : kComb;
 };
 
+// Merge of a row's slice states by its last workgroup: slices in batches of
+// SB, each batch's loads all in flight (one memory round trip), folded in
+// slice order into a running state per group of 4 output dims; GPT groups
+// per thread cover the G * D / 4 groups of the row.
+template <int D, int GPT, int SB>
+__device__ __forceinline__ void merge_slices(__amdgpu_buffer_rsrc_t prs, unsigned char* smem, uint16_t* out,
+                                             int64_t b, int g, int hq, int G, int n_split, int tid) {
+  const int stride = 2 * G + G * D;
+  const int n_g4 = G * (D / 4);
+  float* st = reinterpret_cast<float*>(smem);  // [SB][2G] maxima and sums of the batch
+  float Mr[GPT], Lr[GPT];
+  f32x4_t Or[GPT];
+#pragma unroll
+  for (int q4 = 0; q4 < GPT; ++q4) {
+    Mr[q4] = -__builtin_inff();
+    Lr[q4] = 0.f;
+    Or[q4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s0 = 0; s0 < n_split; s0 += SB) {
+    const int nb = n_split - s0 < SB ? n_split - s0 : SB;
+    __syncthreads();  // the previous batch's statistics are consumed
+    for (int i = tid; i < nb * 2 * G; i += 256) {
+      const int sl = i / (2 * G), j = i % (2 * G);
+      st[i] = __uint_as_float(load_coherent(prs, (s0 + sl) * stride + j));
+    }
+    f32x4_t ov[GPT][SB];
+#pragma unroll
+    for (int q4 = 0; q4 < GPT; ++q4) {
+      const int gi = tid + 256 * q4;
+      const int h = gi / (D / 4), e4 = 4 * (gi % (D / 4));
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        ov[q4][j] = (gi < n_g4 && j < nb)
+                        ? __builtin_bit_cast(f32x4_t, load4_coherent(prs, (s0 + j) * stride + 2 * G + h * D + e4))
+                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q4 = 0; q4 < GPT; ++q4) {
+      const int gi = tid + 256 * q4;
+      if (gi >= n_g4) continue;
+      const int h = gi / (D / 4);
+      float ms[SB];
+      float mb = Mr[q4];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        ms[j] = j < nb ? st[j * 2 * G + h] : -__builtin_inff();
+        mb = fmaxf(mb, ms[j]);
+      }
+      if (mb == -__builtin_inff()) continue;  // no visible key so far
+      const float a = __builtin_amdgcn_exp2f(Mr[q4] - mb);  // 0 while Mr = -inf
+      Lr[q4] *= a;
+      Or[q4] *= a;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const float f = __builtin_amdgcn_exp2f(ms[j] - mb);  // 0 for empty and missing slices
+        Lr[q4] += j < nb ? f * st[j * 2 * G + G + h] : 0.f;
+        Or[q4] += f * ov[q4][j];
+      }
+      Mr[q4] = mb;
+    }
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < GPT; ++q4) {
+    const int gi = tid + 256 * q4;
+    if (gi >= n_g4) continue;
+    const int h = gi / (D / 4), e4 = 4 * (gi % (D / 4));
+    const float inv = 1.f / Lr[q4];
+    const u32x2_t v = {pack_bf16x2(Or[q4][0] * inv, Or[q4][1] * inv), pack_bf16x2(Or[q4][2] * inv, Or[q4][3] * inv)};
+    *reinterpret_cast<u32x2_t*>(out + (b * hq + (int64_t)g * G + h) * D + e4) = v;
+  }
+}
+
 template <int D, bool GATHER>
 __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, const int32_t* __restrict__ sel,
                                                           uint16_t* __restrict__ out, float* __restrict__ part,
-                                                          int64_t kv_len, int64_t kv_cap, int hq, int hkv, int G,
-                                                          int bs, int top_k, float scale_log2, int bpw, int n_split) {
+                                                          uint32_t* __restrict__ counters, int64_t kv_len,
+                                                          int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k,
+                                                          float scale_log2, int bpw, int n_split) {
   using SM = DecodeSmem<D>;
   constexpr int RS = SM::RS;
   constexpr int KS = D / 32;  // 32-wide K steps of the QK^T product
   constexpr int DT = D / 16;  // 16-wide dim tiles of the PV product
   __shared__ __align__(16) unsigned char smem[SM::kBytes];
+  __shared__ int last_wg;
 
   const int64_t row = blockIdx.x / n_split;
   const int split = blockIdx.x % n_split;
@@ -245,73 +323,63 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
     for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
 
+  if (n_split == 1) {
+    for (int idx = tid; idx < G * D; idx += 256) {
+      const int h = idx / D, e = idx % D;
+      float M = -__builtin_inff();
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
+      float L = 0.f, O = 0.f;
+      for (int ww = 0; ww < 4; ++ww) {
+        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
+        L += f * cl[ww * 16 + h];
+        O += f * co[(ww * 16 + h) * D + e];
+      }
+      out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
+    }
+    return;
+  }
+
+  // Several slices per row: this slice's state goes out with stores that
+  // reach the device-coherent level (cache policy sc1: no L2 write-back
+  // needed), then one ticket per workgroup; the last workgroup of the row
+  // to arrive merges every slice in order and resets the row's counter.
+  const int stride = 2 * G + G * D;  // floats per slice: maxima, sums, outputs
+  const auto prs = __builtin_amdgcn_make_buffer_rsrc(part + row * (int64_t)n_split * stride, 0,
+                                                     n_split * stride * 4, kBufferFlags);
+  const int soff = split * stride;
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D, e = idx % D;
     float M = -__builtin_inff();
     for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
     float L = 0.f, O = 0.f;
-    if (M != -__builtin_inff()) {
+    if (M != -__builtin_inff()) {  // a slice may hold no visible key
       for (int ww = 0; ww < 4; ++ww) {
         const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
         L += f * cl[ww * 16 + h];
         O += f * co[(ww * 16 + h) * D + e];
       }
     }
-    if (n_split == 1) {
-      out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
-    } else {
-      float* pp = part + (row * n_split + split) * (int64_t)(2 * G + G * D);
-      if (e == 0) {
-        pp[h] = M;
-        pp[G + h] = L;
-      }
-      pp[2 * G + h * D + e] = O;
+    if (e == 0) {
+      store_coherent(prs, soff + h, __float_as_uint(M));
+      store_coherent(prs, soff + G + h, __float_as_uint(L));
     }
+    store_coherent(prs, soff + 2 * G + h * D + e, __float_as_uint(O));
   }
-}
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (uint32_t)(n_split - 1);
+    if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_wg = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_wg) return;
 
-// Merge the slices' partial softmax states of one (row, query head), one
-// output dim per thread, slices in order.
-template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                           int hq, int hkv, int G, int n_split) {
-  const int64_t row = blockIdx.x / G;
-  const int h = blockIdx.x % G;
-  const int e = threadIdx.x;
-  const int64_t b = row / hkv;
-  const int g = (int)(row % hkv);
-  const int64_t stride = 2 * G + G * D;
-  const float* pr = part + row * n_split * stride;
-  // Slices in batches of 32 whose loads all go out at once (one memory round
-  // trip per batch), folded in slice order into a running state.
-  constexpr int kBatch = 32;
-  float M = -__builtin_inff(), L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
-    float ms[kBatch], ls[kBatch], os[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const bool ok = s0 + j < n_split;
-      const float* ps = pr + (int64_t)(s0 + j) * stride;
-      ms[j] = ok ? ps[h] : -__builtin_inff();
-      ls[j] = ok ? ps[G + h] : 0.f;
-      os[j] = ok ? ps[2 * G + h * D + e] : 0.f;
-    }
-    float mb = M;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) mb = fmaxf(mb, ms[j]);
-    if (mb == -__builtin_inff()) continue;  // no visible key so far
-    const float a = __builtin_amdgcn_exp2f(M - mb);  // 0 while M = -inf
-    L *= a;
-    O *= a;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const float f = __builtin_amdgcn_exp2f(ms[j] - mb);  // 0 for empty slices
-      L += f * ls[j];
-      O += f * os[j];
-    }
-    M = mb;
-  }
-  out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
+  // 64 registers of staged values per batch: 16 slices for one group of 4
+  // dims per thread, 8 slices for two (G = 16 at d = 128)
+  if (G * (D / 4) <= 256) merge_slices<D, 1, 16>(prs, smem, out, b, g, hq, G, n_split, tid);
+  else merge_slices<D, 2, 8>(prs, smem, out, b, g, hq, G, n_split, tid);
 }
 
 template <int D>
@@ -320,14 +388,13 @@ hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const 
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const float scale_log2 = s.scale * 1.4426950408889634f;
   auto kern = s.bs < kUnit ? decode_attn_kernel<D, true> : decode_attn_kernel<D, false>;
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + decode_counter_bytes(rows))
+                                 : nullptr;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * plan.n_split)), dim3(256), 0, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sel,
-                     static_cast<uint16_t*>(out), static_cast<float*>(ws), kv_len, kv_cap, s.hq, s.hkv, s.group,
-                     s.bs, s.top_k, scale_log2, plan.blocks_per_wg, plan.n_split);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.n_split == 1) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(rows * s.group)), dim3(D), 0, st,
-                     static_cast<const float*>(ws), static_cast<uint16_t*>(out), s.hq, s.hkv, s.group, plan.n_split);
+                     static_cast<uint16_t*>(out), part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
+                     scale_log2, plan.blocks_per_wg, plan.n_split);
   return hipGetLastError();
 }
 
@@ -346,7 +413,10 @@ DecodePlan plan_decode(const Dims& s, int64_t kv_len) {
   if (bpw > s.top_k) bpw = s.top_k;
   p.blocks_per_wg = bpw;
   p.n_split = (s.top_k + bpw - 1) / bpw;
-  p.ws_bytes = p.n_split > 1 ? (size_t)rows * p.n_split * (2 * s.group + s.group * s.d) * sizeof(float) : 0;
+  // arrival counters (kept at zero between calls), then the partial states
+  p.ws_bytes = p.n_split > 1 ? decode_counter_bytes(rows) +
+                                   (size_t)rows * p.n_split * (2 * s.group + s.group * s.d) * sizeof(float)
+                             : 0;
   return p;
 }
 

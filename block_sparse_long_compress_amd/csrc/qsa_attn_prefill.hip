@@ -163,7 +163,6 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) { wait_vmcnt_le_impl<63>(n 
 // vmcnt waits that publish a wave's copies.
 __device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(uintptr_t)p; }
 // Word 3 of a raw buffer descriptor (byte offsets, no swizzle).
-constexpr int kBufferFlags = 0x00020000;
 typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ lds_void_t* lds_ptr(void* p) { return (lds_void_t*)(uintptr_t)lds_addr(p); }
 // 16 bytes per lane from buffer `rs` at byte offset voff into LDS at dst + 16 * lane.

@@ -384,6 +384,26 @@ __device__ __forceinline__ uint64_t topk_fold_sorted(uint64_t cur, uint64_t fres
   return wave_merge_desc(cur, fresh_desc);
 }
 
+// ---------------------------------------------------------------- device-coherent access
+//
+// Buffer loads and stores with cache policy sc1 reach the device-coherent
+// level directly (no L2 write-back or invalidate of other data), so workgroups
+// of one kernel on different XCDs can hand data over once the stores have
+// completed. Offsets are in 4-byte words from the resource base.
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource word 3 for gfx950
+constexpr int kPolicySc1 = 16;
+
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t rs, int word, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, rs, word * 4, 0, kPolicySc1);
+}
+__device__ __forceinline__ uint32_t load_coherent(__amdgpu_buffer_rsrc_t rs, int word) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, word * 4, 0, kPolicySc1);
+}
+__device__ __forceinline__ u32x4_t load4_coherent(__amdgpu_buffer_rsrc_t rs, int word) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, word * 4, 0, kPolicySc1);
+}
+
 // ---------------------------------------------------------------- MFMA
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {

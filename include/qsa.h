@@ -117,8 +117,12 @@ const char* qsa_status_str(qsa_status status);
 /* Bytes of device workspace the given op needs for these sizes (0 if none;
  * (size_t)-1 if the arguments are invalid). op is one of QSA_OP_*.
  * QSA_OP_SELECT and QSA_OP_PREFILL take q_len and kv_len = q_pos0 + q_len;
- * QSA_OP_DECODE takes kv_len (q_len ignored). The workspace holds only
- * scratch data of one call; its contents need no initialisation. */
+ * QSA_OP_DECODE takes kv_len (q_len ignored). Select and prefill workspaces
+ * hold only scratch data of one call and need no initialisation. A decode
+ * workspace starts with one arrival counter per (sequence, KV head)
+ * (4 * b * Hkv bytes rounded up to 256): zero-fill it once before its first
+ * use; every call leaves the counters at zero, so it can then be reused by
+ * any later decode call it is large enough for. */
 size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_t kv_len);
 
 /* Block compression ("Qwen4 architecture: QSA, GatedResidual, PLE", section 1:
@@ -156,7 +160,9 @@ qsa_status qsa_score_select(const qsa_shape* shape, const void* q, int64_t q_len
  * Address-Selection Problem...": ordinary attention restricted to the
  * selected cells). q: [b][Hq][d]; k, v: [b][Hkv][kv_cap][d];
  * sel: [b][Hkv][k] from qsa_score_select; out: [b][Hq][d]. Blocks shorter
- * than 32 keys are gathered several to one 32-key MFMA step.
+ * than 32 keys are gathered several to one 32-key MFMA step. When a row is
+ * split over several workgroups, the last one to finish merges the slices
+ * (see the workspace note of qsa_workspace_bytes: zero-filled before first use).
  * ws: device scratch of qsa_workspace_bytes(shape, QSA_OP_DECODE, 1, kv_len). */
 qsa_status qsa_sparse_attn_decode(const qsa_shape* shape, const void* q, const void* k, const void* v,
                                   int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out,

@@ -66,7 +66,7 @@ def test_workspace_sizes(qsa):
     assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_PREFILL, 100, 100) == 2 * 128 * 128 * 2
     # decode: one partial softmax state per (row, slice) when a row is split
     dec = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE, 1, 32768)
-    assert dec % (2 * (2 * 8 + 8 * 128) * 4) == 0
+    assert (dec - 256) % (2 * (2 * 8 + 8 * 128) * 4) == 0  # arrival counters, then partial states
     # select: chunk lists of the split path (decode) or nothing (tile path)
     assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 8192, 8192) == 0
     assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 1, 1 << 20) % (2 * 15 * 8) == 0

@@ -202,9 +202,10 @@ REUSE_CASES = [
 
 @pytest.mark.parametrize("w,steps", REUSE_CASES, ids=lambda x: case_id(x) if isinstance(x, S.Workload) else "")
 def test_workspace_reuse_across_decode_steps(w, steps):
-    """One select and one decode workspace, filled with garbage once, serve a
-    run of decode steps (split selection and split attention): every step
-    equals a call with fresh workspaces."""
+    """One select and one decode workspace, filled with garbage once (the
+    decode counters zeroed), serve a run of decode steps (split selection and
+    split attention): every step equals a call with fresh workspaces, so every
+    call leaves the counters at zero."""
     case = Case(w, seed=8)
     b, hq, d = w.batch, w.n_q_heads, w.head_dim
     shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k, keep_tail=w.keep_tail)
@@ -216,7 +217,11 @@ def test_workspace_reuse_across_decode_steps(w, steps):
     n_dec = max(qsa.qsa_workspace_bytes(shape, qsa.QSA_OP_DECODE, 1, n) for n in steps)
     assert n_sel > 0 and n_dec > 0, "both calls must take their split paths"
     ws_sel = torch.full((n_sel,), 0xA5, dtype=torch.uint8, device="cuda")
+    # decode workspace: arrival counters zero-filled once (the documented
+    # precondition), garbage in the partial states
     ws_dec = torch.full((n_dec,), 0x5A, dtype=torch.uint8, device="cuda")
+    n_cnt = (4 * b * w.n_kv_heads + 255) // 256 * 256
+    ws_dec[:n_cnt].zero_()
     for n in steps:
         log(f"workspace reuse step kv_len={n}")
         outs = []
@@ -230,6 +235,7 @@ def test_workspace_reuse_across_decode_steps(w, steps):
         torch.cuda.synchronize()
         assert torch.equal(outs[0][0], outs[1][0])
         assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+        assert int(ws_dec[:n_cnt].count_nonzero()) == 0, "arrival counters not left at zero"
     # the last step against the oracle (rows at position n - 1 read only
     # blocks and keys below n)
     rows = [(bb, 0, g) for bb in range(b) for g in range(w.n_kv_heads)]
