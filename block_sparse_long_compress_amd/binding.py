@@ -113,13 +113,11 @@ def _stream(t, stream):
 
 
 def workspace(shape: QsaShape, op: int, q_len: int, kv_len: int, device) -> torch.Tensor | None:
-    """A workspace for these sizes, ready for its first call (decode workspaces start zero-filled)."""
+    """A zero-filled workspace for these sizes, ready for its first call and reusable afterwards."""
     need = qsa_workspace_bytes(shape, op, q_len, kv_len)
     if need == 0:
         return None
-    if op == QSA_OP_DECODE:
-        return torch.zeros(need, dtype=torch.uint8, device=device)
-    return torch.empty(need, dtype=torch.uint8, device=device)
+    return torch.zeros(need, dtype=torch.uint8, device=device)
 
 
 def _workspace(shape, op, q_len, kv_len, ws, device):
