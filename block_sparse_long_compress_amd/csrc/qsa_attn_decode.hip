@@ -389,7 +389,7 @@ hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const 
   const float scale_log2 = s.scale * 1.4426950408889634f;
   auto kern = s.bs < kUnit ? decode_attn_kernel<D, true> : decode_attn_kernel<D, false>;
   uint32_t* counters = static_cast<uint32_t*>(ws);
-  float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + decode_counter_bytes(rows))
+  float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows))
                                  : nullptr;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * plan.n_split)), dim3(256), 0, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sel,
@@ -414,7 +414,7 @@ DecodePlan plan_decode(const Dims& s, int64_t kv_len) {
   p.blocks_per_wg = bpw;
   p.n_split = (s.top_k + bpw - 1) / bpw;
   // arrival counters (kept at zero between calls), then the partial states
-  p.ws_bytes = p.n_split > 1 ? decode_counter_bytes(rows) +
+  p.ws_bytes = p.n_split > 1 ? counter_bytes(rows) +
                                    (size_t)rows * p.n_split * (2 * s.group + s.group * s.d) * sizeof(float)
                              : 0;
   return p;

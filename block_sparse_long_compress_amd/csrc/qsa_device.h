@@ -403,6 +403,12 @@ __device__ __forceinline__ uint32_t load_coherent(__amdgpu_buffer_rsrc_t rs, int
 __device__ __forceinline__ u32x4_t load4_coherent(__amdgpu_buffer_rsrc_t rs, int word) {
   return __builtin_amdgcn_raw_buffer_load_b128(rs, word * 4, 0, kPolicySc1);
 }
+__device__ __forceinline__ u32x2_t load2_coherent(__amdgpu_buffer_rsrc_t rs, int word) {
+  return __builtin_amdgcn_raw_buffer_load_b64(rs, word * 4, 0, kPolicySc1);
+}
+__device__ __forceinline__ void store2_coherent(__amdgpu_buffer_rsrc_t rs, int word, uint32_t lo, uint32_t hi) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, rs, word * 4, 0, kPolicySc1);
+}
 
 // ---------------------------------------------------------------- MFMA
 

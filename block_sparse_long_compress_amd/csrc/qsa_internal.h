@@ -18,6 +18,11 @@ struct Dims {
 hipError_t launch_compress(const Dims& s, const void* k, int64_t kv_cap, int64_t blk_begin, int64_t blk_end,
                            float* k_comp, hipStream_t st);
 
+// Bytes at the start of a workspace holding one arrival counter per row (of
+// the decode attention, or of the split selection); they must be zero before
+// the first call and every call leaves them zero.
+inline size_t counter_bytes(int64_t rows) { return ((size_t)rows * 4 + 255) / 256 * 256; }
+
 // Selection ------------------------------------------------------------------
 struct SelectPlan {
   bool tiled;          // prefill-style tile path (rows share candidates)
@@ -44,10 +49,7 @@ struct DecodePlan {
   size_t ws_bytes;
 };
 DecodePlan plan_decode(const Dims& s, int64_t kv_len);
-// Bytes at the start of a decode workspace holding one arrival counter per
-// (sequence, KV head); they must be zero before the first call and every call
-// leaves them zero.
-inline size_t decode_counter_bytes(int64_t rows) { return ((size_t)rows * 4 + 255) / 256 * 256; }
+
 hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
                          int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* ws, hipStream_t st);
 

@@ -26,10 +26,12 @@
 //    chunks spread over the whole GPU. Each wave streams 64 compressed keys
 //    per step with fully coalesced 16-byte loads (1 KiB per instruction),
 //    finishes the dot products with a transpose-reduce butterfly, and keeps a
-//    running top list; the chunk's list goes to the workspace and a merge
-//    kernel reduces the lists of a row, skipping every key below the best
-//    chunk-local cutoff (a valid lower bound of the row's cutoff); when all
-//    the lists of a row hold at most 256 keys, one wave takes them at once.
+//    running top list; the chunk's list goes to the workspace with
+//    device-coherent stores, and the last workgroup of the row to finish
+//    (an arrival counter per row) reduces the lists, skipping every key below
+//    the best chunk-local cutoff (a valid lower bound of the row's cutoff);
+//    when all the lists of a row hold at most 256 keys, one wave takes them
+//    at once.
 //  * large path (k > 64, the released budget of 512 blocks): a score pass
 //    writes every candidate's score and, per chunk of 256 candidates, the
 //    chunk's 16 best keys in order; one workgroup per row then finds the
@@ -252,29 +254,136 @@ __device__ __forceinline__ float dot64_rows(const float* __restrict__ rows_base,
   return res[0];
 }
 
+constexpr int kMergeCap = 2048;              // survivors kept in LDS; more go straight from memory
+constexpr int kSmallMergeKeys = 4 * kWave;   // lists this small are merged by one wave at once
+
+struct SplitSmem {
+  uint64_t lists[4][kWave];
+  uint64_t surv[kMergeCap];
+  uint64_t bound;
+  int n_surv;
+  int last_wg;
+};
+
+// Key i of a row's chunk lists in the workspace (device-coherent read; the
+// lists were written by other workgroups of the same kernel).
+__device__ __forceinline__ uint64_t list_key(__amdgpu_buffer_rsrc_t rs, int64_t i) {
+  const u32x2_t v = load2_coherent(rs, (int)(2 * i));
+  return ((uint64_t)v[1] << 32) | v[0];
+}
+
+// Merge of lists that hold at most 256 keys in all (the first `slots`
+// entries of each of the n_chunks lists, stride sm): wave 0 loads every key
+// at once (4 per lane) and takes the top set directly.
+__device__ void merge_lists_small(__amdgpu_buffer_rsrc_t rs, int64_t n_chunks, int sm, int slots, int forced,
+                                  int top_k, uint64_t* scratch, int32_t* sel_row, float* score_row) {
+  const int lane = lane_id();
+  const int n_keys = (int)n_chunks * slots;
+  uint64_t x[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = lane + kWave * p;
+    x[p] = i < n_keys ? list_key(rs, (int64_t)(i / slots) * sm + i % slots) : 0ull;
+  }
+  TopSet set{0ull, 0, 0ull};
+  topset_absorb<4>(set, x, slots, scratch);
+  finalize_row(set.keys, slots, forced, top_k, sel_row, score_row);
+}
+
+// Merge of a row's chunk lists (each descending) by one workgroup. The
+// slots-th largest of the chunk maxima is a key that at least `slots` real
+// keys reach, so every key below it can be dropped: only a short prefix of
+// each list survives (on noise-like scores a few keys beyond `slots` in
+// total). Survivors are folded in groups of 64.
+__device__ void merge_lists(__amdgpu_buffer_rsrc_t rs, int64_t n_chunks, int sm, int slots, int forced, int top_k,
+                            SplitSmem& smem, int32_t* sel_row, float* score_row) {
+  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  // The first 4 entries of this thread's first chunk list load together with
+  // the chunk maxima below (survivors rarely go deeper on noise-like scores).
+  constexpr int kPre = 4;
+  uint64_t pre[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) pre[j] = (tid < n_chunks && j < slots) ? list_key(rs, (int64_t)tid * sm + j) : 0ull;
+  // bound = slots-th largest chunk maximum (0 when there are fewer chunks)
+  if (w == 0) {
+    uint64_t cur = 0ull;
+    for (int64_t base = 0; base < n_chunks; base += kWave) {
+      const uint64_t x = base + lane < n_chunks ? list_key(rs, (base + lane) * sm) : 0ull;
+      cur = topk_fold(cur, x, slots);
+    }
+    if (lane == 0) {
+      smem.bound = n_chunks >= slots ? readlane_u64(cur, slots - 1) : 0ull;
+      smem.n_surv = 0;
+    }
+  }
+  __syncthreads();
+  const uint64_t bound = smem.bound;
+  // survivors: the prefix of each list at or above the bound, read in groups
+  // of 4 independent loads
+  for (int64_t c = tid; c < n_chunks; c += 256) {
+    for (int j0 = 0; j0 < slots; j0 += kPre) {
+      uint64_t x[kPre];
+#pragma unroll
+      for (int j = 0; j < kPre; ++j)
+        x[j] = (c == tid && j0 == 0) ? pre[j] : (j0 + j < slots ? list_key(rs, c * sm + j0 + j) : 0ull);
+      bool more = true;
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) {
+        if (more && j0 + j < slots && x[j] >= bound) {
+          const int at = atomicAdd(&smem.n_surv, 1);
+          if (at < kMergeCap) smem.surv[at] = x[j];
+        } else {
+          more = false;
+        }
+      }
+      if (!more) break;
+    }
+  }
+  __syncthreads();
+  const int total = smem.n_surv;
+  uint64_t cur = 0ull;
+  if (total <= kMergeCap) {
+    for (int base = kWave * w; base < total; base += 4 * kWave) {
+      const uint64_t x = base + lane < total ? smem.surv[base + lane] : 0ull;
+      cur = topk_fold(cur, x, slots);
+    }
+  } else {  // adversarial inputs: fold every key at or above the bound from memory
+    const int64_t n_keys = n_chunks * sm;
+    for (int64_t base = (int64_t)kWave * w; base < n_keys; base += 4 * kWave) {
+      const int64_t idx = base + lane;
+      uint64_t key = 0ull;
+      if (idx < n_keys && (int)(idx % sm) < slots) key = list_key(rs, idx);
+      cur = topk_fold(cur, key >= bound ? key : 0ull, slots);
+    }
+  }
+  cur = merge_wave_lists(smem.lists, cur, slots);
+  if (w == 0) finalize_row(cur, slots, forced, top_k, sel_row, score_row);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__ q, const float* __restrict__ k_comp,
                                                            int32_t* __restrict__ sel, float* __restrict__ sel_scores,
-                                                           uint64_t* __restrict__ ws, int64_t q_len, int64_t q_pos0,
-                                                           int64_t nb_cap, int hq, int hkv, int G, int bs, int top_k,
-                                                           float scale, int keep_tail, int chunk, int64_t n_chunks) {
+                                                           uint32_t* __restrict__ counters, uint64_t* __restrict__ ws,
+                                                           int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
+                                                           int hkv, int G, int bs, int top_k, float scale,
+                                                           int keep_tail, int chunk, int64_t n_chunks) {
   constexpr int LPR = D / 4;
-  __shared__ uint64_t lists[4][kWave];
+  __shared__ SplitSmem smem;
 
   const int64_t row = blockIdx.x / n_chunks;
   const int64_t ch = blockIdx.x % n_chunks;
   const int64_t b = row / (q_len * hkv);
   const int64_t t = (row / hkv) % q_len;
   const int g = (int)(row % hkv);
-  const int lane = lane_id(), w = wave_id();
+  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
   const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
   const int slots = frame_slots(fr, top_k);
+  const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
+  int32_t* sel_row = sel + off;
+  float* score_row = sel_scores ? sel_scores + off : nullptr;
 
   if (slots == 0) {  // nothing to score: the forced block alone
-    if (ch == 0 && w == 0) {
-      const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-      finalize_row(0ull, 0, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
-    }
+    if (ch == 0 && w == 0) finalize_row(0ull, 0, fr.forced, top_k, sel_row, score_row);
     return;
   }
   // Each lane sums its own 4 dims of the group's queries: no barrier, so the
@@ -291,119 +400,33 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
     const uint64_t key = cand < c_end ? make_key(s * scale, (int)cand) : 0ull;
     cur = topk_fold(cur, key, slots);
   }
-  cur = merge_wave_lists(lists, cur, slots);
-  if (w != 0) return;
+  cur = merge_wave_lists(smem.lists, cur, slots);
   if (n_chunks == 1) {
-    const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-    finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
-  } else if (lane < slots) {
-    ws[(row * n_chunks + ch) * (top_k - 1) + lane] = cur;
+    if (w == 0) finalize_row(cur, slots, fr.forced, top_k, sel_row, score_row);
+    return;
   }
-}
-
-// One workgroup per row: reduce the row's chunk lists (each descending) to
-// the final top list. The slots-th largest of the chunk maxima is a key that
-// at least `slots` real keys reach, so every key below it can be dropped:
-// only a short prefix of each list survives (on noise-like scores a few keys
-// beyond `slots` in total). Survivors are folded in groups of 64.
-constexpr int kMergeCap = 2048;  // survivors kept in LDS; more go straight from memory
-
-__global__ __launch_bounds__(256) void select_merge_kernel(int32_t* __restrict__ sel, float* __restrict__ sel_scores,
-                                                           const uint64_t* __restrict__ ws, int64_t q_len,
-                                                           int64_t q_pos0, int hkv, int bs, int top_k, int keep_tail,
-                                                           int64_t n_chunks) {
-  __shared__ uint64_t lists[4][kWave];
-  __shared__ uint64_t surv[kMergeCap];
-  __shared__ uint64_t bound_s;
-  __shared__ int n_surv;
-  const int64_t row = blockIdx.x;
-  const int64_t b = row / (q_len * hkv);
-  const int64_t t = (row / hkv) % q_len;
-  const int g = (int)(row % hkv);
-  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
-  const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
-  const int slots = frame_slots(fr, top_k);
-  if (slots == 0) return;  // written by the split kernel
+  // Several chunks per row: the chunk's list goes out with device-coherent
+  // stores, then one ticket per workgroup; the last workgroup of the row to
+  // arrive merges the lists and resets the row's counter.
   const int sm = top_k - 1;
-  const uint64_t* lst = ws + row * n_chunks * sm;
-
-  // bound = slots-th largest chunk maximum (0 when there are fewer chunks)
-  if (w == 0) {
-    uint64_t cur = 0ull;
-    for (int64_t base = 0; base < n_chunks; base += kWave) {
-      const uint64_t x = base + lane < n_chunks ? lst[(base + lane) * sm] : 0ull;
-      cur = topk_fold(cur, x, slots);
-    }
-    if (lane == 0) {
-      bound_s = n_chunks >= slots ? readlane_u64(cur, slots - 1) : 0ull;
-      n_surv = 0;
-    }
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(ws + row * n_chunks * sm, 0, (int)(n_chunks * sm * 8),
+                                                    kBufferFlags);
+  if (w == 0 && lane < slots) store2_coherent(rs, (int)(2 * (ch * sm + lane)), (uint32_t)cur, (uint32_t)(cur >> 32));
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (uint32_t)(n_chunks - 1);
+    if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    smem.last_wg = last ? 1 : 0;
   }
   __syncthreads();
-  const uint64_t bound = bound_s;
-  // survivors: the prefix of each list at or above the bound
-  for (int64_t c = tid; c < n_chunks; c += 256) {
-    for (int j = 0; j < slots; ++j) {
-      const uint64_t x = lst[c * sm + j];
-      if (x < bound) break;
-      const int at = atomicAdd(&n_surv, 1);
-      if (at < kMergeCap) surv[at] = x;
-    }
+  if (!smem.last_wg) return;
+  if (n_chunks * slots <= kSmallMergeKeys) {
+    if (w == 0) merge_lists_small(rs, n_chunks, sm, slots, fr.forced, top_k, smem.lists[0], sel_row, score_row);
+  } else {
+    merge_lists(rs, n_chunks, sm, slots, fr.forced, top_k, smem, sel_row, score_row);
   }
-  __syncthreads();
-  const int total = n_surv;
-  uint64_t cur = 0ull;
-  if (total <= kMergeCap) {
-    for (int base = kWave * w; base < total; base += 4 * kWave) {
-      const uint64_t x = base + lane < total ? surv[base + lane] : 0ull;
-      cur = topk_fold(cur, x, slots);
-    }
-  } else {  // adversarial inputs: fold every key at or above the bound from memory
-    const int64_t n_keys = n_chunks * sm;
-    for (int64_t base = (int64_t)kWave * w; base < n_keys; base += 4 * kWave) {
-      const int64_t idx = base + lane;
-      uint64_t key = 0ull;
-      if (idx < n_keys && (int)(idx % sm) < slots) key = lst[idx];
-      cur = topk_fold(cur, key >= bound ? key : 0ull, slots);
-    }
-  }
-  cur = merge_wave_lists(lists, cur, slots);
-  if (w != 0) return;
-  const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-  finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
-}
-
-// Merge for rows whose chunk lists hold at most 256 keys in total: one wave
-// loads every key at once (4 per lane) and takes the top set directly.
-constexpr int kSmallMergeKeys = 4 * kWave;
-
-__global__ __launch_bounds__(64) void select_merge_small_kernel(int32_t* __restrict__ sel,
-                                                                float* __restrict__ sel_scores,
-                                                                const uint64_t* __restrict__ ws, int64_t q_len,
-                                                                int64_t q_pos0, int hkv, int bs, int top_k,
-                                                                int keep_tail, int64_t n_chunks) {
-  __shared__ uint64_t scratch[kWave];
-  const int64_t row = blockIdx.x;
-  const int64_t b = row / (q_len * hkv);
-  const int64_t t = (row / hkv) % q_len;
-  const int g = (int)(row % hkv);
-  const int lane = lane_id();
-  const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
-  const int slots = frame_slots(fr, top_k);
-  if (slots == 0) return;  // written by the split kernel
-  const int sm = top_k - 1;
-  const uint64_t* lst = ws + row * n_chunks * sm;
-  const int n_keys = (int)n_chunks * slots;  // the first `slots` entries of each list
-  uint64_t x[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int i = lane + kWave * p;
-    x[p] = i < n_keys ? lst[(int64_t)(i / slots) * sm + i % slots] : 0ull;
-  }
-  TopSet set{0ull, 0, 0ull};
-  topset_absorb<4>(set, x, slots, scratch);
-  const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
-  finalize_row(set.keys, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
 }
 
 // ------------------------------------------------------------------ large path
@@ -741,18 +764,11 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
                        nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, s.scale, s.keep_tail);
     return hipGetLastError();
   }
-  uint64_t* wsk = static_cast<uint64_t*>(ws);
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  uint64_t* wsk = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + (plan.n_chunks > 1 ? counter_bytes(rows) : 0));
   hipLaunchKernelGGL((select_split_kernel<T, D>), dim3((unsigned)(rows * plan.n_chunks)), dim3(256), 0, st, q,
-                     k_comp, sel, sel_scores, wsk, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
-                     s.scale, s.keep_tail, plan.chunk, plan.n_chunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.n_chunks == 1) return e;
-  if (plan.n_chunks * (s.top_k - 1) <= kSmallMergeKeys)
-    hipLaunchKernelGGL(select_merge_small_kernel, dim3((unsigned)rows), dim3(64), 0, st, sel, sel_scores, wsk, q_len,
-                       q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, plan.n_chunks);
-  else
-    hipLaunchKernelGGL(select_merge_kernel, dim3((unsigned)rows), dim3(256), 0, st, sel, sel_scores, wsk, q_len,
-                       q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, plan.n_chunks);
+                     k_comp, sel, sel_scores, counters, wsk, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs,
+                     s.top_k, s.scale, s.keep_tail, plan.chunk, plan.n_chunks);
   return hipGetLastError();
 }
 
@@ -789,7 +805,8 @@ SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
     p.chunk = 256 * u;
   }
   p.n_chunks = (max_cand + p.chunk - 1) / p.chunk;
-  if (p.n_chunks > 1) p.ws_bytes = (size_t)rows * p.n_chunks * (s.top_k - 1) * sizeof(uint64_t);
+  // arrival counters (kept at zero between calls), then the chunk lists
+  if (p.n_chunks > 1) p.ws_bytes = counter_bytes(rows) + (size_t)rows * p.n_chunks * (s.top_k - 1) * sizeof(uint64_t);
   return p;
 }
 

@@ -117,12 +117,15 @@ const char* qsa_status_str(qsa_status status);
 /* Bytes of device workspace the given op needs for these sizes (0 if none;
  * (size_t)-1 if the arguments are invalid). op is one of QSA_OP_*.
  * QSA_OP_SELECT and QSA_OP_PREFILL take q_len and kv_len = q_pos0 + q_len;
- * QSA_OP_DECODE takes kv_len (q_len ignored). Select and prefill workspaces
- * hold only scratch data of one call and need no initialisation. A decode
- * workspace starts with one arrival counter per (sequence, KV head)
- * (4 * b * Hkv bytes rounded up to 256): zero-fill it once before its first
- * use; every call leaves the counters at zero, so it can then be reused by
- * any later decode call it is large enough for. */
+ * QSA_OP_DECODE takes kv_len (q_len ignored).
+ * Zero-fill a workspace once before its first use. Decode workspaces, and
+ * selection workspaces whose rows are split over several workgroups, start
+ * with one arrival counter per row ((sequence, KV head), resp. (sequence,
+ * token, KV head): 4 bytes each, the area rounded up to 256 bytes); the last
+ * workgroup of a row to finish does the row's final step and resets its
+ * counter, so every call leaves that area at zero and the workspace can be
+ * reused by any later call of the same op it is large enough for. The rest is
+ * scratch of one call. */
 size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_t kv_len);
 
 /* Block compression ("Qwen4 architecture: QSA, GatedResidual, PLE", section 1:

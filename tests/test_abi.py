@@ -67,9 +67,9 @@ def test_workspace_sizes(qsa):
     # decode: one partial softmax state per (row, slice) when a row is split
     dec = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE, 1, 32768)
     assert (dec - 256) % (2 * (2 * 8 + 8 * 128) * 4) == 0  # arrival counters, then partial states
-    # select: chunk lists of the split path (decode) or nothing (tile path)
+    # select: arrival counters + chunk lists of the split path (decode), or nothing (tile path)
     assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 8192, 8192) == 0
-    assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 1, 1 << 20) % (2 * 15 * 8) == 0
+    assert (qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 1, 1 << 20) - 256) % (2 * 15 * 8) == 0
     f32 = good_shape(qsa, dtype=qsa.QSA_F32, head_dim=64, n_q_heads=2, n_kv_heads=1, block_size=32, top_k=4)
     assert qsa.qsa_workspace_bytes(f32, qsa.QSA_OP_PREFILL, 512, 512) == 0
     assert qsa.qsa_workspace_bytes(f32, qsa.QSA_OP_DECODE, 1, 512) == 0
