@@ -11,10 +11,13 @@ input, with every input already resident in HBM:
 * prefill workloads: compress every block, score + select for every token,
   sparse prefill attention; throughput is prompt tokens per second.
 
-The whole step is captured once in a HIP graph and the timed region replays
-it `steps` times (wall clock, synchronised on both sides). A second timed
-region replays each ABI call's own graph with HIP events recorded between the
-calls on the launch stream, giving per-call durations. The roofline entry is
+The step is captured in HIP graphs, `--graph-steps` whole steps back to back
+per graph (8 by default, so the host's graph-launch cost, tens of
+microseconds, does not starve the GPU between short steps), and the timed
+region runs exactly `steps` steps (wall clock, synchronised on both sides). A
+decode step is the one qsa_decode_step call. A second timed region launches
+each ABI call eagerly with HIP events recorded between the calls on the
+launch stream, giving per-call durations. The roofline entry is
 the call with the largest average duration, against the bound of its kernels
 (HBM bytes or bf16 MFMA flops, algorithmic counts only).
 
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch the calls eagerly instead of replaying graphs")
+    ap.add_argument("--graph-steps", type=int, default=8,
+                    help="whole steps captured back to back in one graph (amortises the host's graph launch)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (reference for memory counters)")
     return ap.parse_args()
@@ -128,10 +133,14 @@ class Step:
         self.sel = torch.empty(b, q_len, hkv, k, dtype=torch.int32, device="cuda")
         self.out = torch.empty_like(self.q)
         self.ws_sel = self._ws(qsa.QSA_OP_SELECT, q_len, w.kv_len)
+        self.fused = False
         if w.mode == "decode":
             self.q_dec = self.q.view(b, hq, d)
             self.out_dec = self.out.view(b, hq, d)
+            self.sel_dec = self.sel.view(b, hkv, k)
             self.ws_att = self._ws(qsa.QSA_OP_DECODE, 1, w.kv_len)
+            self.ws_step = self._ws(qsa.QSA_OP_DECODE_STEP, 1, w.kv_len)
+            self.fused = qsa.qsa_decode_step_fused(self.shape, w.kv_len)
             # everything before the new token is already compressed
             qsa.qsa_compress_keys(self.shape, self.k, w.kv_len - 1, self.k_comp)
             self.blk_begin = (w.kv_len - 1) // bs
@@ -141,13 +150,24 @@ class Step:
             self.blk_begin = 0
             self.n_new_blocks = w.kv_len // bs
         torch.cuda.synchronize()
+        # `calls`: the ABI calls of a step, each timed on its own; `step_calls`:
+        # what one step enqueues (a decode step is the one qsa_decode_step call,
+        # which runs the separate calls itself when it is not fused)
         self.calls = [("select", self.select), ("attend", self.attend)]
         if self.n_new_blocks > 0:
             self.calls.insert(0, ("compress", self.compress))
+        self.step_calls = [("step", self.decode_step)] if w.mode == "decode" else self.calls
+        if self.fused:
+            self.calls = self.step_calls
 
     def _ws(self, op, q_len, kv_len):
         ws = self.qsa.workspace(self.shape, op, q_len, kv_len, "cuda")
         return ws if ws is not None else self.torch.empty(16, dtype=self.torch.uint8, device="cuda")
+
+    def decode_step(self):
+        w = self.w
+        self.qsa.qsa_decode_step(self.shape, self.q_dec, self.k, self.v, self.k_comp, w.kv_len, self.sel_dec,
+                                 self.out_dec, ws=self.ws_step)
 
     def compress(self):
         self.qsa.qsa_compress_keys(self.shape, self.k, self.w.kv_len, self.k_comp, block_begin=self.blk_begin)
@@ -172,13 +192,16 @@ def capture_step(torch, st, stream):
     step's compression could run beside select + attend, since the block it
     closes is the token's own block and never one of its candidates; a
     forked graph branch costs more than the few microseconds it would hide.)"""
-    for _, fn in st.calls:
+    for _, fn in st.step_calls:
         fn()
 
 
-def run_gpu(w, steps, warmup, seed, use_graph):
-    """Timed region: `steps` replays of one graph holding a whole step (wall clock,
-    synchronised on both sides).
+def run_gpu(w, steps, warmup, seed, use_graph, graph_steps=8):
+    """Timed region: exactly `steps` whole steps, replayed from graphs that hold
+    `graph_steps` consecutive steps each (plus a one-step graph for the
+    remainder), wall clock, synchronised on both sides. Every step recomputes
+    everything from the resident inputs; the grouping only spreads the host's
+    graph-launch cost (tens of microseconds) over several steps.
 
     Per-call durations: the calls are launched eagerly, HIP events recorded
     between them on the launch stream, all queued behind a GPU sleep so that
@@ -190,23 +213,34 @@ def run_gpu(w, steps, warmup, seed, use_graph):
     st = Step(w, seed)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for _, fn in st.calls:
+        for _, fn in st.step_calls + st.calls:
             fn()  # eager warm-up before capture
         torch.cuda.synchronize()
+        group = max(1, graph_steps) if use_graph else 1
         if use_graph:
             step_graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(step_graph, stream=stream):
                 capture_step(torch, st, stream)
             run_step = step_graph.replay
+            group_graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(group_graph, stream=stream):
+                for _ in range(group):
+                    capture_step(torch, st, stream)
+            run_group = group_graph.replay
         else:
             def run_step():
                 capture_step(torch, st, stream)
+            run_group = run_step
         torch.cuda.synchronize()
         for _ in range(warmup):
             run_step()
+        for _ in range(max(1, warmup // group)):
+            run_group()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
+        for _ in range(steps // group):
+            run_group()
+        for _ in range(steps % group):
             run_step()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -361,8 +395,10 @@ def main():
     import qsa_synth as S
 
     w = S.WORKLOADS[args.workload]
-    st, wall, per_call, cold_s, call_timing = run_gpu(w, args.steps, args.warmup, args.seed, not args.no_graph)
+    st, wall, per_call, cold_s, call_timing = run_gpu(w, args.steps, args.warmup, args.seed, not args.no_graph,
+                                                      args.graph_steps)
     model = work_model(w, st.n_new_blocks)
+    model["step"] = {"bytes": sum(m["bytes"] for m in model.values()), "flops": sum(m["flops"] for m in model.values())}
     ms_per_step = 1e3 * wall / args.steps
     tokens = w.batch if w.mode == "decode" else w.batch * w.kv_len
     value = tokens * args.steps / wall
@@ -395,8 +431,11 @@ def main():
         "config": {"workload": w.name, "mode": w.mode, "batch": w.batch, "kv_len": w.kv_len,
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "top_k": w.top_k, "keep_tail": w.keep_tail, "seed": args.seed,
-                   "graphs": not args.no_graph},
-        "roofline": {"bound": bound, "kernel": f"{dominant} call", "achieved": round(achieved, 2), "peak": peak,
+                   "graphs": not args.no_graph, "graph_steps": 1 if args.no_graph else max(1, args.graph_steps),
+                   "fused_decode_step": st.fused},
+        "roofline": {"bound": bound,
+                     "kernel": "decode_step_kernel (the whole step)" if dominant == "step" else f"{dominant} call",
+                     "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name, dominant)},
         "calls": calls,

@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     QSA_F32,
     QSA_OP_COMPRESS,
     QSA_OP_DECODE,
+    QSA_OP_DECODE_STEP,
     QSA_OP_PREFILL,
     QSA_OP_SELECT,
     QsaError,
@@ -26,6 +27,8 @@ from .binding import (  # noqa: F401
     abi_version,
     make_shape,
     qsa_compress_keys,
+    qsa_decode_step,
+    qsa_decode_step_fused,
     qsa_score_select,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_prefill,

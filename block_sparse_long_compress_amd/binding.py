@@ -18,10 +18,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("QSA_LIB", os.path.join(HERE, "lib", "libqsa.so"))
 
 QSA_F32, QSA_BF16 = 0, 1
-QSA_OP_COMPRESS, QSA_OP_SELECT, QSA_OP_DECODE, QSA_OP_PREFILL = 0, 1, 2, 3
+QSA_OP_COMPRESS, QSA_OP_SELECT, QSA_OP_DECODE, QSA_OP_PREFILL, QSA_OP_DECODE_STEP = 0, 1, 2, 3, 4
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_ERR_WORKSPACE", 4: "QSA_ERR_HIP"}
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
-            "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill")
+            "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused")
 
 
 class QsaError(RuntimeError):
@@ -65,6 +65,10 @@ def _load() -> ctypes.CDLL:
     lib.qsa_sparse_attn_decode.argtypes = [SH, P, P, P, I64, I64, P, P, P, SZ, P]
     lib.qsa_sparse_attn_prefill.restype = ctypes.c_int
     lib.qsa_sparse_attn_prefill.argtypes = [SH, P, P, P, I64, I64, I64, P, P, P, SZ, P]
+    lib.qsa_decode_step.restype = ctypes.c_int
+    lib.qsa_decode_step.argtypes = [SH, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
+    lib.qsa_decode_step_fused.restype = ctypes.c_int
+    lib.qsa_decode_step_fused.argtypes = [SH, I64]
     return lib
 
 
@@ -164,3 +168,21 @@ def qsa_sparse_attn_prefill(shape: QsaShape, q, k, v, q_pos0: int, sel, out, ws=
                                        _ptr(sel), _ptr(out), _ptr(ws), nbytes, _stream(q, stream)),
            "qsa_sparse_attn_prefill")
     return out
+
+
+def qsa_decode_step(shape: QsaShape, q, k, v, k_comp, kv_len: int, sel, out, sel_scores=None, ws=None, stream=None):
+    """One decode step for ``q`` ``[b][Hq][d]`` at position ``kv_len - 1``: compress the block it completes
+    (into ``k_comp``), select (``sel`` ``[b][Hkv][k]``) and attend (``out``)."""
+    ws, nbytes = _workspace(shape, QSA_OP_DECODE_STEP, 1, kv_len, ws, q.device)
+    _check(LIB.qsa_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_comp), kv_len, k.shape[2],
+                               _ptr(sel), _ptr(sel_scores), _ptr(out), _ptr(ws), nbytes, _stream(q, stream)),
+           "qsa_decode_step")
+    return out
+
+
+def qsa_decode_step_fused(shape: QsaShape, kv_len: int) -> bool:
+    """Whether qsa_decode_step runs these sizes as one fused kernel."""
+    r = LIB.qsa_decode_step_fused(ctypes.byref(shape), kv_len)
+    if r < 0:
+        raise QsaError(1, "qsa_decode_step_fused")
+    return bool(r)

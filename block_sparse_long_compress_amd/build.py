@@ -25,6 +25,7 @@ SOURCES = [
     "qsa_attn_decode.hip",
     "qsa_attn_prefill.hip",
     "qsa_attn_f32.hip",
+    "qsa_decode_step.hip",
 ]
 
 ARCH = "gfx950"

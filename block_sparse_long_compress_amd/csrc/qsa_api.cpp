@@ -104,6 +104,16 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
     case QSA_OP_PREFILL:
       if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
       return qsa::plan_prefill(s, q_len, kv_len - q_len).ws_bytes;
+    case QSA_OP_DECODE_STEP: {
+      if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
+      const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
+      if (sp.fused) return sp.ws_bytes;
+      // the separate calls, each on its own part (the decode part keeps
+      // counters at its start that the selection must not overwrite)
+      const size_t a = qsa::align_up(qsa::plan_select(s, 1, kv_len - 1).ws_bytes, 256);
+      const size_t d = s.dtype == QSA_BF16 ? qsa::plan_decode(s, kv_len).ws_bytes : 0;
+      return a + d;
+    }
   }
   return (size_t)-1;
 }
@@ -184,6 +194,43 @@ qsa_status qsa_sparse_attn_prefill(const qsa_shape* shape, const void* q, const 
   const qsa::PrefillPlan plan = qsa::plan_prefill(s, q_len, q_pos0);
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
   return hip_status(qsa::launch_prefill(s, plan, q, k, v, q_len, q_pos0, kv_cap, sel, out, ws, hs));
+}
+
+int qsa_decode_step_fused(const qsa_shape* shape, int64_t kv_len) {
+  Dims s;
+  if (check_shape(shape, &s) != QSA_OK || kv_len <= 0 || kv_len > kMaxPositions) return -1;
+  return qsa::plan_decode_step(s, kv_len).fused ? 1 : 0;
+}
+
+qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,
+                           int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !k || !v || !k_comp || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_comp) || !aligned16(sel) || !aligned16(out))
+    return QSA_ERR_INVALID;
+  if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
+  if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
+  if (sp.fused) {
+    if ((int64_t)s.batch * s.hkv * sp.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+    if (sp.ws_bytes > 0 && (!ws || ws_bytes < sp.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+    return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, hs));
+  }
+  // separate launches: the block the new token completed, then selection and attention
+  const size_t need = qsa_workspace_bytes(shape, QSA_OP_DECODE_STEP, 1, kv_len);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  st = qsa_compress_keys(shape, k, kv_len, kv_cap, (kv_len - 1) / s.bs, k_comp, stream);
+  if (st != QSA_OK) return st;
+  const size_t sel_part = qsa::align_up(qsa::plan_select(s, 1, kv_len - 1).ws_bytes, 256);
+  st = qsa_score_select(shape, q, 1, kv_len - 1, k_comp, kv_len, kv_cap, sel, sel_scores, ws, sel_part, stream);
+  if (st != QSA_OK) return st;
+  void* ws_dec = ws ? static_cast<char*>(ws) + sel_part : nullptr;
+  return qsa_sparse_attn_decode(shape, q, k, v, kv_len, kv_cap, sel, out, ws_dec, need - sel_part, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,293 @@
+// One whole decode step per (sequence, KV head) in one workgroup: compress the
+// block the new token completed, score the compressed blocks and keep the
+// top-k ("Qwen4 in llama.cpp: Dissecting PR #27742", section "QSA Is an
+// Address-Selection Problem, Not a New Attention Equation": compressed-block
+// scoring, top-k, cache addresses), then attend over the kept blocks (same
+// section: ordinary attention over the selected cells).
+//
+// The separate calls hand the selection from kernel to kernel through HBM
+// and pay a launch and a cold read at each hand-off; for rows of a few
+// thousand candidates those latencies dominate the step. Here the 8 waves of
+// a workgroup stream the row's compressed keys (64 per wave-step, the
+// selection kernels' coalesced dot products) into per-wave top lists, merge
+// them in LDS, write the row's selection, and attend over it from LDS with the
+// decode kernels' unit loop; the waves' softmax states merge in LDS. When
+// the rows alone leave most of the GPU idle, each row gets S workgroups:
+// every one of them computes the (cheap) selection itself, attends over its
+// own slice of it, and the last to finish merges the S partial states
+// through the workspace exactly as the decode kernel merges its slices.
+// Selections equal the separate calls' (same arithmetic); outputs agree
+// within rounding (another merge order of the attention states).
+#include "qsa_decode_unit.h"
+#include "qsa_device.h"
+#include "qsa_internal.h"
+#include "qsa_select_wave.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kStepWaves = 8;
+
+template <int D>
+struct StepSmem {
+  static constexpr int RS = kStageRowBytes<D>;
+  static constexpr int kStage = kStepWaves * kUnit * RS;       // V staging, one 32-row slice per wave
+  static constexpr int kComb = kStepWaves * (32 + 16 * D) * 4;  // the waves' softmax states
+  static constexpr int kBytes = kStage > kComb ? kStage : kComb;
+};
+
+template <int D, int BS>
+__global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    float* __restrict__ k_comp, int32_t* __restrict__ sel, float* __restrict__ sel_scores, uint16_t* __restrict__ out,
+    float* __restrict__ part, uint32_t* __restrict__ counters, int64_t kv_len, int64_t kv_cap, int hq, int hkv, int G,
+    int top_k, float scale, int keep_tail, int bpw, int n_split) {
+  using SM = StepSmem<D>;
+  constexpr int LPR = D / 4;  // lanes covering one compressed key row (float32)
+  constexpr int DT = D / 16;
+  __shared__ __align__(16) unsigned char big[SM::kBytes];
+  __shared__ uint64_t lists[kStepWaves][kWave];
+  __shared__ __align__(16) float knew[D];
+  __shared__ int ids[kWave];
+  __shared__ int last_wg;
+
+  const int64_t row = blockIdx.x / n_split;
+  const int split = (int)(blockIdx.x % n_split);
+  const int64_t b = row / hkv;
+  const int g = (int)(row % hkv);
+  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  const int lg = lane / 16, col = lane % 16;
+  const int64_t p = kv_len - 1;
+  const Frame fr = row_frame(p, BS, keep_tail);
+  const int slots = frame_slots(fr, top_k);
+  const int64_t nb_cap = kv_cap / BS;
+  const int64_t kv_off = ((int64_t)b * hkv + g) * kv_cap;
+  const uint16_t* q_heads = q + (b * hq + (int64_t)g * G) * D;
+  float* kc_row = k_comp + ((int64_t)b * hkv + g) * nb_cap * D;
+
+  // 1. the block completed by the new token (if any): its mean goes to
+  // k_comp for later steps and to LDS, since with keep_tail it is a candidate
+  // of this step. The last wave computes it, as the compression kernel does.
+  const bool closes = kv_len % BS == 0;
+  const int c_new = (int)(kv_len / BS) - 1;
+  const bool new_is_cand = closes && c_new < fr.n_cand;
+  if (closes && w == kStepWaves - 1) {  // every slice needs it; slice 0 stores it
+    constexpr int VEC = 8;             // bf16 per 16-byte load
+    constexpr int LPK = D / VEC;       // lanes covering one key row
+    constexpr int RPL = kWave / LPK;   // rows per wave-wide load
+    constexpr int NLOAD = BS / RPL;
+    const int r0 = lane / LPK, c0 = (lane % LPK) * VEC;
+    const uint16_t* src = k + (kv_off + (int64_t)c_new * BS + r0) * D + c0;
+    u32x4_t raw[NLOAD];
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) raw[j] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)j * RPL * D);
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc[2 * h] += bf16_lo(raw[j][h]);
+        acc[2 * h + 1] += bf16_hi(raw[j][h]);
+      }
+#pragma unroll
+    for (int m = LPK; m < kWave; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += shfl_xor_f32(acc[e], m);
+    if (r0 == 0) {
+      constexpr float inv = 1.0f / BS;
+      float* dst = kc_row + (int64_t)c_new * D + c0;
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const f32x4_t val = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+        if (split == 0) *reinterpret_cast<f32x4_t*>(dst + e) = val;
+        *reinterpret_cast<f32x4_t*>(&knew[c0 + e]) = val;
+      }
+    }
+  }
+
+  // 2. scores and the top list of each wave (candidates read from k_comp; the
+  // new block, when it competes, from LDS below)
+  const f32x4_t qv = group_sum4(q_heads + 4 * (lane % LPR), G, D);
+  const int64_t n_glob = fr.n_cand - (new_is_cand ? 1 : 0);
+  uint64_t cur = 0ull;
+  if (slots > 0) {
+    for (int64_t base = (int64_t)kWave * w; base < n_glob; base += kWave * kStepWaves) {
+      const float s = dot64_rows<D>(kc_row + base * D, n_glob - base, qv);
+      const int64_t cand = base + dot64_row<D>(lane);
+      cur = topk_fold(cur, cand < n_glob ? make_key(s * scale, (int)cand) : 0ull, slots);
+    }
+  }
+  __syncthreads();  // knew written
+  if (new_is_cand && slots > 0 && w == 0) {
+    float part = qv[0] * knew[4 * (lane % LPR)] + qv[1] * knew[4 * (lane % LPR) + 1] +
+                 qv[2] * knew[4 * (lane % LPR) + 2] + qv[3] * knew[4 * (lane % LPR) + 3];
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) part += xor_lane_f32(part, m);
+    cur = topk_fold(cur, lane == 0 ? make_key(part * scale, c_new) : 0ull, slots);
+  }
+  cur = merge_wave_lists<kStepWaves>(lists, cur, slots > 0 ? slots : 1);
+  if (w == 0) {
+    // every slice holds the same selection; slice 0 writes it out
+    const int64_t off = row * top_k;
+    if (split == 0) finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr, ids);
+    else finalize_row(cur, slots, fr.forced, top_k, nullptr, nullptr, ids);
+  }
+  __syncthreads();
+
+  // 3. attention over the selection, units round-robin over the waves
+  u32x4_t qf[D / 32];
+  load_q_operands<D>(q_heads, G, qf);
+  const int e0 = split * bpw;
+  const int n_e = top_k - e0 < bpw ? top_k - e0 : bpw;  // this slice's entries of the selection
+  const int sel_mine = lane < n_e ? ids[e0 + lane] : -1;
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float scale_log2 = scale * 1.4426950408889634f;
+  attend_units<D, false>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, BS, p, scale_log2,
+                         big + w * kUnit * SM::RS, w, kStepWaves, m_run, l_run, o);
+  l_run = sum_col4(l_run);
+  __syncthreads();  // staging area becomes the combine area
+  float* cm = reinterpret_cast<float*>(big);  // [NW][16] running maxima
+  float* cl = cm + kStepWaves * 16;            // [NW][16] sums
+  float* co = cl + kStepWaves * 16;            // [NW][16][D] unnormalised outputs
+  if (lane < 16) {
+    cm[w * 16 + col] = m_run;
+    cl[w * 16 + col] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
+  __syncthreads();
+  if (n_split == 1) {
+    for (int idx = tid; idx < G * D; idx += kStepWaves * kWave) {
+      const int h = idx / D, e = idx % D;
+      float M = -__builtin_inff();
+      for (int ww = 0; ww < kStepWaves; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
+      float L = 0.f, O = 0.f;
+      for (int ww = 0; ww < kStepWaves; ++ww) {
+        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);  // 0 for waves without a unit
+        L += f * cl[ww * 16 + h];
+        O += f * co[(ww * 16 + h) * D + e];
+      }
+      out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
+    }
+    return;
+  }
+  // several slices per row: partial state out at the device-coherent level,
+  // a ticket, and the last slice merges (as in the decode kernel)
+  const int stride = 2 * G + G * D;
+  const auto prs = __builtin_amdgcn_make_buffer_rsrc(part + row * (int64_t)n_split * stride, 0,
+                                                     n_split * stride * 4, kBufferFlags);
+  const int soff = split * stride;
+  for (int idx = tid; idx < G * D; idx += kStepWaves * kWave) {
+    const int h = idx / D, e = idx % D;
+    float M = -__builtin_inff();
+    for (int ww = 0; ww < kStepWaves; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
+    float L = 0.f, O = 0.f;
+    if (M != -__builtin_inff()) {  // a slice may hold no visible key
+      for (int ww = 0; ww < kStepWaves; ++ww) {
+        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
+        L += f * cl[ww * 16 + h];
+        O += f * co[(ww * 16 + h) * D + e];
+      }
+    }
+    if (e == 0) {
+      store_coherent(prs, soff + h, __float_as_uint(M));
+      store_coherent(prs, soff + G + h, __float_as_uint(L));
+    }
+    store_coherent(prs, soff + 2 * G + h * D + e, __float_as_uint(O));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (uint32_t)(n_split - 1);
+    if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_wg = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_wg) return;
+  merge_slices<D, 1, 16, kStepWaves * kWave>(prs, big, out, b, g, hq, G, n_split, tid);
+}
+
+template <int D>
+hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
+                         float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out,
+                         void* ws, hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  const dim3 grid((unsigned)(rows * plan.n_split)), block(kStepWaves * kWave);
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows)) : nullptr;
+  const auto* qp = static_cast<const uint16_t*>(q);
+  const auto* kp = static_cast<const uint16_t*>(k);
+  const auto* vp = static_cast<const uint16_t*>(v);
+  auto* op = static_cast<uint16_t*>(out);
+  switch (s.bs) {
+    case 32:
+      hipLaunchKernelGGL((decode_step_kernel<D, 32>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
+                         part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail,
+                         plan.blocks_per_wg, plan.n_split);
+      break;
+    case 64:
+      hipLaunchKernelGGL((decode_step_kernel<D, 64>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
+                         part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail,
+                         plan.blocks_per_wg, plan.n_split);
+      break;
+    case 128:
+      hipLaunchKernelGGL((decode_step_kernel<D, 128>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
+                         part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail,
+                         plan.blocks_per_wg, plan.n_split);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+StepPlan plan_decode_step(const Dims& s, int64_t kv_len) {
+  StepPlan p{};
+  p.fused = false;
+  if (s.dtype != 1 || s.top_k > 64 || s.bs < 32) return p;
+  // A workgroup streams its row's compressed keys alone: worth it while the
+  // row is short (the per-CU read rate bounds it) or the rows alone fill
+  // the GPU (then HBM bounds it either way).
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  const int64_t row_bytes = max_candidates(s, kv_len) * s.d * 4;
+  if (row_bytes > (512 << 10) && rows < 64) return p;
+  p.fused = true;
+  // Few rows: slices of the selection that give each wave about one 32-key
+  // unit, as long as the grid stays small (every slice repeats the scan).
+  const int upb = s.bs / kUnit;
+  p.blocks_per_wg = s.top_k;
+  p.n_split = 1;
+  if (rows <= 32) {
+    const int bpw = (kStepWaves + upb - 1) / upb;
+    const int n = (s.top_k + bpw - 1) / bpw;
+    const int cap = (int)(256 / rows);
+    if (n > 1 && cap > 1) {
+      p.n_split = n < cap ? n : cap;
+      p.blocks_per_wg = (s.top_k + p.n_split - 1) / p.n_split;
+      p.n_split = (s.top_k + p.blocks_per_wg - 1) / p.blocks_per_wg;
+    }
+  }
+  p.ws_bytes = p.n_split > 1 ? counter_bytes(rows) +
+                                   (size_t)rows * p.n_split * (2 * s.group + s.group * s.d) * sizeof(float)
+                             : 0;
+  return p;
+}
+
+hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
+                              float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                              void* out, void* ws, hipStream_t st) {
+  return s.d == 64 ? launch_step_d<64>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, st)
+                   : launch_step_d<128>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, st);
+}
+
+}  // namespace qsa

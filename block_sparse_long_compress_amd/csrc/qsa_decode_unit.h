@@ -1,0 +1,280 @@
+// One wave's share of sparse decode attention over a slice of the selection
+// list (shared by the decode kernel and the fused decode step).
+//
+// bf16 inputs, bf16 MFMA (v_mfma_f32_16x16x32_bf16), float32 softmax and
+// accumulation. Work unit = 32 keys: 32 consecutive keys of one selected
+// block, or for blocks shorter than 32 keys (Bs = 4, 8, 16) the keys of
+// 32/Bs consecutive entries of the selection list, each row addressed on its
+// own (the position of every key row is computed once per unit and shared
+// across lanes with ds_bpermute). Per unit the wave computes S^T = K Q^T with
+// the keys as the 16-row M operand and the G query heads of the KV head as
+// the N columns (G <= 16; columns >= G are zero queries and are ignored),
+// keeps an online softmax per column in the exp2 domain, and accumulates
+// O^T = V^T P^T. K fragments are loaded straight from HBM in operand layout
+// (16 contiguous bytes per lane). V rows are staged in the wave's own LDS
+// slice with coalesced loads and read back transposed, two bytes at a time,
+// into the V^T operand.
+#pragma once
+
+#include "qsa_device.h"
+
+namespace qsa {
+
+constexpr int kUnit = 32;
+
+// Element j of a lane's 8-wide K-dimension operand slot, for lane group lg,
+// is key kkey(lg, j) of the 32-key unit. S^T tiles 0 and 1 hold keys
+// 4*lg+i and 16+4*lg+i in lane group lg (MFMA output layout), so P^T can be
+// fed to the PV product without any lane exchange.
+__device__ __forceinline__ int kkey(int lg, int j) { return j < 4 ? 4 * lg + j : 12 + 4 * lg + j; }
+
+template <int D>
+constexpr int kStageRowBytes = 2 * D + 16;  // LDS row stride of staged V (bytes)
+
+// Q operands of the row's G query heads (head j in column j; columns >= G zero).
+template <int D>
+__device__ __forceinline__ void load_q_operands(const uint16_t* __restrict__ q_heads, int G, u32x4_t (&qf)[D / 32]) {
+  const int lane = lane_id(), lg = lane / 16, col = lane % 16;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    qf[s] = u32x4_t{0u, 0u, 0u, 0u};
+    if (col < G) qf[s] = *reinterpret_cast<const u32x4_t*>(q_heads + (int64_t)col * D + 32 * s + 8 * lg);
+  }
+}
+
+// Units idx = first, first + stride, ... of a slice of n_e selection entries
+// (entry j of the slice in lane j's sel_mine, -1 for padding), attended by
+// one wave into (m_run, l_run, o). kbase, vbase point at position 0 of the
+// row's keys and values; p is the query position; vs is the wave's 32-row
+// staging slice. One unit in flight per wave: a second register set would
+// halve the waves per SIMD, and more waves hide latency at least as well.
+template <int D, bool GATHER>
+__device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const uint16_t* __restrict__ kbase,
+                                             const uint16_t* __restrict__ vbase, int sel_mine, int n_e, int bs,
+                                             int64_t p, float scale_log2, unsigned char* vs, int first, int stride,
+                                             float& m_run, float& l_run, f32x4_t (&o)[D / 16]) {
+  constexpr int RS = kStageRowBytes<D>;
+  constexpr int KS = D / 32;  // 32-wide K steps of the QK^T product
+  constexpr int DT = D / 16;  // 16-wide dim tiles of the PV product
+  const int lane = lane_id();
+  const int lg = lane / 16, col = lane % 16;
+  const int upb = GATHER ? 1 : bs / kUnit;  // units per block
+  const int bpu = GATHER ? kUnit / bs : 1;  // blocks per unit
+  const int n_units = GATHER ? (n_e + bpu - 1) / bpu : n_e * upb;
+  constexpr int VCH = kUnit * D / 8 / kWave;  // 16-byte V chunks per lane
+  struct Unit {
+    u32x4_t kf[2][KS];
+    u32x4_t vr[VCH];
+    int64_t key0;  // contiguous units: position of key row 0
+    int mpos[2];   // gathered units: position of key row 16*st + 4*lg (-1: not visible)
+    bool ok;
+  };
+  auto fetch = [&](int idx, Unit& u) {
+    u.ok = false;
+    if (idx >= n_units) return;
+    if constexpr (GATHER) {
+      // Row r of the unit is key r % Bs of slice entry idx*bpu + r/Bs; lanes
+      // r and r + 32 compute it, every other lane fetches it with bpermute.
+      // idx*bpu + r/Bs < 64: the slice holds at most 64 entries and bpu
+      // divides 64.
+      const int r = lane & (kUnit - 1);
+      const int slot = idx * bpu + r / bs;
+      const int c = __builtin_amdgcn_ds_bpermute(slot << 2, sel_mine);
+      const int64_t pos = (int64_t)c * bs + (r % bs);
+      const int rowpos = (slot < n_e && c >= 0 && pos <= p) ? (int)pos : -1;
+      if (__ballot(rowpos >= 0) == 0) return;
+      u.ok = true;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int kp = __builtin_amdgcn_ds_bpermute((16 * st + col) << 2, rowpos);
+        u.mpos[st] = __builtin_amdgcn_ds_bpermute((16 * st + 4 * lg) << 2, rowpos);
+        const uint16_t* kb = kbase + (int64_t)(kp >= 0 ? kp : 0) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          u.kf[st][s] = kp >= 0 ? *reinterpret_cast<const u32x4_t*>(kb + 32 * s + 8 * lg) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int ci = lane + kWave * j;
+        const int rr = ci / (D / 8), c8 = ci % (D / 8);
+        const int vp = __builtin_amdgcn_ds_bpermute(rr << 2, rowpos);
+        u.vr[j] = vp >= 0 ? *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)(vp >= 0 ? vp : 0) * D + 8 * c8)
+                          : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    } else {
+      const int c = __builtin_amdgcn_readlane(sel_mine, idx / upb);
+      if (c < 0) return;
+      u.key0 = (int64_t)c * bs + (int64_t)(idx % upb) * kUnit;
+      if (u.key0 > p) return;
+      u.ok = true;
+      const uint16_t* kb = kbase + u.key0 * D;
+      const uint16_t* vb = vbase + u.key0 * D;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int kr = 16 * st + col;
+        const bool ok = u.key0 + kr <= p;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          u.kf[st][s] = ok ? *reinterpret_cast<const u32x4_t*>(kb + (int64_t)kr * D + 32 * s + 8 * lg)
+                           : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < VCH; ++j) {
+        const int ci = lane + kWave * j;
+        const int r = ci / (D / 8), c8 = ci % (D / 8);
+        u.vr[j] = u.key0 + r <= p ? *reinterpret_cast<const u32x4_t*>(vb + (int64_t)r * D + 8 * c8)
+                                  : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto consume = [&](const Unit& u) {
+    if (!u.ok) return;
+#pragma unroll
+    for (int j = 0; j < VCH; ++j) {
+      const int ci = lane + kWave * j;
+      const int r = ci / (D / 8), c8 = ci % (D / 8);
+      *reinterpret_cast<u32x4_t*>(vs + r * RS + 16 * c8) = u.vr[j];
+    }
+
+    f32x4_t sacc[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      sacc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) sacc[st] = mfma_bf16(u.kf[st][s], qf[s], sacc[st]);
+    }
+    float x[2][4];
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // rows 16*st + 4*lg + i (i < 4) lie in one block of >= 4 keys
+        const bool ok = GATHER ? (u.mpos[st] >= 0 && u.mpos[st] + i <= p) : (u.key0 + 16 * st + 4 * lg + i <= p);
+        x[st][i] = ok ? sacc[st][i] * scale_log2 : -__builtin_inff();
+        mloc = fmaxf(mloc, x[st][i]);
+      }
+    mloc = max_col4(mloc);
+    const float m_new = fmaxf(m_run, mloc);  // finite: the unit has a visible key
+    if (__ballot(m_new > m_run) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    m_run = m_new;
+    float pr[2][4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[st][i] = __builtin_amdgcn_exp2f(x[st][i] - m_new);
+        l_run += pr[st][i];
+      }
+    const u32x4_t pf = {pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                        pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3])};
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const unsigned char* src = vs + 2 * (16 * dt + col);
+      uint32_t wv[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(src + kkey(lg, 2 * h) * RS);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(src + kkey(lg, 2 * h + 1) * RS);
+        wv[h] = lo | (hi << 16);
+      }
+      o[dt] = mfma_bf16(u32x4_t{wv[0], wv[1], wv[2], wv[3]}, pf, o[dt]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // One unit in flight per wave: a second register set would halve the
+  // waves per SIMD, and more waves hide latency at least as well.
+  for (int idx = first; idx < n_units; idx += stride) {
+    Unit u;
+    fetch(idx, u);
+    consume(u);
+  }
+
+}
+
+// Merge of a row's slice states by its last workgroup: slices in batches of
+// SB, each batch's loads all in flight (one memory round trip), folded in
+// slice order into a running state per group of 4 output dims; GPT groups
+// per thread (NT threads) cover the G * D / 4 groups of the row.
+template <int D, int GPT, int SB, int NT>
+__device__ __forceinline__ void merge_slices(__amdgpu_buffer_rsrc_t prs, unsigned char* smem, uint16_t* out,
+                                             int64_t b, int g, int hq, int G, int n_split, int tid) {
+  const int stride = 2 * G + G * D;
+  const int n_g4 = G * (D / 4);
+  float* st = reinterpret_cast<float*>(smem);  // [SB][2G] maxima and sums of the batch
+  float Mr[GPT], Lr[GPT];
+  f32x4_t Or[GPT];
+#pragma unroll
+  for (int q4 = 0; q4 < GPT; ++q4) {
+    Mr[q4] = -__builtin_inff();
+    Lr[q4] = 0.f;
+    Or[q4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s0 = 0; s0 < n_split; s0 += SB) {
+    const int nb = n_split - s0 < SB ? n_split - s0 : SB;
+    __syncthreads();  // the previous batch's statistics are consumed
+    for (int i = tid; i < nb * 2 * G; i += NT) {
+      const int sl = i / (2 * G), j = i % (2 * G);
+      st[i] = __uint_as_float(load_coherent(prs, (s0 + sl) * stride + j));
+    }
+    f32x4_t ov[GPT][SB];
+#pragma unroll
+    for (int q4 = 0; q4 < GPT; ++q4) {
+      const int gi = tid + NT * q4;
+      const int h = gi / (D / 4), e4 = 4 * (gi % (D / 4));
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        ov[q4][j] = (gi < n_g4 && j < nb)
+                        ? __builtin_bit_cast(f32x4_t, load4_coherent(prs, (s0 + j) * stride + 2 * G + h * D + e4))
+                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q4 = 0; q4 < GPT; ++q4) {
+      const int gi = tid + NT * q4;
+      if (gi >= n_g4) continue;
+      const int h = gi / (D / 4);
+      float ms[SB];
+      float mb = Mr[q4];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        ms[j] = j < nb ? st[j * 2 * G + h] : -__builtin_inff();
+        mb = fmaxf(mb, ms[j]);
+      }
+      if (mb == -__builtin_inff()) continue;  // no visible key so far
+      const float a = __builtin_amdgcn_exp2f(Mr[q4] - mb);  // 0 while Mr = -inf
+      Lr[q4] *= a;
+      Or[q4] *= a;
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        const float f = __builtin_amdgcn_exp2f(ms[j] - mb);  // 0 for empty and missing slices
+        Lr[q4] += j < nb ? f * st[j * 2 * G + G + h] : 0.f;
+        Or[q4] += f * ov[q4][j];
+      }
+      Mr[q4] = mb;
+    }
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < GPT; ++q4) {
+    const int gi = tid + NT * q4;
+    if (gi >= n_g4) continue;
+    const int h = gi / (D / 4), e4 = 4 * (gi % (D / 4));
+    const float inv = 1.f / Lr[q4];
+    const u32x2_t v = {pack_bf16x2(Or[q4][0] * inv, Or[q4][1] * inv), pack_bf16x2(Or[q4][2] * inv, Or[q4][3] * inv)};
+    *reinterpret_cast<u32x2_t*>(out + (b * hq + (int64_t)g * G + h) * D + e4) = v;
+  }
+}
+
+}  // namespace qsa

@@ -63,6 +63,21 @@ hipError_t launch_prefill(const Dims& s, const PrefillPlan& plan, const void* q,
                           int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* ws,
                           hipStream_t st);
 
+// Fused decode step (compress the closed block, select, attend) --------------
+// Whether the fused kernel serves this shape (otherwise the step runs as the
+// separate compress, selection and decode launches), and with how many
+// workgroups (slices of the selection) per row.
+struct StepPlan {
+  bool fused;
+  int blocks_per_wg;
+  int n_split;
+  size_t ws_bytes;
+};
+StepPlan plan_decode_step(const Dims& s, int64_t kv_len);
+hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
+                              float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                              void* out, void* ws, hipStream_t st);
+
 // Generic float32 attention (one wave per query row); used for dtype QSA_F32.
 hipError_t launch_attn_f32(const Dims& s, const float* q, const float* k, const float* v, int64_t q_len,
                            int64_t q_pos0, int64_t kv_cap, const int32_t* sel, float* out, hipStream_t st);

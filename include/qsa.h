@@ -86,7 +86,7 @@ extern "C" {
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
-enum { QSA_OP_COMPRESS = 0, QSA_OP_SELECT = 1, QSA_OP_DECODE = 2, QSA_OP_PREFILL = 3 };
+enum { QSA_OP_COMPRESS = 0, QSA_OP_SELECT = 1, QSA_OP_DECODE = 2, QSA_OP_PREFILL = 3, QSA_OP_DECODE_STEP = 4 };
 
 typedef enum {
   QSA_OK = 0,
@@ -179,6 +179,32 @@ qsa_status qsa_sparse_attn_decode(const qsa_shape* shape, const void* q, const v
 qsa_status qsa_sparse_attn_prefill(const qsa_shape* shape, const void* q, const void* k, const void* v,
                                    int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel,
                                    void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* One whole decode step: the same results as qsa_compress_keys(shape, k,
+ * kv_len, kv_cap, block_begin = (kv_len-1)/Bs, k_comp), then
+ * qsa_score_select for the token at kv_len-1, then qsa_sparse_attn_decode
+ * (the passages cited there). k_comp must already hold the blocks completed
+ * before the new token; the block it completes (if any) is written to it.
+ * sel [b][Hkv][k] and sel_scores (optional) are written as by
+ * qsa_score_select, out [b][Hq][d] as by qsa_sparse_attn_decode.
+ * For bf16, k <= 64 and Bs >= 32, rows that are short (compressed keys of a
+ * row up to 512 KiB) or numerous (64 rows or more) run in one kernel: one
+ * workgroup per (sequence, KV head) compresses, selects and attends with no
+ * hand-off of the selection through memory (with few rows, several
+ * workgroups per row each attend over a slice of the same selection and the
+ * last one merges them, as the decode call does); the attention states merge
+ * in another order than the decode call's, so outputs agree within
+ * rounding. Other shapes run the three calls in order, the selection on the
+ * first part of the workspace and the attention on the rest. ws: device
+ * scratch of qsa_workspace_bytes(shape, QSA_OP_DECODE_STEP, 1, kv_len),
+ * zero-filled before its first use as for the decode call. */
+qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,
+                           int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* 1 when qsa_decode_step runs these sizes as the single fused kernel, 0 when
+ * it runs the separate calls, -1 for invalid arguments. */
+int qsa_decode_step_fused(const qsa_shape* shape, int64_t kv_len);
 
 #ifdef __cplusplus
 }

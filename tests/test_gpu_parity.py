@@ -296,3 +296,50 @@ def test_large_k_clustered_winners():
         assert inside > 300, inside
     st = check_rows(case, sel, out, [(0, 0, g) for g in range(2)], w.kv_len - 1, scores_gpu=scores)
     log(f"clustered winners: {st}")
+
+
+STEP_CASES = [
+    W(mode="decode", batch=3, kv_len=1000, top_k=8),
+    W(mode="decode", batch=2, kv_len=64 * 40, top_k=8),                     # the new token closes a block
+    W(mode="decode", batch=2, kv_len=64 * 40, top_k=8, keep_tail=True),     # ... which then competes
+    W(mode="decode", batch=1, kv_len=64, top_k=4, keep_tail=True),          # its only candidate is the new block
+    W(mode="decode", batch=2, kv_len=50, top_k=4),                          # own block only
+    W(mode="decode", batch=1, kv_len=9000, top_k=64, block_size=32),
+    W(mode="decode", batch=5, kv_len=4096, top_k=12, head_dim=64, block_size=128),
+    W(mode="decode", batch=2, kv_len=3000, n_q_heads=16, n_kv_heads=1, top_k=7),
+    W(mode="decode", batch=2, kv_len=3000, n_q_heads=2, n_kv_heads=2, top_k=7),
+    W(mode="decode", batch=40, kv_len=5000, top_k=16, n_q_heads=8, n_kv_heads=2),  # 80 rows: fused though long
+    # shapes the fused kernel leaves to the separate calls
+    W(mode="decode", batch=1, kv_len=200000, top_k=16),                     # long rows, few of them
+    W(mode="decode", batch=1, kv_len=4 * 20000, top_k=513, block_size=4, keep_tail=True),
+    W(mode="decode", batch=2, kv_len=2222, dtype="f32", sigma=1.0, top_k=5),
+]
+
+
+@pytest.mark.parametrize("w", STEP_CASES, ids=case_id)
+def test_decode_step_parity(w):
+    """qsa_decode_step = compress of the closed block + selection + decode attention, fused or not."""
+    log(f"decode step parity {w}")
+    case = Case(w, seed=11, kv_cap=w.kv_len + 100)
+    b, hq, d, bs = w.batch, w.n_q_heads, w.head_dim, w.block_size
+    shape = qsa.shape_for(case.q, case.k, bs, w.top_k, keep_tail=w.keep_tail)
+    nb = w.kv_len // bs
+    # k_comp holds the blocks closed before the new token; the step adds the one it closes
+    k_comp = torch.full((b, w.n_kv_heads, case.kv_cap // bs, d), float("nan"), device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len - 1, k_comp)
+    k_comp_ref = k_comp.clone()
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp_ref)
+    q = case.q.view(b, hq, d)
+    sel = torch.empty(b, w.n_kv_heads, w.top_k, dtype=torch.int32, device="cuda")
+    scores = torch.empty(b, w.n_kv_heads, w.top_k, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    qsa.qsa_decode_step(shape, q, case.k, case.v, k_comp, w.kv_len, sel, out, sel_scores=scores)
+    out2, sel2 = qsa.decode(q, case.k, case.v, w.kv_len, bs, w.top_k, k_comp_ref, keep_tail=w.keep_tail)
+    torch.cuda.synchronize()
+    assert torch.equal(k_comp[:, :, :nb], k_comp_ref[:, :, :nb]), "compressed keys differ from the compress call"
+    if not (w.keep_tail and w.kv_len % bs == 0):  # else the new block's score may round differently
+        assert torch.equal(sel, sel2), "selection differs from the separate calls"
+    rows = [(bb, 0, g) for bb in range(b) for g in range(w.n_kv_heads)]
+    st = check_rows(case, sel.cpu().numpy()[:, None], from_device(out)[:, None], rows, w.kv_len - 1,
+                    scores_gpu=scores.cpu().numpy()[:, None])
+    log(f"  {st}")
