@@ -221,13 +221,18 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
     if (sp.ws_bytes > 0 && (!ws || ws_bytes < sp.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
     return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, hs));
   }
-  // separate launches: the block the new token completed, then selection and attention
+  // separate launches: the selection (which also compresses the block the new
+  // token closes, if any, before scoring it), then the attention
   const size_t need = qsa_workspace_bytes(shape, QSA_OP_DECODE_STEP, 1, kv_len);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return QSA_ERR_WORKSPACE;
-  st = qsa_compress_keys(shape, k, kv_len, kv_cap, (kv_len - 1) / s.bs, k_comp, stream);
-  if (st != QSA_OK) return st;
-  const size_t sel_part = qsa::align_up(qsa::plan_select(s, 1, kv_len - 1).ws_bytes, 256);
-  st = qsa_score_select(shape, q, 1, kv_len - 1, k_comp, kv_len, kv_cap, sel, sel_scores, ws, sel_part, stream);
+  if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
+  const qsa::SelectPlan sel_plan = qsa::plan_select(s, 1, kv_len - 1);
+  if ((int64_t)s.batch * s.hkv * (sel_plan.n_chunks > 0 ? sel_plan.n_chunks : 1) > 0x7FFFFFFF)
+    return QSA_ERR_UNSUPPORTED;
+  const size_t sel_part = qsa::align_up(sel_plan.ws_bytes, 256);
+  const int64_t close_block = kv_len % s.bs == 0 ? kv_len / s.bs - 1 : -1;
+  st = hip_status(
+      qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores, ws, hs, k, close_block));
   if (st != QSA_OK) return st;
   void* ws_dec = ws ? static_cast<char*>(ws) + sel_part : nullptr;
   return qsa_sparse_attn_decode(shape, q, k, v, kv_len, kv_cap, sel, out, ws_dec, need - sel_part, stream);

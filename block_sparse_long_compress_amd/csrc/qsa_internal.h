@@ -38,9 +38,11 @@ constexpr int64_t kMaxCandLarge = 65536;
 // Candidate blocks of the row at position kv_len - 1 (the most of any row).
 int64_t max_candidates(const Dims& s, int64_t kv_len);
 SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0);
+// close_block >= 0 (decode, q_len = 1): the selection also compresses that
+// block of k_cache into k_comp first (the block the new token closes).
 hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,
                          const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
-                         hipStream_t st);
+                         hipStream_t st, const void* k_cache = nullptr, int64_t close_block = -1);
 
 // Decode attention --------------------------------------------------------------
 struct DecodePlan {

@@ -248,12 +248,14 @@ __device__ void merge_lists(__amdgpu_buffer_rsrc_t rs, int64_t n_chunks, int sm,
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__ q, const float* __restrict__ k_comp,
+__global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__ q, const float* k_comp,
+                                                           const T* __restrict__ k_cache, float* k_comp_w, int64_t kv_cap,
                                                            int32_t* __restrict__ sel, float* __restrict__ sel_scores,
                                                            uint32_t* __restrict__ counters, uint64_t* __restrict__ ws,
                                                            int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
                                                            int hkv, int G, int bs, int top_k, float scale,
-                                                           int keep_tail, int chunk, int64_t n_chunks) {
+                                                           int keep_tail, int chunk, int64_t n_chunks,
+                                                           int64_t close_block) {
   constexpr int LPR = D / 4;
   __shared__ SplitSmem smem;
 
@@ -268,6 +270,14 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
   int32_t* sel_row = sel + off;
   float* score_row = sel_scores ? sel_scores + off : nullptr;
+  if (close_block >= 0 && ch == n_chunks - 1) {
+    // a decode step's closed block, compressed before it is scored (with
+    // keep_tail it is this chunk's last candidate)
+    if (w == 0)
+      compress_block_wave<T, D>(k_cache + ((b * hkv + g) * kv_cap + close_block * bs) * D, bs,
+                                k_comp_w + ((b * hkv + g) * nb_cap + close_block) * D, nullptr);
+    __syncthreads();
+  }
 
   if (slots == 0) {  // nothing to score: the forced block alone
     if (ch == 0 && w == 0) finalize_row(0ull, 0, fr.forced, top_k, sel_row, score_row);
@@ -342,9 +352,10 @@ __device__ __forceinline__ float order_to_float(uint32_t o) {
 // chunk's 16 best keys in descending order (ws_lists, 0 = empty).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void select_large_score_kernel(
-    const T* __restrict__ q, const float* __restrict__ k_comp, uint32_t* __restrict__ ws_scores,
+    const T* __restrict__ q, const float* k_comp, uint32_t* __restrict__ ws_scores,
     uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs,
-    float scale, int keep_tail, int64_t n_chunks) {
+    float scale, int keep_tail, int64_t n_chunks, const T* __restrict__ k_cache, float* k_comp_w, int64_t kv_cap,
+    int64_t close_block) {
   constexpr int LPR = D / 4;
   __shared__ uint64_t tops[4][kLargeList];
   const int64_t row = blockIdx.x / n_chunks;
@@ -355,6 +366,15 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
   const int lane = lane_id(), w = wave_id();
   const int n_cand = row_frame(q_pos0 + t, bs, keep_tail).n_cand;
   const int64_t c_begin = ch * kLargeChunk;
+  const int64_t last_ch = n_cand > 0 ? (n_cand - 1) / kLargeChunk : 0;
+  if (close_block >= 0 && ch == last_ch) {
+    // a decode step's closed block, compressed before it is scored (with
+    // keep_tail it is this chunk's last candidate)
+    if (w == 0)
+      compress_block_wave<T, D>(k_cache + ((b * hkv + g) * kv_cap + close_block * bs) * D, bs,
+                                k_comp_w + ((b * hkv + g) * nb_cap + close_block) * D, nullptr);
+    __syncthreads();
+  }
   if (c_begin >= n_cand) return;  // uniform over the workgroup
 
   const f32x4_t qv = group_sum4(q + ((b * q_len + t) * hq + (int64_t)g * G) * D + 4 * (lane % LPR), G, D);
@@ -627,8 +647,10 @@ __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
 template <typename T, int D>
 hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, int64_t q_len, int64_t q_pos0,
                         const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
-                        hipStream_t st) {
+                        hipStream_t st, const void* k_cache, int64_t close_block) {
   const T* q = static_cast<const T*>(qv);
+  const T* kc = static_cast<const T*>(k_cache);
+  float* kcw = const_cast<float*>(k_comp);
   const int64_t nb_cap = kv_cap / s.bs;
   const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
   if (plan.large) {
@@ -637,7 +659,7 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
     if (plan.n_chunks > 0) {
       hipLaunchKernelGGL((select_large_score_kernel<T, D>), dim3((unsigned)(rows * plan.n_chunks)), dim3(256), 0, st,
                          q, k_comp, wss, wsl, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.scale,
-                         s.keep_tail, plan.n_chunks);
+                         s.keep_tail, plan.n_chunks, kc, kcw, kv_cap, close_block);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -654,8 +676,8 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
   uint32_t* counters = static_cast<uint32_t*>(ws);
   uint64_t* wsk = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + (plan.n_chunks > 1 ? counter_bytes(rows) : 0));
   hipLaunchKernelGGL((select_split_kernel<T, D>), dim3((unsigned)(rows * plan.n_chunks)), dim3(256), 0, st, q,
-                     k_comp, sel, sel_scores, counters, wsk, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs,
-                     s.top_k, s.scale, s.keep_tail, plan.chunk, plan.n_chunks);
+                     k_comp, kc, kcw, kv_cap, sel, sel_scores, counters, wsk, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs,
+                     s.top_k, s.scale, s.keep_tail, plan.chunk, plan.n_chunks, close_block);
   return hipGetLastError();
 }
 
@@ -699,12 +721,12 @@ SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
 
 hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,
                          const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
-                         hipStream_t st) {
+                         hipStream_t st, const void* k_cache, int64_t close_block) {
   if (s.dtype == 1)
-    return s.d == 64 ? launch_typed<uint16_t, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st)
-                     : launch_typed<uint16_t, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st);
-  return s.d == 64 ? launch_typed<float, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st)
-                   : launch_typed<float, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st);
+    return s.d == 64 ? launch_typed<uint16_t, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block)
+                     : launch_typed<uint16_t, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block);
+  return s.d == 64 ? launch_typed<float, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block)
+                   : launch_typed<float, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block);
 }
 
 }  // namespace qsa

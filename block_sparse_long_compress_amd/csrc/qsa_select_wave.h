@@ -131,4 +131,56 @@ __device__ __forceinline__ float dot64_rows(const float* __restrict__ rows_base,
   return res[0];
 }
 
+// Mean of the bs keys of one block (src: the block's first key) by one wave,
+// in the compression kernel's order: each lane accumulates its 16-byte column
+// slice over the rows it visits (16 loads in flight at a time), then a
+// butterfly over the lanes that share a slice finishes the sum. The D floats
+// go to dst and, when given, to dst2.
+template <typename T, int D>
+__device__ __forceinline__ void compress_block_wave(const T* __restrict__ src, int bs, float* dst, float* dst2) {
+  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
+  constexpr int LPR = D / VEC;         // lanes covering one key row
+  constexpr int RPL = kWave / LPR;     // rows per wave-wide load
+  const int lane = lane_id();
+  const int row0 = lane / LPR;
+  const int col = (lane % LPR) * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  for (int r0 = 0; r0 < bs; r0 += 16 * RPL) {
+    u32x4_t raw[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = r0 + j * RPL + row0;
+      raw[j] = r < bs ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * D + col) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc[2 * h] += bf16_lo(raw[j][h]);
+          acc[2 * h + 1] += bf16_hi(raw[j][h]);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) acc[h] += __uint_as_float(raw[j][h]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = LPR; m < kWave; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += shfl_xor_f32(acc[e], m);
+  if (row0 == 0) {
+    const float inv = 1.0f / (float)bs;  // exact: bs is a power of two
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+      const f32x4_t v = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
+      if (dst) *reinterpret_cast<f32x4_t*>(dst + col + e) = v;
+      if (dst2) *reinterpret_cast<f32x4_t*>(dst2 + col + e) = v;
+    }
+  }
+}
+
 }  // namespace qsa

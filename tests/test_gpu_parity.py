@@ -313,6 +313,8 @@ STEP_CASES = [
     W(mode="decode", batch=1, kv_len=200000, top_k=16),                     # long rows, few of them
     W(mode="decode", batch=1, kv_len=4 * 20000, top_k=513, block_size=4, keep_tail=True),
     W(mode="decode", batch=2, kv_len=2222, dtype="f32", sigma=1.0, top_k=5),
+    W(mode="decode", batch=2, kv_len=2240, dtype="f32", sigma=1.0, top_k=5, keep_tail=True),   # closes a block
+    W(mode="decode", batch=1, kv_len=8 * 3000, top_k=100, block_size=8),                    # large-k, closes
 ]
 
 
