@@ -110,7 +110,9 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       if (sp.fused) return sp.ws_bytes;
       // the separate calls, each on its own part (the decode part keeps
       // counters at its start that the selection must not overwrite)
-      const size_t a = qsa::align_up(qsa::plan_select(s, 1, kv_len - 1).ws_bytes, 256);
+      const qsa::SelectPlan sel_plan = qsa::plan_select(s, 1, kv_len - 1);
+      const size_t a = qsa::align_up(sel_plan.ws_bytes, 256);
+      if (s.dtype == QSA_BF16 && sel_plan.large) return a + qsa::plan_pick_attend(s, sel_plan.n_chunks).ws_bytes;
       const size_t d = s.dtype == QSA_BF16 ? qsa::plan_decode(s, kv_len).ws_bytes : 0;
       return a + d;
     }
@@ -231,6 +233,17 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
     return QSA_ERR_UNSUPPORTED;
   const size_t sel_part = qsa::align_up(sel_plan.ws_bytes, 256);
   const int64_t close_block = kv_len % s.bs == 0 ? kv_len / s.bs - 1 : -1;
+  if (s.dtype == QSA_BF16 && sel_plan.large) {
+    // the score pass, then one kernel that picks each row's blocks and
+    // attends over them (its counters and slice states after the scores)
+    const qsa::PickAttendPlan pa = qsa::plan_pick_attend(s, sel_plan.n_chunks);
+    if ((int64_t)s.batch * s.hkv * pa.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+    st = hip_status(qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores, ws, hs, k,
+                                       close_block, false));
+    if (st != QSA_OK) return st;
+    return hip_status(qsa::launch_pick_attend(s, pa, q, k, v, sel, sel_scores, ws, out,
+                                              static_cast<char*>(ws) + sel_part, kv_len, kv_cap, hs));
+  }
   st = hip_status(
       qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores, ws, hs, k, close_block));
   if (st != QSA_OK) return st;

@@ -21,6 +21,7 @@
 #include "qsa_decode_unit.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"
+#include "qsa_select_large.h"
 #include "qsa_select_wave.h"
 
 namespace qsa {
@@ -150,69 +151,76 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   attend_units<D, false>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, BS, p, scale_log2,
                          big + w * kUnit * SM::RS, w, kStepWaves, m_run, l_run, o);
   l_run = sum_col4(l_run);
-  __syncthreads();  // staging area becomes the combine area
-  float* cm = reinterpret_cast<float*>(big);  // [NW][16] running maxima
-  float* cl = cm + kStepWaves * 16;            // [NW][16] sums
-  float* co = cl + kStepWaves * 16;            // [NW][16][D] unnormalised outputs
-  if (lane < 16) {
-    cm[w * 16 + col] = m_run;
-    cl[w * 16 + col] = l_run;
-  }
+  finish_row_slice<D, kStepWaves>(m_run, l_run, o, big, &last_wg, out, part, counters, row, b, g, hq, G, split,
+                                  n_split);
+}
+
+// Decode step with k > 64 (the released budget): after the large-k score
+// pass, each of a row's S workgroups takes the row's cutoff and ids itself
+// (pick_row over the stored scores and chunk lists; slice 0 also writes
+// them out), attends over its slice of the selection, and the last slice
+// merges. The selection reaches the attention through LDS, not through HBM
+// and another launch.
+static_assert(kPickThreads == kStepWaves * kWave, "the pick runs on the step's workgroup");
+
+template <int D, bool GATHER>
+__global__ __launch_bounds__(kStepWaves * kWave) void pick_attend_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int32_t* __restrict__ sel, float* __restrict__ sel_scores, const uint32_t* __restrict__ ws_scores,
+    const uint64_t* __restrict__ ws_lists, uint16_t* __restrict__ out, float* part, uint32_t* counters,
+    int64_t kv_len, int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k, float scale_log2, int keep_tail,
+    int64_t n_chunks, int bpw, int n_split) {
+  using SM = StepSmem<D>;
+  constexpr int DT = D / 16;
+  __shared__ __align__(16) unsigned char big[SM::kBytes];
+  __shared__ PickSmem sm;
+  __shared__ int ids[kMaxTopKLarge];
+  __shared__ int last_wg;
+
+  const int64_t row = blockIdx.x / n_split;
+  const int split = (int)(blockIdx.x % n_split);
+  const int64_t b = row / hkv;
+  const int g = (int)(row % hkv);
+  const int lane = lane_id(), w = wave_id();
+  const int64_t p = kv_len - 1;
+  const Frame fr = row_frame(p, bs, keep_tail);
+  const int64_t off = row * top_k;
+  pick_row(sm, ws_scores + row * n_chunks * kLargeChunk, ws_lists + row * n_chunks * kLargeList, fr.n_cand,
+           frame_slots(fr, top_k), fr.forced, top_k, split == 0 ? sel + off : nullptr,
+           (split == 0 && sel_scores) ? sel_scores + off : nullptr, ids);
+  __syncthreads();
+
+  const int64_t kv_off = ((int64_t)b * hkv + g) * kv_cap;
+  u32x4_t qf[D / 32];
+  load_q_operands<D>(q + (b * hq + (int64_t)g * G) * D, G, qf);
+  const int e0 = split * bpw;
+  const int n_e = top_k - e0 < bpw ? top_k - e0 : bpw;
+  const int sel_mine = lane < n_e ? ids[e0 + lane] : -1;
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  f32x4_t o[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
-  __syncthreads();
-  if (n_split == 1) {
-    for (int idx = tid; idx < G * D; idx += kStepWaves * kWave) {
-      const int h = idx / D, e = idx % D;
-      float M = -__builtin_inff();
-      for (int ww = 0; ww < kStepWaves; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
-      float L = 0.f, O = 0.f;
-      for (int ww = 0; ww < kStepWaves; ++ww) {
-        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);  // 0 for waves without a unit
-        L += f * cl[ww * 16 + h];
-        O += f * co[(ww * 16 + h) * D + e];
-      }
-      out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
-    }
-    return;
-  }
-  // several slices per row: partial state out at the device-coherent level,
-  // a ticket, and the last slice merges (as in the decode kernel)
-  const int stride = 2 * G + G * D;
-  const auto prs = __builtin_amdgcn_make_buffer_rsrc(part + row * (int64_t)n_split * stride, 0,
-                                                     n_split * stride * 4, kBufferFlags);
-  const int soff = split * stride;
-  for (int idx = tid; idx < G * D; idx += kStepWaves * kWave) {
-    const int h = idx / D, e = idx % D;
-    float M = -__builtin_inff();
-    for (int ww = 0; ww < kStepWaves; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
-    float L = 0.f, O = 0.f;
-    if (M != -__builtin_inff()) {  // a slice may hold no visible key
-      for (int ww = 0; ww < kStepWaves; ++ww) {
-        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
-        L += f * cl[ww * 16 + h];
-        O += f * co[(ww * 16 + h) * D + e];
-      }
-    }
-    if (e == 0) {
-      store_coherent(prs, soff + h, __float_as_uint(M));
-      store_coherent(prs, soff + G + h, __float_as_uint(L));
-    }
-    store_coherent(prs, soff + 2 * G + h * D + e, __float_as_uint(O));
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == (uint32_t)(n_split - 1);
-    if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_wg = last ? 1 : 0;
-  }
-  __syncthreads();
-  if (!last_wg) return;
-  merge_slices<D, 1, 16, kStepWaves * kWave>(prs, big, out, b, g, hq, G, n_split, tid);
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  attend_units<D, GATHER>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, bs, p, scale_log2,
+                          big + w * kUnit * SM::RS, w, kStepWaves, m_run, l_run, o);
+  l_run = sum_col4(l_run);
+  finish_row_slice<D, kStepWaves>(m_run, l_run, o, big, &last_wg, out, part, counters, row, b, g, hq, G, split,
+                                  n_split);
+}
+
+template <int D>
+hipError_t launch_pick_attend_d(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
+                                int32_t* sel, float* sel_scores, const uint32_t* ws_scores, const uint64_t* ws_lists,
+                                void* out, void* ws, int64_t kv_len, int64_t kv_cap, hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  float* part = pa.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows)) : nullptr;
+  auto kern = s.bs < kUnit ? pick_attend_kernel<D, true> : pick_attend_kernel<D, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rows * pa.n_split)), dim3(kStepWaves * kWave), 0, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), sel, sel_scores, ws_scores, ws_lists,
+                     static_cast<uint16_t*>(out), part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
+                     s.scale * 1.4426950408889634f, s.keep_tail, pa.n_chunks, pa.blocks_per_wg, pa.n_split);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -288,6 +296,30 @@ hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q
                               void* out, void* ws, hipStream_t st) {
   return s.d == 64 ? launch_step_d<64>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, st)
                    : launch_step_d<128>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, st);
+}
+
+PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks) {
+  PickAttendPlan p{};
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  // one 32-key unit per wave and slice (a slice holds at most 64 entries)
+  int bpw = s.bs < kUnit ? kStepWaves * (kUnit / s.bs) : (kStepWaves * kUnit + s.bs - 1) / s.bs;
+  if (bpw > kWave) bpw = kWave;
+  p.blocks_per_wg = bpw;
+  p.n_split = (s.top_k + bpw - 1) / bpw;
+  p.n_chunks = n_chunks;
+  p.ws_bytes = counter_bytes(rows) + (size_t)rows * p.n_split * (2 * s.group + s.group * s.d) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_pick_attend(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
+                              int32_t* sel, float* sel_scores, const void* ws_select, void* out, void* ws,
+                              int64_t kv_len, int64_t kv_cap, hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  // the score pass's workspace: scores [rows][n_chunks * 256], then the lists
+  const uint32_t* wss = reinterpret_cast<const uint32_t*>(ws_select);
+  const uint64_t* wsl = reinterpret_cast<const uint64_t*>(wss + rows * pa.n_chunks * kLargeChunk);
+  return s.d == 64 ? launch_pick_attend_d<64>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, ws, kv_len, kv_cap, st)
+                   : launch_pick_attend_d<128>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, ws, kv_len, kv_cap, st);
 }
 
 }  // namespace qsa

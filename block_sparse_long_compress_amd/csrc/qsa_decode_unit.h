@@ -277,4 +277,82 @@ __device__ __forceinline__ void merge_slices(__amdgpu_buffer_rsrc_t prs, unsigne
   }
 }
 
+// End of a row slice attended by the NW waves of a workgroup (call with every
+// thread, after attend_units and sum_col4): the waves' softmax states merge
+// in LDS in wave order; with one slice per row that is the output, else the
+// slice's state goes to the workspace with device-coherent stores, the
+// workgroup takes a ticket from the row's arrival counter, and the last one
+// to arrive merges all slices in slice order and resets the counter.
+template <int D, int NW>
+__device__ void finish_row_slice(float m_run, float l_run, const f32x4_t (&o)[D / 16], unsigned char* smem,
+                                 int* last_flag, uint16_t* __restrict__ out, float* part, uint32_t* counters,
+                                 int64_t row, int64_t b, int g, int hq, int G, int split, int n_split) {
+  constexpr int NT = NW * kWave;
+  constexpr int DT = D / 16;
+  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  const int lg = lane / 16, col = lane % 16;
+  __syncthreads();  // staging area becomes the combine area
+  float* cm = reinterpret_cast<float*>(smem);  // [NW][16] running maxima
+  float* cl = cm + NW * 16;                    // [NW][16] sums
+  float* co = cl + NW * 16;                    // [NW][16][D] unnormalised outputs
+  if (lane < 16) {
+    cm[w * 16 + col] = m_run;
+    cl[w * 16 + col] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
+  __syncthreads();
+  if (n_split == 1) {
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int h = idx / D, e = idx % D;
+      float M = -__builtin_inff();
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
+      float L = 0.f, O = 0.f;
+      for (int ww = 0; ww < NW; ++ww) {
+        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);  // 0 for waves without a unit
+        L += f * cl[ww * 16 + h];
+        O += f * co[(ww * 16 + h) * D + e];
+      }
+      out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
+    }
+    return;
+  }
+  const int stride = 2 * G + G * D;
+  const auto prs = __builtin_amdgcn_make_buffer_rsrc(part + row * (int64_t)n_split * stride, 0,
+                                                     n_split * stride * 4, kBufferFlags);
+  const int soff = split * stride;
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int h = idx / D, e = idx % D;
+    float M = -__builtin_inff();
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
+    float L = 0.f, O = 0.f;
+    if (M != -__builtin_inff()) {  // a slice may hold no visible key
+      for (int ww = 0; ww < NW; ++ww) {
+        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
+        L += f * cl[ww * 16 + h];
+        O += f * co[(ww * 16 + h) * D + e];
+      }
+    }
+    if (e == 0) {
+      store_coherent(prs, soff + h, __float_as_uint(M));
+      store_coherent(prs, soff + G + h, __float_as_uint(L));
+    }
+    store_coherent(prs, soff + 2 * G + h * D + e, __float_as_uint(O));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (uint32_t)(n_split - 1);
+    if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!*last_flag) return;
+  if (G * (D / 4) <= NT) merge_slices<D, 1, 16, NT>(prs, smem, out, b, g, hq, G, n_split, tid);
+  else merge_slices<D, 2, 8, NT>(prs, smem, out, b, g, hq, G, n_split, tid);
+}
+
 }  // namespace qsa

@@ -40,9 +40,11 @@ int64_t max_candidates(const Dims& s, int64_t kv_len);
 SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0);
 // close_block >= 0 (decode, q_len = 1): the selection also compresses that
 // block of k_cache into k_comp first (the block the new token closes).
+// pick = false (large path only): the score pass alone, for launch_pick_attend.
 hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,
                          const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
-                         hipStream_t st, const void* k_cache = nullptr, int64_t close_block = -1);
+                         hipStream_t st, const void* k_cache = nullptr, int64_t close_block = -1,
+                         bool pick = true);
 
 // Decode attention --------------------------------------------------------------
 struct DecodePlan {
@@ -79,6 +81,19 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len);
 hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                               float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
                               void* out, void* ws, hipStream_t st);
+
+// Decode step with k > 64 (bf16): the selection's score pass, then one kernel
+// that picks each row's ids and attends over them (S workgroups per row).
+struct PickAttendPlan {
+  int blocks_per_wg;
+  int n_split;
+  int64_t n_chunks;  // of the score pass
+  size_t ws_bytes;   // arrival counters and slice states (after the score pass's part)
+};
+PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks);
+hipError_t launch_pick_attend(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
+                              int32_t* sel, float* sel_scores, const void* ws_select, void* out, void* ws,
+                              int64_t kv_len, int64_t kv_cap, hipStream_t st);
 
 // Generic float32 attention (one wave per query row); used for dtype QSA_F32.
 hipError_t launch_attn_f32(const Dims& s, const float* q, const float* k, const float* v, int64_t q_len,

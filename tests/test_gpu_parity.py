@@ -315,6 +315,10 @@ STEP_CASES = [
     W(mode="decode", batch=2, kv_len=2222, dtype="f32", sigma=1.0, top_k=5),
     W(mode="decode", batch=2, kv_len=2240, dtype="f32", sigma=1.0, top_k=5, keep_tail=True),   # closes a block
     W(mode="decode", batch=1, kv_len=8 * 3000, top_k=100, block_size=8),                    # large-k, closes
+    W(mode="decode", batch=2, kv_len=32 * 700 + 5, top_k=129, block_size=32, head_dim=64),  # large-k, whole units
+    W(mode="decode", batch=2, kv_len=16 * 3000, n_q_heads=16, n_kv_heads=1, top_k=200, block_size=16),  # G = 16
+    W(mode="decode", batch=1, kv_len=3, top_k=513, block_size=4, keep_tail=True),           # no candidate yet
+    W(mode="decode", batch=3, kv_len=4 * 700, top_k=513, block_size=4, keep_tail=True),     # fewer than k blocks
 ]
 
 
