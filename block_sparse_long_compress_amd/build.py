@@ -47,9 +47,15 @@ def compile_flags() -> list[str]:
     ]
 
 
+# Per-source flags. The prefill attention never holds a NaN (masked scores
+# are -inf, and every difference of offsets is guarded), so its max
+# reductions need no NaN-quieting copies of their inputs.
+EXTRA_FLAGS = {"qsa_attn_prefill.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *compile_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

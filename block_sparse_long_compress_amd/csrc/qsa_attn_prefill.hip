@@ -15,8 +15,9 @@
 // exchange (see kkey()).
 //
 // A workgroup owns one tile of consecutive tokens of one (sequence, KV
-// head): W - 1 consumer waves with NCG CGs each (at d = 128 and G = 8: 15
-// waves of one CG, a 30-token tile) and one producer wave. The tile's
+// head): W - NP consumer waves with NCG CGs each and NP producer waves (at
+// d = 128 and G = 8: 15 waves of one CG, a 30-token tile, and 1 producer).
+// The tile's
 // selections are merged into the ascending union of their blocks, each with
 // the set of tile tokens that selected it. The producer copies the union,
 // SK keys at a time (an "item": K rows and V^T operand fragments, 16 KiB at
@@ -180,9 +181,11 @@ __device__ __forceinline__ void lds_wait_ge(const unsigned* c, unsigned target) 
     __builtin_amdgcn_s_sleep(1);
   }
 }
-// Adds 1 (one lane of the wave).
+// Adds 1 (one lane of the wave). Nothing waits for the add: a wave's LDS
+// operations complete in issue order, so it lands after the wave's earlier
+// LDS reads, and a later compiler-counted wait only waits longer.
 __device__ __forceinline__ void lds_signal(unsigned* c) {
-  if (lane_id() == 0) asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds_addr(c)), "v"(1u) : "memory");
+  if (lane_id() == 0) asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(c)), "v"(1u) : "memory");
 }
 // Stores v (one lane of the wave); nothing waits on a store.
 __device__ __forceinline__ void lds_store(unsigned* c, unsigned v) {
@@ -207,6 +210,8 @@ __host__ __device__ inline PrefillLds prefill_lds(int stage_bytes, int stages, i
   L.total = L.cum_done + u_cap * ipb * 4;
   return L;
 }
+
+constexpr int producers_for(int) { return 1; }
 
 template <int D, int BS, int W, int NCG>
 __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
@@ -250,10 +255,11 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   const int64_t b = bg / hkv;
   const int g = bg % hkv;
   const int tpc = 16 / G;
-  // One producer wave (a second one, splitting K and V^T, measured slower:
-  // it takes a consumer's place and the two shares of an item must both land).
-  constexpr int NP = 1;
-  constexpr int FPP = (Stage<D, stage_keys<D, BS, W, NCG>(), W>::kFrags) / NP;  // copies per producer per item
+  // Producer waves (items split between them). One: a second producer at 16
+  // waves measured slower (235 against 210 us at the 8K prompt), since it
+  // takes a consumer's place and the ring, not the copy rate, sets the pace.
+  constexpr int NP = producers_for(W);
+  constexpr int FPP = Stage<D, stage_keys<D, BS, W, NCG>(), W>::kFrags;  // copies per item
   // Items a producer keeps in flight after each wait: issuing the next item
   // must keep its outstanding copies within what vmcnt tracks (63), else the
   // issue itself stalls.
@@ -343,22 +349,20 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   const uint16_t* kg = k + ((b * hkv + g) * kv_cap) * D;
   const uint16_t* vtg = vt + ((b * hkv + g) * n_units) * DT * kWave * 8;
 
-  // Producer / consumer ring, no workgroup barrier. The producer waves copy
-  // each item (SK keys of one union block: K lines and V^T fragments) into
-  // stage it % ring with direct-to-LDS loads (with two producers, one copies
-  // K and one V^T), keep up to kLagP items in flight, and add 1 to
-  // ready[stage] once their share of an item has landed. A consumer wave
-  // visits only the items its tokens selected: it waits until ready shows
-  // all NP shares of that item, computes, and adds 1 to done[stage]. An item
-  // goes into a stage only after every consumer that needs one of the
-  // stage's earlier items is done with it (cum_done), so consumers drift up
-  // to `ring` items apart and a wave that needs a block holds up none of the
-  // waves that do not.
+  // Producer / consumer ring, no workgroup barrier. Producer wave w copies
+  // items w, w + NP, ... (SK keys of one union block: K lines and V^T
+  // fragments) into stage it % ring with direct-to-LDS loads, keeps up to
+  // `lag` of its items in flight, and adds 1 to ready[stage] once an item
+  // has landed. A consumer wave visits only the items its tokens selected:
+  // it waits until ready shows the item, computes, and adds 1 to
+  // done[stage]. An item goes into a stage only after every consumer that
+  // needs one of the stage's earlier items is done with it (cum_done), so
+  // consumers drift up to `ring` items apart and a wave that needs a block
+  // holds up none of the waves that do not. Every wait ends: an item waited
+  // for was issued `ring` items before, and lag * NP < ring keeps it out of
+  // every producer's not-yet-signalled tail.
   if (w < NP) {
-    // every producer walks all items; `lag` of its items stay in flight
-    const int lag = kLagP < ring - 1 ? kLagP : ring - 1;
-    const bool do_k = NP == 1 || w == 0;
-    const bool do_v = NP == 1 || w == 1;
+    const int lag = kLagP < (ring - 1) / NP ? kLagP : (ring - 1) / NP;
     // K: lines 4f .. 4f+3 of the item's rows, this lane fills slot col of
     // line 4f + lg (k_swz()); V^T: fragments are contiguous.
     unsigned k_voff[ST::kKFrags], v_voff[ST::kVFrags];
@@ -370,7 +374,8 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
 #pragma unroll
     for (int f = 0; f < ST::kVFrags; ++f) v_voff[f] = (unsigned)((f * kWave + lane) * 16);
     int ul = -1, ul_base = -1;  // 64 union block ids, one per lane
-    for (int it = 0; it < n_items; ++it) {
+    int k_own = 0;              // items this producer has issued
+    for (int it = w; it < n_items; it += NP, ++k_own) {
       const int slot = it % ring;
       // every consumer that needs one of the stage's earlier items is done with it
       if (it >= ring) lds_wait_ge(&done[slot], (unsigned)cum_done[it - ring]);
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
       // issuing a copy needs no vector ALU work (the consumers keep the
       // vector ALUs busy). Rows past the prefix fall outside the K range and
       // read as zero (masked out below).
-      if (do_k) {
+      {
         const int64_t k_left = key_first < kv_total ? (kv_total - key_first) * (D * 2) : 0;
         const int k_bytes = k_left < ST::kKFrags * 1024 ? (int)k_left : ST::kKFrags * 1024;
         const __amdgpu_buffer_rsrc_t krs =
@@ -396,21 +401,21 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
 #pragma unroll
         for (int f = 0; f < ST::kKFrags; ++f) copy_to_lds(krs, k_voff[f], dst + f * 1024);
       }
-      if (do_v) {
+      {
         const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(vtg + (c * UPB + part * UPC) * (DT * kWave * 8)), (short)0, ST::kVFrags * 1024, kBufferFlags);
 #pragma unroll
         for (int f = 0; f < ST::kVFrags; ++f) copy_to_lds(vrs, v_voff[f], dst + (ST::kKFrags + f) * 1024);
       }
-      if (it >= lag) {
-        // this producer's share of item it - lag has landed
+      if (k_own >= lag) {
+        // this producer's item it - lag * NP has landed
         if (lag == kLagP) wait_vmcnt<kLagP * FPP>();
         else wait_vmcnt_le(lag * FPP);
-        lds_signal(&ready[(it - lag) % ring]);
+        lds_signal(&ready[(it - lag * NP) % ring]);
       }
     }
     wait_vmcnt<0>();
-    for (int it = n_items - lag > 0 ? n_items - lag : 0; it < n_items; ++it) lds_signal(&ready[it % ring]);
+    for (int j = k_own - lag > 0 ? k_own - lag : 0; j < k_own; ++j) lds_signal(&ready[(w + j * NP) % ring]);
     return;
   }
   const int cw = w - NP;
@@ -418,7 +423,12 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   // ---- per CG: this lane's column token, its position, softmax state, Q operands
   u32x4_t qf[NCG][KS];
   f32x4_t o[NCG][DT];
-  float m_run[NCG], l_run[NCG];
+  // Softmax sums: one more PV product per 32 keys with an all-ones V^T
+  // operand sums each column's bf16 P, the same P the outputs accumulate
+  // (every row of the 16 x 16 result holds the column's sum).
+  f32x4_t ol[NCG];
+  const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  float m_run[NCG];
   int pos_q[NCG];  // absolute positions fit in int32 (checked on the host)
   bool row_ok[NCG];
   const int tau = col / G;
@@ -428,7 +438,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
     row_ok[n] = r < rows;
     pos_q[n] = (int)(pos_first + r);
     m_run[n] = -__builtin_inff();
-    l_run[n] = 0.f;
+    ol[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const uint16_t* qs = q + ((b * q_len + t0 + r) * hq + (int64_t)g * G + col % G) * D + 8 * lg;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -462,7 +472,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
     for (int part = 0; part < IPB; ++part) {
     const int it = ui * IPB + part;
     const int slot = it % ring;
-    lds_wait_ge(&ready[slot], (unsigned)(NP * (it / ring + 1)));
+    lds_wait_ge(&ready[slot], (unsigned)(it / ring + 1));
     {
     const int key0 = (int)(c * BS) + part * SK;  // positions fit in int32 (checked on the host)
     const bool diag = key0 + SK > pos_first;           // holds the own block of some token: causal mask
@@ -524,7 +534,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
           const float m_new = grow ? cand : m_old;
           if (__ballot(grow && m_old != -__builtin_inff()) != 0) {
             const float alpha = grow ? __builtin_amdgcn_exp2f(m_old - m_new) : 1.0f;
-            l_run[n] *= alpha;
+            ol[n] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[n][dt] *= alpha;
           }
@@ -534,7 +544,6 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
 #pragma unroll
           for (int i = 0; i < SUB * 4; ++i) {
             pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scale_log2, negm));
-            l_run[n] += pv[i];
           }
           // P^T operand of 32-key step u: tiles 2u, 2u+1 (see kkey())
 #pragma unroll
@@ -546,7 +555,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
         }
       }
 #pragma unroll
-      for (int u = 0; u < UPC; ++u)
+      for (int u = 0; u < UPC; ++u) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vb + ((u * DT + dt) * kWave + lane) * 16);
@@ -554,6 +563,10 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
           for (int n = 0; n < NCG; ++n)
             if (((MASK >> n) & 1u) != 0u) o[n][dt] = mfma_bf16(vf, pf[n][u], o[n][dt]);
         }
+#pragma unroll
+        for (int n = 0; n < NCG; ++n)
+          if (((MASK >> n) & 1u) != 0u) ol[n] = mfma_bf16(ones, pf[n][u], ol[n]);
+      }
     };
     if constexpr (NCG == 2) {
       if (need == 3u) run.template operator()<3u>();
@@ -574,7 +587,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
 
 #pragma unroll
   for (int n = 0; n < NCG; ++n) {
-    const float l = sum_col4(l_run[n]);
+    const float l = ol[n][0];
     if (!row_ok[n]) continue;
     const float inv = 1.0f / l;
     const int r = (cw * NCG + n) * tpc + tau;
@@ -616,7 +629,7 @@ PrefillGeom prefill_geom(const Dims& s, int64_t q_len, int64_t q_pos0) {
   using ST = Stage<D, stage_keys<D, BS, W, NCG>(), W>;
   PrefillGeom gm;
   const int64_t kv_total = q_pos0 + q_len;
-  gm.qt = (W - 1) * NCG * (16 / s.group);  // the producer wave only copies
+  gm.qt = (W - producers_for(W)) * NCG * (16 / s.group);  // producer waves only copy
   gm.n_tiles = (int)((q_len + gm.qt - 1) / gm.qt);
   gm.n_words = (int)(((kv_total - 1) / BS) / 32) + 1;
   const int64_t n_blocks = (kv_total + BS - 1) / BS;
@@ -721,7 +734,7 @@ hipError_t launch_d(const Dims& s, const PrefillPlan& plan, const void* q, const
 PrefillPlan plan_prefill(const Dims& s, int64_t q_len, int64_t q_pos0) {
   PrefillPlan p{};
   const int w = waves_for(s.group, s.d);
-  p.rows_per_wg = (w - 1) * ncg_per_wave(s.group, s.d) * (16 / s.group);
+  p.rows_per_wg = (w - producers_for(w)) * ncg_per_wave(s.group, s.d) * (16 / s.group);
   if (s.dtype != 1) {
     p.ws_bytes = 0;
     return p;
