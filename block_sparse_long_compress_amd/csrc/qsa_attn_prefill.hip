@@ -228,6 +228,9 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
   constexpr int IPB = BS / SK;           // ring items (stages' worth of keys) per block
   constexpr int SUB = SK / 16;           // 16-key S^T tiles per item
   constexpr int UPC = SK / kUnit;        // 32-key PV steps per item
+  // one CG per wave and at most 8 V^T fragments per item: the stage is
+  // released as soon as its V^T fragments are read (see run below)
+  constexpr bool kEarlyDone = NCG == 1 && UPC * DT <= 8;
   extern __shared__ __align__(16) unsigned char smem[];
 
   // Work item: (sequence, KV head, tile). Workgroups go to the 8 XCDs
@@ -502,6 +505,21 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
           }
         }
       }
+      // With one CG per wave the V^T fragments are read right after the S
+      // products are issued (in flight during the softmax) and the stage is
+      // released before the PV products: it is held only until its data has
+      // been read, not for the whole visit.
+      constexpr bool kEarly = kEarlyDone;
+      u32x4_t vfe[kEarly ? UPC : 1][kEarly ? DT : 1];
+      if constexpr (kEarly) {
+#pragma unroll
+        for (int u = 0; u < UPC; ++u)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            vfe[u][dt] = *reinterpret_cast<const u32x4_t*>(vb + ((u * DT + dt) * kWave + lane) * 16);
+        // a wave's LDS operations complete in order: the add lands after the reads
+        lds_signal(&done[slot]);
+      }
       u32x4_t pf[NCG][UPC];
 #pragma unroll
       for (int n = 0; n < NCG; ++n) {
@@ -558,7 +576,9 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
       for (int u = 0; u < UPC; ++u) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vb + ((u * DT + dt) * kWave + lane) * 16);
+          u32x4_t vf;
+          if constexpr (kEarly) vf = vfe[u][dt];
+          else vf = *reinterpret_cast<const u32x4_t*>(vb + ((u * DT + dt) * kWave + lane) * 16);
 #pragma unroll
           for (int n = 0; n < NCG; ++n)
             if (((MASK >> n) & 1u) != 0u) o[n][dt] = mfma_bf16(vf, pf[n][u], o[n][dt]);
@@ -580,7 +600,7 @@ __global__ __launch_bounds__(W * 64, 1) void prefill_attn_kernel(
       if constexpr (NCG > 3) if (need & 8u) run.template operator()<8u>();
     }
     }
-    lds_signal(&done[slot]);
+    if constexpr (!kEarlyDone) lds_signal(&done[slot]);
     }
     }
   }
