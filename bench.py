@@ -77,8 +77,21 @@ def visible_keys(p: int, bs: int, k: int, keep_tail: bool = False) -> int:
     return min(k - 1, n_cand) * bs + (0 if forced is None else p - forced * bs + 1)
 
 
-def work_model(w, n_new_blocks: int):
-    """Algorithmic bytes / flops per ABI call of one step (nothing QSA skips is counted)."""
+def work_model(w, n_new_blocks: int, lens=None):
+    """Algorithmic bytes / flops per ABI call of one step (nothing QSA skips is counted).
+
+    ``lens``: per-sequence lengths of a ragged decode batch (the sum of every
+    sequence's own model, each closing a block when its length is a multiple
+    of the block size)."""
+    if lens is not None and w.ragged:
+        total = {}
+        for n in lens:
+            one = work_model(w.replace(batch=1, kv_len=n, ragged=False), 1 if n % w.block_size == 0 else 0)
+            for key, val in one.items():
+                acc = total.setdefault(key, {"bytes": 0, "flops": 0})
+                acc["bytes"] += val["bytes"]
+                acc["flops"] += val["flops"]
+        return total
     b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
     el = 2 if w.dtype == "bf16" else 4
     m = {}
@@ -139,12 +152,24 @@ class Step:
             self.out_dec = self.out.view(b, hq, d)
             self.sel_dec = self.sel.view(b, hkv, k)
             self.ws_att = self._ws(qsa.QSA_OP_DECODE, 1, w.kv_len)
-            self.ws_step = self._ws(qsa.QSA_OP_DECODE_STEP, 1, w.kv_len)
-            self.fused = qsa.qsa_decode_step_fused(self.shape, w.kv_len)
-            # everything before the new token is already compressed
-            qsa.qsa_compress_keys(self.shape, self.k, w.kv_len - 1, self.k_comp)
-            self.blk_begin = (w.kv_len - 1) // bs
-            self.n_new_blocks = w.kv_len // bs - self.blk_begin
+            self.lens = S.seq_lengths(w, seed)
+            if w.ragged:
+                # every sequence at its own length: one ragged step call
+                self.ws_step = self._ws(qsa.QSA_OP_DECODE_STEP_RAGGED, 1, w.kv_len)
+                self.fused = True
+                self.kv_lens = torch.tensor(self.lens, dtype=torch.int32, device="cuda")
+                one = qsa.make_shape(1, hq, hkv, d, bs, k, self.q.dtype, keep_tail=w.keep_tail)
+                for bb, n in enumerate(self.lens):
+                    qsa.qsa_compress_keys(one, self.k[bb:bb + 1], n - 1, self.k_comp[bb:bb + 1])
+                self.blk_begin = 0
+                self.n_new_blocks = sum(1 for n in self.lens if n % bs == 0)
+            else:
+                self.ws_step = self._ws(qsa.QSA_OP_DECODE_STEP, 1, w.kv_len)
+                self.fused = qsa.qsa_decode_step_fused(self.shape, w.kv_len)
+                # everything before the new token is already compressed
+                qsa.qsa_compress_keys(self.shape, self.k, w.kv_len - 1, self.k_comp)
+                self.blk_begin = (w.kv_len - 1) // bs
+                self.n_new_blocks = w.kv_len // bs - self.blk_begin
         else:
             self.ws_att = self._ws(qsa.QSA_OP_PREFILL, q_len, w.kv_len)
             self.blk_begin = 0
@@ -166,6 +191,10 @@ class Step:
 
     def decode_step(self):
         w = self.w
+        if w.ragged:
+            self.qsa.qsa_decode_step_ragged(self.shape, self.q_dec, self.k, self.v, self.k_comp, self.kv_lens,
+                                            w.kv_len, self.sel_dec, self.out_dec, ws=self.ws_step)
+            return
         self.qsa.qsa_decode_step(self.shape, self.q_dec, self.k, self.v, self.k_comp, w.kv_len, self.sel_dec,
                                  self.out_dec, ws=self.ws_step)
 
@@ -307,7 +336,8 @@ def cpu_baseline(w, seed, budget_s):
             q = S.gen_q(w, seed, 0)
             K = np.stack([S.gen_kv(w, seed, S.TENSOR_K, 0, g, q) for g in range(w.n_kv_heads)])
             V = np.stack([S.gen_kv(w, seed, S.TENSOR_V, 0, g) for g in range(w.n_kv_heads)])
-            p = w.kv_len - 1
+            n0 = S.seq_lengths(w, seed)[0]  # sequence 0's length (all kv_len unless ragged)
+            p = n0 - 1
             n_prev = p // bs  # blocks complete before the new token
             kc = np.zeros((w.n_kv_heads, w.kv_len // bs, w.head_dim))
             kc[:, :n_prev] = O.compress_keys(K[:, : n_prev * bs], bs)
@@ -326,8 +356,11 @@ def cpu_baseline(w, seed, budget_s):
                 if el >= budget_s or n_steps >= 100000:
                     break
             return {"value": n_steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                    "sample": f"{n_steps} decode steps of one sequence (both KV heads: compress of the completed "
-                              f"block, scores over {n_cand} candidates, top-{k} selection, attention) in {el:.1f} s"}
+                    "sample": f"{n_steps} decode steps of one sequence of {n0} tokens (both KV heads: compress of "
+                              f"the completed "
+                              f"block, scores over {n_cand} candidates, top-{k} selection, attention) in {el:.1f} s"
+                              + (" (sequence 0 of the ragged batch; its steps stand for the batch's)" if w.ragged
+                                 else "")}
         # prefill: compress everything, then a uniform sample of query rows, scaled to the full prompt
         Qs, Ks, Vs = S.gen_all(w, seed)
         Q, K, V = (S.as_f32(x, w.dtype) for x in (Qs, Ks, Vs))
@@ -397,7 +430,7 @@ def main():
     w = S.WORKLOADS[args.workload]
     st, wall, per_call, cold_s, call_timing = run_gpu(w, args.steps, args.warmup, args.seed, not args.no_graph,
                                                       args.graph_steps)
-    model = work_model(w, st.n_new_blocks)
+    model = work_model(w, st.n_new_blocks, getattr(st, "lens", None))
     model["step"] = {"bytes": sum(m["bytes"] for m in model.values()), "flops": sum(m["flops"] for m in model.values())}
     ms_per_step = 1e3 * wall / args.steps
     tokens = w.batch if w.mode == "decode" else w.batch * w.kv_len
@@ -432,7 +465,9 @@ def main():
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "top_k": w.top_k, "keep_tail": w.keep_tail, "seed": args.seed,
                    "graphs": not args.no_graph, "graph_steps": 1 if args.no_graph else max(1, args.graph_steps),
-                   "fused_decode_step": st.fused},
+                   "fused_decode_step": st.fused, "ragged": w.ragged,
+                   **({"mean_kv_len": round(float(np.mean(st.lens)), 1), "min_kv_len": int(min(st.lens))}
+                      if w.ragged else {})},
         "roofline": {"bound": bound,
                      "kernel": "decode_step_kernel (the whole step)" if dominant == "step" else f"{dominant} call",
                      "achieved": round(achieved, 2), "peak": peak,

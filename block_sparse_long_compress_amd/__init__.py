@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     QSA_OP_COMPRESS,
     QSA_OP_DECODE,
     QSA_OP_DECODE_STEP,
+    QSA_OP_DECODE_STEP_RAGGED,
     QSA_OP_PREFILL,
     QSA_OP_SELECT,
     QsaError,
@@ -29,6 +30,7 @@ from .binding import (  # noqa: F401
     qsa_compress_keys,
     qsa_decode_step,
     qsa_decode_step_fused,
+    qsa_decode_step_ragged,
     qsa_score_select,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_prefill,

@@ -19,9 +19,11 @@ LIB_PATH = os.environ.get("QSA_LIB", os.path.join(HERE, "lib", "libqsa.so"))
 
 QSA_F32, QSA_BF16 = 0, 1
 QSA_OP_COMPRESS, QSA_OP_SELECT, QSA_OP_DECODE, QSA_OP_PREFILL, QSA_OP_DECODE_STEP = 0, 1, 2, 3, 4
+QSA_OP_DECODE_STEP_RAGGED = 5
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_ERR_WORKSPACE", 4: "QSA_ERR_HIP"}
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
-            "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused")
+            "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused",
+            "qsa_decode_step_ragged")
 
 
 class QsaError(RuntimeError):
@@ -69,6 +71,8 @@ def _load() -> ctypes.CDLL:
     lib.qsa_decode_step.argtypes = [SH, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
     lib.qsa_decode_step_fused.restype = ctypes.c_int
     lib.qsa_decode_step_fused.argtypes = [SH, I64]
+    lib.qsa_decode_step_ragged.restype = ctypes.c_int
+    lib.qsa_decode_step_ragged.argtypes = [SH, P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
     return lib
 
 
@@ -177,6 +181,24 @@ def qsa_decode_step(shape: QsaShape, q, k, v, k_comp, kv_len: int, sel, out, sel
     _check(LIB.qsa_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_comp), kv_len, k.shape[2],
                                _ptr(sel), _ptr(sel_scores), _ptr(out), _ptr(ws), nbytes, _stream(q, stream)),
            "qsa_decode_step")
+    return out
+
+
+def qsa_decode_step_ragged(shape: QsaShape, q, k, v, k_comp, kv_lens, max_kv_len: int, sel, out, sel_scores=None,
+                           ws=None, stream=None):
+    """One decode step for a ragged batch: sequence ``b``'s token sits at position ``kv_lens[b] - 1``
+    (``kv_lens``: int32 device tensor ``[b]``, each at most ``max_kv_len``)."""
+    if kv_lens.dtype != torch.int32 or not kv_lens.is_contiguous() or kv_lens.numel() != k.shape[0]:
+        raise QsaError(1, "qsa_decode_step_ragged: kv_lens must be a contiguous int32 tensor of length batch")
+    if ws is None and LIB.qsa_workspace_bytes(ctypes.byref(shape), QSA_OP_DECODE_STEP_RAGGED, 1,
+                                              max_kv_len) == ctypes.c_size_t(-1).value:
+        nbytes = 0  # a shape the ragged step does not serve: the call reports why
+    else:
+        ws, nbytes = _workspace(shape, QSA_OP_DECODE_STEP_RAGGED, 1, max_kv_len, ws, q.device)
+    _check(LIB.qsa_decode_step_ragged(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_comp), _ptr(kv_lens),
+                                      max_kv_len, k.shape[2], _ptr(sel), _ptr(sel_scores), _ptr(out), _ptr(ws),
+                                      nbytes, _stream(q, stream)),
+           "qsa_decode_step_ragged")
     return out
 
 

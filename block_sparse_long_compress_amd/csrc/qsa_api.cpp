@@ -116,6 +116,11 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       const size_t d = s.dtype == QSA_BF16 ? qsa::plan_decode(s, kv_len).ws_bytes : 0;
       return a + d;
     }
+    case QSA_OP_DECODE_STEP_RAGGED: {
+      if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
+      const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len, true);
+      return sp.fused ? sp.ws_bytes : (size_t)-1;
+    }
   }
   return (size_t)-1;
 }
@@ -249,6 +254,28 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
   if (st != QSA_OK) return st;
   void* ws_dec = ws ? static_cast<char*>(ws) + sel_part : nullptr;
   return qsa_sparse_attn_decode(shape, q, k, v, kv_len, kv_cap, sel, out, ws_dec, need - sel_part, stream);
+}
+
+qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                  float* k_comp, const int32_t* kv_lens, int64_t max_kv_len, int64_t kv_cap,
+                                  int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !k || !v || !k_comp || !kv_lens || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_comp) || !aligned16(sel) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0)
+    return QSA_ERR_INVALID;
+  if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
+  if (max_kv_len <= 0 || kv_cap <= 0 || max_kv_len > kv_cap) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  const qsa::StepPlan sp = qsa::plan_decode_step(s, max_kv_len, true);
+  if (!sp.fused) return QSA_ERR_UNSUPPORTED;  // only the fused kernel reads per-sequence lengths
+  if ((int64_t)s.batch * s.hkv * sp.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (sp.ws_bytes > 0 && (!ws || ws_bytes < sp.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, max_kv_len, kv_cap, sel, sel_scores, out, ws,
+                                            static_cast<hipStream_t>(stream), kv_lens));
 }
 
 }  // extern "C"

@@ -41,8 +41,9 @@ template <int D, int BS>
 __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     float* __restrict__ k_comp, int32_t* __restrict__ sel, float* __restrict__ sel_scores, uint16_t* __restrict__ out,
-    float* __restrict__ part, uint32_t* __restrict__ counters, int64_t kv_len, int64_t kv_cap, int hq, int hkv, int G,
-    int top_k, float scale, int keep_tail, int bpw, int n_split) {
+    float* __restrict__ part, uint32_t* __restrict__ counters, const int32_t* __restrict__ kv_lens,
+    int64_t kv_len_max, int64_t kv_cap, int hq, int hkv, int G, int top_k, float scale, int keep_tail, int bpw,
+    int n_split) {
   using SM = StepSmem<D>;
   constexpr int LPR = D / 4;  // lanes covering one compressed key row (float32)
   constexpr int DT = D / 16;
@@ -56,8 +57,14 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   const int split = (int)(blockIdx.x % n_split);
   const int64_t b = row / hkv;
   const int g = (int)(row % hkv);
-  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
-  const int lg = lane / 16, col = lane % 16;
+  const int lane = lane_id(), w = wave_id();
+  // this sequence's length: one for the batch, or its own (ragged batch,
+  // clamped into [1, kv_len_max] so that every access stays in bounds)
+  int64_t kv_len = kv_len_max;
+  if (kv_lens) {
+    const int64_t n = kv_lens[b];
+    kv_len = n < 1 ? 1 : (n > kv_len_max ? kv_len_max : n);
+  }
   const int64_t p = kv_len - 1;
   const Frame fr = row_frame(p, BS, keep_tail);
   const int slots = frame_slots(fr, top_k);
@@ -226,7 +233,7 @@ hipError_t launch_pick_attend_d(const Dims& s, const PickAttendPlan& pa, const v
 template <int D>
 hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                          float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out,
-                         void* ws, hipStream_t st) {
+                         void* ws, const int32_t* kv_lens, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const dim3 grid((unsigned)(rows * plan.n_split)), block(kStepWaves * kWave);
   uint32_t* counters = static_cast<uint32_t*>(ws);
@@ -238,18 +245,18 @@ hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, con
   switch (s.bs) {
     case 32:
       hipLaunchKernelGGL((decode_step_kernel<D, 32>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
-                         part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail,
-                         plan.blocks_per_wg, plan.n_split);
+                         part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
+                         s.keep_tail, plan.blocks_per_wg, plan.n_split);
       break;
     case 64:
       hipLaunchKernelGGL((decode_step_kernel<D, 64>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
-                         part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail,
-                         plan.blocks_per_wg, plan.n_split);
+                         part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
+                         s.keep_tail, plan.blocks_per_wg, plan.n_split);
       break;
     case 128:
       hipLaunchKernelGGL((decode_step_kernel<D, 128>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
-                         part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail,
-                         plan.blocks_per_wg, plan.n_split);
+                         part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
+                         s.keep_tail, plan.blocks_per_wg, plan.n_split);
       break;
     default:
       return hipErrorInvalidValue;
@@ -259,16 +266,17 @@ hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, con
 
 }  // namespace
 
-StepPlan plan_decode_step(const Dims& s, int64_t kv_len) {
+StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged) {
   StepPlan p{};
   p.fused = false;
   if (s.dtype != 1 || s.top_k > 64 || s.bs < 32) return p;
   // A workgroup streams its row's compressed keys alone: worth it while the
   // row is short (the per-CU read rate bounds it) or the rows alone fill
-  // the GPU (then HBM bounds it either way).
+  // the GPU (then HBM bounds it either way). A ragged batch always runs
+  // fused (kv_len is then the longest sequence's length).
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const int64_t row_bytes = max_candidates(s, kv_len) * s.d * 4;
-  if (row_bytes > (512 << 10) && rows < 64) return p;
+  if (row_bytes > (512 << 10) && rows < 64 && !ragged) return p;
   p.fused = true;
   // Few rows: slices of the selection that give each wave about one 32-key
   // unit, as long as the grid stays small (every slice repeats the scan).
@@ -293,9 +301,10 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len) {
 
 hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                               float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
-                              void* out, void* ws, hipStream_t st) {
-  return s.d == 64 ? launch_step_d<64>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, st)
-                   : launch_step_d<128>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, st);
+                              void* out, void* ws, hipStream_t st, const int32_t* kv_lens) {
+  return s.d == 64
+             ? launch_step_d<64>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, kv_lens, st)
+             : launch_step_d<128>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, kv_lens, st);
 }
 
 PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks) {

@@ -77,10 +77,14 @@ struct StepPlan {
   int n_split;
   size_t ws_bytes;
 };
-StepPlan plan_decode_step(const Dims& s, int64_t kv_len);
+// ragged: a batch of sequences of their own lengths (kv_len is then the
+// longest), which always runs fused when the kernel serves the shape.
+StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged = false);
+// kv_lens (device, [batch], nullable): per-sequence lengths, each clamped
+// into [1, kv_len]; null means every sequence has kv_len.
 hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                               float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
-                              void* out, void* ws, hipStream_t st);
+                              void* out, void* ws, hipStream_t st, const int32_t* kv_lens = nullptr);
 
 // Decode step with k > 64 (bf16): the selection's score pass, then one kernel
 // that picks each row's ids and attends over them (S workgroups per row).

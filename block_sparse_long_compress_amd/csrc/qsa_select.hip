@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   const float* kc_src = k_comp + ((b * hkv + g) * nb_cap) * D;
   uint64_t cur = 0ull;
   for (int64_t base = c_begin + (int64_t)kWave * w; base < c_end; base += 4 * kWave) {
-    const float s = dot64_rows<D>(kc_src + base * D, c_end - base, qv);
+    const float s = dot64_rows<D, true>(kc_src + base * D, c_end - base, qv);
     const int64_t cand = base + dot64_row<D>(lane);
     const uint64_t key = cand < c_end ? make_key(s * scale, (int)cand) : 0ull;
     cur = topk_fold(cur, key, slots);
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
   const int64_t base = c_begin + (int64_t)kWave * w;
   uint64_t key = 0ull;
   if (base < n_cand) {
-    const float sc = dot64_rows<D>(k_comp + ((b * hkv + g) * nb_cap + base) * D, n_cand - base, qv);
+    const float sc = dot64_rows<D, true>(k_comp + ((b * hkv + g) * nb_cap + base) * D, n_cand - base, qv);
     const int64_t cand = base + dot64_row<D>(lane);
     if (cand < n_cand) {
       key = make_key(sc * scale, (int)cand);

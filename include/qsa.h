@@ -82,11 +82,18 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
-enum { QSA_OP_COMPRESS = 0, QSA_OP_SELECT = 1, QSA_OP_DECODE = 2, QSA_OP_PREFILL = 3, QSA_OP_DECODE_STEP = 4 };
+enum {
+  QSA_OP_COMPRESS = 0,
+  QSA_OP_SELECT = 1,
+  QSA_OP_DECODE = 2,
+  QSA_OP_PREFILL = 3,
+  QSA_OP_DECODE_STEP = 4,
+  QSA_OP_DECODE_STEP_RAGGED = 5
+};
 
 typedef enum {
   QSA_OK = 0,
@@ -118,6 +125,8 @@ const char* qsa_status_str(qsa_status status);
  * (size_t)-1 if the arguments are invalid). op is one of QSA_OP_*.
  * QSA_OP_SELECT and QSA_OP_PREFILL take q_len and kv_len = q_pos0 + q_len;
  * QSA_OP_DECODE takes kv_len (q_len ignored).
+ * QSA_OP_DECODE_STEP_RAGGED takes the longest sequence's length as kv_len
+ * and returns (size_t)-1 for shapes the ragged step does not serve.
  * Zero-fill a workspace once before its first use. Decode workspaces, and
  * selection workspaces whose rows are split over several workgroups, start
  * with one arrival counter per row ((sequence, KV head), resp. (sequence,
@@ -205,6 +214,28 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
 /* 1 when qsa_decode_step runs these sizes as the single fused kernel, 0 when
  * it runs the separate calls, -1 for invalid arguments. */
 int qsa_decode_step_fused(const qsa_shape* shape, int64_t kv_len);
+
+/* One decode step for a batch of sequences of different lengths (a ragged
+ * batch): for every sequence b, the same results as qsa_decode_step with
+ * kv_len = kv_lens[b] on that sequence alone ("Qwen4 in llama.cpp:
+ * Dissecting PR #27742", section "QSA Is an Address-Selection Problem, Not a
+ * New Attention Equation": selection and attention are per token; here each
+ * sequence's token sits at its own position kv_lens[b]-1).
+ *   kv_lens     device int32 [batch], 4-byte aligned; values are clamped
+ *               into [1, max_kv_len] (so accesses stay in bounds).
+ *   max_kv_len  host bound, >= every kv_lens[b] and <= kv_cap; it sizes the
+ *               launch and the workspace.
+ * Other arguments as for qsa_decode_step; sequence b reads K/V positions
+ * [0, kv_lens[b]) and k_comp blocks [0, kv_lens[b]/Bs) of its own rows.
+ * Runs as the fused kernel only: bf16, k <= 64 and Bs >= 32, else
+ * QSA_ERR_UNSUPPORTED. ws: qsa_workspace_bytes(shape,
+ * QSA_OP_DECODE_STEP_RAGGED, 1, max_kv_len) bytes, zero-filled before first
+ * use. Outputs equal the per-sequence qsa_decode_step's up to the rounding
+ * of the attention merge order (selections are identical). */
+qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                  float* k_comp, const int32_t* kv_lens, int64_t max_kv_len, int64_t kv_cap,
+                                  int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

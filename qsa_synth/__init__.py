@@ -14,6 +14,11 @@ regenerated on its own):
 * Values are float32 standard normals times ``sigma`` (1.0 or 0.5, both
   exact in binary), rounded once to bfloat16 with round-to-nearest-even for
   the bf16 workloads.
+* A ragged decode workload gives sequence ``b`` the length
+  ``seq_lengths(w, seed)[b]``: integers drawn uniformly from
+  ``[kv_len/8, kv_len]`` (tensor id 4), the last one set to ``kv_len``; the
+  inputs are generated for ``kv_len`` positions and a sequence reads only
+  its first ``length`` of them.
 * The planted workload (batched decode) shifts every key of 8 chosen
   complete blocks per ``(b, kv_head)`` by ``2*sigma`` along the unit vector
   of the sum of that KV head's query heads (bf16-rounded), in float32 before
@@ -29,7 +34,7 @@ from concurrent.futures import ProcessPoolExecutor
 
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_PLANT = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_PLANT, TENSOR_LEN = 0, 1, 2, 3, 4
 
 
 @dataclasses.dataclass(frozen=True)
@@ -50,6 +55,7 @@ class Workload:
     sigma: float
     planted: int = 0
     keep_tail: bool = False  # selection frame of the released budget (see the oracle)
+    ragged: bool = False  # decode: every sequence has its own length (see seq_lengths)
 
     @property
     def q_len(self) -> int:
@@ -69,13 +75,16 @@ class Workload:
 
 # The five workloads: tiny fp32 prefill, bf16 decode at 32K, bf16 prefill at
 # 8K, batched bf16 decode at 128K with planted blocks, bf16 decode at 1M; then
-# bf16 decode in the released budget regime at 256K.
+# a ragged batched decode and bf16 decode in the released budget regime at 256K.
 WORKLOADS = {
     "prefill_512_f32": Workload("prefill_512_f32", 1, "prefill", 1, 512, 2, 1, 64, 32, 4, "f32", 1.0),
     "decode_32k": Workload("decode_32k", 2, "decode", 1, 32768, 16, 2, 128, 64, 16, "bf16", 0.5),
     "prefill_8k": Workload("prefill_8k", 3, "prefill", 1, 8192, 16, 2, 128, 64, 16, "bf16", 0.5),
     "decode_b64_128k": Workload("decode_b64_128k", 4, "decode", 64, 131072, 16, 2, 128, 64, 16, "bf16", 0.5, planted=8),
     "decode_1m": Workload("decode_1m", 5, "decode", 1, 1048576, 16, 2, 128, 64, 32, "bf16", 0.5),
+    # a ragged batch: 64 sequences of 16K .. 128K tokens
+    "decode_b64_ragged": Workload("decode_b64_ragged", 7, "decode", 64, 131072, 16, 2, 128, 64, 16, "bf16", 0.5,
+                                  ragged=True),
     # the released budget regime: ratio 4, 2048-token budget (512 blocks + the
     # partial-tail slot), 262144-token context = 65536 compressed blocks
     "decode_256k_r4": Workload("decode_256k_r4", 6, "decode", 1, 262144, 16, 2, 128, 4, 513, "bf16", 0.5,
@@ -112,6 +121,16 @@ def gen_q(w: Workload, seed: int, b: int) -> np.ndarray:
     """Queries of sequence b, ``[q_len][Hq][d]`` float32 (values exact in ``w.dtype``)."""
     x = _rng(seed, w.cfg_id, TENSOR_Q, b).standard_normal((w.q_len, w.n_q_heads, w.head_dim), dtype=np.float32)
     return _store(x * np.float32(w.sigma), w.dtype)
+
+
+def seq_lengths(w: Workload, seed: int) -> list[int]:
+    """Per-sequence lengths of a decode workload (all ``kv_len`` unless ``w.ragged``)."""
+    if not w.ragged:
+        return [w.kv_len] * w.batch
+    lo = max(1, w.kv_len // 8)
+    n = _rng(seed, w.cfg_id, TENSOR_LEN).integers(lo, w.kv_len + 1, size=w.batch)
+    n[-1] = w.kv_len
+    return [int(x) for x in n]
 
 
 def planted_blocks(w: Workload, seed: int, b: int, g: int) -> np.ndarray:

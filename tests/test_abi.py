@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 2
+    assert qsa.abi_version() == 3
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -153,3 +153,32 @@ def test_argument_validation(qsa):
     assert lib.qsa_sparse_attn_prefill(sh, P, P, N, 64, 0, 64, P, P, P, big, N) == INV
     assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 64, 0, 64, P, P, N, 0, N) == WS
     assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 64, 0, 64, P, P, P, 16, N) == WS
+
+
+def test_ragged_decode_step_arguments(qsa):
+    """Per-sequence lengths: validated on the host; the ragged step serves only the fused kernel's shapes."""
+    lib = qsa.LIB
+    sh = good_shape(qsa, batch=4)
+    shr = ctypes.byref(sh)
+    P, N, MIS4 = ctypes.c_void_p(4096), None, ctypes.c_void_p(4098)
+    big = 1 << 30
+    INV, UNS, WS = 1, 2, 3
+    ws = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 131072)
+    assert ws == qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 4096)  # same per-row plan
+    call = lib.qsa_decode_step_ragged
+    assert call(shr, P, P, P, P, N, 64, 64, P, N, P, P, big, N) == INV           # no lengths
+    assert call(shr, P, P, P, P, MIS4, 64, 64, P, N, P, P, big, N) == INV        # lengths not 4-byte aligned
+    assert call(shr, P, P, P, P, P, 65, 64, P, N, P, P, big, N) == INV           # bound beyond capacity
+    assert call(shr, P, P, P, P, P, 0, 64, P, N, P, P, big, N) == INV
+    assert call(shr, N, P, P, P, P, 64, 64, P, N, P, P, big, N) == INV
+    # shapes without the fused kernel: f32, k > 64, Bs < 32
+    for kw in (dict(dtype=qsa.QSA_F32), dict(top_k=65), dict(block_size=16)):
+        bad = good_shape(qsa, batch=4, **kw)
+        assert call(ctypes.byref(bad), P, P, P, P, P, 4096, 4096, P, N, P, P, big, N) == UNS
+        with pytest.raises(qsa.QsaError):
+            qsa.qsa_workspace_bytes(bad, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 4096)
+    # few long rows: the ragged step still runs fused (the plain step would not)
+    one = good_shape(qsa, batch=1)
+    assert not qsa.qsa_decode_step_fused(one, 1 << 20)
+    assert qsa.qsa_workspace_bytes(one, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 1 << 20) > 0
+    assert call(ctypes.byref(one), P, P, P, P, P, 1 << 20, 1 << 20, P, N, P, P, 8, N) == WS

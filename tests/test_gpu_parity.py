@@ -349,3 +349,64 @@ def test_decode_step_parity(w):
     st = check_rows(case, sel.cpu().numpy()[:, None], from_device(out)[:, None], rows, w.kv_len - 1,
                     scores_gpu=scores.cpu().numpy()[:, None])
     log(f"  {st}")
+
+
+def _lengths(batch: int, max_len: int, seed: int) -> list[int]:
+    rng = np.random.default_rng(seed)
+    n = [int(x) for x in rng.integers(1, max_len + 1, size=batch)]
+    n[-1] = max_len
+    return n
+
+
+RAGGED_CASES = [
+    # single token, one short of a block, closing the first block, mid, closing block 65, the longest
+    (W(mode="decode", batch=6, kv_len=9000, top_k=16), [1, 63, 64, 1000, 4160, 9000]),
+    (W(mode="decode", batch=5, kv_len=5000, top_k=8, block_size=32, keep_tail=True), [32, 33, 2048, 4999, 5000]),
+    (W(mode="decode", batch=70, kv_len=3000, top_k=16, n_q_heads=8, n_kv_heads=2, head_dim=64, block_size=128),
+     _lengths(70, 3000, 5)),   # 140 rows: one workgroup per row
+    (W(mode="decode", batch=3, kv_len=40000, top_k=64, n_q_heads=16, n_kv_heads=1), [17, 20000, 40000]),  # G = 16
+]
+
+
+@pytest.mark.parametrize("w,lens", RAGGED_CASES, ids=lambda x: case_id(x) if isinstance(x, S.Workload) else None)
+def test_decode_step_ragged(w, lens):
+    """A ragged batch: every sequence matches the oracle at its own length, and the per-sequence step."""
+    log(f"ragged decode step {w} lens={lens[:8]}")
+    case = Case(w, seed=13, kv_cap=w.kv_len + 100)
+    b, hq, hkv, d, bs = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size
+    shape = qsa.shape_for(case.q, case.k, bs, w.top_k, keep_tail=w.keep_tail)
+    one = qsa.make_shape(1, hq, hkv, d, bs, w.top_k, case.q.dtype, keep_tail=w.keep_tail)
+    nbc = case.kv_cap // bs
+    k_comp = torch.full((b, hkv, nbc, d), float("nan"), device="cuda")
+    k_ref = torch.full((b, hkv, nbc, d), float("nan"), device="cuda")
+    for bb, n in enumerate(lens):  # the blocks closed before each sequence's new token
+        qsa.qsa_compress_keys(one, case.k[bb:bb + 1], n - 1, k_comp[bb:bb + 1])
+        qsa.qsa_compress_keys(one, case.k[bb:bb + 1], n, k_ref[bb:bb + 1])
+    q = case.q.view(b, hq, d)
+    kv_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sel = torch.empty(b, hkv, w.top_k, dtype=torch.int32, device="cuda")
+    scores = torch.empty(b, hkv, w.top_k, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    qsa.qsa_decode_step_ragged(shape, q, case.k, case.v, k_comp, kv_lens, w.kv_len, sel, out, sel_scores=scores)
+    torch.cuda.synchronize()
+    sel_h, out_h, sc_h = sel.cpu().numpy(), from_device(out), scores.cpu().numpy()
+    for bb, n in enumerate(lens):
+        nb = n // bs
+        assert torch.equal(k_comp[bb, :, :nb], k_ref[bb, :, :nb]), f"sequence {bb}: compressed keys"
+        rows = [(bb, 0, g) for g in range(hkv)]
+        st = check_rows(case, sel_h[:, None], out_h[:, None], rows, n - 1, scores_gpu=sc_h[:, None])
+        if bb < 8 or bb == b - 1:
+            log(f"  seq {bb} len {n}: {st}")
+    # the same sequences one at a time through the plain step
+    k_one = k_ref.clone()
+    for bb, n in list(enumerate(lens))[:: max(1, len(lens) // 6)]:
+        k_one[bb:bb + 1].copy_(k_comp[bb:bb + 1])
+        s1 = torch.empty(1, hkv, w.top_k, dtype=torch.int32, device="cuda")
+        o1 = torch.empty(1, hq, d, dtype=q.dtype, device="cuda")
+        qsa.qsa_decode_step(one, q[bb:bb + 1], case.k[bb:bb + 1], case.v[bb:bb + 1], k_one[bb:bb + 1], n, s1, o1)
+        torch.cuda.synchronize()
+        if not (w.keep_tail and n % bs == 0):
+            assert torch.equal(s1[0], sel[bb]), f"sequence {bb}: selection differs from the single-sequence step"
+        err = (o1[0].float() - out[bb].float()).abs().max().item()
+        assert err <= 2e-2, f"sequence {bb}: output differs from the single-sequence step by {err}"
+

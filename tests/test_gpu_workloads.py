@@ -4,7 +4,8 @@ configuration the benchmark times (plans depend only on the shapes).
 Selections are checked row by row wherever the oracle can afford it (every
 row of the 32K, 8K, 1M and 256K ratio-4 workloads; sampled rows of the 64 x 128K batch,
 plus the planted-block property on all of its rows). Outputs are compared on
-every row of the decode workloads and on sampled rows of the prefill.
+every row of the decode workloads and on sampled rows of the prefill; the ragged
+batch is checked on six sampled sequences at their own lengths.
 """
 from __future__ import annotations
 
@@ -92,3 +93,38 @@ def test_batched_decode_planted_workload():
     sc_s = scores.cpu().numpy()[sub_b][:, None]
     st = check_rows(sub, sel_s, out_s, [(idx[b], 0, g) for b, g in sample], w.kv_len - 1, scores_gpu=sc_s)
     log(f"  sampled rows: {st}")
+
+
+def test_ragged_batched_decode_workload():
+    """The ragged batch (64 sequences of 16K .. 128K tokens) as the benchmark runs it: one ragged step call."""
+    w = S.WORKLOADS["decode_b64_ragged"]
+    lens = S.seq_lengths(w, 0)
+    log(f"workload decode_b64_ragged: generating 2 x 4 GiB (lengths {min(lens)} .. {max(lens)})")
+    case = Case(w, seed=0)
+    log("workload decode_b64_ragged: running")
+    hq, hkv, d, bs = w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size
+    shape = qsa.shape_for(case.q, case.k, bs, w.top_k)
+    one = qsa.make_shape(1, hq, hkv, d, bs, w.top_k, case.q.dtype)
+    k_comp = torch.empty(w.batch, hkv, w.kv_len // bs, d, device="cuda")
+    for b, n in enumerate(lens):
+        qsa.qsa_compress_keys(one, case.k[b:b + 1], n - 1, k_comp[b:b + 1])
+    q = case.q.view(w.batch, hq, d)
+    kv_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sel = torch.empty(w.batch, hkv, w.top_k, dtype=torch.int32, device="cuda")
+    scores = torch.empty(w.batch, hkv, w.top_k, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    qsa.qsa_decode_step_ragged(shape, q, case.k, case.v, k_comp, kv_lens, w.kv_len, sel, out, sel_scores=scores)
+    torch.cuda.synchronize()
+    sel_h, out_h, sc_h = sel.cpu().numpy(), from_device(out), scores.cpu().numpy()
+    # sampled sequences: the shortest, the longest and a spread in between
+    order = np.argsort(lens)
+    pick = sorted({int(order[0]), int(order[-1]), *[int(order[i]) for i in (10, 25, 40, 55)]})
+    case.K, case.V, case.Q = case.K[pick], case.V[pick], case.Q[pick]
+    sub = Case.__new__(Case)
+    sub.__dict__.update(case.__dict__)
+    sub.w = w.replace(batch=len(pick), ragged=False)
+    sub._kc = None
+    for i, b in enumerate(pick):
+        st = check_rows(sub, sel_h[pick][:, None], out_h[pick][:, None], [(i, 0, g) for g in range(hkv)], lens[b] - 1,
+                        scores_gpu=sc_h[pick][:, None])
+        log(f"  sequence {b} (length {lens[b]}): {st}")
