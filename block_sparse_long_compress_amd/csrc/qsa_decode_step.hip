@@ -278,18 +278,18 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged) {
   const int64_t row_bytes = max_candidates(s, kv_len) * s.d * 4;
   if (row_bytes > (512 << 10) && rows < 64 && !ragged) return p;
   p.fused = true;
-  // Few rows: slices of the selection that give each wave about one 32-key
-  // unit, as long as the grid stays small (every slice repeats the scan).
-  const int upb = s.bs / kUnit;
+  // Few rows: slices of the selection down to one block per workgroup, as
+  // long as the grid stays within 256 workgroups. Every slice repeats the
+  // (L2-resident) scan; more, shorter slices still measured faster at 32K
+  // positions (1, 2, 4, 8, 16 slices per row: 24.1, 22.3, 18.4, 17.3,
+  // 17.1 us per step), since the attention's latency chain shortens.
   p.blocks_per_wg = s.top_k;
   p.n_split = 1;
   if (rows <= 32) {
-    const int bpw = (kStepWaves + upb - 1) / upb;
-    const int n = (s.top_k + bpw - 1) / bpw;
     const int cap = (int)(256 / rows);
-    if (n > 1 && cap > 1) {
-      p.n_split = n < cap ? n : cap;
-      p.blocks_per_wg = (s.top_k + p.n_split - 1) / p.n_split;
+    const int n = s.top_k < cap ? s.top_k : cap;
+    if (n > 1) {
+      p.blocks_per_wg = (s.top_k + n - 1) / n;
       p.n_split = (s.top_k + p.blocks_per_wg - 1) / p.blocks_per_wg;
     }
   }
