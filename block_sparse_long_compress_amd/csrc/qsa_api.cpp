@@ -224,7 +224,7 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
   if (sp.fused) {
-    if ((int64_t)s.batch * s.hkv * sp.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+    if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
     if (sp.ws_bytes > 0 && (!ws || ws_bytes < sp.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
     return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, hs));
   }
@@ -272,7 +272,7 @@ qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const v
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
   const qsa::StepPlan sp = qsa::plan_decode_step(s, max_kv_len, true);
   if (!sp.fused) return QSA_ERR_UNSUPPORTED;  // only the fused kernel reads per-sequence lengths
-  if ((int64_t)s.batch * s.hkv * sp.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   if (sp.ws_bytes > 0 && (!ws || ws_bytes < sp.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
   return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, max_kv_len, kv_cap, sel, sel_scores, out, ws,
                                             static_cast<hipStream_t>(stream), kv_lens));

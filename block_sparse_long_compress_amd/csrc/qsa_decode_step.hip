@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
     float* __restrict__ k_comp, int32_t* __restrict__ sel, float* __restrict__ sel_scores, uint16_t* __restrict__ out,
     float* __restrict__ part, uint32_t* __restrict__ counters, const int32_t* __restrict__ kv_lens,
     int64_t kv_len_max, int64_t kv_cap, int hq, int hkv, int G, int top_k, float scale, int keep_tail, int bpw,
-    int n_split) {
+    int n_split, int64_t n_rows) {
   using SM = StepSmem<D>;
   constexpr int LPR = D / 4;  // lanes covering one compressed key row (float32)
   constexpr int DT = D / 16;
@@ -53,8 +53,20 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   __shared__ int ids[kWave];
   __shared__ int last_wg;
 
-  const int64_t row = blockIdx.x / n_split;
-  const int split = (int)(blockIdx.x % n_split);
+  // Several slices per row: all slices of a row on one XCD (workgroups go
+  // to the 8 XCDs round-robin), so that they share its L2 copy of the row's
+  // compressed keys; grid slots past the last row exit at once.
+  int64_t row;
+  int split;
+  if (n_split > 1) {
+    const int64_t slot = blockIdx.x / 8;
+    row = (int64_t)(blockIdx.x % 8) + 8 * (slot / n_split);
+    split = (int)(slot % n_split);
+    if (row >= n_rows) return;
+  } else {
+    row = blockIdx.x;
+    split = 0;
+  }
   const int64_t b = row / hkv;
   const int g = (int)(row % hkv);
   const int lane = lane_id(), w = wave_id();
@@ -235,7 +247,8 @@ hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, con
                          float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out,
                          void* ws, const int32_t* kv_lens, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
-  const dim3 grid((unsigned)(rows * plan.n_split)), block(kStepWaves * kWave);
+  const int64_t n_wg = plan.n_split > 1 ? 8 * ((rows + 7) / 8) * plan.n_split : rows;
+  const dim3 grid((unsigned)n_wg), block(kStepWaves * kWave);
   uint32_t* counters = static_cast<uint32_t*>(ws);
   float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows)) : nullptr;
   const auto* qp = static_cast<const uint16_t*>(q);
@@ -246,17 +259,17 @@ hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, con
     case 32:
       hipLaunchKernelGGL((decode_step_kernel<D, 32>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
                          part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
-                         s.keep_tail, plan.blocks_per_wg, plan.n_split);
+                         s.keep_tail, plan.blocks_per_wg, plan.n_split, rows);
       break;
     case 64:
       hipLaunchKernelGGL((decode_step_kernel<D, 64>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
                          part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
-                         s.keep_tail, plan.blocks_per_wg, plan.n_split);
+                         s.keep_tail, plan.blocks_per_wg, plan.n_split, rows);
       break;
     case 128:
       hipLaunchKernelGGL((decode_step_kernel<D, 128>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
                          part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
-                         s.keep_tail, plan.blocks_per_wg, plan.n_split);
+                         s.keep_tail, plan.blocks_per_wg, plan.n_split, rows);
       break;
     default:
       return hipErrorInvalidValue;
