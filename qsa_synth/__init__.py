@@ -34,7 +34,7 @@ from concurrent.futures import ProcessPoolExecutor
 
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_PLANT, TENSOR_LEN = 0, 1, 2, 3, 4
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_PLANT, TENSOR_LEN, TENSOR_WQ, TENSOR_WK = 0, 1, 2, 3, 4, 5, 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -131,6 +131,15 @@ def seq_lengths(w: Workload, seed: int) -> list[int]:
     n = _rng(seed, w.cfg_id, TENSOR_LEN).integers(lo, w.kv_len + 1, size=w.batch)
     n[-1] = w.kv_len
     return [int(x) for x in n]
+
+
+def indexer_weights(seed: int, cfg_id: int, d: int, d_idx: int) -> tuple[np.ndarray, np.ndarray]:
+    """Synthetic indexer projections ``(W_q, W_k)``, each ``[d][d_idx]`` float32: standard normals
+    divided by ``sqrt(d)`` (tensor ids 5 and 6), so projected values keep the inputs' scale."""
+    s = np.float32(1.0 / np.sqrt(d))
+    w_q = _rng(seed, cfg_id, TENSOR_WQ).standard_normal((d, d_idx), dtype=np.float32) * s
+    w_k = _rng(seed, cfg_id, TENSOR_WK).standard_normal((d, d_idx), dtype=np.float32) * s
+    return w_q, w_k
 
 
 def planted_blocks(w: Workload, seed: int, b: int, g: int) -> np.ndarray:
