@@ -100,8 +100,15 @@ def work_model(w, n_new_blocks: int, lens=None):
         cand = frame(p, bs, w.keep_tail)[0]
         rows = b * hkv
         m["compress"] = {"bytes": rows * n_new_blocks * (bs * d * el + d * 4), "flops": 0}
-        m["select"] = {"bytes": rows * cand * d * 4 + b * hq * d * el + rows * k * 4,
-                       "flops": 2 * d * rows * cand}
+        if w.indexer_dim:
+            di, G = w.indexer_dim, hq // hkv
+            m["index_keys"] = {"bytes": rows * n_new_blocks * (d + di) * 4 + d * di * 4,
+                               "flops": 2 * d * di * rows * n_new_blocks}
+            m["select"] = {"bytes": rows * cand * di * 4 + b * hq * d * el + d * di * 4 + rows * k * 4,
+                           "flops": rows * (2 * G * d * di + 2 * G * di * cand)}
+        else:
+            m["select"] = {"bytes": rows * cand * d * 4 + b * hq * d * el + rows * k * 4,
+                           "flops": 2 * d * rows * cand}
         vis = visible_keys(p, bs, k, w.keep_tail)
         m["attend"] = {"bytes": rows * vis * d * el * 2 + 2 * b * hq * d * el + rows * k * 4,
                        "flops": 4 * d * hq * b * vis}
@@ -163,6 +170,18 @@ class Step:
                     qsa.qsa_compress_keys(one, self.k[bb:bb + 1], n - 1, self.k_comp[bb:bb + 1])
                 self.blk_begin = 0
                 self.n_new_blocks = sum(1 for n in self.lens if n % bs == 0)
+            elif w.indexer_dim:
+                # learned-indexer selection: the separate calls (compress and project the closed block,
+                # indexer select, decode attention)
+                self.ws_step = None
+                w_q, w_k = S.indexer_weights(seed, w.cfg_id, d, w.indexer_dim)
+                self.w_q, self.w_k = torch.from_numpy(w_q).cuda(), torch.from_numpy(w_k).cuda()
+                self.ix = qsa.make_indexer(w.indexer_dim, w.indexer_agg)
+                self.k_idx = torch.empty(b, hkv, cap // bs, w.indexer_dim, dtype=torch.float32, device="cuda")
+                qsa.qsa_compress_keys(self.shape, self.k, w.kv_len - 1, self.k_comp)
+                qsa.qsa_indexer_keys(self.shape, self.ix, self.w_k, self.k_comp, w.kv_len - 1, cap, self.k_idx)
+                self.blk_begin = (w.kv_len - 1) // bs
+                self.n_new_blocks = w.kv_len // bs - self.blk_begin
             else:
                 self.ws_step = self._ws(qsa.QSA_OP_DECODE_STEP, 1, w.kv_len)
                 self.fused = qsa.qsa_decode_step_fused(self.shape, w.kv_len)
@@ -181,7 +200,9 @@ class Step:
         self.calls = [("select", self.select), ("attend", self.attend)]
         if self.n_new_blocks > 0:
             self.calls.insert(0, ("compress", self.compress))
-        self.step_calls = [("step", self.decode_step)] if w.mode == "decode" else self.calls
+        if self.n_new_blocks > 0 and w.indexer_dim:
+            self.calls.insert(1, ("index_keys", self.index_keys))
+        self.step_calls = [("step", self.decode_step)] if w.mode == "decode" and not w.indexer_dim else self.calls
         if self.fused:
             self.calls = self.step_calls
 
@@ -201,8 +222,17 @@ class Step:
     def compress(self):
         self.qsa.qsa_compress_keys(self.shape, self.k, self.w.kv_len, self.k_comp, block_begin=self.blk_begin)
 
+    def index_keys(self):
+        w = self.w
+        self.qsa.qsa_indexer_keys(self.shape, self.ix, self.w_k, self.k_comp, w.kv_len, w.kv_len, self.k_idx,
+                                  block_begin=self.blk_begin)
+
     def select(self):
         w = self.w
+        if w.indexer_dim:
+            self.qsa.qsa_indexer_select(self.shape, self.ix, self.w_q, self.q, w.q_pos0, self.k_idx, w.kv_len,
+                                        w.kv_len, self.sel)
+            return
         self.qsa.qsa_score_select(self.shape, self.q, w.q_pos0, self.k_comp, w.kv_len, w.kv_len, self.sel,
                                   ws=self.ws_sel)
 
@@ -339,16 +369,26 @@ def cpu_baseline(w, seed, budget_s):
             n0 = S.seq_lengths(w, seed)[0]  # sequence 0's length (all kv_len unless ragged)
             p = n0 - 1
             n_prev = p // bs  # blocks complete before the new token
-            kc = np.zeros((w.n_kv_heads, w.kv_len // bs, w.head_dim))
-            kc[:, :n_prev] = O.compress_keys(K[:, : n_prev * bs], bs)
+            kc = np.zeros((w.n_kv_heads, w.kv_len // bs, w.indexer_dim or w.head_dim))
+            if w.indexer_dim:
+                from oracle import qsa_indexer as IX
+                w_q, w_k = (x.astype(np.float64) for x in S.indexer_weights(seed, w.cfg_id, w.head_dim, w.indexer_dim))
+                iscale = IX.default_indexer_scale(w.indexer_dim)
+                kc[:, :n_prev] = IX.indexer_keys(K[:, : n_prev * bs], w_k, bs)
+            else:
+                kc[:, :n_prev] = O.compress_keys(K[:, : n_prev * bs], bs)
             n_cand, forced = O.selection_frame(p, bs, w.keep_tail)
             n_steps, t0 = 0, time.perf_counter()
             while True:
                 if (p + 1) % bs == 0:  # the new token completes its block
-                    kc[:, n_prev:n_prev + 1] = O.compress_keys(K[:, n_prev * bs:(n_prev + 1) * bs], bs)
+                    blk = K[:, n_prev * bs:(n_prev + 1) * bs]
+                    kc[:, n_prev:n_prev + 1] = IX.indexer_keys(blk, w_k, bs) if w.indexer_dim else O.compress_keys(blk, bs)
                 for g in range(w.n_kv_heads):
                     qg = q[0, g * G:(g + 1) * G].astype(np.float64)
-                    sc = O.block_scores(qg, kc[g], n_cand, scale)
+                    if w.indexer_dim:
+                        sc = IX.indexer_scores(qg, w_q, kc[g], n_cand, iscale, w.indexer_agg)
+                    else:
+                        sc = O.block_scores(qg, kc[g], n_cand, scale)
                     sel = O.select_in_frame(sc, n_cand, forced, k)
                     O.attend_given_selection(qg, K[g], V[g], sel, p, bs, scale)
                 n_steps += 1
@@ -466,6 +506,8 @@ def main():
                    "block_size": w.block_size, "top_k": w.top_k, "keep_tail": w.keep_tail, "seed": args.seed,
                    "graphs": not args.no_graph, "graph_steps": 1 if args.no_graph else max(1, args.graph_steps),
                    "fused_decode_step": st.fused, "ragged": w.ragged,
+                   **({"indexer_dim": w.indexer_dim, "indexer_agg": ["sum", "max", "softmax"][w.indexer_agg]}
+                      if w.indexer_dim else {}),
                    **({"mean_kv_len": round(float(np.mean(st.lens)), 1), "min_kv_len": int(min(st.lens))}
                       if w.ragged else {})},
         "roofline": {"bound": bound,

@@ -15,6 +15,9 @@ from .binding import (  # noqa: F401
     EXPORTED,
     LIB,
     LIB_PATH,
+    QSA_AGG_MAX,
+    QSA_AGG_SOFTMAX,
+    QSA_AGG_SUM,
     QSA_BF16,
     QSA_F32,
     QSA_OP_COMPRESS,
@@ -24,13 +27,17 @@ from .binding import (  # noqa: F401
     QSA_OP_PREFILL,
     QSA_OP_SELECT,
     QsaError,
+    QsaIndexer,
     QsaShape,
     abi_version,
+    make_indexer,
     make_shape,
     qsa_compress_keys,
     qsa_decode_step,
     qsa_decode_step_fused,
     qsa_decode_step_ragged,
+    qsa_indexer_keys,
+    qsa_indexer_select,
     qsa_score_select,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_prefill,

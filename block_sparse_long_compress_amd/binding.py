@@ -20,10 +20,11 @@ LIB_PATH = os.environ.get("QSA_LIB", os.path.join(HERE, "lib", "libqsa.so"))
 QSA_F32, QSA_BF16 = 0, 1
 QSA_OP_COMPRESS, QSA_OP_SELECT, QSA_OP_DECODE, QSA_OP_PREFILL, QSA_OP_DECODE_STEP = 0, 1, 2, 3, 4
 QSA_OP_DECODE_STEP_RAGGED = 5
+QSA_AGG_SUM, QSA_AGG_MAX, QSA_AGG_SOFTMAX = 0, 1, 2
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_ERR_WORKSPACE", 4: "QSA_ERR_HIP"}
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
             "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused",
-            "qsa_decode_step_ragged")
+            "qsa_decode_step_ragged", "qsa_indexer_keys", "qsa_indexer_select")
 
 
 class QsaError(RuntimeError):
@@ -44,6 +45,10 @@ class QsaShape(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("keep_tail", ctypes.c_int32),
     ]
+
+
+class QsaIndexer(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("agg", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 def _load() -> ctypes.CDLL:
@@ -73,6 +78,11 @@ def _load() -> ctypes.CDLL:
     lib.qsa_decode_step_fused.argtypes = [SH, I64]
     lib.qsa_decode_step_ragged.restype = ctypes.c_int
     lib.qsa_decode_step_ragged.argtypes = [SH, P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
+    IX = ctypes.POINTER(QsaIndexer)
+    lib.qsa_indexer_keys.restype = ctypes.c_int
+    lib.qsa_indexer_keys.argtypes = [SH, IX, P, P, I64, I64, I64, P, P]
+    lib.qsa_indexer_select.restype = ctypes.c_int
+    lib.qsa_indexer_select.argtypes = [SH, IX, P, P, I64, I64, P, I64, I64, P, P, P]
     return lib
 
 
@@ -208,3 +218,27 @@ def qsa_decode_step_fused(shape: QsaShape, kv_len: int) -> bool:
     if r < 0:
         raise QsaError(1, "qsa_decode_step_fused")
     return bool(r)
+
+
+def make_indexer(dim: int, agg: int, scale: float = 0.0) -> QsaIndexer:
+    """Indexer struct: dimension (64 or 128), QSA_AGG_* aggregation, scale (0 = 1/sqrt(dim))."""
+    return QsaIndexer(dim, agg, float(scale))
+
+
+def qsa_indexer_keys(shape: QsaShape, idx: QsaIndexer, w_k, k_comp, kv_len: int, kv_cap: int, k_idx,
+                     block_begin: int = 0, stream=None):
+    """Indexer keys of complete blocks ``block_begin .. kv_len//Bs - 1`` (``W_k^T`` times the compressed keys)."""
+    _check(LIB.qsa_indexer_keys(ctypes.byref(shape), ctypes.byref(idx), _ptr(w_k), _ptr(k_comp), kv_len, kv_cap,
+                                block_begin, _ptr(k_idx), _stream(k_comp, stream)),
+           "qsa_indexer_keys")
+    return k_idx
+
+
+def qsa_indexer_select(shape: QsaShape, idx: QsaIndexer, w_q, q, q_pos0: int, k_idx, kv_len: int, kv_cap: int, sel,
+                       sel_scores=None, stream=None):
+    """Selection scored in indexer space for ``q`` ``[b][q_len][Hq][d]`` rows at positions ``q_pos0 ..``."""
+    q_len = q.shape[1]
+    _check(LIB.qsa_indexer_select(ctypes.byref(shape), ctypes.byref(idx), _ptr(w_q), _ptr(q), q_len, q_pos0,
+                                  _ptr(k_idx), kv_len, kv_cap, _ptr(sel), _ptr(sel_scores), _stream(q, stream)),
+           "qsa_indexer_select")
+    return sel

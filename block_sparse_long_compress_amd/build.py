@@ -26,6 +26,7 @@ SOURCES = [
     "qsa_attn_prefill.hip",
     "qsa_attn_f32.hip",
     "qsa_decode_step.hip",
+    "qsa_indexer.hip",
 ]
 
 ARCH = "gfx950"

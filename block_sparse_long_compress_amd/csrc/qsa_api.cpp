@@ -278,4 +278,57 @@ qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const v
                                             static_cast<hipStream_t>(stream), kv_lens));
 }
 
+namespace {
+qsa_status check_indexer(const qsa_indexer* idx, const Dims& s, qsa::IndexerDims* out) {
+  if (!idx) return QSA_ERR_INVALID;
+  if (idx->dim != 64 && idx->dim != 128) return QSA_ERR_INVALID;
+  if (idx->agg < QSA_AGG_SUM || idx->agg > QSA_AGG_SOFTMAX) return QSA_ERR_INVALID;
+  if (!std::isfinite(idx->scale) || idx->scale < 0.f) return QSA_ERR_INVALID;
+  (void)s;
+  out->dim = idx->dim;
+  out->agg = idx->agg;
+  out->scale = idx->scale == 0.f ? (float)(1.0 / std::sqrt((double)idx->dim)) : idx->scale;
+  return QSA_OK;
+}
+}  // namespace
+
+qsa_status qsa_indexer_keys(const qsa_shape* shape, const qsa_indexer* idx, const float* w_k,
+                            const float* k_comp, int64_t kv_len, int64_t kv_cap, int64_t block_begin,
+                            float* k_idx, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  qsa::IndexerDims ix;
+  st = check_indexer(idx, s, &ix);
+  if (st != QSA_OK) return st;
+  if (kv_len < 0 || kv_cap <= 0 || kv_len > kv_cap || block_begin < 0) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  const int64_t blk_end = kv_len / s.bs;
+  if (block_begin >= blk_end) return QSA_OK;  // no complete block in range
+  if (!w_k || !k_comp || !k_idx || !aligned16(w_k) || !aligned16(k_comp) || !aligned16(k_idx))
+    return QSA_ERR_INVALID;
+  return hip_status(qsa::launch_indexer_keys(s, ix, w_k, k_comp, kv_cap, block_begin, blk_end, k_idx,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, const float* w_q, const void* q,
+                              int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_len, int64_t kv_cap,
+                              int32_t* sel, float* sel_scores, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  qsa::IndexerDims ix;
+  st = check_indexer(idx, s, &ix);
+  if (st != QSA_OK) return st;
+  if (q_len <= 0 || q_pos0 < 0 || kv_len != q_pos0 + q_len || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
+  if (!w_q || !q || !sel || !aligned16(w_q) || !aligned16(q) || !aligned16(sel)) return QSA_ERR_INVALID;
+  if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  if (s.top_k > 64) return QSA_ERR_UNSUPPORTED;
+  if ((int64_t)s.batch * q_len * s.hkv > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (qsa::max_candidates(s, kv_len) > 0 && (!k_idx || !aligned16(k_idx))) return QSA_ERR_INVALID;
+  return hip_status(qsa::launch_indexer_select(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,294 @@
+// Learned-indexer selection: block selection scored in a separate, lower-
+// dimensional indexer space ("Qwen4 in llama.cpp: Dissecting PR #27742",
+// section "QSA Is an Address-Selection Problem, Not a New Attention
+// Equation": indexer projections feed the compressed-block representation,
+// which is scored to pick the kept blocks).
+//
+// Indexer keys: the compressed attention keys projected by W_k ([d][dim],
+// shared by all heads); projecting a block's mean equals averaging its
+// projected keys. Indexer scores: every query head of a KV head's group is
+// projected by W_q and scored against each candidate's indexer key, and the
+// heads' scores are aggregated (sum, max, or each head's softmax over the
+// candidates summed over the heads). Selection frame, forced block and
+// output format are those of the default selection.
+//
+// Both kernels stream small, L2-resident data; they favour plain fixed-order
+// float32 arithmetic (deterministic) over peak rate.
+#include "qsa_device.h"
+#include "qsa_internal.h"
+#include "qsa_select_wave.h"
+
+namespace qsa {
+namespace {
+
+// One wave per (sequence, KV head, block): k_idx = W_k^T k_comp, the sum
+// over the d inputs in ascending order. W_k is staged in LDS once per
+// workgroup (16-byte loads, all in flight together); lane l holds the
+// compressed key's elements l, l + 64 (d = 128), each broadcast from its
+// lane in turn.
+template <int D, int DI>
+__global__ __launch_bounds__(256) void indexer_keys_kernel(const float* __restrict__ k_comp,
+                                                           const float* __restrict__ w_k, float* __restrict__ k_idx,
+                                                           int64_t nb_cap, int64_t blk_begin, int64_t n_blk,
+                                                           int64_t n_items) {
+  constexpr int EPL = DI / kWave;  // outputs per lane
+  constexpr int IPL = D / kWave;   // inputs per lane
+  __shared__ __align__(16) float wk_s[D * DI];
+  {
+    constexpr int NW4 = D * DI / 4 / 256;
+    f32x4_t wv[NW4];
+#pragma unroll
+    for (int i = 0; i < NW4; ++i) wv[i] = *reinterpret_cast<const f32x4_t*>(w_k + 4 * (threadIdx.x + 256 * i));
+#pragma unroll
+    for (int i = 0; i < NW4; ++i) *reinterpret_cast<f32x4_t*>(&wk_s[4 * (threadIdx.x + 256 * i)]) = wv[i];
+  }
+  __syncthreads();
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave_id();
+  if (item >= n_items) return;
+  const int64_t bg = item / n_blk;
+  const int64_t c = blk_begin + item % n_blk;
+  const int lane = lane_id();
+  const float* src = k_comp + (bg * nb_cap + c) * D;
+  float x[IPL];
+#pragma unroll
+  for (int i = 0; i < IPL; ++i) x[i] = src[lane + kWave * i];
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < IPL; ++i) {
+#pragma unroll 8
+    for (int j = 0; j < kWave; ++j) {
+      const float kj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[i]), j));
+      const float* wr = wk_s + (kWave * i + j) * DI + lane;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(kj, wr[kWave * e], acc[e]);
+    }
+  }
+  float* dst = k_idx + (bg * nb_cap + c) * DI + lane;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[kWave * e] = acc[e];
+}
+
+constexpr int kIdxThreads = 256;
+constexpr int kIdxWaves = kIdxThreads / kWave;
+
+// One workgroup per (sequence, query row, KV head).
+// 1. the G query heads are projected into LDS (already scaled);
+// 2. each thread scores its candidates c = tid, tid + 256, ...: the G head
+//    scores of the candidate (its indexer key read as float4s), aggregated;
+//    with the softmax aggregation a first pass finds every head's maximum
+//    and normaliser over the row's candidates and a second pass scores;
+// 3. per-wave top lists, merged, and the row's selection written as the
+//    default selection writes it.
+template <typename T, int D, int DI, int AGG>
+__global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
+    const T* __restrict__ q, const float* __restrict__ w_q, const float* __restrict__ k_idx,
+    int32_t* __restrict__ sel, float* __restrict__ sel_scores, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
+    int hkv, int G, int bs, int top_k, float scale, int keep_tail) {
+  __shared__ __align__(16) float qi[16 * DI];
+  __shared__ __align__(16) float wq_s[D * DI];  // W_q, staged once per workgroup
+  __shared__ __align__(16) float qs[16 * D];    // the group's query heads, as float
+  __shared__ uint64_t lists[kIdxWaves][kWave];
+  __shared__ float red_m[kIdxWaves][16], red_z[kIdxWaves][16];
+  __shared__ float head_m[16], head_z[16];
+
+  const int64_t row = blockIdx.x;
+  const int g = (int)(row % hkv);
+  const int64_t bt = row / hkv;
+  const int64_t t = bt % q_len;
+  const int64_t b = bt / q_len;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int64_t p = q_pos0 + t;
+  const Frame fr = row_frame(p, bs, keep_tail);
+  const int slots = frame_slots(fr, top_k);
+
+  // 1. projected, scaled query heads: W_q and the heads staged in LDS with
+  // 16-byte loads (all issued before the first store), then one output per
+  // thread and step, the d terms summed in ascending order
+  const T* qh = q + ((b * q_len + t) * hq + (int64_t)g * G) * D;
+  {
+    constexpr int NW4 = D * DI / 4 / kIdxThreads;  // float4s of W_q per thread
+    f32x4_t wv[NW4];
+#pragma unroll
+    for (int i = 0; i < NW4; ++i) wv[i] = *reinterpret_cast<const f32x4_t*>(w_q + 4 * (tid + kIdxThreads * i));
+    for (int i = tid; i < G * D / 4; i += kIdxThreads)
+      *reinterpret_cast<f32x4_t*>(&qs[4 * i]) = load4_f32(qh + 4 * i);
+#pragma unroll
+    for (int i = 0; i < NW4; ++i) *reinterpret_cast<f32x4_t*>(&wq_s[4 * (tid + kIdxThreads * i)]) = wv[i];
+  }
+  __syncthreads();
+  for (int o = tid; o < G * DI; o += kIdxThreads) {
+    const int h = o / DI, e = o % DI;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < D; ++j) acc = __builtin_fmaf(qs[h * D + j], wq_s[j * DI + e], acc);
+    qi[o] = acc * scale;
+  }
+  __syncthreads();
+
+  const float* krow = k_idx + ((b * hkv + g) * nb_cap) * DI;
+  // head scores of candidate c into s[0 .. G-1]
+  auto head_scores = [&](int c, float (&s)[16]) {
+    f32x4_t kv[DI / 4];
+#pragma unroll
+    for (int e4 = 0; e4 < DI / 4; ++e4) kv[e4] = *reinterpret_cast<const f32x4_t*>(krow + (int64_t)c * DI + 4 * e4);
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e4 = 0; e4 < DI / 4; ++e4) {
+        const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(&qi[h * DI + 4 * e4]);
+        acc = __builtin_fmaf(qv[0], kv[e4][0], acc);
+        acc = __builtin_fmaf(qv[1], kv[e4][1], acc);
+        acc = __builtin_fmaf(qv[2], kv[e4][2], acc);
+        acc = __builtin_fmaf(qv[3], kv[e4][3], acc);
+      }
+      s[h] = acc;
+    }
+  };
+
+  if constexpr (AGG == kAggSoftmax) {
+    // pass 1: every head's maximum and normaliser over the candidates
+    float m[16], z[16];
+    for (int h = 0; h < 16; ++h) {
+      m[h] = -__builtin_inff();
+      z[h] = 0.f;
+    }
+    for (int c = tid; c < fr.n_cand; c += kIdxThreads) {
+      float s[16];
+      head_scores(c, s);
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], s[h]);
+        z[h] = z[h] * __expf(m[h] - mn) + __expf(s[h] - mn);
+        m[h] = mn;
+      }
+    }
+    for (int h = 0; h < G; ++h) {
+      float mh = m[h], zh = z[h];
+      for (int d = 1; d < kWave; d <<= 1) {
+        const float mo = __shfl_xor(mh, d, kWave), zo = __shfl_xor(zh, d, kWave);
+        const float mn = fmaxf(mh, mo);
+        zh = (mn == -__builtin_inff()) ? 0.f : zh * __expf(mh - mn) + zo * __expf(mo - mn);
+        mh = mn;
+      }
+      if (lane == 0) {
+        red_m[w][h] = mh;
+        red_z[w][h] = zh;
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float mh = -__builtin_inff(), zh = 0.f;
+      for (int ww = 0; ww < kIdxWaves; ++ww) {
+        const float mo = red_m[ww][tid], zo = red_z[ww][tid];
+        const float mn = fmaxf(mh, mo);
+        zh = (mn == -__builtin_inff()) ? 0.f : zh * __expf(mh - mn) + zo * __expf(mo - mn);
+        mh = mn;
+      }
+      head_m[tid] = mh;
+      head_z[tid] = zh;
+    }
+    __syncthreads();
+  }
+
+  // 2. aggregated scores, folded into each wave's top list (a wave's lanes
+  // cover 64 consecutive candidates per round)
+  uint64_t cur = 0ull;
+  if (slots > 0) {
+    for (int base = kWave * w; base < fr.n_cand; base += kIdxThreads) {
+      const int c = base + lane;
+      uint64_t key = 0ull;
+      if (c < fr.n_cand) {
+        float s[16];
+        head_scores(c, s);
+        float a;
+        if constexpr (AGG == kAggSum) {
+          a = 0.f;
+          for (int h = 0; h < G; ++h) a += s[h];
+        } else if constexpr (AGG == kAggMax) {
+          a = s[0];
+          for (int h = 1; h < G; ++h) a = fmaxf(a, s[h]);
+        } else {
+          a = 0.f;
+          for (int h = 0; h < G; ++h) a += __expf(s[h] - head_m[h]) / head_z[h];
+        }
+        key = make_key(a, c);
+      }
+      cur = topk_fold(cur, key, slots);
+    }
+  }
+  cur = merge_wave_lists<kIdxWaves>(lists, cur, slots > 0 ? slots : 1);
+  if (w == 0) {
+    const int64_t off = row * top_k;
+    finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+  }
+}
+
+template <int D, int DI>
+hipError_t launch_keys(const float* w_k, const float* k_comp, int64_t nb_cap, int64_t blk_begin, int64_t n_blk,
+                       int64_t n_items, float* k_idx, hipStream_t st) {
+  hipLaunchKernelGGL((indexer_keys_kernel<D, DI>), dim3((unsigned)((n_items + 3) / 4)), dim3(256), 0, st, k_comp, w_k,
+                     k_idx, nb_cap, blk_begin, n_blk, n_items);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DI>
+hipError_t launch_select_t(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
+                           int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                           hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  const int64_t nb_cap = kv_cap / s.bs;
+  const T* qp = static_cast<const T*>(q);
+  const dim3 grid((unsigned)rows), block(kIdxThreads);
+  switch (ix.agg) {
+    case kAggSum:
+      hipLaunchKernelGGL((indexer_select_kernel<T, D, DI, kAggSum>), grid, block, 0, st, qp, w_q, k_idx, sel,
+                         sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
+      break;
+    case kAggMax:
+      hipLaunchKernelGGL((indexer_select_kernel<T, D, DI, kAggMax>), grid, block, 0, st, qp, w_q, k_idx, sel,
+                         sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
+      break;
+    default:
+      hipLaunchKernelGGL((indexer_select_kernel<T, D, DI, kAggSoftmax>), grid, block, 0, st, qp, w_q, k_idx, sel,
+                         sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_select_d(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
+                           int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                           hipStream_t st) {
+  if (s.d == 64)
+    return ix.dim == 64 ? launch_select_t<T, 64, 64>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st)
+                        : launch_select_t<T, 64, 128>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
+  return ix.dim == 64 ? launch_select_t<T, 128, 64>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st)
+                      : launch_select_t<T, 128, 128>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
+}
+
+}  // namespace
+
+hipError_t launch_indexer_keys(const Dims& s, const IndexerDims& ix, const float* w_k, const float* k_comp,
+                               int64_t kv_cap, int64_t blk_begin, int64_t blk_end, float* k_idx, hipStream_t st) {
+  const int64_t n_blk = blk_end - blk_begin;
+  if (n_blk <= 0) return hipSuccess;
+  const int64_t nb_cap = kv_cap / s.bs;
+  const int64_t n_items = (int64_t)s.batch * s.hkv * n_blk;
+  if (s.d == 64)
+    return ix.dim == 64 ? launch_keys<64, 64>(w_k, k_comp, nb_cap, blk_begin, n_blk, n_items, k_idx, st)
+                        : launch_keys<64, 128>(w_k, k_comp, nb_cap, blk_begin, n_blk, n_items, k_idx, st);
+  return ix.dim == 64 ? launch_keys<128, 64>(w_k, k_comp, nb_cap, blk_begin, n_blk, n_items, k_idx, st)
+                      : launch_keys<128, 128>(w_k, k_comp, nb_cap, blk_begin, n_blk, n_items, k_idx, st);
+}
+
+hipError_t launch_indexer_select(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q,
+                                 int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel,
+                                 float* sel_scores, hipStream_t st) {
+  if (s.dtype == 1)
+    return launch_select_d<uint16_t>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
+  return launch_select_d<float>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
+}
+
+}  // namespace qsa

@@ -14,6 +14,21 @@ struct Dims {
   int keep_tail;   // selection frame: 0 = own block kept, 1 = only the partial tail kept
 };
 
+// Learned-indexer variant of the selection: indexer dimension (64 or 128),
+// aggregation of the group's head scores, resolved scale (never 0).
+constexpr int kAggSum = 0, kAggMax = 1, kAggSoftmax = 2;
+struct IndexerDims {
+  int dim, agg;
+  float scale;
+};
+// Indexer keys of blocks [blk_begin, blk_end): W_k^T k_comp per block.
+hipError_t launch_indexer_keys(const Dims& s, const IndexerDims& ix, const float* w_k, const float* k_comp,
+                               int64_t kv_cap, int64_t blk_begin, int64_t blk_end, float* k_idx, hipStream_t st);
+// Selection of every (sequence, query row, KV head) scored in indexer space.
+hipError_t launch_indexer_select(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q,
+                                 int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel,
+                                 float* sel_scores, hipStream_t st);
+
 // Block compression, blocks [blk_begin, blk_end) of every (b, g).
 hipError_t launch_compress(const Dims& s, const void* k, int64_t kv_cap, int64_t blk_begin, int64_t blk_end,
                            float* k_comp, hipStream_t st);

@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 3
+#define QSA_ABI_VERSION 4
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -236,6 +236,54 @@ qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const v
                                   float* k_comp, const int32_t* kv_lens, int64_t max_kv_len, int64_t kv_cap,
                                   int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * Learned-indexer variant of the selection ("Qwen4 in llama.cpp: Dissecting
+ * PR #27742", section "QSA Is an Address-Selection Problem, Not a New
+ * Attention Equation": indexer projections feed the compressed-block
+ * representation that is scored to pick the kept blocks). The pages give
+ * neither the projections nor how a group's heads combine; this library's
+ * reading: keys and query heads are projected into an indexer space of
+ * `dim` dimensions by W_k and W_q (float32 [head_dim][dim], shared by all
+ * heads), a block's indexer key is the mean of its projected keys, each
+ * query head scores a candidate with scale * <q W_q, indexer key>, and the
+ * heads of a KV head's group combine by `agg`:
+ *   QSA_AGG_SUM      the sum of the head scores;
+ *   QSA_AGG_MAX      the largest head score;
+ *   QSA_AGG_SOFTMAX  each head's scores turned into a softmax over the row's
+ *                    candidates, summed over the heads.
+ * Frame, forced block, top_k, tie rule and output format are those of
+ * qsa_score_select. */
+enum { QSA_AGG_SUM = 0, QSA_AGG_MAX = 1, QSA_AGG_SOFTMAX = 2 };
+
+typedef struct {
+  int32_t dim;  /* indexer dimension: 64 or 128 */
+  int32_t agg;  /* QSA_AGG_* */
+  float scale;  /* score scale; 0 means 1/sqrt(dim) */
+} qsa_indexer;
+
+/* Indexer keys k_idx [b][Hkv][kv_cap/Bs][dim] (float32) of the complete
+ * blocks block_begin .. kv_len/Bs - 1: W_k^T times the block's compressed key
+ * (k_comp as written by qsa_compress_keys), which equals the mean of the
+ * block's projected keys. w_k: device float32 [head_dim][dim]. No workspace.
+ * Errors as qsa_compress_keys; QSA_ERR_INVALID also for a bad indexer
+ * struct (dim not 64 or 128, agg out of range, scale negative or not
+ * finite). */
+qsa_status qsa_indexer_keys(const qsa_shape* shape, const qsa_indexer* idx, const float* w_k,
+                            const float* k_comp, int64_t kv_len, int64_t kv_cap, int64_t block_begin,
+                            float* k_idx, void* stream);
+
+/* Selection scored in indexer space for query rows at positions q_pos0 ..
+ * q_pos0+q_len-1 (layouts and frame as qsa_score_select; kv_len must be
+ * q_pos0 + q_len). w_q: device float32 [head_dim][dim]; k_idx as written by
+ * qsa_indexer_keys for every block below the rows' own blocks (and, with
+ * keep_tail, the complete own block). sel_scores (optional) receives the
+ * aggregated score of every kept candidate (+inf for the forced block, -inf
+ * for padding). One workgroup per (sequence, row, KV head); no workspace.
+ * QSA_ERR_UNSUPPORTED for top_k > 64. */
+qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, const float* w_q, const void* q,
+                              int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_len, int64_t kv_cap,
+                              int32_t* sel, float* sel_scores, void* stream);
 
 #ifdef __cplusplus
 }

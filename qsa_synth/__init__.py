@@ -56,6 +56,8 @@ class Workload:
     planted: int = 0
     keep_tail: bool = False  # selection frame of the released budget (see the oracle)
     ragged: bool = False  # decode: every sequence has its own length (see seq_lengths)
+    indexer_dim: int = 0  # learned-indexer selection: indexer dimension (0 = the default selection)
+    indexer_agg: int = 0  # its aggregation of a group's head scores: 0 sum, 1 max, 2 softmax
 
     @property
     def q_len(self) -> int:
@@ -82,6 +84,9 @@ WORKLOADS = {
     "prefill_8k": Workload("prefill_8k", 3, "prefill", 1, 8192, 16, 2, 128, 64, 16, "bf16", 0.5),
     "decode_b64_128k": Workload("decode_b64_128k", 4, "decode", 64, 131072, 16, 2, 128, 64, 16, "bf16", 0.5, planted=8),
     "decode_1m": Workload("decode_1m", 5, "decode", 1, 1048576, 16, 2, 128, 64, 32, "bf16", 0.5),
+    # the 32K decode with a learned indexer (64 dimensions, max over the heads)
+    "decode_32k_indexer": Workload("decode_32k_indexer", 8, "decode", 1, 32768, 16, 2, 128, 64, 16, "bf16", 0.5,
+                                   indexer_dim=64, indexer_agg=1),
     # a ragged batch: 64 sequences of 16K .. 128K tokens
     "decode_b64_ragged": Workload("decode_b64_ragged", 7, "decode", 64, 131072, 16, 2, 128, 64, 16, "bf16", 0.5,
                                   ragged=True),

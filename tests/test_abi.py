@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 3
+    assert qsa.abi_version() == 4
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -182,3 +182,28 @@ def test_ragged_decode_step_arguments(qsa):
     assert not qsa.qsa_decode_step_fused(one, 1 << 20)
     assert qsa.qsa_workspace_bytes(one, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 1 << 20) > 0
     assert call(ctypes.byref(one), P, P, P, P, P, 1 << 20, 1 << 20, P, N, P, P, 8, N) == WS
+
+
+def test_indexer_arguments(qsa):
+    """The indexer calls validate their struct and arguments on the host."""
+    lib = qsa.LIB
+    sh = ctypes.byref(good_shape(qsa))
+    P, N, MIS = ctypes.c_void_p(4096), None, ctypes.c_void_p(4100)
+    INV, UNS = 1, 2
+    ok = qsa.make_indexer(64, qsa.QSA_AGG_MAX)
+    for bad in (qsa.make_indexer(96, 0), qsa.make_indexer(64, 3), qsa.make_indexer(64, -1),
+                qsa.make_indexer(64, 0, -1.0), qsa.make_indexer(64, 0, float("inf"))):
+        assert lib.qsa_indexer_keys(sh, ctypes.byref(bad), P, P, 128, 128, 0, P, N) == INV
+        assert lib.qsa_indexer_select(sh, ctypes.byref(bad), P, P, 1, 127, P, 128, 128, P, N, N) == INV
+    ix = ctypes.byref(ok)
+    assert lib.qsa_indexer_keys(sh, None, P, P, 128, 128, 0, P, N) == INV
+    assert lib.qsa_indexer_keys(sh, ix, N, P, 128, 128, 0, P, N) == INV
+    assert lib.qsa_indexer_keys(sh, ix, P, P, 128, 128, 0, MIS, N) == INV
+    assert lib.qsa_indexer_keys(sh, ix, P, P, 129, 128, 0, P, N) == INV
+    assert lib.qsa_indexer_keys(sh, ix, N, N, 63, 128, 0, N, N) == 0  # no complete block: nothing to do
+    assert lib.qsa_indexer_select(sh, ix, P, P, 1, 127, P, 129, 256, P, N, N) == INV  # kv_len != q_pos0 + q_len
+    assert lib.qsa_indexer_select(sh, ix, N, P, 1, 127, P, 128, 256, P, N, N) == INV
+    assert lib.qsa_indexer_select(sh, ix, P, P, 1, 127, P, 128, 256, MIS, N, N) == INV
+    assert lib.qsa_indexer_select(sh, ix, P, P, 1, 127, N, 128, 256, P, N, N) == INV  # candidates, no keys
+    big_k = ctypes.byref(good_shape(qsa, top_k=65))
+    assert lib.qsa_indexer_select(big_k, ix, P, P, 1, 127, P, 128, 256, P, N, N) == UNS

@@ -128,3 +128,43 @@ def test_ragged_batched_decode_workload():
         st = check_rows(sub, sel_h[pick][:, None], out_h[pick][:, None], [(i, 0, g) for g in range(hkv)], lens[b] - 1,
                         scores_gpu=sc_h[pick][:, None])
         log(f"  sequence {b} (length {lens[b]}): {st}")
+
+
+def test_indexer_decode_workload():
+    """The 32K decode with a learned indexer (64 dimensions, max over the heads), as the benchmark runs it."""
+    from oracle import qsa_indexer as IX
+    from oracle import qsa_oracle as O
+    from qsa_check import check_selection_frame
+
+    w = S.WORKLOADS["decode_32k_indexer"]
+    case = Case(w, seed=0)
+    b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    G = hq // hkv
+    w_q, w_k = S.indexer_weights(0, w.cfg_id, d, w.indexer_dim)
+    shape = qsa.shape_for(case.q, case.k, bs, k)
+    ix = qsa.make_indexer(w.indexer_dim, w.indexer_agg)
+    k_comp = torch.empty(b, hkv, w.kv_len // bs, d, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    k_idx = torch.empty(b, hkv, w.kv_len // bs, w.indexer_dim, device="cuda")
+    qsa.qsa_indexer_keys(shape, ix, torch.from_numpy(w_k).cuda(), k_comp, w.kv_len, w.kv_len, k_idx)
+    sel = torch.empty(b, 1, hkv, k, dtype=torch.int32, device="cuda")
+    qsa.qsa_indexer_select(shape, ix, torch.from_numpy(w_q).cuda(), case.q, w.kv_len - 1, k_idx, w.kv_len, w.kv_len,
+                           sel)
+    q = case.q.view(b, hq, d)
+    out = torch.empty_like(q)
+    qsa.qsa_sparse_attn_decode(shape, q, case.k, case.v, w.kv_len, sel.view(b, hkv, k), out)
+    torch.cuda.synchronize()
+    p = w.kv_len - 1
+    n_cand, forced = O.selection_frame(p, bs, False)
+    ref_k = IX.indexer_keys(case.K, w_k.astype(np.float64), bs)
+    sel_h, out_h = sel.cpu().numpy(), from_device(out)
+    for g in range(hkv):
+        qg = case.Q[0, 0, g * G:(g + 1) * G].astype(np.float64)
+        sc = IX.indexer_scores(qg, w_q.astype(np.float64), ref_k[0, g], n_cand,
+                               IX.default_indexer_scale(w.indexer_dim), w.indexer_agg)
+        row = [int(x) for x in sel_h[0, 0, g]]
+        st = check_selection_frame(row, sc, n_cand, forced, k)
+        ref = O.attend_given_selection(qg, case.K[0, g], case.V[0, g], row, p, bs, O.default_scale(d))
+        err = float(np.abs(out_h[0, g * G:(g + 1) * G] - ref).max())
+        assert err <= 2e-2
+        log(f"  KV head {g}: selection {st}, output error {err:.2e}")
