@@ -110,8 +110,14 @@ def work_model(w, n_new_blocks: int, lens=None):
             m["select"] = {"bytes": rows * cand * d * 4 + b * hq * d * el + rows * k * 4,
                            "flops": 2 * d * rows * cand}
         vis = visible_keys(p, bs, k, w.keep_tail)
-        m["attend"] = {"bytes": rows * vis * d * el * 2 + 2 * b * hq * d * el + rows * k * 4,
-                       "flops": 4 * d * hq * b * vis}
+        if w.kv_q8:
+            # 8-bit codes plus a float16 scale per 32 values, for K and V
+            m["quantize"] = {"bytes": rows * 2 * (d * el + d + d // 32 * 2), "flops": 0}
+            m["attend"] = {"bytes": rows * vis * (d + d // 32 * 2) * 2 + 2 * b * hq * d * el + rows * k * 4,
+                           "flops": 4 * d * hq * b * vis}
+        else:
+            m["attend"] = {"bytes": rows * vis * d * el * 2 + 2 * b * hq * d * el + rows * k * 4,
+                           "flops": 4 * d * hq * b * vis}
     else:
         T = w.kv_len
         nb = T // bs
@@ -170,6 +176,15 @@ class Step:
                     qsa.qsa_compress_keys(one, self.k[bb:bb + 1], n - 1, self.k_comp[bb:bb + 1])
                 self.blk_begin = 0
                 self.n_new_blocks = sum(1 for n in self.lens if n % bs == 0)
+            elif w.kv_q8:
+                # the attention reads the rotated 8-bit cache: the separate calls (compress the closed
+                # block, quantize the new position, select, attend)
+                self.ws_step = None
+                self.kq, self.vq, self.ks, self.vs = qsa.kv_q8_buffers(self.k)
+                qsa.qsa_kv_quantize(self.shape, self.k, self.v, w.kv_len - 1, self.kq, self.vq, self.ks, self.vs)
+                qsa.qsa_compress_keys(self.shape, self.k, w.kv_len - 1, self.k_comp)
+                self.blk_begin = (w.kv_len - 1) // bs
+                self.n_new_blocks = w.kv_len // bs - self.blk_begin
             elif w.indexer_dim:
                 # learned-indexer selection: the separate calls (compress and project the closed block,
                 # indexer select, decode attention)
@@ -202,7 +217,10 @@ class Step:
             self.calls.insert(0, ("compress", self.compress))
         if self.n_new_blocks > 0 and w.indexer_dim:
             self.calls.insert(1, ("index_keys", self.index_keys))
-        self.step_calls = [("step", self.decode_step)] if w.mode == "decode" and not w.indexer_dim else self.calls
+        if w.kv_q8:
+            self.calls.insert(len(self.calls) - 2, ("quantize", self.quantize))
+        separate = w.indexer_dim or w.kv_q8
+        self.step_calls = [("step", self.decode_step)] if w.mode == "decode" and not separate else self.calls
         if self.fused:
             self.calls = self.step_calls
 
@@ -222,6 +240,11 @@ class Step:
     def compress(self):
         self.qsa.qsa_compress_keys(self.shape, self.k, self.w.kv_len, self.k_comp, block_begin=self.blk_begin)
 
+    def quantize(self):
+        w = self.w
+        self.qsa.qsa_kv_quantize(self.shape, self.k, self.v, w.kv_len, self.kq, self.vq, self.ks, self.vs,
+                                 pos_begin=w.kv_len - 1)
+
     def index_keys(self):
         w = self.w
         self.qsa.qsa_indexer_keys(self.shape, self.ix, self.w_k, self.k_comp, w.kv_len, w.kv_len, self.k_idx,
@@ -238,7 +261,10 @@ class Step:
 
     def attend(self):
         w = self.w
-        if w.mode == "decode":
+        if w.mode == "decode" and w.kv_q8:
+            self.qsa.qsa_sparse_attn_decode_q8(self.shape, self.q_dec, self.kq, self.vq, self.ks, self.vs, w.kv_len,
+                                               self.sel_dec, self.out_dec, ws=self.ws_att)
+        elif w.mode == "decode":
             self.qsa.qsa_sparse_attn_decode(self.shape, self.q_dec, self.k, self.v, w.kv_len, self.sel,
                                             self.out_dec, ws=self.ws_att)
         else:
@@ -506,6 +532,7 @@ def main():
                    "block_size": w.block_size, "top_k": w.top_k, "keep_tail": w.keep_tail, "seed": args.seed,
                    "graphs": not args.no_graph, "graph_steps": 1 if args.no_graph else max(1, args.graph_steps),
                    "fused_decode_step": st.fused, "ragged": w.ragged,
+                   **({"kv_cache": "rotated 8-bit (codes + float16 scale per 32)"} if w.kv_q8 else {}),
                    **({"indexer_dim": w.indexer_dim, "indexer_agg": ["sum", "max", "softmax"][w.indexer_agg]}
                       if w.indexer_dim else {}),
                    **({"mean_kv_len": round(float(np.mean(st.lens)), 1), "min_kv_len": int(min(st.lens))}

@@ -38,6 +38,9 @@ from .binding import (  # noqa: F401
     qsa_decode_step_ragged,
     qsa_indexer_keys,
     qsa_indexer_select,
+    qsa_kv_quantize,
+    qsa_sparse_attn_decode_q8,
+    kv_q8_buffers,
     qsa_score_select,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_prefill,

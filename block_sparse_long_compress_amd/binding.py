@@ -24,7 +24,8 @@ QSA_AGG_SUM, QSA_AGG_MAX, QSA_AGG_SOFTMAX = 0, 1, 2
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_ERR_WORKSPACE", 4: "QSA_ERR_HIP"}
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
             "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused",
-            "qsa_decode_step_ragged", "qsa_indexer_keys", "qsa_indexer_select")
+            "qsa_decode_step_ragged", "qsa_indexer_keys", "qsa_indexer_select", "qsa_kv_quantize",
+            "qsa_sparse_attn_decode_q8")
 
 
 class QsaError(RuntimeError):
@@ -83,6 +84,10 @@ def _load() -> ctypes.CDLL:
     lib.qsa_indexer_keys.argtypes = [SH, IX, P, P, I64, I64, I64, P, P]
     lib.qsa_indexer_select.restype = ctypes.c_int
     lib.qsa_indexer_select.argtypes = [SH, IX, P, P, I64, I64, P, I64, I64, P, P, P]
+    lib.qsa_kv_quantize.restype = ctypes.c_int
+    lib.qsa_kv_quantize.argtypes = [SH, P, P, I64, I64, I64, P, P, P, P, P]
+    lib.qsa_sparse_attn_decode_q8.restype = ctypes.c_int
+    lib.qsa_sparse_attn_decode_q8.argtypes = [SH, P, P, P, P, P, I64, I64, P, P, P, SZ, P]
     return lib
 
 
@@ -242,3 +247,29 @@ def qsa_indexer_select(shape: QsaShape, idx: QsaIndexer, w_q, q, q_pos0: int, k_
                                   _ptr(k_idx), kv_len, kv_cap, _ptr(sel), _ptr(sel_scores), _stream(q, stream)),
            "qsa_indexer_select")
     return sel
+
+
+def kv_q8_buffers(k, device=None):
+    """Empty 8-bit cache buffers shaped for bf16 ``k`` ``[b][Hkv][cap][d]``: (k_q, v_q, k_scales, v_scales)."""
+    b, hkv, cap, d = k.shape
+    device = device or k.device
+    codes = [torch.empty(b, hkv, cap, d, dtype=torch.int8, device=device) for _ in range(2)]
+    scales = [torch.empty(b, hkv, cap, d // 32, dtype=torch.int16, device=device) for _ in range(2)]
+    return codes[0], codes[1], scales[0], scales[1]
+
+
+def qsa_kv_quantize(shape: QsaShape, k, v, kv_len: int, k_q, v_q, k_scales, v_scales, pos_begin: int = 0,
+                    stream=None):
+    """Rotate and quantize positions ``pos_begin .. kv_len-1`` of K and V into the 8-bit cache."""
+    _check(LIB.qsa_kv_quantize(ctypes.byref(shape), _ptr(k), _ptr(v), kv_len, k.shape[2], pos_begin, _ptr(k_q),
+                               _ptr(v_q), _ptr(k_scales), _ptr(v_scales), _stream(k, stream)), "qsa_kv_quantize")
+
+
+def qsa_sparse_attn_decode_q8(shape: QsaShape, q, k_q, v_q, k_scales, v_scales, kv_len: int, sel, out, ws=None,
+                              stream=None):
+    """Decode attention over the rotated 8-bit cache (``q`` ``[b][Hq][d]``, ``sel`` ``[b][Hkv][k]``)."""
+    ws, nbytes = _workspace(shape, QSA_OP_DECODE, 1, kv_len, ws, q.device)
+    _check(LIB.qsa_sparse_attn_decode_q8(ctypes.byref(shape), _ptr(q), _ptr(k_q), _ptr(v_q), _ptr(k_scales),
+                                         _ptr(v_scales), kv_len, k_q.shape[2], _ptr(sel), _ptr(out), _ptr(ws), nbytes,
+                                         _stream(q, stream)), "qsa_sparse_attn_decode_q8")
+    return out

@@ -27,6 +27,7 @@ SOURCES = [
     "qsa_attn_f32.hip",
     "qsa_decode_step.hip",
     "qsa_indexer.hip",
+    "qsa_kv_q8.hip",
 ]
 
 ARCH = "gfx950"

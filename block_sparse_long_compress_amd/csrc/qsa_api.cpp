@@ -331,4 +331,44 @@ qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, co
                                                static_cast<hipStream_t>(stream)));
 }
 
+qsa_status qsa_kv_quantize(const qsa_shape* shape, const void* k, const void* v, int64_t kv_len, int64_t kv_cap,
+                           int64_t pos_begin, int8_t* k_q, int8_t* v_q, uint16_t* k_scales, uint16_t* v_scales,
+                           void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (kv_len < 0 || kv_cap <= 0 || kv_len > kv_cap || pos_begin < 0) return QSA_ERR_INVALID;
+  if (s.dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  if (pos_begin >= kv_len) return QSA_OK;  // nothing in range
+  if (!k || !v || !k_q || !v_q || !k_scales || !v_scales) return QSA_ERR_INVALID;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_q) || !aligned16(v_q) || !aligned16(k_scales) ||
+      !aligned16(v_scales))
+    return QSA_ERR_INVALID;
+  if ((int64_t)s.batch * s.hkv * (kv_len - pos_begin) * 2 / 4 + 1 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  return hip_status(qsa::launch_kv_quantize(s, k, v, kv_cap, pos_begin, kv_len, k_q, v_q, k_scales, v_scales,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, const int8_t* k_q, const int8_t* v_q,
+                                     const uint16_t* k_scales, const uint16_t* v_scales, int64_t kv_len,
+                                     int64_t kv_cap, const int32_t* sel, void* out, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !k_q || !v_q || !k_scales || !v_scales || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_q) || !aligned16(v_q) || !aligned16(k_scales) || !aligned16(v_scales) ||
+      !aligned16(sel) || !aligned16(out))
+    return QSA_ERR_INVALID;
+  if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
+  if (s.dtype != QSA_BF16 || s.bs < 32) return QSA_ERR_UNSUPPORTED;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len);
+  if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  return hip_status(qsa::launch_decode_q8(s, plan, q, k_q, v_q, k_scales, v_scales, kv_len, kv_cap, sel, out, ws,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -31,6 +31,31 @@ __device__ __forceinline__ int kkey(int lg, int j) { return j < 4 ? 4 * lg + j :
 template <int D>
 constexpr int kStageRowBytes = 2 * D + 16;  // LDS row stride of staged V (bytes)
 
+// A quantized K/V cache (8-bit codes, one float16 scale per 32 values of a
+// row: value = code * scale), read by attend_units<..., true> in place of
+// the bf16 cache; the values are widened to bf16 operands on load.
+struct Q8Cache {
+  const int8_t* k;     // codes [positions][D] of the row's keys
+  const int8_t* v;     // codes of its values
+  const uint16_t* ks;  // float16 scales [positions][D/32]
+  const uint16_t* vs;
+};
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// 8 codes (two little-endian words) times one scale, as 4 packed bf16 pairs.
+__device__ __forceinline__ u32x4_t dequant8_bf16(u32x2_t codes, float scale) {
+  uint32_t r[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t w = codes[h / 2] >> (16 * (h % 2));
+    const float a = (float)(int8_t)(w & 0xFF) * scale;
+    const float b = (float)(int8_t)((w >> 8) & 0xFF) * scale;
+    r[h] = pack_bf16x2(a, b);
+  }
+  return u32x4_t{r[0], r[1], r[2], r[3]};
+}
+
 // Q operands of the row's G query heads (head j in column j; columns >= G zero).
 template <int D>
 __device__ __forceinline__ void load_q_operands(const uint16_t* __restrict__ q_heads, int G, u32x4_t (&qf)[D / 32]) {
@@ -48,11 +73,13 @@ __device__ __forceinline__ void load_q_operands(const uint16_t* __restrict__ q_h
 // row's keys and values; p is the query position; vs is the wave's 32-row
 // staging slice. One unit in flight per wave: a second register set would
 // halve the waves per SIMD, and more waves hide latency at least as well.
-template <int D, bool GATHER>
+template <int D, bool GATHER, bool Q8 = false>
 __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const uint16_t* __restrict__ kbase,
                                              const uint16_t* __restrict__ vbase, int sel_mine, int n_e, int bs,
                                              int64_t p, float scale_log2, unsigned char* vs, int first, int stride,
-                                             float& m_run, float& l_run, f32x4_t (&o)[D / 16]) {
+                                             float& m_run, float& l_run, f32x4_t (&o)[D / 16],
+                                             Q8Cache q8 = Q8Cache{nullptr, nullptr, nullptr, nullptr}) {
+  static_assert(!(Q8 && GATHER), "the quantized cache is read in whole 32-key units");
   constexpr int RS = kStageRowBytes<D>;
   constexpr int KS = D / 32;  // 32-wide K steps of the QK^T product
   constexpr int DT = D / 16;  // 16-wide dim tiles of the PV product
@@ -107,6 +134,36 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
       u.key0 = (int64_t)c * bs + (int64_t)(idx % upb) * kUnit;
       if (u.key0 > p) return;
       u.ok = true;
+      if constexpr (Q8) {
+        // the same operands from the codes: 8 codes (one 32-value scale) per fragment
+        u32x2_t kc[2][KS], vc[VCH];
+        float ksc[2][KS], vsc[VCH];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int64_t key = u.key0 + 16 * st + col;
+          const bool ok = key <= p;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            kc[st][s] = ok ? *reinterpret_cast<const u32x2_t*>(q8.k + key * D + 32 * s + 8 * lg) : u32x2_t{0u, 0u};
+            ksc[st][s] = ok ? f16_bits_to_f32(q8.ks[key * (D / 32) + s]) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) {
+          const int ci = lane + kWave * j;
+          const int r = ci / (D / 8), c8 = ci % (D / 8);
+          const int64_t key = u.key0 + r;
+          const bool ok = key <= p;
+          vc[j] = ok ? *reinterpret_cast<const u32x2_t*>(q8.v + key * D + 8 * c8) : u32x2_t{0u, 0u};
+          vsc[j] = ok ? f16_bits_to_f32(q8.vs[key * (D / 32) + c8 / 4]) : 0.f;
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int s = 0; s < KS; ++s) u.kf[st][s] = dequant8_bf16(kc[st][s], ksc[st][s]);
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) u.vr[j] = dequant8_bf16(vc[j], vsc[j]);
+      } else {
       const uint16_t* kb = kbase + u.key0 * D;
       const uint16_t* vb = vbase + u.key0 * D;
 #pragma unroll
@@ -124,6 +181,7 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
         const int r = ci / (D / 8), c8 = ci % (D / 8);
         u.vr[j] = u.key0 + r <= p ? *reinterpret_cast<const u32x4_t*>(vb + (int64_t)r * D + 8 * c8)
                                   : u32x4_t{0u, 0u, 0u, 0u};
+      }
       }
     }
   };

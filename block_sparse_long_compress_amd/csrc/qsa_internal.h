@@ -29,6 +29,11 @@ hipError_t launch_indexer_select(const Dims& s, const IndexerDims& ix, const flo
                                  int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel,
                                  float* sel_scores, hipStream_t st);
 
+// Rotated 8-bit K/V cache: positions [pos_begin, pos_end) of every (b, g)
+// rotated (Walsh-Hadamard) and quantized (codes + float16 scale per 32).
+hipError_t launch_kv_quantize(const Dims& s, const void* k, const void* v, int64_t kv_cap, int64_t pos_begin,
+                              int64_t pos_end, int8_t* kq, int8_t* vq, uint16_t* ks, uint16_t* vs, hipStream_t st);
+
 // Block compression, blocks [blk_begin, blk_end) of every (b, g).
 hipError_t launch_compress(const Dims& s, const void* k, int64_t kv_cap, int64_t blk_begin, int64_t blk_end,
                            float* k_comp, hipStream_t st);
@@ -71,6 +76,11 @@ DecodePlan plan_decode(const Dims& s, int64_t kv_len);
 
 hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
                          int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* ws, hipStream_t st);
+// Decode attention over the rotated 8-bit cache (same plan and workspace as
+// launch_decode; Bs >= 32).
+hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q, const int8_t* kq, const int8_t* vq,
+                            const uint16_t* ks, const uint16_t* vs, int64_t kv_len, int64_t kv_cap,
+                            const int32_t* sel, void* out, void* ws, hipStream_t st);
 
 // Prefill attention -------------------------------------------------------------
 struct PrefillPlan {

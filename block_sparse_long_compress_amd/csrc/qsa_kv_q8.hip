@@ -1,0 +1,273 @@
+// Rotated, 8-bit quantized K/V cache and the decode attention that reads it
+// ("Qwen4 in llama.cpp: Dissecting PR #27742", section "Quantized KV Exposed
+// a Backend Storage Invariant": K and V are stored in a Hadamard-rotated
+// basis and quantized; attention runs in the rotated basis and its output is
+// rotated back, which is exact because the scaled Hadamard matrix is its own
+// inverse; the indexer keeps reading the unrotated compressed keys).
+//
+// Rotation: the unnormalised Walsh-Hadamard transform of a head vector
+// (entries +-1, Sylvester order), butterfly stages h = 1, 2, ..., d/2 in that
+// order, pair (i, i + h) becoming (x_i + x_{i+h}, x_i - x_{i+h}) in float32.
+// Since H^T H = d I, scores use (H q).(H k) / d and outputs H (sum p H v) / d.
+//
+// Quantization (per 32 values of a rotated row, float32): scale = the
+// largest magnitude / 127, rounded to float16 and stored; code =
+// round-half-even(value / scale) clamped to [-127, 127] (0 when the scale
+// is 0); dequantized value = code * scale.
+#include "qsa_decode_unit.h"
+#include "qsa_device.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+// In-place unnormalised Walsh-Hadamard transform of a D-vector held by one
+// wave, lane l holding elements l and l + 64 (D = 128) or l (D = 64).
+template <int D>
+__device__ __forceinline__ void fwht_wave(float (&v)[D / kWave]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int h = 1; h < kWave && h < D; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D / kWave; ++i) {
+      const float other = shfl_xor_f32(v[i], h);
+      v[i] = (lane & h) ? other - v[i] : v[i] + other;
+    }
+  }
+  if constexpr (D == 2 * kWave) {
+    const float a = v[0], b = v[1];
+    v[0] = a + b;
+    v[1] = a - b;
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+// One wave per (sequence, KV head, position, K or V): rotate the row, then
+// quantize each 32-value group.
+template <int D>
+__global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                          int8_t* __restrict__ kq, int8_t* __restrict__ vq,
+                                                          uint16_t* __restrict__ ks, uint16_t* __restrict__ vs,
+                                                          int64_t kv_cap, int64_t pos_begin, int64_t n_pos,
+                                                          int64_t n_items) {
+  constexpr int EPL = D / kWave;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave_id();
+  if (item >= 2 * n_items) return;
+  const bool is_v = item >= n_items;
+  const int64_t it = is_v ? item - n_items : item;
+  const int64_t bg = it / n_pos;
+  const int64_t pos = pos_begin + it % n_pos;
+  const int64_t rowoff = (bg * kv_cap + pos) * D;
+  const uint16_t* src = (is_v ? v : k) + rowoff;
+  const int lane = lane_id();
+  float x[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) x[i] = bf16_to_f32(src[lane + kWave * i]);
+  fwht_wave<D>(x);
+  int8_t* dq = (is_v ? vq : kq) + rowoff;
+  uint16_t* ds = (is_v ? vs : ks) + (bg * kv_cap + pos) * (D / 32);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    // the 32 lanes of element lane + 64 i that share a group
+    float amax = fabsf(x[i]);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, shfl_xor_f32(amax, m));
+    const uint16_t sbits = f32_to_f16_bits(amax / 127.0f);
+    const float scale = f16_bits_to_f32(sbits);
+    float c = scale > 0.f ? __builtin_rintf(x[i] / scale) : 0.f;
+    c = fminf(fmaxf(c, -127.f), 127.f);
+    dq[lane + kWave * i] = (int8_t)(int)c;
+    if ((lane & 31) == 0) ds[(lane + kWave * i) / 32] = sbits;
+  }
+}
+
+template <int D>
+struct Q8Smem {
+  static constexpr int RS = kStageRowBytes<D>;
+  static constexpr int kStage = 4 * kUnit * RS;
+  static constexpr int kComb = 4 * (32 + 16 * D) * 4;
+  static constexpr int kBytes = kStage > kComb ? kStage : kComb;
+};
+
+// Decode attention over the rotated quantized cache: one workgroup (4 waves)
+// per (sequence, KV head, slice of the selection). The G query heads are
+// rotated into LDS (bf16 operands), the units are those of the bf16 decode
+// kernel with the codes widened on load, and the combined state of the
+// slice is rotated back (H O / d) before it is written, which commutes with
+// the softmax merge of the slices (a linear combination of the states).
+template <int D>
+__global__ __launch_bounds__(256) void decode_attn_q8_kernel(
+    const uint16_t* __restrict__ q, const int8_t* __restrict__ kq, const int8_t* __restrict__ vq,
+    const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs_, const int32_t* __restrict__ sel,
+    uint16_t* __restrict__ out, float* __restrict__ part, uint32_t* __restrict__ counters, int64_t kv_len,
+    int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k, float scale_log2, int bpw, int n_split) {
+  using SM = Q8Smem<D>;
+  constexpr int DT = D / 16;
+  constexpr int EPL = D / kWave;
+  __shared__ __align__(16) unsigned char smem[SM::kBytes];
+  __shared__ __align__(16) uint16_t qrot[16 * D];
+  __shared__ __align__(16) float comb_o[16 * D];  // the slice's combined output, rotated back
+  __shared__ float comb_m[16], comb_l[16];
+  __shared__ int last_wg;
+
+  const int64_t row = blockIdx.x / n_split;
+  const int split = blockIdx.x % n_split;
+  const int64_t b = row / hkv;
+  const int g = (int)(row % hkv);
+  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
+  const int lg = lane / 16, col = lane % 16;
+  const int64_t p = kv_len - 1;
+  const int e0 = split * bpw;
+  const int n_e = top_k - e0 < bpw ? top_k - e0 : bpw;
+  const int64_t kv_off = ((int64_t)b * hkv + g) * kv_cap;
+
+  // rotated query heads (bf16), head h by wave h % 4
+  const uint16_t* qh = q + (b * hq + (int64_t)g * G) * D;
+  for (int h = w; h < G; h += 4) {
+    float x[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) x[i] = bf16_to_f32(qh[(int64_t)h * D + lane + kWave * i]);
+    fwht_wave<D>(x);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) qrot[h * D + lane + kWave * i] = f32_to_bf16(x[i]);
+  }
+  __syncthreads();
+  u32x4_t qf[D / 32];
+  load_q_operands<D>(qrot, G, qf);
+
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int sel_mine = lane < n_e ? sel[row * top_k + e0 + lane] : -1;
+  const Q8Cache cache{kq + kv_off * D, vq + kv_off * D, ks + kv_off * (D / 32), vs_ + kv_off * (D / 32)};
+  attend_units<D, false, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2,
+                               smem + w * kUnit * SM::RS, w, 4, m_run, l_run, o, cache);
+  l_run = sum_col4(l_run);
+
+  // combine the waves' states in LDS (wave order), rotate the combined O
+  // back, then write the output (one slice) or the slice state
+  __syncthreads();  // staging area becomes the combine area
+  float* cm = reinterpret_cast<float*>(smem);  // [4][16] running maxima
+  float* cl = cm + 4 * 16;                     // [4][16] sums
+  float* co = cl + 4 * 16;                     // [4][16][D] unnormalised outputs
+  if (lane < 16) {
+    cm[w * 16 + col] = m_run;
+    cl[w * 16 + col] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, e = idx % D;
+    float M = -__builtin_inff();
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
+    float L = 0.f, O = 0.f;
+    if (M != -__builtin_inff()) {  // a slice may hold no visible key
+      for (int ww = 0; ww < 4; ++ww) {
+        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
+        L += f * cl[ww * 16 + h];
+        O += f * co[(ww * 16 + h) * D + e];
+      }
+    }
+    if (e == 0) {
+      comb_m[h] = M;
+      comb_l[h] = L;
+    }
+    comb_o[idx] = O;
+  }
+  __syncthreads();
+  constexpr float inv_d = 1.0f / D;  // exact: D is a power of two
+  for (int h = w; h < G; h += 4) {
+    float x[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) x[i] = comb_o[h * D + lane + kWave * i];
+    fwht_wave<D>(x);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) comb_o[h * D + lane + kWave * i] = x[i] * inv_d;
+  }
+  __syncthreads();
+
+  if (n_split == 1) {
+    for (int idx = tid; idx < G * D; idx += 256) {
+      const int h = idx / D, e = idx % D;
+      out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(comb_o[idx] / comb_l[h]);
+    }
+    return;
+  }
+  // several slices: this slice's state with device-coherent stores, a
+  // ticket, and the last workgroup of the row merges (as the bf16 decode)
+  const int stride = 2 * G + G * D;
+  const auto prs = __builtin_amdgcn_make_buffer_rsrc(part + row * (int64_t)n_split * stride, 0,
+                                                     n_split * stride * 4, kBufferFlags);
+  const int soff = split * stride;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, e = idx % D;
+    if (e == 0) {
+      store_coherent(prs, soff + h, __float_as_uint(comb_m[h]));
+      store_coherent(prs, soff + G + h, __float_as_uint(comb_l[h]));
+    }
+    store_coherent(prs, soff + 2 * G + idx, __float_as_uint(comb_o[idx]));
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == (uint32_t)(n_split - 1);
+    if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_wg = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_wg) return;
+  if (G * (D / 4) <= 256) merge_slices<D, 1, 16, 256>(prs, smem, out, b, g, hq, G, n_split, tid);
+  else merge_slices<D, 2, 8, 256>(prs, smem, out, b, g, hq, G, n_split, tid);
+}
+
+template <int D>
+hipError_t launch_quant_d(const void* k, const void* v, int8_t* kq, int8_t* vq, uint16_t* ks, uint16_t* vs,
+                          int64_t kv_cap, int64_t pos_begin, int64_t n_pos, int64_t rows, hipStream_t st) {
+  const int64_t n_items = rows * n_pos;
+  hipLaunchKernelGGL((kv_quantize_kernel<D>), dim3((unsigned)((2 * n_items + 3) / 4)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), kq, vq, ks, vs, kv_cap,
+                     pos_begin, n_pos, n_items);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_q8_d(const Dims& s, const DecodePlan& plan, const void* q, const int8_t* kq, const int8_t* vq,
+                       const uint16_t* ks, const uint16_t* vs, int64_t kv_len, int64_t kv_cap, const int32_t* sel,
+                       void* out, void* ws, hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  // (H q).(H k) = d q.k: the 1/d of the rotation is folded into the scale
+  const float scale_log2 = s.scale * 1.4426950408889634f / (float)D;
+  uint32_t* counters = static_cast<uint32_t*>(ws);
+  float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows)) : nullptr;
+  hipLaunchKernelGGL((decode_attn_q8_kernel<D>), dim3((unsigned)(rows * plan.n_split)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(q), kq, vq, ks, vs, sel, static_cast<uint16_t*>(out), part,
+                     counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, scale_log2, plan.blocks_per_wg,
+                     plan.n_split);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kv_quantize(const Dims& s, const void* k, const void* v, int64_t kv_cap, int64_t pos_begin,
+                              int64_t pos_end, int8_t* kq, int8_t* vq, uint16_t* ks, uint16_t* vs, hipStream_t st) {
+  const int64_t n_pos = pos_end - pos_begin;
+  if (n_pos <= 0) return hipSuccess;
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  return s.d == 64 ? launch_quant_d<64>(k, v, kq, vq, ks, vs, kv_cap, pos_begin, n_pos, rows, st)
+                   : launch_quant_d<128>(k, v, kq, vq, ks, vs, kv_cap, pos_begin, n_pos, rows, st);
+}
+
+hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q, const int8_t* kq, const int8_t* vq,
+                            const uint16_t* ks, const uint16_t* vs, int64_t kv_len, int64_t kv_cap,
+                            const int32_t* sel, void* out, void* ws, hipStream_t st) {
+  return s.d == 64 ? launch_q8_d<64>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, ws, st)
+                   : launch_q8_d<128>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, ws, st);
+}
+
+}  // namespace qsa

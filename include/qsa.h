@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 4
+#define QSA_ABI_VERSION 5
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -284,6 +284,43 @@ qsa_status qsa_indexer_keys(const qsa_shape* shape, const qsa_indexer* idx, cons
 qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, const float* w_q, const void* q,
                               int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_len, int64_t kv_cap,
                               int32_t* sel, float* sel_scores, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Rotated 8-bit K/V cache ("Qwen4 in llama.cpp: Dissecting PR #27742",
+ * section "Quantized KV Exposed a Backend Storage Invariant": K and V are
+ * stored Hadamard-rotated and quantized, attention runs in the rotated basis
+ * and its output is rotated back; the indexer's compressed keys stay
+ * unrotated, so qsa_compress_keys and qsa_score_select keep reading the
+ * bf16 keys). This library's reading of the storage:
+ *   rotation  the unnormalised Walsh-Hadamard transform of each head_dim
+ *             row (Sylvester order), butterfly stages h = 1, 2, ...,
+ *             head_dim/2 in that order, pair (i, i+h) -> (x_i + x_{i+h},
+ *             x_i - x_{i+h}), in float32;
+ *   codes     per 32 values of a rotated row: scale = (largest magnitude /
+ *             127) rounded to float16, code = round-half-even(value /
+ *             scale) clamped to [-127, 127] (0 if the scale is 0);
+ *             value = code * scale.
+ * Layouts: k_q, v_q int8 [b][Hkv][kv_cap][head_dim]; k_scales, v_scales
+ * float16 bit patterns [b][Hkv][kv_cap][head_dim/32]; all 16-byte aligned. */
+
+/* Rotate and quantize positions pos_begin .. kv_len-1 of K and V (bf16,
+ * [b][Hkv][kv_cap][head_dim]) into the 8-bit cache. No workspace.
+ * QSA_ERR_UNSUPPORTED for float32 shapes; QSA_OK without work when
+ * pos_begin >= kv_len. */
+qsa_status qsa_kv_quantize(const qsa_shape* shape, const void* k, const void* v, int64_t kv_len, int64_t kv_cap,
+                           int64_t pos_begin, int8_t* k_q, int8_t* v_q, uint16_t* k_scales, uint16_t* v_scales,
+                           void* stream);
+
+/* qsa_sparse_attn_decode over the 8-bit cache: the query heads are rotated,
+ * scores use (H q).(H k)/head_dim, and every slice's output is rotated back
+ * before the slices merge. Same selection, plan and workspace as
+ * qsa_sparse_attn_decode (ws: qsa_workspace_bytes(shape, QSA_OP_DECODE, 1,
+ * kv_len) bytes, zero-filled before first use). bf16 with Bs >= 32 only,
+ * else QSA_ERR_UNSUPPORTED. */
+qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, const int8_t* k_q, const int8_t* v_q,
+                                     const uint16_t* k_scales, const uint16_t* v_scales, int64_t kv_len,
+                                     int64_t kv_cap, const int32_t* sel, void* out, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 #ifdef __cplusplus
 }

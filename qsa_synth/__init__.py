@@ -58,6 +58,7 @@ class Workload:
     ragged: bool = False  # decode: every sequence has its own length (see seq_lengths)
     indexer_dim: int = 0  # learned-indexer selection: indexer dimension (0 = the default selection)
     indexer_agg: int = 0  # its aggregation of a group's head scores: 0 sum, 1 max, 2 softmax
+    kv_q8: bool = False   # decode attention over the rotated 8-bit K/V cache
 
     @property
     def q_len(self) -> int:
@@ -87,6 +88,9 @@ WORKLOADS = {
     # the 32K decode with a learned indexer (64 dimensions, max over the heads)
     "decode_32k_indexer": Workload("decode_32k_indexer", 8, "decode", 1, 32768, 16, 2, 128, 64, 16, "bf16", 0.5,
                                    indexer_dim=64, indexer_agg=1),
+    # the batched decode with the attention reading a rotated 8-bit K/V cache
+    "decode_b64_128k_q8": Workload("decode_b64_128k_q8", 9, "decode", 64, 131072, 16, 2, 128, 64, 16, "bf16", 0.5,
+                                   planted=8, kv_q8=True),
     # a ragged batch: 64 sequences of 16K .. 128K tokens
     "decode_b64_ragged": Workload("decode_b64_ragged", 7, "decode", 64, 131072, 16, 2, 128, 64, 16, "bf16", 0.5,
                                   ragged=True),

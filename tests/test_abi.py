@@ -27,7 +27,7 @@ def qsa():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_four_steps():
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 4
+    assert qsa.abi_version() == 5
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)

@@ -1,0 +1,123 @@
+"""GPU parity of the rotated 8-bit K/V cache path.
+
+Codes and float16 scales are integers decided in float32: they must equal
+the oracle's bit for bit. The decode attention over the cache is compared
+with the oracle's float64 attention over the same dequantized cache and the
+same selection (bf16 output tolerance), and reported against plain bf16
+attention for scale.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_compress_amd as qsa
+import qsa_synth as S
+from gpu_common import Case, from_device, log
+from oracle import qsa_kv_q8 as Q
+from oracle import qsa_oracle as O
+from qsa_check import BF16_ABS_TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def W(**kw) -> S.Workload:
+    base = dict(name="q8", cfg_id=92, mode="decode", batch=2, kv_len=9000, n_q_heads=16, n_kv_heads=2,
+                head_dim=128, block_size=64, top_k=16, dtype="bf16", sigma=0.5)
+    base.update(kw)
+    return S.Workload(**base)
+
+
+CASES = [
+    W(),                                                                  # several slices per row
+    W(batch=3, kv_len=5000, top_k=64, block_size=32, head_dim=64),
+    W(batch=1, kv_len=40000, top_k=16, n_q_heads=16, n_kv_heads=1),      # G = 16
+    W(batch=40, kv_len=2000, top_k=8, block_size=128, n_q_heads=8),       # 80 rows
+    W(batch=1, kv_len=50, top_k=4),                                       # own block only
+]
+
+
+def case_id(w):
+    return f"b{w.batch}-n{w.kv_len}-h{w.n_q_heads}x{w.n_kv_heads}-d{w.head_dim}-bs{w.block_size}-k{w.top_k}"
+
+
+def quantized(case):
+    w = case.w
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k)
+    kq, vq, ks, vs = qsa.kv_q8_buffers(case.k)
+    qsa.qsa_kv_quantize(shape, case.k, case.v, w.kv_len, kq, vq, ks, vs)
+    return shape, kq, vq, ks, vs
+
+
+@pytest.mark.parametrize("w", CASES, ids=case_id)
+def test_q8_codes_bit_exact(w):
+    log(f"q8 codes {case_id(w)}")
+    case = Case(w, seed=31)
+    _, kq, vq, ks, vs = quantized(case)
+    torch.cuda.synchronize()
+    n = w.kv_len
+    rng = np.random.default_rng(0)
+    rows = [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    if len(rows) > 8:
+        rows = [rows[i] for i in sorted(rng.choice(len(rows), 8, replace=False))]
+    for b, g in rows:
+        for X, codes, sc in ((case.K, kq, ks), (case.V, vq, vs)):
+            want_c, want_s = Q.quantize_cache(X[b, g, :n])
+            got_c = codes[b, g, :n].cpu().numpy()
+            got_s = sc[b, g, :n].cpu().numpy().view(np.uint16)
+            assert np.array_equal(got_c, want_c), f"codes of {(b, g)}"
+            assert np.array_equal(got_s, want_s.view(np.uint16)), f"scales of {(b, g)}"
+
+
+def test_q8_incremental_quantization():
+    """Quantizing positions in two calls (pos_begin) writes the same cache as one call."""
+    w = W(batch=2, kv_len=3000)
+    case = Case(w, seed=32)
+    shape, kq, vq, ks, vs = quantized(case)
+    kq2, vq2, ks2, vs2 = qsa.kv_q8_buffers(case.k)
+    qsa.qsa_kv_quantize(shape, case.k, case.v, 1777, kq2, vq2, ks2, vs2)
+    qsa.qsa_kv_quantize(shape, case.k, case.v, w.kv_len, kq2, vq2, ks2, vs2, pos_begin=1777)
+    torch.cuda.synchronize()
+    n = w.kv_len
+    for a, c in ((kq, kq2), (vq, vq2), (ks, ks2), (vs, vs2)):
+        assert torch.equal(a[:, :, :n], c[:, :, :n])
+
+
+@pytest.mark.parametrize("w", CASES, ids=case_id)
+def test_q8_decode_parity(w):
+    log(f"q8 decode {case_id(w)}")
+    case = Case(w, seed=33)
+    b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    G = hq // hkv
+    shape, kq, vq, ks, vs = quantized(case)
+    # the selection reads the unrotated compressed keys, as without the 8-bit cache
+    k_comp = torch.empty(b, hkv, max(1, w.kv_len // bs), d, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    q = case.q.view(b, hq, d)
+    sel = torch.empty(b, 1, hkv, k, dtype=torch.int32, device="cuda")
+    qsa.qsa_score_select(shape, case.q, w.kv_len - 1, k_comp, w.kv_len, w.kv_len, sel)
+    out = torch.empty_like(q)
+    qsa.qsa_sparse_attn_decode_q8(shape, q, kq, vq, ks, vs, w.kv_len, sel.view(b, hkv, k), out)
+    out_bf = torch.empty_like(q)
+    qsa.qsa_sparse_attn_decode(shape, q, case.k, case.v, w.kv_len, sel.view(b, hkv, k), out_bf)
+    torch.cuda.synchronize()
+    out_h, sel_h, bf_h = from_device(out), sel.cpu().numpy(), from_device(out_bf)
+    rng = np.random.default_rng(1)
+    rows = [(bb, g) for bb in range(b) for g in range(hkv)]
+    if len(rows) > 12:
+        rows = [rows[i] for i in sorted(rng.choice(len(rows), 12, replace=False))]
+    worst, vs_plain = 0.0, 0.0
+    p = w.kv_len - 1
+    for bb, g in rows:
+        qg = case.Q[bb, 0, g * G:(g + 1) * G].astype(np.float64)
+        selr = [int(x) for x in sel_h[bb, 0, g]]
+        kq_o, ks_o = Q.quantize_cache(case.K[bb, g, :w.kv_len])  # the oracle's own cache
+        vq_o, vs_o = Q.quantize_cache(case.V[bb, g, :w.kv_len])
+        ref = Q.attend_q8(qg, kq_o, ks_o, vq_o, vs_o, selr, p, bs, O.default_scale(d))
+        got = out_h[bb, g * G:(g + 1) * G]
+        err = float(np.abs(got - ref).max())
+        assert err <= BF16_ABS_TOL, f"row {(bb, g)}: error {err:.3e}"
+        worst = max(worst, err)
+        vs_plain = max(vs_plain, float(np.abs(got - bf_h[bb, g * G:(g + 1) * G]).max()))
+    log(f"  max error against the 8-bit oracle {worst:.2e}; largest difference from bf16 attention {vs_plain:.2e}")

@@ -168,3 +168,40 @@ def test_indexer_decode_workload():
         err = float(np.abs(out_h[0, g * G:(g + 1) * G] - ref).max())
         assert err <= 2e-2
         log(f"  KV head {g}: selection {st}, output error {err:.2e}")
+
+
+def test_batched_decode_q8_workload():
+    """The 64 x 128K batch with the attention reading the rotated 8-bit cache (sampled rows)."""
+    from oracle import qsa_kv_q8 as Q
+    from oracle import qsa_oracle as O
+
+    w = S.WORKLOADS["decode_b64_128k_q8"]
+    log("workload decode_b64_128k_q8: generating 2 x 4 GiB")
+    case = Case(w, seed=0)
+    hq, hkv, d, bs, k = w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    G = hq // hkv
+    shape = qsa.shape_for(case.q, case.k, bs, k)
+    kq, vq, ks, vs = qsa.kv_q8_buffers(case.k)
+    qsa.qsa_kv_quantize(shape, case.k, case.v, w.kv_len, kq, vq, ks, vs)
+    k_comp = torch.empty(w.batch, hkv, w.kv_len // bs, d, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    sel = torch.empty(w.batch, 1, hkv, k, dtype=torch.int32, device="cuda")
+    qsa.qsa_score_select(shape, case.q, w.kv_len - 1, k_comp, w.kv_len, w.kv_len, sel)
+    q = case.q.view(w.batch, hq, d)
+    out = torch.empty_like(q)
+    qsa.qsa_sparse_attn_decode_q8(shape, q, kq, vq, ks, vs, w.kv_len, sel.view(w.batch, hkv, k), out)
+    torch.cuda.synchronize()
+    sel_h, out_h = sel.cpu().numpy(), from_device(out)
+    for b in range(w.batch):  # planted blocks are found from the unrotated compressed keys
+        for g in range(hkv):
+            assert set(S.planted_blocks(w, 0, b, g).tolist()) <= set(sel_h[b, 0, g].tolist())
+    p = w.kv_len - 1
+    for b, g in [(0, 0), (17, 1), (63, 0)]:
+        kq_o, ks_o = Q.quantize_cache(case.K[b, g])
+        vq_o, vs_o = Q.quantize_cache(case.V[b, g])
+        assert np.array_equal(kq[b, g].cpu().numpy(), kq_o), "codes"
+        qg = case.Q[b, 0, g * G:(g + 1) * G].astype(np.float64)
+        ref = Q.attend_q8(qg, kq_o, ks_o, vq_o, vs_o, [int(x) for x in sel_h[b, 0, g]], p, bs, O.default_scale(d))
+        err = float(np.abs(out_h[b, g * G:(g + 1) * G] - ref).max())
+        assert err <= 2e-2
+        log(f"  row {(b, g)}: output error {err:.2e}")
