@@ -44,14 +44,18 @@ struct Q8Cache {
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
 // 8 codes (two little-endian words) times one scale, as 4 packed bf16 pairs.
+// The codes are biased to unsigned bytes (xor 0x80), widened one byte per
+// instruction, and (c + 128 - 128) * scale is one fused multiply-add.
 __device__ __forceinline__ u32x4_t dequant8_bf16(u32x2_t codes, float scale) {
+  const float off = -128.0f * scale;
   uint32_t r[4];
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const uint32_t w = codes[h / 2] >> (16 * (h % 2));
-    const float a = (float)(int8_t)(w & 0xFF) * scale;
-    const float b = (float)(int8_t)((w >> 8) & 0xFF) * scale;
-    r[h] = pack_bf16x2(a, b);
+  for (int wi = 0; wi < 2; ++wi) {
+    const uint32_t w = codes[wi] ^ 0x80808080u;
+    const float c0 = (float)(w & 0xFFu), c1 = (float)((w >> 8) & 0xFFu);  // one byte-to-float instruction each
+    const float c2 = (float)((w >> 16) & 0xFFu), c3 = (float)(w >> 24);
+    r[2 * wi] = pack_bf16x2(__builtin_fmaf(c0, scale, off), __builtin_fmaf(c1, scale, off));
+    r[2 * wi + 1] = pack_bf16x2(__builtin_fmaf(c2, scale, off), __builtin_fmaf(c3, scale, off));
   }
   return u32x4_t{r[0], r[1], r[2], r[3]};
 }
@@ -136,33 +140,55 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
       u.ok = true;
       if constexpr (Q8) {
         // the same operands from the codes: 8 codes (one 32-value scale) per fragment
+        // K: each lane's key row holds its D/32 scales in one load
         u32x2_t kc[2][KS], vc[VCH];
-        float ksc[2][KS], vsc[VCH];
+        uint32_t ksw[2][(KS + 1) / 2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int64_t key = u.key0 + 16 * st + col;
           const bool ok = key <= p;
 #pragma unroll
-          for (int s = 0; s < KS; ++s) {
+          for (int s = 0; s < KS; ++s)
             kc[st][s] = ok ? *reinterpret_cast<const u32x2_t*>(q8.k + key * D + 32 * s + 8 * lg) : u32x2_t{0u, 0u};
-            ksc[st][s] = ok ? f16_bits_to_f32(q8.ks[key * (D / 32) + s]) : 0.f;
+          if constexpr (KS == 4) {
+            const u32x2_t w = ok ? *reinterpret_cast<const u32x2_t*>(q8.ks + key * 4) : u32x2_t{0u, 0u};
+            ksw[st][0] = w[0];
+            ksw[st][1] = w[1];
+          } else {
+            ksw[st][0] = ok ? *reinterpret_cast<const uint32_t*>(q8.ks + key * 2) : 0u;
           }
         }
+        // V: the unit's 32 x D/32 scales loaded once across the wave (lane l:
+        // row l * KS / 64, two scales), each lane's pair fetched with bpermute
+        constexpr int SPL = 2;  // scales per lane
+        static_assert(kUnit * (D / 32) == SPL * kWave || kUnit * (D / 32) == kWave, "scale layout");
+        const int sl_row = (lane * SPL) / (D / 32);
+        const bool sl_ok = (kUnit * (D / 32) == SPL * kWave || lane < kUnit) && u.key0 + sl_row <= p;
+        const uint32_t vsw =
+            sl_ok ? (kUnit * (D / 32) == SPL * kWave ? *reinterpret_cast<const uint32_t*>(q8.vs + u.key0 * (D / 32) + SPL * lane)
+                                                    : *reinterpret_cast<const uint32_t*>(q8.vs + (u.key0 + lane) * (D / 32)))
+                  : 0u;
 #pragma unroll
         for (int j = 0; j < VCH; ++j) {
           const int ci = lane + kWave * j;
           const int r = ci / (D / 8), c8 = ci % (D / 8);
           const int64_t key = u.key0 + r;
-          const bool ok = key <= p;
-          vc[j] = ok ? *reinterpret_cast<const u32x2_t*>(q8.v + key * D + 8 * c8) : u32x2_t{0u, 0u};
-          vsc[j] = ok ? f16_bits_to_f32(q8.vs[key * (D / 32) + c8 / 4]) : 0.f;
+          vc[j] = key <= p ? *reinterpret_cast<const u32x2_t*>(q8.v + key * D + 8 * c8) : u32x2_t{0u, 0u};
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int s = 0; s < KS; ++s) u.kf[st][s] = dequant8_bf16(kc[st][s], ksc[st][s]);
+          for (int s = 0; s < KS; ++s)
+            u.kf[st][s] = dequant8_bf16(kc[st][s], f16_bits_to_f32((uint16_t)(ksw[st][s / 2] >> (16 * (s % 2)))));
 #pragma unroll
-        for (int j = 0; j < VCH; ++j) u.vr[j] = dequant8_bf16(vc[j], vsc[j]);
+        for (int j = 0; j < VCH; ++j) {
+          const int ci = lane + kWave * j;
+          const int r = ci / (D / 8), c8 = ci % (D / 8);
+          const int si = r * (D / 32) + c8 / 4;  // scale index within the unit
+          const uint32_t wsrc = (uint32_t)__builtin_amdgcn_ds_bpermute((si / SPL) << 2, (int)vsw);
+          const float sc = f16_bits_to_f32((uint16_t)(wsrc >> (16 * (si % SPL))));
+          u.vr[j] = dequant8_bf16(vc[j], sc);
+        }
       } else {
       const uint16_t* kb = kbase + u.key0 * D;
       const uint16_t* vb = vbase + u.key0 * D;
