@@ -14,14 +14,21 @@
 // candidates, ranked by the 64-bit key of qsa_device.h (score descending, id
 // ascending), and writes ids ascending.
 //
-// Three paths:
-//  * tile path (many query rows, prefill): a workgroup takes 16 consecutive
-//    rows of one (b, g), which share the candidate prefix. Candidate chunks
-//    of 64 compressed keys are staged in LDS and scored with fp32 MFMA
-//    (16x16x4, full fp32 products); every 128 candidates each wave updates
-//    four rows' running top sets by threshold selection (the m-th largest
-//    key found bit by bit with ballot counts, no sorting), and the final set
-//    is sorted by id once.
+// Four paths:
+//  * row path (many query rows, top_k <= 16: prefill): a workgroup takes 64
+//    consecutive rows of one (b, g), which share the candidate prefix.
+//    Rounds of 128 compressed keys are staged in LDS and scored with fp32
+//    MFMA (16x16x4, full fp32 products) against the group-summed queries held
+//    in registers; the product layout leaves each lane 16 scores of one row,
+//    which it sorts in registers (bitonic network) and merges into its own
+//    running top-16 list. At the end the lists of a row (4 lanes, 2 waves)
+//    merge pairwise and each lane writes a quarter of the row's selection.
+//  * tile path (many query rows, larger top_k): a workgroup takes 16
+//    consecutive rows of one (b, g). Candidate chunks of 64 compressed keys
+//    are staged in LDS and scored with fp32 MFMA as above; every 128
+//    candidates each wave updates four rows' running top sets by threshold
+//    selection (the m-th largest key found bit by bit with ballot counts, no
+//    sorting), and the final set is sorted by id once.
 //  * split path (few rows, decode): the candidates of a row are cut into
 //    chunks spread over the whole GPU. Each wave streams 64 compressed keys
 //    per step with fully coalesced 16-byte loads (1 KiB per instruction),
@@ -137,6 +144,246 @@ __global__ __launch_bounds__(256) void select_tile_kernel(const T* __restrict__ 
     const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
     finalize_row(set[rr].keys, frame_slots(fr, top_k), fr.forced, top_k, sel + off,
                  sel_scores ? sel_scores + off : nullptr);
+  }
+}
+
+// ------------------------------------------------------------------ row path
+
+constexpr int kRowsPerWg = 64;  // 4 groups of 16 query rows, two waves per group
+constexpr int kRowKeep = 16;    // keys a lane keeps (the path serves top_k <= 16)
+constexpr int kRowRound = 128;  // candidates staged per round: 64 for each wave of a group
+
+template <int D>
+constexpr int rows_lds_bytes() {
+  return (kRowsPerWg + kRowRound) * (D + 4) * (int)sizeof(float);
+}
+
+// Compare-exchange that leaves the larger key in a.
+__device__ __forceinline__ void cx_desc(uint64_t& a, uint64_t& b) {
+  const bool swap = b > a;
+  const uint64_t hi = swap ? b : a;
+  const uint64_t lo = swap ? a : b;
+  a = hi;
+  b = lo;
+}
+
+// Bitonic sort of N keys held in registers, descending.
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&x)[N]) {
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          if ((i & k) == 0) cx_desc(x[i], x[l]);
+          else cx_desc(x[l], x[i]);
+        }
+      }
+}
+
+// a := the N largest of two descending lists a and b, descending. The
+// elementwise maximum of a and reversed b holds them and is bitonic, so one
+// bitonic merge sorts it.
+template <int N>
+__device__ __forceinline__ void merge_top_desc(uint64_t (&a)[N], const uint64_t (&b)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = a[i] > b[N - 1 - i] ? a[i] : b[N - 1 - i];
+#pragma unroll
+  for (int j = N >> 1; j > 0; j >>= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int l = i ^ j;
+      if (l > i) cx_desc(a[i], a[l]);
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(512) void select_rows_kernel(const T* __restrict__ q, const float* __restrict__ k_comp,
+                                                          int32_t* __restrict__ sel, float* __restrict__ sel_scores,
+                                                          int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
+                                                          int hkv, int G, int bs, int top_k, float scale,
+                                                          int keep_tail) {
+  constexpr int QP = D + 4;  // padded row stride (floats): conflict-free 16-byte reads
+  extern __shared__ __align__(16) unsigned char smem[];
+  float(*qbar)[QP] = reinterpret_cast<float(*)[QP]>(smem);
+  float(*kc)[QP] = reinterpret_cast<float(*)[QP]>(smem + kRowsPerWg * QP * sizeof(float));
+  // after the last round the staging area carries the second waves' lists
+  uint64_t(*xl)[kRowKeep] = reinterpret_cast<uint64_t(*)[kRowKeep]>(smem + kRowsPerWg * QP * sizeof(float));
+
+  const int64_t t0 = (int64_t)blockIdx.x * kRowsPerWg;
+  const int g = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int rg = w & 3, half = w >> 2;  // row group, half of each round's candidates
+  const int m = lane & 15, kg = lane >> 4;
+  const int rows = (int)(q_len - t0 < kRowsPerWg ? q_len - t0 : kRowsPerWg);
+
+  // Group-summed queries: a thread's 16-byte chunks (up to two at a time,
+  // every head's load issued before the first add), summed in head order.
+  {
+    constexpr int EPL = 16 / (int)sizeof(T);  // elements per chunk
+    constexpr int CPR = D / EPL;              // chunks per row
+    constexpr int NCH = kRowsPerWg * CPR / 512;
+    constexpr int NB = NCH < 2 ? NCH : 2;
+#pragma unroll
+    for (int c0 = 0; c0 < NCH; c0 += NB) {
+      u32x4_t raw[NB][16];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int idx = tid + 512 * (c0 + i);
+        const int r = idx / CPR, e = (idx % CPR) * EPL;
+        const T* src = q + ((b * q_len + t0 + r) * hq + (int64_t)g * G) * D + e;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j < G && r < rows) raw[i][j] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)j * D);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int idx = tid + 512 * (c0 + i);
+        const int r = idx / CPR, e = (idx % CPR) * EPL;
+        float acc[EPL];
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) acc[x] = 0.f;
+        if (r < rows) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if (j < G) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                if constexpr (EPL == 8) {
+                  acc[2 * x] += bf16_lo(raw[i][j][x]);
+                  acc[2 * x + 1] += bf16_hi(raw[i][j][x]);
+                } else {
+                  acc[x] += __uint_as_float(raw[i][j][x]);
+                }
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < EPL; x += 4)
+          *reinterpret_cast<f32x4_t*>(&qbar[r][e + x]) = f32x4_t{acc[x], acc[x + 1], acc[x + 2], acc[x + 3]};
+      }
+    }
+  }
+  // candidates of every row are below the last row's candidate count
+  const int64_t cand_end = row_frame(q_pos0 + t0 + rows - 1, bs, keep_tail).n_cand;
+  const int r = 16 * rg + m;  // this lane's row
+  const bool row_ok = r < rows;
+  const Frame fr = row_frame(q_pos0 + t0 + (row_ok ? r : 0), bs, keep_tail);
+  const int64_t n_cand = row_ok ? fr.n_cand : 0;
+  const float* kc_src = k_comp + ((b * hkv + g) * nb_cap) * D;
+
+  uint64_t top[kRowKeep];
+#pragma unroll
+  for (int i = 0; i < kRowKeep; ++i) top[i] = 0ull;
+  float qr[D / 4];  // the row's query sum, dims 16u + 4kg + e at qr[4u + e]
+  for (int64_t c0 = 0; c0 < cand_end; c0 += kRowRound) {
+    if (c0 > 0) __syncthreads();  // the previous round's keys fully read
+    {
+      constexpr int NK = kRowRound * D / 4 / 512;  // 16-byte chunks per thread, all loads first
+      f32x4_t v[NK];
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int idx = tid + 512 * i;
+        const int c = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
+        v[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (c0 + c < cand_end) v[i] = *reinterpret_cast<const f32x4_t*>(kc_src + (c0 + c) * D + e4);
+      }
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int idx = tid + 512 * i;
+        *reinterpret_cast<f32x4_t*>(&kc[idx / (D / 4)][(idx % (D / 4)) * 4]) = v[i];
+      }
+    }
+    __syncthreads();
+    if (c0 == 0) {
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&qbar[r][16 * u + 4 * kg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qr[4 * u + e] = a[e];
+      }
+    }
+    // scores of candidates c0 + 64 half + 16 ct + 4 kg + v for this lane's row
+    // (keys as operand A, queries as operand B: output column = query row)
+    uint64_t x[kRowKeep];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < D / 16; ++u) {
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&kc[64 * half + 16 * ct + m][16 * u + 4 * kg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], qr[4 * u + e], acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t cand = c0 + 64 * half + 16 * ct + 4 * kg + v;
+        x[4 * ct + v] = cand < n_cand ? make_key(acc[v] * scale, (int)cand) : 0ull;
+      }
+    }
+    sort_desc<kRowKeep>(x);
+    merge_top_desc<kRowKeep>(top, x);
+  }
+  // the row's four lanes, then its two waves, to one list
+#pragma unroll
+  for (int j = 16; j <= 32; j <<= 1) {
+    uint64_t o[kRowKeep];
+#pragma unroll
+    for (int i = 0; i < kRowKeep; ++i) o[i] = xor_lane_u64(top[i], j);
+    merge_top_desc<kRowKeep>(top, o);
+  }
+  __syncthreads();  // every wave is done with the staging area
+  if (half == 1 && kg == 0) {
+#pragma unroll
+    for (int i = 0; i < kRowKeep; ++i) xl[r][i] = top[i];
+  }
+  __syncthreads();
+  if (half == 1 || !row_ok) return;
+  {
+    uint64_t o[kRowKeep];
+#pragma unroll
+    for (int i = 0; i < kRowKeep; ++i) o[i] = xl[r][i];
+    merge_top_desc<kRowKeep>(top, o);
+  }
+
+  // Selection in ascending id order: entry i < slots is kept key i, entry
+  // slots the forced block; lane kg places entries 4kg .. 4kg+3 at their
+  // rank among the ids and pads positions past the real entries with -1.
+  const int slots = frame_slots(fr, top_k);
+  const int n_real = slots + (fr.forced >= 0 ? 1 : 0);
+  int ids[kRowKeep];
+#pragma unroll
+  for (int i = 0; i < kRowKeep; ++i)
+    ids[i] = i < slots ? key_id(top[i]) : ((i == slots && fr.forced >= 0) ? fr.forced : 0x7FFFFFFF);
+  const int64_t off = ((b * q_len + t0 + r) * hkv + g) * top_k;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int j = 4 * kg + v;
+    uint64_t key_j = 0ull;
+    int id_j = 0x7FFFFFFF;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (kg == c) {
+        key_j = top[4 * c + v];
+        id_j = ids[4 * c + v];
+      }
+    }
+    const float sc_j = j < slots ? key_score(key_j) : __builtin_inff();
+    if (j < n_real) {
+      int rank = 0;
+#pragma unroll
+      for (int i = 0; i < kRowKeep; ++i) rank += ids[i] < id_j ? 1 : 0;
+      sel[off + rank] = id_j;
+      if (sel_scores) sel_scores[off + rank] = sc_j;
+    } else if (j < top_k) {
+      sel[off + j] = -1;
+      if (sel_scores) sel_scores[off + j] = -__builtin_inff();
+    }
   }
 }
 
@@ -422,6 +669,16 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
     if (!pick) return hipSuccess;
     hipLaunchKernelGGL(select_large_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, st, sel, sel_scores,
                        wss, wsl, q_len, q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, plan.n_chunks);
+    return hipGetLastError();
+  }
+  if (plan.tiled && s.top_k <= kRowKeep) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&select_rows_kernel<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        rows_lds_bytes<D>());
+    if (attr != hipSuccess) return attr;
+    dim3 grid((unsigned)((q_len + kRowsPerWg - 1) / kRowsPerWg), (unsigned)s.hkv, (unsigned)s.batch);
+    hipLaunchKernelGGL((select_rows_kernel<T, D>), grid, dim3(512), rows_lds_bytes<D>(), st, q, k_comp, sel,
+                       sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, s.scale, s.keep_tail);
     return hipGetLastError();
   }
   if (plan.tiled) {

@@ -49,6 +49,7 @@ PREFILL_CASES = [
     W(kv_len=600, top_k=3, block_size=128),
     W(kv_len=700, top_k=1),                                   # own block only
     W(kv_len=700, top_k=64, block_size=32),                    # k beyond the candidates: dense
+    W(kv_len=3000, top_k=24, block_size=32),                   # top_k > 16: threshold-select tile path
     W(kv_len=530, n_q_heads=4, n_kv_heads=4, top_k=5),         # G = 1
     W(kv_len=530, n_q_heads=8, n_kv_heads=4, top_k=5),         # G = 2
     W(kv_len=530, n_q_heads=8, n_kv_heads=2, top_k=5),         # G = 4
@@ -85,11 +86,20 @@ def test_prefill_parity(w):
     log(f"  {st}")
 
 
-def test_chunked_prefill_parity():
+CHUNKED_CASES = [
+    (W(batch=2, kv_len=900, top_k=6), 333),
+    # long prefixes: several 128-candidate rounds of the row selection path
+    (W(batch=1, kv_len=64 * 300 + 5, top_k=16), 64 * 300 - 100),
+    (W(batch=2, kv_len=32 * 400 + 31, top_k=9, head_dim=64, block_size=32, keep_tail=True), 32 * 400 - 70),
+    (W(batch=1, kv_len=64 * 260, top_k=12, dtype="f32", sigma=1.0), 64 * 260 - 129),
+]
+
+
+@pytest.mark.parametrize("c", CHUNKED_CASES, ids=lambda c: f"{case_id(c[0])}-from{c[1]}")
+def test_chunked_prefill_parity(c):
     """Query rows [q_pos0, kv_len) over a cache that already holds the earlier keys."""
-    w = W(batch=2, kv_len=900, top_k=6)
+    w, q_pos0 = c
     case = Case(w, seed=2)
-    q_pos0 = 333
     sel, out, scores, _ = run_prefill(case, q_pos0=q_pos0, q_rows=slice(q_pos0, w.kv_len))
     # oracle rows are indexed by absolute position: shift the query view
     case.Q = case.Q[:, q_pos0:]
