@@ -23,6 +23,44 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
 
+// Decode-step workspace: two arrival-counter areas at fixed offsets (the
+// fused step's or the attention's counters, then the split selection's),
+// then scratch whose size follows kv_len (the selection's chunk lists or
+// scores, then the attention's slice states). Whatever path a step takes,
+// its counters live in those two areas, which every call leaves at zero, so
+// one workspace zero-filled once serves a decode loop whose kv_len, and
+// with it the path, changes from step to step.
+struct StepWs {
+  size_t sel_off;   // the selection's workspace (a split selection's counters land on the second area)
+  size_t part_off;  // the attention's slice states
+  size_t total;     // 0 when the step needs no workspace
+};
+
+StepWs step_ws(const Dims& s, int64_t kv_len) {
+  StepWs w{};
+  const size_t cnt = qsa::counter_bytes((int64_t)s.batch * s.hkv);
+  const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
+  size_t att = 0, sel_ws = 0, sel_scratch = 0;
+  w.sel_off = cnt;
+  if (sp.fused) {
+    att = sp.ws_bytes;
+  } else {
+    const qsa::SelectPlan sel_plan = qsa::plan_select(s, 1, kv_len - 1);
+    sel_ws = sel_plan.ws_bytes;
+    if (sel_plan.large) {  // scores and lists, no counters
+      w.sel_off = 2 * cnt;
+      sel_scratch = sel_ws;
+    } else {
+      sel_scratch = sel_ws > cnt ? sel_ws - cnt : 0;
+    }
+    if (s.dtype == QSA_BF16)
+      att = sel_plan.large ? qsa::plan_pick_attend(s, sel_plan.n_chunks).ws_bytes : qsa::plan_decode(s, kv_len).ws_bytes;
+  }
+  w.part_off = 2 * cnt + qsa::align_up(sel_scratch, 256);
+  w.total = (att == 0 && sel_ws == 0) ? 0 : w.part_off + (att > cnt ? att - cnt : 0);
+  return w;
+}
+
 // Shape checks shared by every entry point.
 qsa_status check_shape(const qsa_shape* sh, Dims* out) {
   if (!sh) return QSA_ERR_INVALID;
@@ -106,15 +144,7 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       return qsa::plan_prefill(s, q_len, kv_len - q_len).ws_bytes;
     case QSA_OP_DECODE_STEP: {
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
-      const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
-      if (sp.fused) return sp.ws_bytes;
-      // the separate calls, each on its own part (the decode part keeps
-      // counters at its start that the selection must not overwrite)
-      const qsa::SelectPlan sel_plan = qsa::plan_select(s, 1, kv_len - 1);
-      const size_t a = qsa::align_up(sel_plan.ws_bytes, 256);
-      if (s.dtype == QSA_BF16 && sel_plan.large) return a + qsa::plan_pick_attend(s, sel_plan.n_chunks).ws_bytes;
-      const size_t d = s.dtype == QSA_BF16 ? qsa::plan_decode(s, kv_len).ws_bytes : 0;
-      return a + d;
+      return step_ws(s, kv_len).total;
     }
     case QSA_OP_DECODE_STEP_RAGGED: {
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
@@ -178,7 +208,9 @@ qsa_status qsa_sparse_attn_decode(const qsa_shape* shape, const void* q, const v
   const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len);
   if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
-  return hip_status(qsa::launch_decode(s, plan, q, k, v, kv_len, kv_cap, sel, out, ws, hs));
+  // arrival counters at the start of the workspace, the slice states after them
+  char* part = ws ? static_cast<char*>(ws) + qsa::counter_bytes((int64_t)s.batch * s.hkv) : nullptr;
+  return hip_status(qsa::launch_decode(s, plan, q, k, v, kv_len, kv_cap, sel, out, ws, part, hs));
 }
 
 qsa_status qsa_sparse_attn_prefill(const qsa_shape* shape, const void* q, const void* k, const void* v,
@@ -223,37 +255,41 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
+  const StepWs lay = step_ws(s, kv_len);
+  if (lay.total > 0 && (!ws || ws_bytes < lay.total || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  char* sel_ws = base ? base + lay.sel_off : nullptr;
+  char* part = base ? base + lay.part_off : nullptr;
   if (sp.fused) {
     if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-    if (sp.ws_bytes > 0 && (!ws || ws_bytes < sp.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
-    return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, hs));
+    return hip_status(
+        qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, base, part, hs));
   }
   // separate launches: the selection (which also compresses the block the new
   // token closes, if any, before scoring it), then the attention
-  const size_t need = qsa_workspace_bytes(shape, QSA_OP_DECODE_STEP, 1, kv_len);
-  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return QSA_ERR_WORKSPACE;
   if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
   const qsa::SelectPlan sel_plan = qsa::plan_select(s, 1, kv_len - 1);
   if ((int64_t)s.batch * s.hkv * (sel_plan.n_chunks > 0 ? sel_plan.n_chunks : 1) > 0x7FFFFFFF)
     return QSA_ERR_UNSUPPORTED;
-  const size_t sel_part = qsa::align_up(sel_plan.ws_bytes, 256);
   const int64_t close_block = kv_len % s.bs == 0 ? kv_len / s.bs - 1 : -1;
   if (s.dtype == QSA_BF16 && sel_plan.large) {
     // the score pass, then one kernel that picks each row's blocks and
-    // attends over them (its counters and slice states after the scores)
+    // attends over them
     const qsa::PickAttendPlan pa = qsa::plan_pick_attend(s, sel_plan.n_chunks);
     if ((int64_t)s.batch * s.hkv * pa.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-    st = hip_status(qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores, ws, hs, k,
+    st = hip_status(qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores, sel_ws, hs, k,
                                        close_block, false));
     if (st != QSA_OK) return st;
-    return hip_status(qsa::launch_pick_attend(s, pa, q, k, v, sel, sel_scores, ws, out,
-                                              static_cast<char*>(ws) + sel_part, kv_len, kv_cap, hs));
+    return hip_status(
+        qsa::launch_pick_attend(s, pa, q, k, v, sel, sel_scores, sel_ws, out, base, part, kv_len, kv_cap, hs));
   }
   st = hip_status(
-      qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores, ws, hs, k, close_block));
+      qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores, sel_ws, hs, k, close_block));
   if (st != QSA_OK) return st;
-  void* ws_dec = ws ? static_cast<char*>(ws) + sel_part : nullptr;
-  return qsa_sparse_attn_decode(shape, q, k, v, kv_len, kv_cap, sel, out, ws_dec, need - sel_part, stream);
+  if (s.dtype == QSA_F32) return qsa_sparse_attn_decode(shape, q, k, v, kv_len, kv_cap, sel, out, nullptr, 0, stream);
+  const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len);
+  if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  return hip_status(qsa::launch_decode(s, plan, q, k, v, kv_len, kv_cap, sel, out, base, part, hs));
 }
 
 qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const void* k, const void* v,
@@ -274,8 +310,9 @@ qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const v
   if (!sp.fused) return QSA_ERR_UNSUPPORTED;  // only the fused kernel reads per-sequence lengths
   if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   if (sp.ws_bytes > 0 && (!ws || ws_bytes < sp.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  char* part = ws ? static_cast<char*>(ws) + qsa::counter_bytes((int64_t)s.batch * s.hkv) : nullptr;
   return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, max_kv_len, kv_cap, sel, sel_scores, out, ws,
-                                            static_cast<hipStream_t>(stream), kv_lens));
+                                            part, static_cast<hipStream_t>(stream), kv_lens));
 }
 
 namespace {

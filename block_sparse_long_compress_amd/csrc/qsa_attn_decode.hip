@@ -147,13 +147,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
 
 template <int D>
 hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
-                    int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* ws, hipStream_t st) {
+                    int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, uint32_t* counters, float* part,
+                    hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const float scale_log2 = s.scale * 1.4426950408889634f;
   auto kern = s.bs < kUnit ? decode_attn_kernel<D, true> : decode_attn_kernel<D, false>;
-  uint32_t* counters = static_cast<uint32_t*>(ws);
-  float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows))
-                                 : nullptr;
+  if (plan.n_split == 1) part = nullptr;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * plan.n_split)), dim3(256), 0, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sel,
                      static_cast<uint16_t*>(out), part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
@@ -184,9 +183,12 @@ DecodePlan plan_decode(const Dims& s, int64_t kv_len) {
 }
 
 hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
-                         int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* ws, hipStream_t st) {
-  return s.d == 64 ? launch_d<64>(s, plan, q, k, v, kv_len, kv_cap, sel, out, ws, st)
-                   : launch_d<128>(s, plan, q, k, v, kv_len, kv_cap, sel, out, ws, st);
+                         int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* counters, void* part,
+                         hipStream_t st) {
+  uint32_t* c = static_cast<uint32_t*>(counters);
+  float* pt = static_cast<float*>(part);
+  return s.d == 64 ? launch_d<64>(s, plan, q, k, v, kv_len, kv_cap, sel, out, c, pt, st)
+                   : launch_d<128>(s, plan, q, k, v, kv_len, kv_cap, sel, out, c, pt, st);
 }
 
 }  // namespace qsa

@@ -229,10 +229,10 @@ __global__ __launch_bounds__(kStepWaves * kWave) void pick_attend_kernel(
 template <int D>
 hipError_t launch_pick_attend_d(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
                                 int32_t* sel, float* sel_scores, const uint32_t* ws_scores, const uint64_t* ws_lists,
-                                void* out, void* ws, int64_t kv_len, int64_t kv_cap, hipStream_t st) {
+                                void* out, uint32_t* counters, float* part, int64_t kv_len, int64_t kv_cap,
+                                hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
-  uint32_t* counters = static_cast<uint32_t*>(ws);
-  float* part = pa.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows)) : nullptr;
+  if (pa.n_split == 1) part = nullptr;
   auto kern = s.bs < kUnit ? pick_attend_kernel<D, true> : pick_attend_kernel<D, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * pa.n_split)), dim3(kStepWaves * kWave), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
@@ -245,12 +245,12 @@ hipError_t launch_pick_attend_d(const Dims& s, const PickAttendPlan& pa, const v
 template <int D>
 hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                          float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out,
-                         void* ws, const int32_t* kv_lens, hipStream_t st) {
+                         uint32_t* counters, float* part, const int32_t* kv_lens,
+                         hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const int64_t n_wg = plan.n_split > 1 ? 8 * ((rows + 7) / 8) * plan.n_split : rows;
   const dim3 grid((unsigned)n_wg), block(kStepWaves * kWave);
-  uint32_t* counters = static_cast<uint32_t*>(ws);
-  float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows)) : nullptr;
+  if (plan.n_split == 1) part = nullptr;
   const auto* qp = static_cast<const uint16_t*>(q);
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
@@ -314,10 +314,12 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged) {
 
 hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                               float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
-                              void* out, void* ws, hipStream_t st, const int32_t* kv_lens) {
+                              void* out, void* counters, void* part, hipStream_t st, const int32_t* kv_lens) {
+  uint32_t* c = static_cast<uint32_t*>(counters);
+  float* pt = static_cast<float*>(part);
   return s.d == 64
-             ? launch_step_d<64>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, kv_lens, st)
-             : launch_step_d<128>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, ws, kv_lens, st);
+             ? launch_step_d<64>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, c, pt, kv_lens, st)
+             : launch_step_d<128>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, c, pt, kv_lens, st);
 }
 
 PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks) {
@@ -334,14 +336,17 @@ PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks) {
 }
 
 hipError_t launch_pick_attend(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
-                              int32_t* sel, float* sel_scores, const void* ws_select, void* out, void* ws,
-                              int64_t kv_len, int64_t kv_cap, hipStream_t st) {
+                              int32_t* sel, float* sel_scores, const void* ws_select, void* out, void* counters,
+                              void* part, int64_t kv_len, int64_t kv_cap, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   // the score pass's workspace: scores [rows][n_chunks * 256], then the lists
   const uint32_t* wss = reinterpret_cast<const uint32_t*>(ws_select);
   const uint64_t* wsl = reinterpret_cast<const uint64_t*>(wss + rows * pa.n_chunks * kLargeChunk);
-  return s.d == 64 ? launch_pick_attend_d<64>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, ws, kv_len, kv_cap, st)
-                   : launch_pick_attend_d<128>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, ws, kv_len, kv_cap, st);
+  uint32_t* c = static_cast<uint32_t*>(counters);
+  float* pt = static_cast<float*>(part);
+  return s.d == 64 ? launch_pick_attend_d<64>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, c, pt, kv_len, kv_cap, st)
+                   : launch_pick_attend_d<128>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, c, pt, kv_len, kv_cap,
+                                               st);
 }
 
 }  // namespace qsa

@@ -74,8 +74,12 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(const Dims& s, int64_t kv_len);
 
+// counters: the plan's arrival counters (counter_bytes(rows), zero between
+// calls); part: its slice states (ws_bytes past the counters). The decode
+// call keeps both in one workspace, the decode step at separate places.
 hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
-                         int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* ws, hipStream_t st);
+                         int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* counters, void* part,
+                         hipStream_t st);
 // Decode attention over the rotated 8-bit cache (same plan and workspace as
 // launch_decode; Bs >= 32).
 hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q, const int8_t* kq, const int8_t* vq,
@@ -107,9 +111,11 @@ struct StepPlan {
 StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged = false);
 // kv_lens (device, [batch], nullable): per-sequence lengths, each clamped
 // into [1, kv_len]; null means every sequence has kv_len.
+// counters / part: as for launch_decode (used when plan.n_split > 1).
 hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                               float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
-                              void* out, void* ws, hipStream_t st, const int32_t* kv_lens = nullptr);
+                              void* out, void* counters, void* part, hipStream_t st,
+                              const int32_t* kv_lens = nullptr);
 
 // Decode step with k > 64 (bf16): the selection's score pass, then one kernel
 // that picks each row's ids and attends over them (S workgroups per row).
@@ -117,12 +123,13 @@ struct PickAttendPlan {
   int blocks_per_wg;
   int n_split;
   int64_t n_chunks;  // of the score pass
-  size_t ws_bytes;   // arrival counters and slice states (after the score pass's part)
+  size_t ws_bytes;   // arrival counters (counter_bytes(rows)), then slice states
 };
 PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks);
+// counters / part: as for launch_decode.
 hipError_t launch_pick_attend(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
-                              int32_t* sel, float* sel_scores, const void* ws_select, void* out, void* ws,
-                              int64_t kv_len, int64_t kv_cap, hipStream_t st);
+                              int32_t* sel, float* sel_scores, const void* ws_select, void* out, void* counters,
+                              void* part, int64_t kv_len, int64_t kv_cap, hipStream_t st);
 
 // Generic float32 attention (one wave per query row); used for dtype QSA_F32.
 hipError_t launch_attn_f32(const Dims& s, const float* q, const float* k, const float* v, int64_t q_len,

@@ -164,7 +164,10 @@ def test_ragged_decode_step_arguments(qsa):
     big = 1 << 30
     INV, UNS, WS = 1, 2, 3
     ws = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 131072)
-    assert ws == qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 4096)  # same per-row plan
+    # same per-row plan; the plain step's workspace also reserves the split
+    # selection's counter area (one 4-byte counter per row, 256-byte rounded)
+    cnt = (4 * sh.batch * sh.n_kv_heads + 255) // 256 * 256
+    assert ws > 0 and qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 4096) == ws + cnt
     call = lib.qsa_decode_step_ragged
     assert call(shr, P, P, P, P, N, 64, 64, P, N, P, P, big, N) == INV           # no lengths
     assert call(shr, P, P, P, P, MIS4, 64, 64, P, N, P, P, big, N) == INV        # lengths not 4-byte aligned

@@ -258,6 +258,42 @@ def test_workspace_reuse_across_decode_steps(w, steps):
     log(f"  {st}")
 
 
+def test_decode_step_workspace_reuse():
+    """A decode loop on one zero-initialised workspace whose steps switch
+    between the fused kernel (short rows, slices with arrival counters) and
+    the separate calls (split selection and split attention, each with its
+    counters): every step equals a call with a fresh workspace, so the
+    counter areas sit where every path expects them and every call leaves
+    them at zero."""
+    w = W(mode="decode", batch=1, kv_len=32 * 5000 + 9, top_k=32, block_size=32, head_dim=64, n_q_heads=8,
+          n_kv_heads=1)
+    case = Case(w, seed=9)
+    b, hq, d, bs = w.batch, w.n_q_heads, w.head_dim, w.block_size
+    shape = qsa.shape_for(case.q, case.k, bs, w.top_k)
+    steps = [40000, 160009, 160000, 50001, 159999, 120001, 140000, 30000, 160009]
+    fused = [qsa.qsa_decode_step_fused(shape, n) for n in steps]
+    assert any(fused) and not all(fused), fused
+    n_ws = max(qsa.qsa_workspace_bytes(shape, qsa.QSA_OP_DECODE_STEP, 1, n) for n in steps)
+    ws = torch.zeros(n_ws, dtype=torch.uint8, device="cuda")
+    q = case.q.view(b, hq, d)
+    for n in steps:
+        log(f"decode step workspace reuse kv_len={n}")
+        outs = []
+        for wsx in (ws, None):
+            k_comp = torch.zeros(b, w.n_kv_heads, w.kv_len // bs, d, device="cuda")
+            qsa.qsa_compress_keys(shape, case.k, n - 1, k_comp)
+            sel = torch.empty(b, w.n_kv_heads, w.top_k, dtype=torch.int32, device="cuda")
+            out = torch.empty_like(q)
+            qsa.qsa_decode_step(shape, q, case.k, case.v, k_comp, n, sel, out, ws=wsx)
+            outs.append((sel, out))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0], outs[1][0])
+        assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    rows = [(bb, 0, g) for bb in range(b) for g in range(w.n_kv_heads)]
+    st = check_rows(case, outs[0][0].cpu().numpy()[:, None], from_device(outs[0][1])[:, None], rows, steps[-1] - 1)
+    log(f"  {st}")
+
+
 def _restore_keys(case: Case, K32: np.ndarray) -> None:
     """Replace the case's keys by ``K32`` rounded to its storage type (host view and device copy)."""
     w = case.w
@@ -321,6 +357,12 @@ STEP_CASES = [
     W(mode="decode", batch=40, kv_len=5000, top_k=16, n_q_heads=8, n_kv_heads=2),  # 80 rows: fused though long
     # shapes the fused kernel leaves to the separate calls
     W(mode="decode", batch=1, kv_len=200000, top_k=16),                     # long rows, few of them
+    # long rows, k <= 64: chunk lists merged in every attention slice
+    W(mode="decode", batch=1, kv_len=32 * 5000 + 9, top_k=32, block_size=32, head_dim=64, n_q_heads=8,
+      n_kv_heads=1),                                                         # 20 lists of 31
+    W(mode="decode", batch=2, kv_len=64 * 3200, top_k=16),                  # closes a block
+    W(mode="decode", batch=1, kv_len=32 * 5000, top_k=32, block_size=32, head_dim=64, n_q_heads=8, n_kv_heads=1,
+      keep_tail=True),                                                       # the closed block competes
     W(mode="decode", batch=1, kv_len=4 * 20000, top_k=513, block_size=4, keep_tail=True),
     W(mode="decode", batch=2, kv_len=2222, dtype="f32", sigma=1.0, top_k=5),
     W(mode="decode", batch=2, kv_len=2240, dtype="f32", sigma=1.0, top_k=5, keep_tail=True),   # closes a block
