@@ -71,6 +71,21 @@ __device__ __forceinline__ void load_q_operands(const uint16_t* __restrict__ q_h
   }
 }
 
+// Q operands in the 8-bit cache's dim order: step s = 2t + h takes, in lane
+// group lg, dims 64 t + 16 lg + 8 h .. +7 (a lane's 16-byte code load covers
+// both steps of a pair). Any order of the dims gives the same dot products.
+template <int D>
+__device__ __forceinline__ void load_q8_query_operands(const uint16_t* __restrict__ q_heads, int G,
+                                                       u32x4_t (&qf)[D / 32]) {
+  const int lane = lane_id(), lg = lane / 16, col = lane % 16;
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    qf[s] = u32x4_t{0u, 0u, 0u, 0u};
+    if (col < G)
+      qf[s] = *reinterpret_cast<const u32x4_t*>(q_heads + (int64_t)col * D + 64 * (s / 2) + 16 * lg + 8 * (s % 2));
+  }
+}
+
 // Units idx = first, first + stride, ... of a slice of n_e selection entries
 // (entry j of the slice in lane j's sel_mine, -1 for padding), attended by
 // one wave into (m_run, l_run, o). kbase, vbase point at position 0 of the
@@ -139,27 +154,31 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
       if (u.key0 > p) return;
       u.ok = true;
       if constexpr (Q8) {
-        // the same operands from the codes: 8 codes (one 32-value scale) per fragment
-        // K: each lane's key row holds its D/32 scales in one load
-        u32x2_t kc[2][KS], vc[VCH];
-        uint32_t ksw[2][(KS + 1) / 2];
+        // K from the codes, 16 per lane and load: the lane's row (16 st +
+        // col) at bytes 64 t + 16 lg .. +15, which are the dims of operand
+        // steps s = 2t (first 8) and 2t + 1 (last 8) in this cache's dim
+        // order (load_q8_query_operands gives the query the same order), all
+        // in scale group 2t + lg/2. The unit's 32 x D/32 key scales are
+        // loaded once across the wave (lane l: bytes 4l .. 4l+3) and each
+        // lane's scales fetched with bpermute.
+        static_assert(KS % 2 == 0, "two operand steps per 16-byte load");
+        u32x4_t kc16[2][KS / 2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int64_t key = u.key0 + 16 * st + col;
           const bool ok = key <= p;
 #pragma unroll
-          for (int s = 0; s < KS; ++s)
-            kc[st][s] = ok ? *reinterpret_cast<const u32x2_t*>(q8.k + key * D + 32 * s + 8 * lg) : u32x2_t{0u, 0u};
-          if constexpr (KS == 4) {
-            const u32x2_t w = ok ? *reinterpret_cast<const u32x2_t*>(q8.ks + key * 4) : u32x2_t{0u, 0u};
-            ksw[st][0] = w[0];
-            ksw[st][1] = w[1];
-          } else {
-            ksw[st][0] = ok ? *reinterpret_cast<const uint32_t*>(q8.ks + key * 2) : 0u;
-          }
+          for (int t = 0; t < KS / 2; ++t)
+            kc16[st][t] = ok ? *reinterpret_cast<const u32x4_t*>(q8.k + key * D + 64 * t + 16 * lg)
+                             : u32x4_t{0u, 0u, 0u, 0u};
         }
+        constexpr int KSW = kUnit * (D / 32) / 2;  // 32-bit words of the unit's key scales
+        const uint32_t ksw_all = (lane < KSW && u.key0 + (2 * lane) / (D / 32) <= p)
+                                     ? *reinterpret_cast<const uint32_t*>(q8.ks + u.key0 * (D / 32) + 2 * lane)
+                                     : 0u;
         // V: the unit's 32 x D/32 scales loaded once across the wave (lane l:
         // row l * KS / 64, two scales), each lane's pair fetched with bpermute
+        u32x2_t vc[VCH];
         constexpr int SPL = 2;  // scales per lane
         static_assert(kUnit * (D / 32) == SPL * kWave || kUnit * (D / 32) == kWave, "scale layout");
         const int sl_row = (lane * SPL) / (D / 32);
@@ -178,8 +197,15 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int s = 0; s < KS; ++s)
-            u.kf[st][s] = dequant8_bf16(kc[st][s], f16_bits_to_f32((uint16_t)(ksw[st][s / 2] >> (16 * (s % 2)))));
+          for (int t = 0; t < KS / 2; ++t) {
+            const int si = (16 * st + col) * (D / 32) + 2 * t + lg / 2;  // scale index within the unit
+            const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((si / 2) << 2, (int)ksw_all);
+            const float sc = f16_bits_to_f32((uint16_t)(w >> (16 * (si % 2))));
+            u.kf[st][2 * t] = dequant8_bf16(u32x2_t{kc16[st][t][0], kc16[st][t][1]}, sc);
+            u.kf[st][2 * t + 1] = dequant8_bf16(u32x2_t{kc16[st][t][2], kc16[st][t][3]}, sc);
+          }
+        // widened V goes straight to the wave's staging slice (the previous
+        // unit's reads of it ended at its closing wave barrier)
 #pragma unroll
         for (int j = 0; j < VCH; ++j) {
           const int ci = lane + kWave * j;
@@ -187,7 +213,7 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
           const int si = r * (D / 32) + c8 / 4;  // scale index within the unit
           const uint32_t wsrc = (uint32_t)__builtin_amdgcn_ds_bpermute((si / SPL) << 2, (int)vsw);
           const float sc = f16_bits_to_f32((uint16_t)(wsrc >> (16 * (si % SPL))));
-          u.vr[j] = dequant8_bf16(vc[j], sc);
+          *reinterpret_cast<u32x4_t*>(vs + r * RS + 16 * c8) = dequant8_bf16(vc[j], sc);
         }
       } else {
       const uint16_t* kb = kbase + u.key0 * D;
@@ -213,11 +239,13 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
   };
   auto consume = [&](const Unit& u) {
     if (!u.ok) return;
+    if constexpr (!Q8) {  // (the 8-bit fetch stages V itself)
 #pragma unroll
-    for (int j = 0; j < VCH; ++j) {
-      const int ci = lane + kWave * j;
-      const int r = ci / (D / 8), c8 = ci % (D / 8);
-      *reinterpret_cast<u32x4_t*>(vs + r * RS + 16 * c8) = u.vr[j];
+      for (int j = 0; j < VCH; ++j) {
+        const int ci = lane + kWave * j;
+        const int r = ci / (D / 8), c8 = ci % (D / 8);
+        *reinterpret_cast<u32x4_t*>(vs + r * RS + 16 * c8) = u.vr[j];
+      }
     }
 
     f32x4_t sacc[2];

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void decode_attn_q8_kernel(
   }
   __syncthreads();
   u32x4_t qf[D / 32];
-  load_q_operands<D>(qrot, G, qf);
+  load_q8_query_operands<D>(qrot, G, qf);  // the cache's dim order (attend_units' 8-bit loads)
 
   float m_run = -__builtin_inff(), l_run = 0.f;
   f32x4_t o[DT];
