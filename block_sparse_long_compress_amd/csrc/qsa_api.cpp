@@ -138,7 +138,8 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       return qsa::plan_select(s, q_len, kv_len - q_len).ws_bytes;
     case QSA_OP_DECODE:
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
-      return s.dtype == QSA_BF16 ? qsa::plan_decode(s, kv_len).ws_bytes : 0;
+      // the narrow plan's (the 8-bit decode's), which covers the bf16 decode's too
+      return s.dtype == QSA_BF16 ? qsa::plan_decode(s, kv_len, false).ws_bytes : 0;
     case QSA_OP_PREFILL:
       if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
       return qsa::plan_prefill(s, q_len, kv_len - q_len).ws_bytes;
@@ -401,7 +402,7 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
   if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
   if (s.dtype != QSA_BF16 || s.bs < 32) return QSA_ERR_UNSUPPORTED;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
-  const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len);
+  const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len, false);  // 4-wave slices at every row count
   if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
   return hip_status(qsa::launch_decode_q8(s, plan, q, k_q, v_q, k_scales, v_scales, kv_len, kv_cap, sel, out, ws,

@@ -6,11 +6,13 @@
 // The per-wave unit loop (bf16 MFMA, float32 online softmax, gathered units
 // for blocks shorter than 32 keys) is in qsa_decode_unit.h.
 //
-// Grid: one workgroup (4 waves) per (sequence, KV head, slice of the
-// selection list). Waves take units round-robin; the workgroup merges its
-// waves' partial softmax states in LDS and writes the output directly when a
-// row has one slice. Otherwise it writes its partial state to the workspace
-// at the device-coherent level and takes a ticket from the row's arrival
+// Grid: one workgroup per (sequence, KV head, slice of the selection list):
+// 4 waves on slices of a few blocks when the rows are few, 8 waves on the
+// whole selection when the rows alone fill the GPU (as the fused decode
+// step). Waves take units round-robin; the workgroup merges its waves'
+// partial softmax states in LDS and writes the output directly when a row
+// has one slice. Otherwise it writes its partial state to the workspace at
+// the device-coherent level and takes a ticket from the row's arrival
 // counter; the last workgroup of the row merges all slices in slice order
 // and resets the counter to zero. The merge order is fixed, so results are
 // bitwise reproducible whichever workgroup arrives last.
@@ -21,24 +23,21 @@
 namespace qsa {
 namespace {
 
-template <int D>
+template <int D, int NW>
 struct DecodeSmem {
   static constexpr int RS = kStageRowBytes<D>;
-  static constexpr int kStage = 4 * kUnit * RS;
-  static constexpr int kComb = 4 * (32 + 16 * D) * 4;
+  static constexpr int kStage = NW * kUnit * RS;          // V staging, one 32-row slice per wave
+  static constexpr int kComb = NW * (32 + 16 * D) * 4;    // the waves' softmax states
   static constexpr int kBytes = kStage > kComb ? kStage : kComb;
 };
 
-template <int D, bool GATHER>
-__global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v, const int32_t* __restrict__ sel,
-                                                          uint16_t* __restrict__ out, float* __restrict__ part,
-                                                          uint32_t* __restrict__ counters, int64_t kv_len,
-                                                          int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k,
-                                                          float scale_log2, int bpw, int n_split) {
-  using SM = DecodeSmem<D>;
-  constexpr int RS = SM::RS;
-  constexpr int KS = D / 32;  // 32-wide K steps of the QK^T product
+template <int D, bool GATHER, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ sel, uint16_t* __restrict__ out, float* __restrict__ part,
+    uint32_t* __restrict__ counters, int64_t kv_len, int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k,
+    float scale_log2, int bpw, int n_split) {
+  using SM = DecodeSmem<D, NW>;
   constexpr int DT = D / 16;  // 16-wide dim tiles of the PV product
   __shared__ __align__(16) unsigned char smem[SM::kBytes];
   __shared__ int last_wg;
@@ -47,8 +46,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
   const int split = blockIdx.x % n_split;
   const int64_t b = row / hkv;
   const int g = (int)(row % hkv);
-  const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
-  const int lg = lane / 16, col = lane % 16;
+  const int lane = lane_id(), w = wave_id();
   const int64_t p = kv_len - 1;
   const int e0 = split * bpw;
   const int e1 = e0 + bpw < top_k ? e0 + bpw : top_k;
@@ -56,93 +54,19 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const uint16_t* __rest
   const int32_t* sel_row = sel + row * top_k;
   const int64_t kv_off = ((int64_t)b * hkv + g) * kv_cap;
 
-  u32x4_t qf[KS];
+  // The slice's block ids, one per lane (bpw <= 64), loaded with Q.
+  const int sel_mine = lane < n_e ? sel_row[e0 + lane] : -1;
+  u32x4_t qf[D / 32];
   load_q_operands<D>(q + (b * hq + (int64_t)g * G) * D, G, qf);
 
   float m_run = -__builtin_inff(), l_run = 0.f;
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  unsigned char* vs = smem + w * kUnit * RS;
-
-  // The slice's block ids, one per lane (bpw <= 64), loaded with Q.
-  const int sel_mine = lane < e1 - e0 ? sel_row[e0 + lane] : -1;
-
-  attend_units<D, GATHER>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, bs, p, scale_log2, vs, w, 4, m_run,
-                         l_run, o);
-
+  attend_units<D, GATHER>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, bs, p, scale_log2,
+                          smem + w * kUnit * SM::RS, w, NW, m_run, l_run, o);
   l_run = sum_col4(l_run);
-  __syncthreads();  // staging area becomes the combine area
-  float* cm = reinterpret_cast<float*>(smem);  // [4][16] running maxima
-  float* cl = cm + 4 * 16;                     // [4][16] sums
-  float* co = cl + 4 * 16;                     // [4][16][D] unnormalised outputs
-  if (lane < 16) {
-    cm[w * 16 + col] = m_run;
-    cl[w * 16 + col] = l_run;
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
-  __syncthreads();
-
-  if (n_split == 1) {
-    for (int idx = tid; idx < G * D; idx += 256) {
-      const int h = idx / D, e = idx % D;
-      float M = -__builtin_inff();
-      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
-      float L = 0.f, O = 0.f;
-      for (int ww = 0; ww < 4; ++ww) {
-        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
-        L += f * cl[ww * 16 + h];
-        O += f * co[(ww * 16 + h) * D + e];
-      }
-      out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
-    }
-    return;
-  }
-
-  // Several slices per row: this slice's state goes out with stores that
-  // reach the device-coherent level (cache policy sc1: no L2 write-back
-  // needed), then one ticket per workgroup; the last workgroup of the row
-  // to arrive merges every slice in order and resets the row's counter.
-  const int stride = 2 * G + G * D;  // floats per slice: maxima, sums, outputs
-  const auto prs = __builtin_amdgcn_make_buffer_rsrc(part + row * (int64_t)n_split * stride, 0,
-                                                     n_split * stride * 4, kBufferFlags);
-  const int soff = split * stride;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, e = idx % D;
-    float M = -__builtin_inff();
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
-    float L = 0.f, O = 0.f;
-    if (M != -__builtin_inff()) {  // a slice may hold no visible key
-      for (int ww = 0; ww < 4; ++ww) {
-        const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
-        L += f * cl[ww * 16 + h];
-        O += f * co[(ww * 16 + h) * D + e];
-      }
-    }
-    if (e == 0) {
-      store_coherent(prs, soff + h, __float_as_uint(M));
-      store_coherent(prs, soff + G + h, __float_as_uint(L));
-    }
-    store_coherent(prs, soff + 2 * G + h * D + e, __float_as_uint(O));
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == (uint32_t)(n_split - 1);
-    if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_wg = last ? 1 : 0;
-  }
-  __syncthreads();
-  if (!last_wg) return;
-
-  // 64 registers of staged values per batch: 16 slices for one group of 4
-  // dims per thread, 8 slices for two (G = 16 at d = 128)
-  if (G * (D / 4) <= 256) merge_slices<D, 1, 16, 256>(prs, smem, out, b, g, hq, G, n_split, tid);
-  else merge_slices<D, 2, 8, 256>(prs, smem, out, b, g, hq, G, n_split, tid);
+  finish_row_slice<D, NW>(m_run, l_run, o, smem, &last_wg, out, part, counters, row, b, g, hq, G, split, n_split);
 }
 
 template <int D>
@@ -151,9 +75,11 @@ hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const 
                     hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const float scale_log2 = s.scale * 1.4426950408889634f;
-  auto kern = s.bs < kUnit ? decode_attn_kernel<D, true> : decode_attn_kernel<D, false>;
+  auto kern = plan.waves == 8 ? (s.bs < kUnit ? decode_attn_kernel<D, true, 8> : decode_attn_kernel<D, false, 8>)
+                              : (s.bs < kUnit ? decode_attn_kernel<D, true, 4> : decode_attn_kernel<D, false, 4>);
   if (plan.n_split == 1) part = nullptr;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(rows * plan.n_split)), dim3(256), 0, st, static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rows * plan.n_split)), dim3(plan.waves * kWave), 0, st,
+                     static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sel,
                      static_cast<uint16_t*>(out), part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
                      scale_log2, plan.blocks_per_wg, plan.n_split);
@@ -162,10 +88,21 @@ hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const 
 
 }  // namespace
 
-DecodePlan plan_decode(const Dims& s, int64_t kv_len) {
+DecodePlan plan_decode(const Dims& s, int64_t kv_len, bool wide) {
   (void)kv_len;
   DecodePlan p{};
   const int64_t rows = (int64_t)s.batch * s.hkv;
+  p.waves = 4;
+  if (wide && rows >= 128 && s.top_k <= kWave) {
+    // the rows alone fill the GPU: one 8-wave workgroup per row over the
+    // whole selection (the fused decode step's shape; 64 x 128K attention
+    // 19.2 -> 16.6 us against 4-block slices), no slice states to merge
+    p.waves = 8;
+    p.blocks_per_wg = s.top_k;
+    p.n_split = 1;
+    p.ws_bytes = 0;
+    return p;
+  }
   // Smallest slices that still give every wave a unit, grown while the grid
   // stays above ~512 workgroups (fewer partial states to merge). A slice
   // holds at most 64 entries (one per lane).

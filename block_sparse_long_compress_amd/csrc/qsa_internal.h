@@ -68,11 +68,15 @@ hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, i
 
 // Decode attention --------------------------------------------------------------
 struct DecodePlan {
+  int waves;  // per workgroup: 4, or 8 with one slice per row when the rows fill the GPU
   int blocks_per_wg;
   int n_split;
   size_t ws_bytes;
 };
-DecodePlan plan_decode(const Dims& s, int64_t kv_len);
+// wide = false keeps 4-wave slices for every row count (the 8-bit cache
+// decode, whose waves keep one unit in flight and so want more workgroups).
+// The decode workspace is sized by the narrow plan, which covers both.
+DecodePlan plan_decode(const Dims& s, int64_t kv_len, bool wide = true);
 
 // counters: the plan's arrival counters (counter_bytes(rows), zero between
 // calls); part: its slice states (ws_bytes past the counters). The decode

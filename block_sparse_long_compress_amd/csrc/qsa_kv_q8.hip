@@ -82,27 +82,29 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
   }
 }
 
-template <int D>
+template <int D, int NW>
 struct Q8Smem {
   static constexpr int RS = kStageRowBytes<D>;
-  static constexpr int kStage = 4 * kUnit * RS;
-  static constexpr int kComb = 4 * (32 + 16 * D) * 4;
+  static constexpr int kStage = NW * kUnit * RS;
+  static constexpr int kComb = NW * (32 + 16 * D) * 4;
   static constexpr int kBytes = kStage > kComb ? kStage : kComb;
 };
 
-// Decode attention over the rotated quantized cache: one workgroup (4 waves)
-// per (sequence, KV head, slice of the selection). The G query heads are
+// Decode attention over the rotated quantized cache: one workgroup per
+// (sequence, KV head, slice of the selection), 4 or 8 waves as the bf16
+// decode kernel plans them. The G query heads are
 // rotated into LDS (bf16 operands), the units are those of the bf16 decode
 // kernel with the codes widened on load, and the combined state of the
 // slice is rotated back (H O / d) before it is written, which commutes with
 // the softmax merge of the slices (a linear combination of the states).
-template <int D>
-__global__ __launch_bounds__(256) void decode_attn_q8_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_attn_q8_kernel(
     const uint16_t* __restrict__ q, const int8_t* __restrict__ kq, const int8_t* __restrict__ vq,
     const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs_, const int32_t* __restrict__ sel,
     uint16_t* __restrict__ out, float* __restrict__ part, uint32_t* __restrict__ counters, int64_t kv_len,
     int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k, float scale_log2, int bpw, int n_split) {
-  using SM = Q8Smem<D>;
+  using SM = Q8Smem<D, NW>;
+  constexpr int NT = NW * kWave;
   constexpr int DT = D / 16;
   constexpr int EPL = D / kWave;
   __shared__ __align__(16) unsigned char smem[SM::kBytes];
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(256) void decode_attn_q8_kernel(
 
   // rotated query heads (bf16), head h by wave h % 4
   const uint16_t* qh = q + (b * hq + (int64_t)g * G) * D;
-  for (int h = w; h < G; h += 4) {
+  for (int h = w; h < G; h += NW) {
     float x[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) x[i] = bf16_to_f32(qh[(int64_t)h * D + lane + kWave * i]);
@@ -143,15 +145,15 @@ __global__ __launch_bounds__(256) void decode_attn_q8_kernel(
   const int sel_mine = lane < n_e ? sel[row * top_k + e0 + lane] : -1;
   const Q8Cache cache{kq + kv_off * D, vq + kv_off * D, ks + kv_off * (D / 32), vs_ + kv_off * (D / 32)};
   attend_units<D, false, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2,
-                               smem + w * kUnit * SM::RS, w, 4, m_run, l_run, o, cache);
+                               smem + w * kUnit * SM::RS, w, NW, m_run, l_run, o, cache);
   l_run = sum_col4(l_run);
 
   // combine the waves' states in LDS (wave order), rotate the combined O
   // back, then write the output (one slice) or the slice state
   __syncthreads();  // staging area becomes the combine area
-  float* cm = reinterpret_cast<float*>(smem);  // [4][16] running maxima
-  float* cl = cm + 4 * 16;                     // [4][16] sums
-  float* co = cl + 4 * 16;                     // [4][16][D] unnormalised outputs
+  float* cm = reinterpret_cast<float*>(smem);  // [NW][16] running maxima
+  float* cl = cm + NW * 16;                    // [NW][16] sums
+  float* co = cl + NW * 16;                    // [NW][16][D] unnormalised outputs
   if (lane < 16) {
     cm[w * 16 + col] = m_run;
     cl[w * 16 + col] = l_run;
@@ -161,13 +163,13 @@ __global__ __launch_bounds__(256) void decode_attn_q8_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D, e = idx % D;
     float M = -__builtin_inff();
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
     float L = 0.f, O = 0.f;
     if (M != -__builtin_inff()) {  // a slice may hold no visible key
-      for (int ww = 0; ww < 4; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
         L += f * cl[ww * 16 + h];
         O += f * co[(ww * 16 + h) * D + e];
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void decode_attn_q8_kernel(
   }
   __syncthreads();
   constexpr float inv_d = 1.0f / D;  // exact: D is a power of two
-  for (int h = w; h < G; h += 4) {
+  for (int h = w; h < G; h += NW) {
     float x[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) x[i] = comb_o[h * D + lane + kWave * i];
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void decode_attn_q8_kernel(
   __syncthreads();
 
   if (n_split == 1) {
-    for (int idx = tid; idx < G * D; idx += 256) {
+    for (int idx = tid; idx < G * D; idx += NT) {
       const int h = idx / D, e = idx % D;
       out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(comb_o[idx] / comb_l[h]);
     }
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void decode_attn_q8_kernel(
   const auto prs = __builtin_amdgcn_make_buffer_rsrc(part + row * (int64_t)n_split * stride, 0,
                                                      n_split * stride * 4, kBufferFlags);
   const int soff = split * stride;
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D, e = idx % D;
     if (e == 0) {
       store_coherent(prs, soff + h, __float_as_uint(comb_m[h]));
@@ -222,8 +224,8 @@ __global__ __launch_bounds__(256) void decode_attn_q8_kernel(
   }
   __syncthreads();
   if (!last_wg) return;
-  if (G * (D / 4) <= 256) merge_slices<D, 1, 16, 256>(prs, smem, out, b, g, hq, G, n_split, tid);
-  else merge_slices<D, 2, 8, 256>(prs, smem, out, b, g, hq, G, n_split, tid);
+  if (G * (D / 4) <= NT) merge_slices<D, 1, 16, NT>(prs, smem, out, b, g, hq, G, n_split, tid);
+  else merge_slices<D, 2, 8, NT>(prs, smem, out, b, g, hq, G, n_split, tid);
 }
 
 template <int D>
@@ -245,7 +247,8 @@ hipError_t launch_q8_d(const Dims& s, const DecodePlan& plan, const void* q, con
   const float scale_log2 = s.scale * 1.4426950408889634f / (float)D;
   uint32_t* counters = static_cast<uint32_t*>(ws);
   float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows)) : nullptr;
-  hipLaunchKernelGGL((decode_attn_q8_kernel<D>), dim3((unsigned)(rows * plan.n_split)), dim3(256), 0, st,
+  auto kern = plan.waves == 8 ? decode_attn_q8_kernel<D, 8> : decode_attn_q8_kernel<D, 4>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(rows * plan.n_split)), dim3(plan.waves * kWave), 0, st,
                      static_cast<const uint16_t*>(q), kq, vq, ks, vs, sel, static_cast<uint16_t*>(out), part,
                      counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, scale_log2, plan.blocks_per_wg,
                      plan.n_split);

@@ -117,6 +117,9 @@ DECODE_CASES = [
     W(mode="decode", batch=2, kv_len=3000, n_q_heads=16, n_kv_heads=1, top_k=7),
     W(mode="decode", batch=2, kv_len=3000, n_q_heads=2, n_kv_heads=2, top_k=7),
     W(mode="decode", batch=2, kv_len=2222, dtype="f32", sigma=1.0, top_k=5),
+    # 128 rows: one 8-wave workgroup per row over the whole selection
+    W(mode="decode", batch=64, kv_len=3000, top_k=16),
+    W(mode="decode", batch=64, kv_len=1001, top_k=9, block_size=4, head_dim=64),     # gathered units
     # keep_tail: own block complete (it competes) and still filling
     W(mode="decode", batch=2, kv_len=64 * 40, top_k=8, keep_tail=True),
     W(mode="decode", batch=2, kv_len=64 * 40 + 17, top_k=8, keep_tail=True),

@@ -35,6 +35,7 @@ CASES = [
     W(batch=1, kv_len=40000, top_k=16, n_q_heads=16, n_kv_heads=1),      # G = 16
     W(batch=40, kv_len=2000, top_k=8, block_size=128, n_q_heads=8),       # 80 rows
     W(batch=1, kv_len=50, top_k=4),                                       # own block only
+    W(batch=64, kv_len=3000, top_k=16),                                   # 128 rows: 8-wave workgroups
 ]
 
 
