@@ -177,9 +177,11 @@ class Step:
                 self.blk_begin = 0
                 self.n_new_blocks = sum(1 for n in self.lens if n % bs == 0)
             elif w.kv_q8:
-                # the attention reads the rotated 8-bit cache: the separate calls (compress the closed
-                # block, quantize the new position, select, attend)
-                self.ws_step = None
+                # the attention reads the rotated 8-bit cache: one qsa_decode_step_q8 call (quantize the
+                # new position, then compress, select and attend in one kernel) where the fused kernel
+                # serves the shape, else the separate calls
+                self.fused = qsa.qsa_decode_step_fused(self.shape, w.kv_len)
+                self.ws_step = self._ws(qsa.QSA_OP_DECODE_STEP, 1, w.kv_len) if self.fused else None
                 self.kq, self.vq, self.ks, self.vs = qsa.kv_q8_buffers(self.k)
                 qsa.qsa_kv_quantize(self.shape, self.k, self.v, w.kv_len - 1, self.kq, self.vq, self.ks, self.vs)
                 qsa.qsa_compress_keys(self.shape, self.k, w.kv_len - 1, self.k_comp)
@@ -219,7 +221,7 @@ class Step:
             self.calls.insert(1, ("index_keys", self.index_keys))
         if w.kv_q8:
             self.calls.insert(len(self.calls) - 2, ("quantize", self.quantize))
-        separate = w.indexer_dim or w.kv_q8
+        separate = w.indexer_dim or (w.kv_q8 and not self.fused)
         self.step_calls = [("step", self.decode_step)] if w.mode == "decode" and not separate else self.calls
         if self.fused:
             self.calls = self.step_calls
@@ -230,6 +232,10 @@ class Step:
 
     def decode_step(self):
         w = self.w
+        if w.kv_q8:
+            self.qsa.qsa_decode_step_q8(self.shape, self.q_dec, self.k, self.v, self.k_comp, self.kq, self.vq,
+                                        self.ks, self.vs, w.kv_len, self.sel_dec, self.out_dec, ws=self.ws_step)
+            return
         if w.ragged:
             self.qsa.qsa_decode_step_ragged(self.shape, self.q_dec, self.k, self.v, self.k_comp, self.kv_lens,
                                             w.kv_len, self.sel_dec, self.out_dec, ws=self.ws_step)
@@ -538,7 +544,9 @@ def main():
                    **({"mean_kv_len": round(float(np.mean(st.lens)), 1), "min_kv_len": int(min(st.lens))}
                       if w.ragged else {})},
         "roofline": {"bound": bound,
-                     "kernel": "decode_step_kernel (the whole step)" if dominant == "step" else f"{dominant} call",
+                     "kernel": (("kv_quantize_kernel + decode_step_kernel over the 8-bit cache (the whole step)"
+                                 if w.kv_q8 else "decode_step_kernel (the whole step)")
+                                if dominant == "step" else f"{dominant} call"),
                      "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name, dominant)},

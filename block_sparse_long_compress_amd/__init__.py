@@ -40,6 +40,7 @@ from .binding import (  # noqa: F401
     qsa_indexer_select,
     qsa_kv_quantize,
     qsa_sparse_attn_decode_q8,
+    qsa_decode_step_q8,
     kv_q8_buffers,
     qsa_score_select,
     qsa_sparse_attn_decode,

@@ -25,7 +25,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_E
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
             "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused",
             "qsa_decode_step_ragged", "qsa_indexer_keys", "qsa_indexer_select", "qsa_kv_quantize",
-            "qsa_sparse_attn_decode_q8")
+            "qsa_sparse_attn_decode_q8", "qsa_decode_step_q8")
 
 
 class QsaError(RuntimeError):
@@ -88,6 +88,8 @@ def _load() -> ctypes.CDLL:
     lib.qsa_kv_quantize.argtypes = [SH, P, P, I64, I64, I64, P, P, P, P, P]
     lib.qsa_sparse_attn_decode_q8.restype = ctypes.c_int
     lib.qsa_sparse_attn_decode_q8.argtypes = [SH, P, P, P, P, P, I64, I64, P, P, P, SZ, P]
+    lib.qsa_decode_step_q8.restype = ctypes.c_int
+    lib.qsa_decode_step_q8.argtypes = [SH, P, P, P, P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
     return lib
 
 
@@ -272,4 +274,15 @@ def qsa_sparse_attn_decode_q8(shape: QsaShape, q, k_q, v_q, k_scales, v_scales, 
     _check(LIB.qsa_sparse_attn_decode_q8(ctypes.byref(shape), _ptr(q), _ptr(k_q), _ptr(v_q), _ptr(k_scales),
                                          _ptr(v_scales), kv_len, k_q.shape[2], _ptr(sel), _ptr(out), _ptr(ws), nbytes,
                                          _stream(q, stream)), "qsa_sparse_attn_decode_q8")
+    return out
+
+
+def qsa_decode_step_q8(shape: QsaShape, q, k, v, k_comp, k_q, v_q, k_scales, v_scales, kv_len: int, sel, out,
+                       sel_scores=None, ws=None, stream=None):
+    """One decode step over the 8-bit cache: quantize position ``kv_len - 1`` of ``k``/``v`` into it, then compress,
+    select and attend over the codes in one kernel (``qsa_decode_step``'s fused shapes only)."""
+    ws, nbytes = _workspace(shape, QSA_OP_DECODE_STEP, 1, kv_len, ws, q.device)
+    _check(LIB.qsa_decode_step_q8(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_comp), _ptr(k_q), _ptr(v_q),
+                                  _ptr(k_scales), _ptr(v_scales), kv_len, k.shape[2], _ptr(sel), _ptr(sel_scores),
+                                  _ptr(out), _ptr(ws), nbytes, _stream(q, stream)), "qsa_decode_step_q8")
     return out

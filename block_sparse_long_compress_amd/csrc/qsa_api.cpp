@@ -409,4 +409,33 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
                                           static_cast<hipStream_t>(stream)));
 }
 
+qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,
+                              int8_t* k_q, int8_t* v_q, uint16_t* k_scales, uint16_t* v_scales, int64_t kv_len,
+                              int64_t kv_cap, int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !k || !v || !k_comp || !k_q || !v_q || !k_scales || !v_scales || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_comp) || !aligned16(k_q) || !aligned16(v_q) ||
+      !aligned16(k_scales) || !aligned16(v_scales) || !aligned16(sel) || !aligned16(out))
+    return QSA_ERR_INVALID;
+  if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
+  if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
+  if (!sp.fused) return QSA_ERR_UNSUPPORTED;  // the separate calls serve the other shapes
+  if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  const StepWs lay = step_ws(s, kv_len);
+  if (lay.total > 0 && (!ws || ws_bytes < lay.total || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // the new position into the 8-bit cache, then the fused step over it
+  st = hip_status(qsa::launch_kv_quantize(s, k, v, kv_cap, kv_len - 1, kv_len, k_q, v_q, k_scales, v_scales, hs));
+  if (st != QSA_OK) return st;
+  char* base = static_cast<char*>(ws);
+  const qsa::Q8Cache cache{k_q, v_q, k_scales, v_scales};
+  return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, base,
+                                            base ? base + lay.part_off : nullptr, hs, nullptr, &cache));
+}
+
 }  // extern "C"

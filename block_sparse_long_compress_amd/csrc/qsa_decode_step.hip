@@ -29,22 +29,27 @@ namespace {
 
 constexpr int kStepWaves = 8;
 
-template <int D>
+template <int D, bool ROT = false>
 struct StepSmem {
   static constexpr int RS = kStageRowBytes<D>;
-  static constexpr int kStage = kStepWaves * kUnit * RS;       // V staging, one 32-row slice per wave
-  static constexpr int kComb = kStepWaves * (32 + 16 * D) * 4;  // the waves' softmax states
+  static constexpr int kStage = kStepWaves * kUnit * RS;  // V staging, one 32-row slice per wave
+  // the waves' softmax states (and, rotated cache, the workgroup's combined one)
+  static constexpr int kComb = (kStepWaves + (ROT ? 1 : 0)) * (32 + 16 * D) * 4;
   static constexpr int kBytes = kStage > kComb ? kStage : kComb;
 };
 
-template <int D, int BS>
+// Q8: the attention reads the rotated 8-bit cache (q8: codes and scales of
+// every row, [b][Hkv][kv_cap] like k and v); the query heads are rotated
+// first and the output rotated back. Compression and selection still read
+// the bf16 keys.
+template <int D, int BS, bool Q8 = false>
 __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     float* __restrict__ k_comp, int32_t* __restrict__ sel, float* __restrict__ sel_scores, uint16_t* __restrict__ out,
     float* __restrict__ part, uint32_t* __restrict__ counters, const int32_t* __restrict__ kv_lens,
     int64_t kv_len_max, int64_t kv_cap, int hq, int hkv, int G, int top_k, float scale, int keep_tail, int bpw,
-    int n_split, int64_t n_rows) {
-  using SM = StepSmem<D>;
+    int n_split, int64_t n_rows, Q8Cache q8) {
+  using SM = StepSmem<D, Q8>;
   constexpr int LPR = D / 4;  // lanes covering one compressed key row (float32)
   constexpr int DT = D / 16;
   __shared__ __align__(16) unsigned char big[SM::kBytes];
@@ -52,6 +57,7 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   __shared__ __align__(16) float knew[D];
   __shared__ int ids[kWave];
   __shared__ int last_wg;
+  __shared__ __align__(16) uint16_t qrot[Q8 ? 16 * D : 8];  // rotated query heads (bf16)
 
   // Several slices per row: all slices of a row on one XCD (workgroups go
   // to the 8 XCDs round-robin), so that they share its L2 copy of the row's
@@ -158,7 +164,22 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
 
   // 3. attention over the selection, units round-robin over the waves
   u32x4_t qf[D / 32];
-  load_q_operands<D>(q_heads, G, qf);
+  if constexpr (Q8) {
+    // (H q).(H k) = D q.k: the 1/D goes into the scale below
+    constexpr int EPL = D / kWave;
+    for (int h = w; h < G; h += kStepWaves) {
+      float x[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) x[i] = bf16_to_f32(q_heads[(int64_t)h * D + lane + kWave * i]);
+      fwht_wave<D>(x);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) qrot[h * D + lane + kWave * i] = f32_to_bf16(x[i]);
+    }
+    __syncthreads();
+    load_q8_query_operands<D>(qrot, G, qf);
+  } else {
+    load_q_operands<D>(q_heads, G, qf);
+  }
   const int e0 = split * bpw;
   const int n_e = top_k - e0 < bpw ? top_k - e0 : bpw;  // this slice's entries of the selection
   const int sel_mine = lane < n_e ? ids[e0 + lane] : -1;
@@ -166,12 +187,15 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const float scale_log2 = scale * 1.4426950408889634f;
-  attend_units<D, false>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, BS, p, scale_log2,
-                         big + w * kUnit * SM::RS, w, kStepWaves, m_run, l_run, o);
+  const float scale_log2 = scale * 1.4426950408889634f / (Q8 ? (float)D : 1.0f);
+  const Q8Cache rq = Q8 ? Q8Cache{q8.k + kv_off * D, q8.v + kv_off * D, q8.ks + kv_off * (D / 32),
+                                  q8.vs + kv_off * (D / 32)}
+                        : q8;
+  attend_units<D, false, Q8>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, BS, p, scale_log2,
+                             big + w * kUnit * SM::RS, w, kStepWaves, m_run, l_run, o, rq);
   l_run = sum_col4(l_run);
-  finish_row_slice<D, kStepWaves>(m_run, l_run, o, big, &last_wg, out, part, counters, row, b, g, hq, G, split,
-                                  n_split);
+  finish_row_slice<D, kStepWaves, Q8>(m_run, l_run, o, big, &last_wg, out, part, counters, row, b, g, hq, G,
+                                      split, n_split);
 }
 
 // Decode step with k > 64 (the released budget): after the large-k score
@@ -242,10 +266,10 @@ hipError_t launch_pick_attend_d(const Dims& s, const PickAttendPlan& pa, const v
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool Q8>
 hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                          float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out,
-                         uint32_t* counters, float* part, const int32_t* kv_lens,
+                         uint32_t* counters, float* part, const int32_t* kv_lens, const Q8Cache& q8,
                          hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const int64_t n_wg = plan.n_split > 1 ? 8 * ((rows + 7) / 8) * plan.n_split : rows;
@@ -255,25 +279,12 @@ hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, con
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
   auto* op = static_cast<uint16_t*>(out);
-  switch (s.bs) {
-    case 32:
-      hipLaunchKernelGGL((decode_step_kernel<D, 32>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
-                         part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
-                         s.keep_tail, plan.blocks_per_wg, plan.n_split, rows);
-      break;
-    case 64:
-      hipLaunchKernelGGL((decode_step_kernel<D, 64>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
-                         part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
-                         s.keep_tail, plan.blocks_per_wg, plan.n_split, rows);
-      break;
-    case 128:
-      hipLaunchKernelGGL((decode_step_kernel<D, 128>), grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op,
-                         part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale,
-                         s.keep_tail, plan.blocks_per_wg, plan.n_split, rows);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+  auto kern = s.bs == 32 ? decode_step_kernel<D, 32, Q8>
+                         : (s.bs == 64 ? decode_step_kernel<D, 64, Q8> : decode_step_kernel<D, 128, Q8>);
+  if (s.bs != 32 && s.bs != 64 && s.bs != 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op, part, counters, kv_lens,
+                     kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail, plan.blocks_per_wg,
+                     plan.n_split, rows, q8);
   return hipGetLastError();
 }
 
@@ -314,12 +325,20 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged) {
 
 hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                               float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
-                              void* out, void* counters, void* part, hipStream_t st, const int32_t* kv_lens) {
+                              void* out, void* counters, void* part, hipStream_t st, const int32_t* kv_lens,
+                              const Q8Cache* q8) {
   uint32_t* c = static_cast<uint32_t*>(counters);
   float* pt = static_cast<float*>(part);
-  return s.d == 64
-             ? launch_step_d<64>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, c, pt, kv_lens, st)
-             : launch_step_d<128>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, c, pt, kv_lens, st);
+  if (q8)
+    return s.d == 64 ? launch_step_d<64, true>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, c, pt,
+                                               kv_lens, *q8, st)
+                     : launch_step_d<128, true>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, c,
+                                                pt, kv_lens, *q8, st);
+  const Q8Cache none{nullptr, nullptr, nullptr, nullptr};
+  return s.d == 64 ? launch_step_d<64, false>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, c, pt,
+                                              kv_lens, none, st)
+                   : launch_step_d<128, false>(s, plan, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, c, pt,
+                                               kv_lens, none, st);
 }
 
 PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks) {

@@ -17,6 +17,7 @@
 #pragma once
 
 #include "qsa_device.h"
+#include "qsa_internal.h"
 
 namespace qsa {
 
@@ -30,16 +31,6 @@ __device__ __forceinline__ int kkey(int lg, int j) { return j < 4 ? 4 * lg + j :
 
 template <int D>
 constexpr int kStageRowBytes = 2 * D + 16;  // LDS row stride of staged V (bytes)
-
-// A quantized K/V cache (8-bit codes, one float16 scale per 32 values of a
-// row: value = code * scale), read by attend_units<..., true> in place of
-// the bf16 cache; the values are widened to bf16 operands on load.
-struct Q8Cache {
-  const int8_t* k;     // codes [positions][D] of the row's keys
-  const int8_t* v;     // codes of its values
-  const uint16_t* ks;  // float16 scales [positions][D/32]
-  const uint16_t* vs;
-};
 
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
@@ -68,6 +59,26 @@ __device__ __forceinline__ void load_q_operands(const uint16_t* __restrict__ q_h
   for (int s = 0; s < D / 32; ++s) {
     qf[s] = u32x4_t{0u, 0u, 0u, 0u};
     if (col < G) qf[s] = *reinterpret_cast<const u32x4_t*>(q_heads + (int64_t)col * D + 32 * s + 8 * lg);
+  }
+}
+
+// In-place unnormalised Walsh-Hadamard transform of a D-vector held by one
+// wave, lane l holding elements l and l + 64 (D = 128) or l (D = 64).
+template <int D>
+__device__ __forceinline__ void fwht_wave(float (&v)[D / kWave]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int h = 1; h < kWave && h < D; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D / kWave; ++i) {
+      const float other = shfl_xor_f32(v[i], h);
+      v[i] = (lane & h) ? other - v[i] : v[i] + other;
+    }
+  }
+  if constexpr (D == 2 * kWave) {
+    const float a = v[0], b = v[1];
+    v[0] = a + b;
+    v[1] = a - b;
   }
 }
 
@@ -395,7 +406,12 @@ __device__ __forceinline__ void merge_slices(__amdgpu_buffer_rsrc_t prs, unsigne
 // slice's state goes to the workspace with device-coherent stores, the
 // workgroup takes a ticket from the row's arrival counter, and the last one
 // to arrive merges all slices in slice order and resets the counter.
-template <int D, int NW>
+//
+// ROT (the rotated 8-bit cache): the workgroup's combined state is rotated
+// back (H o / D per head, the float32 butterflies) before it is written or
+// merged; the rotation is linear, so the slices' merge commutes with it.
+// The combine area then needs (NW + 1) * (32 + 16 D) floats.
+template <int D, int NW, bool ROT = false>
 __device__ void finish_row_slice(float m_run, float l_run, const f32x4_t (&o)[D / 16], unsigned char* smem,
                                  int* last_flag, uint16_t* __restrict__ out, float* part, uint32_t* counters,
                                  int64_t row, int64_t b, int g, int hq, int G, int split, int n_split) {
@@ -416,6 +432,70 @@ __device__ void finish_row_slice(float m_run, float l_run, const f32x4_t (&o)[D 
 #pragma unroll
     for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
+  if constexpr (ROT) {
+    constexpr int EPL = D / kWave;
+    float* bm = co + NW * 16 * D;  // [16] the workgroup's maxima
+    float* bl = bm + 16;           // [16] sums
+    float* bo = bl + 16;           // [16][D] outputs, rotated back below
+    for (int idx = tid; idx < G * D; idx += NT) {
+      const int h = idx / D, e = idx % D;
+      float M = -__builtin_inff();
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, cm[ww * 16 + h]);
+      float L = 0.f, O = 0.f;
+      if (M != -__builtin_inff()) {  // a slice may hold no visible key
+        for (int ww = 0; ww < NW; ++ww) {
+          const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
+          L += f * cl[ww * 16 + h];
+          O += f * co[(ww * 16 + h) * D + e];
+        }
+      }
+      if (e == 0) {
+        bm[h] = M;
+        bl[h] = L;
+      }
+      bo[idx] = O;
+    }
+    __syncthreads();
+    constexpr float inv_d = 1.0f / D;  // exact: D is a power of two
+    for (int h = w; h < G; h += NW) {
+      float x[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) x[i] = bo[h * D + lane + kWave * i];
+      fwht_wave<D>(x);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) bo[h * D + lane + kWave * i] = x[i] * inv_d;
+    }
+    __syncthreads();
+    if (n_split == 1) {
+      for (int idx = tid; idx < G * D; idx += NT)
+        out[(b * hq + (int64_t)g * G + idx / D) * D + idx % D] = f32_to_bf16(bo[idx] / bl[idx / D]);
+      return;
+    }
+    const int stride = 2 * G + G * D;
+    const auto prs = __builtin_amdgcn_make_buffer_rsrc(part + row * (int64_t)n_split * stride, 0,
+                                                       n_split * stride * 4, kBufferFlags);
+    const int soff = split * stride;
+    for (int idx = tid; idx < G * D; idx += NT) {
+      if (idx % D == 0) {
+        store_coherent(prs, soff + idx / D, __float_as_uint(bm[idx / D]));
+        store_coherent(prs, soff + G + idx / D, __float_as_uint(bl[idx / D]));
+      }
+      store_coherent(prs, soff + 2 * G + idx, __float_as_uint(bo[idx]));
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = prev == (uint32_t)(n_split - 1);
+      if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *last_flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (!*last_flag) return;
+    if (G * (D / 4) <= NT) merge_slices<D, 1, 16, NT>(prs, smem, out, b, g, hq, G, n_split, tid);
+    else merge_slices<D, 2, 8, NT>(prs, smem, out, b, g, hq, G, n_split, tid);
+    return;
+  }
   if (n_split == 1) {
     for (int idx = tid; idx < G * D; idx += NT) {
       const int h = idx / D, e = idx % D;

@@ -115,11 +115,23 @@ struct StepPlan {
 StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged = false);
 // kv_lens (device, [batch], nullable): per-sequence lengths, each clamped
 // into [1, kv_len]; null means every sequence has kv_len.
-// counters / part: as for launch_decode (used when plan.n_split > 1).
+// counters / part: as for launch_decode (used when plan.n_split > 1). q8:
+// attend over the rotated 8-bit cache instead of k and v (compression and
+// selection still read k); Bs >= 32.
+// A quantized K/V cache (8-bit codes, one float16 scale per 32 values of a
+// row: value = code * scale), read by attend_units<..., true> in place of
+// the bf16 cache; the values are widened to bf16 operands on load.
+struct Q8Cache {
+  const int8_t* k;     // codes [positions][D] of the row's keys
+  const int8_t* v;     // codes of its values
+  const uint16_t* ks;  // float16 scales [positions][D/32]
+  const uint16_t* vs;
+};
+
 hipError_t launch_decode_step(const Dims& s, const StepPlan& plan, const void* q, const void* k, const void* v,
                               float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
                               void* out, void* counters, void* part, hipStream_t st,
-                              const int32_t* kv_lens = nullptr);
+                              const int32_t* kv_lens = nullptr, const Q8Cache* q8 = nullptr);
 
 // Decode step with k > 64 (bf16): the selection's score pass, then one kernel
 // that picks each row's ids and attends over them (S workgroups per row).

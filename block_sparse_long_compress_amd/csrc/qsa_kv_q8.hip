@@ -21,26 +21,6 @@
 namespace qsa {
 namespace {
 
-// In-place unnormalised Walsh-Hadamard transform of a D-vector held by one
-// wave, lane l holding elements l and l + 64 (D = 128) or l (D = 64).
-template <int D>
-__device__ __forceinline__ void fwht_wave(float (&v)[D / kWave]) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int h = 1; h < kWave && h < D; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < D / kWave; ++i) {
-      const float other = shfl_xor_f32(v[i], h);
-      v[i] = (lane & h) ? other - v[i] : v[i] + other;
-    }
-  }
-  if constexpr (D == 2 * kWave) {
-    const float a = v[0], b = v[1];
-    v[0] = a + b;
-    v[1] = a - b;
-  }
-}
-
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
 
 // One wave per (sequence, KV head, position, K or V): rotate the row, then

@@ -82,7 +82,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 5
+#define QSA_ABI_VERSION 6
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -321,6 +321,24 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
                                      const uint16_t* k_scales, const uint16_t* v_scales, int64_t kv_len,
                                      int64_t kv_cap, const int32_t* sel, void* out, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* One decode step over the 8-bit cache: qsa_kv_quantize of the new position
+ * kv_len - 1, then, in one kernel, what qsa_decode_step does (compress the
+ * block the new token closes from the bf16 keys k, select from k_comp) with
+ * the attention of qsa_sparse_attn_decode_q8 over the codes. k and v are the
+ * bf16 cache the new position is quantized from ([b][Hkv][kv_cap][head_dim],
+ * read only at kv_len - 1 and, for the compression, in the closed block);
+ * k_q, v_q, k_scales, v_scales as for qsa_kv_quantize, holding positions
+ * 0 .. kv_len - 2 already. sel, sel_scores (optional), out as for
+ * qsa_decode_step. Serves the shapes that qsa_decode_step runs as its fused
+ * kernel (qsa_decode_step_fused(shape, kv_len) == 1), else
+ * QSA_ERR_UNSUPPORTED (the separate calls serve the others). ws: device
+ * scratch of qsa_workspace_bytes(shape, QSA_OP_DECODE_STEP, 1, kv_len),
+ * zero-filled before its first use (the same layout as qsa_decode_step). */
+qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,
+                              int8_t* k_q, int8_t* v_q, uint16_t* k_scales, uint16_t* v_scales, int64_t kv_len,
+                              int64_t kv_cap, int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,
+                              void* stream);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 5
+    assert qsa.abi_version() == 6
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -210,3 +210,29 @@ def test_indexer_arguments(qsa):
     assert lib.qsa_indexer_select(sh, ix, P, P, 1, 127, N, 128, 256, P, N, N) == INV  # candidates, no keys
     big_k = ctypes.byref(good_shape(qsa, top_k=65))
     assert lib.qsa_indexer_select(big_k, ix, P, P, 1, 127, P, 128, 256, P, N, N) == UNS
+
+
+def test_decode_step_q8_arguments(qsa):
+    """The fused step over the 8-bit cache validates its arguments on the host and serves the fused shapes only."""
+    lib = qsa.LIB
+    sh = good_shape(qsa, batch=4)
+    shr = ctypes.byref(sh)
+    P, N, MIS = ctypes.c_void_p(4096), None, ctypes.c_void_p(4100)
+    big = 1 << 30
+    INV, UNS, WS = 1, 2, 3
+    call = lib.qsa_decode_step_q8
+    #            shape q  k  v  kc kq vq ks vs kv_len kv_cap sel scores out ws  bytes stream
+    assert call(shr, P, P, P, P, N, P, P, P, 4096, 4096, P, N, P, P, big, N) == INV      # no key codes
+    assert call(shr, P, P, P, P, P, P, MIS, P, 4096, 4096, P, N, P, P, big, N) == INV    # scales misaligned
+    assert call(shr, P, P, P, P, P, P, P, P, 4097, 4096, P, N, P, P, big, N) == INV      # beyond capacity
+    assert call(shr, P, P, P, P, P, P, P, P, 0, 4096, P, N, P, P, big, N) == INV
+    # shapes the fused kernel does not serve: f32, k > 64, Bs < 32, few long rows
+    for kw in (dict(dtype=qsa.QSA_F32), dict(top_k=65), dict(block_size=16)):
+        bad = ctypes.byref(good_shape(qsa, batch=4, **kw))
+        assert call(bad, P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, big, N) == UNS
+    one = good_shape(qsa, batch=1)
+    assert not qsa.qsa_decode_step_fused(one, 1 << 20)
+    assert call(ctypes.byref(one), P, P, P, P, P, P, P, P, 1 << 20, 1 << 20, P, N, P, P, big, N) == UNS
+    # the workspace of the plain step (same layout)
+    need = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 4096)
+    assert need > 0 and call(shr, P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, need - 1, N) == WS

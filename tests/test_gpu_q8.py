@@ -122,3 +122,70 @@ def test_q8_decode_parity(w):
         worst = max(worst, err)
         vs_plain = max(vs_plain, float(np.abs(got - bf_h[bb, g * G:(g + 1) * G]).max()))
     log(f"  max error against the 8-bit oracle {worst:.2e}; largest difference from bf16 attention {vs_plain:.2e}")
+
+
+STEP_CASES = [
+    W(),                                                                  # slices of the selection per row
+    W(batch=64, kv_len=3000, top_k=16),                                   # 128 rows: one workgroup per row
+    W(batch=2, kv_len=64 * 40, top_k=8, keep_tail=True),                  # the closed block competes
+    W(batch=2, kv_len=64 * 40 + 1, top_k=8),                              # the new token opens a block
+    W(batch=3, kv_len=5000, top_k=64, block_size=32, head_dim=64),
+    W(batch=1, kv_len=40000, top_k=16, n_q_heads=16, n_kv_heads=1),      # G = 16
+    W(batch=1, kv_len=50, top_k=4),                                       # own block only
+]
+
+
+@pytest.mark.parametrize("w", STEP_CASES, ids=lambda w: case_id(w) + ("-tail" if w.keep_tail else ""))
+def test_q8_decode_step_parity(w):
+    """The fused step over the 8-bit cache: the new position's codes and the closed block's compressed key as the
+    separate calls write them, the bf16 fused step's selection, and the 8-bit oracle's attention over it."""
+    log(f"q8 decode step {case_id(w)}")
+    case = Case(w, seed=34, kv_cap=w.kv_len + 70)
+    b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    G, n = hq // hkv, w.kv_len
+    shape = qsa.shape_for(case.q, case.k, bs, k, keep_tail=w.keep_tail)
+    assert qsa.qsa_decode_step_fused(shape, n)
+    kq, vq, ks, vs = qsa.kv_q8_buffers(case.k)
+    qsa.qsa_kv_quantize(shape, case.k, case.v, n - 1, kq, vq, ks, vs)  # the step quantizes position n - 1
+    nb_cap = case.kv_cap // bs
+    k_comp = torch.full((b, hkv, nb_cap, d), float("nan"), device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, n - 1, k_comp)
+    k_comp_bf = k_comp.clone()
+    q = case.q.view(b, hq, d)
+    sel = torch.empty(b, hkv, k, dtype=torch.int32, device="cuda")
+    scores = torch.empty(b, hkv, k, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    qsa.qsa_decode_step_q8(shape, q, case.k, case.v, k_comp, kq, vq, ks, vs, n, sel, out, sel_scores=scores)
+    # references from the separate calls and the bf16 fused step
+    kq2, vq2, ks2, vs2 = qsa.kv_q8_buffers(case.k)
+    qsa.qsa_kv_quantize(shape, case.k, case.v, n, kq2, vq2, ks2, vs2)
+    k_comp_ref = torch.full_like(k_comp, float("nan"))
+    qsa.qsa_compress_keys(shape, case.k, n, k_comp_ref)
+    sel_bf = torch.empty_like(sel)
+    out_bf = torch.empty_like(q)
+    qsa.qsa_decode_step(shape, q, case.k, case.v, k_comp_bf, n, sel_bf, out_bf)
+    out_sep = torch.empty_like(q)
+    qsa.qsa_sparse_attn_decode_q8(shape, q, kq2, vq2, ks2, vs2, n, sel, out_sep)
+    torch.cuda.synchronize()
+    for a, c in ((kq, kq2), (vq, vq2), (ks, ks2), (vs, vs2)):
+        assert torch.equal(a[:, :, :n], c[:, :, :n]), "8-bit cache differs from the quantize call"
+    nb = n // bs
+    assert torch.equal(k_comp[:, :, :nb], k_comp_ref[:, :, :nb]), "compressed keys differ from the compress call"
+    if not (w.keep_tail and n % bs == 0):  # else the new block's score may round differently
+        assert torch.equal(sel, sel_bf), "selection differs from the bf16 fused step"
+    out_h, sel_h, sep_h = from_device(out), sel.cpu().numpy(), from_device(out_sep)
+    assert np.abs(out_h - sep_h).max() <= BF16_ABS_TOL, "output differs from the separate 8-bit call"
+    rng = np.random.default_rng(2)
+    rows = [(bb, g) for bb in range(b) for g in range(hkv)]
+    if len(rows) > 10:
+        rows = [rows[i] for i in sorted(rng.choice(len(rows), 10, replace=False))]
+    worst = 0.0
+    for bb, g in rows:
+        qg = case.Q[bb, 0, g * G:(g + 1) * G].astype(np.float64)
+        kq_o, ks_o = Q.quantize_cache(case.K[bb, g, :n])  # the oracle's own cache
+        vq_o, vs_o = Q.quantize_cache(case.V[bb, g, :n])
+        ref = Q.attend_q8(qg, kq_o, ks_o, vq_o, vs_o, [int(x) for x in sel_h[bb, g]], n - 1, bs, O.default_scale(d))
+        err = float(np.abs(out_h[bb, g * G:(g + 1) * G] - ref).max())
+        assert err <= BF16_ABS_TOL, f"row {(bb, g)}: error {err:.3e}"
+        worst = max(worst, err)
+    log(f"  max error against the 8-bit oracle {worst:.2e}")
