@@ -36,10 +36,10 @@ struct StepWs {
   size_t total;     // 0 when the step needs no workspace
 };
 
-StepWs step_ws(const Dims& s, int64_t kv_len) {
+StepWs step_ws(const Dims& s, int64_t kv_len, bool q8 = false) {
   StepWs w{};
   const size_t cnt = qsa::counter_bytes((int64_t)s.batch * s.hkv);
-  const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
+  const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len, false, q8);
   size_t att = 0, sel_ws = 0, sel_scratch = 0;
   w.sel_off = cnt;
   if (sp.fused) {
@@ -145,7 +145,11 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       return qsa::plan_prefill(s, q_len, kv_len - q_len).ws_bytes;
     case QSA_OP_DECODE_STEP: {
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
-      return step_ws(s, kv_len).total;
+    {
+      // the plain step's and the 8-bit step's (same layout; the latter may split rows more)
+      const size_t a = step_ws(s, kv_len).total, b8 = step_ws(s, kv_len, true).total;
+      return a > b8 ? a : b8;
+    }
     }
     case QSA_OP_DECODE_STEP_RAGGED: {
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
@@ -423,10 +427,10 @@ qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void*
   if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
   if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
-  const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
+  const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len, false, true);
   if (!sp.fused) return QSA_ERR_UNSUPPORTED;  // the separate calls serve the other shapes
   if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  const StepWs lay = step_ws(s, kv_len);
+  const StepWs lay = step_ws(s, kv_len, true);
   if (lay.total > 0 && (!ws || ws_bytes < lay.total || !aligned16(ws))) return QSA_ERR_WORKSPACE;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   // the new position into the 8-bit cache, then the fused step over it

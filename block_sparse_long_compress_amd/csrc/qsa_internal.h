@@ -112,7 +112,7 @@ struct StepPlan {
 };
 // ragged: a batch of sequences of their own lengths (kv_len is then the
 // longest), which always runs fused when the kernel serves the shape.
-StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged = false);
+StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged = false, bool q8 = false);
 // kv_lens (device, [batch], nullable): per-sequence lengths, each clamped
 // into [1, kv_len]; null means every sequence has kv_len.
 // counters / part: as for launch_decode (used when plan.n_split > 1). q8:
