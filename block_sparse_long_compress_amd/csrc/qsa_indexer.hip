@@ -70,8 +70,6 @@ __global__ __launch_bounds__(256) void indexer_keys_kernel(const float* __restri
   for (int e = 0; e < EPL; ++e) dst[kWave * e] = acc[e];
 }
 
-constexpr int kIdxThreads = 256;
-constexpr int kIdxWaves = kIdxThreads / kWave;
 
 // One workgroup per (sequence, query row, KV head).
 // 1. the G query heads are projected into LDS (already scaled);
@@ -81,11 +79,12 @@ constexpr int kIdxWaves = kIdxThreads / kWave;
 //    and normaliser over the row's candidates and a second pass scores;
 // 3. per-wave top lists, merged, and the row's selection written as the
 //    default selection writes it.
-template <typename T, int D, int DI, int AGG>
+template <typename T, int D, int DI, int AGG, int kIdxThreads>
 __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
     const T* __restrict__ q, const float* __restrict__ w_q, const float* __restrict__ k_idx,
     int32_t* __restrict__ sel, float* __restrict__ sel_scores, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
     int hkv, int G, int bs, int top_k, float scale, int keep_tail) {
+  constexpr int kIdxWaves = kIdxThreads / kWave;
   __shared__ __align__(16) float qi[16 * DI];
   __shared__ __align__(16) float wq_s[D * DI];  // W_q, staged once per workgroup
   __shared__ __align__(16) float qs[16 * D];    // the group's query heads, as float
@@ -232,29 +231,34 @@ hipError_t launch_keys(const float* w_k, const float* k_comp, int64_t nb_cap, in
   return hipGetLastError();
 }
 
+template <typename T, int D, int DI, int NT>
+hipError_t launch_select_nt(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
+                            int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                            hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  const int64_t nb_cap = kv_cap / s.bs;
+  const T* qp = static_cast<const T*>(q);
+  const dim3 grid((unsigned)rows), block(NT);
+  auto kern = ix.agg == kAggSum   ? indexer_select_kernel<T, D, DI, kAggSum, NT>
+              : ix.agg == kAggMax ? indexer_select_kernel<T, D, DI, kAggMax, NT>
+                                  : indexer_select_kernel<T, D, DI, kAggSoftmax, NT>;
+  hipLaunchKernelGGL(kern, grid, block, 0, st, qp, w_q, k_idx, sel, sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv,
+                     s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
+  return hipGetLastError();
+}
+
+// Rows fewer than the CUs (decode): 8 waves per row, so that the projection
+// and the candidates of the few rows spread over more of each CU (32K decode,
+// 2 rows: the call 18.2 -> 15.9 us event-timed; 16 waves would cap the
+// registers at 128 and spill a candidate's indexer key); otherwise 4 waves.
 template <typename T, int D, int DI>
 hipError_t launch_select_t(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
                            int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel, float* sel_scores,
                            hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
-  const int64_t nb_cap = kv_cap / s.bs;
-  const T* qp = static_cast<const T*>(q);
-  const dim3 grid((unsigned)rows), block(kIdxThreads);
-  switch (ix.agg) {
-    case kAggSum:
-      hipLaunchKernelGGL((indexer_select_kernel<T, D, DI, kAggSum>), grid, block, 0, st, qp, w_q, k_idx, sel,
-                         sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
-      break;
-    case kAggMax:
-      hipLaunchKernelGGL((indexer_select_kernel<T, D, DI, kAggMax>), grid, block, 0, st, qp, w_q, k_idx, sel,
-                         sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
-      break;
-    default:
-      hipLaunchKernelGGL((indexer_select_kernel<T, D, DI, kAggSoftmax>), grid, block, 0, st, qp, w_q, k_idx, sel,
-                         sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
-      break;
-  }
-  return hipGetLastError();
+  if (rows < 256)
+    return launch_select_nt<T, D, DI, 512>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
+  return launch_select_nt<T, D, DI, 256>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
 }
 
 template <typename T>
