@@ -127,93 +127,122 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
   __syncthreads();
 
   const float* krow = k_idx + ((b * hkv + g) * nb_cap) * DI;
-  // head scores of candidate c into s[0 .. G-1]
-  auto head_scores = [&](int c, float (&s)[16]) {
-    f32x4_t kv[DI / 4];
+  // Head scores by fp32 MFMA (16x16x4): the indexer keys of 16 candidates as
+  // operand A, the projected query heads as operand B (head m in column m,
+  // columns >= G zero), so lane (kg, m) ends a tile with the scores of
+  // candidates 4kg .. 4kg+3 for head m. Its head's query dims 16u + 4kg + e
+  // stay in registers (qb[4u + e]).
+  const int kg = lane >> 4, m = lane & 15;
+  float qb[DI / 4];
 #pragma unroll
-    for (int e4 = 0; e4 < DI / 4; ++e4) kv[e4] = *reinterpret_cast<const f32x4_t*>(krow + (int64_t)c * DI + 4 * e4);
-    for (int h = 0; h < G; ++h) {
-      float acc = 0.f;
+  for (int u = 0; u < DI / 16; ++u) {
+    f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+    if (m < G) a = *reinterpret_cast<const f32x4_t*>(&qi[m * DI + 16 * u + 4 * kg]);
 #pragma unroll
-      for (int e4 = 0; e4 < DI / 4; ++e4) {
-        const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(&qi[h * DI + 4 * e4]);
-        acc = __builtin_fmaf(qv[0], kv[e4][0], acc);
-        acc = __builtin_fmaf(qv[1], kv[e4][1], acc);
-        acc = __builtin_fmaf(qv[2], kv[e4][2], acc);
-        acc = __builtin_fmaf(qv[3], kv[e4][3], acc);
+    for (int e = 0; e < 4; ++e) qb[4 * u + e] = a[e];
+  }
+  // scores of candidates c0 + 16 t + 4 kg + v (t < 4) for head m, into acc[t][v]
+  auto pass_scores = [&](int c0, f32x4_t (&acc)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int c = c0 + 16 * t + m;  // this lane's operand row
+      const bool ok = c < fr.n_cand;
+#pragma unroll
+      for (int u = 0; u < DI / 16; ++u) {
+        const f32x4_t kv = ok ? *reinterpret_cast<const f32x4_t*>(krow + (int64_t)c * DI + 16 * u + 4 * kg)
+                              : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t] = mfma_f32(kv[e], qb[4 * u + e], acc[t]);
       }
-      s[h] = acc;
     }
   };
 
   if constexpr (AGG == kAggSoftmax) {
-    // pass 1: every head's maximum and normaliser over the candidates
-    float m[16], z[16];
-    for (int h = 0; h < 16; ++h) {
-      m[h] = -__builtin_inff();
-      z[h] = 0.f;
+    // pass 1: every head's maximum and normaliser over the candidates (lane
+    // (kg, m) folds its 16 candidates per pass for head m, then the lanes of
+    // a head and the waves are combined)
+    float mh = -__builtin_inff(), zh = 0.f;
+    for (int base = kWave * w; base < fr.n_cand; base += kIdxThreads) {
+      f32x4_t acc[4];
+      pass_scores(base, acc);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (base + 16 * t + 4 * kg + v < fr.n_cand) {
+            const float x = acc[t][v];
+            const float mn = fmaxf(mh, x);
+            zh = zh * __expf(mh - mn) + __expf(x - mn);
+            mh = mn;
+          }
+        }
     }
-    for (int c = tid; c < fr.n_cand; c += kIdxThreads) {
-      float s[16];
-      head_scores(c, s);
-      for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], s[h]);
-        z[h] = z[h] * __expf(m[h] - mn) + __expf(s[h] - mn);
-        m[h] = mn;
-      }
+#pragma unroll
+    for (int d = 16; d < kWave; d <<= 1) {
+      const float mo = __shfl_xor(mh, d, kWave), zo = __shfl_xor(zh, d, kWave);
+      const float mn = fmaxf(mh, mo);
+      zh = (mn == -__builtin_inff()) ? 0.f : zh * __expf(mh - mn) + zo * __expf(mo - mn);
+      mh = mn;
     }
-    for (int h = 0; h < G; ++h) {
-      float mh = m[h], zh = z[h];
-      for (int d = 1; d < kWave; d <<= 1) {
-        const float mo = __shfl_xor(mh, d, kWave), zo = __shfl_xor(zh, d, kWave);
-        const float mn = fmaxf(mh, mo);
-        zh = (mn == -__builtin_inff()) ? 0.f : zh * __expf(mh - mn) + zo * __expf(mo - mn);
-        mh = mn;
-      }
-      if (lane == 0) {
-        red_m[w][h] = mh;
-        red_z[w][h] = zh;
-      }
+    if (lane < 16) {
+      red_m[w][lane] = mh;
+      red_z[w][lane] = zh;
     }
     __syncthreads();
     if (tid < G) {
-      float mh = -__builtin_inff(), zh = 0.f;
+      float hm = -__builtin_inff(), hz = 0.f;
       for (int ww = 0; ww < kIdxWaves; ++ww) {
         const float mo = red_m[ww][tid], zo = red_z[ww][tid];
-        const float mn = fmaxf(mh, mo);
-        zh = (mn == -__builtin_inff()) ? 0.f : zh * __expf(mh - mn) + zo * __expf(mo - mn);
-        mh = mn;
+        const float mn = fmaxf(hm, mo);
+        hz = (mn == -__builtin_inff()) ? 0.f : hz * __expf(hm - mn) + zo * __expf(mo - mn);
+        hm = mn;
       }
-      head_m[tid] = mh;
-      head_z[tid] = zh;
+      head_m[tid] = hm;
+      head_z[tid] = hz;
     }
     __syncthreads();
   }
 
-  // 2. aggregated scores, folded into each wave's top list (a wave's lanes
-  // cover 64 consecutive candidates per round)
+  // 2. aggregated scores: per candidate over the 16 head lanes, then lane
+  // (kg, m) takes candidate 16 (m / 4) + 4 kg + m % 4 of the pass into the
+  // wave's top list (64 candidates per pass, one per lane)
   uint64_t cur = 0ull;
   if (slots > 0) {
-    for (int base = kWave * w; base < fr.n_cand; base += kIdxThreads) {
-      const int c = base + lane;
-      uint64_t key = 0ull;
-      if (c < fr.n_cand) {
-        float s[16];
-        head_scores(c, s);
-        float a;
-        if constexpr (AGG == kAggSum) {
-          a = 0.f;
-          for (int h = 0; h < G; ++h) a += s[h];
-        } else if constexpr (AGG == kAggMax) {
-          a = s[0];
-          for (int h = 1; h < G; ++h) a = fmaxf(a, s[h]);
-        } else {
-          a = 0.f;
-          for (int h = 0; h < G; ++h) a += __expf(s[h] - head_m[h]) / head_z[h];
-        }
-        key = make_key(a, c);
+    float hm = 0.f, hz = 1.f;
+    if constexpr (AGG == kAggSoftmax) {
+      if (m < G) {
+        hm = head_m[m];
+        hz = head_z[m];
       }
-      cur = topk_fold(cur, key, slots);
+    }
+    for (int base = kWave * w; base < fr.n_cand; base += kIdxThreads) {
+      f32x4_t acc[4];
+      pass_scores(base, acc);
+      float red[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = acc[t][v];
+          if constexpr (AGG == kAggMax) x = m < G ? x : -__builtin_inff();
+          if constexpr (AGG == kAggSoftmax) x = m < G ? __expf(x - hm) / hz : 0.f;
+#pragma unroll
+          for (int d = 1; d < 16; d <<= 1) {
+            const float o = xor_lane_f32(x, d);
+            x = AGG == kAggMax ? fmaxf(x, o) : x + o;
+          }
+          red[t][v] = x;
+        }
+      const int t_me = m >> 2, v_me = m & 3;
+      float a = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (t == t_me && v == v_me) a = red[t][v];
+      const int c = base + 16 * t_me + 4 * kg + v_me;
+      cur = topk_fold(cur, c < fr.n_cand ? make_key(a, c) : 0ull, slots);
     }
   }
   cur = merge_wave_lists<kIdxWaves>(lists, cur, slots > 0 ? slots : 1);
