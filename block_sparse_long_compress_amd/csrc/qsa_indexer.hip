@@ -71,10 +71,10 @@ __global__ __launch_bounds__(256) void indexer_keys_kernel(const float* __restri
 }
 
 
-// One workgroup per (sequence, query row, KV head).
+// One workgroup per (sequence, query row, KV head), 4 or 8 waves.
 // 1. the G query heads are projected into LDS (already scaled);
-// 2. each thread scores its candidates c = tid, tid + 256, ...: the G head
-//    scores of the candidate (its indexer key read as float4s), aggregated;
+// 2. each wave scores 64 candidates per pass with fp32 MFMA, the G head
+//    scores of each candidate aggregated across the product's head columns;
 //    with the softmax aggregation a first pass finds every head's maximum
 //    and normaliser over the row's candidates and a second pass scores;
 // 3. per-wave top lists, merged, and the row's selection written as the
