@@ -86,7 +86,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
     int hkv, int G, int bs, int top_k, float scale, int keep_tail) {
   constexpr int kIdxWaves = kIdxThreads / kWave;
   __shared__ __align__(16) float qi[16 * DI];
-  __shared__ __align__(16) float wq_s[D * DI];  // W_q, staged once per workgroup
   __shared__ __align__(16) float qs[16 * D];    // the group's query heads, as float
   __shared__ uint64_t lists[kIdxWaves][kWave];
   __shared__ float red_m[kIdxWaves][16], red_z[kIdxWaves][16];
@@ -102,27 +101,30 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
   const Frame fr = row_frame(p, bs, keep_tail);
   const int slots = frame_slots(fr, top_k);
 
-  // 1. projected, scaled query heads: W_q and the heads staged in LDS with
-  // 16-byte loads (all issued before the first store), then one output per
-  // thread and step, the d terms summed in ascending order
+  // 1. projected, scaled query heads by fp32 MFMA: the heads (as float, in
+  // LDS) as operand A, W_q read straight from memory as operand B; wave w
+  // computes the 16 outputs 16n .. 16n+15 (n = w, w + waves, ...) of every
+  // head, the d terms in steps of 4 (the MFMA's own sum within a step)
   const T* qh = q + ((b * q_len + t) * hq + (int64_t)g * G) * D;
-  {
-    constexpr int NW4 = D * DI / 4 / kIdxThreads;  // float4s of W_q per thread
-    f32x4_t wv[NW4];
-#pragma unroll
-    for (int i = 0; i < NW4; ++i) wv[i] = *reinterpret_cast<const f32x4_t*>(w_q + 4 * (tid + kIdxThreads * i));
-    for (int i = tid; i < G * D / 4; i += kIdxThreads)
-      *reinterpret_cast<f32x4_t*>(&qs[4 * i]) = load4_f32(qh + 4 * i);
-#pragma unroll
-    for (int i = 0; i < NW4; ++i) *reinterpret_cast<f32x4_t*>(&wq_s[4 * (tid + kIdxThreads * i)]) = wv[i];
-  }
+  for (int i = tid; i < G * D / 4; i += kIdxThreads)
+    *reinterpret_cast<f32x4_t*>(&qs[4 * i]) = load4_f32(qh + 4 * i);
   __syncthreads();
-  for (int o = tid; o < G * DI; o += kIdxThreads) {
-    const int h = o / DI, e = o % DI;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < D; ++j) acc = __builtin_fmaf(qs[h * D + j], wq_s[j * DI + e], acc);
-    qi[o] = acc * scale;
+  {
+    const int pk = lane >> 4, pm = lane & 15;
+    for (int n = w; n < DI / 16; n += kIdxWaves) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int u = 0; u < D / 16; ++u) {
+        const int d0 = 16 * u + 4 * pk;
+        f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+        if (pm < G) a = *reinterpret_cast<const f32x4_t*>(&qs[pm * D + d0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(a[e], w_q[(int64_t)(d0 + e) * DI + 16 * n + pm], acc);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (4 * pk + v < G) qi[(4 * pk + v) * DI + 16 * n + pm] = acc[v] * scale;
+    }
   }
   __syncthreads();
 
