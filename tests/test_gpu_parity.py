@@ -13,6 +13,7 @@ import torch
 
 import block_sparse_long_compress_amd as qsa
 import qsa_synth as S
+from oracle import qsa_oracle as O
 from gpu_common import Case, check_compress, check_rows, from_device, log
 
 pytestmark = pytest.mark.gpu
@@ -465,3 +466,40 @@ def test_decode_step_ragged(w, lens):
         err = (o1[0].float() - out[bb].float()).abs().max().item()
         assert err <= 2e-2, f"sequence {bb}: output differs from the single-sequence step by {err}"
 
+
+
+TIE_CASES = [
+    W(kv_len=3000, top_k=16, block_size=32),                      # prefill row path
+    W(kv_len=3000, top_k=24, block_size=32),                      # prefill threshold-select tile path
+    W(kv_len=2000, top_k=12, block_size=32, keep_tail=True),      # row path, keep-tail frame
+    W(mode="decode", batch=2, kv_len=64 * 3000, top_k=16),        # split decode path (chunk lists)
+]
+
+
+@pytest.mark.parametrize("w", TIE_CASES, ids=lambda w: case_id(w) + "-" + w.mode)
+def test_equal_scores_keep_smallest_ids(w):
+    """Zero queries give every candidate the same score: each row keeps its smallest candidate ids (and its
+    forced block), on every selection path; the outputs match the oracle over that selection."""
+    case = Case(w, seed=7)
+    case.Q = np.zeros_like(case.Q)
+    case.q = torch.zeros_like(case.q)
+    bs, k = w.block_size, w.top_k
+    if w.mode == "prefill":
+        sel, out, scores, _ = run_prefill(case)
+        q_len, pos0 = w.kv_len, 0
+    else:
+        sel, out, scores, _ = run_decode(case)
+        q_len, pos0 = 1, w.kv_len - 1
+    for bb in range(w.batch):
+        for t in range(q_len):
+            n_cand, forced = O.selection_frame(pos0 + t, bs, w.keep_tail)
+            kept = list(range(min(n_cand, k - 1))) + ([forced] if forced is not None else [])
+            want = sorted(kept) + [-1] * (k - len(kept))
+            for g in range(w.n_kv_heads):
+                assert sel[bb, t, g].tolist() == want, f"row {(bb, t, g)}"
+    rows = all_rows(w, q_len)
+    if len(rows) > 600:
+        rng = np.random.default_rng(3)
+        rows = [rows[i] for i in sorted(rng.choice(len(rows), 600, replace=False))]
+    st = check_rows(case, sel, out, rows, pos0, scores_gpu=scores)
+    log(f"equal scores ({w.mode}, k={k}): {st}")
