@@ -92,12 +92,15 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   float* kc_row = k_comp + ((int64_t)b * hkv + g) * nb_cap * D;
 
   // 1. the block completed by the new token (if any): its mean goes to
-  // k_comp for later steps and to LDS, since with keep_tail it is a candidate
-  // of this step. The last wave computes it, as the compression kernel does.
+  // k_comp for later steps and, with keep_tail (where it is a candidate of
+  // this step), to LDS first. A wave computes it as the compression kernel
+  // does. In the default frame it is the token's own block, never a
+  // candidate: with several slices per row, slice 0 stores it during the
+  // attention phase instead, off the scan's critical path (see 3.).
   const bool closes = kv_len % BS == 0;
   const int c_new = (int)(kv_len / BS) - 1;
   const bool new_is_cand = closes && c_new < fr.n_cand;
-  if (closes && w == kStepWaves - 1) {  // every slice needs it; slice 0 stores it
+  auto compress_new = [&](bool to_lds) {
     constexpr int VEC = 8;             // bf16 per 16-byte load
     constexpr int LPK = D / VEC;       // lanes covering one key row
     constexpr int RPL = kWave / LPK;   // rows per wave-wide load
@@ -128,10 +131,15 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
       for (int e = 0; e < VEC; e += 4) {
         const f32x4_t val = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
         if (split == 0) *reinterpret_cast<f32x4_t*>(dst + e) = val;
-        *reinterpret_cast<f32x4_t*>(&knew[c0 + e]) = val;
+        if (to_lds) *reinterpret_cast<f32x4_t*>(&knew[c0 + e]) = val;
       }
     }
-  }
+  };
+  // deferred when the row has slices: slice 0's last wave then holds few or
+  // no attention units (with one slice per row every wave has units, and the
+  // compression measured cheaper here, during the scan)
+  const bool defer_new = closes && !new_is_cand && n_split > 1;
+  if (closes && !defer_new && w == kStepWaves - 1) compress_new(new_is_cand);  // slice 0 stores it
 
   // 2. scores and the top list of each wave (candidates read from k_comp; the
   // new block, when it competes, from LDS below)
@@ -187,6 +195,9 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the closed block of the default frame (not a candidate) when deferred:
+  // stored by slice 0's last wave, which holds the fewest units of the slice
+  if (defer_new && split == 0 && w == kStepWaves - 1) compress_new(false);
   const float scale_log2 = scale * 1.4426950408889634f / (Q8 ? (float)D : 1.0f);
   const Q8Cache rq = Q8 ? Q8Cache{q8.k + kv_off * D, q8.v + kv_off * D, q8.ks + kv_off * (D / 32),
                                   q8.vs + kv_off * (D / 32)}

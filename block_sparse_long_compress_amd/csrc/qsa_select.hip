@@ -518,17 +518,26 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
   int32_t* sel_row = sel + off;
   float* score_row = sel_scores ? sel_scores + off : nullptr;
-  if (close_block >= 0 && ch == n_chunks - 1) {
-    // a decode step's closed block, compressed before it is scored (with
-    // keep_tail it is this chunk's last candidate)
-    if (w == 0)
-      compress_block_wave<T, D>(k_cache + ((b * hkv + g) * kv_cap + close_block * bs) * D, bs,
-                                k_comp_w + ((b * hkv + g) * nb_cap + close_block) * D, nullptr);
+  // A decode step's closed block: with keep_tail it is this row's last
+  // candidate, compressed by the last chunk before it scores; in the default
+  // frame it is the token's own block, never a candidate, and the first
+  // workgroup of the row to post its list stores it (below), off the path
+  // to the merge.
+  auto compress_closed = [&]() {
+    compress_block_wave<T, D>(k_cache + ((b * hkv + g) * kv_cap + close_block * bs) * D, bs,
+                              k_comp_w + ((b * hkv + g) * nb_cap + close_block) * D, nullptr);
+  };
+  const bool close_first = close_block >= 0 && keep_tail;
+  if (close_first && ch == n_chunks - 1) {
+    if (w == 0) compress_closed();
     __syncthreads();
   }
 
   if (slots == 0) {  // nothing to score: the forced block alone
-    if (ch == 0 && w == 0) finalize_row(0ull, 0, fr.forced, top_k, sel_row, score_row);
+    if (ch == 0 && w == 0) {
+      finalize_row(0ull, 0, fr.forced, top_k, sel_row, score_row);
+      if (close_block >= 0 && !close_first) compress_closed();
+    }
     return;
   }
   // Each lane sums its own 4 dims of the group's queries: no barrier, so the
@@ -547,7 +556,10 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
   }
   cur = merge_wave_lists(smem.lists, cur, slots);
   if (n_chunks == 1) {
-    if (w == 0) finalize_row(cur, slots, fr.forced, top_k, sel_row, score_row);
+    if (w == 0) {
+      finalize_row(cur, slots, fr.forced, top_k, sel_row, score_row);
+      if (close_block >= 0 && !close_first) compress_closed();
+    }
     return;
   }
   // Several chunks per row: the chunk's list goes out with device-coherent
@@ -563,10 +575,13 @@ __global__ __launch_bounds__(256) void select_split_kernel(const T* __restrict__
     const uint32_t prev = __hip_atomic_fetch_add(counters + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = prev == (uint32_t)(n_chunks - 1);
     if (last) __hip_atomic_store(counters + row, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    smem.last_wg = last ? 1 : 0;
+    smem.last_wg = last ? 1 : (prev == 0u ? 2 : 0);  // 2: the first to arrive (never the last: n_chunks > 1)
   }
   __syncthreads();
-  if (!smem.last_wg) return;
+  if (smem.last_wg != 1) {
+    if (smem.last_wg == 2 && w == 0 && close_block >= 0 && !close_first) compress_closed();
+    return;
+  }
   if (n_chunks * slots <= kSmallMergeKeys) {
     if (w == 0) merge_lists_small(rs, n_chunks, sm, slots, fr.forced, top_k, smem.lists[0], sel_row, score_row);
   } else {
