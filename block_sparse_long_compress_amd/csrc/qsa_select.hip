@@ -680,6 +680,12 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
                          s.keep_tail, plan.n_chunks, kc, kcw, kv_cap, close_block);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || !pick) return e;
+    } else if (close_block >= 0) {
+      // no candidate to score (default frame, the new token closes block 0):
+      // the score pass that would compress the closed block does not run, so
+      // compress it here; later steps score it
+      const hipError_t e = launch_compress(s, k_cache, kv_cap, close_block, close_block + 1, kcw, st);
+      if (e != hipSuccess || !pick) return e;
     }
     if (!pick) return hipSuccess;
     hipLaunchKernelGGL(select_large_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, st, sel, sel_scores,

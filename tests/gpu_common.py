@@ -8,7 +8,7 @@ import torch
 
 import qsa_synth as S
 from oracle import qsa_oracle as O
-from qsa_check import BF16_ABS_TOL, F32_REL_TOL, check_selection_frame, jaccard
+from qsa_check import check_output_row, check_selection_frame, jaccard
 
 
 def log(msg: str) -> None:
@@ -75,13 +75,18 @@ def check_rows(case: Case, sel: np.ndarray, out: np.ndarray, rows, q_pos0: int, 
                check_output=True) -> dict:
     """Selection (acceptance rule) and output parity for the given (b, t, g) rows.
 
+    Outputs are compared with the oracle's attention over the GPU's own
+    (validated) selection by :func:`qsa_check.check_output_row`: bf16 within
+    the 2e-2 acceptance bound and the per-row companion bound, fp32 within
+    1e-5 of each row's largest output.
+
     ``sel`` is ``[b][q_len][Hkv][k]``, ``out`` ``[b][q_len][Hq][d]`` (GPU, as float32).
     """
     w = case.w
     G, Bs, k = w.group, w.block_size, w.top_k
     kc = case.k_comp64()
     stats = {"clear": 0, "ambiguous": 0, "jaccard": []}
-    max_err = 0.0
+    max_err = max_ratio = 0.0
     for b, t, g in rows:
         p = q_pos0 + t
         n_cand, forced = O.selection_frame(p, Bs, w.keep_tail)
@@ -104,14 +109,11 @@ def check_rows(case: Case, sel: np.ndarray, out: np.ndarray, rows, q_pos0: int, 
         if check_output:
             ref = O.attend_given_selection(qg, case.K[b, g], case.V[b, g], row_sel, p, Bs, case.scale)
             got = out[b, t, g * G:(g + 1) * G].astype(np.float64)
-            err = np.abs(got - ref)
-            if w.dtype == "bf16":
-                assert err.max() <= BF16_ABS_TOL, f"row {(b, t, g)}: bf16 error {err.max():.3e}"
-            else:
-                lim = F32_REL_TOL * np.abs(ref).max(axis=1, keepdims=True)
-                assert (err <= lim).all(), f"row {(b, t, g)}: fp32 error {(err / lim).max():.3e} x tolerance"
-            max_err = max(max_err, float(err.max()))
+            ratio = check_output_row(got, ref, w.dtype, where=f"row {(b, t, g)}:")
+            max_ratio = max(max_ratio, ratio)
+            max_err = max(max_err, float(np.abs(got - ref).max()))
     stats["max_err"] = max_err
+    stats["max_err_over_row_bound"] = round(max_ratio, 4)
     stats["mean_jaccard"] = float(np.mean(stats["jaccard"])) if stats["jaccard"] else 1.0
     del stats["jaccard"]
     return stats

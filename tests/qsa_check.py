@@ -9,6 +9,12 @@ equal the oracle's exactly; otherwise every kept candidate must score at
 least ``s_m - tol`` and every dropped one at most ``s_m1 + tol`` with
 ``tol = REL_GAP * max(|s_m|, |s_m1|)``.
 
+Outputs: bf16 results must lie within ``BF16_ABS_TOL`` absolute of the
+oracle (the acceptance bound), and, per (row, head), within
+``BF16_ROW_REL_TOL * max|o_ref| + BF16_ROW_ABS_FLOOR`` (the companion bound
+of :func:`check_output_row`), which a one-block gather error cannot pass.
+fp32 results must lie within ``F32_REL_TOL`` of the row's largest output.
+
 Overlap between two selections is reported as the Jaccard index
 ``|A ∩ B| / |A ∪ B|`` ("Qwen4 in llama.cpp: Dissecting PR #27742", section
 "QSA Is an Address-Selection Problem, Not a New Attention Equation").
@@ -20,10 +26,65 @@ import numpy as np
 REL_GAP = 1e-3
 BF16_ABS_TOL = 2e-2
 F32_REL_TOL = 1e-5
+# Companion bound of a bf16 output row (one query head's d outputs), derived
+# from the arithmetic the attention kernels do in bf16:
+#  * the output is rounded once to bf16: at most 2^-9 of |o| per element;
+#  * each softmax weight is rounded to bf16 (relative error <= 2^-9) before
+#    the PV product, and numerator and denominator use the same rounded
+#    weights, so the output stays an exact weighted average whose weights are
+#    perturbed by independent errors of at most 2^-9: the error of an element
+#    behaves like a sum of n random terms of size 2^-9 * w_t * |v_t - o|,
+#    about 0.6 * 2^-9 * sigma / sqrt(n) per element and below 2 * 2^-9 * the
+#    row's largest |o| (itself about 2.5 * sigma / sqrt(n)) at the tail of
+#    the rows checked;
+#  * scores and accumulators are float32 (relative 2^-24 per operation),
+#    negligible next to the two terms above.
+# 2^-7 = 4 * 2^-9 covers their sum with room to spare; the absolute floor
+# covers rows whose outputs are all near zero. Swapping one kept block for
+# another moves an output row by far more (about a quarter of its largest
+# element on the sigma-0.5 workloads), which the absolute bound of 2e-2 does
+# not see when outputs are ~0.05.
+BF16_ROW_REL_TOL = 2.0 ** -7
+BF16_ROW_ABS_FLOOR = 1e-4
 
 
 class SelectionMismatch(AssertionError):
     pass
+
+
+class OutputMismatch(AssertionError):
+    pass
+
+
+def output_row_bound(ref, rel: float = BF16_ROW_REL_TOL, floor: float = BF16_ROW_ABS_FLOOR) -> np.ndarray:
+    """Companion bound of every output row: ``rel * max_e |ref| + floor`` over the last axis (kept)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    return rel * np.abs(ref).max(axis=-1, keepdims=True) + floor
+
+
+def check_output_row(got, ref, dtype: str, rel: float = BF16_ROW_REL_TOL, floor: float = BF16_ROW_ABS_FLOOR,
+                     where: str = "") -> float:
+    """Check GPU outputs ``got`` against oracle outputs ``ref`` (rows on the last axis).
+
+    bf16: every element within ``BF16_ABS_TOL`` (the acceptance bound) and
+    every row within :func:`output_row_bound` (the companion bound). fp32:
+    every row within ``F32_REL_TOL`` of its largest reference output.
+    Returns the largest ratio of error to the row bound (<= 1 when it passes);
+    raises :class:`OutputMismatch` otherwise.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    if dtype == "bf16":
+        if not err.max() <= BF16_ABS_TOL:
+            raise OutputMismatch(f"{where} bf16 error {err.max():.3e} above {BF16_ABS_TOL}")
+        lim = output_row_bound(ref, rel, floor)
+    else:
+        lim = F32_REL_TOL * np.abs(ref).max(axis=-1, keepdims=True) + 1e-30
+    ratio = float((err / lim).max()) if err.size else 0.0
+    if not ratio <= 1.0:
+        raise OutputMismatch(f"{where} {dtype} output error {ratio:.3f} x its row bound (max abs {err.max():.3e})")
+    return ratio
 
 
 def jaccard(a, b) -> float:

@@ -374,6 +374,10 @@ STEP_CASES = [
     W(mode="decode", batch=2, kv_len=32 * 700 + 5, top_k=129, block_size=32, head_dim=64),  # large-k, whole units
     W(mode="decode", batch=2, kv_len=16 * 3000, n_q_heads=16, n_kv_heads=1, top_k=200, block_size=16),  # G = 16
     W(mode="decode", batch=1, kv_len=3, top_k=513, block_size=4, keep_tail=True),           # no candidate yet
+    # k > 64, default frame, the new token closes block 0: no candidate to score, the block is still compressed
+    W(mode="decode", batch=1, kv_len=4, top_k=100, block_size=4),
+    W(mode="decode", batch=2, kv_len=64, top_k=129, block_size=64),
+    W(mode="decode", batch=2, kv_len=32, top_k=70, block_size=32, dtype="f32", sigma=1.0),
     W(mode="decode", batch=3, kv_len=4 * 700, top_k=513, block_size=4, keep_tail=True),     # fewer than k blocks
 ]
 

@@ -43,6 +43,26 @@ def test_worked_example_by_hand():
     assert O.select_in_frame(got, 3, 3, 3) == [0, 2, 3]
 
 
+def test_default_indexer_scale_by_hand():
+    """The indexer's default scale is 1/sqrt(dim): 1/8 for 64 dimensions, 1/4 for 16, and for 128 the
+    value whose square times 128 is 1. A worked example with the default scale: two identity-projected
+    heads in a 16-dimensional indexer space scoring one candidate."""
+    assert I.default_indexer_scale(64) == 0.125
+    assert I.default_indexer_scale(16) == 0.25
+    s128 = I.default_indexer_scale(128)
+    assert abs(s128 * s128 * 128 - 1.0) < 4e-16 and 0.0883 < s128 < 0.0884
+    eye = np.eye(16)
+    q = np.zeros((2, 16))
+    q[0, 0], q[1, 3] = 2.0, -1.0
+    k_idx = np.zeros((1, 16))
+    k_idx[0, 0], k_idx[0, 3] = 3.0, 4.0
+    per_head = I.head_scores(q, eye, k_idx, 1, I.default_indexer_scale(16))
+    # head 0: 2 * 3 / 4 = 1.5; head 1: -1 * 4 / 4 = -1
+    assert per_head.tolist() == [[1.5, -1.0]]
+    assert I.indexer_scores(q, eye, k_idx, 1, I.default_indexer_scale(16), I.AGG_SUM).tolist() == [0.5]
+    assert I.indexer_scores(q, eye, k_idx, 1, I.default_indexer_scale(16), I.AGG_MAX).tolist() == [1.5]
+
+
 def test_project_then_average_equals_average_then_project():
     rng = np.random.default_rng(1)
     K = rng.standard_normal((2, 3, 100, 16))

@@ -263,6 +263,45 @@ def test_dense_equivalence_below_budget(N, Bs, k, G):
         assert list(sel[0, t, 0][: own + 1]) == list(range(own + 1))
 
 
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_default_scale_is_the_library_default(d):
+    """The oracle's default scale (scale=None) is the one scaled dot-product attention uses by default:
+    torch's SDPA with ``scale=None`` takes 1/sqrt(head_dim) itself, so nothing of the oracle's is
+    passed to the reference ("Qwen Model Architecture: From Transformer to MoE...", section "Attention:
+    what the model is 'looking at'": dot-product relevance, then a weighted sum of V)."""
+    rng = np.random.default_rng(d)
+    N, Bs = 96, 8
+    k = N // Bs + 1  # dense regime: every causal block kept
+    Q = rng.standard_normal((1, N, 4, d))
+    K = rng.standard_normal((1, 2, N, d))
+    V = rng.standard_normal((1, 2, N, d))
+    out, _ = O.qsa_prefill(Q, K, V, Bs, k, scale=None)
+    G = 2
+    q = torch.from_numpy(np.ascontiguousarray(Q.transpose(0, 2, 1, 3)))
+    kk = torch.from_numpy(K).repeat_interleave(G, dim=1)
+    vv = torch.from_numpy(V).repeat_interleave(G, dim=1)
+    ref = F.scaled_dot_product_attention(q, kk, vv, is_causal=True).numpy().transpose(0, 2, 1, 3)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    # a decode row too: the last row's output with the default scale
+    o_dec, _ = O.qsa_decode(Q[:, -1], K, V, N, Bs, k, scale=None)
+    np.testing.assert_allclose(o_dec, ref[:, -1], rtol=0, atol=1e-12)
+    # and the value itself, worked by hand for d = 64: 1/sqrt(64) = 1/8
+    assert O.default_scale(64) == 0.125
+
+
+def test_default_scale_changes_the_output():
+    """The pin above has power: a scale of 1/d or sqrt(d) instead of 1/sqrt(d) moves the output."""
+    rng = np.random.default_rng(5)
+    N, Bs, d = 64, 8, 64
+    Q = rng.standard_normal((1, N, 2, d))
+    K = rng.standard_normal((1, 1, N, d))
+    V = rng.standard_normal((1, 1, N, d))
+    ref, _ = O.qsa_prefill(Q, K, V, Bs, N // Bs + 1, scale=None)
+    for wrong in (1.0 / d, math.sqrt(d), 1.0):
+        bad, _ = O.qsa_prefill(Q, K, V, Bs, N // Bs + 1, scale=wrong)
+        assert np.abs(bad - ref).max() > 1e-2
+
+
 @pytest.mark.parametrize("N,Bs,k", [(64, 4, 17), (99, 8, 13), (50, 1, 51)])
 def test_dense_equivalence_keep_tail(N, Bs, k):
     """keep_tail: with top_k - 1 slots for every complete block, sparse equals dense causal attention."""
