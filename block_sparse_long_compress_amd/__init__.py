@@ -35,6 +35,8 @@ from .binding import (  # noqa: F401
     qsa_compress_keys,
     qsa_decode_step,
     qsa_decode_step_fused,
+    qsa_decode_step_noalloc,
+    QSA_NOALLOC_SCRATCH_BYTES,
     qsa_decode_step_ragged,
     qsa_indexer_keys,
     qsa_indexer_select,

@@ -25,7 +25,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_E
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
             "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused",
             "qsa_decode_step_ragged", "qsa_indexer_keys", "qsa_indexer_select", "qsa_kv_quantize",
-            "qsa_sparse_attn_decode_q8", "qsa_decode_step_q8")
+            "qsa_sparse_attn_decode_q8", "qsa_decode_step_q8", "qsa_decode_step_noalloc")
+QSA_NOALLOC_SCRATCH_BYTES = 8 << 20  # include/qsa.h
 
 
 class QsaError(RuntimeError):
@@ -90,6 +91,8 @@ def _load() -> ctypes.CDLL:
     lib.qsa_sparse_attn_decode_q8.argtypes = [SH, P, P, P, P, P, I64, I64, P, P, P, SZ, P]
     lib.qsa_decode_step_q8.restype = ctypes.c_int
     lib.qsa_decode_step_q8.argtypes = [SH, P, P, P, P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
+    lib.qsa_decode_step_noalloc.restype = ctypes.c_int
+    lib.qsa_decode_step_noalloc.argtypes = [SH, P, P, P, P, I64, I64, P, P, P, P]
     return lib
 
 
@@ -198,6 +201,16 @@ def qsa_decode_step(shape: QsaShape, q, k, v, k_comp, kv_len: int, sel, out, sel
     _check(LIB.qsa_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_comp), kv_len, k.shape[2],
                                _ptr(sel), _ptr(sel_scores), _ptr(out), _ptr(ws), nbytes, _stream(q, stream)),
            "qsa_decode_step")
+    return out
+
+
+def qsa_decode_step_noalloc(shape: QsaShape, q, k, v, k_comp, kv_len: int, sel, out, sel_scores=None,
+                            stream=None):
+    """``qsa_decode_step`` with its workspace in the library's own device memory: nothing is allocated
+    (not even here), for callers that cannot allocate. Calls that may overlap on one GPU race."""
+    _check(LIB.qsa_decode_step_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_comp), kv_len,
+                                       k.shape[2], _ptr(sel), _ptr(sel_scores), _ptr(out), _stream(q, stream)),
+           "qsa_decode_step_noalloc")
     return out
 
 

@@ -28,6 +28,7 @@ SOURCES = [
     "qsa_decode_step.hip",
     "qsa_indexer.hip",
     "qsa_kv_q8.hip",
+    "qsa_noalloc.hip",
 ]
 
 ARCH = "gfx950"

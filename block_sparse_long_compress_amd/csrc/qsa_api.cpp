@@ -246,9 +246,15 @@ int qsa_decode_step_fused(const qsa_shape* shape, int64_t kv_len) {
   return qsa::plan_decode_step(s, kv_len).fused ? 1 : 0;
 }
 
-qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,
-                           int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out, void* ws,
-                           size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace qsa {
+// Every check of qsa_decode_step except the workspace's, in the order the
+// call makes them, including the limits of the plan the step will take: a
+// step that passes enqueues all its launches (barring a runtime failure).
+qsa_status decode_step_validate(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                const float* k_comp, int64_t kv_len, int64_t kv_cap, const int32_t* sel,
+                                const float* sel_scores, const void* out) {
   Dims s;
   qsa_status st = check_shape(shape, &s);
   if (st != QSA_OK) return st;
@@ -258,6 +264,32 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
   if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
   if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
+  if (sp.fused)
+    return (int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF ? QSA_ERR_UNSUPPORTED : QSA_OK;
+  if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
+  const qsa::SelectPlan sel_plan = qsa::plan_select(s, 1, kv_len - 1);
+  if ((int64_t)s.batch * s.hkv * (sel_plan.n_chunks > 0 ? sel_plan.n_chunks : 1) > 0x7FFFFFFF)
+    return QSA_ERR_UNSUPPORTED;
+  if (s.dtype == QSA_BF16 && sel_plan.large) {
+    if ((int64_t)s.batch * s.hkv * qsa::plan_pick_attend(s, sel_plan.n_chunks).n_split > 0x7FFFFFFF)
+      return QSA_ERR_UNSUPPORTED;
+  } else if (s.dtype == QSA_BF16) {
+    if ((int64_t)s.batch * s.hkv * qsa::plan_decode(s, kv_len).n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  }
+  return QSA_OK;
+}
+}  // namespace qsa
+
+extern "C" {
+
+qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,
+                           int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  qsa_status st = qsa::decode_step_validate(shape, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out);
+  if (st != QSA_OK) return st;
+  Dims s;
+  check_shape(shape, &s);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len);
   const StepWs lay = step_ws(s, kv_len);
@@ -265,23 +297,17 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
   char* base = static_cast<char*>(ws);
   char* sel_ws = base ? base + lay.sel_off : nullptr;
   char* part = base ? base + lay.part_off : nullptr;
-  if (sp.fused) {
-    if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (sp.fused)
     return hip_status(
         qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, base, part, hs));
-  }
   // separate launches: the selection (which also compresses the block the new
   // token closes, if any, before scoring it), then the attention
-  if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
   const qsa::SelectPlan sel_plan = qsa::plan_select(s, 1, kv_len - 1);
-  if ((int64_t)s.batch * s.hkv * (sel_plan.n_chunks > 0 ? sel_plan.n_chunks : 1) > 0x7FFFFFFF)
-    return QSA_ERR_UNSUPPORTED;
   const int64_t close_block = kv_len % s.bs == 0 ? kv_len / s.bs - 1 : -1;
   if (s.dtype == QSA_BF16 && sel_plan.large) {
     // the score pass, then one kernel that picks each row's blocks and
     // attends over them
     const qsa::PickAttendPlan pa = qsa::plan_pick_attend(s, sel_plan.n_chunks);
-    if ((int64_t)s.batch * s.hkv * pa.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
     st = hip_status(qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores, sel_ws, hs, k,
                                        close_block, false));
     if (st != QSA_OK) return st;
@@ -293,7 +319,6 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
   if (st != QSA_OK) return st;
   if (s.dtype == QSA_F32) return qsa_sparse_attn_decode(shape, q, k, v, kv_len, kv_cap, sel, out, nullptr, 0, stream);
   const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len);
-  if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   return hip_status(qsa::launch_decode(s, plan, q, k, v, kv_len, kv_cap, sel, out, base, part, hs));
 }
 

@@ -45,7 +45,8 @@
  * Ownership: the caller allocates and frees every buffer (device memory for
  * all tensors and the workspace; `shape` is host memory read during the
  * call). The library never allocates, frees, synchronises, or keeps a
- * pointer after returning. All work is enqueued on `stream` (a hipStream_t;
+ * pointer after returning (qsa_decode_step_noalloc alone uses device memory
+ * of the library's own: a fixed array, see there). All work is enqueued on `stream` (a hipStream_t;
  * NULL = the null stream), in order; results are ready when the stream
  * reaches that point.
  *
@@ -82,7 +83,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 6
+#define QSA_ABI_VERSION 7
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -339,6 +340,32 @@ qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void*
                               int8_t* k_q, int8_t* v_q, uint16_t* k_scales, uint16_t* v_scales, int64_t kv_len,
                               int64_t kv_cap, int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * qsa_decode_step with its workspace in library-owned device memory instead
+ * of a caller buffer. Same arguments, results and errors as qsa_decode_step
+ * without ws / ws_bytes; the same kernels run.
+ *   scratch   a device array of QSA_NOALLOC_SCRATCH_BYTES inside the library,
+ *             one per GPU the library runs on, held until the process ends;
+ *             its address is looked up on the first call on each device.
+ *   errors    QSA_ERR_WORKSPACE when the step's workspace
+ *             (qsa_workspace_bytes(shape, QSA_OP_DECODE_STEP, 1, kv_len))
+ *             exceeds QSA_NOALLOC_SCRATCH_BYTES; QSA_ERR_HIP when the lookup
+ *             fails; the rest as qsa_decode_step (every check runs before
+ *             anything is enqueued).
+ *   work      a small kernel zeroes the step's arrival counters in the
+ *             scratch, then the step runs; both on `stream`. Nothing is
+ *             allocated or freed.
+ *   races     every call on one GPU shares that GPU's scratch: calls that
+ *             may overlap on one GPU (other streams, other host threads)
+ *             race and must be ordered by the caller. */
+#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+qsa_status qsa_decode_step_noalloc(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                   float* k_comp, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                                   void* out, void* stream);
 
 #ifdef __cplusplus
 }

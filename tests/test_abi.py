@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 6
+    assert qsa.abi_version() == 7
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -236,3 +236,29 @@ def test_decode_step_q8_arguments(qsa):
     # the workspace of the plain step (same layout)
     need = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 4096)
     assert need > 0 and call(shr, P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, need - 1, N) == WS
+
+
+def test_decode_step_noalloc_arguments(qsa):
+    """The allocation-free decode step checks everything on the host first (nothing is launched here) and
+    rejects steps whose workspace exceeds the library's scratch array."""
+    lib = qsa.LIB
+    sh = good_shape(qsa, batch=4)
+    shr = ctypes.byref(sh)
+    P, N, MIS = ctypes.c_void_p(4096), None, ctypes.c_void_p(4100)
+    INV, UNS, WS = 1, 2, 3
+    call = lib.qsa_decode_step_noalloc
+    #            shape q  k  v  kc  kv_len kv_cap sel scores out stream
+    assert call(shr, N, P, P, P, 4096, 4096, P, N, P, N) == INV       # no query
+    assert call(shr, P, P, P, MIS, 4096, 4096, P, N, P, N) == INV     # misaligned compressed keys
+    assert call(shr, P, P, P, P, 4097, 4096, P, N, P, N) == INV       # beyond capacity
+    assert call(shr, P, P, P, P, 0, 4096, P, N, P, N) == INV
+    assert call(ctypes.byref(good_shape(qsa, head_dim=96)), P, P, P, P, 4096, 4096, P, N, P, N) == UNS
+    # a step whose workspace exceeds the scratch array: 4096 sequences at 128K
+    big = good_shape(qsa, batch=4096)
+    need = qsa.qsa_workspace_bytes(big, qsa.QSA_OP_DECODE_STEP, 1, 1 << 17)
+    assert need > qsa.QSA_NOALLOC_SCRATCH_BYTES
+    assert call(ctypes.byref(big), P, P, P, P, 1 << 17, 1 << 17, P, N, P, N) == WS
+    # the header's limit and the binding's agree
+    text = open(HEADER).read()
+    assert "#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)" in text
+    assert qsa.QSA_NOALLOC_SCRATCH_BYTES == 8 << 20
