@@ -153,8 +153,10 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
     }
     case QSA_OP_DECODE_STEP_RAGGED: {
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
+      // the decode step's layout: two arrival-counter areas, then the rest
       const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len, true);
-      return sp.fused ? sp.ws_bytes : (size_t)-1;
+      if (!sp.fused) return (size_t)-1;
+      return sp.ws_bytes > 0 ? sp.ws_bytes + qsa::counter_bytes((int64_t)s.batch * s.hkv) : 0;
     }
   }
   return (size_t)-1;
@@ -339,8 +341,10 @@ qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const v
   const qsa::StepPlan sp = qsa::plan_decode_step(s, max_kv_len, true);
   if (!sp.fused) return QSA_ERR_UNSUPPORTED;  // only the fused kernel reads per-sequence lengths
   if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  if (sp.ws_bytes > 0 && (!ws || ws_bytes < sp.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
-  char* part = ws ? static_cast<char*>(ws) + qsa::counter_bytes((int64_t)s.batch * s.hkv) : nullptr;
+  const size_t cnt = qsa::counter_bytes((int64_t)s.batch * s.hkv);
+  const size_t need = sp.ws_bytes > 0 ? sp.ws_bytes + cnt : 0;  // two counter areas, then the rest
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  char* part = ws ? static_cast<char*>(ws) + 2 * cnt : nullptr;
   return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, max_kv_len, kv_cap, sel, sel_scores, out, ws,
                                             part, static_cast<hipStream_t>(stream), kv_lens));
 }

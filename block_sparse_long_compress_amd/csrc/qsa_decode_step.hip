@@ -18,6 +18,8 @@
 // through the workspace exactly as the decode kernel merges its slices.
 // Selections equal the separate calls' (same arithmetic); outputs agree
 // within rounding (another merge order of the attention states).
+#include <cstdlib>
+
 #include "qsa_decode_unit.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -28,6 +30,19 @@ namespace qsa {
 namespace {
 
 constexpr int kStepWaves = 8;
+// Polls of a scan part waiting for the other parts' lists (each poll an
+// atomic load and a short sleep, well under a microsecond) before it scores
+// their candidates itself: far beyond the few microseconds parts that run
+// together take, and a bound on the wait when a partner is not yet running.
+// The environment variable QSA_SCAN_WAIT_POLLS overrides it (tests set 0 to
+// drive every part through the fallback).
+constexpr int kScanWaitPolls = 4096;
+int scan_wait_polls() {
+  const char* e = getenv("QSA_SCAN_WAIT_POLLS");
+  if (!e || !*e) return kScanWaitPolls;
+  const long v = strtol(e, nullptr, 10);
+  return v < 0 ? 0 : (v > (1 << 20) ? (1 << 20) : (int)v);
+}
 
 template <int D, bool ROT = false>
 struct StepSmem {
@@ -46,9 +61,10 @@ template <int D, int BS, bool Q8 = false>
 __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     float* __restrict__ k_comp, int32_t* __restrict__ sel, float* __restrict__ sel_scores, uint16_t* __restrict__ out,
-    float* __restrict__ part, uint32_t* __restrict__ counters, const int32_t* __restrict__ kv_lens,
+    float* __restrict__ part_ws, uint32_t* __restrict__ counters, uint32_t* __restrict__ scan_tickets,
+    const int32_t* __restrict__ kv_lens,
     int64_t kv_len_max, int64_t kv_cap, int hq, int hkv, int G, int top_k, float scale, int keep_tail, int bpw,
-    int n_split, int64_t n_rows, Q8Cache q8) {
+    int n_split, int n_scan, int wait_polls, int64_t n_rows, Q8Cache q8) {
   using SM = StepSmem<D, Q8>;
   constexpr int LPR = D / 4;  // lanes covering one compressed key row (float32)
   constexpr int DT = D / 16;
@@ -62,16 +78,22 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   // Several slices per row: all slices of a row on one XCD (workgroups go
   // to the 8 XCDs round-robin), so that they share its L2 copy of the row's
   // compressed keys; grid slots past the last row exit at once.
+  // Several scan parts per row (n_scan > 1: rows that fill a fraction of
+  // the GPU): part j scores the j-th share of the row's candidates, the
+  // parts exchange their top lists (2b) and each attends over the j-th
+  // slice of the selection.
   int64_t row;
-  int split;
+  int split = 0, part = 0;
   if (n_split > 1) {
     const int64_t slot = blockIdx.x / 8;
     row = (int64_t)(blockIdx.x % 8) + 8 * (slot / n_split);
     split = (int)(slot % n_split);
     if (row >= n_rows) return;
+  } else if (n_scan > 1) {
+    row = blockIdx.x / n_scan;
+    part = (int)(blockIdx.x % n_scan);
   } else {
     row = blockIdx.x;
-    split = 0;
   }
   const int64_t b = row / hkv;
   const int g = (int)(row % hkv);
@@ -130,7 +152,7 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) {
         const f32x4_t val = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
-        if (split == 0) *reinterpret_cast<f32x4_t*>(dst + e) = val;
+        if (split == 0 && part == n_scan - 1) *reinterpret_cast<f32x4_t*>(dst + e) = val;
         if (to_lds) *reinterpret_cast<f32x4_t*>(&knew[c0 + e]) = val;
       }
     }
@@ -139,22 +161,30 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   // no attention units (with one slice per row every wave has units, and the
   // compression measured cheaper here, during the scan)
   const bool defer_new = closes && !new_is_cand && n_split > 1;
-  if (closes && !defer_new && w == kStepWaves - 1) compress_new(new_is_cand);  // slice 0 stores it
+  // slice 0 (the last scan part) stores it
+  if (closes && !defer_new && w == kStepWaves - 1 && part == n_scan - 1) compress_new(new_is_cand);
 
   // 2. scores and the top list of each wave (candidates read from k_comp; the
   // new block, when it competes, from LDS below)
   const f32x4_t qv = group_sum4(q_heads + 4 * (lane % LPR), G, D);
   const int64_t n_glob = fr.n_cand - (new_is_cand ? 1 : 0);
-  uint64_t cur = 0ull;
-  if (slots > 0) {
-    for (int64_t base = (int64_t)kWave * w; base < n_glob; base += kWave * kStepWaves) {
-      const float s = dot64_rows<D>(kc_row + base * D, n_glob - base, qv);
-      const int64_t cand = base + dot64_row<D>(lane);
-      cur = topk_fold(cur, cand < n_glob ? make_key(s * scale, (int)cand) : 0ull, slots);
-    }
+  int64_t c_lo = 0, c_hi = n_glob;  // this part's candidates
+  const int64_t per_part = ((n_glob + n_scan - 1) / n_scan + kWave - 1) / kWave * kWave;
+  if (n_scan > 1) {
+    c_lo = part * per_part < n_glob ? part * per_part : n_glob;
+    c_hi = c_lo + per_part < n_glob ? c_lo + per_part : n_glob;
   }
+  uint64_t cur = 0ull;
+  auto scan = [&](int64_t lo, int64_t hi) {
+    for (int64_t base = lo + (int64_t)kWave * w; base < hi; base += kWave * kStepWaves) {
+      const float s = dot64_rows<D>(kc_row + base * D, hi - base, qv);
+      const int64_t cand = base + dot64_row<D>(lane);
+      cur = topk_fold(cur, cand < hi ? make_key(s * scale, (int)cand) : 0ull, slots);
+    }
+  };
+  if (slots > 0) scan(c_lo, c_hi);
   __syncthreads();  // knew written
-  if (new_is_cand && slots > 0 && w == 0) {
+  if (new_is_cand && slots > 0 && w == 0 && part == n_scan - 1) {
     float part = qv[0] * knew[4 * (lane % LPR)] + qv[1] * knew[4 * (lane % LPR) + 1] +
                  qv[2] * knew[4 * (lane % LPR) + 2] + qv[3] * knew[4 * (lane % LPR) + 3];
 #pragma unroll
@@ -162,10 +192,87 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
     cur = topk_fold(cur, lane == 0 ? make_key(part * scale, c_new) : 0ull, slots);
   }
   cur = merge_wave_lists<kStepWaves>(lists, cur, slots > 0 ? slots : 1);
+
+  // 2b. several scan parts: every part posts its top list (descending keys)
+  // to the workspace and marks it posted in the row's ticket word (bit j of
+  // the low byte for part j), then waits, bounded, until every part's bit is
+  // set and merges the other lists into its own: all parts hold the same
+  // selection. A part that times out (a partner not yet running) scores the
+  // other parts' candidates itself instead, with the same result. Each part
+  // then sets its bit of the second byte; the part that completes that byte
+  // resets the word for the next call.
+  // Hand-off: the lists are written with device-coherent (sc1) stores, which
+  // go through the XCD's L2 to the device-coherent level, and the posting
+  // wave waits for them to complete (s_waitcnt) before it issues the
+  // ticket's atomic, which is itself performed at the device-coherent level.
+  // A part that observes another part's posted bit has therefore observed an
+  // atomic issued after that part's stores were complete, and it reads the
+  // lists with sc1 loads, served from the device-coherent level and not from
+  // a stale L2 line of its own XCD. No release/acquire fence is needed (an
+  // agent-scope release would write back the whole L2).
+  if (n_scan > 1) {
+    uint32_t* scan_word = scan_tickets + row;
+    const uint32_t all = (1u << n_scan) - 1u;
+    const auto lrs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint32_t*>(part_ws) + row * n_scan * 2 * kWave,
+                                                       0, n_scan * 2 * kWave * 4, kBufferFlags);
+    if (w == 0) {
+      if (slots > 0 && lane < slots)
+        store2_coherent(lrs, 2 * (part * kWave + lane), (uint32_t)cur, (uint32_t)(cur >> 32));
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's list stores have completed
+      if (lane == 0) {
+        uint32_t seen = __hip_atomic_fetch_or(scan_word, 1u << part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) |
+                        (1u << part);
+        for (int poll = 0; (seen & all) != all && poll < wait_polls; ++poll) {
+          __builtin_amdgcn_s_sleep(2);
+          seen = __hip_atomic_load(scan_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        last_wg = (seen & all) == all ? 1 : 0;  // 1: every list posted
+      }
+    }
+    __syncthreads();
+    if (last_wg) {
+      if (w == 0 && slots > 0) {
+        for (int j = 0; j < n_scan; ++j) {
+          if (j == part) continue;
+          const u32x2_t x = lane < slots ? load2_coherent(lrs, 2 * (j * kWave + lane)) : u32x2_t{0u, 0u};
+          cur = topk_fold_sorted(cur, ((uint64_t)x[1] << 32) | x[0], slots);
+        }
+      }
+    } else {
+      // the other parts' candidates, scored here (and the closed block when
+      // it competes: the last part scores it from LDS, so recompute it here);
+      // wave 0 keeps this part's merged list, the other waves start afresh
+      // (their lists are in wave 0's already)
+      if (w != 0) cur = 0ull;
+      if (slots > 0) {
+        for (int j = 0; j < n_scan; ++j) {
+          if (j == part) continue;
+          const int64_t lo = j * per_part < n_glob ? j * per_part : n_glob;
+          scan(lo, lo + per_part < n_glob ? lo + per_part : n_glob);
+        }
+        if (new_is_cand && part != n_scan - 1 && w == kStepWaves - 1) compress_new(true);
+      }
+      __syncthreads();
+      if (new_is_cand && slots > 0 && w == 0 && part != n_scan - 1) {
+        float dp = qv[0] * knew[4 * (lane % LPR)] + qv[1] * knew[4 * (lane % LPR) + 1] +
+                   qv[2] * knew[4 * (lane % LPR) + 2] + qv[3] * knew[4 * (lane % LPR) + 3];
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) dp += xor_lane_f32(dp, m);
+        cur = topk_fold(cur, lane == 0 ? make_key(dp * scale, c_new) : 0ull, slots);
+      }
+      cur = merge_wave_lists<kStepWaves>(lists, cur, slots > 0 ? slots : 1);
+    }
+    if (w == 0 && lane == 0) {
+      const uint32_t done = 1u << (8 + part);
+      const uint32_t prev = __hip_atomic_fetch_or(scan_word, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (((prev | done) >> 8) == all) __hip_atomic_store(scan_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   if (w == 0) {
     // every slice holds the same selection; slice 0 writes it out
     const int64_t off = row * top_k;
-    if (split == 0) finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr, ids);
+    if (split == 0 && part == 0)
+      finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr, ids);
     else finalize_row(cur, slots, fr.forced, top_k, nullptr, nullptr, ids);
   }
   __syncthreads();
@@ -188,7 +295,9 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   } else {
     load_q_operands<D>(q_heads, G, qf);
   }
-  const int e0 = split * bpw;
+  // the attention slice: a scan part attends over its share of the selection
+  const int slice = n_scan > 1 ? part : split, n_slices = n_scan > 1 ? n_scan : n_split;
+  const int e0 = slice * bpw;
   const int n_e = top_k - e0 < bpw ? top_k - e0 : bpw;  // this slice's entries of the selection
   const int sel_mine = lane < n_e ? ids[e0 + lane] : -1;
   float m_run = -__builtin_inff(), l_run = 0.f;
@@ -205,8 +314,9 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   attend_units<D, false, Q8>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, BS, p, scale_log2,
                              big + w * kUnit * SM::RS, w, kStepWaves, m_run, l_run, o, rq);
   l_run = sum_col4(l_run);
-  finish_row_slice<D, kStepWaves, Q8>(m_run, l_run, o, big, &last_wg, out, part, counters, row, b, g, hq, G,
-                                      split, n_split);
+  float* states = n_scan > 1 ? part_ws + n_rows * n_scan * 2 * kWave : part_ws;
+  finish_row_slice<D, kStepWaves, Q8>(m_run, l_run, o, big, &last_wg, out, states, counters, row, b, g, hq, G, slice,
+                                      n_slices);
 }
 
 // Decode step with k > 64 (the released budget): after the large-k score
@@ -283,9 +393,9 @@ hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, con
                          uint32_t* counters, float* part, const int32_t* kv_lens, const Q8Cache& q8,
                          hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
-  const int64_t n_wg = plan.n_split > 1 ? 8 * ((rows + 7) / 8) * plan.n_split : rows;
+  const int64_t n_wg = plan.n_split > 1 ? 8 * ((rows + 7) / 8) * plan.n_split : rows * plan.n_scan;
   const dim3 grid((unsigned)n_wg), block(kStepWaves * kWave);
-  if (plan.n_split == 1) part = nullptr;
+  if (plan.n_split == 1 && plan.n_scan == 1) part = nullptr;
   const auto* qp = static_cast<const uint16_t*>(q);
   const auto* kp = static_cast<const uint16_t*>(k);
   const auto* vp = static_cast<const uint16_t*>(v);
@@ -293,9 +403,12 @@ hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, con
   auto kern = s.bs == 32 ? decode_step_kernel<D, 32, Q8>
                          : (s.bs == 64 ? decode_step_kernel<D, 64, Q8> : decode_step_kernel<D, 128, Q8>);
   if (s.bs != 32 && s.bs != 64 && s.bs != 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op, part, counters, kv_lens,
+  // the scan tickets: the second arrival-counter area of the step's workspace
+  uint32_t* scan_tickets = counters ? counters + counter_bytes(rows) / 4 : nullptr;
+  hipLaunchKernelGGL(kern, grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op, part, counters, scan_tickets,
+                     kv_lens,
                      kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail, plan.blocks_per_wg,
-                     plan.n_split, rows, q8);
+                     plan.n_split, plan.n_scan, plan.n_scan > 1 ? scan_wait_polls() : 0, rows, q8);
   return hipGetLastError();
 }
 
@@ -320,6 +433,7 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged, bool q8) {
   // 17.1 us per step), since the attention's latency chain shortens.
   p.blocks_per_wg = s.top_k;
   p.n_split = 1;
+  p.n_scan = 1;
   if (rows <= 32) {
     const int cap = (int)(256 / rows);
     const int n = s.top_k < cap ? s.top_k : cap;
@@ -336,9 +450,21 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged, bool q8) {
     p.blocks_per_wg = (s.top_k + 1) / 2;
     p.n_split = (s.top_k + p.blocks_per_wg - 1) / p.blocks_per_wg;
   }
+  if (p.n_split == 1 && rows < 256 && !q8) {
+    // Rows that fill less than the GPU with one workgroup each: split every
+    // row's candidate scan over up to 4 workgroups, which exchange their top
+    // lists and attend over a share of the selection each, so that the
+    // scan and the gather both stream on every CU.
+    const int64_t n = 256 / rows;
+    p.n_scan = (int)(n < 4 ? n : 4);
+    p.blocks_per_wg = (s.top_k + p.n_scan - 1) / p.n_scan;
+  }
   p.ws_bytes = p.n_split > 1 ? counter_bytes(rows) +
                                    (size_t)rows * p.n_split * (2 * s.group + s.group * s.d) * sizeof(float)
                              : 0;
+  if (p.n_scan > 1)  // the lists, then the slice states
+    p.ws_bytes = counter_bytes(rows) + (size_t)rows * p.n_scan * kWave * sizeof(uint64_t) +
+                 (size_t)rows * p.n_scan * (2 * s.group + s.group * s.d) * sizeof(float);
   return p;
 }
 

@@ -107,7 +107,8 @@ hipError_t launch_prefill(const Dims& s, const PrefillPlan& plan, const void* q,
 struct StepPlan {
   bool fused;
   int blocks_per_wg;
-  int n_split;
+  int n_split;  // workgroups attending over slices of a row's selection
+  int n_scan;   // workgroups scanning shares of a row's candidates (n_split == 1)
   size_t ws_bytes;
 };
 // ragged: a batch of sequences of their own lengths (kv_len is then the

@@ -134,7 +134,10 @@ const char* qsa_status_str(qsa_status status);
  * token, KV head): 4 bytes each, the area rounded up to 256 bytes); the last
  * workgroup of a row to finish does the row's final step and resets its
  * counter, so every call leaves that area at zero and the workspace can be
- * reused by any later call of the same op it is large enough for. The rest is
+ * reused by any later call of the same op it is large enough for. Decode-step
+ * workspaces (QSA_OP_DECODE_STEP, QSA_OP_DECODE_STEP_RAGGED) start with two
+ * such areas at fixed offsets, which every path of the step leaves at zero,
+ * so one workspace serves steps that take different paths. The rest is
  * scratch of one call. */
 size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_t kv_len);
 

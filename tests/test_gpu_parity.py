@@ -507,3 +507,49 @@ def test_equal_scores_keep_smallest_ids(w):
         rows = [rows[i] for i in sorted(rng.choice(len(rows), 600, replace=False))]
     st = check_rows(case, sel, out, rows, pos0, scores_gpu=scores)
     log(f"equal scores ({w.mode}, k={k}): {st}")
+
+
+SCAN_FALLBACK_CASES = [
+    W(mode="decode", batch=64, kv_len=5000, top_k=16),                                   # 128 rows: 2 scan parts
+    W(mode="decode", batch=40, kv_len=64 * 80, top_k=16, n_q_heads=8, n_kv_heads=2),    # 80 rows: 3 parts, closes a block
+    W(mode="decode", batch=64, kv_len=64 * 40, top_k=8, keep_tail=True),                # the closed block competes
+]
+
+
+@pytest.mark.parametrize("w", SCAN_FALLBACK_CASES, ids=case_id)
+def test_decode_step_scan_wait_fallback(w, monkeypatch):
+    """Rows whose candidate scan is split over several workgroups exchange their top lists through the
+    workspace; a part that finds a list missing when its bounded wait ends scores the other parts'
+    candidates itself. With the wait cut to nothing from the host (QSA_SCAN_WAIT_POLLS=0), the first part
+    of every row to post takes that path: the step's results must equal the normal step's bitwise, and
+    the oracle's."""
+    case = Case(w, seed=21, kv_cap=w.kv_len + 64)
+    b, hq, d, bs, k = w.batch, w.n_q_heads, w.head_dim, w.block_size, w.top_k
+    shape = qsa.shape_for(case.q, case.k, bs, k, keep_tail=w.keep_tail)
+    assert qsa.qsa_decode_step_fused(shape, w.kv_len)
+    q = case.q.view(b, hq, d)
+    results = []
+    for polls in (None, "0"):
+        if polls is None:
+            monkeypatch.delenv("QSA_SCAN_WAIT_POLLS", raising=False)
+        else:
+            monkeypatch.setenv("QSA_SCAN_WAIT_POLLS", polls)
+        k_comp = torch.full((b, w.n_kv_heads, case.kv_cap // bs, d), float("nan"), device="cuda")
+        qsa.qsa_compress_keys(shape, case.k, w.kv_len - 1, k_comp)
+        sel = torch.empty(b, w.n_kv_heads, k, dtype=torch.int32, device="cuda")
+        scores = torch.empty(b, w.n_kv_heads, k, dtype=torch.float32, device="cuda")
+        out = torch.empty_like(q)
+        qsa.qsa_decode_step(shape, q, case.k, case.v, k_comp, w.kv_len, sel, out, sel_scores=scores)
+        torch.cuda.synchronize()
+        results.append((sel, scores, out, k_comp))
+    monkeypatch.delenv("QSA_SCAN_WAIT_POLLS", raising=False)
+    (s0, c0, o0, k0), (s1, c1, o1, k1) = results
+    nb = w.kv_len // bs
+    assert torch.equal(s0, s1), "selection"
+    assert torch.equal(c0.view(torch.int32), c1.view(torch.int32)), "selection scores"
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)), "output"
+    assert torch.equal(k0[:, :, :nb], k1[:, :, :nb]), "compressed keys"
+    rows = [(bb, 0, g) for bb in range(b) for g in range(w.n_kv_heads)]
+    st = check_rows(case, s1.cpu().numpy()[:, None], from_device(o1)[:, None], rows, w.kv_len - 1,
+                    scores_gpu=c1.cpu().numpy()[:, None])
+    log(f"scan wait fallback {case_id(w)}: {st}")
