@@ -9,15 +9,9 @@
 #include "../../include/qsa.h"
 #include "qsa_internal.h"
 
-namespace qsa {
-int prefill_smem_bytes(const Dims& s, int64_t q_len, int64_t q_pos0);
-}
-
 namespace {
 
 using qsa::Dims;
-
-constexpr int kMaxLds = 160 * 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -96,10 +90,10 @@ constexpr int64_t kMaxPositions = int64_t(1) << 31;
 
 qsa_status check_prefill_limits(const Dims& s, int64_t q_len, int64_t q_pos0) {
   if (q_len > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
-  // the bf16 MFMA kernel stages whole 32-key units of one block and holds a
-  // row's selection in one 64-bit token mask
-  if (s.dtype == QSA_BF16 && (s.bs < 32 || s.top_k > 64)) return QSA_ERR_UNSUPPORTED;
-  if (s.dtype == QSA_BF16 && qsa::prefill_smem_bytes(s, q_len, q_pos0) > kMaxLds) return QSA_ERR_UNSUPPORTED;
+  // one workgroup per query row on the per-row path
+  if (s.dtype == QSA_BF16 && qsa::plan_prefill(s, q_len, q_pos0).rows &&
+      (int64_t)s.batch * q_len * s.hkv > 0x7FFFFFFF)
+    return QSA_ERR_UNSUPPORTED;
   return QSA_OK;
 }
 

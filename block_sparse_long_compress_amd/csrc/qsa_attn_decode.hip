@@ -69,6 +69,64 @@ __global__ __launch_bounds__(NW * kWave) void decode_attn_kernel(
   finish_row_slice<D, NW>(m_run, l_run, o, smem, &last_wg, out, part, counters, row, b, g, hq, G, split, n_split);
 }
 
+// Prefill rows one at a time: one 8-wave workgroup per (sequence, query
+// row, KV head), attending over the row's whole selection in chunks of 64
+// entries (one per lane) with the decode unit loop, causal at the row's own
+// position; the waves' states merge in LDS and the row is written directly.
+// This serves the shapes the tiled prefill kernel does not: blocks shorter
+// than 32 keys (gathered 32-key units) and selections of more than 64
+// blocks, such as the released budget of 512 blocks of 4 keys plus the tail
+// ("Qwen4 in llama.cpp: Dissecting PR #27742", section "QSA Is an
+// Address-Selection Problem, Not a New Attention Equation"). Every row reads
+// its own keys: rows share none of their K/V traffic, as in decode.
+template <int D, bool GATHER>
+__global__ __launch_bounds__(8 * kWave) void prefill_rows_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ sel, uint16_t* __restrict__ out, int64_t q_len, int64_t q_pos0, int64_t kv_cap,
+    int hq, int hkv, int G, int bs, int top_k, float scale_log2) {
+  constexpr int NW = 8;
+  using SM = DecodeSmem<D, NW>;
+  constexpr int DT = D / 16;
+  __shared__ __align__(16) unsigned char smem[SM::kBytes];
+  __shared__ int last_wg;
+
+  const int64_t row = blockIdx.x;           // ((b * q_len) + t) * hkv + g
+  const int64_t bt = row / hkv;             // b * q_len + t
+  const int g = (int)(row % hkv);
+  const int64_t b = bt / q_len;
+  const int64_t p = q_pos0 + bt % q_len;    // the row's absolute position
+  const int lane = lane_id(), w = wave_id();
+  const int32_t* sel_row = sel + row * top_k;
+  const int64_t kv_off = ((int64_t)b * hkv + g) * kv_cap;
+
+  u32x4_t qf[D / 32];
+  load_q_operands<D>(q + (bt * hq + (int64_t)g * G) * D, G, qf);
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int e0 = 0; e0 < top_k; e0 += kWave) {
+    const int n_e = top_k - e0 < kWave ? top_k - e0 : kWave;
+    const int sel_mine = lane < n_e ? sel_row[e0 + lane] : -1;
+    attend_units<D, GATHER>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, bs, p, scale_log2,
+                            smem + w * kUnit * SM::RS, w, NW, m_run, l_run, o);
+  }
+  l_run = sum_col4(l_run);
+  finish_row_slice<D, NW>(m_run, l_run, o, smem, &last_wg, out, nullptr, nullptr, row, bt, g, hq, G, 0, 1);
+}
+
+template <int D>
+hipError_t launch_prefill_rows_d(const Dims& s, const void* q, const void* k, const void* v, int64_t q_len,
+                                 int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  auto kern = s.bs < kUnit ? prefill_rows_kernel<D, true> : prefill_rows_kernel<D, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(8 * kWave), 0, st, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sel,
+                     static_cast<uint16_t*>(out), q_len, q_pos0, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
+                     s.scale * 1.4426950408889634f);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
                     int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, uint32_t* counters, float* part,
@@ -117,6 +175,12 @@ DecodePlan plan_decode(const Dims& s, int64_t kv_len, bool wide) {
                                    (size_t)rows * p.n_split * (2 * s.group + s.group * s.d) * sizeof(float)
                              : 0;
   return p;
+}
+
+hipError_t launch_prefill_rows(const Dims& s, const void* q, const void* k, const void* v, int64_t q_len,
+                               int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, hipStream_t st) {
+  return s.d == 64 ? launch_prefill_rows_d<64>(s, q, k, v, q_len, q_pos0, kv_cap, sel, out, st)
+                   : launch_prefill_rows_d<128>(s, q, k, v, q_len, q_pos0, kv_cap, sel, out, st);
 }
 
 hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,

@@ -751,11 +751,18 @@ hipError_t launch_d(const Dims& s, const PrefillPlan& plan, const void* q, const
 
 }  // namespace
 
+int prefill_smem_bytes(const Dims& s, int64_t q_len, int64_t q_pos0);
+
 PrefillPlan plan_prefill(const Dims& s, int64_t q_len, int64_t q_pos0) {
   PrefillPlan p{};
   const int w = waves_for(s.group, s.d);
   p.rows_per_wg = (w - producers_for(w)) * ncg_per_wave(s.group, s.d) * (16 / s.group);
-  if (s.dtype != 1) {
+  // The tiled kernel stages whole 32-key units of one block, holds a tile
+  // row's selection in 64-bit token masks and keeps its block lists in LDS;
+  // other bf16 shapes run one query row per workgroup.
+  p.rows = s.dtype == 1 && (s.bs < 32 || s.top_k > 64 || prefill_smem_bytes(s, q_len, q_pos0) > 160 * 1024);
+  if (s.dtype != 1 || p.rows) {
+    p.rows_per_wg = 1;
     p.ws_bytes = 0;
     return p;
   }
@@ -778,6 +785,7 @@ int prefill_smem_bytes(const Dims& s, int64_t q_len, int64_t q_pos0) {
 hipError_t launch_prefill(const Dims& s, const PrefillPlan& plan, const void* q, const void* k, const void* v,
                           int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* ws,
                           hipStream_t st) {
+  if (plan.rows) return launch_prefill_rows(s, q, k, v, q_len, q_pos0, kv_cap, sel, out, st);
   return s.d == 64 ? launch_d<64>(s, plan, q, k, v, q_len, q_pos0, kv_cap, sel, out, ws, st)
                    : launch_d<128>(s, plan, q, k, v, q_len, q_pos0, kv_cap, sel, out, ws, st);
 }

@@ -92,10 +92,15 @@ hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q
 
 // Prefill attention -------------------------------------------------------------
 struct PrefillPlan {
+  bool rows;        // bf16 shapes the tiled kernel does not serve: one workgroup per query row
   int rows_per_wg;
   size_t ws_bytes;
 };
 PrefillPlan plan_prefill(const Dims& s, int64_t q_len, int64_t q_pos0);
+// bf16 prefill one query row per workgroup (decode unit loop, causal at the
+// row's position, any block size, any top_k); no workspace.
+hipError_t launch_prefill_rows(const Dims& s, const void* q, const void* k, const void* v, int64_t q_len,
+                               int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, hipStream_t st);
 hipError_t launch_prefill(const Dims& s, const PrefillPlan& plan, const void* q, const void* k, const void* v,
                           int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* ws,
                           hipStream_t st);

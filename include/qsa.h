@@ -58,8 +58,8 @@
  *   QSA_ERR_UNSUPPORTED  valid but not implemented: d not in {64,128},
  *                        Bs not a power of two in [4,128], k > 513,
  *                        G not in {1,2,4,8,16}; selection with k > 64 and
- *                        more than 65536 candidates per row; bf16 prefill
- *                        attention with Bs < 32 or k > 64; too many blocks
+ *                        more than 65536 candidates per row; too many
+ *                        blocks or rows for a launch
  *   QSA_ERR_WORKSPACE    ws_bytes below qsa_workspace_bytes(...) or ws NULL
  *                        while bytes are needed
  *   QSA_ERR_HIP          a kernel launch was rejected by the runtime
@@ -188,6 +188,11 @@ qsa_status qsa_sparse_attn_decode(const qsa_shape* shape, const void* q, const v
  * (same passage as decode, every row with its own selection; causal inside
  * the own block). q, out: [b][q_len][Hq][d]; k, v: [b][Hkv][kv_cap][d]
  * holding at least q_pos0 + q_len positions; sel: [b][q_len][Hkv][k].
+ * bf16: blocks of 32 keys or more with top_k <= 64 run as tiles of query
+ * rows sharing staged K/V (the workspace holds a copy of V in the MFMA
+ * operand order); shorter blocks and larger top_k (the released budget of
+ * 512 blocks of 4 keys plus the tail) run one query row per workgroup, with
+ * no workspace. float32 runs one query row per wave, no workspace.
  * ws: device scratch of qsa_workspace_bytes(shape, QSA_OP_PREFILL, q_len, q_pos0 + q_len). */
 qsa_status qsa_sparse_attn_prefill(const qsa_shape* shape, const void* q, const void* k, const void* v,
                                    int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel,

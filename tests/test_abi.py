@@ -102,9 +102,12 @@ def test_op_specific_limits(qsa):
     """Shapes every op accepts except the one whose kernels lack the path (checked before any launch)."""
     lib = qsa.LIB
     P = ctypes.c_void_p(4096)
+    # bf16 prefill attention serves every block size and top_k (short blocks and k > 64 one query row per
+    # workgroup, without a workspace): no UNSUPPORTED for them, and their workspace is 0 bytes
     for kw in (dict(block_size=16), dict(top_k=65), dict(block_size=4, top_k=513, keep_tail=1)):
-        sh = ctypes.byref(good_shape(qsa, **kw))
-        assert lib.qsa_sparse_attn_prefill(sh, P, P, P, 64, 0, 64, P, P, P, 1 << 30, None) == 2
+        sh = good_shape(qsa, **kw)
+        assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_PREFILL, 2048, 2048) == 0
+        assert lib.qsa_sparse_attn_prefill(ctypes.byref(sh), P, P, P, 0, 0, 64, P, P, P, 0, None) == 1  # invalid
     # k > 64 selection holds at most 65536 candidates per row
     sh = good_shape(qsa, block_size=4, top_k=513, keep_tail=1)
     n = 4 * 65536

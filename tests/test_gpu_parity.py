@@ -69,6 +69,14 @@ PREFILL_CASES = [
     W(kv_len=300, dtype="f32", sigma=1.0, head_dim=64, n_q_heads=4, n_kv_heads=2, block_size=8, top_k=5),
     W(kv_len=700, dtype="f32", sigma=1.0, head_dim=64, n_q_heads=2, n_kv_heads=1, block_size=4, top_k=100,
       keep_tail=True),
+    # bf16, one query row per workgroup: blocks shorter than 32 keys (gathered units), k > 64
+    W(kv_len=300, head_dim=64, n_q_heads=4, n_kv_heads=2, block_size=8, top_k=5),
+    W(kv_len=1500, block_size=16, top_k=20),
+    W(kv_len=700, head_dim=64, n_q_heads=2, n_kv_heads=1, block_size=4, top_k=100, keep_tail=True),
+    W(kv_len=3000, block_size=64, top_k=80),                                    # k > 64, whole-block units
+    # the released budget (512 blocks of 4 keys plus the tail, keep-tail frame): dense up to 2051 cached
+    # positions, the first discard at 2052 (rows 2050 and 2051), sparse rows after
+    W(kv_len=2600, block_size=4, top_k=513, keep_tail=True),
 ]
 
 
@@ -93,6 +101,8 @@ CHUNKED_CASES = [
     (W(batch=1, kv_len=64 * 300 + 5, top_k=16), 64 * 300 - 100),
     (W(batch=2, kv_len=32 * 400 + 31, top_k=9, head_dim=64, block_size=32, keep_tail=True), 32 * 400 - 70),
     (W(batch=1, kv_len=64 * 260, top_k=12, dtype="f32", sigma=1.0), 64 * 260 - 129),
+    # the released budget, rows past a long prefix (one query row per workgroup)
+    (W(batch=1, kv_len=4 * 5000 + 2, top_k=513, block_size=4, keep_tail=True), 4 * 5000 - 300),
 ]
 
 
