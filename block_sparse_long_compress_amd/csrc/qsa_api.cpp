@@ -129,6 +129,8 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       return 0;
     case QSA_OP_SELECT:
       if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
+      // k > 64 serves at most kMaxCandLarge candidates per row
+      if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return (size_t)-1;
       return qsa::plan_select(s, q_len, kv_len - q_len).ws_bytes;
     case QSA_OP_DECODE:
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
@@ -139,6 +141,8 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       return qsa::plan_prefill(s, q_len, kv_len - q_len).ws_bytes;
     case QSA_OP_DECODE_STEP: {
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
+      if (!qsa::plan_decode_step(s, kv_len).fused && s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge)
+        return (size_t)-1;  // the selection's large-k limit
     {
       // the plain step's and the 8-bit step's (same layout; the latter may split rows more)
       const size_t a = step_ws(s, kv_len).total, b8 = step_ws(s, kv_len, true).total;

@@ -123,7 +123,9 @@ int qsa_abi_version(void);
 const char* qsa_status_str(qsa_status status);
 
 /* Bytes of device workspace the given op needs for these sizes (0 if none;
- * (size_t)-1 if the arguments are invalid). op is one of QSA_OP_*.
+ * (size_t)-1 if the arguments are invalid or the op does not serve the
+ * shape: selection, and decode steps that select separately, with k > 64
+ * over more than 65536 candidates per row). op is one of QSA_OP_*.
  * QSA_OP_SELECT and QSA_OP_PREFILL take q_len and kv_len = q_pos0 + q_len;
  * QSA_OP_DECODE takes kv_len (q_len ignored).
  * QSA_OP_DECODE_STEP_RAGGED takes the longest sequence's length as kv_len
