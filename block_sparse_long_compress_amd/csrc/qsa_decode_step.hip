@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
     float* __restrict__ part_ws, uint32_t* __restrict__ counters, uint32_t* __restrict__ scan_tickets,
     const int32_t* __restrict__ kv_lens,
     int64_t kv_len_max, int64_t kv_cap, int hq, int hkv, int G, int top_k, float scale, int keep_tail, int bpw,
-    int n_split, int n_scan, int wait_polls, int64_t n_rows, Q8Cache q8) {
+    int n_split, int n_scan, int n_attend, int wait_polls, int64_t n_rows, Q8Cache q8) {
   using SM = StepSmem<D, Q8>;
   constexpr int LPR = D / 4;  // lanes covering one compressed key row (float32)
   constexpr int DT = D / 16;
@@ -79,9 +79,9 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   // to the 8 XCDs round-robin), so that they share its L2 copy of the row's
   // compressed keys; grid slots past the last row exit at once.
   // Several scan parts per row (n_scan > 1: rows that fill a fraction of
-  // the GPU): part j scores the j-th share of the row's candidates, the
-  // parts exchange their top lists (2b) and each attends over the j-th
-  // slice of the selection.
+  // the GPU, or long rows): part j scores the j-th share of the row's
+  // candidates, the parts exchange their top lists (2b), and the first
+  // n_attend parts each attend over a slice of the selection.
   int64_t row;
   int split = 0, part = 0;
   if (n_split > 1) {
@@ -194,56 +194,71 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   cur = merge_wave_lists<kStepWaves>(lists, cur, slots > 0 ? slots : 1);
 
   // 2b. several scan parts: every part posts its top list (descending keys)
-  // to the workspace and marks it posted in the row's ticket word (bit j of
-  // the low byte for part j), then waits, bounded, until every part's bit is
-  // set and merges the other lists into its own: all parts hold the same
-  // selection. A part that times out (a partner not yet running) scores the
-  // other parts' candidates itself instead, with the same result. Each part
-  // then sets its bit of the second byte; the part that completes that byte
-  // resets the word for the next call.
+  // to the workspace and counts itself in the row's ticket word (low 16
+  // bits: parts posted), then waits, bounded, until every part has posted,
+  // and merges every list: all parts hold the same selection. A part that
+  // times out (a partner not yet running) scores the other parts'
+  // candidates itself instead, with the same result. Each part then counts
+  // itself done (high 16 bits); the part completing that count resets the
+  // word for the next call (by then every part has stopped polling it).
   // Hand-off: the lists are written with device-coherent (sc1) stores, which
   // go through the XCD's L2 to the device-coherent level, and the posting
   // wave waits for them to complete (s_waitcnt) before it issues the
   // ticket's atomic, which is itself performed at the device-coherent level.
-  // A part that observes another part's posted bit has therefore observed an
+  // A part that observes another part's count has therefore observed an
   // atomic issued after that part's stores were complete, and it reads the
   // lists with sc1 loads, served from the device-coherent level and not from
   // a stale L2 line of its own XCD. No release/acquire fence is needed (an
   // agent-scope release would write back the whole L2).
   if (n_scan > 1) {
     uint32_t* scan_word = scan_tickets + row;
-    const uint32_t all = (1u << n_scan) - 1u;
     const auto lrs = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint32_t*>(part_ws) + row * n_scan * 2 * kWave,
                                                        0, n_scan * 2 * kWave * 4, kBufferFlags);
+    const bool attends = part < n_attend;
     if (w == 0) {
       if (slots > 0 && lane < slots)
         store2_coherent(lrs, 2 * (part * kWave + lane), (uint32_t)cur, (uint32_t)(cur >> 32));
       __builtin_amdgcn_s_waitcnt(0);  // this wave's list stores have completed
-      if (lane == 0) {
-        uint32_t seen = __hip_atomic_fetch_or(scan_word, 1u << part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) |
-                        (1u << part);
-        for (int poll = 0; (seen & all) != all && poll < wait_polls; ++poll) {
+      if (lane == 0 && !attends) {
+        // a part that does not attend is done once its list is posted
+        const uint32_t prev = __hip_atomic_fetch_add(scan_word, 1u | (1u << 16), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if ((int)(prev >> 16) + 1 == n_scan) __hip_atomic_store(scan_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0 && attends) {
+        uint32_t seen = __hip_atomic_fetch_add(scan_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        for (int poll = 0; (int)(seen & 0xFFFFu) < n_scan && poll < wait_polls; ++poll) {
           __builtin_amdgcn_s_sleep(2);
           seen = __hip_atomic_load(scan_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        last_wg = (seen & all) == all ? 1 : 0;  // 1: every list posted
+        last_wg = (int)(seen & 0xFFFFu) >= n_scan ? 1 : 0;  // 1: every list posted
       }
     }
+    if (!attends) return;
     __syncthreads();
+    // wave 0 keeps this part's merged list; the other waves (whose lists are
+    // in it already) start afresh and fold the other parts' lists, or score
+    // their candidates, and the waves' lists merge below
+    if (w != 0) cur = 0ull;
     if (last_wg) {
-      if (w == 0 && slots > 0) {
-        for (int j = 0; j < n_scan; ++j) {
-          if (j == part) continue;
-          const u32x2_t x = lane < slots ? load2_coherent(lrs, 2 * (j * kWave + lane)) : u32x2_t{0u, 0u};
-          cur = topk_fold_sorted(cur, ((uint64_t)x[1] << 32) | x[0], slots);
+      if (slots > 0) {
+        // the other parts' lists, several loads in flight per wave, then folded
+        constexpr int kLoads = 4;
+        for (int j0 = w; j0 < n_scan; j0 += kStepWaves * kLoads) {
+          u32x2_t x[kLoads];
+#pragma unroll
+          for (int i = 0; i < kLoads; ++i) {
+            const int j = j0 + i * kStepWaves;
+            x[i] = (j < n_scan && j != part && lane < slots) ? load2_coherent(lrs, 2 * (j * kWave + lane))
+                                                           : u32x2_t{0u, 0u};
+          }
+#pragma unroll
+          for (int i = 0; i < kLoads; ++i) cur = topk_fold_sorted(cur, ((uint64_t)x[i][1] << 32) | x[i][0], slots);
         }
       }
     } else {
       // the other parts' candidates, scored here (and the closed block when
-      // it competes: the last part scores it from LDS, so recompute it here);
-      // wave 0 keeps this part's merged list, the other waves start afresh
-      // (their lists are in wave 0's already)
-      if (w != 0) cur = 0ull;
+      // it competes: the last part scores it from LDS, so recompute it here)
       if (slots > 0) {
         for (int j = 0; j < n_scan; ++j) {
           if (j == part) continue;
@@ -260,12 +275,11 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
         for (int m = 1; m < LPR; m <<= 1) dp += xor_lane_f32(dp, m);
         cur = topk_fold(cur, lane == 0 ? make_key(dp * scale, c_new) : 0ull, slots);
       }
-      cur = merge_wave_lists<kStepWaves>(lists, cur, slots > 0 ? slots : 1);
     }
+    cur = merge_wave_lists<kStepWaves>(lists, cur, slots > 0 ? slots : 1);
     if (w == 0 && lane == 0) {
-      const uint32_t done = 1u << (8 + part);
-      const uint32_t prev = __hip_atomic_fetch_or(scan_word, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (((prev | done) >> 8) == all) __hip_atomic_store(scan_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev = __hip_atomic_fetch_add(scan_word, 1u << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int)(prev >> 16) + 1 == n_scan) __hip_atomic_store(scan_word, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (w == 0) {
@@ -296,7 +310,7 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
     load_q_operands<D>(q_heads, G, qf);
   }
   // the attention slice: a scan part attends over its share of the selection
-  const int slice = n_scan > 1 ? part : split, n_slices = n_scan > 1 ? n_scan : n_split;
+  const int slice = n_scan > 1 ? part : split, n_slices = n_scan > 1 ? n_attend : n_split;
   const int e0 = slice * bpw;
   const int n_e = top_k - e0 < bpw ? top_k - e0 : bpw;  // this slice's entries of the selection
   const int sel_mine = lane < n_e ? ids[e0 + lane] : -1;
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   attend_units<D, false, Q8>(qf, k + kv_off * D, v + kv_off * D, sel_mine, n_e, BS, p, scale_log2,
                              big + w * kUnit * SM::RS, w, kStepWaves, m_run, l_run, o, rq);
   l_run = sum_col4(l_run);
-  float* states = n_scan > 1 ? part_ws + n_rows * n_scan * 2 * kWave : part_ws;
+  float* states = n_scan > 1 ? part_ws + n_rows * n_scan * 2 * kWave : part_ws;  // [row][n_attend] states
   finish_row_slice<D, kStepWaves, Q8>(m_run, l_run, o, big, &last_wg, out, states, counters, row, b, g, hq, G, slice,
                                       n_slices);
 }
@@ -408,33 +422,32 @@ hipError_t launch_step_d(const Dims& s, const StepPlan& plan, const void* q, con
   hipLaunchKernelGGL(kern, grid, block, 0, st, qp, kp, vp, k_comp, sel, sel_scores, op, part, counters, scan_tickets,
                      kv_lens,
                      kv_len, kv_cap, s.hq, s.hkv, s.group, s.top_k, s.scale, s.keep_tail, plan.blocks_per_wg,
-                     plan.n_split, plan.n_scan, plan.n_scan > 1 ? scan_wait_polls() : 0, rows, q8);
+                     plan.n_split, plan.n_scan, plan.n_attend, plan.n_scan > 1 ? scan_wait_polls() : 0, rows, q8);
   return hipGetLastError();
 }
 
 }  // namespace
 
 StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged, bool q8) {
+  (void)ragged;
   StepPlan p{};
   p.fused = false;
   if (s.dtype != 1 || s.top_k > 64 || s.bs < 32) return p;
-  // A workgroup streams its row's compressed keys alone: worth it while the
-  // row is short (the per-CU read rate bounds it) or the rows alone fill
-  // the GPU (then HBM bounds it either way). A ragged batch always runs
-  // fused (kv_len is then the longest sequence's length).
-  const int64_t rows = (int64_t)s.batch * s.hkv;
-  const int64_t row_bytes = max_candidates(s, kv_len) * s.d * 4;
-  if (row_bytes > (512 << 10) && rows < 64 && !ragged) return p;
   p.fused = true;
-  // Few rows: slices of the selection down to one block per workgroup, as
-  // long as the grid stays within 256 workgroups. Every slice repeats the
-  // (L2-resident) scan; more, shorter slices still measured faster at 32K
-  // positions (1, 2, 4, 8, 16 slices per row: 24.1, 22.3, 18.4, 17.3,
-  // 17.1 us per step), since the attention's latency chain shortens.
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  const int64_t cand = max_candidates(s, kv_len);
+  const bool long_rows = cand * s.d * 4 > (512 << 10);  // compressed keys of a row beyond 512 KiB
   p.blocks_per_wg = s.top_k;
   p.n_split = 1;
   p.n_scan = 1;
-  if (rows <= 32) {
+  p.n_attend = 1;
+  // Few short rows: slices of the selection down to one block per
+  // workgroup, as long as the grid stays within 256 workgroups. Every slice
+  // repeats the (L2-resident) scan; more, shorter slices still measured
+  // faster at 32K positions (1, 2, 4, 8, 16 slices per row: 24.1, 22.3,
+  // 18.4, 17.3, 17.1 us per step), since the attention's latency chain
+  // shortens.
+  if (rows <= 32 && !long_rows) {
     const int cap = (int)(256 / rows);
     const int n = s.top_k < cap ? s.top_k : cap;
     if (n > 1) {
@@ -442,7 +455,7 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged, bool q8) {
       p.n_split = (s.top_k + p.blocks_per_wg - 1) / p.blocks_per_wg;
     }
   }
-  if (q8 && rows > 32) {
+  if (q8 && rows > 32 && !long_rows) {
     // over the 8-bit cache the attention phase is latency-bound (each unit
     // waits for its codes, then widens them): two slices per row, each
     // rescanning the row's compressed keys, measured 48.6 us against 54.2 us
@@ -450,21 +463,33 @@ StepPlan plan_decode_step(const Dims& s, int64_t kv_len, bool ragged, bool q8) {
     p.blocks_per_wg = (s.top_k + 1) / 2;
     p.n_split = (s.top_k + p.blocks_per_wg - 1) / p.blocks_per_wg;
   }
-  if (p.n_split == 1 && rows < 256 && !q8) {
-    // Rows that fill less than the GPU with one workgroup each: split every
-    // row's candidate scan over up to 4 workgroups, which exchange their top
-    // lists and attend over a share of the selection each, so that the
-    // scan and the gather both stream on every CU.
-    const int64_t n = 256 / rows;
-    p.n_scan = (int)(n < 4 ? n : 4);
-    p.blocks_per_wg = (s.top_k + p.n_scan - 1) / p.n_scan;
+  if (p.n_split == 1 && rows < 256 && (!q8 || long_rows)) {
+    // Rows that leave CUs idle with one workgroup each, or that are long:
+    // split every row's candidate scan over several workgroups (at least
+    // 256 candidates each, at most 64 per row and one round of the GPU's 256
+    // CUs), which exchange their top lists. The first n_attend of them
+    // attend over a share of the selection each: as many as give every
+    // wave of a workgroup one 32-key unit (8 units), so that the slices to
+    // merge stay few; the others are done once their list is posted.
+    int64_t n = 256 / rows;
+    const int64_t by_cand = (cand + 255) / 256;
+    if (by_cand < n) n = by_cand;
+    if (n > 64) n = 64;
+    if (n > 1) {
+      p.n_scan = (int)n;
+      const int per_slice = (8 * kUnit + s.bs - 1) / s.bs;  // blocks giving every wave one unit
+      int n_att = (s.top_k + per_slice - 1) / per_slice;
+      if (n_att > p.n_scan) n_att = p.n_scan;
+      p.n_attend = n_att;
+      p.blocks_per_wg = (s.top_k + n_att - 1) / n_att;
+    }
   }
   p.ws_bytes = p.n_split > 1 ? counter_bytes(rows) +
                                    (size_t)rows * p.n_split * (2 * s.group + s.group * s.d) * sizeof(float)
                              : 0;
   if (p.n_scan > 1)  // the lists, then the slice states
     p.ws_bytes = counter_bytes(rows) + (size_t)rows * p.n_scan * kWave * sizeof(uint64_t) +
-                 (size_t)rows * p.n_scan * (2 * s.group + s.group * s.d) * sizeof(float);
+                 (size_t)rows * p.n_attend * (2 * s.group + s.group * s.d) * sizeof(float);
   return p;
 }
 

@@ -114,6 +114,7 @@ struct StepPlan {
   int blocks_per_wg;
   int n_split;  // workgroups attending over slices of a row's selection
   int n_scan;   // workgroups scanning shares of a row's candidates (n_split == 1)
+  int n_attend; // of those, the ones attending over a slice of the selection each
   size_t ws_bytes;
 };
 // ragged: a batch of sequences of their own lengths (kv_len is then the

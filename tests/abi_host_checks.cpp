@@ -117,8 +117,8 @@ int main() {
   expect(qsa_decode_step_ragged(&good, P, P, P, PF, reinterpret_cast<const int32_t*>(MIS4), 64, 64, PI, nullptr, P,
                                 P, 1 << 20, nullptr),
          QSA_ERR_INVALID, "ragged lengths misaligned");
-  qsa_shape big = shape(4096, 16, 2, 128, 64, 16, QSA_BF16);
-  expect(qsa_decode_step_noalloc(&big, P, P, P, PF, 131072, 131072, PI, nullptr, P, nullptr), QSA_ERR_WORKSPACE,
+  qsa_shape big = shape(64, 16, 2, 128, 4, 513, QSA_BF16, 1);
+  expect(qsa_decode_step_noalloc(&big, P, P, P, PF, 262144, 262144, PI, nullptr, P, nullptr), QSA_ERR_WORKSPACE,
          "no-alloc step beyond its scratch");
   expect(qsa_decode_step_noalloc(&good, nullptr, P, P, PF, 64, 64, PI, nullptr, P, nullptr), QSA_ERR_INVALID,
          "no-alloc step without query");

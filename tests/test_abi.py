@@ -169,7 +169,7 @@ def test_ragged_decode_step_arguments(qsa):
     ws = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 131072)
     # same per-row plan and the same layout as the plain step's workspace
     # (two arrival-counter areas, then the slice states)
-    assert ws > 0 and qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 4096) == ws
+    assert ws > 0 and qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 131072) == ws
     call = lib.qsa_decode_step_ragged
     assert call(shr, P, P, P, P, N, 64, 64, P, N, P, P, big, N) == INV           # no lengths
     assert call(shr, P, P, P, P, MIS4, 64, 64, P, N, P, P, big, N) == INV        # lengths not 4-byte aligned
@@ -182,9 +182,9 @@ def test_ragged_decode_step_arguments(qsa):
         assert call(ctypes.byref(bad), P, P, P, P, P, 4096, 4096, P, N, P, P, big, N) == UNS
         with pytest.raises(qsa.QsaError):
             qsa.qsa_workspace_bytes(bad, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 4096)
-    # few long rows: the ragged step still runs fused (the plain step would not)
+    # few long rows: one fused kernel (the rows' scans split over several workgroups), ragged or not
     one = good_shape(qsa, batch=1)
-    assert not qsa.qsa_decode_step_fused(one, 1 << 20)
+    assert qsa.qsa_decode_step_fused(one, 1 << 20)
     assert qsa.qsa_workspace_bytes(one, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 1 << 20) > 0
     assert call(ctypes.byref(one), P, P, P, P, P, 1 << 20, 1 << 20, P, N, P, P, 8, N) == WS
 
@@ -228,13 +228,14 @@ def test_decode_step_q8_arguments(qsa):
     assert call(shr, P, P, P, P, P, P, MIS, P, 4096, 4096, P, N, P, P, big, N) == INV    # scales misaligned
     assert call(shr, P, P, P, P, P, P, P, P, 4097, 4096, P, N, P, P, big, N) == INV      # beyond capacity
     assert call(shr, P, P, P, P, P, P, P, P, 0, 4096, P, N, P, P, big, N) == INV
-    # shapes the fused kernel does not serve: f32, k > 64, Bs < 32, few long rows
+    # shapes the fused kernel does not serve: f32, k > 64, Bs < 32
     for kw in (dict(dtype=qsa.QSA_F32), dict(top_k=65), dict(block_size=16)):
         bad = ctypes.byref(good_shape(qsa, batch=4, **kw))
         assert call(bad, P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, big, N) == UNS
+    # few long rows run fused too (scan split over several workgroups): the workspace is checked
     one = good_shape(qsa, batch=1)
-    assert not qsa.qsa_decode_step_fused(one, 1 << 20)
-    assert call(ctypes.byref(one), P, P, P, P, P, P, P, P, 1 << 20, 1 << 20, P, N, P, P, big, N) == UNS
+    assert qsa.qsa_decode_step_fused(one, 1 << 20)
+    assert call(ctypes.byref(one), P, P, P, P, P, P, P, P, 1 << 20, 1 << 20, P, N, P, P, 8, N) == WS
     # the workspace of the plain step (same layout)
     need = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 4096)
     assert need > 0 and call(shr, P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, need - 1, N) == WS
@@ -255,11 +256,12 @@ def test_decode_step_noalloc_arguments(qsa):
     assert call(shr, P, P, P, P, 4097, 4096, P, N, P, N) == INV       # beyond capacity
     assert call(shr, P, P, P, P, 0, 4096, P, N, P, N) == INV
     assert call(ctypes.byref(good_shape(qsa, head_dim=96)), P, P, P, P, 4096, 4096, P, N, P, N) == UNS
-    # a step whose workspace exceeds the scratch array: 4096 sequences at 128K
-    big = good_shape(qsa, batch=4096)
-    need = qsa.qsa_workspace_bytes(big, qsa.QSA_OP_DECODE_STEP, 1, 1 << 17)
+    # a step whose workspace exceeds the scratch array: the released budget (every candidate's score in
+    # the workspace) for 64 sequences of 262,144 positions
+    big = good_shape(qsa, batch=64, block_size=4, top_k=513, keep_tail=1)
+    need = qsa.qsa_workspace_bytes(big, qsa.QSA_OP_DECODE_STEP, 1, 1 << 18)
     assert need > qsa.QSA_NOALLOC_SCRATCH_BYTES
-    assert call(ctypes.byref(big), P, P, P, P, 1 << 17, 1 << 17, P, N, P, N) == WS
+    assert call(ctypes.byref(big), P, P, P, P, 1 << 18, 1 << 18, P, N, P, N) == WS
     # the header's limit and the binding's agree
     text = open(HEADER).read()
     assert "#define QSA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)" in text

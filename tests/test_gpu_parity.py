@@ -274,19 +274,19 @@ def test_workspace_reuse_across_decode_steps(w, steps):
 
 def test_decode_step_workspace_reuse():
     """A decode loop on one zero-initialised workspace whose steps switch
-    between the fused kernel (short rows, slices with arrival counters) and
-    the separate calls (split selection and split attention, each with its
-    counters): every step equals a call with a fresh workspace, so the
-    counter areas sit where every path expects them and every call leaves
-    them at zero."""
+    between the fused kernel's plans (short rows: slices of the selection
+    with arrival counters; long rows: the scan split over several
+    workgroups, with a ticket word and slice counters): every step equals a
+    call with a fresh workspace, so the counter areas sit where every plan
+    expects them and every call leaves them at zero."""
     w = W(mode="decode", batch=1, kv_len=32 * 5000 + 9, top_k=32, block_size=32, head_dim=64, n_q_heads=8,
           n_kv_heads=1)
     case = Case(w, seed=9)
     b, hq, d, bs = w.batch, w.n_q_heads, w.head_dim, w.block_size
     shape = qsa.shape_for(case.q, case.k, bs, w.top_k)
     steps = [40000, 160009, 160000, 50001, 159999, 120001, 140000, 30000, 160009]
-    fused = [qsa.qsa_decode_step_fused(shape, n) for n in steps]
-    assert any(fused) and not all(fused), fused
+    # compressed keys of 256 bytes: rows up to 2,048 candidates (65,536 positions) are short, the rest long
+    assert any(n // 32 * 256 <= 512 << 10 for n in steps) and any(n // 32 * 256 > 512 << 10 for n in steps)
     n_ws = max(qsa.qsa_workspace_bytes(shape, qsa.QSA_OP_DECODE_STEP, 1, n) for n in steps)
     ws = torch.zeros(n_ws, dtype=torch.uint8, device="cuda")
     q = case.q.view(b, hq, d)
@@ -369,8 +369,10 @@ STEP_CASES = [
     W(mode="decode", batch=2, kv_len=3000, n_q_heads=16, n_kv_heads=1, top_k=7),
     W(mode="decode", batch=2, kv_len=3000, n_q_heads=2, n_kv_heads=2, top_k=7),
     W(mode="decode", batch=40, kv_len=5000, top_k=16, n_q_heads=8, n_kv_heads=2),  # 80 rows: fused though long
-    # shapes the fused kernel leaves to the separate calls
-    W(mode="decode", batch=1, kv_len=200000, top_k=16),                     # long rows, few of them
+    # long rows, few of them: the scan split over many workgroups per row
+    W(mode="decode", batch=1, kv_len=200000, top_k=16),
+    W(mode="decode", batch=3, kv_len=64 * 9000 + 7, top_k=32, keep_tail=True),
+    W(mode="decode", batch=1, kv_len=64 * 9000, top_k=64, n_q_heads=16, n_kv_heads=1),   # closes a block
     # long rows, k <= 64: chunk lists merged in every attention slice
     W(mode="decode", batch=1, kv_len=32 * 5000 + 9, top_k=32, block_size=32, head_dim=64, n_q_heads=8,
       n_kv_heads=1),                                                         # 20 lists of 31
@@ -520,9 +522,10 @@ def test_equal_scores_keep_smallest_ids(w):
 
 
 SCAN_FALLBACK_CASES = [
-    W(mode="decode", batch=64, kv_len=5000, top_k=16),                                   # 128 rows: 2 scan parts
-    W(mode="decode", batch=40, kv_len=64 * 80, top_k=16, n_q_heads=8, n_kv_heads=2),    # 80 rows: 3 parts, closes a block
-    W(mode="decode", batch=64, kv_len=64 * 40, top_k=8, keep_tail=True),                # the closed block competes
+    W(mode="decode", batch=64, kv_len=64 * 1100 + 5, top_k=16),                          # 128 rows: 2 scan parts
+    W(mode="decode", batch=40, kv_len=64 * 2000, top_k=16, n_q_heads=8, n_kv_heads=2),  # 80 rows: 3 parts, closes a block
+    W(mode="decode", batch=64, kv_len=64 * 1040, top_k=8, keep_tail=True),              # the closed block competes
+    W(mode="decode", batch=1, kv_len=64 * 20000, top_k=32),                             # 2 long rows: 32 parts each
 ]
 
 

@@ -132,6 +132,7 @@ STEP_CASES = [
     W(batch=3, kv_len=5000, top_k=64, block_size=32, head_dim=64),
     W(batch=1, kv_len=40000, top_k=16, n_q_heads=16, n_kv_heads=1),      # G = 16
     W(batch=1, kv_len=50, top_k=4),                                       # own block only
+    W(batch=1, kv_len=64 * 5000 + 3, top_k=16),                           # long rows: the scan split over workgroups
 ]
 
 
