@@ -188,8 +188,7 @@ qsa_status qsa_score_select(const qsa_shape* shape, const void* q, int64_t q_len
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
   if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
   const qsa::SelectPlan plan = qsa::plan_select(s, q_len, q_pos0);
-  const int64_t grid = plan.tiled ? (q_len + 15) / 16 : (int64_t)s.batch * q_len * s.hkv * plan.n_chunks;
-  if (grid > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (plan.grid > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
   return hip_status(qsa::launch_select(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws,
                                        static_cast<hipStream_t>(stream)));

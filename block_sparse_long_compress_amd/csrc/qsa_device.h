@@ -225,8 +225,8 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
   return x;
 }
 
-// Same network restricted to the first N lanes' groups (N = 16, 32 or 64):
-// every group of N lanes is sorted descending on its own.
+// Same network restricted to groups of N lanes (N = 16, 32 or 64): the first
+// group is sorted descending (groups alternate direction after it).
 template <int N>
 __device__ __forceinline__ uint64_t wave_sort_desc_n(uint64_t x) {
   const int lane = lane_id();
@@ -242,6 +242,57 @@ __device__ __forceinline__ uint64_t wave_sort_desc_n(uint64_t x) {
     }
   }
   return x;
+}
+
+// Reversal inside each 16-lane row (lane i <- lane i ^ 15), DPP row_mirror.
+__device__ __forceinline__ uint64_t mirror16_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, 0x140, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), 0x140, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Every 16-lane group sorted descending on its own (bitonic, DPP steps only).
+__device__ __forceinline__ uint64_t sort16_groups_desc(uint64_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= 16; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t y = xor_lane_u64(x, j);
+      const bool lower = (lane & j) == 0;
+      const bool desc = k == 16 || (lane & k) == 0;
+      x = (lower == desc) ? (x > y ? x : y) : (x < y ? x : y);
+    }
+  }
+  return x;
+}
+
+// Per 16-lane group: the 16 largest of two descending groups a and b, in
+// descending order. max(a[i], b[15 - i]) holds exactly those 16 as a
+// bitonic sequence, which the half-cleaner steps put in order.
+__device__ __forceinline__ uint64_t prune16_desc(uint64_t a, uint64_t b) {
+  const int lane = lane_id();
+  const uint64_t r = mirror16_u64(b);
+  uint64_t x = a > r ? a : r;
+#pragma unroll
+  for (int j = 8; j > 0; j >>= 1) {
+    const uint64_t y = xor_lane_u64(x, j);
+    x = (lane & j) == 0 ? (x > y ? x : y) : (x < y ? x : y);
+  }
+  return x;
+}
+
+// The 16 largest of 256 keys held four per lane, descending in every 16-lane
+// group (so in lanes 0..15): the groups of each register are sorted, then
+// merged pairwise keeping the larger half (registers, then the groups
+// 16 and 32 lanes apart).
+__device__ __forceinline__ uint64_t top16_of_256(const uint64_t (&x)[4]) {
+  uint64_t s[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) s[p] = sort16_groups_desc(x[p]);
+  uint64_t c = prune16_desc(prune16_desc(s[0], s[1]), prune16_desc(s[2], s[3]));
+  c = prune16_desc(c, xor_lane_u64(c, 16));
+  return prune16_desc(c, xor_lane_u64(c, 32));
 }
 
 // ------------------------------------------------------------ threshold select

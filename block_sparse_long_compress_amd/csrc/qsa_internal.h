@@ -45,10 +45,11 @@ inline size_t counter_bytes(int64_t rows) { return ((size_t)rows * 4 + 255) / 25
 
 // Selection ------------------------------------------------------------------
 struct SelectPlan {
-  bool tiled;          // prefill-style tile path (rows share candidates)
+  bool tiled;          // prefill-style tile path (rows share candidates); with large, the tiled score pass
   bool large;          // top_k > 64: score pass + per-row radix select
   int chunk;           // split path: candidates per chunk (multiple of 64)
   int64_t n_chunks;    // split / large path: chunks per row (the longest row's)
+  int64_t grid;        // workgroups of the plan's largest launch
   size_t ws_bytes;
 };
 // Largest top_k of the large-k selection path (its candidate pool fits LDS).

@@ -40,12 +40,13 @@
 //    when all the lists of a row hold at most 256 keys, one wave takes them
 //    at once.
 //  * large path (k > 64, the released budget of 512 blocks): a score pass
-//    writes every candidate's score and, per chunk of 256 candidates, the
-//    chunk's 16 best keys in order; one workgroup per row then finds the
-//    cutoff by radix selection over the union of those lists, re-expands the
-//    few chunks whose 16th key still reaches the cutoff (only they can hide
-//    more kept keys), and emits the kept ids in ascending order straight from
-//    an LDS bitmap of the candidates.
+//    (per row, or, for 16 or more query rows, per tile of 16 rows sharing a
+//    chunk's compressed keys) writes every candidate's score and, per chunk
+//    of 256 candidates, the chunk's 16 best keys in order; one workgroup per
+//    row then finds the cutoff by radix selection over the union of those
+//    lists, re-expands the few chunks whose 16th key still reaches the cutoff
+//    (only they can hide more kept keys), and emits the kept ids in ascending
+//    order straight from an LDS bitmap of the candidates.
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "qsa_select_large.h"
@@ -646,6 +647,105 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
   }
 }
 
+// The score pass for many query rows (prefill): a workgroup takes a tile of
+// 16 consecutive rows of one (b, g) and one chunk of 256 candidates, which
+// the rows share (k_comp is read once per tile instead of once per row).
+// Scores come from fp32 MFMA as in the tile path; wave w scores candidates
+// 16w .. 16w + 15 of each pass of 64, and as no other wave needs them it
+// loads their compressed keys straight into its operand registers, two
+// passes ahead. Outputs are those of the per-row pass:
+// every score of every row, and per (row, chunk) the chunk's 16 best keys in
+// descending order when the row's candidates exceed the pick pool.
+// Workgroups are ordered tile-fastest, so that the tiles reading one chunk
+// run together and share its L2 copy.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void select_large_tile_kernel(
+    const T* __restrict__ q, const float* __restrict__ k_comp, uint32_t* __restrict__ ws_scores,
+    uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs,
+    float scale, int keep_tail, int64_t n_chunks, int64_t n_tiles) {
+  constexpr int QP = D + 4;  // padded row strides (floats): conflict-free 16-byte reads
+  constexpr int PASSES = kLargeChunk / kTileCands;
+  constexpr int DU = D / 16;  // 16-byte operand loads per lane and pass
+  __shared__ float qbar[kTileRows][QP];
+  __shared__ float sc[kTileRows][kLargeChunk + 4];
+
+  const int64_t tile = blockIdx.x % n_tiles;
+  const int64_t ch = (blockIdx.x / n_tiles) % n_chunks;
+  const int64_t bg = blockIdx.x / (n_tiles * n_chunks);
+  const int64_t b = bg / hkv;
+  const int g = (int)(bg % hkv);
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int64_t t0 = tile * kTileRows;
+  const int rows = (int)(q_len - t0 < kTileRows ? q_len - t0 : kTileRows);
+  const int64_t c_begin = ch * kLargeChunk;
+  // the tile's last row has the most candidates
+  const int64_t cand_end = row_frame(q_pos0 + t0 + rows - 1, bs, keep_tail).n_cand;
+  if (c_begin >= cand_end) return;  // uniform over the workgroup
+
+  for (int idx = tid; idx < kTileRows * D / 4; idx += 256) {
+    const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    if (r < rows) v = group_sum4(q + ((b * q_len + t0 + r) * hq + (int64_t)g * G) * D + e4, G, D);
+    *reinterpret_cast<f32x4_t*>(&qbar[r][e4]) = v;
+  }
+  const float* kc_src = k_comp + (bg * nb_cap) * D;
+  const int m = lane % 16, kg = lane / 16;
+  // B operands of pass p: candidate c_begin + 64p + 16w + m, dims 16u + 4kg .. + 3
+  // (candidates past the tile's last reach are read as zero)
+  auto load_pass = [&](int pass, f32x4_t (&kb)[DU]) {
+    const int64_t cand = c_begin + pass * kTileCands + 16 * w + m;
+#pragma unroll
+    for (int u = 0; u < DU; ++u)
+      kb[u] = cand < cand_end ? *reinterpret_cast<const f32x4_t*>(kc_src + cand * D + 16 * u + 4 * kg)
+                              : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  f32x4_t kb[2][DU];
+  load_pass(0, kb[0]);
+  load_pass(1, kb[1]);
+  __syncthreads();  // qbar written
+  f32x4_t qa[DU];  // A operands: row m, dims 16u + 4kg .. + 3
+#pragma unroll
+  for (int u = 0; u < DU; ++u) qa[u] = *reinterpret_cast<const f32x4_t*>(&qbar[m][16 * u + 4 * kg]);
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < DU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = mfma_f32(qa[u][e], kb[pass % 2][u][e], acc);
+    if (pass + 2 < PASSES) load_pass(pass + 2, kb[pass % 2]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[4 * kg + i][pass * kTileCands + 16 * w + m] = acc[i] * scale;
+  }
+  __syncthreads();
+  // every row's scores of the chunk (coalesced along the candidates)
+  for (int idx = tid; idx < rows * kLargeChunk; idx += 256) {
+    const int r = idx / kLargeChunk, c = idx % kLargeChunk;
+    const int64_t cand = c_begin + c;
+    if (cand < row_frame(q_pos0 + t0 + r, bs, keep_tail).n_cand) {
+      const int64_t row = (b * q_len + t0 + r) * hkv + g;
+      ws_scores[row * n_chunks * kLargeChunk + cand] = score_order_bits(sc[r][c]);
+    }
+  }
+  // the chunk's 16 best keys of each row that needs them (wave w: rows 4w .. 4w + 3)
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = 4 * w + rr;
+    if (r >= rows) break;
+    const int64_t n_cand = row_frame(q_pos0 + t0 + r, bs, keep_tail).n_cand;
+    if (n_cand <= kPoolCap || c_begin >= n_cand) continue;  // uniform over the wave
+    static_assert(kLargeChunk == 4 * kWave && kLargeList == 16, "top16_of_256");
+    uint64_t x[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int64_t cand = c_begin + p * kWave + lane;
+      x[p] = cand < n_cand ? make_key(sc[r][p * kWave + lane], (int)cand) : 0ull;
+    }
+    const uint64_t top = top16_of_256(x);
+    const int64_t row = (b * q_len + t0 + r) * hkv + g;
+    if (lane < kLargeList) ws_lists[(row * n_chunks + ch) * kLargeList + lane] = top;
+  }
+}
+
 // One workgroup per row: cutoff, then the kept ids in ascending order.
 __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
     int32_t* __restrict__ sel, float* __restrict__ sel_scores, const uint32_t* __restrict__ ws_scores,
@@ -674,7 +774,16 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
   if (plan.large) {
     uint32_t* wss = static_cast<uint32_t*>(ws);
     uint64_t* wsl = reinterpret_cast<uint64_t*>(wss + rows * plan.n_chunks * kLargeChunk);
-    if (plan.n_chunks > 0) {
+    if (plan.n_chunks > 0 && plan.tiled) {
+      // prefill rows (close_block < 0: nothing to compress)
+      const int64_t n_tiles = (q_len + kTileRows - 1) / kTileRows;
+      hipLaunchKernelGGL((select_large_tile_kernel<T, D>),
+                         dim3((unsigned)((int64_t)s.batch * s.hkv * plan.n_chunks * n_tiles)), dim3(256), 0, st, q,
+                         k_comp, wss, wsl, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.scale, s.keep_tail,
+                         plan.n_chunks, n_tiles);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess || !pick) return e;
+    } else if (plan.n_chunks > 0) {
       hipLaunchKernelGGL((select_large_score_kernel<T, D>), dim3((unsigned)(rows * plan.n_chunks)), dim3(256), 0, st,
                          q, k_comp, wss, wsl, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.scale,
                          s.keep_tail, plan.n_chunks, kc, kcw, kv_cap, close_block);
@@ -734,9 +843,15 @@ SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
     p.large = true;
     p.n_chunks = (max_cand + kLargeChunk - 1) / kLargeChunk;
     p.ws_bytes = (size_t)rows * p.n_chunks * (kLargeChunk * sizeof(uint32_t) + kLargeList * sizeof(uint64_t));
+    // many query rows: the score pass over tiles of rows sharing a chunk
+    p.tiled = q_len >= kTileRows;
+    const int64_t score_grid = p.tiled ? (int64_t)s.batch * s.hkv * p.n_chunks * ((q_len + kTileRows - 1) / kTileRows)
+                                       : rows * p.n_chunks;
+    p.grid = score_grid > rows ? score_grid : rows;
     return p;
   }
   p.tiled = q_len >= kTileRows;
+  p.grid = p.tiled ? (q_len + kTileRows - 1) / kTileRows : rows;
   if (p.tiled || max_cand <= 0) return p;
   if (rows * max_cand <= 8192 && max_cand <= 2048) {
     // small problem: one workgroup per row, no merge launch
@@ -749,6 +864,7 @@ SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
     p.chunk = 256 * u;
   }
   p.n_chunks = (max_cand + p.chunk - 1) / p.chunk;
+  p.grid = rows * p.n_chunks;
   // arrival counters (kept at zero between calls), then the chunk lists
   if (p.n_chunks > 1) p.ws_bytes = counter_bytes(rows) + (size_t)rows * p.n_chunks * (s.top_k - 1) * sizeof(uint64_t);
   return p;

@@ -103,6 +103,10 @@ CHUNKED_CASES = [
     (W(batch=1, kv_len=64 * 260, top_k=12, dtype="f32", sigma=1.0), 64 * 260 - 129),
     # the released budget, rows past a long prefix (one query row per workgroup)
     (W(batch=1, kv_len=4 * 5000 + 2, top_k=513, block_size=4, keep_tail=True), 4 * 5000 - 300),
+    # k > 64 past the pick pool (12288 candidates): the tiled score pass writes per-chunk lists
+    # (3 tiles of 16 rows, the last ragged)
+    (W(batch=1, kv_len=4 * 20000 + 2, top_k=513, block_size=4, keep_tail=True), 4 * 20000 - 40),
+    (W(batch=2, kv_len=4 * 14000 + 1, top_k=129, block_size=4, head_dim=64), 4 * 14000 - 19),
 ]
 
 
