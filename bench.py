@@ -126,15 +126,18 @@ def work_model(w, n_new_blocks: int, lens=None):
             m["attend"] = {"bytes": rows * vis * d * el * 2 + 2 * b * hq * d * el + rows * k * 4,
                            "flops": 4 * d * hq * b * vis}
     else:
-        T = w.kv_len
+        # query rows [q_pos0, kv_len) over every key below kv_len; the blocks
+        # completed before q_pos0 are already compressed
+        T, t0 = w.kv_len, w.q_pos0
+        qn = T - t0
         nb = T // bs
         rows = b * hkv
-        m["compress"] = {"bytes": rows * nb * (bs * d * el + d * 4), "flops": 0}
-        cand_sum = sum(frame(t, bs, w.keep_tail)[0] for t in range(T))
-        m["select"] = {"bytes": rows * nb * d * 4 + b * T * hq * d * el + b * T * hkv * k * 4,
+        m["compress"] = {"bytes": rows * n_new_blocks * (bs * d * el + d * 4), "flops": 0}
+        cand_sum = sum(frame(t, bs, w.keep_tail)[0] for t in range(t0, T))
+        m["select"] = {"bytes": rows * nb * d * 4 + b * qn * hq * d * el + b * qn * hkv * k * 4,
                        "flops": 2 * d * rows * cand_sum}
-        vis_sum = sum(visible_keys(t, bs, k, w.keep_tail) for t in range(T))
-        m["attend"] = {"bytes": 2 * b * T * hq * d * el + rows * T * d * el * 2 + b * T * hkv * k * 4,
+        vis_sum = sum(visible_keys(t, bs, k, w.keep_tail) for t in range(t0, T))
+        m["attend"] = {"bytes": 2 * b * qn * hq * d * el + rows * T * d * el * 2 + b * qn * hkv * k * 4,
                        "flops": 4 * d * hq * b * vis_sum}
     return m
 
@@ -215,8 +218,11 @@ class Step:
                 self.n_new_blocks = w.kv_len // bs - self.blk_begin
         else:
             self.ws_att = self._ws(qsa.QSA_OP_PREFILL, q_len, w.kv_len)
-            self.blk_begin = 0
-            self.n_new_blocks = w.kv_len // bs
+            # a prefill chunk at q_pos0: the blocks completed before it are already compressed
+            self.blk_begin = q_pos0 // bs
+            if self.blk_begin > 0:
+                qsa.qsa_compress_keys(self.shape, self.k, q_pos0, self.k_comp)
+            self.n_new_blocks = w.kv_len // bs - self.blk_begin
         torch.cuda.synchronize()
         # `calls`: the ABI calls of a step, each timed on its own; `step_calls`:
         # what one step enqueues (a decode step is the one qsa_decode_step call,
@@ -281,7 +287,7 @@ class Step:
             self.qsa.qsa_sparse_attn_decode(self.shape, self.q_dec, self.k, self.v, w.kv_len, self.sel,
                                             self.out_dec, ws=self.ws_att)
         else:
-            self.qsa.qsa_sparse_attn_prefill(self.shape, self.q, self.k, self.v, 0, self.sel, self.out,
+            self.qsa.qsa_sparse_attn_prefill(self.shape, self.q, self.k, self.v, w.q_pos0, self.sel, self.out,
                                              ws=self.ws_att)
 
 
@@ -433,14 +439,19 @@ def _cpu_prefill_worker(job):
         scale = O.default_scale(w.head_dim)
         Qs, Ks, Vs = S.gen_all(w, seed, workers=1)
         Q, K, V = (S.as_f32(x, w.dtype) for x in (Qs, Ks, Vs))
+        # blocks completed before the chunk's first row are already compressed (untimed)
+        blk0, nb = w.q_pos0 // bs, w.kv_len // bs
+        kc_old = O.compress_keys(K[:, :, : blk0 * bs], bs) if blk0 else None
         t0 = time.perf_counter()
-        kc = O.compress_keys(K, bs)
+        kc = O.compress_keys(K[:, :, blk0 * bs: nb * bs], bs)
         t_comp = time.perf_counter() - t0
+        if kc_old is not None:
+            kc = np.concatenate([kc_old, kc], axis=2)
         done, t1 = 0, time.perf_counter()
         for t in rows:
             n_cand, forced = O.selection_frame(int(t), bs, w.keep_tail)
             for g in range(w.n_kv_heads):
-                qg = Q[0, t, g * G:(g + 1) * G].astype(np.float64)
+                qg = Q[0, t - w.q_pos0, g * G:(g + 1) * G].astype(np.float64)
                 sc = O.block_scores(qg, kc[0, g], n_cand, scale)
                 sel = O.select_in_frame(sc, n_cand, forced, k)
                 O.attend_given_selection(qg, K[0, g], V[0, g], sel, int(t), bs, scale)
@@ -475,19 +486,20 @@ def cpu_baseline(w, seed, budget_s):
                           f"sequence ({total} steps in all; sequence of {n0} tokens, both KV heads: compress of "
                           f"the completed block, scores over {n_cand} candidates, top-{w.top_k} selection, "
                           f"attention); rate = sum of the workers' rates"}
-    order = np.random.default_rng(seed).permutation(w.kv_len)
+    order = w.q_pos0 + np.random.default_rng(seed).permutation(w.q_len)
     jobs = [(w, seed, order[i::n], budget_s) for i in range(n)]
     with ctx.Pool(n) as pool:
         res = pool.map(_cpu_prefill_worker, jobs)
     row_rate = sum(done / el for done, el, _ in res)
     done = sum(d for d, _, _ in res)
     t_comp = float(np.median([tc for _, _, tc in res]))
-    est = t_comp + w.kv_len / row_rate
-    return {"value": w.batch * w.kv_len / est, "unit": "tokens/s", "cores": n, "kind": "oracle",
-            "sample": f"{n} single-threaded worker processes, each {budget_s:.0f} s: compression of all "
-                      f"{w.kv_len // w.block_size} blocks ({t_comp:.3f} s) + {done} of the {w.kv_len} query rows "
-                      f"(both KV heads) in all, drawn in random order; the prompt time is one compression plus "
-                      f"every row at the pool's row rate ({row_rate:.1f} rows/s)"}
+    est = t_comp + w.q_len / row_rate
+    n_new = w.kv_len // w.block_size - w.q_pos0 // w.block_size
+    return {"value": w.batch * w.q_len / est, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{n} single-threaded worker processes, each {budget_s:.0f} s: compression of the "
+                      f"{n_new} blocks the prompt completes ({t_comp:.3f} s) + {done} of its {w.q_len} query "
+                      f"rows (both KV heads) in all, drawn in random order; the prompt time is one compression "
+                      f"plus every row at the pool's row rate ({row_rate:.1f} rows/s)"}
 
 
 # ------------------------------------------------------------- measured traffic
@@ -534,7 +546,7 @@ def record(w, st, timing, steps, seed, graph_steps):
     """The workload's figures: rate from the timed (cold) steps, roofline of its dominant call."""
     model = work_model(w, st.n_new_blocks, getattr(st, "lens", None))
     model["step"] = {"bytes": sum(m["bytes"] for m in model.values()), "flops": sum(m["flops"] for m in model.values())}
-    tokens = w.batch if w.mode == "decode" else w.batch * w.kv_len
+    tokens = w.batch if w.mode == "decode" else w.batch * w.q_len
     step_s = float(np.mean(timing["step_s"]))
     per_call = {n: float(np.mean(v)) for n, v in timing["per_call_s"].items()}
     dominant = max(per_call, key=lambda n: per_call[n])
@@ -565,6 +577,8 @@ def record(w, st, timing, steps, seed, graph_steps):
         cfg.update({"indexer_dim": w.indexer_dim, "indexer_agg": ["sum", "max", "softmax"][w.indexer_agg]})
     if w.ragged:
         cfg.update({"mean_kv_len": round(float(np.mean(st.lens)), 1), "min_kv_len": int(min(st.lens))})
+    if w.mode == "prefill" and w.q_pos0:
+        cfg.update({"q_rows": w.q_len, "q_pos0": w.q_pos0})
     return {
         "value": round(tokens / step_s, 2),
         "ms_per_step": round(1e3 * step_s, 5),

@@ -19,6 +19,9 @@ regenerated on its own):
   ``[kv_len/8, kv_len]`` (tensor id 4), the last one set to ``kv_len``; the
   inputs are generated for ``kv_len`` positions and a sequence reads only
   its first ``length`` of them.
+* A prefill workload with ``q_rows`` set has query rows only for the last
+  ``q_rows`` positions (a prefill chunk at the end of a long context); K and
+  V still cover every position.
 * The planted workload (batched decode) shifts every key of 8 chosen
   complete blocks per ``(b, kv_head)`` by ``2*sigma`` along the unit vector
   of the sum of that KV head's query heads (bf16-rounded), in float32 before
@@ -59,14 +62,17 @@ class Workload:
     indexer_dim: int = 0  # learned-indexer selection: indexer dimension (0 = the default selection)
     indexer_agg: int = 0  # its aggregation of a group's head scores: 0 sum, 1 max, 2 softmax
     kv_q8: bool = False   # decode attention over the rotated 8-bit K/V cache
+    q_rows: int = 0       # prefill: only the last q_rows positions are query rows (0 = every position)
 
     @property
     def q_len(self) -> int:
-        return self.kv_len if self.mode == "prefill" else 1
+        if self.mode != "prefill":
+            return 1
+        return self.q_rows if self.q_rows else self.kv_len
 
     @property
     def q_pos0(self) -> int:
-        return 0 if self.mode == "prefill" else self.kv_len - 1
+        return self.kv_len - self.q_len
 
     @property
     def group(self) -> int:
@@ -98,6 +104,10 @@ WORKLOADS = {
     # partial-tail slot), 262144-token context = 65536 compressed blocks
     "decode_256k_r4": Workload("decode_256k_r4", 6, "decode", 1, 262144, 16, 2, 128, 4, 513, "bf16", 0.5,
                                keep_tail=True),
+    # the same regime for a prefill chunk: the last 512 query rows of a
+    # 262144-token context (every row scores 65536 candidates)
+    "prefill_256k_r4_tail": Workload("prefill_256k_r4_tail", 10, "prefill", 1, 262144, 16, 2, 128, 4, 513, "bf16",
+                                     0.5, keep_tail=True, q_rows=512),
 }
 
 

@@ -92,6 +92,28 @@ def test_prefill_8k_workload():
     log(f"  sampled outputs: {st}")
 
 
+def test_prefill_256k_r4_tail_workload():
+    """The released budget at full context: the last 512 query rows of a 262144-token prefill (ratio 4,
+    top-513 with the partial-tail slot). Every row scores 65536 candidates, so the selection takes the
+    tiled large-k score pass with per-chunk lists, and the bf16 attention one query row per workgroup.
+    Every row's selection and sampled rows' outputs against the oracle."""
+    w = S.WORKLOADS["prefill_256k_r4_tail"]
+    log("workload prefill_256k_r4_tail: generating")
+    case = Case(w, seed=0)
+    out, sel, k_comp, scores = qsa.prefill(case.q, case.k, case.v, w.block_size, w.top_k, q_pos0=w.q_pos0,
+                                           with_scores=True, keep_tail=True)
+    torch.cuda.synchronize()
+    sel, out, scores = sel.cpu().numpy(), from_device(out), scores.cpu().numpy()
+    check_compress(case, k_comp)
+    rows = [(0, t, g) for t in range(w.q_len) for g in range(w.n_kv_heads)]
+    st = check_rows(case, sel, out, rows, w.q_pos0, scores_gpu=scores, check_output=False)
+    log(f"  selections of all {len(rows)} rows: {st}")
+    rng = np.random.default_rng(0)
+    sample = sorted(set(rng.integers(0, w.q_len, 24).tolist()) | {0, 15, 16, w.q_len - 1})
+    st = check_rows(case, sel, out, [(0, t, g) for t in sample for g in range(2)], w.q_pos0)
+    log(f"  sampled outputs: {st}")
+
+
 @pytest.fixture(scope="module")
 def batch_128k():
     w = S.WORKLOADS["decode_b64_128k"]
