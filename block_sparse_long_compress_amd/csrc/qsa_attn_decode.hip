@@ -27,7 +27,7 @@ template <int D, int NW>
 struct DecodeSmem {
   static constexpr int RS = kStageRowBytes<D>;
   static constexpr int kStage = NW * kUnit * RS;          // V staging, one 32-row slice per wave
-  static constexpr int kComb = NW * (32 + 16 * D) * 4;    // the waves' softmax states
+  static constexpr int kComb = NW * (32 + 16 * kCombStride<D>) * 4;  // the waves' softmax states
   static constexpr int kBytes = kStage > kComb ? kStage : kComb;
 };
 

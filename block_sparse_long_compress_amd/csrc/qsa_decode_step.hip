@@ -49,7 +49,7 @@ struct StepSmem {
   static constexpr int RS = kStageRowBytes<D>;
   static constexpr int kStage = kStepWaves * kUnit * RS;  // V staging, one 32-row slice per wave
   // the waves' softmax states (and, rotated cache, the workgroup's combined one)
-  static constexpr int kComb = (kStepWaves + (ROT ? 1 : 0)) * (32 + 16 * D) * 4;
+  static constexpr int kComb = (kStepWaves + (ROT ? 1 : 0)) * (32 + 16 * kCombStride<D>) * 4;
   static constexpr int kBytes = kStage > kComb ? kStage : kComb;
 };
 

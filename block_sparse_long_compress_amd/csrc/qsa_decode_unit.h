@@ -31,6 +31,11 @@ __device__ __forceinline__ int kkey(int lg, int j) { return j < 4 ? 4 * lg + j :
 
 template <int D>
 constexpr int kStageRowBytes = 2 * D + 16;  // LDS row stride of staged V (bytes)
+// Row stride (floats) of the waves' unnormalised outputs when a workgroup
+// combines them in LDS: one 16-byte slot past D, so that the 16 lanes of a
+// lane group, which write 16 rows at one column, spread over the banks.
+template <int D>
+constexpr int kCombStride = D + 4;
 
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
@@ -420,9 +425,12 @@ __device__ void finish_row_slice(float m_run, float l_run, const f32x4_t (&o)[D 
   const int lane = lane_id(), w = wave_id(), tid = threadIdx.x;
   const int lg = lane / 16, col = lane % 16;
   __syncthreads();  // staging area becomes the combine area
+  // row stride of co padded by 16 bytes: the 16 lanes of a lane group write
+  // rows 16 bytes apart in the banks, not all into the same four banks
+  constexpr int CS = kCombStride<D>;
   float* cm = reinterpret_cast<float*>(smem);  // [NW][16] running maxima
   float* cl = cm + NW * 16;                    // [NW][16] sums
-  float* co = cl + NW * 16;                    // [NW][16][D] unnormalised outputs
+  float* co = cl + NW * 16;                    // [NW][16][CS] unnormalised outputs
   if (lane < 16) {
     cm[w * 16 + col] = m_run;
     cl[w * 16 + col] = l_run;
@@ -430,11 +438,11 @@ __device__ void finish_row_slice(float m_run, float l_run, const f32x4_t (&o)[D 
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
+    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * CS + 16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
   if constexpr (ROT) {
     constexpr int EPL = D / kWave;
-    float* bm = co + NW * 16 * D;  // [16] the workgroup's maxima
+    float* bm = co + NW * 16 * CS;  // [16] the workgroup's maxima
     float* bl = bm + 16;           // [16] sums
     float* bo = bl + 16;           // [16][D] outputs, rotated back below
     for (int idx = tid; idx < G * D; idx += NT) {
@@ -446,7 +454,7 @@ __device__ void finish_row_slice(float m_run, float l_run, const f32x4_t (&o)[D 
         for (int ww = 0; ww < NW; ++ww) {
           const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
           L += f * cl[ww * 16 + h];
-          O += f * co[(ww * 16 + h) * D + e];
+          O += f * co[(ww * 16 + h) * CS + e];
         }
       }
       if (e == 0) {
@@ -505,7 +513,7 @@ __device__ void finish_row_slice(float m_run, float l_run, const f32x4_t (&o)[D 
       for (int ww = 0; ww < NW; ++ww) {
         const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);  // 0 for waves without a unit
         L += f * cl[ww * 16 + h];
-        O += f * co[(ww * 16 + h) * D + e];
+        O += f * co[(ww * 16 + h) * CS + e];
       }
       out[(b * hq + (int64_t)g * G + h) * D + e] = f32_to_bf16(O / L);
     }
@@ -524,7 +532,7 @@ __device__ void finish_row_slice(float m_run, float l_run, const f32x4_t (&o)[D 
       for (int ww = 0; ww < NW; ++ww) {
         const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
         L += f * cl[ww * 16 + h];
-        O += f * co[(ww * 16 + h) * D + e];
+        O += f * co[(ww * 16 + h) * CS + e];
       }
     }
     if (e == 0) {

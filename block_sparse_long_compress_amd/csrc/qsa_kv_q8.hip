@@ -66,7 +66,7 @@ template <int D, int NW>
 struct Q8Smem {
   static constexpr int RS = kStageRowBytes<D>;
   static constexpr int kStage = NW * kUnit * RS;
-  static constexpr int kComb = NW * (32 + 16 * D) * 4;
+  static constexpr int kComb = NW * (32 + 16 * kCombStride<D>) * 4;
   static constexpr int kBytes = kStage > kComb ? kStage : kComb;
 };
 
@@ -133,7 +133,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_attn_q8_kernel(
   __syncthreads();  // staging area becomes the combine area
   float* cm = reinterpret_cast<float*>(smem);  // [NW][16] running maxima
   float* cl = cm + NW * 16;                    // [NW][16] sums
-  float* co = cl + NW * 16;                    // [NW][16][D] unnormalised outputs
+  constexpr int CS = kCombStride<D>;           // padded row stride (conflict-free 16-byte writes)
+  float* co = cl + NW * 16;                    // [NW][16][CS] unnormalised outputs
   if (lane < 16) {
     cm[w * 16 + col] = m_run;
     cl[w * 16 + col] = l_run;
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_attn_q8_kernel(
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * D + 16 * dt + 4 * lg + i] = o[dt][i];
+    for (int i = 0; i < 4; ++i) co[(w * 16 + col) * CS + 16 * dt + 4 * lg + i] = o[dt][i];
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += NT) {
     const int h = idx / D, e = idx % D;
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_attn_q8_kernel(
       for (int ww = 0; ww < NW; ++ww) {
         const float f = __builtin_amdgcn_exp2f(cm[ww * 16 + h] - M);
         L += f * cl[ww * 16 + h];
-        O += f * co[(ww * 16 + h) * D + e];
+        O += f * co[(ww * 16 + h) * CS + e];
       }
     }
     if (e == 0) {
