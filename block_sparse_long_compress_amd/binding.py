@@ -25,7 +25,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_E
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
             "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused",
             "qsa_decode_step_ragged", "qsa_indexer_keys", "qsa_indexer_select", "qsa_kv_quantize",
-            "qsa_sparse_attn_decode_q8", "qsa_decode_step_q8", "qsa_decode_step_noalloc")
+            "qsa_sparse_attn_decode_q8", "qsa_sparse_attn_prefill_q8", "qsa_decode_step_q8",
+            "qsa_decode_step_noalloc")
 QSA_NOALLOC_SCRATCH_BYTES = 8 << 20  # include/qsa.h
 
 
@@ -89,6 +90,8 @@ def _load() -> ctypes.CDLL:
     lib.qsa_kv_quantize.argtypes = [SH, P, P, I64, I64, I64, P, P, P, P, P]
     lib.qsa_sparse_attn_decode_q8.restype = ctypes.c_int
     lib.qsa_sparse_attn_decode_q8.argtypes = [SH, P, P, P, P, P, I64, I64, P, P, P, SZ, P]
+    lib.qsa_sparse_attn_prefill_q8.restype = ctypes.c_int
+    lib.qsa_sparse_attn_prefill_q8.argtypes = [SH, P, P, P, P, P, I64, I64, I64, P, P, P]
     lib.qsa_decode_step_q8.restype = ctypes.c_int
     lib.qsa_decode_step_q8.argtypes = [SH, P, P, P, P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
     lib.qsa_decode_step_noalloc.restype = ctypes.c_int
@@ -287,6 +290,16 @@ def qsa_sparse_attn_decode_q8(shape: QsaShape, q, k_q, v_q, k_scales, v_scales, 
     _check(LIB.qsa_sparse_attn_decode_q8(ctypes.byref(shape), _ptr(q), _ptr(k_q), _ptr(v_q), _ptr(k_scales),
                                          _ptr(v_scales), kv_len, k_q.shape[2], _ptr(sel), _ptr(out), _ptr(ws), nbytes,
                                          _stream(q, stream)), "qsa_sparse_attn_decode_q8")
+    return out
+
+
+def qsa_sparse_attn_prefill_q8(shape: QsaShape, q, k_q, v_q, k_scales, v_scales, q_pos0: int, sel, out,
+                               stream=None):
+    """Prefill attention over the rotated 8-bit cache for ``q`` ``[b][q_len][Hq][d]`` at positions ``q_pos0 ..``
+    (``sel`` ``[b][q_len][Hkv][k]``); no workspace."""
+    _check(LIB.qsa_sparse_attn_prefill_q8(ctypes.byref(shape), _ptr(q), _ptr(k_q), _ptr(v_q), _ptr(k_scales),
+                                          _ptr(v_scales), q.shape[1], q_pos0, k_q.shape[2], _ptr(sel), _ptr(out),
+                                          _stream(q, stream)), "qsa_sparse_attn_prefill_q8")
     return out
 
 

@@ -439,6 +439,24 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
                                           static_cast<hipStream_t>(stream)));
 }
 
+qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, const int8_t* k_q, const int8_t* v_q,
+                                      const uint16_t* k_scales, const uint16_t* v_scales, int64_t q_len,
+                                      int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !k_q || !v_q || !k_scales || !v_scales || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_q) || !aligned16(v_q) || !aligned16(k_scales) || !aligned16(v_scales) ||
+      !aligned16(sel) || !aligned16(out))
+    return QSA_ERR_INVALID;
+  if (q_len <= 0 || q_pos0 < 0 || kv_cap <= 0 || q_pos0 + q_len > kv_cap) return QSA_ERR_INVALID;
+  if (s.dtype != QSA_BF16 || s.bs < 32) return QSA_ERR_UNSUPPORTED;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  if ((int64_t)s.batch * q_len * s.hkv > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;  // one workgroup per row
+  return hip_status(qsa::launch_prefill_q8(s, q, k_q, v_q, k_scales, v_scales, q_len, q_pos0, kv_cap, sel, out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,
                               int8_t* k_q, int8_t* v_q, uint16_t* k_scales, uint16_t* v_scales, int64_t kv_len,
                               int64_t kv_cap, int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,

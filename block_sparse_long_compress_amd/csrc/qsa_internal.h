@@ -85,6 +85,11 @@ DecodePlan plan_decode(const Dims& s, int64_t kv_len, bool wide = true);
 hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
                          int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* counters, void* part,
                          hipStream_t st);
+// Prefill attention over the rotated 8-bit cache, one workgroup per query
+// row (any top_k; Bs >= 32); no workspace.
+hipError_t launch_prefill_q8(const Dims& s, const void* q, const int8_t* kq, const int8_t* vq, const uint16_t* ks,
+                             const uint16_t* vs, int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel,
+                             void* out, hipStream_t st);
 // Decode attention over the rotated 8-bit cache (same plan and workspace as
 // launch_decode; Bs >= 32).
 hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q, const int8_t* kq, const int8_t* vq,

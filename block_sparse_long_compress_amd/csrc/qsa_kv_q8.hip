@@ -1,4 +1,5 @@
-// Rotated, 8-bit quantized K/V cache and the decode attention that reads it
+// Rotated, 8-bit quantized K/V cache and the decode and prefill attention
+// that read it
 // ("Qwen4 in llama.cpp: Dissecting PR #27742", section "Quantized KV Exposed
 // a Backend Storage Invariant": K and V are stored in a Hadamard-rotated
 // basis and quantized; attention runs in the rotated basis and its output is
@@ -209,6 +210,78 @@ __global__ __launch_bounds__(NW * kWave) void decode_attn_q8_kernel(
   else merge_slices<D, 2, 8, NT>(prs, smem, out, b, g, hq, G, n_split, tid);
 }
 
+// Prefill rows over the rotated quantized cache: one 8-wave workgroup per
+// (sequence, query row, KV head), as the bf16 prefill runs the shapes its
+// tiled kernel does not serve. The row's query heads are rotated into LDS,
+// its whole selection is attended in chunks of 64 entries (one per lane)
+// with the codes widened on load, causal at the row's own position, and the
+// waves' combined output is rotated back (H O / d) and written.
+template <int D>
+__global__ __launch_bounds__(8 * kWave) void prefill_rows_q8_kernel(
+    const uint16_t* __restrict__ q, const int8_t* __restrict__ kq, const int8_t* __restrict__ vq,
+    const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs_, const int32_t* __restrict__ sel,
+    uint16_t* __restrict__ out, int64_t q_len, int64_t q_pos0, int64_t kv_cap, int hq, int hkv, int G, int bs,
+    int top_k, float scale_log2) {
+  constexpr int NW = 8;
+  constexpr int EPL = D / kWave;
+  constexpr int DT = D / 16;
+  constexpr int RS = kStageRowBytes<D>;
+  constexpr int kStage = NW * kUnit * RS;
+  constexpr int kComb = (NW + 1) * (32 + 16 * kCombStride<D>) * 4;  // waves' states, then the rotated-back row
+  __shared__ __align__(16) unsigned char smem[kStage > kComb ? kStage : kComb];
+  __shared__ __align__(16) uint16_t qrot[16 * D];
+  __shared__ int last_wg;
+
+  const int64_t row = blockIdx.x;  // ((b * q_len) + t) * hkv + g
+  const int64_t bt = row / hkv;    // b * q_len + t
+  const int g = (int)(row % hkv);
+  const int64_t b = bt / q_len;
+  const int64_t p = q_pos0 + bt % q_len;  // the row's absolute position
+  const int lane = lane_id(), w = wave_id();
+  const int64_t kv_off = ((int64_t)b * hkv + g) * kv_cap;
+
+  const uint16_t* qh = q + (bt * hq + (int64_t)g * G) * D;
+  for (int h = w; h < G; h += NW) {
+    float x[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) x[i] = bf16_to_f32(qh[(int64_t)h * D + lane + kWave * i]);
+    fwht_wave<D>(x);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) qrot[h * D + lane + kWave * i] = f32_to_bf16(x[i]);
+  }
+  __syncthreads();
+  u32x4_t qf[D / 32];
+  load_q8_query_operands<D>(qrot, G, qf);  // the cache's dim order (attend_units' 8-bit loads)
+
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const Q8Cache cache{kq + kv_off * D, vq + kv_off * D, ks + kv_off * (D / 32), vs_ + kv_off * (D / 32)};
+  const int32_t* sel_row = sel + row * top_k;
+  for (int e0 = 0; e0 < top_k; e0 += kWave) {
+    const int n_e = top_k - e0 < kWave ? top_k - e0 : kWave;
+    const int sel_mine = lane < n_e ? sel_row[e0 + lane] : -1;
+    attend_units<D, false, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2, smem + w * kUnit * RS, w,
+                                 NW, m_run, l_run, o, cache);
+  }
+  l_run = sum_col4(l_run);
+  finish_row_slice<D, NW, true>(m_run, l_run, o, smem, &last_wg, out, nullptr, nullptr, row, bt, g, hq, G, 0, 1);
+}
+
+template <int D>
+hipError_t launch_prefill_q8_d(const Dims& s, const void* q, const int8_t* kq, const int8_t* vq, const uint16_t* ks,
+                               const uint16_t* vs, int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel,
+                               void* out, hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  // (H q).(H k) = d q.k: the 1/d of the rotation is folded into the scale
+  const float scale_log2 = s.scale * 1.4426950408889634f / (float)D;
+  hipLaunchKernelGGL((prefill_rows_q8_kernel<D>), dim3((unsigned)rows), dim3(8 * kWave), 0, st,
+                     static_cast<const uint16_t*>(q), kq, vq, ks, vs, sel, static_cast<uint16_t*>(out), q_len,
+                     q_pos0, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, scale_log2);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_quant_d(const void* k, const void* v, int8_t* kq, int8_t* vq, uint16_t* ks, uint16_t* vs,
                           int64_t kv_cap, int64_t pos_begin, int64_t n_pos, int64_t rows, hipStream_t st) {
@@ -252,6 +325,13 @@ hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q
                             const int32_t* sel, void* out, void* ws, hipStream_t st) {
   return s.d == 64 ? launch_q8_d<64>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, ws, st)
                    : launch_q8_d<128>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, ws, st);
+}
+
+hipError_t launch_prefill_q8(const Dims& s, const void* q, const int8_t* kq, const int8_t* vq, const uint16_t* ks,
+                             const uint16_t* vs, int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel,
+                             void* out, hipStream_t st) {
+  return s.d == 64 ? launch_prefill_q8_d<64>(s, q, kq, vq, ks, vs, q_len, q_pos0, kv_cap, sel, out, st)
+                   : launch_prefill_q8_d<128>(s, q, kq, vq, ks, vs, q_len, q_pos0, kv_cap, sel, out, st);
 }
 
 }  // namespace qsa

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 7
+#define QSA_ABI_VERSION 8
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -332,6 +332,18 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
                                      const uint16_t* k_scales, const uint16_t* v_scales, int64_t kv_len,
                                      int64_t kv_cap, const int32_t* sel, void* out, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* qsa_sparse_attn_prefill over the 8-bit cache: query rows at positions
+ * q_pos0 .. q_pos0+q_len-1 (q, sel and out laid out as for
+ * qsa_sparse_attn_prefill), k_q, v_q, k_scales, v_scales holding positions
+ * 0 .. q_pos0+q_len-1. Each row's query heads are rotated, its scores are
+ * (H q).(H k)/head_dim over the codes, causal at the row's own position, and
+ * its output is rotated back; one workgroup per (sequence, row, KV head), any
+ * top_k; no workspace. bf16 with Bs >= 32 only, else QSA_ERR_UNSUPPORTED
+ * (also when batch * q_len * Hkv exceeds 2^31 - 1). */
+qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, const int8_t* k_q, const int8_t* v_q,
+                                      const uint16_t* k_scales, const uint16_t* v_scales, int64_t q_len,
+                                      int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* stream);
 
 /* One decode step over the 8-bit cache: qsa_kv_quantize of the new position
  * kv_len - 1, then, in one kernel, what qsa_decode_step does (compress the

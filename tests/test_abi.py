@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 7
+    assert qsa.abi_version() == 8
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -239,6 +239,26 @@ def test_decode_step_q8_arguments(qsa):
     # the workspace of the plain step (same layout)
     need = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_DECODE_STEP, 1, 4096)
     assert need > 0 and call(shr, P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, need - 1, N) == WS
+
+
+def test_prefill_q8_arguments(qsa):
+    """Prefill over the 8-bit cache validates its arguments on the host: bf16 with Bs >= 32 only, any top_k."""
+    lib = qsa.LIB
+    sh = good_shape(qsa, batch=2)
+    shr = ctypes.byref(sh)
+    P, N, MIS = ctypes.c_void_p(4096), None, ctypes.c_void_p(4100)
+    INV, UNS = 1, 2
+    call = lib.qsa_sparse_attn_prefill_q8
+    #            shape q  kq vq ks vs q_len q_pos0 kv_cap sel out stream
+    assert call(shr, P, N, P, P, P, 64, 0, 4096, P, P, N) == INV       # no key codes
+    assert call(shr, P, P, P, MIS, P, 64, 0, 4096, P, P, N) == INV     # key scales misaligned
+    assert call(shr, P, P, P, P, P, 64, 4040, 4096, P, P, N) == INV    # rows beyond capacity
+    assert call(shr, P, P, P, P, P, 0, 0, 4096, P, P, N) == INV        # no rows
+    assert call(shr, P, P, P, P, P, 64, -1, 4096, P, P, N) == INV
+    for kw in (dict(dtype=qsa.QSA_F32), dict(block_size=16)):
+        bad = ctypes.byref(good_shape(qsa, batch=2, **kw))
+        assert call(bad, P, P, P, P, P, 64, 0, 4096, P, P, N) == UNS
+    assert call(ctypes.byref(good_shape(qsa, batch=2, head_dim=96)), P, P, P, P, P, 64, 0, 4096, P, P, N) == UNS
 
 
 def test_decode_step_noalloc_arguments(qsa):

@@ -1,10 +1,11 @@
 """GPU parity of the rotated 8-bit K/V cache path.
 
 Codes and float16 scales are integers decided in float32: they must equal
-the oracle's bit for bit. The decode attention over the cache is compared
-with the oracle's float64 attention over the same dequantized cache and the
-same selection (bf16 output tolerance), and reported against plain bf16
-attention for scale.
+the oracle's bit for bit. The decode and prefill attention over the cache
+are compared with the oracle's float64 attention over the same dequantized
+cache and the same selection (bf16 output tolerance; the prefill rows also
+against the per-row companion bound), and the decode reported against plain
+bf16 attention for scale.
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ import qsa_synth as S
 from gpu_common import Case, from_device, log
 from oracle import qsa_kv_q8 as Q
 from oracle import qsa_oracle as O
-from qsa_check import BF16_ABS_TOL
+from qsa_check import BF16_ABS_TOL, check_output_row
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +123,53 @@ def test_q8_decode_parity(w):
         worst = max(worst, err)
         vs_plain = max(vs_plain, float(np.abs(got - bf_h[bb, g * G:(g + 1) * G]).max()))
     log(f"  max error against the 8-bit oracle {worst:.2e}; largest difference from bf16 attention {vs_plain:.2e}")
+
+
+PREFILL_CASES = [
+    # (workload, first query row): prefill rows over the 8-bit cache, one workgroup per row
+    (W(mode="prefill", batch=1, kv_len=700, top_k=6), 0),                                  # every row from 0
+    (W(mode="prefill", batch=2, kv_len=1500, top_k=80, block_size=32, head_dim=64), 1100),  # k > 64: two chunks
+    (W(mode="prefill", batch=1, kv_len=64 * 40 + 7, top_k=8, keep_tail=True), 64 * 40 - 60),  # keep-tail frame
+    (W(mode="prefill", batch=1, kv_len=600, top_k=4, block_size=128, n_q_heads=16, n_kv_heads=1), 0),  # G = 16
+]
+
+
+@pytest.mark.parametrize("c", PREFILL_CASES, ids=lambda c: f"{case_id(c[0])}-from{c[1]}")
+def test_q8_prefill_parity(c):
+    """Prefill rows over the 8-bit cache against the oracle's attention over its own dequantized cache and the
+    GPU's selection (the bf16 selection path, checked elsewhere), on sampled rows of every (sequence, KV head):
+    the 2e-2 acceptance bound and the per-row companion bound."""
+    w, q_pos0 = c
+    log(f"q8 prefill {case_id(w)} from {q_pos0}")
+    case = Case(w, seed=34)
+    b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    G = hq // hkv
+    shape, kq, vq, ks, vs = quantized(case)
+    k_comp = torch.empty(b, hkv, max(1, w.kv_len // bs), d, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    q_rows = case.q[:, q_pos0:].contiguous()
+    n = w.kv_len - q_pos0
+    sel = torch.empty(b, n, hkv, k, dtype=torch.int32, device="cuda")
+    qsa.qsa_score_select(shape, q_rows, q_pos0, k_comp, w.kv_len, w.kv_len, sel)
+    out = torch.empty_like(q_rows)
+    qsa.qsa_sparse_attn_prefill_q8(shape, q_rows, kq, vq, ks, vs, q_pos0, sel, out)
+    torch.cuda.synchronize()
+    out_h, sel_h = from_device(out), sel.cpu().numpy()
+    rng = np.random.default_rng(2)
+    ts = sorted(set(rng.integers(0, n, 10).tolist()) | {0, n - 1})
+    worst = 0.0
+    for bb in range(b):
+        for g in range(hkv):
+            kq_o, ks_o = Q.quantize_cache(case.K[bb, g, :w.kv_len])  # the oracle's own cache
+            vq_o, vs_o = Q.quantize_cache(case.V[bb, g, :w.kv_len])
+            for t in ts:
+                p = q_pos0 + t
+                qg = case.Q[bb, p, g * G:(g + 1) * G].astype(np.float64)
+                selr = [int(x) for x in sel_h[bb, t, g]]
+                ref = Q.attend_q8(qg, kq_o, ks_o, vq_o, vs_o, selr, p, bs, O.default_scale(d))
+                worst = max(worst, check_output_row(out_h[bb, t, g * G:(g + 1) * G], ref, "bf16",
+                                                    where=f"row {(bb, p, g)}:"))
+    log(f"  largest error over its row bound {worst:.3f}")
 
 
 STEP_CASES = [
