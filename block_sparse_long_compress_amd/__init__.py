@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     QSA_OP_DECODE,
     QSA_OP_DECODE_STEP,
     QSA_OP_DECODE_STEP_RAGGED,
+    QSA_OP_INDEXER_SELECT,
     QSA_OP_PREFILL,
     QSA_OP_SELECT,
     QsaError,

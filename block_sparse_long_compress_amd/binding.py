@@ -20,6 +20,7 @@ LIB_PATH = os.environ.get("QSA_LIB", os.path.join(HERE, "lib", "libqsa.so"))
 QSA_F32, QSA_BF16 = 0, 1
 QSA_OP_COMPRESS, QSA_OP_SELECT, QSA_OP_DECODE, QSA_OP_PREFILL, QSA_OP_DECODE_STEP = 0, 1, 2, 3, 4
 QSA_OP_DECODE_STEP_RAGGED = 5
+QSA_OP_INDEXER_SELECT = 6
 QSA_AGG_SUM, QSA_AGG_MAX, QSA_AGG_SOFTMAX = 0, 1, 2
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_ERR_WORKSPACE", 4: "QSA_ERR_HIP"}
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
@@ -85,7 +86,7 @@ def _load() -> ctypes.CDLL:
     lib.qsa_indexer_keys.restype = ctypes.c_int
     lib.qsa_indexer_keys.argtypes = [SH, IX, P, P, I64, I64, I64, P, P]
     lib.qsa_indexer_select.restype = ctypes.c_int
-    lib.qsa_indexer_select.argtypes = [SH, IX, P, P, I64, I64, P, I64, I64, P, P, P]
+    lib.qsa_indexer_select.argtypes = [SH, IX, P, P, I64, I64, P, I64, I64, P, P, P, SZ, P]
     lib.qsa_kv_quantize.restype = ctypes.c_int
     lib.qsa_kv_quantize.argtypes = [SH, P, P, I64, I64, I64, P, P, P, P, P]
     lib.qsa_sparse_attn_decode_q8.restype = ctypes.c_int
@@ -258,11 +259,14 @@ def qsa_indexer_keys(shape: QsaShape, idx: QsaIndexer, w_k, k_comp, kv_len: int,
 
 
 def qsa_indexer_select(shape: QsaShape, idx: QsaIndexer, w_q, q, q_pos0: int, k_idx, kv_len: int, kv_cap: int, sel,
-                       sel_scores=None, stream=None):
-    """Selection scored in indexer space for ``q`` ``[b][q_len][Hq][d]`` rows at positions ``q_pos0 ..``."""
+                       sel_scores=None, ws=None, stream=None):
+    """Selection scored in indexer space for ``q`` ``[b][q_len][Hq][d]`` rows at positions ``q_pos0 ..`` (a workspace
+    only for top_k > 64)."""
     q_len = q.shape[1]
+    ws, nbytes = _workspace(shape, QSA_OP_INDEXER_SELECT, q_len, kv_len, ws, q.device)
     _check(LIB.qsa_indexer_select(ctypes.byref(shape), ctypes.byref(idx), _ptr(w_q), _ptr(q), q_len, q_pos0,
-                                  _ptr(k_idx), kv_len, kv_cap, _ptr(sel), _ptr(sel_scores), _stream(q, stream)),
+                                  _ptr(k_idx), kv_len, kv_cap, _ptr(sel), _ptr(sel_scores), _ptr(ws), nbytes,
+                                  _stream(q, stream)),
            "qsa_indexer_select")
     return sel
 

@@ -149,6 +149,12 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       return a > b8 ? a : b8;
     }
     }
+    case QSA_OP_INDEXER_SELECT:
+      if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
+      if (s.top_k <= 64) return 0;
+      // the large selection's scores and chunk lists (at most kMaxCandLarge candidates per row)
+      if (qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return (size_t)-1;
+      return qsa::plan_select(s, q_len, kv_len - q_len).ws_bytes;
     case QSA_OP_DECODE_STEP_RAGGED: {
       if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
       // the decode step's layout: two arrival-counter areas, then the rest
@@ -381,7 +387,7 @@ qsa_status qsa_indexer_keys(const qsa_shape* shape, const qsa_indexer* idx, cons
 
 qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, const float* w_q, const void* q,
                               int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_len, int64_t kv_cap,
-                              int32_t* sel, float* sel_scores, void* stream) {
+                              int32_t* sel, float* sel_scores, void* ws, size_t ws_bytes, void* stream) {
   Dims s;
   qsa_status st = check_shape(shape, &s);
   if (st != QSA_OK) return st;
@@ -392,10 +398,16 @@ qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, co
   if (!w_q || !q || !sel || !aligned16(w_q) || !aligned16(q) || !aligned16(sel)) return QSA_ERR_INVALID;
   if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
-  if (s.top_k > 64) return QSA_ERR_UNSUPPORTED;
+  if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
   if ((int64_t)s.batch * q_len * s.hkv > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   if (qsa::max_candidates(s, kv_len) > 0 && (!k_idx || !aligned16(k_idx))) return QSA_ERR_INVALID;
-  return hip_status(qsa::launch_indexer_select(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores,
+  if (s.top_k > 64) {
+    // the large selection's score and list workspace, and its list launch (rows x chunks)
+    const qsa::SelectPlan plan = qsa::plan_select(s, q_len, q_pos0);
+    if ((int64_t)s.batch * q_len * s.hkv * plan.n_chunks > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+    if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  }
+  return hip_status(qsa::launch_indexer_select(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws,
                                                static_cast<hipStream_t>(stream)));
 }
 

@@ -78,12 +78,15 @@ __global__ __launch_bounds__(256) void indexer_keys_kernel(const float* __restri
 //    with the softmax aggregation a first pass finds every head's maximum
 //    and normaliser over the row's candidates and a second pass scores;
 // 3. per-wave top lists, merged, and the row's selection written as the
-//    default selection writes it.
-template <typename T, int D, int DI, int AGG, int kIdxThreads>
+//    default selection writes it; or (LARGE, top_k > 64) every candidate's
+//    aggregated score written to ws_scores in the large selection's layout
+//    ([row][n_chunks * 256] score order bits), for its per-row pick.
+template <typename T, int D, int DI, int AGG, int kIdxThreads, bool LARGE>
 __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
     const T* __restrict__ q, const float* __restrict__ w_q, const float* __restrict__ k_idx,
-    int32_t* __restrict__ sel, float* __restrict__ sel_scores, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq,
-    int hkv, int G, int bs, int top_k, float scale, int keep_tail) {
+    int32_t* __restrict__ sel, float* __restrict__ sel_scores, uint32_t* __restrict__ ws_scores, int64_t n_chunks,
+    int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs, int top_k, float scale,
+    int keep_tail) {
   constexpr int kIdxWaves = kIdxThreads / kWave;
   __shared__ __align__(16) float qi[16 * DI];
   __shared__ __align__(16) float qs[16 * D];    // the group's query heads, as float
@@ -244,9 +247,14 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
         for (int v = 0; v < 4; ++v)
           if (t == t_me && v == v_me) a = red[t][v];
       const int c = base + 16 * t_me + 4 * kg + v_me;
-      cur = topk_fold(cur, c < fr.n_cand ? make_key(a, c) : 0ull, slots);
+      if constexpr (LARGE) {
+        if (c < fr.n_cand) ws_scores[row * n_chunks * 256 + c] = score_order_bits(a);
+      } else {
+        cur = topk_fold(cur, c < fr.n_cand ? make_key(a, c) : 0ull, slots);
+      }
     }
   }
+  if constexpr (LARGE) return;
   cur = merge_wave_lists<kIdxWaves>(lists, cur, slots > 0 ? slots : 1);
   if (w == 0) {
     const int64_t off = row * top_k;
@@ -262,20 +270,31 @@ hipError_t launch_keys(const float* w_k, const float* k_comp, int64_t nb_cap, in
   return hipGetLastError();
 }
 
-template <typename T, int D, int DI, int NT>
-hipError_t launch_select_nt(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
+template <typename T, int D, int DI, int NT, bool LARGE>
+hipError_t launch_select_nl(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
                             int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel, float* sel_scores,
-                            hipStream_t st) {
+                            uint32_t* ws_scores, int64_t n_chunks, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
   const int64_t nb_cap = kv_cap / s.bs;
   const T* qp = static_cast<const T*>(q);
   const dim3 grid((unsigned)rows), block(NT);
-  auto kern = ix.agg == kAggSum   ? indexer_select_kernel<T, D, DI, kAggSum, NT>
-              : ix.agg == kAggMax ? indexer_select_kernel<T, D, DI, kAggMax, NT>
-                                  : indexer_select_kernel<T, D, DI, kAggSoftmax, NT>;
-  hipLaunchKernelGGL(kern, grid, block, 0, st, qp, w_q, k_idx, sel, sel_scores, q_len, q_pos0, nb_cap, s.hq, s.hkv,
-                     s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
+  auto kern = ix.agg == kAggSum   ? indexer_select_kernel<T, D, DI, kAggSum, NT, LARGE>
+              : ix.agg == kAggMax ? indexer_select_kernel<T, D, DI, kAggMax, NT, LARGE>
+                                  : indexer_select_kernel<T, D, DI, kAggSoftmax, NT, LARGE>;
+  hipLaunchKernelGGL(kern, grid, block, 0, st, qp, w_q, k_idx, sel, sel_scores, ws_scores, n_chunks, q_len, q_pos0,
+                     nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
   return hipGetLastError();
+}
+
+template <typename T, int D, int DI, int NT>
+hipError_t launch_select_nt(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
+                            int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                            uint32_t* ws_scores, int64_t n_chunks, hipStream_t st) {
+  if (ws_scores)
+    return launch_select_nl<T, D, DI, NT, true>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores,
+                                                ws_scores, n_chunks, st);
+  return launch_select_nl<T, D, DI, NT, false>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, nullptr,
+                                               0, st);
 }
 
 // Rows fewer than the CUs (decode): 8 waves per row, so that the projection
@@ -285,22 +304,22 @@ hipError_t launch_select_nt(const Dims& s, const IndexerDims& ix, const float* w
 template <typename T, int D, int DI>
 hipError_t launch_select_t(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
                            int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel, float* sel_scores,
-                           hipStream_t st) {
+                           uint32_t* ws_scores, int64_t n_chunks, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
   if (rows < 256)
-    return launch_select_nt<T, D, DI, 512>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
-  return launch_select_nt<T, D, DI, 256>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
+    return launch_select_nt<T, D, DI, 512>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws_scores, n_chunks, st);
+  return launch_select_nt<T, D, DI, 256>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws_scores, n_chunks, st);
 }
 
 template <typename T>
 hipError_t launch_select_d(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q, int64_t q_len,
                            int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel, float* sel_scores,
-                           hipStream_t st) {
+                           uint32_t* ws_scores, int64_t n_chunks, hipStream_t st) {
   if (s.d == 64)
-    return ix.dim == 64 ? launch_select_t<T, 64, 64>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st)
-                        : launch_select_t<T, 64, 128>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
-  return ix.dim == 64 ? launch_select_t<T, 128, 64>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st)
-                      : launch_select_t<T, 128, 128>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
+    return ix.dim == 64 ? launch_select_t<T, 64, 64>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws_scores, n_chunks, st)
+                        : launch_select_t<T, 64, 128>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws_scores, n_chunks, st);
+  return ix.dim == 64 ? launch_select_t<T, 128, 64>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws_scores, n_chunks, st)
+                      : launch_select_t<T, 128, 128>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws_scores, n_chunks, st);
 }
 
 }  // namespace
@@ -320,10 +339,25 @@ hipError_t launch_indexer_keys(const Dims& s, const IndexerDims& ix, const float
 
 hipError_t launch_indexer_select(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q,
                                  int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel,
-                                 float* sel_scores, hipStream_t st) {
-  if (s.dtype == 1)
-    return launch_select_d<uint16_t>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
-  return launch_select_d<float>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, st);
+                                 float* sel_scores, void* ws, hipStream_t st) {
+  if (s.top_k <= 64)
+    return s.dtype == 1
+               ? launch_select_d<uint16_t>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, nullptr, 0, st)
+               : launch_select_d<float>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, nullptr, 0, st);
+  // top_k > 64: every candidate's aggregated score in ws (the large
+  // selection's layout), then its per-row pick, which also writes the rows
+  // without candidates (the forced block and padding)
+  const int64_t n_chunks = plan_select(s, q_len, q_pos0).n_chunks;
+  if (n_chunks > 0) {
+    uint32_t* ws_scores = static_cast<uint32_t*>(ws);
+    const hipError_t e =
+        s.dtype == 1 ? launch_select_d<uint16_t>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores,
+                                                 ws_scores, n_chunks, st)
+                     : launch_select_d<float>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws_scores,
+                                              n_chunks, st);
+    if (e != hipSuccess) return e;
+  }
+  return launch_large_pick(s, q_len, q_pos0, n_chunks, ws, true, sel, sel_scores, st);
 }
 
 }  // namespace qsa

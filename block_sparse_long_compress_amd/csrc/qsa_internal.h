@@ -25,9 +25,11 @@ struct IndexerDims {
 hipError_t launch_indexer_keys(const Dims& s, const IndexerDims& ix, const float* w_k, const float* k_comp,
                                int64_t kv_cap, int64_t blk_begin, int64_t blk_end, float* k_idx, hipStream_t st);
 // Selection of every (sequence, query row, KV head) scored in indexer space.
+// top_k > 64: the scores go to ws (the large selection's layout, n_chunks =
+// plan_select(s, q_len, q_pos0).n_chunks) and the large pick runs on them.
 hipError_t launch_indexer_select(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q,
                                  int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel,
-                                 float* sel_scores, hipStream_t st);
+                                 float* sel_scores, void* ws, hipStream_t st);
 
 // Rotated 8-bit K/V cache: positions [pos_begin, pos_end) of every (b, g)
 // rotated (Walsh-Hadamard) and quantized (codes + float16 scale per 32).
@@ -66,6 +68,13 @@ hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, i
                          const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
                          hipStream_t st, const void* k_cache = nullptr, int64_t close_block = -1,
                          bool pick = true);
+
+// The large selection's pick over scores already in ws (scores of rows x
+// n_chunks x 256 candidates, then the chunk lists): lists = true first
+// rebuilds the chunk lists from the scores where a row's candidates exceed
+// the pick pool (a score pass that wrote scores only).
+hipError_t launch_large_pick(const Dims& s, int64_t q_len, int64_t q_pos0, int64_t n_chunks, void* ws, bool lists,
+                             int32_t* sel, float* sel_scores, hipStream_t st);
 
 // Decode attention --------------------------------------------------------------
 struct DecodePlan {

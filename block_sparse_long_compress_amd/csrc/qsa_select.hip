@@ -746,6 +746,35 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
   }
 }
 
+// Per (row, chunk of 256 candidates) of a score pass that wrote scores
+// only: the chunk's 16 best keys in descending order, rebuilt from the
+// written score bits (key = score bits : complemented id, as everywhere).
+// One wave per (row, chunk); only rows whose candidates exceed the pick pool
+// need them, the others return at once.
+__global__ __launch_bounds__(kWave) void select_large_lists_kernel(const uint32_t* __restrict__ ws_scores,
+                                                                   uint64_t* __restrict__ ws_lists, int64_t q_len,
+                                                                   int64_t q_pos0, int hkv, int bs, int keep_tail,
+                                                                   int64_t n_chunks) {
+  const int64_t row = blockIdx.x / n_chunks;
+  const int64_t ch = blockIdx.x % n_chunks;
+  const int64_t t = (row / hkv) % q_len;
+  const int64_t n_cand = row_frame(q_pos0 + t, bs, keep_tail).n_cand;
+  const int64_t c_begin = ch * kLargeChunk;
+  if (n_cand <= kPoolCap || c_begin >= n_cand) return;
+  const int lane = lane_id();
+  static_assert(kLargeChunk == 4 * kWave && kLargeList == 16, "top16_of_256");
+  uint64_t x[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int64_t cand = c_begin + p * kWave + lane;
+    x[p] = cand < n_cand ? ((uint64_t)ws_scores[row * n_chunks * kLargeChunk + cand] << 32) |
+                               (uint64_t)(0xFFFFFFFFu - (uint32_t)cand)
+                         : 0ull;
+  }
+  const uint64_t top = top16_of_256(x);
+  if (lane < kLargeList) ws_lists[(row * n_chunks + ch) * kLargeList + lane] = top;
+}
+
 // One workgroup per row: cutoff, then the kept ids in ascending order.
 __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
     int32_t* __restrict__ sel, float* __restrict__ sel_scores, const uint32_t* __restrict__ ws_scores,
@@ -868,6 +897,22 @@ SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
   // arrival counters (kept at zero between calls), then the chunk lists
   if (p.n_chunks > 1) p.ws_bytes = counter_bytes(rows) + (size_t)rows * p.n_chunks * (s.top_k - 1) * sizeof(uint64_t);
   return p;
+}
+
+hipError_t launch_large_pick(const Dims& s, int64_t q_len, int64_t q_pos0, int64_t n_chunks, void* ws, bool lists,
+                             int32_t* sel, float* sel_scores, hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  uint32_t* wss = static_cast<uint32_t*>(ws);
+  uint64_t* wsl = reinterpret_cast<uint64_t*>(wss + rows * n_chunks * kLargeChunk);
+  if (lists && n_chunks * kLargeChunk > kPoolCap) {
+    hipLaunchKernelGGL(select_large_lists_kernel, dim3((unsigned)(rows * n_chunks)), dim3(kWave), 0, st, wss, wsl,
+                       q_len, q_pos0, s.hkv, s.bs, s.keep_tail, n_chunks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(select_large_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, st, sel, sel_scores, wss,
+                     wsl, q_len, q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, n_chunks);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,

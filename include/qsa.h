@@ -93,7 +93,8 @@ enum {
   QSA_OP_DECODE = 2,
   QSA_OP_PREFILL = 3,
   QSA_OP_DECODE_STEP = 4,
-  QSA_OP_DECODE_STEP_RAGGED = 5
+  QSA_OP_DECODE_STEP_RAGGED = 5,
+  QSA_OP_INDEXER_SELECT = 6
 };
 
 typedef enum {
@@ -124,9 +125,10 @@ const char* qsa_status_str(qsa_status status);
 
 /* Bytes of device workspace the given op needs for these sizes (0 if none;
  * (size_t)-1 if the arguments are invalid or the op does not serve the
- * shape: selection, and decode steps that select separately, with k > 64
- * over more than 65536 candidates per row). op is one of QSA_OP_*.
- * QSA_OP_SELECT and QSA_OP_PREFILL take q_len and kv_len = q_pos0 + q_len;
+ * shape: selection (default or indexer), and decode steps that select
+ * separately, with k > 64 over more than 65536 candidates per row). op is one of QSA_OP_*.
+ * QSA_OP_SELECT, QSA_OP_PREFILL and QSA_OP_INDEXER_SELECT take q_len and
+ * kv_len = q_pos0 + q_len;
  * QSA_OP_DECODE takes kv_len (q_len ignored).
  * QSA_OP_DECODE_STEP_RAGGED takes the longest sequence's length as kv_len
  * and returns (size_t)-1 for shapes the ragged step does not serve.
@@ -290,11 +292,16 @@ qsa_status qsa_indexer_keys(const qsa_shape* shape, const qsa_indexer* idx, cons
  * qsa_indexer_keys for every block below the rows' own blocks (and, with
  * keep_tail, the complete own block). sel_scores (optional) receives the
  * aggregated score of every kept candidate (+inf for the forced block, -inf
- * for padding). One workgroup per (sequence, row, KV head); no workspace.
- * QSA_ERR_UNSUPPORTED for top_k > 64. */
+ * for padding). One workgroup per (sequence, row, KV head) scores the row's
+ * candidates. top_k <= 64: the row's top list is kept in registers and ws is
+ * not used. top_k > 64: every candidate's aggregated score goes to ws and
+ * the large selection's per-row pick (radix cutoff) runs on them, as in
+ * qsa_score_select; ws: qsa_workspace_bytes(shape, QSA_OP_INDEXER_SELECT,
+ * q_len, kv_len) bytes (no zero-fill needed), else QSA_ERR_WORKSPACE;
+ * QSA_ERR_UNSUPPORTED with more than 65536 candidates per row. */
 qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, const float* w_q, const void* q,
                               int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_len, int64_t kv_cap,
-                              int32_t* sel, float* sel_scores, void* stream);
+                              int32_t* sel, float* sel_scores, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Rotated 8-bit K/V cache ("Qwen4 in llama.cpp: Dissecting PR #27742",

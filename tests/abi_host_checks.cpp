@@ -66,9 +66,10 @@ int main() {
               if (kt && k < 2) continue;
               qsa_shape s = shape(b, 16, 2, d, bs, k, dt, kt);
               for (int64_t n : lens) {
-                for (int op = 0; op <= QSA_OP_DECODE_STEP_RAGGED; ++op) {
+                for (int op = 0; op <= QSA_OP_INDEXER_SELECT; ++op) {
                   // prefill and selection over the last 4096 query rows of n positions
-                  const int64_t q_len = (op == QSA_OP_PREFILL || op == QSA_OP_SELECT) ? (n < 4096 ? n : 4096) : 1;
+                  const bool rows = op == QSA_OP_PREFILL || op == QSA_OP_SELECT || op == QSA_OP_INDEXER_SELECT;
+                  const int64_t q_len = rows ? (n < 4096 ? n : 4096) : 1;
                   const size_t w = qsa_workspace_bytes(&s, op, q_len, n);
                   if (w != BAD && w > (size_t(1) << 40)) {  // at most 1 TiB for these sizes
                     std::fprintf(stderr, "FAIL workspace %zu for op %d d %d bs %d k %d b %d n %lld\n", w, op, d, bs,
@@ -126,8 +127,12 @@ int main() {
   expect(qsa_indexer_keys(&good, &bad_ix, PF, PF, 64, 64, 0, PF, nullptr), QSA_ERR_INVALID, "indexer dim 96");
   qsa_indexer ix{64, QSA_AGG_MAX, 0.f};
   qsa_shape k65 = shape(2, 16, 2, 128, 64, 65, QSA_BF16);
-  expect(qsa_indexer_select(&k65, &ix, PF, P, 1, 127, PF, 128, 256, PI, nullptr, nullptr), QSA_ERR_UNSUPPORTED,
-         "indexer k > 64");
+  expect(qsa_indexer_select(&k65, &ix, PF, P, 1, 127, PF, 128, 256, PI, nullptr, nullptr, 0, nullptr),
+         QSA_ERR_WORKSPACE, "indexer k > 64 without workspace");
+  qsa_shape k65b4 = shape(2, 16, 2, 128, 4, 65, QSA_BF16);
+  expect(qsa_indexer_select(&k65b4, &ix, PF, P, 1, 4 * 70000 - 1, PF, 4 * 70000, 4 * 70000, PI, nullptr, P,
+                            size_t(1) << 40, nullptr),
+         QSA_ERR_UNSUPPORTED, "indexer k > 64 over more than 65536 candidates");
   const int8_t* PC = static_cast<const int8_t*>(P);
   const uint16_t* PS = static_cast<const uint16_t*>(P);
   expect(qsa_sparse_attn_prefill_q8(&good, P, PC, PC, static_cast<const uint16_t*>(MIS), PS, 64, 0, 4096, PI, P,

@@ -199,19 +199,26 @@ def test_indexer_arguments(qsa):
     for bad in (qsa.make_indexer(96, 0), qsa.make_indexer(64, 3), qsa.make_indexer(64, -1),
                 qsa.make_indexer(64, 0, -1.0), qsa.make_indexer(64, 0, float("inf"))):
         assert lib.qsa_indexer_keys(sh, ctypes.byref(bad), P, P, 128, 128, 0, P, N) == INV
-        assert lib.qsa_indexer_select(sh, ctypes.byref(bad), P, P, 1, 127, P, 128, 128, P, N, N) == INV
+        assert lib.qsa_indexer_select(sh, ctypes.byref(bad), P, P, 1, 127, P, 128, 128, P, N, N, 0, N) == INV
     ix = ctypes.byref(ok)
     assert lib.qsa_indexer_keys(sh, None, P, P, 128, 128, 0, P, N) == INV
     assert lib.qsa_indexer_keys(sh, ix, N, P, 128, 128, 0, P, N) == INV
     assert lib.qsa_indexer_keys(sh, ix, P, P, 128, 128, 0, MIS, N) == INV
     assert lib.qsa_indexer_keys(sh, ix, P, P, 129, 128, 0, P, N) == INV
     assert lib.qsa_indexer_keys(sh, ix, N, N, 63, 128, 0, N, N) == 0  # no complete block: nothing to do
-    assert lib.qsa_indexer_select(sh, ix, P, P, 1, 127, P, 129, 256, P, N, N) == INV  # kv_len != q_pos0 + q_len
-    assert lib.qsa_indexer_select(sh, ix, N, P, 1, 127, P, 128, 256, P, N, N) == INV
-    assert lib.qsa_indexer_select(sh, ix, P, P, 1, 127, P, 128, 256, MIS, N, N) == INV
-    assert lib.qsa_indexer_select(sh, ix, P, P, 1, 127, N, 128, 256, P, N, N) == INV  # candidates, no keys
-    big_k = ctypes.byref(good_shape(qsa, top_k=65))
-    assert lib.qsa_indexer_select(big_k, ix, P, P, 1, 127, P, 128, 256, P, N, N) == UNS
+    sel_ix = lib.qsa_indexer_select
+    assert sel_ix(sh, ix, P, P, 1, 127, P, 129, 256, P, N, N, 0, N) == INV  # kv_len != q_pos0 + q_len
+    assert sel_ix(sh, ix, N, P, 1, 127, P, 128, 256, P, N, N, 0, N) == INV
+    assert sel_ix(sh, ix, P, P, 1, 127, P, 128, 256, MIS, N, N, 0, N) == INV
+    assert sel_ix(sh, ix, P, P, 1, 127, N, 128, 256, P, N, N, 0, N) == INV  # candidates, no keys
+    # k > 64: the large selection's workspace (none for k <= 64), at most 65536 candidates per row
+    big_k = good_shape(qsa, top_k=65, block_size=4)
+    need = qsa.qsa_workspace_bytes(big_k, qsa.QSA_OP_INDEXER_SELECT, 1, 4000)
+    assert need > 0 and qsa.qsa_workspace_bytes(good_shape(qsa), qsa.QSA_OP_INDEXER_SELECT, 1, 4000) == 0
+    assert sel_ix(ctypes.byref(big_k), ix, P, P, 1, 3999, P, 4000, 4096, P, N, N, 0, N) == 3
+    assert sel_ix(ctypes.byref(big_k), ix, P, P, 1, 3999, P, 4000, 4096, P, N, P, need - 1, N) == 3
+    assert sel_ix(ctypes.byref(big_k), ix, P, P, 1, 4 * 70000 - 1, P, 4 * 70000, 4 * 70000, P, N, P, 1 << 40,
+                  N) == UNS
 
 
 def test_decode_step_q8_arguments(qsa):

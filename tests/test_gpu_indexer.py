@@ -42,6 +42,13 @@ CASES = [
     (W(mode="prefill", batch=1, kv_len=1000, block_size=32, top_k=8), 64, I.AGG_MAX),
     (W(mode="prefill", batch=1, kv_len=777, block_size=32, top_k=6), 128, I.AGG_SOFTMAX),
     (W(mode="decode", batch=1, kv_len=40, top_k=4), 64, I.AGG_SUM),                     # no candidate yet
+    # k > 64: every score to the workspace, then the large selection's pick (the pool of all scores up to
+    # 12288 candidates, the per-chunk lists beyond)
+    (W(block_size=4, top_k=100, kv_len=4 * 2000 + 3), 64, I.AGG_SUM),
+    (W(batch=1, block_size=4, top_k=513, kv_len=4 * 20000, keep_tail=True), 64, I.AGG_MAX),
+    (W(batch=1, block_size=8, top_k=129, kv_len=8 * 14000 + 5), 128, I.AGG_SOFTMAX),
+    (W(mode="prefill", batch=1, kv_len=700, block_size=4, top_k=100, head_dim=64), 64, I.AGG_SUM),
+    (W(mode="decode", batch=1, kv_len=3, block_size=4, top_k=100), 64, I.AGG_SUM),      # no candidate yet
 ]
 
 
