@@ -346,8 +346,8 @@ __global__ __launch_bounds__(kStepWaves * kWave) void pick_attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int32_t* __restrict__ sel, float* __restrict__ sel_scores, const uint32_t* __restrict__ ws_scores,
     const uint64_t* __restrict__ ws_lists, uint16_t* __restrict__ out, float* part, uint32_t* counters,
-    int64_t kv_len, int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k, float scale_log2, int keep_tail,
-    int64_t n_chunks, int bpw, int n_split) {
+    const int32_t* __restrict__ kv_lens, int64_t kv_len, int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k,
+    float scale_log2, int keep_tail, int64_t n_chunks, int bpw, int n_split) {
   using SM = StepSmem<D>;
   constexpr int DT = D / 16;
   __shared__ __align__(16) unsigned char big[SM::kBytes];
@@ -360,7 +360,14 @@ __global__ __launch_bounds__(kStepWaves * kWave) void pick_attend_kernel(
   const int64_t b = row / hkv;
   const int g = (int)(row % hkv);
   const int lane = lane_id(), w = wave_id();
-  const int64_t p = kv_len - 1;
+  // this sequence's length: the batch's, or its own (ragged batch, clamped
+  // into [1, kv_len] as the score pass clamps it)
+  int64_t n = kv_len;
+  if (kv_lens) {
+    n = kv_lens[b];
+    n = n < 1 ? 1 : (n > kv_len ? kv_len : n);
+  }
+  const int64_t p = n - 1;
   const Frame fr = row_frame(p, bs, keep_tail);
   const int64_t off = row * top_k;
   pick_row(sm, ws_scores + row * n_chunks * kLargeChunk, ws_lists + row * n_chunks * kLargeList, fr.n_cand,
@@ -389,15 +396,15 @@ template <int D>
 hipError_t launch_pick_attend_d(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
                                 int32_t* sel, float* sel_scores, const uint32_t* ws_scores, const uint64_t* ws_lists,
                                 void* out, uint32_t* counters, float* part, int64_t kv_len, int64_t kv_cap,
-                                hipStream_t st) {
+                                const int32_t* kv_lens, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   if (pa.n_split == 1) part = nullptr;
   auto kern = s.bs < kUnit ? pick_attend_kernel<D, true> : pick_attend_kernel<D, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * pa.n_split)), dim3(kStepWaves * kWave), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), sel, sel_scores, ws_scores, ws_lists,
-                     static_cast<uint16_t*>(out), part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
-                     s.scale * 1.4426950408889634f, s.keep_tail, pa.n_chunks, pa.blocks_per_wg, pa.n_split);
+                     static_cast<uint16_t*>(out), part, counters, kv_lens, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs,
+                     s.top_k, s.scale * 1.4426950408889634f, s.keep_tail, pa.n_chunks, pa.blocks_per_wg, pa.n_split);
   return hipGetLastError();
 }
 
@@ -526,16 +533,17 @@ PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks) {
 
 hipError_t launch_pick_attend(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
                               int32_t* sel, float* sel_scores, const void* ws_select, void* out, void* counters,
-                              void* part, int64_t kv_len, int64_t kv_cap, hipStream_t st) {
+                              void* part, int64_t kv_len, int64_t kv_cap, hipStream_t st, const int32_t* kv_lens) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   // the score pass's workspace: scores [rows][n_chunks * 256], then the lists
   const uint32_t* wss = reinterpret_cast<const uint32_t*>(ws_select);
   const uint64_t* wsl = reinterpret_cast<const uint64_t*>(wss + rows * pa.n_chunks * kLargeChunk);
   uint32_t* c = static_cast<uint32_t*>(counters);
   float* pt = static_cast<float*>(part);
-  return s.d == 64 ? launch_pick_attend_d<64>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, c, pt, kv_len, kv_cap, st)
+  return s.d == 64 ? launch_pick_attend_d<64>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, c, pt, kv_len, kv_cap,
+                                              kv_lens, st)
                    : launch_pick_attend_d<128>(s, pa, q, k, v, sel, sel_scores, wss, wsl, out, c, pt, kv_len, kv_cap,
-                                               st);
+                                               kv_lens, st);
 }
 
 }  // namespace qsa

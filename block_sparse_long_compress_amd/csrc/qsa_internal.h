@@ -64,10 +64,14 @@ SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0);
 // close_block >= 0 (decode, q_len = 1): the selection also compresses that
 // block of k_cache into k_comp first (the block the new token closes).
 // pick = false (large path only): the score pass alone, for launch_pick_attend.
+// kv_lens (device, [batch], large path with pick = false and q_len = 1 only):
+// a ragged decode batch; each row's position comes from its sequence's
+// length (clamped into [1, q_pos0 + 1]) and each row compresses the block
+// its own new token closes (close_block is then ignored).
 hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,
                          const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
                          hipStream_t st, const void* k_cache = nullptr, int64_t close_block = -1,
-                         bool pick = true);
+                         bool pick = true, const int32_t* kv_lens = nullptr);
 
 // The large selection's pick over scores already in ws (scores of rows x
 // n_chunks x 256 candidates, then the chunk lists): lists = true first
@@ -164,10 +168,12 @@ struct PickAttendPlan {
   size_t ws_bytes;   // arrival counters (counter_bytes(rows)), then slice states
 };
 PickAttendPlan plan_pick_attend(const Dims& s, int64_t n_chunks);
-// counters / part: as for launch_decode.
+// counters / part: as for launch_decode. kv_lens (device, [batch], nullable):
+// a ragged batch, each sequence at its own length (clamped into [1, kv_len]).
 hipError_t launch_pick_attend(const Dims& s, const PickAttendPlan& pa, const void* q, const void* k, const void* v,
                               int32_t* sel, float* sel_scores, const void* ws_select, void* out, void* counters,
-                              void* part, int64_t kv_len, int64_t kv_cap, hipStream_t st);
+                              void* part, int64_t kv_len, int64_t kv_cap, hipStream_t st,
+                              const int32_t* kv_lens = nullptr);
 
 // Generic float32 attention (one wave per query row); used for dtype QSA_F32.
 hipError_t launch_attn_f32(const Dims& s, const float* q, const float* k, const float* v, int64_t q_len,

@@ -603,7 +603,7 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
     const T* __restrict__ q, const float* k_comp, uint32_t* __restrict__ ws_scores,
     uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs,
     float scale, int keep_tail, int64_t n_chunks, const T* __restrict__ k_cache, float* k_comp_w, int64_t kv_cap,
-    int64_t close_block) {
+    int64_t close_block, const int32_t* __restrict__ kv_lens) {
   constexpr int LPR = D / 4;
   __shared__ uint64_t tops[4][kLargeList];
   const int64_t row = blockIdx.x / n_chunks;
@@ -612,7 +612,16 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
   const int64_t t = (row / hkv) % q_len;
   const int g = (int)(row % hkv);
   const int lane = lane_id(), w = wave_id();
-  const int n_cand = row_frame(q_pos0 + t, bs, keep_tail).n_cand;
+  int64_t p = q_pos0 + t;
+  if (kv_lens) {
+    // a ragged decode batch (q_len = 1): sequence b's own length, clamped
+    // into [1, q_pos0 + 1], and the block its new token closes, if any
+    int64_t n = kv_lens[b];
+    n = n < 1 ? 1 : (n > q_pos0 + 1 ? q_pos0 + 1 : n);
+    p = n - 1;
+    close_block = n % bs == 0 ? n / bs - 1 : -1;
+  }
+  const int n_cand = row_frame(p, bs, keep_tail).n_cand;
   const int64_t c_begin = ch * kLargeChunk;
   const int64_t last_ch = n_cand > 0 ? (n_cand - 1) / kLargeChunk : 0;
   if (close_block >= 0 && ch == last_ch) {
@@ -794,7 +803,7 @@ __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
 template <typename T, int D>
 hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, int64_t q_len, int64_t q_pos0,
                         const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
-                        hipStream_t st, const void* k_cache, int64_t close_block, bool pick) {
+                        hipStream_t st, const void* k_cache, int64_t close_block, bool pick, const int32_t* kv_lens) {
   const T* q = static_cast<const T*>(qv);
   const T* kc = static_cast<const T*>(k_cache);
   float* kcw = const_cast<float*>(k_comp);
@@ -815,7 +824,7 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
     } else if (plan.n_chunks > 0) {
       hipLaunchKernelGGL((select_large_score_kernel<T, D>), dim3((unsigned)(rows * plan.n_chunks)), dim3(256), 0, st,
                          q, k_comp, wss, wsl, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.scale,
-                         s.keep_tail, plan.n_chunks, kc, kcw, kv_cap, close_block);
+                         s.keep_tail, plan.n_chunks, kc, kcw, kv_cap, close_block, kv_lens);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || !pick) return e;
     } else if (close_block >= 0) {
@@ -917,12 +926,13 @@ hipError_t launch_large_pick(const Dims& s, int64_t q_len, int64_t q_pos0, int64
 
 hipError_t launch_select(const Dims& s, const SelectPlan& plan, const void* q, int64_t q_len, int64_t q_pos0,
                          const float* k_comp, int64_t kv_cap, int32_t* sel, float* sel_scores, void* ws,
-                         hipStream_t st, const void* k_cache, int64_t close_block, bool pick) {
+                         hipStream_t st, const void* k_cache, int64_t close_block, bool pick,
+                         const int32_t* kv_lens) {
   if (s.dtype == 1)
-    return s.d == 64 ? launch_typed<uint16_t, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block, pick)
-                     : launch_typed<uint16_t, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block, pick);
-  return s.d == 64 ? launch_typed<float, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block, pick)
-                   : launch_typed<float, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block, pick);
+    return s.d == 64 ? launch_typed<uint16_t, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block, pick, kv_lens)
+                     : launch_typed<uint16_t, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block, pick, kv_lens);
+  return s.d == 64 ? launch_typed<float, 64>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block, pick, kv_lens)
+                   : launch_typed<float, 128>(s, plan, q, q_len, q_pos0, k_comp, kv_cap, sel, sel_scores, ws, st, k_cache, close_block, pick, kv_lens);
 }
 
 }  // namespace qsa

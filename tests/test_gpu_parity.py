@@ -441,6 +441,13 @@ RAGGED_CASES = [
     (W(mode="decode", batch=70, kv_len=3000, top_k=16, n_q_heads=8, n_kv_heads=2, head_dim=64, block_size=128),
      _lengths(70, 3000, 5)),   # 140 rows: one workgroup per row
     (W(mode="decode", batch=3, kv_len=40000, top_k=64, n_q_heads=16, n_kv_heads=1), [17, 20000, 40000]),  # G = 16
+    # k > 64: the large selection's score pass and the pick-and-attend kernel read the lengths. The
+    # released budget (one token, no complete block, the first block closed, the first discard, past the
+    # pick pool), a default frame with gathered 8-key blocks, and a batch with no candidate anywhere
+    (W(mode="decode", batch=5, kv_len=4 * 20000 + 2, top_k=513, block_size=4, keep_tail=True),
+     [1, 3, 4, 2052, 4 * 20000 + 2]),
+    (W(mode="decode", batch=4, kv_len=8 * 3000, top_k=129, block_size=8), [8, 9, 1000, 8 * 3000]),
+    (W(mode="decode", batch=3, kv_len=4, top_k=100, block_size=4), [1, 2, 4]),
 ]
 
 
