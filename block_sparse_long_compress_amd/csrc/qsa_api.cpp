@@ -56,24 +56,27 @@ StepWs step_ws(const Dims& s, int64_t kv_len, bool q8 = false) {
 }
 
 // The ragged decode step on the shapes it serves without the fused kernel
-// (bf16, top_k > 64): the large selection's score pass (at least one chunk,
-// so that sequences closing a block compress it even when no sequence has a
-// candidate yet) and the pick-and-attend kernel, in the decode step's layout.
+// (bf16 with top_k > 64 or blocks shorter than 32 keys, float32): the large
+// selection's score pass (at least one chunk, so that sequences closing a
+// block compress it even when no sequence has a candidate yet), then for
+// bf16 the pick-and-attend kernel's slice states, in the decode step's
+// layout (float32 picks into sel and attends without a workspace).
 StepWs ragged_large_ws(const Dims& s, int64_t max_kv_len, int64_t* n_chunks) {
   StepWs w{};
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const size_t cnt = qsa::counter_bytes(rows);
-  int64_t nc = qsa::plan_select(s, 1, max_kv_len - 1).n_chunks;
+  int64_t nc = qsa::plan_select_large(s, 1, max_kv_len - 1).n_chunks;
   if (nc < 1) nc = 1;
   const size_t sel_ws = (size_t)rows * nc * (256 * sizeof(uint32_t) + 16 * sizeof(uint64_t));
-  const size_t att = qsa::plan_pick_attend(s, nc).ws_bytes;
+  // bf16: the pick-and-attend kernel's slice states; float32 attends with
+  // one wave per row and needs none
+  const size_t att = s.dtype == QSA_BF16 ? qsa::plan_pick_attend(s, nc).ws_bytes : 0;
   w.sel_off = 2 * cnt;
   w.part_off = 2 * cnt + qsa::align_up(sel_ws, 256);
   w.total = w.part_off + (att > cnt ? att - cnt : 0);
   if (n_chunks) *n_chunks = nc;
   return w;
 }
-bool ragged_large(const Dims& s) { return s.dtype == QSA_BF16 && s.top_k > 64; }
 
 // Shape checks shared by every entry point.
 qsa_status check_shape(const qsa_shape* sh, Dims* out) {
@@ -180,7 +183,7 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       // the decode step's layout: two arrival-counter areas, then the rest
       const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len, true);
       if (!sp.fused) {
-        if (!ragged_large(s) || qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return (size_t)-1;
+        if (qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return (size_t)-1;
         return ragged_large_ws(s, kv_len, nullptr).total;
       }
       return sp.ws_bytes > 0 ? sp.ws_bytes + qsa::counter_bytes((int64_t)s.batch * s.hkv) : 0;
@@ -366,24 +369,30 @@ qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const v
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
   const qsa::StepPlan sp = qsa::plan_decode_step(s, max_kv_len, true);
   if (!sp.fused) {
-    // bf16 with k > 64: the large selection's score pass and the
-    // pick-and-attend kernel, both reading per-sequence lengths; the other
-    // shapes without the fused kernel (float32, blocks shorter than 32 keys
-    // with k <= 64) are not served
-    if (!ragged_large(s) || qsa::max_candidates(s, max_kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
+    // every shape without the fused kernel (bf16 with k > 64 or blocks
+    // shorter than 32 keys, float32): the large selection's score pass,
+    // which compresses each sequence's closed block, then for bf16 the
+    // pick-and-attend kernel, for float32 the per-row pick and the float32
+    // attention; every kernel reads the per-sequence lengths
+    if (qsa::max_candidates(s, max_kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
     int64_t n_chunks = 0;
     const StepWs lay = ragged_large_ws(s, max_kv_len, &n_chunks);
     const int64_t rows = (int64_t)s.batch * s.hkv;
     const qsa::PickAttendPlan pa = qsa::plan_pick_attend(s, n_chunks);
     if (rows * n_chunks > 0x7FFFFFFF || rows * pa.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
     if (!ws || ws_bytes < lay.total || !aligned16(ws)) return QSA_ERR_WORKSPACE;
-    qsa::SelectPlan sel_plan = qsa::plan_select(s, 1, max_kv_len - 1);
+    qsa::SelectPlan sel_plan = qsa::plan_select_large(s, 1, max_kv_len - 1);
     sel_plan.n_chunks = n_chunks;
     char* base = static_cast<char*>(ws);
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool f32 = s.dtype == QSA_F32;
     st = hip_status(qsa::launch_select(s, sel_plan, q, 1, max_kv_len - 1, k_comp, kv_cap, sel, sel_scores,
-                                       base + lay.sel_off, hs, k, -1, false, kv_lens));
+                                       base + lay.sel_off, hs, k, -1, f32, kv_lens));
     if (st != QSA_OK) return st;
+    if (f32)
+      return hip_status(qsa::launch_attn_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
+                                             static_cast<const float*>(v), 1, max_kv_len - 1, kv_cap, sel,
+                                             static_cast<float*>(out), hs, kv_lens));
     return hip_status(qsa::launch_pick_attend(s, pa, q, k, v, sel, sel_scores, base + lay.sel_off, out, base,
                                               base + lay.part_off, max_kv_len, kv_cap, hs, kv_lens));
   }

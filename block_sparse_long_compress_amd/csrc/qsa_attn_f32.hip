@@ -8,7 +8,9 @@
 //
 // Lane j scores key j of each 64-key slice (a full-precision dot product with
 // the head's query, read from LDS), then every lane accumulates 1 or 2
-// output dims over the slice's values. The float32 path exists for exact
+// output dims over the slice's values. With kv_lens (a ragged decode batch,
+// q_len = 1) sequence b's token sits at position kv_lens[b] - 1, clamped
+// into [0, q_pos0]. The float32 path exists for exact
 // parity on small fp32 workloads; the bf16 MFMA kernels are the fast path.
 #include "qsa_device.h"
 #include "qsa_internal.h"
@@ -21,14 +23,18 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ v, const int32_t* __restrict__ sel,
                                                       float* __restrict__ out, int64_t q_len, int64_t q_pos0,
                                                       int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k,
-                                                      float scale) {
+                                                      float scale, const int32_t* __restrict__ kv_lens) {
   constexpr int DPL = D / kWave;  // output dims per lane
   __shared__ float qh[D];
   const int64_t t = blockIdx.x;
   const int g = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int lane = lane_id();
-  const int64_t p = q_pos0 + t;
+  int64_t p = q_pos0 + t;
+  if (kv_lens) {
+    const int64_t n = kv_lens[b];
+    p = (n < 1 ? 1 : (n > q_pos0 + 1 ? q_pos0 + 1 : n)) - 1;
+  }
   const int64_t own = p / bs;
   const int32_t* srow = sel + ((b * q_len + t) * hkv + g) * top_k;
   const float* kb = k + ((b * hkv + g) * kv_cap) * D;
@@ -90,14 +96,15 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ 
 }  // namespace
 
 hipError_t launch_attn_f32(const Dims& s, const float* q, const float* k, const float* v, int64_t q_len,
-                           int64_t q_pos0, int64_t kv_cap, const int32_t* sel, float* out, hipStream_t st) {
+                           int64_t q_pos0, int64_t kv_cap, const int32_t* sel, float* out, hipStream_t st,
+                           const int32_t* kv_lens) {
   dim3 grid((unsigned)q_len, (unsigned)s.hkv, (unsigned)s.batch);
   if (s.d == 64)
     hipLaunchKernelGGL((attn_f32_kernel<64>), grid, dim3(64), 0, st, q, k, v, sel, out, q_len, q_pos0, kv_cap, s.hq,
-                       s.hkv, s.group, s.bs, s.top_k, s.scale);
+                       s.hkv, s.group, s.bs, s.top_k, s.scale, kv_lens);
   else
     hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(64), 0, st, q, k, v, sel, out, q_len, q_pos0, kv_cap, s.hq,
-                       s.hkv, s.group, s.bs, s.top_k, s.scale);
+                       s.hkv, s.group, s.bs, s.top_k, s.scale, kv_lens);
   return hipGetLastError();
 }
 

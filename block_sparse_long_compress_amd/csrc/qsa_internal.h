@@ -61,6 +61,10 @@ constexpr int64_t kMaxCandLarge = 65536;
 // Candidate blocks of the row at position kv_len - 1 (the most of any row).
 int64_t max_candidates(const Dims& s, int64_t kv_len);
 SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0);
+// The large-k path's plan (score pass over 256-candidate chunks, then the
+// per-row pick) for any top_k: the ragged decode step takes it for every
+// shape the fused kernel does not serve.
+SelectPlan plan_select_large(const Dims& s, int64_t q_len, int64_t q_pos0);
 // close_block >= 0 (decode, q_len = 1): the selection also compresses that
 // block of k_cache into k_comp first (the block the new token closes).
 // pick = false (large path only): the score pass alone, for launch_pick_attend.
@@ -176,8 +180,10 @@ hipError_t launch_pick_attend(const Dims& s, const PickAttendPlan& pa, const voi
                               const int32_t* kv_lens = nullptr);
 
 // Generic float32 attention (one wave per query row); used for dtype QSA_F32.
+// kv_lens (q_len = 1): per-sequence lengths of a ragged decode batch.
 hipError_t launch_attn_f32(const Dims& s, const float* q, const float* k, const float* v, int64_t q_len,
-                           int64_t q_pos0, int64_t kv_cap, const int32_t* sel, float* out, hipStream_t st);
+                           int64_t q_pos0, int64_t kv_cap, const int32_t* sel, float* out, hipStream_t st,
+                           const int32_t* kv_lens = nullptr);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

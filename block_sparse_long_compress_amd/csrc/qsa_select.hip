@@ -785,16 +785,23 @@ __global__ __launch_bounds__(kWave) void select_large_lists_kernel(const uint32_
 }
 
 // One workgroup per row: cutoff, then the kept ids in ascending order.
+// kv_lens (a ragged decode batch, q_len = 1): sequence b's token sits at
+// position kv_lens[b] - 1, clamped as the score pass clamps it.
 __global__ __launch_bounds__(kPickThreads) void select_large_pick_kernel(
     int32_t* __restrict__ sel, float* __restrict__ sel_scores, const uint32_t* __restrict__ ws_scores,
     const uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int hkv, int bs, int top_k, int keep_tail,
-    int64_t n_chunks) {
+    int64_t n_chunks, const int32_t* __restrict__ kv_lens) {
   __shared__ PickSmem sm;
   const int64_t row = blockIdx.x;
   const int64_t b = row / (q_len * hkv);
   const int64_t t = (row / hkv) % q_len;
   const int g = (int)(row % hkv);
-  const Frame fr = row_frame(q_pos0 + t, bs, keep_tail);
+  int64_t p = q_pos0 + t;
+  if (kv_lens) {
+    const int64_t n = kv_lens[b];
+    p = (n < 1 ? 1 : (n > q_pos0 + 1 ? q_pos0 + 1 : n)) - 1;
+  }
+  const Frame fr = row_frame(p, bs, keep_tail);
   const int64_t off = ((b * q_len + t) * hkv + g) * top_k;
   pick_row(sm, ws_scores + row * n_chunks * kLargeChunk, ws_lists + row * n_chunks * kLargeList, fr.n_cand,
            frame_slots(fr, top_k), fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr, nullptr);
@@ -836,7 +843,7 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
     }
     if (!pick) return hipSuccess;
     hipLaunchKernelGGL(select_large_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, st, sel, sel_scores,
-                       wss, wsl, q_len, q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, plan.n_chunks);
+                       wss, wsl, q_len, q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, plan.n_chunks, kv_lens);
     return hipGetLastError();
   }
   if (plan.tiled && s.top_k <= kRowKeep) {
@@ -869,7 +876,24 @@ int64_t max_candidates(const Dims& s, int64_t kv_len) {
   return s.keep_tail ? kv_len / s.bs : (kv_len - 1) / s.bs;
 }
 
+SelectPlan plan_select_large(const Dims& s, int64_t q_len, int64_t q_pos0) {
+  SelectPlan p{};
+  const int64_t max_cand = max_candidates(s, q_pos0 + q_len);  // candidates of the last row
+  const int64_t rows = (int64_t)s.batch * q_len * s.hkv;
+  p.chunk = kLargeChunk;
+  p.large = true;
+  p.n_chunks = (max_cand + kLargeChunk - 1) / kLargeChunk;
+  p.ws_bytes = (size_t)rows * p.n_chunks * (kLargeChunk * sizeof(uint32_t) + kLargeList * sizeof(uint64_t));
+  // many query rows: the score pass over tiles of rows sharing a chunk
+  p.tiled = q_len >= kTileRows;
+  const int64_t score_grid = p.tiled ? (int64_t)s.batch * s.hkv * p.n_chunks * ((q_len + kTileRows - 1) / kTileRows)
+                                     : rows * p.n_chunks;
+  p.grid = score_grid > rows ? score_grid : rows;
+  return p;
+}
+
 SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
+  if (s.top_k > 64) return plan_select_large(s, q_len, q_pos0);
   SelectPlan p{};
   const int64_t kv_len = q_pos0 + q_len;
   const int64_t max_cand = max_candidates(s, kv_len);  // candidates of the last row
@@ -877,17 +901,6 @@ SelectPlan plan_select(const Dims& s, int64_t q_len, int64_t q_pos0) {
   p.chunk = 256;
   p.n_chunks = 1;
   p.ws_bytes = 0;
-  if (s.top_k > 64) {
-    p.large = true;
-    p.n_chunks = (max_cand + kLargeChunk - 1) / kLargeChunk;
-    p.ws_bytes = (size_t)rows * p.n_chunks * (kLargeChunk * sizeof(uint32_t) + kLargeList * sizeof(uint64_t));
-    // many query rows: the score pass over tiles of rows sharing a chunk
-    p.tiled = q_len >= kTileRows;
-    const int64_t score_grid = p.tiled ? (int64_t)s.batch * s.hkv * p.n_chunks * ((q_len + kTileRows - 1) / kTileRows)
-                                       : rows * p.n_chunks;
-    p.grid = score_grid > rows ? score_grid : rows;
-    return p;
-  }
   p.tiled = q_len >= kTileRows;
   p.grid = p.tiled ? (q_len + kTileRows - 1) / kTileRows : rows;
   if (p.tiled || max_cand <= 0) return p;
@@ -920,7 +933,7 @@ hipError_t launch_large_pick(const Dims& s, int64_t q_len, int64_t q_pos0, int64
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(select_large_pick_kernel, dim3((unsigned)rows), dim3(kPickThreads), 0, st, sel, sel_scores, wss,
-                     wsl, q_len, q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, n_chunks);
+                     wsl, q_len, q_pos0, s.hkv, s.bs, s.top_k, s.keep_tail, n_chunks, nullptr);
   return hipGetLastError();
 }
 

@@ -240,11 +240,12 @@ int qsa_decode_step_fused(const qsa_shape* shape, int64_t kv_len);
  *               launch and the workspace.
  * Other arguments as for qsa_decode_step; sequence b reads K/V positions
  * [0, kv_lens[b]) and k_comp blocks [0, kv_lens[b]/Bs) of its own rows.
- * Serves bf16 shapes: k <= 64 with Bs >= 32 as the fused kernel, and
- * k > 64 (any Bs, at most 65536 candidates per row) as the large
- * selection's score pass and the pick-and-attend kernel, both reading the
- * per-sequence lengths; float32, and Bs < 32 with k <= 64, give
- * QSA_ERR_UNSUPPORTED. ws: qsa_workspace_bytes(shape,
+ * bf16 with k <= 64 and Bs >= 32 runs as the fused kernel. Every other
+ * shape (at most 65536 candidates per row, else QSA_ERR_UNSUPPORTED) runs
+ * the large selection's score pass, which also compresses each sequence's
+ * closed block, then for bf16 the pick-and-attend kernel, for float32 the
+ * per-row pick and the float32 attention; every kernel reads the
+ * per-sequence lengths. ws: qsa_workspace_bytes(shape,
  * QSA_OP_DECODE_STEP_RAGGED, 1, max_kv_len) bytes, zero-filled before first
  * use. Outputs equal the per-sequence qsa_decode_step's up to the rounding
  * of the attention merge order (selections are identical). */

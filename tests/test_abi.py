@@ -159,8 +159,8 @@ def test_argument_validation(qsa):
 
 
 def test_ragged_decode_step_arguments(qsa):
-    """Per-sequence lengths: validated on the host; the ragged step serves the fused kernel's shapes and bf16 with
-    k > 64 (the large selection and pick-and-attend), not float32 or Bs < 32 with k <= 64."""
+    """Per-sequence lengths: validated on the host; the ragged step serves the fused kernel's shapes, and every
+    other shape (bf16 with k > 64 or Bs < 32, float32) through the large selection, up to 65536 candidates."""
     lib = qsa.LIB
     sh = good_shape(qsa, batch=4)
     shr = ctypes.byref(sh)
@@ -177,15 +177,18 @@ def test_ragged_decode_step_arguments(qsa):
     assert call(shr, P, P, P, P, P, 65, 64, P, N, P, P, big, N) == INV           # bound beyond capacity
     assert call(shr, P, P, P, P, P, 0, 64, P, N, P, P, big, N) == INV
     assert call(shr, N, P, P, P, P, 64, 64, P, N, P, P, big, N) == INV
-    # shapes served by neither: f32, Bs < 32 with k <= 64, k > 64 over more than 65536 candidates
-    for kw, n in ((dict(dtype=qsa.QSA_F32), 4096), (dict(block_size=16), 4096),
+    # not served: the large selection's candidate limit (unfused shapes, more than 65536 candidates per row)
+    for kw, n in ((dict(dtype=qsa.QSA_F32), 64 * 70000), (dict(block_size=16), 16 * 70000),
                   (dict(top_k=513, block_size=4), 4 * 70000)):
         bad = good_shape(qsa, batch=4, **kw)
         assert call(ctypes.byref(bad), P, P, P, P, P, n, n, P, N, P, P, big, N) == UNS
         with pytest.raises(qsa.QsaError):
             qsa.qsa_workspace_bytes(bad, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, n)
-    # k > 64: the large selection's workspace (at least one chunk, even before any candidate exists)
-    for kw, n in ((dict(top_k=65), 4096), (dict(top_k=513, block_size=4), 4 * 20000), (dict(top_k=100, block_size=4), 3)):
+    # the large selection's workspace (at least one chunk, even before any candidate exists): k > 64,
+    # Bs < 32 with k <= 64, float32 with any k
+    for kw, n in ((dict(top_k=65), 4096), (dict(top_k=513, block_size=4), 4 * 20000), (dict(top_k=100, block_size=4), 3),
+                  (dict(block_size=16), 4096), (dict(block_size=4, top_k=8), 3), (dict(dtype=qsa.QSA_F32), 4096),
+                  (dict(dtype=qsa.QSA_F32, top_k=100, block_size=8), 5000)):
         large = good_shape(qsa, batch=4, **kw)
         need = qsa.qsa_workspace_bytes(large, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, n)
         assert need > 0

@@ -448,6 +448,15 @@ RAGGED_CASES = [
      [1, 3, 4, 2052, 4 * 20000 + 2]),
     (W(mode="decode", batch=4, kv_len=8 * 3000, top_k=129, block_size=8), [8, 9, 1000, 8 * 3000]),
     (W(mode="decode", batch=3, kv_len=4, top_k=100, block_size=4), [1, 2, 4]),
+    # the other shapes without the fused kernel go through the same large selection: bf16 blocks shorter
+    # than 32 keys with k <= 64 (pick-and-attend; past the pick pool; no candidate anywhere), and float32
+    # (per-row pick, then the float32 attention) with k <= 64 and k > 64
+    (W(mode="decode", batch=5, kv_len=16 * 500, top_k=16, block_size=16), [1, 16, 17, 4000, 16 * 500]),
+    (W(mode="decode", batch=3, kv_len=4 * 13000 + 1, top_k=64, block_size=4, keep_tail=True), [4, 2000, 4 * 13000 + 1]),
+    (W(mode="decode", batch=3, kv_len=8, top_k=8, block_size=8), [1, 7, 8]),
+    (W(mode="decode", batch=4, kv_len=3000, top_k=16, dtype="f32", sigma=1.0), [1, 64, 1500, 3000]),
+    (W(mode="decode", batch=3, kv_len=8 * 1200, top_k=100, block_size=8, dtype="f32", sigma=1.0, keep_tail=True),
+     [8, 801, 8 * 1200]),
 ]
 
 
