@@ -53,19 +53,34 @@ __device__ __forceinline__ f32x4_t load4_f32(const uint16_t* p) {
 }
 
 // Sum over the G (<= 16) query heads of a group of four consecutive dims:
-// p points at head 0, heads are `stride` elements apart. All loads are
-// issued before the first add; the sum runs in head order from 0.
-template <typename T>
-__device__ __forceinline__ f32x4_t group_sum4(const T* p, int G, int64_t stride) {
-  f32x4_t v[16];
+// p points at head 0, heads are `stride` elements apart. The sum runs in
+// head order from 0.
+template <int GC, typename T>
+__device__ __forceinline__ f32x4_t group_sum4_n(const T* p, int64_t stride) {
+  // keeps the loads (head 0's, common to every case) from being hoisted
+  // above the dispatch, where the compiler would wait for it on its own
+  asm volatile("" ::: "memory");
+  f32x4_t v[GC];
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < G) v[j] = load4_f32(p + j * stride);
+  for (int j = 0; j < GC; ++j) v[j] = load4_f32(p + j * stride);
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < G) s += v[j];
+  for (int j = 0; j < GC; ++j) s += v[j];
   return s;
+}
+// G is one of 1, 2, 4, 8, 16 (uniform over the wave). Each case issues all
+// its loads before the first add: with a runtime bound on the head loop the
+// compiler guards every load with a branch and waits for it inside the
+// branch, which makes the G loads one memory round trip each.
+template <typename T>
+__device__ __forceinline__ f32x4_t group_sum4(const T* p, int G, int64_t stride) {
+  switch (G) {
+    case 1: return group_sum4_n<1>(p, stride);
+    case 2: return group_sum4_n<2>(p, stride);
+    case 4: return group_sum4_n<4>(p, stride);
+    case 8: return group_sum4_n<8>(p, stride);
+    default: return group_sum4_n<16>(p, stride);
+  }
 }
 
 // ---------------------------------------------------------------- shuffles

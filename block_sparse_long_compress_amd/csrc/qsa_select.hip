@@ -665,22 +665,36 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
 // passes ahead. Outputs are those of the per-row pass:
 // every score of every row, and per (row, chunk) the chunk's 16 best keys in
 // descending order when the row's candidates exceed the pick pool.
-// Workgroups are ordered tile-fastest, so that the tiles reading one chunk
-// run together and share its L2 copy.
+// Workgroups go to the 8 XCDs round-robin; the grid is laid out so that
+// every (sequence, KV head, chunk) goes to one XCD (XCD x takes the chunks
+// x, x + 8, ... of the flattened (sequence, KV head, chunk) order) and its
+// tiles are dispatched there one after another: they run together and read
+// the chunk's compressed keys from that XCD's L2, which fetches them once.
+// Grid of select_large_tile_kernel: 8 XCD lanes of ceil(n_bg * n_chunks / 8)
+// chunks of n_tiles workgroups each.
+inline int64_t large_tile_grid(int64_t n_bg, int64_t n_chunks, int64_t n_tiles) {
+  return 8 * n_tiles * ((n_bg * n_chunks + 7) / 8);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void select_large_tile_kernel(
     const T* __restrict__ q, const float* __restrict__ k_comp, uint32_t* __restrict__ ws_scores,
     uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs,
-    float scale, int keep_tail, int64_t n_chunks, int64_t n_tiles) {
+    float scale, int keep_tail, int64_t n_chunks, int64_t n_tiles, int64_t n_bg) {
   constexpr int QP = D + 4;  // padded row strides (floats): conflict-free 16-byte reads
   constexpr int PASSES = kLargeChunk / kTileCands;
   constexpr int DU = D / 16;  // 16-byte operand loads per lane and pass
   __shared__ float qbar[kTileRows][QP];
   __shared__ float sc[kTileRows][kLargeChunk + 4];
+  __shared__ int ncand[kTileRows];  // candidates of each row of the tile
+  static_assert(kLargeChunk == 256, "one thread per candidate of the chunk");
 
-  const int64_t tile = blockIdx.x % n_tiles;
-  const int64_t ch = (blockIdx.x / n_tiles) % n_chunks;
-  const int64_t bg = blockIdx.x / (n_tiles * n_chunks);
+  const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int64_t tile = j % n_tiles;
+  const int64_t gc = xcd + 8 * (j / n_tiles);  // flattened (sequence, KV head, chunk)
+  if (gc >= n_bg * n_chunks) return;           // spare slots of the last round
+  const int64_t ch = gc % n_chunks;
+  const int64_t bg = gc / n_chunks;
   const int64_t b = bg / hkv;
   const int g = (int)(bg % hkv);
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
@@ -690,6 +704,7 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
   // the tile's last row has the most candidates
   const int64_t cand_end = row_frame(q_pos0 + t0 + rows - 1, bs, keep_tail).n_cand;
   if (c_begin >= cand_end) return;  // uniform over the workgroup
+  if (tid < kTileRows) ncand[tid] = tid < rows ? row_frame(q_pos0 + t0 + tid, bs, keep_tail).n_cand : 0;
 
   for (int idx = tid; idx < kTileRows * D / 4; idx += 256) {
     const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
@@ -727,20 +742,20 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
     for (int i = 0; i < 4; ++i) sc[4 * kg + i][pass * kTileCands + 16 * w + m] = acc[i] * scale;
   }
   __syncthreads();
-  // every row's scores of the chunk (coalesced along the candidates)
-  for (int idx = tid; idx < rows * kLargeChunk; idx += 256) {
-    const int r = idx / kLargeChunk, c = idx % kLargeChunk;
-    const int64_t cand = c_begin + c;
-    if (cand < row_frame(q_pos0 + t0 + r, bs, keep_tail).n_cand) {
-      const int64_t row = (b * q_len + t0 + r) * hkv + g;
-      ws_scores[row * n_chunks * kLargeChunk + cand] = score_order_bits(sc[r][c]);
-    }
+  // every row's scores of the chunk (thread tid: candidate c_begin + tid of
+  // each row, coalesced along the candidates)
+  {
+    const int64_t cand = c_begin + tid;
+    const int64_t stride = (int64_t)hkv * n_chunks * kLargeChunk;  // from one row of the tile to the next
+    uint32_t* dst = ws_scores + ((b * q_len + t0) * hkv + g) * n_chunks * kLargeChunk + cand;
+    for (int r = 0; r < rows; ++r, dst += stride)
+      if (cand < ncand[r]) *dst = score_order_bits(sc[r][tid]);
   }
   // the chunk's 16 best keys of each row that needs them (wave w: rows 4w .. 4w + 3)
   for (int rr = 0; rr < 4; ++rr) {
     const int r = 4 * w + rr;
     if (r >= rows) break;
-    const int64_t n_cand = row_frame(q_pos0 + t0 + r, bs, keep_tail).n_cand;
+    const int64_t n_cand = ncand[r];
     if (n_cand <= kPoolCap || c_begin >= n_cand) continue;  // uniform over the wave
     static_assert(kLargeChunk == 4 * kWave && kLargeList == 16, "top16_of_256");
     uint64_t x[4];
@@ -822,10 +837,10 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
     if (plan.n_chunks > 0 && plan.tiled) {
       // prefill rows (close_block < 0: nothing to compress)
       const int64_t n_tiles = (q_len + kTileRows - 1) / kTileRows;
-      hipLaunchKernelGGL((select_large_tile_kernel<T, D>),
-                         dim3((unsigned)((int64_t)s.batch * s.hkv * plan.n_chunks * n_tiles)), dim3(256), 0, st, q,
-                         k_comp, wss, wsl, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs, s.scale, s.keep_tail,
-                         plan.n_chunks, n_tiles);
+      const int64_t n_bg = (int64_t)s.batch * s.hkv;
+      hipLaunchKernelGGL((select_large_tile_kernel<T, D>), dim3((unsigned)large_tile_grid(n_bg, plan.n_chunks, n_tiles)),
+                         dim3(256), 0, st, q, k_comp, wss, wsl, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs,
+                         s.scale, s.keep_tail, plan.n_chunks, n_tiles, n_bg);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess || !pick) return e;
     } else if (plan.n_chunks > 0) {
@@ -886,7 +901,8 @@ SelectPlan plan_select_large(const Dims& s, int64_t q_len, int64_t q_pos0) {
   p.ws_bytes = (size_t)rows * p.n_chunks * (kLargeChunk * sizeof(uint32_t) + kLargeList * sizeof(uint64_t));
   // many query rows: the score pass over tiles of rows sharing a chunk
   p.tiled = q_len >= kTileRows;
-  const int64_t score_grid = p.tiled ? (int64_t)s.batch * s.hkv * p.n_chunks * ((q_len + kTileRows - 1) / kTileRows)
+  const int64_t score_grid = p.tiled ? large_tile_grid((int64_t)s.batch * s.hkv, p.n_chunks,
+                                                       (q_len + kTileRows - 1) / kTileRows)
                                      : rows * p.n_chunks;
   p.grid = score_grid > rows ? score_grid : rows;
   return p;
