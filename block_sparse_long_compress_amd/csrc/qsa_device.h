@@ -223,6 +223,15 @@ __device__ __forceinline__ uint32_t wave_suffix_sum_u32(uint32_t v) {
   return v;
 }
 
+// Compare-exchange of a bitonic network: the larger of x and its partner y
+// where take_max holds, else the smaller. One comparison decides which to
+// keep (x == y: either, the same key); written this way the compiler emits
+// one 64-bit compare, a lane-mask operation and two selects, rather than
+// both a maximum and a minimum and a select between them.
+__device__ __forceinline__ uint64_t cas_u64(uint64_t x, uint64_t y, bool take_max) {
+  return ((x > y) == take_max) ? x : y;
+}
+
 // Bitonic sort of one key per lane across the wave, descending (lane 0 = largest).
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
   const int lane = lane_id();
@@ -234,7 +243,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
       bool lower = (lane & j) == 0;
       bool desc = (lane & k) == 0;
       bool take_max = (lower == desc);
-      x = take_max ? (x > y ? x : y) : (x < y ? x : y);
+      x = cas_u64(x, y, take_max);
     }
   }
   return x;
@@ -253,7 +262,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc_n(uint64_t x) {
       bool lower = (lane & j) == 0;
       bool desc = (lane & k) == 0;
       bool take_max = (lower == desc);
-      x = take_max ? (x > y ? x : y) : (x < y ? x : y);
+      x = cas_u64(x, y, take_max);
     }
   }
   return x;
@@ -276,7 +285,7 @@ __device__ __forceinline__ uint64_t sort16_groups_desc(uint64_t x) {
       const uint64_t y = xor_lane_u64(x, j);
       const bool lower = (lane & j) == 0;
       const bool desc = k == 16 || (lane & k) == 0;
-      x = (lower == desc) ? (x > y ? x : y) : (x < y ? x : y);
+      x = cas_u64(x, y, lower == desc);
     }
   }
   return x;
@@ -292,7 +301,7 @@ __device__ __forceinline__ uint64_t prune16_desc(uint64_t a, uint64_t b) {
 #pragma unroll
   for (int j = 8; j > 0; j >>= 1) {
     const uint64_t y = xor_lane_u64(x, j);
-    x = (lane & j) == 0 ? (x > y ? x : y) : (x < y ? x : y);
+    x = cas_u64(x, y, (lane & j) == 0);
   }
   return x;
 }
@@ -422,7 +431,7 @@ __device__ __forceinline__ uint64_t wave_merge_desc(uint64_t cur, uint64_t fresh
   for (int j = kWave / 2; j > 0; j >>= 1) {
     uint64_t y = xor_lane_u64(x, j);
     bool lower = (lane & j) == 0;
-    x = lower ? (x > y ? x : y) : (x < y ? x : y);
+    x = cas_u64(x, y, lower);
   }
   return x;
 }
