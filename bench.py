@@ -198,9 +198,11 @@ class Step:
                 self.blk_begin = (w.kv_len - 1) // bs
                 self.n_new_blocks = w.kv_len // bs - self.blk_begin
             elif w.indexer_dim:
-                # learned-indexer selection: the separate calls (compress and project the closed block,
-                # indexer select, decode attention)
+                # learned-indexer selection: one qsa_indexer_decode_step call where it serves the shape
+                # (bf16, k <= 64), else the separate calls (compress and project the closed block, indexer
+                # select, decode attention)
                 self.ws_step = None
+                self.fused = w.dtype == "bf16" and w.top_k <= 64
                 w_q, w_k = S.indexer_weights(seed, w.cfg_id, d, w.indexer_dim)
                 self.w_q, self.w_k = torch.from_numpy(w_q).cuda(), torch.from_numpy(w_k).cuda()
                 self.ix = qsa.make_indexer(w.indexer_dim, w.indexer_agg)
@@ -234,7 +236,7 @@ class Step:
             self.calls.insert(1, ("index_keys", self.index_keys))
         if w.kv_q8:
             self.calls.insert(len(self.calls) - 2, ("quantize", self.quantize))
-        separate = w.indexer_dim or (w.kv_q8 and not self.fused)
+        separate = (w.indexer_dim or w.kv_q8) and not self.fused
         self.step_calls = [("step", self.decode_step)] if w.mode == "decode" and not separate else self.calls
         if self.fused:
             self.calls = self.step_calls
@@ -245,6 +247,10 @@ class Step:
 
     def decode_step(self):
         w = self.w
+        if w.indexer_dim:
+            self.qsa.qsa_indexer_decode_step(self.shape, self.ix, self.w_q, self.w_k, self.q_dec, self.k, self.v,
+                                             self.k_comp, self.k_idx, w.kv_len, self.sel_dec, self.out_dec)
+            return
         if w.kv_q8:
             self.qsa.qsa_decode_step_q8(self.shape, self.q_dec, self.k, self.v, self.k_comp, self.kq, self.vq,
                                         self.ks, self.vs, w.kv_len, self.sel_dec, self.out_dec, ws=self.ws_step)
@@ -538,6 +544,8 @@ def measured_traffic(workload, call):
 KERNELS = {
     "step": "decode_step_kernel (compress of the closed block, selection and attention in one kernel)",
     "step_q8": "kv_quantize_kernel + decode_step_kernel over the 8-bit cache",
+    "step_indexer": "indexer_select_kernel as the indexer decode step (compress and indexer key of the closed "
+                    "block, indexer selection and attention in one kernel)",
     "attend_prefill": "vt_pack_kernel + prefill_attn_kernel",
 }
 
@@ -556,7 +564,8 @@ def record(w, st, timing, steps, seed, graph_steps):
         kernel = KERNELS["attend_prefill"]
     else:
         achieved, peak, unit, bound = model[dominant]["bytes"] / dur / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
-        kernel = (KERNELS["step_q8"] if w.kv_q8 else KERNELS["step"]) if dominant == "step" else f"{dominant} call"
+        step_kernel = KERNELS["step_q8"] if w.kv_q8 else KERNELS["step_indexer"] if w.indexer_dim else KERNELS["step"]
+        kernel = step_kernel if dominant == "step" else f"{dominant} call"
     calls = {}
     for n, t in per_call.items():
         entry = {"us": round(t * 1e6, 3), "p10_us": round(1e6 * float(np.percentile(timing["per_call_s"][n], 10)), 3),

@@ -39,6 +39,7 @@ from .binding import (  # noqa: F401
     qsa_decode_step_noalloc,
     QSA_NOALLOC_SCRATCH_BYTES,
     qsa_decode_step_ragged,
+    qsa_indexer_decode_step,
     qsa_indexer_keys,
     qsa_indexer_select,
     qsa_kv_quantize,

@@ -27,7 +27,7 @@ EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_com
             "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused",
             "qsa_decode_step_ragged", "qsa_indexer_keys", "qsa_indexer_select", "qsa_kv_quantize",
             "qsa_sparse_attn_decode_q8", "qsa_sparse_attn_prefill_q8", "qsa_decode_step_q8",
-            "qsa_decode_step_noalloc")
+            "qsa_decode_step_noalloc", "qsa_indexer_decode_step")
 QSA_NOALLOC_SCRATCH_BYTES = 8 << 20  # include/qsa.h
 
 
@@ -87,6 +87,8 @@ def _load() -> ctypes.CDLL:
     lib.qsa_indexer_keys.argtypes = [SH, IX, P, P, I64, I64, I64, P, P]
     lib.qsa_indexer_select.restype = ctypes.c_int
     lib.qsa_indexer_select.argtypes = [SH, IX, P, P, I64, I64, P, I64, I64, P, P, P, SZ, P]
+    lib.qsa_indexer_decode_step.restype = ctypes.c_int
+    lib.qsa_indexer_decode_step.argtypes = [SH, IX, P, P, P, P, P, P, P, I64, I64, P, P, P, P]
     lib.qsa_kv_quantize.restype = ctypes.c_int
     lib.qsa_kv_quantize.argtypes = [SH, P, P, I64, I64, I64, P, P, P, P, P]
     lib.qsa_sparse_attn_decode_q8.restype = ctypes.c_int
@@ -269,6 +271,18 @@ def qsa_indexer_select(shape: QsaShape, idx: QsaIndexer, w_q, q, q_pos0: int, k_
                                   _stream(q, stream)),
            "qsa_indexer_select")
     return sel
+
+
+def qsa_indexer_decode_step(shape: QsaShape, idx: QsaIndexer, w_q, w_k, q, k, v, k_comp, k_idx, kv_len: int, sel, out,
+                            sel_scores=None, stream=None):
+    """One decode step with the learned indexer in one kernel: ``q`` ``[b][Hq][d]``, the caches ``[b][Hkv][cap][...]``
+    (``k_comp`` and ``k_idx`` gain the block the token at ``kv_len - 1`` closes), ``sel`` ``[b][Hkv][k]``, ``out``
+    ``[b][Hq][d]``."""
+    _check(LIB.qsa_indexer_decode_step(ctypes.byref(shape), ctypes.byref(idx), _ptr(w_q), _ptr(w_k), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(k_comp), _ptr(k_idx), kv_len, k.shape[2], _ptr(sel),
+                                       _ptr(sel_scores), _ptr(out), _stream(q, stream)),
+           "qsa_indexer_decode_step")
+    return out
 
 
 def kv_q8_buffers(k, device=None):

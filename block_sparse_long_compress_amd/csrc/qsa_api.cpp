@@ -464,6 +464,28 @@ qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, co
                                                static_cast<hipStream_t>(stream)));
 }
 
+qsa_status qsa_indexer_decode_step(const qsa_shape* shape, const qsa_indexer* idx, const float* w_q,
+                                   const float* w_k, const void* q, const void* k, const void* v, float* k_comp,
+                                   float* k_idx, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                                   void* out, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  qsa::IndexerDims ix;
+  st = check_indexer(idx, s, &ix);
+  if (st != QSA_OK) return st;
+  if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
+  if (!w_q || !w_k || !q || !k || !v || !k_comp || !k_idx || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(w_q) || !aligned16(w_k) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_comp) ||
+      !aligned16(k_idx) || !aligned16(sel) || !aligned16(out))
+    return QSA_ERR_INVALID;
+  if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  if (s.dtype != QSA_BF16 || s.top_k > 64) return QSA_ERR_UNSUPPORTED;
+  return hip_status(qsa::launch_indexer_step(s, ix, w_q, w_k, q, k, v, k_comp, k_idx, kv_len, kv_cap, sel,
+                                             sel_scores, out, static_cast<hipStream_t>(stream)));
+}
+
 qsa_status qsa_kv_quantize(const qsa_shape* shape, const void* k, const void* v, int64_t kv_len, int64_t kv_cap,
                            int64_t pos_begin, int8_t* k_q, int8_t* v_q, uint16_t* k_scales, uint16_t* v_scales,
                            void* stream) {

@@ -14,6 +14,7 @@
 //
 // Both kernels stream small, L2-resident data; they favour plain fixed-order
 // float32 arithmetic (deterministic) over peak rate.
+#include "qsa_decode_unit.h"
 #include "qsa_device.h"
 #include "qsa_internal.h"
 #include "qsa_select_wave.h"
@@ -81,18 +82,41 @@ __global__ __launch_bounds__(256) void indexer_keys_kernel(const float* __restri
 //    default selection writes it; or (LARGE, top_k > 64) every candidate's
 //    aggregated score written to ws_scores in the large selection's layout
 //    ([row][n_chunks * 256] score order bits), for its per-row pick.
-template <typename T, int D, int DI, int AGG, int kIdxThreads, bool LARGE>
+// STEP (a decode step, bf16, q_len = 1, top_k <= 64): before 2., the last
+// wave compresses the block the new token closes (if any) into k_comp_w,
+// then projects it into k_idx_w while the other waves project the query
+// heads (its indexer key is read from LDS where it is a candidate, with
+// keep_tail); after 3. the workgroup attends over its selection as the
+// fused decode step does, one slice, and writes out.
+template <int D, int NW>
+constexpr int idx_stage_bytes() {
+  const int stage = NW * kUnit * kStageRowBytes<D>;
+  const int comb = NW * (32 + 16 * kCombStride<D>) * 4;
+  return stage > comb ? stage : comb;
+}
+
+template <typename T, int D, int DI, int AGG, int kIdxThreads, bool LARGE, bool STEP = false>
 __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
     const T* __restrict__ q, const float* __restrict__ w_q, const float* __restrict__ k_idx,
     int32_t* __restrict__ sel, float* __restrict__ sel_scores, uint32_t* __restrict__ ws_scores, int64_t n_chunks,
     int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs, int top_k, float scale,
-    int keep_tail) {
+    int keep_tail, const T* __restrict__ k_cache = nullptr, const T* __restrict__ v_cache = nullptr,
+    const float* __restrict__ w_k = nullptr, float* __restrict__ k_comp_w = nullptr, float* __restrict__ k_idx_w = nullptr,
+    T* __restrict__ out = nullptr, int64_t kv_cap = 0, float attn_scale_log2 = 0.f) {
   constexpr int kIdxWaves = kIdxThreads / kWave;
+  static_assert(!(STEP && LARGE), "the fused step keeps the selection in the workgroup");
   __shared__ __align__(16) float qi[16 * DI];
   __shared__ __align__(16) float qs[16 * D];    // the group's query heads, as float
   __shared__ uint64_t lists[kIdxWaves][kWave];
   __shared__ float red_m[kIdxWaves][16], red_z[kIdxWaves][16];
   __shared__ float head_m[16], head_z[16];
+  // STEP only: the attention's staging and combine area, the closed block's
+  // mean key and indexer key, and the selection
+  __shared__ __align__(16) unsigned char big[STEP ? idx_stage_bytes<D, kIdxWaves>() : 16];
+  __shared__ __align__(16) float knew[STEP ? D : 4];
+  __shared__ __align__(16) float kinew[STEP ? DI : 4];
+  __shared__ int ids[STEP ? kWave : 1];
+  __shared__ int last_wg;
 
   const int64_t row = blockIdx.x;
   const int g = (int)(row % hkv);
@@ -103,6 +127,18 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
   const int64_t p = q_pos0 + t;
   const Frame fr = row_frame(p, bs, keep_tail);
   const int slots = frame_slots(fr, top_k);
+  // STEP: the block the token at p closes, if any, and the candidate whose
+  // indexer key comes from LDS (that block, where it competes)
+  const bool closes = STEP && (p + 1) % bs == 0;
+  const int64_t c_new = (p + 1) / bs - 1;
+  const int64_t c_lds = closes && keep_tail ? c_new : -1;
+  const int64_t bg_off = ((int64_t)b * hkv + g) * nb_cap;  // this (sequence, KV head)'s first block
+  if constexpr (STEP) {
+    static_assert(sizeof(T) == 2, "the fused step attends over a bf16 cache");
+    if (closes && w == kIdxWaves - 1)
+      compress_block_wave<T, D>(k_cache + (((int64_t)b * hkv + g) * kv_cap + c_new * bs) * D, bs,
+                                k_comp_w + (bg_off + c_new) * D, knew);
+  }
 
   // 1. projected, scaled query heads by fp32 MFMA: the heads (as float, in
   // LDS) as operand A, W_q read straight from memory as operand B; wave w
@@ -127,6 +163,27 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (4 * pk + v < G) qi[(4 * pk + v) * DI + 16 * n + pm] = acc[v] * scale;
+    }
+  }
+  if constexpr (STEP) {
+    // the closed block's indexer key, in the indexer keys kernel's order (a
+    // fused multiply-add chain over the d inputs in ascending order)
+    if (closes && w == kIdxWaves - 1) {
+      constexpr int EPL = DI / kWave;
+      float acc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll 16
+      for (int i = 0; i < D; ++i) {
+        const float kj = knew[i];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(kj, w_k[(int64_t)i * DI + lane + kWave * e], acc[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        k_idx_w[(bg_off + c_new) * DI + lane + kWave * e] = acc[e];
+        kinew[lane + kWave * e] = acc[e];
+      }
     }
   }
   __syncthreads();
@@ -155,8 +212,10 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
       const bool ok = c < fr.n_cand;
 #pragma unroll
       for (int u = 0; u < DI / 16; ++u) {
-        const f32x4_t kv = ok ? *reinterpret_cast<const f32x4_t*>(krow + (int64_t)c * DI + 16 * u + 4 * kg)
-                              : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t kv = ok ? *reinterpret_cast<const f32x4_t*>(krow + (int64_t)c * DI + 16 * u + 4 * kg)
+                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (STEP)
+          if (c == c_lds) kv = *reinterpret_cast<const f32x4_t*>(&kinew[16 * u + 4 * kg]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[t] = mfma_f32(kv[e], qb[4 * u + e], acc[t]);
       }
@@ -258,7 +317,31 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_select_kernel(
   cur = merge_wave_lists<kIdxWaves>(lists, cur, slots > 0 ? slots : 1);
   if (w == 0) {
     const int64_t off = row * top_k;
-    finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr);
+    finalize_row(cur, slots, fr.forced, top_k, sel + off, sel_scores ? sel_scores + off : nullptr,
+                 STEP ? ids : nullptr);
+  }
+  if constexpr (STEP) {
+    // 4. attention over the selection (ids: ascending, forced block last,
+    // -1 padding), the whole selection as one slice
+    __syncthreads();
+    const int64_t kv_off = ((int64_t)b * hkv + g) * kv_cap;
+    const uint16_t* kc = reinterpret_cast<const uint16_t*>(k_cache) + kv_off * D;
+    const uint16_t* vc = reinterpret_cast<const uint16_t*>(v_cache) + kv_off * D;
+    u32x4_t qf[D / 32];
+    load_q_operands<D>(reinterpret_cast<const uint16_t*>(qh), G, qf);
+    const int sel_mine = lane < top_k ? ids[lane] : -1;
+    float m_run = -__builtin_inff(), l_run = 0.f;
+    f32x4_t o[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    unsigned char* vs = big + w * kUnit * kStageRowBytes<D>;
+    if (bs < kUnit)
+      attend_units<D, true>(qf, kc, vc, sel_mine, top_k, bs, p, attn_scale_log2, vs, w, kIdxWaves, m_run, l_run, o);
+    else
+      attend_units<D, false>(qf, kc, vc, sel_mine, top_k, bs, p, attn_scale_log2, vs, w, kIdxWaves, m_run, l_run, o);
+    l_run = sum_col4(l_run);
+    finish_row_slice<D, kIdxWaves>(m_run, l_run, o, big, &last_wg, reinterpret_cast<uint16_t*>(out), nullptr, nullptr,
+                                   row, b, g, hq, G, 0, 1);
   }
 }
 
@@ -282,7 +365,9 @@ hipError_t launch_select_nl(const Dims& s, const IndexerDims& ix, const float* w
               : ix.agg == kAggMax ? indexer_select_kernel<T, D, DI, kAggMax, NT, LARGE>
                                   : indexer_select_kernel<T, D, DI, kAggSoftmax, NT, LARGE>;
   hipLaunchKernelGGL(kern, grid, block, 0, st, qp, w_q, k_idx, sel, sel_scores, ws_scores, n_chunks, q_len, q_pos0,
-                     nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail);
+                     nb_cap, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale, s.keep_tail, static_cast<const T*>(nullptr),
+                     static_cast<const T*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr),
+                     static_cast<float*>(nullptr), static_cast<T*>(nullptr), (int64_t)0, 0.f);
   return hipGetLastError();
 }
 
@@ -322,7 +407,46 @@ hipError_t launch_select_d(const Dims& s, const IndexerDims& ix, const float* w_
                       : launch_select_t<T, 128, 128>(s, ix, w_q, q, q_len, q_pos0, k_idx, kv_cap, sel, sel_scores, ws_scores, n_chunks, st);
 }
 
+template <int D, int DI, int NT>
+hipError_t launch_step_nt(const Dims& s, const IndexerDims& ix, const float* w_q, const float* w_k, const void* q,
+                          const void* k, const void* v, float* k_comp, float* k_idx, int64_t kv_len, int64_t kv_cap,
+                          int32_t* sel, float* sel_scores, void* out, hipStream_t st) {
+  const int64_t rows = (int64_t)s.batch * s.hkv;
+  const auto* qp = static_cast<const uint16_t*>(q);
+  auto kern = ix.agg == kAggSum   ? indexer_select_kernel<uint16_t, D, DI, kAggSum, NT, false, true>
+              : ix.agg == kAggMax ? indexer_select_kernel<uint16_t, D, DI, kAggMax, NT, false, true>
+                                  : indexer_select_kernel<uint16_t, D, DI, kAggSoftmax, NT, false, true>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(NT), 0, st, qp, w_q, k_idx, sel, sel_scores, nullptr,
+                     (int64_t)0, (int64_t)1, kv_len - 1, kv_cap / s.bs, s.hq, s.hkv, s.group, s.bs, s.top_k, ix.scale,
+                     s.keep_tail, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), w_k, k_comp,
+                     k_idx, static_cast<uint16_t*>(out), kv_cap, s.scale * 1.4426950408889634f);
+  return hipGetLastError();
+}
+
+template <int D, int DI>
+hipError_t launch_step_t(const Dims& s, const IndexerDims& ix, const float* w_q, const float* w_k, const void* q,
+                         const void* k, const void* v, float* k_comp, float* k_idx, int64_t kv_len, int64_t kv_cap,
+                         int32_t* sel, float* sel_scores, void* out, hipStream_t st) {
+  // as the selection: 8 waves per row when the rows are fewer than the CUs
+  if ((int64_t)s.batch * s.hkv < 256)
+    return launch_step_nt<D, DI, 512>(s, ix, w_q, w_k, q, k, v, k_comp, k_idx, kv_len, kv_cap, sel, sel_scores, out, st);
+  return launch_step_nt<D, DI, 256>(s, ix, w_q, w_k, q, k, v, k_comp, k_idx, kv_len, kv_cap, sel, sel_scores, out, st);
+}
+
 }  // namespace
+
+hipError_t launch_indexer_step(const Dims& s, const IndexerDims& ix, const float* w_q, const float* w_k,
+                               const void* q, const void* k, const void* v, float* k_comp, float* k_idx,
+                               int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out,
+                               hipStream_t st) {
+  if (s.d == 64)
+    return ix.dim == 64
+               ? launch_step_t<64, 64>(s, ix, w_q, w_k, q, k, v, k_comp, k_idx, kv_len, kv_cap, sel, sel_scores, out, st)
+               : launch_step_t<64, 128>(s, ix, w_q, w_k, q, k, v, k_comp, k_idx, kv_len, kv_cap, sel, sel_scores, out, st);
+  return ix.dim == 64
+             ? launch_step_t<128, 64>(s, ix, w_q, w_k, q, k, v, k_comp, k_idx, kv_len, kv_cap, sel, sel_scores, out, st)
+             : launch_step_t<128, 128>(s, ix, w_q, w_k, q, k, v, k_comp, k_idx, kv_len, kv_cap, sel, sel_scores, out, st);
+}
 
 hipError_t launch_indexer_keys(const Dims& s, const IndexerDims& ix, const float* w_k, const float* k_comp,
                                int64_t kv_cap, int64_t blk_begin, int64_t blk_end, float* k_idx, hipStream_t st) {

@@ -30,6 +30,14 @@ hipError_t launch_indexer_keys(const Dims& s, const IndexerDims& ix, const float
 hipError_t launch_indexer_select(const Dims& s, const IndexerDims& ix, const float* w_q, const void* q,
                                  int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_cap, int32_t* sel,
                                  float* sel_scores, void* ws, hipStream_t st);
+// One decode step with the learned indexer (bf16, top_k <= 64), one
+// workgroup per (sequence, KV head): compress the block the new token at
+// kv_len - 1 closes (if any) into k_comp and its indexer key into k_idx,
+// select in indexer space, attend over the selection into out.
+hipError_t launch_indexer_step(const Dims& s, const IndexerDims& ix, const float* w_q, const float* w_k,
+                               const void* q, const void* k, const void* v, float* k_comp, float* k_idx,
+                               int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores, void* out,
+                               hipStream_t st);
 
 // Rotated 8-bit K/V cache: positions [pos_begin, pos_end) of every (b, g)
 // rotated (Walsh-Hadamard) and quantized (codes + float16 scale per 32).

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 8
+#define QSA_ABI_VERSION 9
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -306,6 +306,32 @@ qsa_status qsa_indexer_keys(const qsa_shape* shape, const qsa_indexer* idx, cons
 qsa_status qsa_indexer_select(const qsa_shape* shape, const qsa_indexer* idx, const float* w_q, const void* q,
                               int64_t q_len, int64_t q_pos0, const float* k_idx, int64_t kv_len, int64_t kv_cap,
                               int32_t* sel, float* sel_scores, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step with the learned indexer, in one kernel: the same results
+ * as qsa_compress_keys and qsa_indexer_keys over the block the new token
+ * closes (if any; block_begin = (kv_len-1)/Bs), then qsa_indexer_select
+ * (q_len = 1, q_pos0 = kv_len-1) and qsa_sparse_attn_decode on its
+ * selection ("Qwen4 in llama.cpp: Dissecting PR #27742", section "QSA Is an
+ * Address-Selection Problem, Not a New Attention Equation": the indexer
+ * scores compressed blocks, and attention runs over the kept ones).
+ *   q           [b][Hq][d] bf16, the new token's query heads;
+ *   k, v        [b][Hkv][kv_cap][d] bf16, holding positions 0 .. kv_len-1;
+ *   k_comp      [b][Hkv][kv_cap/Bs][d] float32, blocks below (kv_len-1)/Bs
+ *               written; the closed block is added;
+ *   k_idx       [b][Hkv][kv_cap/Bs][dim] float32, the same blocks; the
+ *               closed block's indexer key is added;
+ *   w_q, w_k    device float32 [d][dim];
+ *   sel, sel_scores, out: as qsa_decode_step.
+ * One workgroup per (sequence, KV head); no workspace. Serves bf16 with
+ * top_k <= 64 (QSA_ERR_UNSUPPORTED otherwise: use the separate calls).
+ * Selections and the two caches equal the separate calls' bit for bit;
+ * outputs agree up to the rounding of the attention's merge order.
+ * QSA_ERR_INVALID for null or misaligned pointers (all 16-byte aligned),
+ * kv_len outside [1, kv_cap] or a bad indexer struct. */
+qsa_status qsa_indexer_decode_step(const qsa_shape* shape, const qsa_indexer* idx, const float* w_q,
+                                   const float* w_k, const void* q, const void* k, const void* v, float* k_comp,
+                                   float* k_idx, int64_t kv_len, int64_t kv_cap, int32_t* sel, float* sel_scores,
+                                   void* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Rotated 8-bit K/V cache ("Qwen4 in llama.cpp: Dissecting PR #27742",

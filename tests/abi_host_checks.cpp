@@ -133,6 +133,13 @@ int main() {
   expect(qsa_indexer_select(&k65b4, &ix, PF, P, 1, 4 * 70000 - 1, PF, 4 * 70000, 4 * 70000, PI, nullptr, P,
                             size_t(1) << 40, nullptr),
          QSA_ERR_UNSUPPORTED, "indexer k > 64 over more than 65536 candidates");
+  float* PFW = static_cast<float*>(P);
+  expect(qsa_indexer_decode_step(&good, &ix, PF, PF, P, P, P, PFW, PFW, 257, 256, PI, nullptr, P, nullptr),
+         QSA_ERR_INVALID, "indexer step beyond capacity");
+  expect(qsa_indexer_decode_step(&good, &ix, PF, nullptr, P, P, P, PFW, PFW, 64, 256, PI, nullptr, P, nullptr),
+         QSA_ERR_INVALID, "indexer step without W_k");
+  expect(qsa_indexer_decode_step(&k65, &ix, PF, PF, P, P, P, PFW, PFW, 128, 256, PI, nullptr, P, nullptr),
+         QSA_ERR_UNSUPPORTED, "indexer step with k > 64");
   const int8_t* PC = static_cast<const int8_t*>(P);
   const uint16_t* PS = static_cast<const uint16_t*>(P);
   expect(qsa_sparse_attn_prefill_q8(&good, P, PC, PC, static_cast<const uint16_t*>(MIS), PS, 64, 0, 4096, PI, P,

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 8
+    assert qsa.abi_version() == 9
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -230,6 +230,26 @@ def test_indexer_arguments(qsa):
     assert sel_ix(ctypes.byref(big_k), ix, P, P, 1, 3999, P, 4000, 4096, P, N, P, need - 1, N) == 3
     assert sel_ix(ctypes.byref(big_k), ix, P, P, 1, 4 * 70000 - 1, P, 4 * 70000, 4 * 70000, P, N, P, 1 << 40,
                   N) == UNS
+    # the fused indexer decode step: (shape, idx, w_q, w_k, q, k, v, k_comp, k_idx, kv_len, kv_cap, sel,
+    # sel_scores, out, stream); bf16 with k <= 64 only
+    step = lib.qsa_indexer_decode_step
+    for bad in (qsa.make_indexer(96, 0), qsa.make_indexer(64, 3)):
+        assert step(sh, ctypes.byref(bad), P, P, P, P, P, P, P, 128, 256, P, N, P, N) == INV
+    assert step(sh, None, P, P, P, P, P, P, P, 128, 256, P, N, P, N) == INV
+    for i in range(2, 9):  # each required pointer null, then misaligned
+        args = [P] * 7
+        args[i - 2] = N
+        assert step(sh, ix, *args, 128, 256, P, N, P, N) == INV
+        args[i - 2] = MIS
+        assert step(sh, ix, *args, 128, 256, P, N, P, N) == INV
+    assert step(sh, ix, P, P, P, P, P, P, P, 128, 256, N, N, P, N) == INV       # no sel
+    assert step(sh, ix, P, P, P, P, P, P, P, 128, 256, P, MIS, P, N) == INV     # misaligned sel_scores
+    assert step(sh, ix, P, P, P, P, P, P, P, 128, 256, P, N, N, N) == INV       # no out
+    assert step(sh, ix, P, P, P, P, P, P, P, 0, 256, P, N, P, N) == INV         # kv_len < 1
+    assert step(sh, ix, P, P, P, P, P, P, P, 257, 256, P, N, P, N) == INV       # kv_len beyond capacity
+    assert step(ctypes.byref(big_k), ix, P, P, P, P, P, P, P, 128, 256, P, N, P, N) == UNS
+    assert step(ctypes.byref(good_shape(qsa, dtype=qsa.QSA_F32)), ix, P, P, P, P, P, P, P, 128, 256, P, N, P,
+                N) == UNS
 
 
 def test_decode_step_q8_arguments(qsa):

@@ -143,3 +143,78 @@ def test_indexer_selection_drives_attention():
             worst = max(worst, float(err))
             assert err <= BF16_ABS_TOL
     log(f"  attention over the indexer's selection: max error {worst:.2e} (tolerance {BF16_ABS_TOL}; f32 rel {F32_REL_TOL})")
+
+
+STEP_CASES = [
+    (W(kv_len=9000, top_k=16), 64, I.AGG_SUM),                                          # no block closed
+    (W(kv_len=64 * 150, top_k=16), 64, I.AGG_MAX),                                      # closes its own block
+    (W(kv_len=64 * 150, keep_tail=True, top_k=8), 64, I.AGG_SOFTMAX),                   # closes a candidate
+    (W(kv_len=64 * 150 + 1, keep_tail=True, top_k=8), 128, I.AGG_MAX),
+    (W(n_q_heads=16, n_kv_heads=1, batch=3, kv_len=5000), 64, I.AGG_SOFTMAX),          # G = 16
+    (W(head_dim=64, n_q_heads=8, block_size=16, top_k=24, kv_len=16 * 400), 128, I.AGG_SUM),  # gathered blocks
+    (W(kv_len=64, top_k=4), 64, I.AGG_SUM),                                             # block 0 closed, no candidate
+    (W(kv_len=1, top_k=1), 64, I.AGG_MAX),                                              # the first token
+    (W(batch=130, kv_len=2000, top_k=16), 64, I.AGG_MAX),                               # 260 rows: 4-wave workgroups
+]
+
+
+@pytest.mark.parametrize("c", STEP_CASES, ids=[case_id(c) for c in STEP_CASES])
+def test_indexer_decode_step(c):
+    """The fused indexer decode step: caches and selections bit for bit those of the separate calls, selections
+    and outputs against the oracle."""
+    from qsa_check import check_output_row
+    w, dim, agg = c
+    log(f"indexer step {case_id(c)}")
+    case = Case(w, seed=31, kv_cap=w.kv_len + 64)
+    b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    G, n, cap = hq // hkv, w.kv_len, case.kv_cap
+    w_q, w_k = S.indexer_weights(31, w.cfg_id, d, dim)
+    wq_d, wk_d = torch.from_numpy(w_q).cuda(), torch.from_numpy(w_k).cuda()
+    shape = qsa.shape_for(case.q, case.k, bs, k, keep_tail=w.keep_tail)
+    ix = qsa.make_indexer(dim, agg)
+    # the caches as they stand before the new token
+    k_comp = torch.full((b, hkv, cap // bs, d), float("nan"), device="cuda")
+    k_idx = torch.full((b, hkv, cap // bs, dim), float("nan"), device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, n - 1, k_comp)
+    qsa.qsa_indexer_keys(shape, ix, wk_d, k_comp, n - 1, cap, k_idx)
+    # the separate calls
+    k_comp2, k_idx2 = k_comp.clone(), k_idx.clone()
+    blk = (n - 1) // bs
+    qsa.qsa_compress_keys(shape, case.k, n, k_comp2, block_begin=blk)
+    qsa.qsa_indexer_keys(shape, ix, wk_d, k_comp2, n, cap, k_idx2, block_begin=blk)
+    q = case.q.view(b, 1, hq, d)
+    sel2 = torch.empty(b, 1, hkv, k, dtype=torch.int32, device="cuda")
+    sc2 = torch.empty(b, 1, hkv, k, dtype=torch.float32, device="cuda")
+    qsa.qsa_indexer_select(shape, ix, wq_d, q, n - 1, k_idx2, n, cap, sel2, sc2)
+    out2 = torch.empty(b, hq, d, dtype=case.q.dtype, device="cuda")
+    qsa.qsa_sparse_attn_decode(shape, q.view(b, hq, d), case.k, case.v, n, sel2.view(b, hkv, k), out2)
+    # the fused step
+    sel = torch.empty(b, hkv, k, dtype=torch.int32, device="cuda")
+    sc = torch.empty(b, hkv, k, dtype=torch.float32, device="cuda")
+    out = torch.empty(b, hq, d, dtype=case.q.dtype, device="cuda")
+    qsa.qsa_indexer_decode_step(shape, ix, wq_d, wk_d, q.view(b, hq, d), case.k, case.v, k_comp, k_idx, n, sel, out,
+                                sel_scores=sc)
+    torch.cuda.synchronize()
+    nb = n // bs
+    assert torch.equal(k_comp[:, :, :nb], k_comp2[:, :, :nb]), "compressed keys differ from the separate calls"
+    assert torch.equal(k_idx[:, :, :nb], k_idx2[:, :, :nb]), "indexer keys differ from the separate calls"
+    assert torch.equal(sel, sel2.view(b, hkv, k)), "selection differs from the separate calls"
+    assert torch.equal(sc, sc2.view(b, hkv, k)), "selection scores differ from the separate calls"
+    diff = (out.float() - out2.float()).abs().max().item()
+    assert diff <= BF16_ABS_TOL, f"output differs from the separate calls by {diff}"
+    # against the oracle
+    p = n - 1
+    n_cand, forced = O.selection_frame(p, bs, w.keep_tail)
+    ref_k = I.indexer_keys(case.K[:, :, :n], w_k.astype(np.float64), bs)
+    sel_h, out_h = sel.cpu().numpy(), from_device(out)
+    scale = I.default_indexer_scale(dim)
+    stats, worst = {"clear": 0, "ambiguous": 0}, 0.0
+    for bb in range(b):
+        for g in range(hkv):
+            qg = case.Q[bb, 0, g * G:(g + 1) * G].astype(np.float64)
+            agg_sc = I.aggregate(I.head_scores(qg, w_q.astype(np.float64), ref_k[bb, g], n_cand, scale), agg)
+            row = [int(x) for x in sel_h[bb, g]]
+            stats[check_selection_frame(row, agg_sc, n_cand, forced, k)] += 1
+            ref = O.attend_given_selection(qg, case.K[bb, g], case.V[bb, g], row, p, bs, O.default_scale(d))
+            worst = max(worst, check_output_row(out_h[bb, g * G:(g + 1) * G], ref, "bf16", where=f"row {(bb, g)}:"))
+    log(f"  selections {stats}, output error over the row bound {worst:.3f}, against the separate calls {diff:.2e}")

@@ -186,7 +186,8 @@ def test_ragged_batched_decode_workload():
 
 
 def test_indexer_decode_workload():
-    """The 32K decode with a learned indexer (64 dimensions, max over the heads), as the benchmark runs it."""
+    """The 32K decode with a learned indexer (64 dimensions, max over the heads), as the benchmark runs it: one
+    fused indexer decode step."""
     from oracle import qsa_indexer as IX
     from oracle import qsa_oracle as O
     from qsa_check import check_output_row, check_selection_frame
@@ -198,17 +199,20 @@ def test_indexer_decode_workload():
     w_q, w_k = S.indexer_weights(0, w.cfg_id, d, w.indexer_dim)
     shape = qsa.shape_for(case.q, case.k, bs, k)
     ix = qsa.make_indexer(w.indexer_dim, w.indexer_agg)
-    k_comp = torch.empty(b, hkv, w.kv_len // bs, d, device="cuda")
-    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
-    k_idx = torch.empty(b, hkv, w.kv_len // bs, w.indexer_dim, device="cuda")
-    qsa.qsa_indexer_keys(shape, ix, torch.from_numpy(w_k).cuda(), k_comp, w.kv_len, w.kv_len, k_idx)
-    sel = torch.empty(b, 1, hkv, k, dtype=torch.int32, device="cuda")
-    qsa.qsa_indexer_select(shape, ix, torch.from_numpy(w_q).cuda(), case.q, w.kv_len - 1, k_idx, w.kv_len, w.kv_len,
-                           sel)
+    # the caches hold the blocks closed before the new token; the step (one qsa_indexer_decode_step call, as the
+    # benchmark times it) adds the block the token closes, selects and attends
+    wk_d = torch.from_numpy(w_k).cuda()
+    k_comp = torch.full((b, hkv, w.kv_len // bs, d), float("nan"), device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len - 1, k_comp)
+    k_idx = torch.full((b, hkv, w.kv_len // bs, w.indexer_dim), float("nan"), device="cuda")
+    qsa.qsa_indexer_keys(shape, ix, wk_d, k_comp, w.kv_len - 1, w.kv_len, k_idx)
     q = case.q.view(b, hq, d)
+    sel = torch.empty(b, 1, hkv, k, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
-    qsa.qsa_sparse_attn_decode(shape, q, case.k, case.v, w.kv_len, sel.view(b, hkv, k), out)
+    qsa.qsa_indexer_decode_step(shape, ix, torch.from_numpy(w_q).cuda(), wk_d, q, case.k, case.v, k_comp, k_idx,
+                                w.kv_len, sel.view(b, hkv, k), out)
     torch.cuda.synchronize()
+    assert not torch.isnan(k_comp).any() and not torch.isnan(k_idx).any(), "every block's keys written"
     p = w.kv_len - 1
     n_cand, forced = O.selection_frame(p, bs, False)
     ref_k = IX.indexer_keys(case.K, w_k.astype(np.float64), bs)
