@@ -517,7 +517,7 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
       !aligned16(sel) || !aligned16(out))
     return QSA_ERR_INVALID;
   if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
-  if (s.dtype != QSA_BF16 || s.bs < 32) return QSA_ERR_UNSUPPORTED;
+  if (s.dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
   const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len, false);  // 4-wave slices at every row count
   if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
@@ -537,7 +537,7 @@ qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, con
       !aligned16(sel) || !aligned16(out))
     return QSA_ERR_INVALID;
   if (q_len <= 0 || q_pos0 < 0 || kv_cap <= 0 || q_pos0 + q_len > kv_cap) return QSA_ERR_INVALID;
-  if (s.dtype != QSA_BF16 || s.bs < 32) return QSA_ERR_UNSUPPORTED;
+  if (s.dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
   if ((int64_t)s.batch * q_len * s.hkv > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;  // one workgroup per row
   return hip_status(qsa::launch_prefill_q8(s, q, k_q, v_q, k_scales, v_scales, q_len, q_pos0, kv_cap, sel, out,

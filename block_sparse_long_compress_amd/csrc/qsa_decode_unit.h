@@ -114,7 +114,6 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
                                              int64_t p, float scale_log2, unsigned char* vs, int first, int stride,
                                              float& m_run, float& l_run, f32x4_t (&o)[D / 16],
                                              Q8Cache q8 = Q8Cache{nullptr, nullptr, nullptr, nullptr}) {
-  static_assert(!(Q8 && GATHER), "the quantized cache is read in whole 32-key units");
   constexpr int RS = kStageRowBytes<D>;
   constexpr int KS = D / 32;  // 32-wide K steps of the QK^T product
   constexpr int DT = D / 16;  // 16-wide dim tiles of the PV product
@@ -146,6 +145,56 @@ __device__ __forceinline__ void attend_units(const u32x4_t (&qf)[D / 32], const 
       const int rowpos = (slot < n_e && c >= 0 && pos <= p) ? (int)pos : -1;
       if (__ballot(rowpos >= 0) == 0) return;
       u.ok = true;
+      if constexpr (Q8) {
+        // the 8-bit cache, rows gathered: a lane's K codes are those of the
+        // contiguous case (its row 16 st + col, bytes 64 t + 16 lg, scale
+        // group 2 t + lg/2) at the row's own position, with that row's scale
+        // read directly; V codes and scales likewise per staged row, widened
+        // straight into the wave's staging slice. Rows past the causal bound
+        // or of padding entries read as code 0 with scale 0, i.e. zero.
+        static_assert(KS % 2 == 0, "two operand steps per 16-byte load");
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int kp = __builtin_amdgcn_ds_bpermute((16 * st + col) << 2, rowpos);
+          u.mpos[st] = __builtin_amdgcn_ds_bpermute((16 * st + 4 * lg) << 2, rowpos);
+          const int64_t kr = kp >= 0 ? kp : 0;
+          u32x4_t kc[KS / 2];
+          uint16_t ksc[KS / 2];
+#pragma unroll
+          for (int t = 0; t < KS / 2; ++t) {
+            kc[t] = kp >= 0 ? *reinterpret_cast<const u32x4_t*>(q8.k + kr * D + 64 * t + 16 * lg)
+                            : u32x4_t{0u, 0u, 0u, 0u};
+            ksc[t] = kp >= 0 ? q8.ks[kr * (D / 32) + 2 * t + lg / 2] : (uint16_t)0;
+          }
+#pragma unroll
+          for (int t = 0; t < KS / 2; ++t) {
+            const float sc = f16_bits_to_f32(ksc[t]);
+            u.kf[st][2 * t] = dequant8_bf16(u32x2_t{kc[t][0], kc[t][1]}, sc);
+            u.kf[st][2 * t + 1] = dequant8_bf16(u32x2_t{kc[t][2], kc[t][3]}, sc);
+          }
+        }
+        u32x2_t vc[VCH];
+        uint16_t vsc[VCH];
+        int vrow[VCH];
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) {
+          const int ci = lane + kWave * j;
+          const int rr = ci / (D / 8), c8 = ci % (D / 8);
+          const int vp = __builtin_amdgcn_ds_bpermute(rr << 2, rowpos);
+          const int64_t vr = vp >= 0 ? vp : 0;
+          vrow[j] = rr;
+          vc[j] = vp >= 0 ? *reinterpret_cast<const u32x2_t*>(q8.v + vr * D + 8 * c8) : u32x2_t{0u, 0u};
+          vsc[j] = vp >= 0 ? q8.vs[vr * (D / 32) + c8 / 4] : (uint16_t)0;
+        }
+        // (the previous unit's reads of the staging slice ended at its
+        // closing wave barrier)
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) {
+          const int c8 = (lane + kWave * j) % (D / 8);
+          *reinterpret_cast<u32x4_t*>(vs + vrow[j] * RS + 16 * c8) = dequant8_bf16(vc[j], f16_bits_to_f32(vsc[j]));
+        }
+        return;
+      }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int kp = __builtin_amdgcn_ds_bpermute((16 * st + col) << 2, rowpos);

@@ -125,8 +125,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_attn_q8_kernel(
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int sel_mine = lane < n_e ? sel[row * top_k + e0 + lane] : -1;
   const Q8Cache cache{kq + kv_off * D, vq + kv_off * D, ks + kv_off * (D / 32), vs_ + kv_off * (D / 32)};
-  attend_units<D, false, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2,
-                               smem + w * kUnit * SM::RS, w, NW, m_run, l_run, o, cache);
+  // blocks shorter than a 32-key unit: the unit's rows gathered from several entries
+  if (bs < kUnit)
+    attend_units<D, true, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2, smem + w * kUnit * SM::RS, w,
+                                NW, m_run, l_run, o, cache);
+  else
+    attend_units<D, false, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2, smem + w * kUnit * SM::RS,
+                                 w, NW, m_run, l_run, o, cache);
   l_run = sum_col4(l_run);
 
   // combine the waves' states in LDS (wave order), rotate the combined O
@@ -262,8 +267,12 @@ __global__ __launch_bounds__(8 * kWave) void prefill_rows_q8_kernel(
   for (int e0 = 0; e0 < top_k; e0 += kWave) {
     const int n_e = top_k - e0 < kWave ? top_k - e0 : kWave;
     const int sel_mine = lane < n_e ? sel_row[e0 + lane] : -1;
-    attend_units<D, false, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2, smem + w * kUnit * RS, w,
-                                 NW, m_run, l_run, o, cache);
+    if (bs < kUnit)  // rows gathered from several entries per unit
+      attend_units<D, true, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2, smem + w * kUnit * RS, w,
+                                  NW, m_run, l_run, o, cache);
+    else
+      attend_units<D, false, true>(qf, nullptr, nullptr, sel_mine, n_e, bs, p, scale_log2, smem + w * kUnit * RS, w,
+                                   NW, m_run, l_run, o, cache);
   }
   l_run = sum_col4(l_run);
   finish_row_slice<D, NW, true>(m_run, l_run, o, smem, &last_wg, out, nullptr, nullptr, row, bt, g, hq, G, 0, 1);

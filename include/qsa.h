@@ -363,8 +363,9 @@ qsa_status qsa_kv_quantize(const qsa_shape* shape, const void* k, const void* v,
  * scores use (H q).(H k)/head_dim, and every slice's output is rotated back
  * before the slices merge. Same selection, plan and workspace as
  * qsa_sparse_attn_decode (ws: qsa_workspace_bytes(shape, QSA_OP_DECODE, 1,
- * kv_len) bytes, zero-filled before first use). bf16 with Bs >= 32 only,
- * else QSA_ERR_UNSUPPORTED. */
+ * kv_len) bytes, zero-filled before first use). Blocks shorter than 32 keys
+ * gather each 32-key unit's rows from several entries, as the bf16 kernel
+ * does. bf16 only, else QSA_ERR_UNSUPPORTED. */
 qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, const int8_t* k_q, const int8_t* v_q,
                                      const uint16_t* k_scales, const uint16_t* v_scales, int64_t kv_len,
                                      int64_t kv_cap, const int32_t* sel, void* out, void* ws, size_t ws_bytes,
@@ -376,7 +377,7 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
  * 0 .. q_pos0+q_len-1. Each row's query heads are rotated, its scores are
  * (H q).(H k)/head_dim over the codes, causal at the row's own position, and
  * its output is rotated back; one workgroup per (sequence, row, KV head), any
- * top_k; no workspace. bf16 with Bs >= 32 only, else QSA_ERR_UNSUPPORTED
+ * top_k and block size; no workspace. bf16 only, else QSA_ERR_UNSUPPORTED
  * (also when batch * q_len * Hkv exceeds 2^31 - 1). */
 qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, const int8_t* k_q, const int8_t* v_q,
                                       const uint16_t* k_scales, const uint16_t* v_scales, int64_t q_len,

@@ -147,9 +147,9 @@ int main() {
          QSA_ERR_INVALID, "8-bit prefill scales misaligned");
   expect(qsa_sparse_attn_prefill_q8(&good, P, PC, PC, PS, PS, 64, 4040, 4096, PI, P, nullptr), QSA_ERR_INVALID,
          "8-bit prefill beyond capacity");
-  qsa_shape bs16 = shape(2, 16, 2, 128, 16, 16, QSA_BF16);
-  expect(qsa_sparse_attn_prefill_q8(&bs16, P, PC, PC, PS, PS, 64, 0, 4096, PI, P, nullptr), QSA_ERR_UNSUPPORTED,
-         "8-bit prefill with blocks of 16");
+  qsa_shape f32_16 = shape(2, 16, 2, 128, 16, 16, QSA_F32);
+  expect(qsa_sparse_attn_prefill_q8(&f32_16, P, PC, PC, PS, PS, 64, 0, 4096, PI, P, nullptr), QSA_ERR_UNSUPPORTED,
+         "8-bit prefill with a float32 shape");
   qsa_shape f32 = shape(2, 16, 2, 128, 64, 16, QSA_F32);
   expect(qsa_kv_quantize(&f32, P, P, 64, 64, 0, static_cast<int8_t*>(P), static_cast<int8_t*>(P),
                          static_cast<uint16_t*>(P), static_cast<uint16_t*>(P), nullptr),

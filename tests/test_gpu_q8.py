@@ -37,6 +37,10 @@ CASES = [
     W(batch=40, kv_len=2000, top_k=8, block_size=128, n_q_heads=8),       # 80 rows
     W(batch=1, kv_len=50, top_k=4),                                       # own block only
     W(batch=64, kv_len=3000, top_k=16),                                   # 128 rows: 8-wave workgroups
+    # blocks shorter than a 32-key unit: each unit gathers its rows from several entries
+    W(batch=3, kv_len=3000, top_k=16, block_size=16),
+    W(batch=1, kv_len=8 * 700 + 5, top_k=24, block_size=8, head_dim=64),
+    W(batch=2, kv_len=4 * 2000 + 3, top_k=100, block_size=4),             # k > 64: several slices
 ]
 
 
@@ -131,6 +135,9 @@ PREFILL_CASES = [
     (W(mode="prefill", batch=2, kv_len=1500, top_k=80, block_size=32, head_dim=64), 1100),  # k > 64: two chunks
     (W(mode="prefill", batch=1, kv_len=64 * 40 + 7, top_k=8, keep_tail=True), 64 * 40 - 60),  # keep-tail frame
     (W(mode="prefill", batch=1, kv_len=600, top_k=4, block_size=128, n_q_heads=16, n_kv_heads=1), 0),  # G = 16
+    # gathered units: the released budget's blocks of 4 keys past a prefix, and blocks of 16 from row 0
+    (W(mode="prefill", batch=1, kv_len=4 * 300 + 2, top_k=100, block_size=4), 4 * 300 - 40),
+    (W(mode="prefill", batch=1, kv_len=16 * 60 + 3, top_k=8, block_size=16, head_dim=64), 0),
 ]
 
 
