@@ -268,57 +268,6 @@ __device__ __forceinline__ uint64_t wave_sort_desc_n(uint64_t x) {
   return x;
 }
 
-// Reversal inside each 16-lane row (lane i <- lane i ^ 15), DPP row_mirror.
-__device__ __forceinline__ uint64_t mirror16_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, 0x140, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), 0x140, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Every 16-lane group sorted descending on its own (bitonic, DPP steps only).
-__device__ __forceinline__ uint64_t sort16_groups_desc(uint64_t x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int k = 2; k <= 16; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t y = xor_lane_u64(x, j);
-      const bool lower = (lane & j) == 0;
-      const bool desc = k == 16 || (lane & k) == 0;
-      x = cas_u64(x, y, lower == desc);
-    }
-  }
-  return x;
-}
-
-// Per 16-lane group: the 16 largest of two descending groups a and b, in
-// descending order. max(a[i], b[15 - i]) holds exactly those 16 as a
-// bitonic sequence, which the half-cleaner steps put in order.
-__device__ __forceinline__ uint64_t prune16_desc(uint64_t a, uint64_t b) {
-  const int lane = lane_id();
-  const uint64_t r = mirror16_u64(b);
-  uint64_t x = a > r ? a : r;
-#pragma unroll
-  for (int j = 8; j > 0; j >>= 1) {
-    const uint64_t y = xor_lane_u64(x, j);
-    x = cas_u64(x, y, (lane & j) == 0);
-  }
-  return x;
-}
-
-// The 16 largest of 256 keys held four per lane, descending in every 16-lane
-// group (so in lanes 0..15): the groups of each register are sorted, then
-// merged pairwise keeping the larger half (registers, then the groups
-// 16 and 32 lanes apart).
-__device__ __forceinline__ uint64_t top16_of_256(const uint64_t (&x)[4]) {
-  uint64_t s[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) s[p] = sort16_groups_desc(x[p]);
-  uint64_t c = prune16_desc(prune16_desc(s[0], s[1]), prune16_desc(s[2], s[3]));
-  c = prune16_desc(c, xor_lane_u64(c, 16));
-  return prune16_desc(c, xor_lane_u64(c, 32));
-}
-
 // ------------------------------------------------------------ threshold select
 //
 // Exact selection of the m largest of the keys held P per lane (key 0 =
@@ -441,6 +390,22 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
   return ((uint64_t)hi << 32) | lo;
+}
+
+// The 16 largest of 256 keys held four per lane (0 = empty; the others
+// distinct), descending in lanes 0..15. The 16th largest lane maximum t is a
+// lower bound of the 16th largest key (the 16 largest maxima are keys >= t),
+// and only the 16 lanes whose maximum reaches t hold keys >= t, so at most
+// 64 keys survive the cut; they are gathered (scratch: 64 keys of LDS owned
+// by the calling wave) and sorted. Two wave sorts and a gather, where
+// sorting all 256 keys takes four 16-lane sorts and five merges.
+__device__ __forceinline__ uint64_t top16_of_256(const uint64_t (&x)[4], uint64_t* scratch) {
+  const uint64_t m01 = x[0] > x[1] ? x[0] : x[1];
+  const uint64_t m23 = x[2] > x[3] ? x[2] : x[3];
+  uint64_t t = readlane_u64(wave_sort_desc(m01 > m23 ? m01 : m23), 15);
+  if (t == 0ull) t = 1ull;  // fewer than 16 non-empty lanes: every key survives (at most 60)
+  int count;
+  return wave_sort_desc(gather_keys_ge<4>(x, t, scratch, count));
 }
 
 // Fold one lane-per-candidate batch into a running descending top list

@@ -657,11 +657,12 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
 }
 
 // The score pass for many query rows (prefill): a workgroup takes a tile of
-// 16 consecutive rows of one (b, g) and one chunk of 256 candidates, which
+// 32 consecutive rows of one (b, g) and one chunk of 256 candidates, which
 // the rows share (k_comp is read once per tile instead of once per row).
 // Scores come from fp32 MFMA as in the tile path; wave w scores candidates
-// 16w .. 16w + 15 of each pass of 64, and as no other wave needs them it
-// loads their compressed keys straight into its operand registers, two
+// 16w .. 16w + 15 of each pass of 64 for both 16-row halves of the tile (one
+// load of their compressed keys feeds two products), and as no other wave
+// needs them it loads those keys straight into its operand registers, two
 // passes ahead. Outputs are those of the per-row pass:
 // every score of every row, and per (row, chunk) the chunk's 16 best keys in
 // descending order when the row's candidates exceed the pick pool.
@@ -670,6 +671,8 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
 // x, x + 8, ... of the flattened (sequence, KV head, chunk) order) and its
 // tiles are dispatched there one after another: they run together and read
 // the chunk's compressed keys from that XCD's L2, which fetches them once.
+constexpr int kLargeTileRows = 32;
+
 // Grid of select_large_tile_kernel: 8 XCD lanes of ceil(n_bg * n_chunks / 8)
 // chunks of n_tiles workgroups each.
 inline int64_t large_tile_grid(int64_t n_bg, int64_t n_chunks, int64_t n_tiles) {
@@ -681,12 +684,14 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
     const T* __restrict__ q, const float* __restrict__ k_comp, uint32_t* __restrict__ ws_scores,
     uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs,
     float scale, int keep_tail, int64_t n_chunks, int64_t n_tiles, int64_t n_bg) {
+  constexpr int TR = kLargeTileRows;
   constexpr int QP = D + 4;  // padded row strides (floats): conflict-free 16-byte reads
   constexpr int PASSES = kLargeChunk / kTileCands;
   constexpr int DU = D / 16;  // 16-byte operand loads per lane and pass
-  __shared__ float qbar[kTileRows][QP];
-  __shared__ float sc[kTileRows][kLargeChunk + 4];
-  __shared__ int ncand[kTileRows];  // candidates of each row of the tile
+  __shared__ float qbar[TR][QP];
+  __shared__ float sc[TR][kLargeChunk + 4];
+  __shared__ int ncand[TR];  // candidates of each row of the tile
+  __shared__ uint64_t gather[4][kWave];  // each wave's scratch for its chunk lists
   static_assert(kLargeChunk == 256, "one thread per candidate of the chunk");
 
   const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
@@ -698,15 +703,15 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
   const int64_t b = bg / hkv;
   const int g = (int)(bg % hkv);
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int64_t t0 = tile * kTileRows;
-  const int rows = (int)(q_len - t0 < kTileRows ? q_len - t0 : kTileRows);
+  const int64_t t0 = tile * TR;
+  const int rows = (int)(q_len - t0 < TR ? q_len - t0 : TR);
   const int64_t c_begin = ch * kLargeChunk;
   // the tile's last row has the most candidates
   const int64_t cand_end = row_frame(q_pos0 + t0 + rows - 1, bs, keep_tail).n_cand;
   if (c_begin >= cand_end) return;  // uniform over the workgroup
-  if (tid < kTileRows) ncand[tid] = tid < rows ? row_frame(q_pos0 + t0 + tid, bs, keep_tail).n_cand : 0;
+  if (tid < TR) ncand[tid] = tid < rows ? row_frame(q_pos0 + t0 + tid, bs, keep_tail).n_cand : 0;
 
-  for (int idx = tid; idx < kTileRows * D / 4; idx += 256) {
+  for (int idx = tid; idx < TR * D / 4; idx += 256) {
     const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
     f32x4_t v = {0.f, 0.f, 0.f, 0.f};
     if (r < rows) v = group_sum4(q + ((b * q_len + t0 + r) * hq + (int64_t)g * G) * D + e4, G, D);
@@ -727,19 +732,26 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
   load_pass(0, kb[0]);
   load_pass(1, kb[1]);
   __syncthreads();  // qbar written
-  f32x4_t qa[DU];  // A operands: row m, dims 16u + 4kg .. + 3
+  // A operands, both halves: row 16h + m, dims 16u + 4kg .. + 3
+  f32x4_t qa[2][DU];
 #pragma unroll
-  for (int u = 0; u < DU; ++u) qa[u] = *reinterpret_cast<const f32x4_t*>(&qbar[m][16 * u + 4 * kg]);
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int u = 0; u < DU; ++u) qa[h][u] = *reinterpret_cast<const f32x4_t*>(&qbar[16 * h + m][16 * u + 4 * kg]);
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int u = 0; u < DU; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma_f32(qa[u][e], kb[pass % 2][u][e], acc);
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[h] = mfma_f32(qa[h][u][e], kb[pass % 2][u][e], acc[h]);
     if (pass + 2 < PASSES) load_pass(pass + 2, kb[pass % 2]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[4 * kg + i][pass * kTileCands + 16 * w + m] = acc[i] * scale;
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[16 * h + 4 * kg + i][pass * kTileCands + 16 * w + m] = acc[h][i] * scale;
   }
   __syncthreads();
   // every row's scores of the chunk (thread tid: candidate c_begin + tid of
@@ -751,9 +763,9 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
     for (int r = 0; r < rows; ++r, dst += stride)
       if (cand < ncand[r]) *dst = score_order_bits(sc[r][tid]);
   }
-  // the chunk's 16 best keys of each row that needs them (wave w: rows 4w .. 4w + 3)
-  for (int rr = 0; rr < 4; ++rr) {
-    const int r = 4 * w + rr;
+  // the chunk's 16 best keys of each row that needs them (wave w: rows 8w .. 8w + 7)
+  for (int rr = 0; rr < TR / 4; ++rr) {
+    const int r = (TR / 4) * w + rr;
     if (r >= rows) break;
     const int64_t n_cand = ncand[r];
     if (n_cand <= kPoolCap || c_begin >= n_cand) continue;  // uniform over the wave
@@ -764,7 +776,7 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
       const int64_t cand = c_begin + p * kWave + lane;
       x[p] = cand < n_cand ? make_key(sc[r][p * kWave + lane], (int)cand) : 0ull;
     }
-    const uint64_t top = top16_of_256(x);
+    const uint64_t top = top16_of_256(x, gather[w]);
     const int64_t row = (b * q_len + t0 + r) * hkv + g;
     if (lane < kLargeList) ws_lists[(row * n_chunks + ch) * kLargeList + lane] = top;
   }
@@ -785,6 +797,7 @@ __global__ __launch_bounds__(kWave) void select_large_lists_kernel(const uint32_
   const int64_t n_cand = row_frame(q_pos0 + t, bs, keep_tail).n_cand;
   const int64_t c_begin = ch * kLargeChunk;
   if (n_cand <= kPoolCap || c_begin >= n_cand) return;
+  __shared__ uint64_t gather[kWave];
   const int lane = lane_id();
   static_assert(kLargeChunk == 4 * kWave && kLargeList == 16, "top16_of_256");
   uint64_t x[4];
@@ -795,7 +808,7 @@ __global__ __launch_bounds__(kWave) void select_large_lists_kernel(const uint32_
                                (uint64_t)(0xFFFFFFFFu - (uint32_t)cand)
                          : 0ull;
   }
-  const uint64_t top = top16_of_256(x);
+  const uint64_t top = top16_of_256(x, gather);
   if (lane < kLargeList) ws_lists[(row * n_chunks + ch) * kLargeList + lane] = top;
 }
 
@@ -836,7 +849,7 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
     uint64_t* wsl = reinterpret_cast<uint64_t*>(wss + rows * plan.n_chunks * kLargeChunk);
     if (plan.n_chunks > 0 && plan.tiled) {
       // prefill rows (close_block < 0: nothing to compress)
-      const int64_t n_tiles = (q_len + kTileRows - 1) / kTileRows;
+      const int64_t n_tiles = (q_len + kLargeTileRows - 1) / kLargeTileRows;
       const int64_t n_bg = (int64_t)s.batch * s.hkv;
       hipLaunchKernelGGL((select_large_tile_kernel<T, D>), dim3((unsigned)large_tile_grid(n_bg, plan.n_chunks, n_tiles)),
                          dim3(256), 0, st, q, k_comp, wss, wsl, q_len, q_pos0, nb_cap, s.hq, s.hkv, s.group, s.bs,
@@ -902,7 +915,7 @@ SelectPlan plan_select_large(const Dims& s, int64_t q_len, int64_t q_pos0) {
   // many query rows: the score pass over tiles of rows sharing a chunk
   p.tiled = q_len >= kTileRows;
   const int64_t score_grid = p.tiled ? large_tile_grid((int64_t)s.batch * s.hkv, p.n_chunks,
-                                                       (q_len + kTileRows - 1) / kTileRows)
+                                                       (q_len + kLargeTileRows - 1) / kLargeTileRows)
                                      : rows * p.n_chunks;
   p.grid = score_grid > rows ? score_grid : rows;
   return p;
