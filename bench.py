@@ -238,7 +238,9 @@ class Step:
             self.calls.insert(len(self.calls) - 2, ("quantize", self.quantize))
         separate = (w.indexer_dim or w.kv_q8) and not self.fused
         self.step_calls = [("step", self.decode_step)] if w.mode == "decode" and not separate else self.calls
-        if self.fused:
+        # a decode step is timed as the one step call wherever it is one (also where the step runs more than
+        # one kernel, as for k > 64)
+        if self.fused or (w.mode == "decode" and not separate):
             self.calls = self.step_calls
 
     def _ws(self, op, q_len, kv_len):
@@ -546,6 +548,8 @@ KERNELS = {
     "step_q8": "kv_quantize_kernel + decode_step_kernel over the 8-bit cache",
     "step_indexer": "indexer_select_kernel as the indexer decode step (compress and indexer key of the closed "
                     "block, indexer selection and attention in one kernel)",
+    "step_large": "select_large_score_kernel (scores, with the closed block's compression) + pick_attend_kernel "
+                  "(per-row pick and attention): the decode step for k > 64",
     "attend_prefill": "vt_pack_kernel + prefill_attn_kernel",
 }
 
@@ -564,7 +568,8 @@ def record(w, st, timing, steps, seed, graph_steps):
         kernel = KERNELS["attend_prefill"]
     else:
         achieved, peak, unit, bound = model[dominant]["bytes"] / dur / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
-        step_kernel = KERNELS["step_q8"] if w.kv_q8 else KERNELS["step_indexer"] if w.indexer_dim else KERNELS["step"]
+        step_kernel = (KERNELS["step_q8"] if w.kv_q8 else KERNELS["step_indexer"] if w.indexer_dim
+                       else KERNELS["step"] if st.fused else KERNELS["step_large"])
         kernel = step_kernel if dominant == "step" else f"{dominant} call"
     calls = {}
     for n, t in per_call.items():
