@@ -204,6 +204,39 @@ def test_bitwise_determinism():
     np.testing.assert_array_equal(x[1], y[1])
 
 
+STEP_DETERMINISM = [
+    W(mode="decode", batch=1, kv_len=300000, top_k=16),                                   # 64 scan parts per row
+    W(mode="decode", batch=64, kv_len=20000, top_k=16),                                   # 2 scan parts per row
+    W(mode="decode", batch=1, kv_len=9000, top_k=16),                                     # slices per row
+    W(mode="decode", batch=1, kv_len=4 * 20000 + 2, top_k=513, block_size=4, keep_tail=True),  # score + pick-attend
+]
+
+
+@pytest.mark.parametrize("w", STEP_DETERMINISM, ids=case_id)
+def test_step_bitwise_determinism(w):
+    """The decode step twice on the same inputs: selections, scores, outputs and compressed keys bit for bit
+    (the cross-workgroup list exchange and the slice merges fold in a fixed order)."""
+    case = Case(w, seed=8)
+    b, hq, hkv, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    shape = qsa.shape_for(case.q, case.k, w.block_size, w.top_k, keep_tail=w.keep_tail)
+    q = case.q.view(b, hq, d)
+    ws = qsa.workspace(shape, qsa.QSA_OP_DECODE_STEP, 1, w.kv_len, "cuda")
+    runs = []
+    for _ in range(2):
+        k_comp = torch.zeros(b, hkv, case.kv_cap // w.block_size, d, device="cuda")
+        qsa.qsa_compress_keys(shape, case.k, w.kv_len - 1, k_comp)
+        sel = torch.empty(b, hkv, w.top_k, dtype=torch.int32, device="cuda")
+        sc = torch.empty(b, hkv, w.top_k, dtype=torch.float32, device="cuda")
+        out = torch.empty_like(q)
+        qsa.qsa_decode_step(shape, q, case.k, case.v, k_comp, w.kv_len, sel, out, sel_scores=sc, ws=ws)
+        torch.cuda.synchronize()
+        runs.append((sel.clone(), sc.clone(), out.clone(), k_comp.clone()))
+    for x, y, name in zip(runs[0], runs[1], ("selections", "scores", "outputs", "compressed keys")):
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y), f"{name} differ between runs"
+    log(f"  step determinism {case_id(w)}: fused {qsa.qsa_decode_step_fused(shape, w.kv_len)}")
+
+
 @pytest.mark.parametrize("bs,d", [(64, 128), (4, 128), (4, 64), (8, 64), (16, 128)])
 def test_incremental_compress_matches_full(bs, d):
     """Compressing block by block (a decode loop) gives the same compressed keys as one call."""
