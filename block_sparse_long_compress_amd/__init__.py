@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     QSA_OP_DECODE_STEP,
     QSA_OP_DECODE_STEP_RAGGED,
     QSA_OP_INDEXER_SELECT,
+    QSA_OP_PREFILL_Q8,
     QSA_OP_PREFILL,
     QSA_OP_SELECT,
     QsaError,

@@ -21,6 +21,7 @@ QSA_F32, QSA_BF16 = 0, 1
 QSA_OP_COMPRESS, QSA_OP_SELECT, QSA_OP_DECODE, QSA_OP_PREFILL, QSA_OP_DECODE_STEP = 0, 1, 2, 3, 4
 QSA_OP_DECODE_STEP_RAGGED = 5
 QSA_OP_INDEXER_SELECT = 6
+QSA_OP_PREFILL_Q8 = 7
 QSA_AGG_SUM, QSA_AGG_MAX, QSA_AGG_SOFTMAX = 0, 1, 2
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_ERR_WORKSPACE", 4: "QSA_ERR_HIP"}
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
@@ -94,7 +95,7 @@ def _load() -> ctypes.CDLL:
     lib.qsa_sparse_attn_decode_q8.restype = ctypes.c_int
     lib.qsa_sparse_attn_decode_q8.argtypes = [SH, P, P, P, P, P, I64, I64, P, P, P, SZ, P]
     lib.qsa_sparse_attn_prefill_q8.restype = ctypes.c_int
-    lib.qsa_sparse_attn_prefill_q8.argtypes = [SH, P, P, P, P, P, I64, I64, I64, P, P, P]
+    lib.qsa_sparse_attn_prefill_q8.argtypes = [SH, P, P, P, P, P, I64, I64, I64, P, P, P, SZ, P]
     lib.qsa_decode_step_q8.restype = ctypes.c_int
     lib.qsa_decode_step_q8.argtypes = [SH, P, P, P, P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
     lib.qsa_decode_step_noalloc.restype = ctypes.c_int
@@ -311,13 +312,17 @@ def qsa_sparse_attn_decode_q8(shape: QsaShape, q, k_q, v_q, k_scales, v_scales, 
     return out
 
 
-def qsa_sparse_attn_prefill_q8(shape: QsaShape, q, k_q, v_q, k_scales, v_scales, q_pos0: int, sel, out,
+def qsa_sparse_attn_prefill_q8(shape: QsaShape, q, k_q, v_q, k_scales, v_scales, q_pos0: int, sel, out, ws=None,
                                stream=None):
     """Prefill attention over the rotated 8-bit cache for ``q`` ``[b][q_len][Hq][d]`` at positions ``q_pos0 ..``
-    (``sel`` ``[b][q_len][Hkv][k]``); no workspace."""
+    (``sel`` ``[b][q_len][Hkv][k]``). With its workspace (allocated here when ``ws`` is None) the call takes the
+    tiled bf16 kernel over the codes rotated back where that serves the shape; ``ws`` of zero elements forces one
+    query row per workgroup over the codes."""
+    q_len = q.shape[1]
+    ws, nbytes = _workspace(shape, QSA_OP_PREFILL_Q8, q_len, q_pos0 + q_len, ws, q.device)
     _check(LIB.qsa_sparse_attn_prefill_q8(ctypes.byref(shape), _ptr(q), _ptr(k_q), _ptr(v_q), _ptr(k_scales),
-                                          _ptr(v_scales), q.shape[1], q_pos0, k_q.shape[2], _ptr(sel), _ptr(out),
-                                          _stream(q, stream)), "qsa_sparse_attn_prefill_q8")
+                                          _ptr(v_scales), q_len, q_pos0, k_q.shape[2], _ptr(sel), _ptr(out),
+                                          _ptr(ws), nbytes, _stream(q, stream)), "qsa_sparse_attn_prefill_q8")
     return out
 
 

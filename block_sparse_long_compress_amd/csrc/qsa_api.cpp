@@ -78,6 +78,34 @@ StepWs ragged_large_ws(const Dims& s, int64_t max_kv_len, int64_t* n_chunks) {
   return w;
 }
 
+// Prefill over the 8-bit cache by the tiled bf16 kernel: the cache's
+// positions [0, q_pos0 + q_len) dequantized and rotated back into bf16 rows
+// (K at k_off, V at v_off, each [b][Hkv][n_pad][d], n_pad a whole number of
+// blocks), then the tiled kernel's own workspace at att_off. Taken where the
+// tiled kernel serves the shape and the rows' selected keys (q_len * top_k *
+// Bs) at least match the positions to convert; otherwise tiled is false and
+// the call runs one query row per workgroup over the codes.
+struct Q8PrefillWs {
+  bool tiled;
+  int64_t n_pad;
+  size_t k_off, v_off, att_off, total;
+};
+Q8PrefillWs q8_prefill_ws(const Dims& s, int64_t q_len, int64_t q_pos0) {
+  Q8PrefillWs w{};
+  if (s.dtype != QSA_BF16) return w;
+  const qsa::PrefillPlan plan = qsa::plan_prefill(s, q_len, q_pos0);
+  const int64_t n_pos = q_pos0 + q_len;
+  if (plan.rows || q_len * s.top_k * s.bs < n_pos) return w;
+  w.tiled = true;
+  w.n_pad = (n_pos + s.bs - 1) / s.bs * s.bs;
+  const size_t cache = qsa::align_up((size_t)s.batch * s.hkv * w.n_pad * s.d * sizeof(uint16_t), 256);
+  w.k_off = 0;
+  w.v_off = cache;
+  w.att_off = 2 * cache;
+  w.total = w.att_off + plan.ws_bytes;
+  return w;
+}
+
 // Shape checks shared by every entry point.
 qsa_status check_shape(const qsa_shape* sh, Dims* out) {
   if (!sh) return QSA_ERR_INVALID;
@@ -172,6 +200,9 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
       return a > b8 ? a : b8;
     }
     }
+    case QSA_OP_PREFILL_Q8:
+      if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
+      return q8_prefill_ws(s, q_len, kv_len - q_len).total;
     case QSA_OP_INDEXER_SELECT:
       if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
       if (s.top_k <= 64) return 0;
@@ -528,7 +559,8 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
 
 qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, const int8_t* k_q, const int8_t* v_q,
                                       const uint16_t* k_scales, const uint16_t* v_scales, int64_t q_len,
-                                      int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* stream) {
+                                      int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* ws,
+                                      size_t ws_bytes, void* stream) {
   Dims s;
   qsa_status st = check_shape(shape, &s);
   if (st != QSA_OK) return st;
@@ -539,9 +571,21 @@ qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, con
   if (q_len <= 0 || q_pos0 < 0 || kv_cap <= 0 || q_pos0 + q_len > kv_cap) return QSA_ERR_INVALID;
   if (s.dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const Q8PrefillWs lay = q8_prefill_ws(s, q_len, q_pos0);
+  if (lay.tiled && ws && ws_bytes >= lay.total && aligned16(ws)) {
+    // the codes rotated back into bf16 rows, then the tiled bf16 kernel
+    char* base = static_cast<char*>(ws);
+    uint16_t* kb = reinterpret_cast<uint16_t*>(base + lay.k_off);
+    uint16_t* vb = reinterpret_cast<uint16_t*>(base + lay.v_off);
+    st = hip_status(qsa::launch_dequant_unrotate(s, k_q, v_q, k_scales, v_scales, kv_cap, q_pos0 + q_len, lay.n_pad,
+                                                 kb, vb, hs));
+    if (st != QSA_OK) return st;
+    return hip_status(qsa::launch_prefill(s, qsa::plan_prefill(s, q_len, q_pos0), q, kb, vb, q_len, q_pos0,
+                                          lay.n_pad, sel, out, base + lay.att_off, hs));
+  }
   if ((int64_t)s.batch * q_len * s.hkv > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;  // one workgroup per row
-  return hip_status(qsa::launch_prefill_q8(s, q, k_q, v_q, k_scales, v_scales, q_len, q_pos0, kv_cap, sel, out,
-                                           static_cast<hipStream_t>(stream)));
+  return hip_status(qsa::launch_prefill_q8(s, q, k_q, v_q, k_scales, v_scales, q_len, q_pos0, kv_cap, sel, out, hs));
 }
 
 qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,

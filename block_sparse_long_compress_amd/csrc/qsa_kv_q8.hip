@@ -278,6 +278,46 @@ __global__ __launch_bounds__(8 * kWave) void prefill_rows_q8_kernel(
   finish_row_slice<D, NW, true>(m_run, l_run, o, smem, &last_wg, out, nullptr, nullptr, row, bt, g, hq, G, 0, 1);
 }
 
+// The 8-bit cache rotated back into bf16 rows, for prefill over the cache
+// with the tiled bf16 kernel: position pos of every (sequence, KV head) of K
+// and of V is dequantized (code x scale, exact in float32), transformed by H
+// and divided by D (H H = D I, so this undoes the cache's rotation; the
+// scores and the output of attention over these rows are those over the
+// rotated rows with the query rotated and the output rotated back), and
+// rounded to bf16. Rows [n_pos, n_pad) are written as zeros. One wave per
+// row; lane l holds elements l (and l + 64).
+template <int D>
+__global__ __launch_bounds__(256) void dequant_unrotate_kernel(
+    const int8_t* __restrict__ kq, const int8_t* __restrict__ vq, const uint16_t* __restrict__ ks,
+    const uint16_t* __restrict__ vs, uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, int64_t kv_cap,
+    int64_t n_pos, int64_t n_pad, int64_t n_rows) {
+  constexpr int EPL = D / kWave;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave_id();  // tensor (K, then V), (sequence, KV head), position
+  if (item >= 2 * n_rows * n_pad) return;
+  const int tensor = (int)(item / (n_rows * n_pad));
+  const int64_t rem = item % (n_rows * n_pad);
+  const int64_t bg = rem / n_pad, pos = rem % n_pad;
+  const int lane = lane_id();
+  uint16_t* dst = (tensor ? v_out : k_out) + (bg * n_pad + pos) * D;
+  if (pos >= n_pos) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) dst[lane + kWave * i] = 0;
+    return;
+  }
+  const int8_t* codes = (tensor ? vq : kq) + (bg * kv_cap + pos) * D;
+  const uint16_t* sc = (tensor ? vs : ks) + (bg * kv_cap + pos) * (D / 32);
+  float x[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    x[i] = (float)codes[e] * f16_bits_to_f32(sc[e / 32]);
+  }
+  fwht_wave<D>(x);
+  constexpr float inv_d = 1.0f / D;  // exact: D is a power of two
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) dst[lane + kWave * i] = f32_to_bf16(x[i] * inv_d);
+}
+
 template <int D>
 hipError_t launch_prefill_q8_d(const Dims& s, const void* q, const int8_t* kq, const int8_t* vq, const uint16_t* ks,
                                const uint16_t* vs, int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel,
@@ -334,6 +374,20 @@ hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q
                             const int32_t* sel, void* out, void* ws, hipStream_t st) {
   return s.d == 64 ? launch_q8_d<64>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, ws, st)
                    : launch_q8_d<128>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, ws, st);
+}
+
+hipError_t launch_dequant_unrotate(const Dims& s, const int8_t* kq, const int8_t* vq, const uint16_t* ks,
+                                  const uint16_t* vs, int64_t kv_cap, int64_t n_pos, int64_t n_pad, uint16_t* k_out,
+                                  uint16_t* v_out, hipStream_t st) {
+  const int64_t n_rows = (int64_t)s.batch * s.hkv;
+  const unsigned grid = (unsigned)((2 * n_rows * n_pad + 3) / 4);
+  if (s.d == 64)
+    hipLaunchKernelGGL((dequant_unrotate_kernel<64>), dim3(grid), dim3(256), 0, st, kq, vq, ks, vs, k_out, v_out,
+                       kv_cap, n_pos, n_pad, n_rows);
+  else
+    hipLaunchKernelGGL((dequant_unrotate_kernel<128>), dim3(grid), dim3(256), 0, st, kq, vq, ks, vs, k_out, v_out,
+                       kv_cap, n_pos, n_pad, n_rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_q8(const Dims& s, const void* q, const int8_t* kq, const int8_t* vq, const uint16_t* ks,

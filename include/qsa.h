@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 9
+#define QSA_ABI_VERSION 10
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -94,7 +94,8 @@ enum {
   QSA_OP_PREFILL = 3,
   QSA_OP_DECODE_STEP = 4,
   QSA_OP_DECODE_STEP_RAGGED = 5,
-  QSA_OP_INDEXER_SELECT = 6
+  QSA_OP_INDEXER_SELECT = 6,
+  QSA_OP_PREFILL_Q8 = 7
 };
 
 typedef enum {
@@ -127,7 +128,8 @@ const char* qsa_status_str(qsa_status status);
  * (size_t)-1 if the arguments are invalid or the op does not serve the
  * shape: selection (default or indexer), and decode steps that select
  * separately, with k > 64 over more than 65536 candidates per row). op is one of QSA_OP_*.
- * QSA_OP_SELECT, QSA_OP_PREFILL and QSA_OP_INDEXER_SELECT take q_len and
+ * QSA_OP_SELECT, QSA_OP_PREFILL, QSA_OP_INDEXER_SELECT and QSA_OP_PREFILL_Q8
+ * (0: the call runs one row per workgroup) take q_len and
  * kv_len = q_pos0 + q_len;
  * QSA_OP_DECODE takes kv_len (q_len ignored).
  * QSA_OP_DECODE_STEP_RAGGED takes the longest sequence's length as kv_len
@@ -376,12 +378,24 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
  * qsa_sparse_attn_prefill), k_q, v_q, k_scales, v_scales holding positions
  * 0 .. q_pos0+q_len-1. Each row's query heads are rotated, its scores are
  * (H q).(H k)/head_dim over the codes, causal at the row's own position, and
- * its output is rotated back; one workgroup per (sequence, row, KV head), any
- * top_k and block size; no workspace. bf16 only, else QSA_ERR_UNSUPPORTED
- * (also when batch * q_len * Hkv exceeds 2^31 - 1). */
+ * its output is rotated back. Two ways, the same results up to rounding:
+ *   tiled   where the tiled bf16 prefill serves the shape (Bs >= 32,
+ *           top_k <= 64) and the rows' selected keys (q_len * top_k * Bs)
+ *           are at least the cache's q_pos0 + q_len positions, and ws holds
+ *           qsa_workspace_bytes(shape, QSA_OP_PREFILL_Q8, q_len,
+ *           q_pos0 + q_len) bytes (16-byte aligned, no zero-fill needed):
+ *           those positions are dequantized and rotated back into bf16 rows
+ *           in ws (H H = head_dim I, so attention over them with the plain
+ *           query equals attention over the rotated codes with the rotated
+ *           query, rotated back), then the tiled kernel runs on them;
+ *   rows    otherwise (ws may be null): one workgroup per (sequence, row, KV
+ *           head) over the codes, any top_k and block size.
+ * bf16 only, else QSA_ERR_UNSUPPORTED (also when the rows way is taken and
+ * batch * q_len * Hkv exceeds 2^31 - 1). */
 qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, const int8_t* k_q, const int8_t* v_q,
                                       const uint16_t* k_scales, const uint16_t* v_scales, int64_t q_len,
-                                      int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* stream);
+                                      int64_t q_pos0, int64_t kv_cap, const int32_t* sel, void* out, void* ws,
+                                      size_t ws_bytes, void* stream);
 
 /* One decode step over the 8-bit cache: qsa_kv_quantize of the new position
  * kv_len - 1, then, in one kernel, what qsa_decode_step does (compress the

@@ -66,9 +66,10 @@ int main() {
               if (kt && k < 2) continue;
               qsa_shape s = shape(b, 16, 2, d, bs, k, dt, kt);
               for (int64_t n : lens) {
-                for (int op = 0; op <= QSA_OP_INDEXER_SELECT; ++op) {
+                for (int op = 0; op <= QSA_OP_PREFILL_Q8; ++op) {
                   // prefill and selection over the last 4096 query rows of n positions
-                  const bool rows = op == QSA_OP_PREFILL || op == QSA_OP_SELECT || op == QSA_OP_INDEXER_SELECT;
+                  const bool rows = op == QSA_OP_PREFILL || op == QSA_OP_SELECT || op == QSA_OP_INDEXER_SELECT ||
+                                    op == QSA_OP_PREFILL_Q8;
                   const int64_t q_len = rows ? (n < 4096 ? n : 4096) : 1;
                   const size_t w = qsa_workspace_bytes(&s, op, q_len, n);
                   if (w != BAD && w > (size_t(1) << 40)) {  // at most 1 TiB for these sizes
@@ -143,12 +144,12 @@ int main() {
   const int8_t* PC = static_cast<const int8_t*>(P);
   const uint16_t* PS = static_cast<const uint16_t*>(P);
   expect(qsa_sparse_attn_prefill_q8(&good, P, PC, PC, static_cast<const uint16_t*>(MIS), PS, 64, 0, 4096, PI, P,
-                                    nullptr),
+                                    nullptr, 0, nullptr),
          QSA_ERR_INVALID, "8-bit prefill scales misaligned");
-  expect(qsa_sparse_attn_prefill_q8(&good, P, PC, PC, PS, PS, 64, 4040, 4096, PI, P, nullptr), QSA_ERR_INVALID,
+  expect(qsa_sparse_attn_prefill_q8(&good, P, PC, PC, PS, PS, 64, 4040, 4096, PI, P, nullptr, 0, nullptr), QSA_ERR_INVALID,
          "8-bit prefill beyond capacity");
   qsa_shape f32_16 = shape(2, 16, 2, 128, 16, 16, QSA_F32);
-  expect(qsa_sparse_attn_prefill_q8(&f32_16, P, PC, PC, PS, PS, 64, 0, 4096, PI, P, nullptr), QSA_ERR_UNSUPPORTED,
+  expect(qsa_sparse_attn_prefill_q8(&f32_16, P, PC, PC, PS, PS, 64, 0, 4096, PI, P, nullptr, 0, nullptr), QSA_ERR_UNSUPPORTED,
          "8-bit prefill with a float32 shape");
   qsa_shape f32 = shape(2, 16, 2, 128, 64, 16, QSA_F32);
   expect(qsa_kv_quantize(&f32, P, P, 64, 64, 0, static_cast<int8_t*>(P), static_cast<int8_t*>(P),

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 9
+    assert qsa.abi_version() == 10
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -74,7 +74,7 @@ def test_workspace_sizes(qsa):
     assert qsa.qsa_workspace_bytes(f32, qsa.QSA_OP_PREFILL, 512, 512) == 0
     assert qsa.qsa_workspace_bytes(f32, qsa.QSA_OP_DECODE, 1, 512) == 0
     with pytest.raises(qsa.QsaError):
-        qsa.qsa_workspace_bytes(sh, 7, 1, 1)
+        qsa.qsa_workspace_bytes(sh, 8, 1, 1)  # no such op
     with pytest.raises(qsa.QsaError):
         qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 10, 5)
 
@@ -287,15 +287,21 @@ def test_prefill_q8_arguments(qsa):
     P, N, MIS = ctypes.c_void_p(4096), None, ctypes.c_void_p(4100)
     INV, UNS = 1, 2
     call = lib.qsa_sparse_attn_prefill_q8
-    #            shape q  kq vq ks vs q_len q_pos0 kv_cap sel out stream
-    assert call(shr, P, N, P, P, P, 64, 0, 4096, P, P, N) == INV       # no key codes
-    assert call(shr, P, P, P, MIS, P, 64, 0, 4096, P, P, N) == INV     # key scales misaligned
-    assert call(shr, P, P, P, P, P, 64, 4040, 4096, P, P, N) == INV    # rows beyond capacity
-    assert call(shr, P, P, P, P, P, 0, 0, 4096, P, P, N) == INV        # no rows
-    assert call(shr, P, P, P, P, P, 64, -1, 4096, P, P, N) == INV
+    #            shape q  kq vq ks vs q_len q_pos0 kv_cap sel out ws ws_bytes stream
+    assert call(shr, P, N, P, P, P, 64, 0, 4096, P, P, N, 0, N) == INV       # no key codes
+    assert call(shr, P, P, P, MIS, P, 64, 0, 4096, P, P, N, 0, N) == INV     # key scales misaligned
+    assert call(shr, P, P, P, P, P, 64, 4040, 4096, P, P, N, 0, N) == INV    # rows beyond capacity
+    assert call(shr, P, P, P, P, P, 0, 0, 4096, P, P, N, 0, N) == INV        # no rows
+    assert call(shr, P, P, P, P, P, 64, -1, 4096, P, P, N, 0, N) == INV
     bad = ctypes.byref(good_shape(qsa, batch=2, dtype=qsa.QSA_F32))
-    assert call(bad, P, P, P, P, P, 64, 0, 4096, P, P, N) == UNS
-    assert call(ctypes.byref(good_shape(qsa, batch=2, head_dim=96)), P, P, P, P, P, 64, 0, 4096, P, P, N) == UNS
+    assert call(bad, P, P, P, P, P, 64, 0, 4096, P, P, N, 0, N) == UNS
+    assert call(ctypes.byref(good_shape(qsa, batch=2, head_dim=96)), P, P, P, P, P, 64, 0, 4096, P, P, N, 0, N) == UNS
+    # the tiled way's workspace: the 8K prompt from 0 takes it (the rows' selected keys far beyond the
+    # positions); a few rows at the end of a long context, blocks shorter than 32 keys and k > 64 do not
+    need = qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_PREFILL_Q8, 8192, 8192)
+    assert need >= 3 * 2 * 2 * 8192 * 128 * 2
+    for kw, q_len, n in ((dict(), 4, 1 << 20), (dict(block_size=16), 8192, 8192), (dict(top_k=65), 8192, 8192)):
+        assert qsa.qsa_workspace_bytes(good_shape(qsa, batch=2, **kw), qsa.QSA_OP_PREFILL_Q8, q_len, n) == 0
 
 
 def test_decode_step_noalloc_arguments(qsa):

@@ -245,3 +245,52 @@ def test_q8_decode_step_parity(w):
         assert err <= BF16_ABS_TOL, f"row {(bb, g)}: error {err:.3e}"
         worst = max(worst, err)
     log(f"  max error against the 8-bit oracle {worst:.2e}")
+
+
+@pytest.mark.parametrize("c", [(W(mode="prefill", batch=2, kv_len=1500, top_k=8), 0),
+                               (W(mode="prefill", batch=1, kv_len=64 * 40 + 7, top_k=16, keep_tail=True), 64 * 20),
+                               (W(mode="prefill", batch=1, kv_len=800, top_k=6, head_dim=64, block_size=32), 0)],
+                         ids=lambda c: f"{case_id(c[0])}-from{c[1]}")
+def test_q8_prefill_tiled_and_rows(c):
+    """Prefill over the 8-bit cache both ways: the tiled way (the codes rotated back into bf16 rows in the
+    workspace, then the tiled bf16 kernel) and one row per workgroup over the codes (a workspace of zero bytes),
+    each against the 8-bit oracle with the acceptance and companion bounds on sampled rows."""
+    w, q_pos0 = c
+    log(f"q8 prefill both ways {case_id(w)} from {q_pos0}")
+    case = Case(w, seed=35)
+    b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
+    G = hq // hkv
+    shape, kq, vq, ks, vs = quantized(case)
+    n = w.kv_len - q_pos0
+    assert qsa.qsa_workspace_bytes(shape, qsa.QSA_OP_PREFILL_Q8, n, w.kv_len) > 0, "the tiled way serves this shape"
+    k_comp = torch.empty(b, hkv, max(1, w.kv_len // bs), d, device="cuda")
+    qsa.qsa_compress_keys(shape, case.k, w.kv_len, k_comp)
+    q_rows = case.q[:, q_pos0:].contiguous()
+    sel = torch.empty(b, n, hkv, k, dtype=torch.int32, device="cuda")
+    qsa.qsa_score_select(shape, q_rows, q_pos0, k_comp, w.kv_len, w.kv_len, sel)
+    out_t, out_r = torch.empty_like(q_rows), torch.empty_like(q_rows)
+    qsa.qsa_sparse_attn_prefill_q8(shape, q_rows, kq, vq, ks, vs, q_pos0, sel, out_t)
+    qsa.qsa_sparse_attn_prefill_q8(shape, q_rows, kq, vq, ks, vs, q_pos0, sel, out_r,
+                                   ws=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    sel_h = sel.cpu().numpy()
+    rng = np.random.default_rng(3)
+    ts = sorted(set(rng.integers(0, n, 8).tolist()) | {0, n - 1})
+    worst = {"tiled": 0.0, "rows": 0.0}
+    for name, out in (("tiled", out_t), ("rows", out_r)):
+        out_h = from_device(out)
+        for bb in range(b):
+            for g in range(hkv):
+                kq_o, ks_o = Q.quantize_cache(case.K[bb, g, :w.kv_len])
+                vq_o, vs_o = Q.quantize_cache(case.V[bb, g, :w.kv_len])
+                for t in ts:
+                    p = q_pos0 + t
+                    qg = case.Q[bb, p, g * G:(g + 1) * G].astype(np.float64)
+                    ref = Q.attend_q8(qg, kq_o, ks_o, vq_o, vs_o, [int(x) for x in sel_h[bb, t, g]], p, bs,
+                                      O.default_scale(d))
+                    worst[name] = max(worst[name], check_output_row(out_h[bb, t, g * G:(g + 1) * G], ref, "bf16",
+                                                                    where=f"{name} row {(bb, p, g)}:"))
+    diff = (out_t.float() - out_r.float()).abs().max().item()
+    assert diff <= BF16_ABS_TOL, f"the two ways differ by {diff}"
+    log(f"  largest error over its row bound: tiled {worst['tiled']:.3f}, rows {worst['rows']:.3f}; "
+        f"the two ways differ by at most {diff:.2e}")
