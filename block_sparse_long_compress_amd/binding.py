@@ -329,7 +329,8 @@ def qsa_sparse_attn_prefill_q8(shape: QsaShape, q, k_q, v_q, k_scales, v_scales,
 def qsa_decode_step_q8(shape: QsaShape, q, k, v, k_comp, k_q, v_q, k_scales, v_scales, kv_len: int, sel, out,
                        sel_scores=None, ws=None, stream=None):
     """One decode step over the 8-bit cache: quantize position ``kv_len - 1`` of ``k``/``v`` into it, then compress,
-    select and attend over the codes in one kernel (``qsa_decode_step``'s fused shapes only)."""
+    select and attend over the codes (one kernel on ``qsa_decode_step``'s fused shapes, else the selection call and
+    the 8-bit attention)."""
     ws, nbytes = _workspace(shape, QSA_OP_DECODE_STEP, 1, kv_len, ws, q.device)
     _check(LIB.qsa_decode_step_q8(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_comp), _ptr(k_q), _ptr(v_q),
                                   _ptr(k_scales), _ptr(v_scales), kv_len, k.shape[2], _ptr(sel), _ptr(sel_scores),

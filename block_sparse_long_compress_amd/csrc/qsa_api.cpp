@@ -47,8 +47,10 @@ StepWs step_ws(const Dims& s, int64_t kv_len, bool q8 = false) {
     } else {
       sel_scratch = sel_ws > cnt ? sel_ws - cnt : 0;
     }
-    if (s.dtype == QSA_BF16)
-      att = sel_plan.large ? qsa::plan_pick_attend(s, sel_plan.n_chunks).ws_bytes : qsa::plan_decode(s, kv_len).ws_bytes;
+    if (s.dtype == QSA_BF16)  // q8: the full selection, then the 8-bit cache's decode attention
+      att = q8                ? qsa::plan_decode(s, kv_len, false).ws_bytes
+            : sel_plan.large  ? qsa::plan_pick_attend(s, sel_plan.n_chunks).ws_bytes
+                              : qsa::plan_decode(s, kv_len).ws_bytes;
   }
   w.part_off = 2 * cnt + qsa::align_up(sel_scratch, 256);
   w.total = (att == 0 && sel_ws == 0) ? 0 : w.part_off + (att > cnt ? att - cnt : 0);
@@ -553,7 +555,9 @@ qsa_status qsa_sparse_attn_decode_q8(const qsa_shape* shape, const void* q, cons
   const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len, false);  // 4-wave slices at every row count
   if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
-  return hip_status(qsa::launch_decode_q8(s, plan, q, k_q, v_q, k_scales, v_scales, kv_len, kv_cap, sel, out, ws,
+  char* base = static_cast<char*>(ws);
+  return hip_status(qsa::launch_decode_q8(s, plan, q, k_q, v_q, k_scales, v_scales, kv_len, kv_cap, sel, out, base,
+                                          base ? base + qsa::counter_bytes((int64_t)s.batch * s.hkv) : nullptr,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -602,19 +606,44 @@ qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void*
   if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
   if (kv_len <= 0 || kv_cap <= 0 || kv_len > kv_cap) return QSA_ERR_INVALID;
   if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  if (s.dtype != QSA_BF16) return QSA_ERR_UNSUPPORTED;  // the 8-bit cache holds bf16 rows
+  const int64_t rows = (int64_t)s.batch * s.hkv;
   const qsa::StepPlan sp = qsa::plan_decode_step(s, kv_len, false, true);
-  if (!sp.fused) return QSA_ERR_UNSUPPORTED;  // the separate calls serve the other shapes
-  if ((int64_t)(s.batch * (int64_t)s.hkv + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  qsa::SelectPlan sel_plan{};
+  qsa::DecodePlan att_plan{};
+  if (sp.fused) {
+    if ((rows + 7) * sp.n_split * 8 > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  } else {
+    if (s.top_k > 64 && qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
+    sel_plan = qsa::plan_select(s, 1, kv_len - 1);
+    att_plan = qsa::plan_decode(s, kv_len, false);
+    if (rows * (sel_plan.n_chunks > 0 ? sel_plan.n_chunks : 1) > 0x7FFFFFFF || rows * att_plan.n_split > 0x7FFFFFFF)
+      return QSA_ERR_UNSUPPORTED;
+  }
   const StepWs lay = step_ws(s, kv_len, true);
   if (lay.total > 0 && (!ws || ws_bytes < lay.total || !aligned16(ws))) return QSA_ERR_WORKSPACE;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // the new position into the 8-bit cache, then the fused step over it
+  // the new position into the 8-bit cache first
   st = hip_status(qsa::launch_kv_quantize(s, k, v, kv_cap, kv_len - 1, kv_len, k_q, v_q, k_scales, v_scales, hs));
   if (st != QSA_OK) return st;
   char* base = static_cast<char*>(ws);
-  const qsa::Q8Cache cache{k_q, v_q, k_scales, v_scales};
-  return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, base,
-                                            base ? base + lay.part_off : nullptr, hs, nullptr, &cache));
+  char* part = base ? base + lay.part_off : nullptr;
+  if (sp.fused) {
+    const qsa::Q8Cache cache{k_q, v_q, k_scales, v_scales};
+    return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, base,
+                                              part, hs, nullptr, &cache));
+  }
+  // the other shapes (top_k > 64, blocks shorter than 32 keys): the
+  // selection, which compresses the block the new token closes from the bf16
+  // keys before scoring it and picks every row's blocks, then the 8-bit
+  // cache's decode attention; the selection's counters (if any) sit in the
+  // second counter area, the attention's in the first
+  const int64_t close_block = kv_len % s.bs == 0 ? kv_len / s.bs - 1 : -1;
+  st = hip_status(qsa::launch_select(s, sel_plan, q, 1, kv_len - 1, k_comp, kv_cap, sel, sel_scores,
+                                     base ? base + lay.sel_off : nullptr, hs, k, close_block));
+  if (st != QSA_OK) return st;
+  return hip_status(qsa::launch_decode_q8(s, att_plan, q, k_q, v_q, k_scales, v_scales, kv_len, kv_cap, sel, out, base,
+                                          part, hs));
 }
 
 }  // extern "C"

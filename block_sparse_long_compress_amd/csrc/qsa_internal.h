@@ -111,7 +111,7 @@ hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, c
                          int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* counters, void* part,
                          hipStream_t st);
 // Prefill attention over the rotated 8-bit cache, one workgroup per query
-// row (any top_k; Bs >= 32); no workspace.
+// row (any top_k and block size); no workspace.
 // The 8-bit cache's positions [0, n_pos) of every (sequence, KV head),
 // dequantized and rotated back into bf16 rows k_out, v_out ([b][Hkv][n_pad][d],
 // rows [n_pos, n_pad) zero), for the tiled prefill kernel.
@@ -121,11 +121,11 @@ hipError_t launch_dequant_unrotate(const Dims& s, const int8_t* kq, const int8_t
 hipError_t launch_prefill_q8(const Dims& s, const void* q, const int8_t* kq, const int8_t* vq, const uint16_t* ks,
                              const uint16_t* vs, int64_t q_len, int64_t q_pos0, int64_t kv_cap, const int32_t* sel,
                              void* out, hipStream_t st);
-// Decode attention over the rotated 8-bit cache (same plan and workspace as
-// launch_decode; Bs >= 32).
+// Decode attention over the rotated 8-bit cache (the narrow plan; counters
+// and slice states as for launch_decode).
 hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q, const int8_t* kq, const int8_t* vq,
                             const uint16_t* ks, const uint16_t* vs, int64_t kv_len, int64_t kv_cap,
-                            const int32_t* sel, void* out, void* ws, hipStream_t st);
+                            const int32_t* sel, void* out, void* counters, void* part, hipStream_t st);
 
 // Prefill attention -------------------------------------------------------------
 struct PrefillPlan {

@@ -344,12 +344,12 @@ hipError_t launch_quant_d(const void* k, const void* v, int8_t* kq, int8_t* vq, 
 template <int D>
 hipError_t launch_q8_d(const Dims& s, const DecodePlan& plan, const void* q, const int8_t* kq, const int8_t* vq,
                        const uint16_t* ks, const uint16_t* vs, int64_t kv_len, int64_t kv_cap, const int32_t* sel,
-                       void* out, void* ws, hipStream_t st) {
+                       void* out, void* counters_ws, void* part_ws, hipStream_t st) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   // (H q).(H k) = d q.k: the 1/d of the rotation is folded into the scale
   const float scale_log2 = s.scale * 1.4426950408889634f / (float)D;
-  uint32_t* counters = static_cast<uint32_t*>(ws);
-  float* part = plan.n_split > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(rows)) : nullptr;
+  uint32_t* counters = static_cast<uint32_t*>(counters_ws);
+  float* part = plan.n_split > 1 ? static_cast<float*>(part_ws) : nullptr;
   auto kern = plan.waves == 8 ? decode_attn_q8_kernel<D, 8> : decode_attn_q8_kernel<D, 4>;
   hipLaunchKernelGGL(kern, dim3((unsigned)(rows * plan.n_split)), dim3(plan.waves * kWave), 0, st,
                      static_cast<const uint16_t*>(q), kq, vq, ks, vs, sel, static_cast<uint16_t*>(out), part,
@@ -371,9 +371,9 @@ hipError_t launch_kv_quantize(const Dims& s, const void* k, const void* v, int64
 
 hipError_t launch_decode_q8(const Dims& s, const DecodePlan& plan, const void* q, const int8_t* kq, const int8_t* vq,
                             const uint16_t* ks, const uint16_t* vs, int64_t kv_len, int64_t kv_cap,
-                            const int32_t* sel, void* out, void* ws, hipStream_t st) {
-  return s.d == 64 ? launch_q8_d<64>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, ws, st)
-                   : launch_q8_d<128>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, ws, st);
+                            const int32_t* sel, void* out, void* counters, void* part, hipStream_t st) {
+  return s.d == 64 ? launch_q8_d<64>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, counters, part, st)
+                   : launch_q8_d<128>(s, plan, q, kq, vq, ks, vs, kv_len, kv_cap, sel, out, counters, part, st);
 }
 
 hipError_t launch_dequant_unrotate(const Dims& s, const int8_t* kq, const int8_t* vq, const uint16_t* ks,

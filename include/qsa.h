@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 10
+#define QSA_ABI_VERSION 11
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -405,11 +405,17 @@ qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, con
  * read only at kv_len - 1 and, for the compression, in the closed block);
  * k_q, v_q, k_scales, v_scales as for qsa_kv_quantize, holding positions
  * 0 .. kv_len - 2 already. sel, sel_scores (optional), out as for
- * qsa_decode_step. Serves the shapes that qsa_decode_step runs as its fused
- * kernel (qsa_decode_step_fused(shape, kv_len) == 1), else
- * QSA_ERR_UNSUPPORTED (the separate calls serve the others). ws: device
- * scratch of qsa_workspace_bytes(shape, QSA_OP_DECODE_STEP, 1, kv_len),
- * zero-filled before its first use (the same layout as qsa_decode_step). */
+ * qsa_decode_step. bf16 only (else QSA_ERR_UNSUPPORTED). On the shapes
+ * qsa_decode_step runs as its fused kernel (qsa_decode_step_fused(shape,
+ * kv_len) == 1) the compression, selection and attention are one kernel; on
+ * the others (top_k > 64, blocks shorter than 32 keys) the selection of
+ * qsa_decode_step (compressing the closed block from the bf16 keys) writes
+ * sel, then the attention of qsa_sparse_attn_decode_q8 reads it; top_k > 64
+ * keeps the selection's limit of 65536 candidate blocks per row
+ * (QSA_ERR_UNSUPPORTED beyond). ws: device scratch of
+ * qsa_workspace_bytes(shape, QSA_OP_DECODE_STEP, 1, kv_len), zero-filled
+ * before its first use (the layout of qsa_decode_step: one workspace serves
+ * a loop whose kv_len, and with it the path, changes from step to step). */
 qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void* k, const void* v, float* k_comp,
                               int8_t* k_q, int8_t* v_q, uint16_t* k_scales, uint16_t* v_scales, int64_t kv_len,
                               int64_t kv_cap, int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,

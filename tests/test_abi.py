@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 10
+    assert qsa.abi_version() == 11
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -253,7 +253,7 @@ def test_indexer_arguments(qsa):
 
 
 def test_decode_step_q8_arguments(qsa):
-    """The fused step over the 8-bit cache validates its arguments on the host and serves the fused shapes only."""
+    """The step over the 8-bit cache validates its arguments on the host; bf16 only, any top_k and block size."""
     lib = qsa.LIB
     sh = good_shape(qsa, batch=4)
     shr = ctypes.byref(sh)
@@ -266,10 +266,22 @@ def test_decode_step_q8_arguments(qsa):
     assert call(shr, P, P, P, P, P, P, MIS, P, 4096, 4096, P, N, P, P, big, N) == INV    # scales misaligned
     assert call(shr, P, P, P, P, P, P, P, P, 4097, 4096, P, N, P, P, big, N) == INV      # beyond capacity
     assert call(shr, P, P, P, P, P, P, P, P, 0, 4096, P, N, P, P, big, N) == INV
-    # shapes the fused kernel does not serve: f32, k > 64, Bs < 32
-    for kw in (dict(dtype=qsa.QSA_F32), dict(top_k=65), dict(block_size=16)):
-        bad = ctypes.byref(good_shape(qsa, batch=4, **kw))
-        assert call(bad, P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, big, N) == UNS
+    # the 8-bit cache holds bf16 rows
+    f32 = ctypes.byref(good_shape(qsa, batch=4, dtype=qsa.QSA_F32))
+    assert call(f32, P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, big, N) == UNS
+    # shapes the fused kernel does not serve (k > 64, Bs < 32) run as the selection and the 8-bit attention, in
+    # the workspace of the plain step; k > 64 keeps the large selection's candidate limit
+    for kw in (dict(top_k=65), dict(block_size=16), dict(block_size=4, top_k=513)):
+        other = good_shape(qsa, batch=4, **kw)
+        assert not qsa.qsa_decode_step_fused(other, 4096)
+        need = qsa.qsa_workspace_bytes(other, qsa.QSA_OP_DECODE_STEP, 1, 4096)
+        assert need > 0
+        assert call(ctypes.byref(other), P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, N, need, N) == WS
+        assert call(ctypes.byref(other), P, P, P, P, P, P, P, P, 4096, 4096, P, N, P, P, need - 1, N) == WS
+    wide = good_shape(qsa, batch=1, block_size=4, top_k=100)  # 262144 candidates per row
+    with pytest.raises(qsa.QsaError):
+        qsa.qsa_workspace_bytes(wide, qsa.QSA_OP_DECODE_STEP, 1, 1 << 20)
+    assert call(ctypes.byref(wide), P, P, P, P, P, P, P, P, 1 << 20, 1 << 20, P, N, P, P, big, N) == UNS
     # few long rows run fused too (scan split over several workgroups): the workspace is checked
     one = good_shape(qsa, batch=1)
     assert qsa.qsa_decode_step_fused(one, 1 << 20)

@@ -188,19 +188,26 @@ STEP_CASES = [
     W(batch=1, kv_len=40000, top_k=16, n_q_heads=16, n_kv_heads=1),      # G = 16
     W(batch=1, kv_len=50, top_k=4),                                       # own block only
     W(batch=1, kv_len=64 * 5000 + 3, top_k=16),                           # long rows: the scan split over workgroups
+    # shapes without the fused kernel: the selection call, then the 8-bit decode attention
+    W(batch=2, kv_len=4000, top_k=16, block_size=16),
+    W(batch=2, kv_len=8 * 600, top_k=8, block_size=8, keep_tail=True),   # Bs 8, the closed block competes
+    W(batch=1, kv_len=4 * 3000 + 1, top_k=64, block_size=4),
+    W(batch=2, kv_len=20000, top_k=100),                                  # k > 64: the large selection
+    W(batch=1, kv_len=4 * 30000, top_k=513, block_size=4, keep_tail=True),
 ]
 
 
 @pytest.mark.parametrize("w", STEP_CASES, ids=lambda w: case_id(w) + ("-tail" if w.keep_tail else ""))
 def test_q8_decode_step_parity(w):
-    """The fused step over the 8-bit cache: the new position's codes and the closed block's compressed key as the
-    separate calls write them, the bf16 fused step's selection, and the 8-bit oracle's attention over it."""
+    """The decode step over the 8-bit cache (fused where the kernel serves the shape, else the selection call and
+    the 8-bit attention): the new position's codes and the closed block's compressed key as the separate calls
+    write them, the bf16 step's selection, and the 8-bit oracle's attention over it."""
     log(f"q8 decode step {case_id(w)}")
     case = Case(w, seed=34, kv_cap=w.kv_len + 70)
     b, hq, hkv, d, bs, k = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k
     G, n = hq // hkv, w.kv_len
     shape = qsa.shape_for(case.q, case.k, bs, k, keep_tail=w.keep_tail)
-    assert qsa.qsa_decode_step_fused(shape, n)
+    assert qsa.qsa_decode_step_fused(shape, n) == (bs >= 32 and k <= 64)
     kq, vq, ks, vs = qsa.kv_q8_buffers(case.k)
     qsa.qsa_kv_quantize(shape, case.k, case.v, n - 1, kq, vq, ks, vs)  # the step quantizes position n - 1
     nb_cap = case.kv_cap // bs
