@@ -68,6 +68,25 @@ __device__ __forceinline__ f32x4_t group_sum4_n(const T* p, int64_t stride) {
   for (int j = 0; j < GC; ++j) s += v[j];
   return s;
 }
+// group_sum4_n for NR rows at once (row r's head 0 at p[r]): every load of
+// the NR rows is issued before the first add, so the rows cost one memory
+// round trip together; sums in head order as above.
+template <int GC, int NR, typename T>
+__device__ __forceinline__ void group_sum4_rows(const T* const (&p)[NR], int64_t stride, f32x4_t (&out)[NR]) {
+  asm volatile("" ::: "memory");
+  f32x4_t v[NR][GC];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int j = 0; j < GC; ++j) v[r][j] = load4_f32(p[r] + j * stride);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < GC; ++j) s += v[r][j];
+    out[r] = s;
+  }
+}
 // G is one of 1, 2, 4, 8, 16 (uniform over the wave). Each case issues all
 // its loads before the first add: with a runtime bound on the head loop the
 // compiler guards every load with a branch and waits for it inside the
@@ -232,6 +251,26 @@ __device__ __forceinline__ uint64_t cas_u64(uint64_t x, uint64_t y, bool take_ma
   return ((x > y) == take_max) ? x : y;
 }
 
+__device__ __forceinline__ uint32_t cas_u32(uint32_t x, uint32_t y, bool take_max) {
+  return ((x > y) == take_max) ? x : y;
+}
+
+// Bitonic sort of one 32-bit value per lane across the wave, descending.
+__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t y = xor_lane_u32(x, j);
+      const bool lower = (lane & j) == 0;
+      const bool desc = (lane & k) == 0;
+      x = cas_u32(x, y, lower == desc);
+    }
+  }
+  return x;
+}
+
 // Bitonic sort of one key per lane across the wave, descending (lane 0 = largest).
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) {
   const int lane = lane_id();
@@ -392,20 +431,73 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// LDS written by some lanes of a wave made visible to the others (the wave's
+// LDS operations run in order; this keeps the compiler from reordering them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // The 16 largest of 256 keys held four per lane (0 = empty; the others
-// distinct), descending in lanes 0..15. The 16th largest lane maximum t is a
-// lower bound of the 16th largest key (the 16 largest maxima are keys >= t),
-// and only the 16 lanes whose maximum reaches t hold keys >= t, so at most
-// 64 keys survive the cut; they are gathered (scratch: 64 keys of LDS owned
-// by the calling wave) and sorted. Two wave sorts and a gather, where
-// sorting all 256 keys takes four 16-lane sorts and five merges.
+// distinct), descending in lanes 0..15 (0 in the other lanes).
+// Cut: the 16th largest lane maximum M bounds the 16th largest key from
+// below (the 16 largest maxima are keys >= M), so every one of the 16 best
+// keys has a high word (score image) >= th, the 16th largest high word of
+// the lane maxima. When exactly 16 lanes have a maximum whose high word
+// reaches th, the keys above the cut lie in those lanes: at most 64. (When
+// high words tie at th the cut is M itself, from a sort of the whole keys;
+// with fewer than 16 non-empty lanes every key survives, at most 60.)
+// Order: the survivors are gathered (scratch: 64 keys of LDS owned by the
+// calling wave), each lane counts the survivors above its own key, and the
+// keys of rank < 16 are placed by that rank. The cut sorts 32-bit words and
+// the order needs no sort: about half the instructions of two 64-bit sorts.
 __device__ __forceinline__ uint64_t top16_of_256(const uint64_t (&x)[4], uint64_t* scratch) {
+  const int lane = lane_id();
   const uint64_t m01 = x[0] > x[1] ? x[0] : x[1];
   const uint64_t m23 = x[2] > x[3] ? x[2] : x[3];
-  uint64_t t = readlane_u64(wave_sort_desc(m01 > m23 ? m01 : m23), 15);
-  if (t == 0ull) t = 1ull;  // fewer than 16 non-empty lanes: every key survives (at most 60)
-  int count;
-  return wave_sort_desc(gather_keys_ge<4>(x, t, scratch, count));
+  const uint64_t m = m01 > m23 ? m01 : m23;
+  const uint32_t mh = (uint32_t)(m >> 32);
+  const uint32_t th = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort_desc_u32(mh), 15);
+  uint64_t t;
+  if (th == 0u)
+    t = 1ull;  // fewer than 16 non-empty lanes (real keys have a nonzero high word)
+  else if (lanes_set(mh >= th) == 16)
+    t = (uint64_t)th << 32;
+  else
+    t = readlane_u64(wave_sort_desc(m), 15);
+  // survivors (keys >= t) into scratch[0, c), zeros in scratch[c, 64)
+  int c = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const bool s = x[p] >= t;
+    const uint64_t msk = __ballot(s);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0));
+    if (s) scratch[c + below] = x[p];
+    c += __builtin_popcountll(msk);
+  }
+  if (lane >= c) scratch[lane] = 0ull;
+  wave_lds_sync();
+  const uint64_t r = scratch[lane];
+  uint32_t rank = 0u;  // survivors above r
+  const int n8 = ((c < kWave ? c : kWave) + 7) & ~7;
+  for (int j0 = 0; j0 < n8; j0 += 8) {
+    uint64_t y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = scratch[j0 + i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rank += y[i] > r ? 1u : 0u;
+  }
+  wave_lds_sync();
+  // the key of rank i < 16 to scratch[i]; lanes c .. 15 clear theirs (ranks
+  // are below c, so the two sets of addresses are disjoint)
+  const bool put = r != 0ull && rank < 16u;
+  const bool clear = lane >= c && lane < 16;
+  if (put || clear) scratch[put ? (int)rank : lane] = put ? r : 0ull;
+  wave_lds_sync();
+  const uint64_t out = lane < 16 ? scratch[lane] : 0ull;
+  wave_lds_sync();
+  return out;
 }
 
 // Fold one lane-per-candidate batch into a running descending top list

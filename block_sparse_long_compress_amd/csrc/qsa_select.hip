@@ -680,7 +680,7 @@ inline int64_t large_tile_grid(int64_t n_bg, int64_t n_chunks, int64_t n_tiles) 
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void select_large_tile_kernel(
+__global__ __launch_bounds__(256, 3) void select_large_tile_kernel(
     const T* __restrict__ q, const float* __restrict__ k_comp, uint32_t* __restrict__ ws_scores,
     uint64_t* __restrict__ ws_lists, int64_t q_len, int64_t q_pos0, int64_t nb_cap, int hq, int hkv, int G, int bs,
     float scale, int keep_tail, int64_t n_chunks, int64_t n_tiles, int64_t n_bg) {
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
   constexpr int PASSES = kLargeChunk / kTileCands;
   constexpr int DU = D / 16;  // 16-byte operand loads per lane and pass
   __shared__ float qbar[TR][QP];
-  __shared__ float sc[TR][kLargeChunk + 4];
+  __shared__ uint32_t sc[TR][kLargeChunk + 4];  // order images of the scaled scores
   __shared__ int ncand[TR];  // candidates of each row of the tile
   __shared__ uint64_t gather[4][kWave];  // each wave's scratch for its chunk lists
   static_assert(kLargeChunk == 256, "one thread per candidate of the chunk");
@@ -711,12 +711,6 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
   if (c_begin >= cand_end) return;  // uniform over the workgroup
   if (tid < TR) ncand[tid] = tid < rows ? row_frame(q_pos0 + t0 + tid, bs, keep_tail).n_cand : 0;
 
-  for (int idx = tid; idx < TR * D / 4; idx += 256) {
-    const int r = idx / (D / 4), e4 = (idx % (D / 4)) * 4;
-    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows) v = group_sum4(q + ((b * q_len + t0 + r) * hq + (int64_t)g * G) * D + e4, G, D);
-    *reinterpret_cast<f32x4_t*>(&qbar[r][e4]) = v;
-  }
   const float* kc_src = k_comp + (bg * nb_cap) * D;
   const int m = lane % 16, kg = lane / 16;
   // B operands of pass p: candidate c_begin + 64p + 16w + m, dims 16u + 4kg .. + 3
@@ -728,6 +722,34 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
       kb[u] = cand < cand_end ? *reinterpret_cast<const f32x4_t*>(kc_src + cand * D + 16 * u + 4 * kg)
                               : f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
+  {
+    // the tile's group-summed queries: thread tid sums dims e4 .. e4 + 3 of
+    // rows r0 + RS * i (rows past the tile's end read its last row and store
+    // zeros), all rows' loads issued before the first add (with the first
+    // passes' keys also in flight the kernel would need 232 registers)
+    constexpr int NR = TR * D / 4 / 256, RS = 256 / (D / 4);
+    const int e4 = (tid % (D / 4)) * 4, r0 = tid / (D / 4);
+    const T* p[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = r0 + RS * i < rows ? r0 + RS * i : rows - 1;
+      p[i] = q + ((b * q_len + t0 + r) * hq + (int64_t)g * G) * D + e4;
+    }
+    f32x4_t v[NR];
+    switch (G) {
+      case 1: group_sum4_rows<1, NR>(p, D, v); break;
+      case 2: group_sum4_rows<2, NR>(p, D, v); break;
+      case 4: group_sum4_rows<4, NR>(p, D, v); break;
+      case 8: group_sum4_rows<8, NR>(p, D, v); break;
+      default:
+#pragma unroll
+        for (int i = 0; i < NR; ++i) v[i] = group_sum4_n<16>(p[i], D);
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+      *reinterpret_cast<f32x4_t*>(&qbar[r0 + RS * i][e4]) =
+          r0 + RS * i < rows ? v[i] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   f32x4_t kb[2][DU];
   load_pass(0, kb[0]);
   load_pass(1, kb[1]);
@@ -751,30 +773,44 @@ __global__ __launch_bounds__(256) void select_large_tile_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[16 * h + 4 * kg + i][pass * kTileCands + 16 * w + m] = acc[h][i] * scale;
+      for (int i = 0; i < 4; ++i)
+        sc[16 * h + 4 * kg + i][pass * kTileCands + 16 * w + m] = score_order_bits(acc[h][i] * scale);
   }
   __syncthreads();
   // every row's scores of the chunk (thread tid: candidate c_begin + tid of
   // each row, coalesced along the candidates)
   {
-    const int64_t cand = c_begin + tid;
+    const int cand = (int)c_begin + tid;  // below kMaxCandLarge
     const int64_t stride = (int64_t)hkv * n_chunks * kLargeChunk;  // from one row of the tile to the next
     uint32_t* dst = ws_scores + ((b * q_len + t0) * hkv + g) * n_chunks * kLargeChunk + cand;
-    for (int r = 0; r < rows; ++r, dst += stride)
-      if (cand < ncand[r]) *dst = score_order_bits(sc[r][tid]);
+    // every row's value and count read first (one LDS round trip), then the
+    // stores; rows past the tile's end have no candidates
+    uint32_t v[TR];
+    int nc[TR];
+#pragma unroll
+    for (int r = 0; r < TR; ++r) {
+      v[r] = sc[r][tid];
+      nc[r] = ncand[r];
+    }
+#pragma unroll
+    for (int r = 0; r < TR; ++r)
+      if (cand < nc[r]) dst[r * stride] = v[r];
   }
   // the chunk's 16 best keys of each row that needs them (wave w: rows 8w .. 8w + 7)
   for (int rr = 0; rr < TR / 4; ++rr) {
     const int r = (TR / 4) * w + rr;
     if (r >= rows) break;
-    const int64_t n_cand = ncand[r];
+    const int n_cand = ncand[r];
     if (n_cand <= kPoolCap || c_begin >= n_cand) continue;  // uniform over the wave
     static_assert(kLargeChunk == 4 * kWave && kLargeList == 16, "top16_of_256");
-    uint64_t x[4];
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) o[p] = sc[r][p * kWave + lane];
+    uint64_t x[4];  // keys as make_key forms them (order image : complemented id)
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int64_t cand = c_begin + p * kWave + lane;
-      x[p] = cand < n_cand ? make_key(sc[r][p * kWave + lane], (int)cand) : 0ull;
+      const int cand = (int)c_begin + p * kWave + lane;
+      x[p] = cand < n_cand ? ((uint64_t)o[p] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)cand) : 0ull;
     }
     const uint64_t top = top16_of_256(x, gather[w]);
     const int64_t row = (b * q_len + t0 + r) * hkv + g;
