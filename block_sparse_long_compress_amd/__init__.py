@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     QSA_OP_DECODE_STEP_RAGGED,
     QSA_OP_INDEXER_SELECT,
     QSA_OP_PREFILL_Q8,
+    QSA_OP_SELECT_RAGGED,
     QSA_OP_PREFILL,
     QSA_OP_SELECT,
     QsaError,
@@ -49,6 +50,8 @@ from .binding import (  # noqa: F401
     qsa_decode_step_q8,
     kv_q8_buffers,
     qsa_score_select,
+    qsa_score_select_ragged,
+    qsa_sparse_attn_decode_ragged,
     qsa_sparse_attn_decode,
     qsa_sparse_attn_prefill,
     qsa_workspace_bytes,

@@ -22,13 +22,15 @@ QSA_OP_COMPRESS, QSA_OP_SELECT, QSA_OP_DECODE, QSA_OP_PREFILL, QSA_OP_DECODE_STE
 QSA_OP_DECODE_STEP_RAGGED = 5
 QSA_OP_INDEXER_SELECT = 6
 QSA_OP_PREFILL_Q8 = 7
+QSA_OP_SELECT_RAGGED = 8
 QSA_AGG_SUM, QSA_AGG_MAX, QSA_AGG_SOFTMAX = 0, 1, 2
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_INVALID", 2: "QSA_ERR_UNSUPPORTED", 3: "QSA_ERR_WORKSPACE", 4: "QSA_ERR_HIP"}
 EXPORTED = ("qsa_abi_version", "qsa_status_str", "qsa_workspace_bytes", "qsa_compress_keys", "qsa_score_select",
             "qsa_sparse_attn_decode", "qsa_sparse_attn_prefill", "qsa_decode_step", "qsa_decode_step_fused",
             "qsa_decode_step_ragged", "qsa_indexer_keys", "qsa_indexer_select", "qsa_kv_quantize",
             "qsa_sparse_attn_decode_q8", "qsa_sparse_attn_prefill_q8", "qsa_decode_step_q8",
-            "qsa_decode_step_noalloc", "qsa_indexer_decode_step")
+            "qsa_decode_step_noalloc", "qsa_indexer_decode_step", "qsa_score_select_ragged",
+            "qsa_sparse_attn_decode_ragged")
 QSA_NOALLOC_SCRATCH_BYTES = 8 << 20  # include/qsa.h
 
 
@@ -83,6 +85,10 @@ def _load() -> ctypes.CDLL:
     lib.qsa_decode_step_fused.argtypes = [SH, I64]
     lib.qsa_decode_step_ragged.restype = ctypes.c_int
     lib.qsa_decode_step_ragged.argtypes = [SH, P, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
+    lib.qsa_score_select_ragged.restype = ctypes.c_int
+    lib.qsa_score_select_ragged.argtypes = [SH, P, P, P, I64, I64, P, P, P, SZ, P]
+    lib.qsa_sparse_attn_decode_ragged.restype = ctypes.c_int
+    lib.qsa_sparse_attn_decode_ragged.argtypes = [SH, P, P, P, P, I64, I64, P, P, P, SZ, P]
     IX = ctypes.POINTER(QsaIndexer)
     lib.qsa_indexer_keys.restype = ctypes.c_int
     lib.qsa_indexer_keys.argtypes = [SH, IX, P, P, I64, I64, I64, P, P]
@@ -218,6 +224,39 @@ def qsa_decode_step_noalloc(shape: QsaShape, q, k, v, k_comp, kv_len: int, sel, 
     _check(LIB.qsa_decode_step_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_comp), kv_len,
                                        k.shape[2], _ptr(sel), _ptr(sel_scores), _ptr(out), _stream(q, stream)),
            "qsa_decode_step_noalloc")
+    return out
+
+
+def _check_kv_lens(kv_lens, batch: int, name: str):
+    if kv_lens.dtype != torch.int32 or not kv_lens.is_contiguous() or kv_lens.numel() != batch:
+        raise QsaError(1, f"{name}: kv_lens must be a contiguous int32 tensor of length batch")
+
+
+def qsa_score_select_ragged(shape: QsaShape, q, k_comp, kv_lens, max_kv_len: int, kv_cap: int, sel,
+                            sel_scores=None, ws=None, stream=None):
+    """The selection of a ragged decode batch: sequence ``b``'s token (``q`` ``[b][Hq][d]``) sits at position
+    ``kv_lens[b] - 1``; ``sel`` ``[b][Hkv][k]``."""
+    _check_kv_lens(kv_lens, q.shape[0], "qsa_score_select_ragged")
+    if ws is None and LIB.qsa_workspace_bytes(ctypes.byref(shape), QSA_OP_SELECT_RAGGED, 1,
+                                              max_kv_len) == ctypes.c_size_t(-1).value:
+        nbytes = 0  # a shape the call does not serve: the call reports why
+    else:
+        ws, nbytes = _workspace(shape, QSA_OP_SELECT_RAGGED, 1, max_kv_len, ws, q.device)
+    _check(LIB.qsa_score_select_ragged(ctypes.byref(shape), _ptr(q), _ptr(k_comp), _ptr(kv_lens), max_kv_len,
+                                       kv_cap, _ptr(sel), _ptr(sel_scores), _ptr(ws), nbytes, _stream(q, stream)),
+           "qsa_score_select_ragged")
+    return sel
+
+
+def qsa_sparse_attn_decode_ragged(shape: QsaShape, q, k, v, kv_lens, max_kv_len: int, sel, out, ws=None,
+                                  stream=None):
+    """The attention of a ragged decode batch: sequence ``b``'s token attends at position ``kv_lens[b] - 1``."""
+    _check_kv_lens(kv_lens, q.shape[0], "qsa_sparse_attn_decode_ragged")
+    ws, nbytes = _workspace(shape, QSA_OP_DECODE, 1, max_kv_len, ws, q.device)
+    _check(LIB.qsa_sparse_attn_decode_ragged(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens),
+                                             max_kv_len, k.shape[2], _ptr(sel), _ptr(out), _ptr(ws), nbytes,
+                                             _stream(q, stream)),
+           "qsa_sparse_attn_decode_ragged")
     return out
 
 

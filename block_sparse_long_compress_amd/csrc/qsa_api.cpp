@@ -205,6 +205,10 @@ size_t qsa_workspace_bytes(const qsa_shape* shape, int op, int64_t q_len, int64_
     case QSA_OP_PREFILL_Q8:
       if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
       return q8_prefill_ws(s, q_len, kv_len - q_len).total;
+    case QSA_OP_SELECT_RAGGED:
+      if (kv_len <= 0 || kv_len > kMaxPositions) return (size_t)-1;
+      if (qsa::max_candidates(s, kv_len) > qsa::kMaxCandLarge) return (size_t)-1;
+      return qsa::plan_select_large(s, 1, kv_len - 1).ws_bytes;
     case QSA_OP_INDEXER_SELECT:
       if (q_len <= 0 || kv_len < q_len || kv_len > kMaxPositions) return (size_t)-1;
       if (s.top_k <= 64) return 0;
@@ -384,6 +388,55 @@ qsa_status qsa_decode_step(const qsa_shape* shape, const void* q, const void* k,
   if (s.dtype == QSA_F32) return qsa_sparse_attn_decode(shape, q, k, v, kv_len, kv_cap, sel, out, nullptr, 0, stream);
   const qsa::DecodePlan plan = qsa::plan_decode(s, kv_len);
   return hip_status(qsa::launch_decode(s, plan, q, k, v, kv_len, kv_cap, sel, out, base, part, hs));
+}
+
+qsa_status qsa_score_select_ragged(const qsa_shape* shape, const void* q, const float* k_comp,
+                                   const int32_t* kv_lens, int64_t max_kv_len, int64_t kv_cap, int32_t* sel,
+                                   float* sel_scores, void* ws, size_t ws_bytes, void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !kv_lens || !sel || !aligned16(q) || !aligned16(sel) || (reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0)
+    return QSA_ERR_INVALID;
+  if (sel_scores && !aligned16(sel_scores)) return QSA_ERR_INVALID;
+  if (max_kv_len <= 0 || kv_cap <= 0 || max_kv_len > kv_cap) return QSA_ERR_INVALID;
+  // k_comp is read only for candidate blocks, which exist once a row sits past the first block
+  if (qsa::max_candidates(s, max_kv_len) > 0 && (!k_comp || !aligned16(k_comp))) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  if (qsa::max_candidates(s, max_kv_len) > qsa::kMaxCandLarge) return QSA_ERR_UNSUPPORTED;
+  // every top_k through the large selection's per-row score pass and pick,
+  // which read the per-sequence lengths (no key cache: nothing is compressed)
+  const qsa::SelectPlan plan = qsa::plan_select_large(s, 1, max_kv_len - 1);
+  if (plan.grid > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  return hip_status(qsa::launch_select(s, plan, q, 1, max_kv_len - 1, k_comp, kv_cap, sel, sel_scores, ws,
+                                       static_cast<hipStream_t>(stream), nullptr, -1, true, kv_lens));
+}
+
+qsa_status qsa_sparse_attn_decode_ragged(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                         const int32_t* kv_lens, int64_t max_kv_len, int64_t kv_cap,
+                                         const int32_t* sel, void* out, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  Dims s;
+  qsa_status st = check_shape(shape, &s);
+  if (st != QSA_OK) return st;
+  if (!q || !k || !v || !kv_lens || !sel || !out) return QSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0)
+    return QSA_ERR_INVALID;
+  if (max_kv_len <= 0 || kv_cap <= 0 || max_kv_len > kv_cap) return QSA_ERR_INVALID;
+  if (kv_cap > kMaxPositions) return QSA_ERR_UNSUPPORTED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (s.dtype == QSA_F32)
+    return hip_status(qsa::launch_attn_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), 1, max_kv_len - 1, kv_cap, sel,
+                                           static_cast<float*>(out), hs, kv_lens));
+  const qsa::DecodePlan plan = qsa::plan_decode(s, max_kv_len);
+  if ((int64_t)s.batch * s.hkv * plan.n_split > 0x7FFFFFFF) return QSA_ERR_UNSUPPORTED;
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))) return QSA_ERR_WORKSPACE;
+  // arrival counters at the start of the workspace, the slice states after them
+  char* part = ws ? static_cast<char*>(ws) + qsa::counter_bytes((int64_t)s.batch * s.hkv) : nullptr;
+  return hip_status(qsa::launch_decode(s, plan, q, k, v, max_kv_len, kv_cap, sel, out, ws, part, hs, kv_lens));
 }
 
 qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const void* k, const void* v,

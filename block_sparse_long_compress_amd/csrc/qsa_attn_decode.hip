@@ -36,7 +36,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ sel, uint16_t* __restrict__ out, float* __restrict__ part,
     uint32_t* __restrict__ counters, int64_t kv_len, int64_t kv_cap, int hq, int hkv, int G, int bs, int top_k,
-    float scale_log2, int bpw, int n_split) {
+    float scale_log2, int bpw, int n_split, const int32_t* __restrict__ kv_lens) {
   using SM = DecodeSmem<D, NW>;
   constexpr int DT = D / 16;  // 16-wide dim tiles of the PV product
   __shared__ __align__(16) unsigned char smem[SM::kBytes];
@@ -47,7 +47,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_attn_kernel(
   const int64_t b = row / hkv;
   const int g = (int)(row % hkv);
   const int lane = lane_id(), w = wave_id();
-  const int64_t p = kv_len - 1;
+  // the token's position: kv_len - 1, or with kv_lens (a ragged batch)
+  // sequence b's own length, clamped into [1, kv_len], less one
+  int64_t n = kv_len;
+  if (kv_lens) {
+    n = kv_lens[b];
+    n = n < 1 ? 1 : (n > kv_len ? kv_len : n);
+  }
+  const int64_t p = n - 1;
   const int e0 = split * bpw;
   const int e1 = e0 + bpw < top_k ? e0 + bpw : top_k;
   const int n_e = e1 - e0;
@@ -130,7 +137,7 @@ hipError_t launch_prefill_rows_d(const Dims& s, const void* q, const void* k, co
 template <int D>
 hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
                     int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, uint32_t* counters, float* part,
-                    hipStream_t st) {
+                    hipStream_t st, const int32_t* kv_lens) {
   const int64_t rows = (int64_t)s.batch * s.hkv;
   const float scale_log2 = s.scale * 1.4426950408889634f;
   auto kern = plan.waves == 8 ? (s.bs < kUnit ? decode_attn_kernel<D, true, 8> : decode_attn_kernel<D, false, 8>)
@@ -140,7 +147,7 @@ hipError_t launch_d(const Dims& s, const DecodePlan& plan, const void* q, const 
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sel,
                      static_cast<uint16_t*>(out), part, counters, kv_len, kv_cap, s.hq, s.hkv, s.group, s.bs, s.top_k,
-                     scale_log2, plan.blocks_per_wg, plan.n_split);
+                     scale_log2, plan.blocks_per_wg, plan.n_split, kv_lens);
   return hipGetLastError();
 }
 
@@ -185,11 +192,11 @@ hipError_t launch_prefill_rows(const Dims& s, const void* q, const void* k, cons
 
 hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
                          int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* counters, void* part,
-                         hipStream_t st) {
+                         hipStream_t st, const int32_t* kv_lens) {
   uint32_t* c = static_cast<uint32_t*>(counters);
   float* pt = static_cast<float*>(part);
-  return s.d == 64 ? launch_d<64>(s, plan, q, k, v, kv_len, kv_cap, sel, out, c, pt, st)
-                   : launch_d<128>(s, plan, q, k, v, kv_len, kv_cap, sel, out, c, pt, st);
+  return s.d == 64 ? launch_d<64>(s, plan, q, k, v, kv_len, kv_cap, sel, out, c, pt, st, kv_lens)
+                   : launch_d<128>(s, plan, q, k, v, kv_len, kv_cap, sel, out, c, pt, st, kv_lens);
 }
 
 }  // namespace qsa

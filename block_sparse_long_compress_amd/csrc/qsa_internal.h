@@ -107,9 +107,12 @@ DecodePlan plan_decode(const Dims& s, int64_t kv_len, bool wide = true);
 // counters: the plan's arrival counters (counter_bytes(rows), zero between
 // calls); part: its slice states (ws_bytes past the counters). The decode
 // call keeps both in one workspace, the decode step at separate places.
+// kv_lens (device, [batch], nullable): per-sequence lengths, each clamped
+// into [1, kv_len] (the causal bound of sequence b's token); null means every
+// sequence has kv_len.
 hipError_t launch_decode(const Dims& s, const DecodePlan& plan, const void* q, const void* k, const void* v,
                          int64_t kv_len, int64_t kv_cap, const int32_t* sel, void* out, void* counters, void* part,
-                         hipStream_t st);
+                         hipStream_t st, const int32_t* kv_lens = nullptr);
 // Prefill attention over the rotated 8-bit cache, one workgroup per query
 // row (any top_k and block size); no workspace.
 // The 8-bit cache's positions [0, n_pos) of every (sequence, KV head),

@@ -619,7 +619,9 @@ __global__ __launch_bounds__(256) void select_large_score_kernel(
     int64_t n = kv_lens[b];
     n = n < 1 ? 1 : (n > q_pos0 + 1 ? q_pos0 + 1 : n);
     p = n - 1;
-    close_block = n % bs == 0 ? n / bs - 1 : -1;
+    // the block its token closes, compressed when the keys are given (the
+    // decode step); the selection call alone reads k_comp as it stands
+    close_block = k_cache && n % bs == 0 ? n / bs - 1 : -1;
   }
   const int n_cand = row_frame(p, bs, keep_tail).n_cand;
   const int64_t c_begin = ch * kLargeChunk;

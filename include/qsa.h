@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 11
+#define QSA_ABI_VERSION 12
 
 enum { QSA_F32 = 0, QSA_BF16 = 1 };
 
@@ -95,7 +95,8 @@ enum {
   QSA_OP_DECODE_STEP = 4,
   QSA_OP_DECODE_STEP_RAGGED = 5,
   QSA_OP_INDEXER_SELECT = 6,
-  QSA_OP_PREFILL_Q8 = 7
+  QSA_OP_PREFILL_Q8 = 7,
+  QSA_OP_SELECT_RAGGED = 8
 };
 
 typedef enum {
@@ -132,8 +133,9 @@ const char* qsa_status_str(qsa_status status);
  * (0: the call runs one row per workgroup) take q_len and
  * kv_len = q_pos0 + q_len;
  * QSA_OP_DECODE takes kv_len (q_len ignored).
- * QSA_OP_DECODE_STEP_RAGGED takes the longest sequence's length as kv_len
- * and returns (size_t)-1 for shapes the ragged step does not serve.
+ * QSA_OP_DECODE_STEP_RAGGED and QSA_OP_SELECT_RAGGED take the longest
+ * sequence's length as kv_len (q_len ignored) and return (size_t)-1 for
+ * shapes those calls do not serve.
  * Zero-fill a workspace once before its first use. Decode workspaces, and
  * selection workspaces whose rows are split over several workgroups, start
  * with one arrival counter per row ((sequence, KV head), resp. (sequence,
@@ -255,6 +257,39 @@ qsa_status qsa_decode_step_ragged(const qsa_shape* shape, const void* q, const v
                                   float* k_comp, const int32_t* kv_lens, int64_t max_kv_len, int64_t kv_cap,
                                   int32_t* sel, float* sel_scores, void* out, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/* The selection of a ragged decode batch as a call of its own: for every
+ * sequence b, the selection of qsa_score_select for the single token at
+ * position kv_lens[b] - 1 (q_len = 1, q_pos0 = kv_lens[b] - 1) on that
+ * sequence alone. kv_lens and max_kv_len as for qsa_decode_step_ragged; q
+ * [b][Hq][d]; k_comp as for qsa_score_select, holding every block complete
+ * before each sequence's token (sequence b reads blocks [0, n_cand of its
+ * row)); sel [b][Hkv][k] and sel_scores (optional) as for qsa_score_select.
+ * Any top_k: the large selection's per-row score pass and pick read the
+ * per-sequence lengths (at most 65536 candidates per row, else
+ * QSA_ERR_UNSUPPORTED). Selections equal the oracle's for each sequence (a
+ * tie within rounding may resolve either way, as for qsa_score_select; for
+ * k > 64 they equal qsa_score_select's bit for bit). ws: device scratch of
+ * qsa_workspace_bytes(shape, QSA_OP_SELECT_RAGGED, 1, max_kv_len) bytes
+ * (scores and chunk lists; 0 when no row has a candidate). */
+qsa_status qsa_score_select_ragged(const qsa_shape* shape, const void* q, const float* k_comp,
+                                   const int32_t* kv_lens, int64_t max_kv_len, int64_t kv_cap, int32_t* sel,
+                                   float* sel_scores, void* ws, size_t ws_bytes, void* stream);
+
+/* The attention of a ragged decode batch as a call of its own: for every
+ * sequence b, qsa_sparse_attn_decode with kv_len = kv_lens[b] on that
+ * sequence alone (the causal bound of its token at kv_lens[b] - 1).
+ * kv_lens and max_kv_len as for qsa_decode_step_ragged; q, k, v, sel, out as
+ * for qsa_sparse_attn_decode (sequence b reads K/V positions [0,
+ * kv_lens[b]) of its rows). Same kernels and plan as the decode call at
+ * kv_len = max_kv_len, so outputs equal a per-sequence decode call's up to
+ * the rounding of the slice merge order. ws: device scratch of
+ * qsa_workspace_bytes(shape, QSA_OP_DECODE, 1, max_kv_len), zero-filled
+ * before its first use as for the decode call. */
+qsa_status qsa_sparse_attn_decode_ragged(const qsa_shape* shape, const void* q, const void* k, const void* v,
+                                         const int32_t* kv_lens, int64_t max_kv_len, int64_t kv_cap,
+                                         const int32_t* sel, void* out, void* ws, size_t ws_bytes,
+                                         void* stream);
 
 /* ------------------------------------------------------------------------
  * Learned-indexer variant of the selection ("Qwen4 in llama.cpp: Dissecting

@@ -66,7 +66,7 @@ int main() {
               if (kt && k < 2) continue;
               qsa_shape s = shape(b, 16, 2, d, bs, k, dt, kt);
               for (int64_t n : lens) {
-                for (int op = 0; op <= QSA_OP_PREFILL_Q8; ++op) {
+                for (int op = 0; op <= QSA_OP_SELECT_RAGGED; ++op) {
                   // prefill and selection over the last 4096 query rows of n positions
                   const bool rows = op == QSA_OP_PREFILL || op == QSA_OP_SELECT || op == QSA_OP_INDEXER_SELECT ||
                                     op == QSA_OP_PREFILL_Q8;
@@ -119,6 +119,17 @@ int main() {
   expect(qsa_decode_step_ragged(&good, P, P, P, PF, reinterpret_cast<const int32_t*>(MIS4), 64, 64, PI, nullptr, P,
                                 P, 1 << 20, nullptr),
          QSA_ERR_INVALID, "ragged lengths misaligned");
+  expect(qsa_score_select_ragged(&good, P, PF, reinterpret_cast<const int32_t*>(MIS4), 64, 64, PI, nullptr, P,
+                                 1 << 20, nullptr),
+         QSA_ERR_INVALID, "ragged selection lengths misaligned");
+  expect(qsa_score_select_ragged(&b64, P, PF, reinterpret_cast<const int32_t*>(P), 131072, 131072, PI, nullptr,
+                                 nullptr, 0, nullptr),
+         QSA_ERR_WORKSPACE, "ragged selection without workspace");
+  expect(qsa_sparse_attn_decode_ragged(&good, P, P, P, nullptr, 64, 64, PI, P, P, 1 << 20, nullptr), QSA_ERR_INVALID,
+         "ragged attention without lengths");
+  expect(qsa_sparse_attn_decode_ragged(&good, P, P, P, reinterpret_cast<const int32_t*>(P), 70000, 70000, PI, P,
+                                       nullptr, 0, nullptr),
+         QSA_ERR_WORKSPACE, "ragged attention without workspace");
   qsa_shape big = shape(64, 16, 2, 128, 4, 513, QSA_BF16, 1);
   expect(qsa_decode_step_noalloc(&big, P, P, P, PF, 262144, 262144, PI, nullptr, P, nullptr), QSA_ERR_WORKSPACE,
          "no-alloc step beyond its scratch");

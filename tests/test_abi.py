@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qsa):
 
 
 def test_version_and_status_strings(qsa):
-    assert qsa.abi_version() == 11
+    assert qsa.abi_version() == 12
     for code, name in [(0, "QSA_OK"), (1, "QSA_ERR_INVALID"), (2, "QSA_ERR_UNSUPPORTED"), (3, "QSA_ERR_WORKSPACE"),
                        (4, "QSA_ERR_HIP")]:
         assert qsa.status_str(code).startswith(name)
@@ -74,7 +74,7 @@ def test_workspace_sizes(qsa):
     assert qsa.qsa_workspace_bytes(f32, qsa.QSA_OP_PREFILL, 512, 512) == 0
     assert qsa.qsa_workspace_bytes(f32, qsa.QSA_OP_DECODE, 1, 512) == 0
     with pytest.raises(qsa.QsaError):
-        qsa.qsa_workspace_bytes(sh, 8, 1, 1)  # no such op
+        qsa.qsa_workspace_bytes(sh, 9, 1, 1)  # no such op
     with pytest.raises(qsa.QsaError):
         qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT, 10, 5)
 
@@ -198,6 +198,51 @@ def test_ragged_decode_step_arguments(qsa):
     assert qsa.qsa_decode_step_fused(one, 1 << 20)
     assert qsa.qsa_workspace_bytes(one, qsa.QSA_OP_DECODE_STEP_RAGGED, 1, 1 << 20) > 0
     assert call(ctypes.byref(one), P, P, P, P, P, 1 << 20, 1 << 20, P, N, P, P, 8, N) == WS
+
+
+def test_ragged_select_and_attention_arguments(qsa):
+    """The ragged batch's selection and attention as calls of their own: per-sequence lengths validated on the
+    host; the selection takes the large selection's workspace for any top_k (scores and chunk lists of the
+    longest row), the attention the decode call's."""
+    lib = qsa.LIB
+    sh = good_shape(qsa, batch=4)
+    shr = ctypes.byref(sh)
+    P, N, MIS4 = ctypes.c_void_p(4096), None, ctypes.c_void_p(4098)
+    big = 1 << 30
+    INV, UNS, WS = 1, 2, 3
+    sel = lib.qsa_score_select_ragged
+    #           shape q  kc kv_lens max   cap  sel scores ws bytes stream
+    assert sel(shr, P, P, N, 4096, 4096, P, N, P, big, N) == INV       # no lengths
+    assert sel(shr, P, P, MIS4, 4096, 4096, P, N, P, big, N) == INV    # lengths not 4-byte aligned
+    assert sel(shr, P, P, P, 4097, 4096, P, N, P, big, N) == INV       # bound beyond capacity
+    assert sel(shr, P, P, P, 0, 4096, P, N, P, big, N) == INV
+    assert sel(shr, N, P, P, 4096, 4096, P, N, P, big, N) == INV
+    assert sel(shr, P, N, P, 4096, 4096, P, N, P, big, N) == INV       # candidates but no compressed keys
+    # every top_k: scores (4 bytes) and chunk lists (16 keys of 8 bytes) of every row's 256-candidate chunks
+    rows = 4 * 2
+    for kw, n in ((dict(), 4096), (dict(top_k=513, block_size=4, keep_tail=1), 4 * 20000), (dict(top_k=8), 64 * 300)):
+        shk = good_shape(qsa, batch=4, **kw)
+        need = qsa.qsa_workspace_bytes(shk, qsa.QSA_OP_SELECT_RAGGED, 1, n)
+        cand = n // shk.block_size if shk.keep_tail else (n - 1) // shk.block_size
+        assert need == rows * ((cand + 255) // 256) * (256 * 4 + 16 * 8)
+        assert sel(ctypes.byref(shk), P, P, P, n, n, P, N, P, need - 1, N) == WS
+    # no candidate anywhere: no workspace, k_comp not read
+    assert qsa.qsa_workspace_bytes(sh, qsa.QSA_OP_SELECT_RAGGED, 1, 64) == 0
+    # the large selection's candidate limit
+    wide = good_shape(qsa, batch=4, block_size=4, top_k=16)
+    with pytest.raises(qsa.QsaError):
+        qsa.qsa_workspace_bytes(wide, qsa.QSA_OP_SELECT_RAGGED, 1, 4 * 70000)
+    assert sel(ctypes.byref(wide), P, P, P, 4 * 70000, 4 * 70000, P, N, P, big, N) == UNS
+
+    att = lib.qsa_sparse_attn_decode_ragged
+    #           shape q  k  v  kv_lens max   cap  sel out ws bytes stream
+    assert att(shr, P, P, P, N, 4096, 4096, P, P, P, big, N) == INV    # no lengths
+    assert att(shr, P, P, P, MIS4, 4096, 4096, P, P, P, big, N) == INV
+    assert att(shr, P, P, P, P, 4097, 4096, P, P, P, big, N) == INV
+    assert att(shr, P, P, P, P, 4096, 4096, N, P, P, big, N) == INV    # no selection
+    one = good_shape(qsa, batch=1)
+    need = qsa.qsa_workspace_bytes(one, qsa.QSA_OP_DECODE, 1, 32768)
+    assert need > 0 and att(ctypes.byref(one), P, P, P, P, 32768, 32768, P, P, P, need - 1, N) == WS
 
 
 def test_indexer_arguments(qsa):

@@ -537,6 +537,51 @@ def test_decode_step_ragged(w, lens):
 
 
 
+@pytest.mark.parametrize("w,lens", RAGGED_CASES, ids=lambda x: case_id(x) if isinstance(x, S.Workload) else None)
+def test_ragged_select_and_attention_calls(w, lens):
+    """A ragged batch through the separate calls (qsa_score_select_ragged, then qsa_sparse_attn_decode_ragged
+    on its selection): every sequence matches the oracle at its own length; for k > 64 the selection equals the
+    per-sequence qsa_score_select bit for bit, and every output matches the per-sequence decode call on the same
+    selection."""
+    log(f"ragged separate calls {w} lens={lens[:8]}")
+    case = Case(w, seed=17, kv_cap=w.kv_len + 100)
+    b, hq, hkv, d, bs = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size
+    shape = qsa.shape_for(case.q, case.k, bs, w.top_k, keep_tail=w.keep_tail)
+    one = qsa.make_shape(1, hq, hkv, d, bs, w.top_k, case.q.dtype, keep_tail=w.keep_tail)
+    nbc = case.kv_cap // bs
+    k_comp = torch.full((b, hkv, nbc, d), float("nan"), device="cuda")
+    for bb, n in enumerate(lens):  # every block complete at each sequence's token
+        qsa.qsa_compress_keys(one, case.k[bb:bb + 1], n, k_comp[bb:bb + 1])
+    q = case.q.view(b, hq, d)
+    kv_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sel = torch.empty(b, hkv, w.top_k, dtype=torch.int32, device="cuda")
+    scores = torch.empty(b, hkv, w.top_k, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    qsa.qsa_score_select_ragged(shape, q, k_comp, kv_lens, w.kv_len, case.kv_cap, sel, sel_scores=scores)
+    qsa.qsa_sparse_attn_decode_ragged(shape, q, case.k, case.v, kv_lens, w.kv_len, sel, out)
+    torch.cuda.synchronize()
+    sel_h, out_h, sc_h = sel.cpu().numpy(), from_device(out), scores.cpu().numpy()
+    for bb, n in enumerate(lens):
+        rows = [(bb, 0, g) for g in range(hkv)]
+        st = check_rows(case, sel_h[:, None], out_h[:, None], rows, n - 1, scores_gpu=sc_h[:, None])
+        if bb < 8 or bb == b - 1:
+            log(f"  seq {bb} len {n}: {st}")
+    for bb, n in list(enumerate(lens))[:: max(1, len(lens) // 6)]:
+        if w.top_k > 64:
+            s1 = torch.empty(1, hkv, w.top_k, dtype=torch.int32, device="cuda")
+            sc1 = torch.empty(1, hkv, w.top_k, dtype=torch.float32, device="cuda")
+            qsa.qsa_score_select(one, q[bb:bb + 1].view(1, 1, hq, d), n - 1, k_comp[bb:bb + 1], n, case.kv_cap, s1, sc1)
+            torch.cuda.synchronize()
+            assert torch.equal(s1[0], sel[bb]), f"sequence {bb}: selection differs from the single-sequence call"
+            assert torch.equal(sc1[0], scores[bb]), f"sequence {bb}: scores differ from the single-sequence call"
+        o1 = torch.empty(1, hq, d, dtype=q.dtype, device="cuda")
+        qsa.qsa_sparse_attn_decode(one, q[bb:bb + 1], case.k[bb:bb + 1], case.v[bb:bb + 1], n, sel[bb:bb + 1].clone(),
+                                   o1)
+        torch.cuda.synchronize()
+        err = (o1[0].float() - out[bb].float()).abs().max().item()
+        assert err <= 2e-2, f"sequence {bb}: output differs from the single-sequence decode call by {err}"
+
+
 TIE_CASES = [
     W(kv_len=3000, top_k=16, block_size=32),                      # prefill row path
     W(kv_len=3000, top_k=24, block_size=32),                      # prefill threshold-select tile path
