@@ -668,9 +668,7 @@ template <int D, int BS, int W, int NCG>
 hipError_t launch_kernel(const Dims& s, const PrefillGeom& gm, int64_t q_len, int64_t q_pos0, int64_t kv_cap,
                          int64_t n_units, const void* q, const void* k, const uint16_t* vt, const int32_t* sel,
                          void* out, hipStream_t st) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&prefill_attn_kernel<D, BS, W, NCG>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      160 * 1024);
+  const hipError_t attr = allow_dynamic_lds<&prefill_attn_kernel<D, BS, W, NCG>>(160 * 1024);
   if (attr != hipSuccess) return attr;
   const int n_bg = s.batch * s.hkv;
   // one (sequence, KV head) pair per group of XCDs when pairs and tiles split evenly over the 8 XCDs

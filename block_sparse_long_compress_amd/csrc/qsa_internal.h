@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace qsa {
 
 struct Dims {
@@ -203,5 +205,24 @@ hipError_t launch_attn_f32(const Dims& s, const float* q, const float* k, const 
                            const int32_t* kv_lens = nullptr);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Raises kernel Fn's dynamic LDS limit to `bytes`, once per device: the
+// attribute is set for the device current at the call, so a process that
+// drives several GPUs sets it on each of them before the kernel's first
+// launch there. Returns the result of that device's call.
+template <auto Fn>
+hipError_t allow_dynamic_lds(int bytes) {
+  constexpr int kDevices = 64;
+  static std::once_flag once[kDevices];
+  static hipError_t err[kDevices];
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev, bytes] {
+    err[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(Fn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  });
+  return err[dev];
+}
 
 }  // namespace qsa

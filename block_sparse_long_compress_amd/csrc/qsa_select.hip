@@ -913,9 +913,7 @@ hipError_t launch_typed(const Dims& s, const SelectPlan& plan, const void* qv, i
     return hipGetLastError();
   }
   if (plan.tiled && s.top_k <= kRowKeep) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&select_rows_kernel<T, D>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        rows_lds_bytes<D>());
+    const hipError_t attr = allow_dynamic_lds<&select_rows_kernel<T, D>>(rows_lds_bytes<D>());
     if (attr != hipSuccess) return attr;
     dim3 grid((unsigned)((q_len + kRowsPerWg - 1) / kRowsPerWg), (unsigned)s.hkv, (unsigned)s.batch);
     hipLaunchKernelGGL((select_rows_kernel<T, D>), grid, dim3(512), rows_lds_bytes<D>(), st, q, k_comp, sel,
