@@ -188,8 +188,8 @@ class Step:
                 self.n_new_blocks = sum(1 for n in self.lens if n % bs == 0)
             elif w.kv_q8:
                 # the attention reads the rotated 8-bit cache: one qsa_decode_step_q8 call (quantize the
-                # new position, then compress, select and attend in one kernel) where the fused kernel
-                # serves the shape, else the separate calls
+                # new position, compress, select and attend in one kernel) where the fused kernel serves
+                # the shape, else the separate calls
                 self.fused = qsa.qsa_decode_step_fused(self.shape, w.kv_len)
                 self.ws_step = self._ws(qsa.QSA_OP_DECODE_STEP, 1, w.kv_len) if self.fused else None
                 self.kq, self.vq, self.ks, self.vs = qsa.kv_q8_buffers(self.k)
@@ -545,7 +545,7 @@ def measured_traffic(workload, call):
 
 KERNELS = {
     "step": "decode_step_kernel (compress of the closed block, selection and attention in one kernel)",
-    "step_q8": "kv_quantize_kernel + decode_step_kernel over the 8-bit cache",
+    "step_q8": "decode_step_kernel over the 8-bit cache (quantize of the new position, compress, selection and attention in one kernel)",
     "step_indexer": "indexer_select_kernel as the indexer decode step (compress and indexer key of the closed "
                     "block, indexer selection and attention in one kernel)",
     "step_large": "select_large_score_kernel (scores, with the closed block's compression) + pick_attend_kernel "

@@ -676,11 +676,14 @@ qsa_status qsa_decode_step_q8(const qsa_shape* shape, const void* q, const void*
   const StepWs lay = step_ws(s, kv_len, true);
   if (lay.total > 0 && (!ws || ws_bytes < lay.total || !aligned16(ws))) return QSA_ERR_WORKSPACE;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // the new position into the 8-bit cache first
-  st = hip_status(qsa::launch_kv_quantize(s, k, v, kv_cap, kv_len - 1, kv_len, k_q, v_q, k_scales, v_scales, hs));
-  if (st != QSA_OK) return st;
   char* base = static_cast<char*>(ws);
   char* part = base ? base + lay.part_off : nullptr;
+  // the fused kernel writes the new position into the 8-bit cache itself;
+  // the separate calls quantize it first
+  if (!sp.fused) {
+    st = hip_status(qsa::launch_kv_quantize(s, k, v, kv_cap, kv_len - 1, kv_len, k_q, v_q, k_scales, v_scales, hs));
+    if (st != QSA_OK) return st;
+  }
   if (sp.fused) {
     const qsa::Q8Cache cache{k_q, v_q, k_scales, v_scales};
     return hip_status(qsa::launch_decode_step(s, sp, q, k, v, k_comp, kv_len, kv_cap, sel, sel_scores, out, base,

@@ -294,6 +294,30 @@ __global__ __launch_bounds__(kStepWaves * kWave) void decode_step_kernel(
   // 3. attention over the selection, units round-robin over the waves
   u32x4_t qf[D / 32];
   if constexpr (Q8) {
+    // The new token's K and V rows into the 8-bit cache (the caller's cache
+    // is writable; only this step kernel writes through these pointers). The
+    // slice that attends the token's block writes them, so its own waves read
+    // them back after the barrier below: stores and loads of one CU, with the
+    // stores complete in L2 before the barrier and no line of these rows in
+    // the CU's L1 before them (the kernel reads the cache only in the
+    // attention). When no slice attends that block (a complete block that
+    // lost the selection in the keep-tail frame) slice 0 writes them, for
+    // later steps.
+    {
+      const int own_blk = (int)(p / BS);
+      const int sl = n_scan > 1 ? part : split;
+      const int e0w = sl * bpw;
+      const int n_w = top_k - e0w < bpw ? top_k - e0w : bpw;  // top_k <= 64 in this kernel
+      const unsigned long long hit = __ballot(lane < top_k && ids[lane] == own_blk);
+      const int at = hit != 0ull ? __builtin_ctzll(hit) : -1;
+      const bool writer = at >= 0 ? (at >= e0w && at < e0w + n_w) : sl == 0;
+      if (writer && w < 2) {
+        const int64_t ro = (kv_off + p) * D;
+        quantize_row_wave<D>((w == 0 ? k : v) + ro, const_cast<int8_t*>(w == 0 ? q8.k : q8.v) + ro,
+                             const_cast<uint16_t*>(w == 0 ? q8.ks : q8.vs) + (kv_off + p) * (D / 32));
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    }
     // (H q).(H k) = D q.k: the 1/D goes into the scale below
     constexpr int EPL = D / kWave;
     for (int h = w; h < G; h += kStepWaves) {

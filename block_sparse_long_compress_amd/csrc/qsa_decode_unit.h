@@ -87,6 +87,37 @@ __device__ __forceinline__ void fwht_wave(float (&v)[D / kWave]) {
   }
 }
 
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+// One row of the rotated 8-bit cache, by one wave: the Walsh-Hadamard
+// rotation of the bf16 row src, then for each 32 values a float16 scale (the
+// largest magnitude / 127, rounded to float16) and codes
+// round-half-even(value / scale) clamped to [-127, 127] (0 when the scale is
+// 0), written to dq (D codes) and ds (D / 32 scales).
+template <int D>
+__device__ __forceinline__ void quantize_row_wave(const uint16_t* __restrict__ src, int8_t* __restrict__ dq,
+                                                  uint16_t* __restrict__ ds) {
+  constexpr int EPL = D / kWave;
+  const int lane = lane_id();
+  float x[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) x[i] = bf16_to_f32(src[lane + kWave * i]);
+  fwht_wave<D>(x);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    // the 32 lanes of element lane + 64 i that share a group
+    float amax = fabsf(x[i]);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, shfl_xor_f32(amax, m));
+    const uint16_t sbits = f32_to_f16_bits(amax / 127.0f);
+    const float scale = f16_bits_to_f32(sbits);
+    float c = scale > 0.f ? __builtin_rintf(x[i] / scale) : 0.f;
+    c = fminf(fmaxf(c, -127.f), 127.f);
+    dq[lane + kWave * i] = (int8_t)(int)c;
+    if ((lane & 31) == 0) ds[(lane + kWave * i) / 32] = sbits;
+  }
+}
+
 // Q operands in the 8-bit cache's dim order: step s = 2t + h takes, in lane
 // group lg, dims 64 t + 16 lg + 8 h .. +7 (a lane's 16-byte code load covers
 // both steps of a pair). Any order of the dims gives the same dot products.

@@ -22,8 +22,6 @@
 namespace qsa {
 namespace {
 
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
-
 // One wave per (sequence, KV head, position, K or V): rotate the row, then
 // quantize each 32-value group.
 template <int D>
@@ -32,7 +30,6 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
                                                           uint16_t* __restrict__ ks, uint16_t* __restrict__ vs,
                                                           int64_t kv_cap, int64_t pos_begin, int64_t n_pos,
                                                           int64_t n_items) {
-  constexpr int EPL = D / kWave;
   const int64_t item = (int64_t)blockIdx.x * 4 + wave_id();
   if (item >= 2 * n_items) return;
   const bool is_v = item >= n_items;
@@ -40,27 +37,8 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t* __rest
   const int64_t bg = it / n_pos;
   const int64_t pos = pos_begin + it % n_pos;
   const int64_t rowoff = (bg * kv_cap + pos) * D;
-  const uint16_t* src = (is_v ? v : k) + rowoff;
-  const int lane = lane_id();
-  float x[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) x[i] = bf16_to_f32(src[lane + kWave * i]);
-  fwht_wave<D>(x);
-  int8_t* dq = (is_v ? vq : kq) + rowoff;
-  uint16_t* ds = (is_v ? vs : ks) + (bg * kv_cap + pos) * (D / 32);
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    // the 32 lanes of element lane + 64 i that share a group
-    float amax = fabsf(x[i]);
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, shfl_xor_f32(amax, m));
-    const uint16_t sbits = f32_to_f16_bits(amax / 127.0f);
-    const float scale = f16_bits_to_f32(sbits);
-    float c = scale > 0.f ? __builtin_rintf(x[i] / scale) : 0.f;
-    c = fminf(fmaxf(c, -127.f), 127.f);
-    dq[lane + kWave * i] = (int8_t)(int)c;
-    if ((lane & 31) == 0) ds[(lane + kWave * i) / 32] = sbits;
-  }
+  quantize_row_wave<D>((is_v ? v : k) + rowoff, (is_v ? vq : kq) + rowoff,
+                       (is_v ? vs : ks) + (bg * kv_cap + pos) * (D / 32));
 }
 
 template <int D, int NW>

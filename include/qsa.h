@@ -442,8 +442,9 @@ qsa_status qsa_sparse_attn_prefill_q8(const qsa_shape* shape, const void* q, con
  * 0 .. kv_len - 2 already. sel, sel_scores (optional), out as for
  * qsa_decode_step. bf16 only (else QSA_ERR_UNSUPPORTED). On the shapes
  * qsa_decode_step runs as its fused kernel (qsa_decode_step_fused(shape,
- * kv_len) == 1) the compression, selection and attention are one kernel; on
- * the others (top_k > 64, blocks shorter than 32 keys) the selection of
+ * kv_len) == 1) the quantization of the new position, the compression,
+ * selection and attention are one kernel (the codes equal qsa_kv_quantize's
+ * bit for bit); on the others (top_k > 64, blocks shorter than 32 keys) the selection of
  * qsa_decode_step (compressing the closed block from the bf16 keys) writes
  * sel, then the attention of qsa_sparse_attn_decode_q8 reads it; top_k > 64
  * keeps the selection's limit of 65536 candidate blocks per row

@@ -219,6 +219,12 @@ def test_q8_decode_step_parity(w):
     scores = torch.empty(b, hkv, k, dtype=torch.float32, device="cuda")
     out = torch.empty_like(q)
     qsa.qsa_decode_step_q8(shape, q, case.k, case.v, k_comp, kq, vq, ks, vs, n, sel, out, sel_scores=scores)
+    # The fused kernel writes position n - 1 into the cache and its attention reads it back: a second step over
+    # the cache as the first left it (the position already written) must give the same output bit for bit, which
+    # fails if the first step's attention read the position before its codes were written.
+    out_again = torch.empty_like(q)
+    qsa.qsa_decode_step_q8(shape, q, case.k, case.v, k_comp.clone(), kq, vq, ks, vs, n, torch.empty_like(sel),
+                           out_again)
     # references from the separate calls and the bf16 fused step
     kq2, vq2, ks2, vs2 = qsa.kv_q8_buffers(case.k)
     qsa.qsa_kv_quantize(shape, case.k, case.v, n, kq2, vq2, ks2, vs2)
@@ -232,6 +238,7 @@ def test_q8_decode_step_parity(w):
     torch.cuda.synchronize()
     for a, c in ((kq, kq2), (vq, vq2), (ks, ks2), (vs, vs2)):
         assert torch.equal(a[:, :, :n], c[:, :, :n]), "8-bit cache differs from the quantize call"
+    assert torch.equal(out, out_again), "the step's output depends on whether the new position was in the cache"
     nb = n // bs
     assert torch.equal(k_comp[:, :, :nb], k_comp_ref[:, :, :nb]), "compressed keys differ from the compress call"
     if not (w.keep_tail and n % bs == 0):  # else the new block's score may round differently
